@@ -1,0 +1,219 @@
+/*
+ * linattn_oracle.c -- plain, slow fp64 CPU oracle for causal linear attention.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing on the product path may link, load or call
+ * this file; only the test suite, the smoke check and the benchmark's CPU
+ * baseline leg use it. It shares no code, header or constant with the HIP
+ * library.
+ *
+ * What it computes is the definition of causal linear attention, token by token,
+ * in fp64 on the exact stored input values (bf16 or fp32, upcast exactly):
+ *
+ *   for t = 1..T:  f = psi(k_t);  S = gamma*S + f v_t^T;  Z = gamma*Z + f
+ *                  g = psi(q_t);  o_t = g^T S / (g . Z + eps)   (or g^T S alone)
+ *
+ *  - the recurrent dual S_t = S_{t-1} + phi(k_t)^T v_t, z_t = z_{t-1} + phi(k_t)^T,
+ *    o_t = phi(q_t) S_t / phi(q_t) z_t: "Linear Attention and Retentive Networks",
+ *    section "The Recurrent Dual";
+ *  - the decayed recurrence S_t = gamma S_{t-1} + k_t^T v_t, o_t = q_t S_t:
+ *    same page, "Retentive Networks", recurrent representation (B);
+ *  - eps added to the denominator dot product: "Log-Depth Chunked Linear-Attention
+ *    Scan", Implementation notes (z_t = phi_q S / (phi_q Z + eps));
+ *  - the normaliser Z decays with the same gamma as S, and every step updates the
+ *    state before reading it (the inclusive sum over i <= t of the mathematical
+ *    statement on the same page);
+ *  - feature maps: identity; elu(x)+1 ("Linear Attention and Retentive Networks",
+ *    "The Associative Property and Linear Kernel Formulation"); positive random
+ *    features psi(x)_p = exp(w_p . x - |x|^2/2) / sqrt(m) ("Linearized 2-Simplicial
+ *    Attention", section 3.2 and appendix "Feature scaling": the m^{-1/2} factor
+ *    sits on each feature vector).
+ *
+ * Build: gcc -O2 -std=c99 -ffp-contract=off -fopenmp -shared -fPIC
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { ORC_PSI_IDENTITY = 0, ORC_PSI_ELU1 = 1, ORC_PSI_PRF = 2 };
+enum { ORC_BF16 = 0, ORC_F32 = 1 };
+
+/* Exact upcast of one stored element. bf16 is the top half of an IEEE fp32. */
+static double load_elem(const void* base, int dtype, size_t idx) {
+  if (dtype == ORC_F32) return (double)((const float*)base)[idx];
+  uint32_t bits = (uint32_t)((const uint16_t*)base)[idx] << 16;
+  float f;
+  memcpy(&f, &bits, sizeof f);
+  return (double)f;
+}
+
+static void load_vec(const void* base, int dtype, size_t off, int n, double* out) {
+  for (int j = 0; j < n; ++j) out[j] = load_elem(base, dtype, off + (size_t)j);
+}
+
+/* psi(x) for one vector x[d_k] -> out[n_psi]. w is the head's bank [n_psi][d_k] (PRF only). */
+void oracle_feature_f64(int psi, int d_k, int n_psi, const double* x, const double* w, double* out) {
+  if (psi == ORC_PSI_IDENTITY) {
+    for (int j = 0; j < d_k; ++j) out[j] = x[j];
+  } else if (psi == ORC_PSI_ELU1) {
+    /* elu(x) = x for x > 0, exp(x) - 1 otherwise; plus one. */
+    for (int j = 0; j < d_k; ++j) out[j] = x[j] > 0.0 ? x[j] + 1.0 : exp(x[j]);
+  } else {
+    double sq = 0.0;
+    for (int j = 0; j < d_k; ++j) sq += x[j] * x[j];
+    double inv_sqrt_m = 1.0 / sqrt((double)n_psi);
+    for (int p = 0; p < n_psi; ++p) {
+      double dot = 0.0;
+      for (int j = 0; j < d_k; ++j) dot += w[(size_t)p * d_k + j] * x[j];
+      out[p] = exp(dot - 0.5 * sq) * inv_sqrt_m;
+    }
+  }
+}
+
+/* One token of the recurrence on the state (S[n_psi][d_v], Z[n_psi]).
+ * k_t, v_t update the state; if q_t is given, o_t is written afterwards. */
+static void recurrence_step(int psi, int d_k, int d_v, int n_psi, const double* w, double gamma,
+                            int normalize, double eps, const double* kt, const double* vt,
+                            const double* qt, double* S, double* Z, double* f, double* g,
+                            double* ot) {
+  oracle_feature_f64(psi, d_k, n_psi, kt, w, f);
+  for (int p = 0; p < n_psi; ++p) {
+    double* row = S + (size_t)p * d_v;
+    for (int e = 0; e < d_v; ++e) row[e] = gamma * row[e] + f[p] * vt[e];
+    if (Z) Z[p] = gamma * Z[p] + f[p];
+  }
+  if (!qt) return;
+  oracle_feature_f64(psi, d_k, n_psi, qt, w, g);
+  double den = 0.0;
+  if (normalize) {
+    for (int p = 0; p < n_psi; ++p) den += g[p] * Z[p];
+    den += eps;
+  }
+  /* numerator g^T S, summed over p in increasing order for every column e */
+  for (int e = 0; e < d_v; ++e) ot[e] = 0.0;
+  for (int p = 0; p < n_psi; ++p) {
+    const double* row = S + (size_t)p * d_v;
+    for (int e = 0; e < d_v; ++e) ot[e] += g[p] * row[e];
+  }
+  if (normalize)
+    for (int e = 0; e < d_v; ++e) ot[e] = ot[e] / den;
+}
+
+/*
+ * Prefill oracle over nblk independent (batch, head) blocks, OpenMP across blocks.
+ *   q, k: [nblk][T][d_k], v: [nblk][T][d_v], stored as in_dtype (q may be NULL: state only)
+ *   w: PRF banks [H_w][n_psi][d_k] stored as in_dtype (NULL unless psi == PRF);
+ *   w_head[b]: which bank block b uses (NULL => bank 0)
+ *   gamma[b]: the decay of block b (fp32 value passed as double); NULL => 1
+ *   S0, Z0: initial state [nblk][n_psi][d_v], [nblk][n_psi] (NULL => zero)
+ *   o: [nblk][T][d_v] (NULL if q is NULL); S_out, Z_out: final state (NULL => not written)
+ *   nthreads <= 0 => OpenMP default.
+ * Returns 0, or -1 on an allocation failure or bad argument.
+ */
+int oracle_prefill_f64(int nblk, int T, int d_k, int d_v, int n_psi, int psi, int in_dtype,
+                       const void* q, const void* k, const void* v, const void* w,
+                       const int32_t* w_head, const double* gamma, int normalize, double eps,
+                       const double* S0, const double* Z0, double* o, double* S_out,
+                       double* Z_out, int nthreads) {
+  if (nblk < 0 || T < 0 || d_k <= 0 || d_v <= 0 || n_psi <= 0) return -1;
+  if (psi != ORC_PSI_PRF && n_psi != d_k) return -1;
+  if (psi == ORC_PSI_PRF && !w) return -1;
+  if (q && !o) return -1;
+  int err = 0;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : err)
+#endif
+  for (int b = 0; b < nblk; ++b) {
+    double* S = (double*)calloc((size_t)n_psi * d_v, sizeof(double));
+    double* Z = (double*)calloc((size_t)n_psi, sizeof(double));
+    double* f = (double*)malloc(sizeof(double) * (size_t)n_psi);
+    double* g = (double*)malloc(sizeof(double) * (size_t)n_psi);
+    double* kt = (double*)malloc(sizeof(double) * (size_t)d_k);
+    double* qt = (double*)malloc(sizeof(double) * (size_t)d_k);
+    double* vt = (double*)malloc(sizeof(double) * (size_t)d_v);
+    double* wd = NULL;
+    if (psi == ORC_PSI_PRF) wd = (double*)malloc(sizeof(double) * (size_t)n_psi * d_k);
+    if (!S || !Z || !f || !g || !kt || !qt || !vt || (psi == ORC_PSI_PRF && !wd)) {
+      err |= 1;
+    } else {
+      if (wd) {
+        size_t hw = w_head ? (size_t)w_head[b] : 0;
+        load_vec(w, in_dtype, hw * (size_t)n_psi * d_k, n_psi * d_k, wd);
+      }
+      if (S0) memcpy(S, S0 + (size_t)b * n_psi * d_v, sizeof(double) * (size_t)n_psi * d_v);
+      if (Z0) memcpy(Z, Z0 + (size_t)b * n_psi, sizeof(double) * (size_t)n_psi);
+      double gm = gamma ? gamma[b] : 1.0;
+      for (int t = 0; t < T; ++t) {
+        size_t rowk = ((size_t)b * T + t) * d_k, rowv = ((size_t)b * T + t) * d_v;
+        load_vec(k, in_dtype, rowk, d_k, kt);
+        load_vec(v, in_dtype, rowv, d_v, vt);
+        if (q) load_vec(q, in_dtype, rowk, d_k, qt);
+        recurrence_step(psi, d_k, d_v, n_psi, wd, gm, normalize, eps, kt, vt, q ? qt : NULL, S, Z,
+                        f, g, q ? o + rowv : NULL);
+      }
+      if (S_out) memcpy(S_out + (size_t)b * n_psi * d_v, S, sizeof(double) * (size_t)n_psi * d_v);
+      if (Z_out) memcpy(Z_out + (size_t)b * n_psi, Z, sizeof(double) * (size_t)n_psi);
+    }
+    free(S); free(Z); free(f); free(g); free(kt); free(qt); free(vt); free(wd);
+  }
+  return err ? -1 : 0;
+}
+
+/*
+ * One decode step for nblk independent states, in place: the same loop body as
+ * the prefill recurrence applied to a single token ("Linear Attention and
+ * Retentive Networks", The Recurrent Dual: O(1) memory per step).
+ *   q, k: [nblk][d_k], v: [nblk][d_v] (in_dtype); S [nblk][n_psi][d_v], Z [nblk][n_psi] (fp64, in/out;
+ *   Z may be NULL when normalize == 0); o [nblk][d_v].
+ */
+int oracle_decode_step_f64(int nblk, int d_k, int d_v, int n_psi, int psi, int in_dtype,
+                           const void* q, const void* k, const void* v, const void* w,
+                           const int32_t* w_head, const double* gamma, int normalize, double eps,
+                           double* S, double* Z, double* o, int nthreads) {
+  if (nblk < 0 || d_k <= 0 || d_v <= 0 || n_psi <= 0 || !q || !k || !v || !S || !o) return -1;
+  if (psi != ORC_PSI_PRF && n_psi != d_k) return -1;
+  if (psi == ORC_PSI_PRF && !w) return -1;
+  if (normalize && !Z) return -1;
+  int err = 0;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(static) reduction(| : err)
+#endif
+  for (int b = 0; b < nblk; ++b) {
+    double* f = (double*)malloc(sizeof(double) * (size_t)n_psi);
+    double* g = (double*)malloc(sizeof(double) * (size_t)n_psi);
+    double* kt = (double*)malloc(sizeof(double) * (size_t)d_k);
+    double* qt = (double*)malloc(sizeof(double) * (size_t)d_k);
+    double* vt = (double*)malloc(sizeof(double) * (size_t)d_v);
+    double* wd = NULL;
+    if (psi == ORC_PSI_PRF) wd = (double*)malloc(sizeof(double) * (size_t)n_psi * d_k);
+    if (!f || !g || !kt || !qt || !vt || (psi == ORC_PSI_PRF && !wd)) {
+      err |= 1;
+    } else {
+      if (wd) {
+        size_t hw = w_head ? (size_t)w_head[b] : 0;
+        load_vec(w, in_dtype, hw * (size_t)n_psi * d_k, n_psi * d_k, wd);
+      }
+      load_vec(k, in_dtype, (size_t)b * d_k, d_k, kt);
+      load_vec(q, in_dtype, (size_t)b * d_k, d_k, qt);
+      load_vec(v, in_dtype, (size_t)b * d_v, d_v, vt);
+      recurrence_step(psi, d_k, d_v, n_psi, wd, gamma ? gamma[b] : 1.0, normalize, eps, kt, vt, qt,
+                      S + (size_t)b * n_psi * d_v, Z ? Z + (size_t)b * n_psi : NULL, f, g,
+                      o + (size_t)b * d_v);
+    }
+    free(f); free(g); free(kt); free(qt); free(vt); free(wd);
+  }
+  return err ? -1 : 0;
+}
+
+int oracle_max_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}

@@ -1,0 +1,84 @@
+"""The oracle's pins must catch plausible mistakes.
+
+Each case copies the oracle's C source, plants one mistake (a dropped term, a
+wrong sign, index or scale, a transposed operand), builds the copy on the CPU and
+runs the pin suite against it; the suite must fail. Nothing here touches a GPU or
+the product library.
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "linattn_oracle.c")
+PINS = os.path.join(ROOT, "tests", "test_oracle_pins.py")
+
+MUTATIONS = {
+    "S_not_decayed": [("row[e] = gamma * row[e] + f[p] * vt[e];", "row[e] = row[e] + f[p] * vt[e];")],
+    "Z_not_decayed": [("if (Z) Z[p] = gamma * Z[p] + f[p];", "if (Z) Z[p] = Z[p] + f[p];")],
+    "value_index_dropped": [("row[e] = gamma * row[e] + f[p] * vt[e];", "row[e] = gamma * row[e] + f[p] * vt[0];")],
+    "eps_outside_ratio": [("    den += eps;\n", ""), ("ot[e] = ot[e] / den;", "ot[e] = ot[e] / den + eps;")],
+    "eps_sign": [("den += eps;", "den -= eps;")],
+    "elu_missing_plus_one": [("x[j] > 0.0 ? x[j] + 1.0 : exp(x[j])", "x[j] > 0.0 ? x[j] : exp(x[j])")],
+    "elu_wrong_branch": [("x[j] > 0.0 ? x[j] + 1.0 : exp(x[j])", "x[j] > 0.0 ? exp(x[j]) : x[j] + 1.0")],
+    "prf_norm_not_halved": [("exp(dot - 0.5 * sq)", "exp(dot - sq)")],
+    "prf_norm_sign": [("exp(dot - 0.5 * sq)", "exp(dot + 0.5 * sq)")],
+    "prf_scale_1_over_m": [("1.0 / sqrt((double)n_psi)", "1.0 / (double)n_psi")],
+    "state_transposed": [("ot[e] += g[p] * row[e];",
+                          "ot[e] += g[p] * S[(size_t)(e % n_psi) * d_v + (size_t)(p % d_v)];")],
+    "gamma_of_block0": [("double gm = gamma ? gamma[b] : 1.0;", "double gm = gamma ? gamma[0] : 1.0;")],
+    "bank_of_head0": [("size_t hw = w_head ? (size_t)w_head[b] : 0;\n        load_vec(w, in_dtype, hw",
+                       "size_t hw = 0;\n        load_vec(w, in_dtype, hw")],
+    "initial_Z_ignored": [("if (Z0) memcpy(Z, Z0", "if (0) memcpy(Z, Z0")],
+    "query_feature_from_key": [("oracle_feature_f64(psi, d_k, n_psi, qt, w, g);",
+                                "oracle_feature_f64(psi, d_k, n_psi, kt, w, g);")],
+}
+
+
+def _run_mutation(name, edits, workdir):
+    src = open(SRC).read()
+    for old, new in edits:
+        assert old in src, f"{name}: pattern not found: {old!r}"
+        src = src.replace(old, new, 1)
+    d = os.path.join(workdir, name)
+    os.makedirs(d)
+    c_path = os.path.join(d, "m.c")
+    so_path = os.path.join(d, "m.so")
+    open(c_path, "w").write(src)
+    subprocess.run(["gcc", "-O2", "-std=c99", "-ffp-contract=off", "-fopenmp", "-shared", "-fPIC", c_path,
+                    "-o", so_path, "-lm"], check=True, capture_output=True)
+    env = dict(os.environ, LINATTN_ORACLE_LIB=so_path, OMP_NUM_THREADS="1")
+    r = subprocess.run([sys.executable, "-m", "pytest", PINS, "-x", "-q", "-p", "no:cacheprovider"],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
+    return name, r.returncode, r.stdout[-400:]
+
+
+def test_pins_catch_every_planted_mistake():
+    workdir = tempfile.mkdtemp(prefix="oracle_mut_")
+    try:
+        with cf.ThreadPoolExecutor(max_workers=4) as ex:
+            results = list(ex.map(lambda kv: _run_mutation(kv[0], kv[1], workdir), MUTATIONS.items()))
+    finally:
+        shutil.rmtree(workdir, ignore_errors=True)
+    survivors = [(n, out) for n, rc, out in results if rc == 0]
+    assert not survivors, f"mutations not caught by the pins: {survivors}"
+    # a failure must be a failed assertion, not a broken harness (pytest exit code 1)
+    odd = [(n, rc) for n, rc, _ in results if rc != 1]
+    assert not odd, f"unexpected pytest exit codes: {odd}"
+
+
+def test_unmutated_copy_passes():
+    """Control: the same harness with an unmodified copy passes, so failures above are the planted mistakes."""
+    workdir = tempfile.mkdtemp(prefix="oracle_ctl_")
+    try:
+        name, rc, out = _run_mutation("control", [], workdir)
+    finally:
+        shutil.rmtree(workdir, ignore_errors=True)
+    assert rc == 0, out
