@@ -1,0 +1,229 @@
+#!/usr/bin/env python3
+"""Benchmark of chunkwise causal linear attention on one MI355X.
+
+Headline (the JSON line's `value`): prefill throughput, token*heads per second, on
+the 128k-context decayed-retention workload -- B=1, H=64, T=131035 (ragged: the
+last chunk has 91 tokens), d=128, C=128, identity feature map, per-head
+gamma_h = 1 - 2^(-5 - 5h/63), no denominator, bf16 inputs, fp32 state and output.
+One step = one lin_attn_prefill call over that whole batch (segment summaries,
+segment scan, output pass), inputs resident in HBM before timing starts.
+
+Also reported on the same line:
+  roofline      the output kernel (the dominant one), algorithmic bytes / its
+                average duration from HIP events over the timed region;
+  decode        steps/s of lin_attn_decode_step on 32 streams x 64 heads
+                (d=128, elu+1, gamma 0.999, state from a 4096-token prefix);
+  cpu_baseline  the fp64 oracle timed on this host's cores on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from chunked_causal_linear_k1_amd import binding, inputs, workloads  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E peak
+BYTES_PER_TOKEN_HEAD = 3 * 128 * 2 + 128 * 4   # q, k, v read once (bf16) + o written once (fp32), d = 128
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def traffic_from_profiles(kernel_key: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if present and current."""
+    path = os.path.join(PROFILE_DIR, "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+        return rec.get(kernel_key)
+    except (OSError, ValueError):
+        return None
+
+
+def bench_prefill(w: workloads.Workload, steps: int, warmup: int):
+    log(f"prefill {w.name}: generating inputs on the GPU")
+    inp = inputs.make_prefill_inputs(w, device="cuda")
+    g = inp["gamma"]
+    gam = None if g is None else list(g)
+    o = torch.empty((w.B, w.H, w.T, w.d_v), dtype=torch.float32, device="cuda")
+    desc = binding.prefill_desc(w.B, w.H, w.T, w.d_k, w.d_v, w.n_psi, w.chunk, w.psi, w.normalize, w.eps,
+                                binding.LA_BF16)
+    ws = torch.empty(max(binding.workspace_size(desc), 16), dtype=torch.uint8, device="cuda")
+    kw = dict(psi=w.psi, chunk=w.chunk, normalize=w.normalize, eps=w.eps, gamma=gam, prf_w=inp["prf_w"], o=o,
+              workspace=ws)
+    for _ in range(warmup):
+        binding.lin_attn_prefill(inp["q"], inp["k"], inp["v"], **kw)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for s in range(steps):
+        binding.lin_attn_prefill(inp["q"], inp["k"], inp["v"], events=evs[s], **kw)
+    t1.record()
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    phases = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])] for e in evs])
+    ms = total_ms / steps
+    units = w.token_heads
+    res = {
+        "ms_per_step": ms,
+        "token_heads_per_s": units / (ms * 1e-3),
+        "phase_ms": {"summary": float(phases[:, 0].mean()), "scan": float(phases[:, 1].mean()),
+                     "output": float(phases[:, 2].mean())},
+        "units": units,
+    }
+    del inp, o, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_decode(w: workloads.DecodeWorkload, steps: int, warmup: int):
+    """steps consecutive decode launches, each on its own pre-generated token; state from a GPU prefill
+    of the seeded prefix (the state only sets realistic magnitudes here; parity is tested elsewhere)."""
+    log(f"decode {w.name}: building the state from a {w.prefix_len}-token prefix")
+    prefix = inputs.make_decode_prefix(w, device="cuda")
+    N, H, d = w.N, w.H, w.d_k
+    S = torch.empty((N, H, d, d), dtype=torch.float32, device="cuda")
+    Z = torch.empty((N, H, d), dtype=torch.float32, device="cuda")
+    gam = [w.gamma] * H
+    qp = torch.zeros_like(prefix["k"])
+    binding.lin_attn_prefill(qp, prefix["k"], prefix["v"], psi=w.psi, chunk=64, normalize=w.normalize, eps=w.eps,
+                             gamma=gam, final_S=S, final_Z=Z)
+    del qp, prefix
+    S0, Z0 = S.clone(), Z.clone()
+    toks = inputs.make_decode_steps(w, steps=max(steps, warmup), device="cuda")
+    o = torch.empty((N, H, d), dtype=torch.float32, device="cuda")
+    q, k, v = toks["q"], toks["k"], toks["v"]
+    for t in range(warmup):
+        binding.lin_attn_decode_step(q[t], k[t], v[t], S, Z, psi=w.psi, normalize=w.normalize, eps=w.eps,
+                                     gamma=gam, o=o)
+    S.copy_(S0)
+    Z.copy_(Z0)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for t in range(steps):
+        binding.lin_attn_decode_step(q[t], k[t], v[t], S, Z, psi=w.psi, normalize=w.normalize, eps=w.eps,
+                                     gamma=gam, o=o)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    per_step_bytes = N * H * (2 * (d * d * 4 + d * 4) + 3 * d * 2 + d * 4)
+    step_us = ms * 1e3 / steps
+    return {"steps_per_s": steps / (ms * 1e-3), "us_per_step": step_us, "bytes_per_step": per_step_bytes,
+            "achieved_GBs": per_step_bytes / (step_us * 1e-6) / 1e9,
+            "frac_of_hbm_peak": per_step_bytes / (step_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "note": "state (129 MiB) is re-read every step and can be served partly from the 256 MB "
+                    "Infinity Cache; effective rate"}
+
+
+def cpu_baseline(w: workloads.Workload, budget_s: float):
+    """The fp64 oracle on this host's cores over whole heads of the same workload, until budget_s."""
+    import oracle
+    nthreads = len(os.sched_getaffinity(0))
+    log(f"cpu baseline: fp64 oracle on {nthreads} threads, budget ~{budget_s:.0f}s")
+    inp = inputs.make_prefill_inputs(w, device="cuda")
+    gam = inp["gamma"]
+    q = inp["q"].reshape(w.B * w.H, w.T, w.d_k)
+    k = inp["k"].reshape(w.B * w.H, w.T, w.d_k)
+    v = inp["v"].reshape(w.B * w.H, w.T, w.d_v)
+    done_heads, elapsed = 0, 0.0
+    batch = max(1, min(nthreads, 16))
+    heads = list(range(w.B * w.H))
+    while done_heads < len(heads) and elapsed < budget_s:
+        sel = heads[done_heads:done_heads + batch]
+        qs, ks, vs = q[sel].cpu(), k[sel].cpu(), v[sel].cpu()
+        g = None if gam is None else [float(gam[b % w.H]) for b in sel]
+        t = time.perf_counter()
+        oracle.prefill(qs, ks, vs, w.psi, gamma=g, normalize=w.normalize, eps=float(np.float32(w.eps)),
+                       nthreads=nthreads)
+        elapsed += time.perf_counter() - t
+        done_heads += len(sel)
+    del inp, q, k, v
+    torch.cuda.empty_cache()
+    units = done_heads * w.T
+    return {"value": units / elapsed, "unit": "token*heads/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"{done_heads} of {w.B * w.H} heads x all {w.T} tokens of {w.name} (fp64 recurrence, "
+                      f"OpenMP over heads, {elapsed:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=256)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported by this build "
+              "(multi-GPU sequence/head sharding is described in the design notes, not built)", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    binding.load()
+
+    w = workloads.RETNET_128K
+    pre = bench_prefill(w, args.steps, args.warmup)
+    out_ms = pre["phase_ms"]["output"]
+    achieved = BYTES_PER_TOKEN_HEAD * pre["units"] / (out_ms * 1e-3) / 1e9
+    traffic = traffic_from_profiles("k_output_retnet_128k")
+    roofline = {"kernel": "k_output<128,128>", "bound": "hbm", "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic,
+                "whole_call_frac": round(BYTES_PER_TOKEN_HEAD * pre["units"] / (pre["ms_per_step"] * 1e-3) / 1e9
+                                         / HBM_PEAK_GBS, 4)}
+    line = {
+        "metric": "prefill tokens*heads/s at 128k (decayed retention, ragged T)",
+        "value": round(pre["token_heads_per_s"], 1),
+        "unit": "token*heads/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(pre["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "d_k": w.d_k, "d_v": w.d_v, "chunk": w.chunk,
+                   "psi": "identity", "decay": "gamma_h = 1 - 2^(-5-5h/63)", "normalize": 0,
+                   "state": "fp32", "output": "fp32"},
+        "phase_ms": {k: round(v, 4) for k, v in pre["phase_ms"].items()},
+        "roofline": roofline,
+    }
+    if not args.no_decode:
+        dw = workloads.DECODE_32x64
+        dec = bench_decode(dw, args.decode_steps, warmup=8)
+        line["decode"] = {"workload": dw.name, "steps": args.decode_steps,
+                          "steps_per_s": round(dec["steps_per_s"], 1), "us_per_step": round(dec["us_per_step"], 3),
+                          "roofline": {"bound": "hbm", "achieved": round(dec["achieved_GBs"], 1),
+                                       "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                       "frac": round(dec["frac_of_hbm_peak"], 4),
+                                       "traffic": traffic_from_profiles("k_decode_32x64")},
+                          "note": dec["note"]}
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,185 @@
+"""ctypes binding of liblinattn.so -- argument marshalling only.
+
+Every function here turns torch tensors into the pointers and sizes the C ABI
+(include/linattn.h) takes, calls it on torch's current HIP stream, and raises on
+a non-OK status. All computation happens in the library's HIP kernels; there is
+no fallback path. Device memory (outputs, workspace) comes from torch's caching
+allocator.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+from . import workloads
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblinattn.so")
+
+LA_OK, LA_ERR_NULL, LA_ERR_SHAPE, LA_ERR_UNSUPPORTED, LA_ERR_WORKSPACE, LA_ERR_ALIGN, LA_ERR_VALUE, LA_ERR_HIP = range(8)
+LA_BF16, LA_F32 = 0, 1
+MAX_DECAY_HEADS = 256
+
+EXPORTED = ("lin_attn_prefill_workspace_size", "lin_attn_prefill", "lin_attn_prefill_profiled",
+            "lin_attn_decode_step", "lin_attn_status_string", "lin_attn_version")
+
+
+class PrefillDesc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("T", ctypes.c_int32),
+                ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32), ("n_psi", ctypes.c_int32),
+                ("chunk", ctypes.c_int32), ("psi", ctypes.c_int32), ("normalize", ctypes.c_int32),
+                ("eps", ctypes.c_float), ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32)]
+
+
+class DecodeDesc(ctypes.Structure):
+    _fields_ = [("N", ctypes.c_int32), ("H", ctypes.c_int32), ("d_k", ctypes.c_int32),
+                ("d_v", ctypes.c_int32), ("n_psi", ctypes.c_int32), ("psi", ctypes.c_int32),
+                ("normalize", ctypes.c_int32), ("eps", ctypes.c_float), ("in_dtype", ctypes.c_int32),
+                ("out_dtype", ctypes.c_int32)]
+
+
+class LinAttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: status {status} ({status_string(status)})")
+        self.status = status
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load liblinattn.so; raises if it has not been built (there is no other path)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run python -m chunked_causal_linear_k1_amd.build")
+        lib = ctypes.CDLL(LIB_PATH)
+        vp, fp = ctypes.c_void_p, ctypes.POINTER(ctypes.c_float)
+        lib.lin_attn_prefill_workspace_size.restype = ctypes.c_int
+        lib.lin_attn_prefill_workspace_size.argtypes = [ctypes.POINTER(PrefillDesc), ctypes.POINTER(ctypes.c_size_t)]
+        lib.lin_attn_prefill.restype = ctypes.c_int
+        lib.lin_attn_prefill.argtypes = [ctypes.POINTER(PrefillDesc), vp, vp, vp, fp, vp, vp, vp, vp, vp, vp, vp,
+                                         ctypes.c_size_t, vp]
+        lib.lin_attn_prefill_profiled.restype = ctypes.c_int
+        lib.lin_attn_prefill_profiled.argtypes = lib.lin_attn_prefill.argtypes + [ctypes.POINTER(ctypes.c_void_p)]
+        lib.lin_attn_decode_step.restype = ctypes.c_int
+        lib.lin_attn_decode_step.argtypes = [ctypes.POINTER(DecodeDesc), vp, vp, vp, fp, vp, vp, vp, vp, vp]
+        lib.lin_attn_status_string.restype = ctypes.c_char_p
+        lib.lin_attn_status_string.argtypes = [ctypes.c_int]
+        lib.lin_attn_version.restype = ctypes.c_char_p
+        lib.lin_attn_version.argtypes = []
+        _lib = lib
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return load().lin_attn_status_string(int(status)).decode()
+
+
+def version() -> str:
+    return load().lin_attn_version().decode()
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return LA_BF16
+    if t.dtype == torch.float32:
+        return LA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _gamma_array(gamma, H: int):
+    if gamma is None:
+        return None
+    vals = [float(g) for g in gamma]
+    if len(vals) != H:
+        raise ValueError(f"gamma has {len(vals)} entries, expected H={H}")
+    return (ctypes.c_float * H)(*vals)
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def prefill_desc(B, H, T, d_k, d_v, n_psi, chunk, psi, normalize, eps, in_dtype, out_dtype=LA_F32) -> PrefillDesc:
+    return PrefillDesc(B, H, T, d_k, d_v, n_psi, chunk, psi, normalize, eps, in_dtype, out_dtype)
+
+
+def workspace_size(desc: PrefillDesc) -> int:
+    n = ctypes.c_size_t(0)
+    st = load().lin_attn_prefill_workspace_size(ctypes.byref(desc), ctypes.byref(n))
+    if st != LA_OK:
+        raise LinAttnError(st, "lin_attn_prefill_workspace_size")
+    return int(n.value)
+
+
+def lin_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, psi: int, chunk: int,
+                     normalize: int = 1, eps: float = 1e-6, gamma: Optional[Sequence[float]] = None,
+                     prf_w: Optional[torch.Tensor] = None, init_S: Optional[torch.Tensor] = None,
+                     init_Z: Optional[torch.Tensor] = None, o: Optional[torch.Tensor] = None,
+                     final_S: Optional[torch.Tensor] = None, final_Z: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None, stream=None, events=None) -> torch.Tensor:
+    """o = chunkwise causal linear attention of q, k, v [B, H, T, d] on the GPU (C ABI call).
+
+    events: optional sequence of 4 torch.cuda.Event (timing enabled) recorded at the phase
+    boundaries through lin_attn_prefill_profiled."""
+    B, H, T, d_k = q.shape
+    d_v = v.shape[-1]
+    n_psi = prf_w.shape[1] if prf_w is not None else d_k
+    for t in (q, k, v):
+        if not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous [B, H, T, d]")
+    desc = prefill_desc(B, H, T, d_k, d_v, n_psi, chunk, psi, normalize, eps, _dtype_code(q))
+    if o is None:
+        o = torch.empty((B, H, T, d_v), dtype=torch.float32, device=q.device)
+    ws_bytes = workspace_size(desc)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    g = _gamma_array(gamma, H)
+    args = [ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), g, _ptr(prf_w), _ptr(init_S), _ptr(init_Z), _ptr(o),
+            _ptr(final_S), _ptr(final_Z), _ptr(workspace),
+            0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(stream)]
+    if events is None:
+        st = load().lin_attn_prefill(*args)
+    else:
+        ev = (ctypes.c_void_p * 4)(*[e.cuda_event if e is not None else None for e in events])
+        st = load().lin_attn_prefill_profiled(*args, ev)
+    if st != LA_OK:
+        raise LinAttnError(st, "lin_attn_prefill")
+    return o
+
+
+def lin_attn_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, S: torch.Tensor,
+                         Z: Optional[torch.Tensor], *, psi: int, normalize: int = 1, eps: float = 1e-6,
+                         gamma: Optional[Sequence[float]] = None, prf_w: Optional[torch.Tensor] = None,
+                         o: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """One decode step for q, k, v [N, H, d]; S [N, H, n_psi, d_v], Z [N, H, n_psi] updated in place."""
+    N, H, d_k = q.shape
+    d_v = v.shape[-1]
+    n_psi = S.shape[-2]
+    desc = DecodeDesc(N, H, d_k, d_v, n_psi, psi, normalize, eps, _dtype_code(q), LA_F32)
+    if o is None:
+        o = torch.empty((N, H, d_v), dtype=torch.float32, device=q.device)
+    g = _gamma_array(gamma, H)
+    st = load().lin_attn_decode_step(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), g, _ptr(prf_w), _ptr(S),
+                                     _ptr(Z), _ptr(o), _stream(stream))
+    if st != LA_OK:
+        raise LinAttnError(st, "lin_attn_decode_step")
+    return o
+
+
+def prefill_workload(w: "workloads.Workload", inputs: dict, **kw) -> torch.Tensor:
+    """Run lin_attn_prefill on a named workload's inputs (see inputs.make_prefill_inputs)."""
+    g = inputs.get("gamma")
+    return lin_attn_prefill(inputs["q"], inputs["k"], inputs["v"], psi=w.psi, chunk=w.chunk,
+                            normalize=w.normalize, eps=w.eps, gamma=None if g is None else list(g),
+                            prf_w=inputs.get("prf_w"), **kw)

@@ -1,0 +1,213 @@
+// la_api.cpp -- the extern "C" boundary of liblinattn.so (declared in include/linattn.h).
+//
+// Host side only: validates every argument before anything is enqueued, plans the
+// segment decomposition, carves the caller's workspace, and launches
+//   prefill: segment summaries -> segment scan -> output walk   (three launches)
+//   decode : one launch
+// on the caller's stream. No allocation, no synchronisation, no device switch.
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "la_kernels.hpp"
+
+namespace {
+
+using la::PrefillParams;
+using la::ScanParams;
+
+constexpr int kTargetWorkgroups = 2048;  // prefill parallelism target (8 per CU on 256 CUs)
+
+bool aligned16(const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+la_status check_gamma(const float* gamma, int H) {
+  if (!gamma) return LA_OK;
+  if (H > LA_MAX_DECAY_HEADS) return LA_ERR_UNSUPPORTED;
+  for (int h = 0; h < H; ++h) {
+    const float g = gamma[h];
+    if (!(g > 0.f && g <= 1.f)) return LA_ERR_VALUE;  // also rejects NaN
+  }
+  return LA_OK;
+}
+
+// log2(gamma) evaluated in double from the fp32 value, stored as float (0 for gamma == 1).
+int fill_log2g(const float* gamma, int H, float* out) {
+  int any = 0;
+  for (int h = 0; h < LA_MAX_DECAY_HEADS; ++h) out[h] = 0.f;
+  if (!gamma) return 0;
+  for (int h = 0; h < H; ++h) {
+    out[h] = gamma[h] == 1.f ? 0.f : (float)log2((double)gamma[h]);
+    any |= gamma[h] != 1.f;
+  }
+  return any;
+}
+
+la_status validate_prefill_desc(const la_prefill_desc* d) {
+  if (!d) return LA_ERR_NULL;
+  if (d->B < 1 || d->H < 1 || d->T < 1 || d->d_k < 1 || d->d_v < 1 || d->n_psi < 1 || d->chunk < 1)
+    return LA_ERR_SHAPE;
+  if (d->psi < LA_PSI_IDENTITY || d->psi > LA_PSI_PRF) return LA_ERR_VALUE;
+  if (d->normalize != 0 && d->normalize != 1) return LA_ERR_VALUE;
+  if (!(d->eps >= 0.f) || !isfinite(d->eps)) return LA_ERR_VALUE;
+  if (d->in_dtype != LA_BF16 && d->in_dtype != LA_F32) return LA_ERR_VALUE;
+  if (d->out_dtype != LA_BF16 && d->out_dtype != LA_F32) return LA_ERR_VALUE;
+  if (d->psi != LA_PSI_PRF && d->n_psi != d->d_k) return LA_ERR_SHAPE;
+  // element counts must fit comfortably in 64-bit offsets and the grid's y extent
+  const double tokens = (double)d->B * d->H * d->T;
+  if (tokens * std::max(d->d_k, d->d_v) > 9.0e15) return LA_ERR_SHAPE;
+  if ((long long)d->B * d->H > 65535) return LA_ERR_UNSUPPORTED;
+  if (d->out_dtype != LA_F32) return LA_ERR_UNSUPPORTED;
+  const bool ok = d->in_dtype == LA_BF16
+                      ? la::prefill_bf16_supported(d->chunk, d->d_k, d->d_v, d->n_psi, d->psi)
+                      : la::prefill_f32_supported(d->chunk, d->d_k, d->d_v, d->n_psi, d->psi);
+  return ok ? LA_OK : LA_ERR_UNSUPPORTED;
+}
+
+struct Plan {
+  int n_chunks, seg_chunks, n_seg;
+  size_t ws_bytes;
+};
+
+Plan make_plan(const la_prefill_desc* d) {
+  Plan pl;
+  const long long BH = (long long)d->B * d->H;
+  pl.n_chunks = (int)((d->T + (long long)d->chunk - 1) / d->chunk);
+  long long want = (kTargetWorkgroups + BH - 1) / BH;  // segments per sequence
+  want = std::max(1LL, std::min<long long>(want, pl.n_chunks));
+  pl.seg_chunks = (int)((pl.n_chunks + want - 1) / want);
+  pl.n_seg = (pl.n_chunks + pl.seg_chunks - 1) / pl.seg_chunks;
+  const size_t E = (size_t)d->n_psi * d->d_v + d->n_psi;
+  pl.ws_bytes = (size_t)BH * pl.n_seg * E * sizeof(float);
+  return pl;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* lin_attn_status_string(la_status s) {
+  switch (s) {
+    case LA_OK: return "ok";
+    case LA_ERR_NULL: return "a required pointer is NULL";
+    case LA_ERR_SHAPE: return "a size is out of range or inconsistent";
+    case LA_ERR_UNSUPPORTED: return "combination not supported by this build";
+    case LA_ERR_WORKSPACE: return "workspace missing or too small";
+    case LA_ERR_ALIGN: return "device pointer not 16-byte aligned";
+    case LA_ERR_VALUE: return "invalid value (eps, gamma or enum)";
+    case LA_ERR_HIP: return "HIP runtime error at launch";
+  }
+  return "unknown status";
+}
+
+const char* lin_attn_version(void) { return "0.1.0"; }
+
+la_status lin_attn_prefill_workspace_size(const la_prefill_desc* d, size_t* bytes) {
+  if (!bytes) return LA_ERR_NULL;
+  const la_status st = validate_prefill_desc(d);
+  if (st != LA_OK) return st;
+  *bytes = make_plan(d).ws_bytes;
+  return LA_OK;
+}
+
+la_status lin_attn_prefill_profiled(const la_prefill_desc* d, const void* q, const void* k, const void* v,
+                                    const float* gamma, const void* prf_w, const float* init_S,
+                                    const float* init_Z, void* o, float* final_S, float* final_Z, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream, hipEvent_t* events) {
+  la_status st = validate_prefill_desc(d);
+  if (st != LA_OK) return st;
+  if (!q || !k || !v || !o) return LA_ERR_NULL;
+  if (d->psi == LA_PSI_PRF && !prf_w) return LA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(prf_w) ||
+      !aligned16(init_S) || !aligned16(init_Z) || !aligned16(final_S) || !aligned16(final_Z) ||
+      !aligned16(workspace))
+    return LA_ERR_ALIGN;
+  st = check_gamma(gamma, d->H);
+  if (st != LA_OK) return st;
+  const Plan pl = make_plan(d);
+  if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes)) return LA_ERR_WORKSPACE;
+
+  PrefillParams p;
+  memset(&p, 0, sizeof p);
+  p.q = q; p.k = k; p.v = v; p.prf_w = prf_w; p.o = o;
+  p.ws = (float*)workspace;
+  p.B = d->B; p.H = d->H; p.T = d->T;
+  p.d_k = d->d_k; p.d_v = d->d_v; p.n_psi = d->n_psi; p.C = d->chunk;
+  p.psi = d->psi; p.normalize = d->normalize; p.eps = d->eps;
+  p.n_chunks = pl.n_chunks; p.seg_chunks = pl.seg_chunks; p.n_seg = pl.n_seg;
+  p.has_decay = fill_log2g(gamma, d->H, p.log2g);
+
+  ScanParams sp;
+  memset(&sp, 0, sizeof sp);
+  sp.ws = p.ws;
+  sp.init_S = init_S; sp.final_S = final_S;
+  // without normalisation the normaliser is not maintained: init_Z / final_Z are ignored
+  sp.init_Z = d->normalize ? init_Z : nullptr;
+  sp.final_Z = d->normalize ? final_Z : nullptr;
+  sp.BH = d->B * d->H; sp.H = d->H; sp.T = d->T;
+  sp.n_psi = d->n_psi; sp.d_v = d->d_v;
+  sp.n_seg = pl.n_seg; sp.seg_len = pl.seg_chunks * d->chunk;
+  sp.has_decay = p.has_decay;
+  memcpy(sp.log2g, p.log2g, sizeof sp.log2g);
+
+  auto mark = [&](int i) -> hipError_t {
+    return (events && events[i]) ? hipEventRecord(events[i], stream) : hipSuccess;
+  };
+  const bool bf = d->in_dtype == LA_BF16;
+  hipError_t e = mark(0);
+  if (e == hipSuccess) e = bf ? la::launch_prefill_bf16_summary(p, stream) : la::launch_prefill_f32_summary(p, stream);
+  if (e == hipSuccess) e = mark(1);
+  if (e == hipSuccess) e = la::launch_segment_scan(sp, stream);
+  if (e == hipSuccess) e = mark(2);
+  if (e == hipSuccess) e = bf ? la::launch_prefill_bf16_output(p, stream) : la::launch_prefill_f32_output(p, stream);
+  if (e == hipSuccess) e = mark(3);
+  return e == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
+la_status lin_attn_prefill(const la_prefill_desc* d, const void* q, const void* k, const void* v,
+                           const float* gamma, const void* prf_w, const float* init_S, const float* init_Z,
+                           void* o, float* final_S, float* final_Z, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  return lin_attn_prefill_profiled(d, q, k, v, gamma, prf_w, init_S, init_Z, o, final_S, final_Z, workspace,
+                                   workspace_bytes, stream, nullptr);
+}
+
+la_status lin_attn_decode_step(const la_decode_desc* d, const void* q, const void* k, const void* v,
+                               const float* gamma, const void* prf_w, float* S, float* Z, void* o,
+                               hipStream_t stream) {
+  if (!d) return LA_ERR_NULL;
+  if (d->N < 1 || d->H < 1 || d->d_k < 1 || d->d_v < 1 || d->n_psi < 1) return LA_ERR_SHAPE;
+  if (d->psi < LA_PSI_IDENTITY || d->psi > LA_PSI_PRF) return LA_ERR_VALUE;
+  if (d->normalize != 0 && d->normalize != 1) return LA_ERR_VALUE;
+  if (!(d->eps >= 0.f) || !isfinite(d->eps)) return LA_ERR_VALUE;
+  if (d->in_dtype != LA_BF16 && d->in_dtype != LA_F32) return LA_ERR_VALUE;
+  if (d->out_dtype != LA_BF16 && d->out_dtype != LA_F32) return LA_ERR_VALUE;
+  if (d->psi != LA_PSI_PRF && d->n_psi != d->d_k) return LA_ERR_SHAPE;
+  if ((long long)d->N * d->H > 2147483647LL) return LA_ERR_SHAPE;
+  if (d->out_dtype != LA_F32) return LA_ERR_UNSUPPORTED;
+  if (!la::decode_supported(d->d_k, d->d_v, d->n_psi, d->psi)) return LA_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !S || !o) return LA_ERR_NULL;
+  if (d->normalize && !Z) return LA_ERR_NULL;
+  if (d->psi == LA_PSI_PRF && !prf_w) return LA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(S) || !aligned16(Z) || !aligned16(o) ||
+      !aligned16(prf_w))
+    return LA_ERR_ALIGN;
+  la_status st = check_gamma(gamma, d->H);
+  if (st != LA_OK) return st;
+
+  la::DecodeParams p;
+  memset(&p, 0, sizeof p);
+  p.q = q; p.k = k; p.v = v; p.prf_w = prf_w; p.S = S; p.Z = Z; p.o = (float*)o;
+  p.N = d->N; p.H = d->H; p.d_k = d->d_k; p.d_v = d->d_v; p.n_psi = d->n_psi;
+  p.psi = d->psi; p.normalize = d->normalize; p.eps = d->eps;
+  p.in_f32 = d->in_dtype == LA_F32;
+  if (gamma) {
+    for (int h = 0; h < d->H; ++h) {
+      p.gamma[h] = gamma[h];
+      p.has_decay |= gamma[h] != 1.f;
+    }
+  }
+  return la::launch_decode_step(p, stream) == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
+}  // extern "C"

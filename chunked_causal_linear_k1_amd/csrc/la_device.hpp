@@ -1,0 +1,111 @@
+// la_device.hpp -- device-side building blocks for gfx950 (CDNA4), wave64.
+//
+// MFMA operand layouts used throughout (v_mfma_f32_32x32x16_bf16):
+//   A (32 x 16): lane l holds row m = l%32, k = 8*(l/32) + 0..7
+//   B (16 x 32): lane l holds col n = l%32, k = 8*(l/32) + 0..7
+//   D (32 x 32): lane l holds col n = l%32, rows m = 8*(r/4) + 4*(l/32) + r%4, r = 0..15
+// A D-tile can be fed back as an operand whose k runs over the tile's rows: for
+// k-half q (rows 16q..16q+15) lane (n, h=l/32) supplies registers 8q..8q+7, i.e.
+// rows 16q + perm(h, j) with perm(h, j) = 4h + j for j < 4 and 8 + 4h + (j-4) for
+// j >= 4; the partner operand then reads its k values in that same order.
+//
+// ds_read_b64_tr_b16 (transpose read), per 16-lane group: lane L receives element
+// L%4 of the 4-element chunks addressed by lanes L/4, L/4+4, L/4+8, L/4+12. If lane
+// L' addresses X[r0 + L'/4][c0 + 4*(L'%4)], lane L receives X[r0..r0+3][c0 + L]:
+// four consecutive rows of one column, which is what an operand with k running
+// over rows needs.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace la {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+#define LA_LDS __attribute__((address_space(3)))
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// fp32 -> bf16, round to nearest even (hardware conversion on gfx950).
+__device__ __forceinline__ __bf16 to_bf16(float x) { return (__bf16)x; }
+__device__ __forceinline__ float from_bf16(__bf16 x) { return (float)x; }
+
+// x = hi + lo with hi = bf16(x), lo = bf16(x - hi): a two-term bf16 expansion whose
+// sum carries about 16 significant bits.
+struct bf16_pair {
+  __bf16 hi, lo;
+};
+__device__ __forceinline__ bf16_pair split_bf16(float x) {
+  const __bf16 hi = to_bf16(x);
+  return {hi, to_bf16(x - from_bf16(hi))};
+}
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Transpose read of four bf16 from LDS (see the header comment for the lane mapping).
+__device__ __forceinline__ bf16x4 lds_read_tr4(const __bf16* p) {
+  i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LA_LDS i16x4*)(p));
+  return __builtin_bit_cast(bf16x4, r);
+}
+
+__device__ __forceinline__ bf16x8 cat8(const bf16x4& a, const bf16x4& b) {
+  bf16x8 r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
+  r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
+  return r;
+}
+
+// Operand with k running over 8 consecutive rows of a row-major LDS tile X (pitch in
+// elements): lane (c = l%32, h = l/32) receives X[r0 + 8h + 0..7][c0 + c].
+__device__ __forceinline__ bf16x8 ld_rows8(const __bf16* X, int pitch, int r0, int c0, int lane) {
+  const int L = lane & 15, g = lane >> 4;            // 16-lane group g = 0..3
+  const int col = c0 + 16 * (g & 1) + 4 * (L & 3);
+  const int row = r0 + 8 * (g >> 1) + (L >> 2);
+  bf16x4 lo = lds_read_tr4(X + row * pitch + col);
+  bf16x4 hi = lds_read_tr4(X + (row + 4) * pitch + col);
+  return cat8(lo, hi);
+}
+
+// Same, but the 8 rows follow the D-tile feedback order of k-half q:
+// rows r0 + 16q + {4h..4h+3, 8+4h..8+4h+3}.
+__device__ __forceinline__ bf16x8 ld_rows8_perm(const __bf16* X, int pitch, int r0, int q, int c0, int lane) {
+  const int L = lane & 15, g = lane >> 4;
+  const int col = c0 + 16 * (g & 1) + 4 * (L & 3);
+  const int row = r0 + 16 * q + 4 * (g >> 1) + (L >> 2);
+  bf16x4 a = lds_read_tr4(X + row * pitch + col);
+  bf16x4 b = lds_read_tr4(X + (row + 8) * pitch + col);
+  return cat8(a, b);
+}
+
+// Operand with k running along a row: lane (m = l%32, h) receives X[r0 + m][k0 + 8h + 0..7].
+__device__ __forceinline__ bf16x8 ld_cols8(const __bf16* X, int pitch, int r0, int k0, int lane) {
+  const int m = lane & 31, h = lane >> 5;
+  return *(const bf16x8*)(X + (r0 + m) * pitch + k0 + 8 * h);
+}
+
+// Same in the D-tile feedback order of k-half q: X[r0 + m][k0 + 16q + {4h..4h+3, 8+4h..8+4h+3}].
+__device__ __forceinline__ bf16x8 ld_cols8_perm(const __bf16* X, int pitch, int r0, int k0, int q, int lane) {
+  const int m = lane & 31, h = lane >> 5;
+  const __bf16* p = X + (r0 + m) * pitch + k0 + 16 * q + 4 * h;
+  bf16x4 a = *(const bf16x4*)(p);
+  bf16x4 b = *(const bf16x4*)(p + 8);
+  return cat8(a, b);
+}
+
+// Row index (within a 32x32 D-tile) of accumulator register r in lane l.
+__device__ __forceinline__ int dtile_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
+
+// gamma^n for n >= 0 from log2(gamma) (<= 0); exactly 1 when log2g == 0.
+__device__ __forceinline__ float gpow(float log2g, float n) { return log2g == 0.f ? 1.f : exp2f(n * log2g); }
+
+__device__ __forceinline__ float elu1(float x) { return x > 0.f ? x + 1.f : __expf(x); }
+
+}  // namespace la

@@ -1,0 +1,150 @@
+// la_scan.hip -- exclusive scan of segment summaries under the decayed monoid.
+//
+// Each (batch, head) sequence has n_seg segment summaries X_s = (a_s, S_s, Z_s) in
+// the workspace, a_s = gamma^(L_s) for a segment of L_s tokens. Summaries combine
+// as (a1, X1) (+) (a2, X2) = (a1 a2, a2 X1 + X2) -- the additive monoid of
+// "Log-Depth Chunked Linear-Attention Scan" (Mathematical statement) when
+// gamma = 1, and the chunkwise decay of "Linear Attention and Retentive
+// Networks" (Retentive Networks, representation C) otherwise. The scan replaces
+// X_s with init (+) X_0 (+) ... (+) X_{s-1} and writes init (+) X_0 (+) ... as the
+// final state.
+//
+// The state elements (n_psi*d_v + n_psi per sequence) are independent, so a
+// workgroup takes 64 consecutive elements (one per lane) and spreads the segment
+// axis over W waves: each wave folds its run of segments, the W wave totals are
+// scanned with a Blelloch up-sweep/down-sweep in LDS (log2 W levels each; the
+// down-sweep combines parent-prefix (+) left-sum in that order because the monoid
+// does not commute), and each wave then rewrites its run with exclusive prefixes.
+// Every element is read twice and written once, coalesced; the order of all
+// floating-point operations is fixed, so results are deterministic.
+#include "la_device.hpp"
+#include "la_kernels.hpp"
+
+namespace la {
+namespace {
+
+constexpr int kMaxWaves = 16;
+
+__global__ __launch_bounds__(64 * kMaxWaves) void k_segment_scan(ScanParams p) {
+  __shared__ float sx[kMaxWaves][64];
+  __shared__ float sa[kMaxWaves];
+  const int W = blockDim.x >> 6;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int bh = blockIdx.y, head = bh % p.H;
+  const size_t SE = (size_t)p.n_psi * p.d_v;
+  const size_t E = SE + p.n_psi;
+  const size_t e = (size_t)blockIdx.x * 64 + lane;
+  const bool live = e < E;
+  const float lg = p.has_decay ? p.log2g[head] : 0.f;
+  float* base = p.ws + (size_t)bh * p.n_seg * E + e;
+
+  // this wave's run of segments
+  const int per = (p.n_seg + W - 1) / W;
+  const int s0 = min(w * per, p.n_seg), s1 = min(s0 + per, p.n_seg);
+
+  auto seg_decay = [&](int s) {
+    const int len = min(p.seg_len, p.T - s * p.seg_len);
+    return gpow(lg, (float)len);
+  };
+
+  // 1. fold the run: total = X_s0 (+) ... (+) X_{s1-1}
+  float tx = 0.f, ta = 1.f;
+  for (int s = s0; s < s1; ++s) {
+    const float as = seg_decay(s);
+    const float xs = live ? base[(size_t)s * E] : 0.f;
+    tx = as * tx + xs;
+    ta *= as;
+  }
+  sx[w][lane] = tx;
+  if (lane == 0) sa[w] = ta;
+  __syncthreads();
+
+  // 2. Blelloch over the W wave totals (W is a power of two)
+  for (int d = 1; d < W; d <<= 1) {  // up-sweep: node right <- left (+) right
+    const int right = (w + 1) * 2 * d - 1;
+    const bool act = right < W;
+    float nx = 0.f, na = 1.f;
+    if (act) {
+      const int left = right - d;
+      nx = sa[right] * sx[left][lane] + sx[right][lane];
+      na = sa[left] * sa[right];
+    }
+    __syncthreads();
+    if (act) {
+      sx[right][lane] = nx;
+      if (lane == 0) sa[right] = na;
+    }
+    __syncthreads();
+  }
+  if (w == W - 1) {
+    sx[W - 1][lane] = 0.f;
+    if (lane == 0) sa[W - 1] = 1.f;
+  }
+  __syncthreads();
+  for (int d = W >> 1; d >= 1; d >>= 1) {  // down-sweep
+    const int right = (w + 1) * 2 * d - 1;
+    float lx = 0.f, la_ = 1.f, px = 0.f, pa = 1.f;
+    const bool act = right < W;
+    if (act) {
+      const int left = right - d;
+      lx = sx[left][lane];
+      la_ = sa[left];
+      px = sx[right][lane];
+      pa = sa[right];
+    }
+    __syncthreads();
+    if (act) {
+      const int left = right - d;
+      sx[left][lane] = px;  // left child gets the parent's prefix
+      sx[right][lane] = la_ * px + lx;  // right child: prefix (+) left sum
+      if (lane == 0) {
+        sa[left] = pa;
+        sa[right] = pa * la_;
+      }
+    }
+    __syncthreads();
+  }
+
+  // 3. carry into this run: init (+) prefix_w
+  float cx = sx[w][lane];
+  const float ca = sa[w];
+  if (live) {
+    float init = 0.f;
+    if (e < SE) {
+      if (p.init_S) init = p.init_S[(size_t)bh * SE + e];
+    } else if (p.init_Z) {
+      init = p.init_Z[(size_t)bh * p.n_psi + (e - SE)];
+    }
+    cx = ca * init + cx;
+  }
+  // 4. rewrite the run with exclusive prefixes
+  for (int s = s0; s < s1; ++s) {
+    const float as = seg_decay(s);
+    if (live) {
+      const float xs = base[(size_t)s * E];
+      base[(size_t)s * E] = cx;
+      cx = as * cx + xs;
+    }
+  }
+  // 5. the wave holding the last segment writes the final state
+  if (live && s1 == p.n_seg && s0 < s1) {
+    if (e < SE) {
+      if (p.final_S) p.final_S[(size_t)bh * SE + e] = cx;
+    } else if (p.final_Z) {
+      p.final_Z[(size_t)bh * p.n_psi + (e - SE)] = cx;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_segment_scan(const ScanParams& p, hipStream_t s) {
+  int W = 1;
+  while (W < p.n_seg && W < kMaxWaves) W <<= 1;
+  const size_t E = (size_t)p.n_psi * p.d_v + p.n_psi;
+  dim3 grid((unsigned)((E + 63) / 64), p.BH);
+  hipLaunchKernelGGL(k_segment_scan, grid, dim3(64 * W), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace la

@@ -1,0 +1,185 @@
+/*
+ * linattn.h -- C ABI of liblinattn.so: chunkwise causal linear attention on AMD
+ * Instinct MI355X (gfx950), hand-written HIP kernels.
+ *
+ * What the library computes (per batch b, head h, in the recurrent form the
+ * prefill reproduces exactly up to rounding):
+ *
+ *   S_t = gamma_h S_{t-1} + psi(k_t) v_t^T        (n_psi x d_v, fp32)
+ *   Z_t = gamma_h Z_{t-1} + psi(k_t)              (n_psi, fp32)
+ *   o_t = psi(q_t)^T S_t / (psi(q_t) . Z_t + eps)  if normalize
+ *   o_t = psi(q_t)^T S_t                           otherwise
+ *
+ * Sources (page title, section):
+ *  - "Log-Depth Chunked Linear-Attention Scan", Mathematical statement and
+ *    Implementation notes: states S_t and Z_t summed over i <= t, chunk summaries
+ *    S_c^loc, Z_c^loc, their additive monoid, the exclusive prefix over chunks,
+ *    the three kernels (local pass, scan, output), eps in the denominator, fp32
+ *    summaries, zero contribution from padded positions.
+ *  - "Linear Attention and Retentive Networks": elu(x)+1 feature map (The
+ *    Associative Property and Linear Kernel Formulation), the recurrent dual
+ *    (The Recurrent Dual), per-head decay gamma and the decayed recurrent and
+ *    chunkwise forms (Retentive Networks, Multi-Scale Decay Formulation, B, C).
+ *  - "Linearized 2-Simplicial Attention", section 3.2 and appendix Feature
+ *    scaling: positive random features psi(x)_p = exp(w_p . x - |x|^2/2)/sqrt(m).
+ *
+ * Conventions for every entry point
+ *  - Ownership: the caller allocates and owns every buffer. The library never
+ *    allocates, frees or synchronises device memory and never changes the
+ *    current device; it only enqueues kernels on `stream`.
+ *  - Pointers marked "device" are device addresses on the current device and
+ *    must be 16-byte aligned; "host" pointers are read before the call returns.
+ *  - Layouts are dense row-major (C order) with the stated shapes.
+ *  - Errors: every argument is validated on the host before anything is
+ *    enqueued; an invalid call returns a status != LA_OK and enqueues nothing.
+ *    LA_ERR_HIP reports a launch error (hipGetLastError); faults inside a
+ *    kernel surface at the caller's next synchronisation.
+ *  - Results are deterministic: the same inputs give bitwise-identical outputs
+ *    (fixed reduction orders, no floating-point atomics).
+ *  - Functions are re-entrant and thread-safe; calls that share output or
+ *    workspace buffers must not overlap in time.
+ */
+#ifndef LINATTN_H_
+#define LINATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LA_OK = 0,
+  LA_ERR_NULL = 1,        /* a required pointer is NULL                        */
+  LA_ERR_SHAPE = 2,       /* a size is out of range or inconsistent            */
+  LA_ERR_UNSUPPORTED = 3, /* a valid combination this build has no kernel for  */
+  LA_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required        */
+  LA_ERR_ALIGN = 5,       /* a device pointer is not 16-byte aligned           */
+  LA_ERR_VALUE = 6,       /* eps < 0, gamma outside (0, 1], bad enum value     */
+  LA_ERR_HIP = 7          /* the HIP runtime reported an error at launch       */
+} la_status;
+
+/* Feature map psi. */
+typedef enum {
+  LA_PSI_IDENTITY = 0, /* psi(x) = x; requires n_psi == d_k                        */
+  LA_PSI_ELU1 = 1,     /* psi(x)_j = x_j + 1 if x_j > 0 else exp(x_j); n_psi == d_k */
+  LA_PSI_PRF = 2       /* psi(x)_p = exp(w_p . x - |x|^2/2) / sqrt(n_psi)           */
+} la_psi;
+
+typedef enum { LA_BF16 = 0, LA_F32 = 1 } la_dtype;
+
+/* Prefill (training / prompt) problem description. All fields are int32 so the
+ * struct has the same layout from C, C++ and ctypes. */
+typedef struct {
+  int32_t B, H, T;       /* batch, heads, sequence length (T >= 1, any value:
+                            the last chunk may be ragged)                        */
+  int32_t d_k, d_v;      /* key/query and value widths                           */
+  int32_t n_psi;         /* feature width: == d_k unless psi == LA_PSI_PRF       */
+  int32_t chunk;         /* chunk size C                                         */
+  int32_t psi;           /* la_psi                                               */
+  int32_t normalize;     /* 1: divide by psi(q).Z + eps; 0: numerator only       */
+  float eps;             /* >= 0; used only when normalize == 1                  */
+  int32_t in_dtype;      /* la_dtype of q, k, v and prf_w                        */
+  int32_t out_dtype;     /* la_dtype of o (LA_F32 only in this build)            */
+} la_prefill_desc;
+
+/* Supported sizes in this build (anything else: LA_ERR_UNSUPPORTED):
+ *   in_dtype LA_BF16: d_k == d_v in {64, 128}; chunk in {64, 128};
+ *                     psi identity/elu1 (n_psi == d_k), or PRF with n_psi in
+ *                     {64, 128, 256} and chunk == 64.
+ *   in_dtype LA_F32 : d_k, d_v, n_psi <= 128, chunk in {16, 32, 64}, any psi.
+ *   gamma: when given, at most LA_MAX_DECAY_HEADS heads.                        */
+#define LA_MAX_DECAY_HEADS 256
+
+/* Device workspace bytes lin_attn_prefill needs for `d` (0 is possible).
+ * Pure host function. Returns LA_OK and writes *bytes, or a validation error. */
+la_status lin_attn_prefill_workspace_size(const la_prefill_desc* d, size_t* bytes);
+
+/*
+ * Chunkwise causal linear attention over whole sequences ("Log-Depth Chunked
+ * Linear-Attention Scan", Implementation notes: a chunk-local pass that emits
+ * chunk summaries, an exclusive associative scan over them, and an output pass;
+ * with decay, the chunkwise recurrent representation of "Linear Attention and
+ * Retentive Networks", section C, whose summaries combine as
+ * (a1, S1) (+) (a2, S2) = (a1 a2, a2 S1 + S2)).
+ *
+ *   q, k      device [B, H, T, d_k] in_dtype
+ *   v         device [B, H, T, d_v] in_dtype
+ *   gamma     host   [H] fp32 per-head decay, 0 < gamma <= 1; NULL means 1
+ *   prf_w     device [H, n_psi, d_k] in_dtype (the PRF bank, one per head,
+ *             shared over the batch); required iff psi == LA_PSI_PRF
+ *   init_S    device [B, H, n_psi, d_v] fp32 state before token 1, or NULL (zero)
+ *   init_Z    device [B, H, n_psi] fp32, or NULL (zero); ignored when normalize == 0
+ *   o         device [B, H, T, d_v] out_dtype, written for every t < T
+ *   final_S   device [B, H, n_psi, d_v] fp32 state after token T, or NULL
+ *   final_Z   device [B, H, n_psi] fp32, or NULL; not written when normalize == 0
+ *             (without a denominator the normaliser is not maintained)
+ *   workspace device buffer of at least lin_attn_prefill_workspace_size bytes
+ *             (contents on entry ignored; NULL allowed when that size is 0)
+ * Outputs must not alias inputs. Asynchronous on `stream`.
+ */
+la_status lin_attn_prefill(const la_prefill_desc* d, const void* q, const void* k, const void* v,
+                           const float* gamma, const void* prf_w, const float* init_S,
+                           const float* init_Z, void* o, float* final_S, float* final_Z,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * lin_attn_prefill with phase timing for profilers and benchmarks: identical work
+ * and results, plus four events recorded on `stream` -- events[0] before the
+ * segment-summary kernel, events[1] after it, events[2] after the segment scan,
+ * events[3] after the output kernel. `events` is a host array of 4 events created
+ * by the caller on the current device; NULL entries are skipped.
+ */
+la_status lin_attn_prefill_profiled(const la_prefill_desc* d, const void* q, const void* k,
+                                    const void* v, const float* gamma, const void* prf_w,
+                                    const float* init_S, const float* init_Z, void* o,
+                                    float* final_S, float* final_Z, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream,
+                                    hipEvent_t* events);
+
+/* Batched single-token decode description: N independent streams x H heads. */
+typedef struct {
+  int32_t N, H;
+  int32_t d_k, d_v, n_psi;
+  int32_t psi;       /* la_psi */
+  int32_t normalize;
+  float eps;
+  int32_t in_dtype;  /* la_dtype of q, k, v, prf_w */
+  int32_t out_dtype; /* la_dtype of o (LA_F32 only in this build) */
+} la_decode_desc;
+
+/* Supported: in_dtype LA_BF16 or LA_F32; d_k == d_v in {64, 128}; psi identity
+ * or elu1 (n_psi == d_k), or PRF with n_psi in {64, 128, 256}.                  */
+
+/*
+ * One recurrent decode step for every (stream, head), updating the state in
+ * place ("Linear Attention and Retentive Networks", The Recurrent Dual and
+ * recurrent representation B: O(1) memory per step, no token-level cache):
+ *   S <- gamma S + psi(k) v^T;  Z <- gamma Z + psi(k);
+ *   o  = psi(q)^T S / (psi(q) . Z + eps)   (numerator only if normalize == 0)
+ * The update comes first, so o includes the new token.
+ *
+ *   q, k  device [N, H, d_k] in_dtype;  v device [N, H, d_v] in_dtype
+ *   gamma host [H] fp32 or NULL (1);  prf_w device [H, n_psi, d_k] or NULL
+ *   S     device [N, H, n_psi, d_v] fp32, read and written in place
+ *   Z     device [N, H, n_psi] fp32, in place; when normalize == 0 it is neither
+ *         read nor written and may be NULL
+ *   o     device [N, H, d_v] out_dtype
+ */
+la_status lin_attn_decode_step(const la_decode_desc* d, const void* q, const void* k, const void* v,
+                               const float* gamma, const void* prf_w, float* S, float* Z, void* o,
+                               hipStream_t stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* lin_attn_status_string(la_status s);
+
+/* Library version as "major.minor.patch". */
+const char* lin_attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LINATTN_H_ */

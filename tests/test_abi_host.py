@@ -1,0 +1,139 @@
+"""Host-side checks of liblinattn.so that need no GPU.
+
+The library must load, export every function include/linattn.h declares, and
+reject invalid arguments with the documented status codes before anything is
+enqueued (so these calls never reach the device). The workspace planner is a pure
+host function.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from chunked_causal_linear_k1_amd import binding
+from chunked_causal_linear_k1_amd.binding import (LA_BF16, LA_ERR_ALIGN, LA_ERR_NULL, LA_ERR_SHAPE,
+                                                  LA_ERR_UNSUPPORTED, LA_ERR_VALUE, LA_ERR_WORKSPACE, LA_F32, LA_OK,
+                                                  DecodeDesc, PrefillDesc)
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "linattn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(binding.LIB_PATH), reason="liblinattn.so not built")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lin_attn_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    lib = binding.load()
+    names = _declared_functions()
+    assert set(names) == set(binding.EXPORTED), names
+    for n in names:
+        assert hasattr(lib, n), f"missing export {n}"
+
+
+def test_status_strings_and_version():
+    for s in range(8):
+        msg = binding.status_string(s)
+        assert isinstance(msg, str) and msg
+    assert binding.status_string(0) == "ok"
+    assert binding.status_string(99) == "unknown status"
+    assert re.fullmatch(r"\d+\.\d+\.\d+", binding.version())
+
+
+def _desc(**kw):
+    base = dict(B=1, H=2, T=1000, d_k=128, d_v=128, n_psi=128, chunk=64, psi=1, normalize=1, eps=1e-6,
+                in_dtype=LA_BF16, out_dtype=LA_F32)
+    base.update(kw)
+    return PrefillDesc(**base)
+
+
+def _ws(desc):
+    n = ctypes.c_size_t(0)
+    st = binding.load().lin_attn_prefill_workspace_size(ctypes.byref(desc), ctypes.byref(n))
+    return st, n.value
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=0), LA_ERR_SHAPE), (dict(B=0), LA_ERR_SHAPE), (dict(H=-1), LA_ERR_SHAPE),
+    (dict(d_k=0), LA_ERR_SHAPE), (dict(chunk=0), LA_ERR_SHAPE),
+    (dict(n_psi=64), LA_ERR_SHAPE),                       # n_psi != d_k without PRF
+    (dict(psi=3), LA_ERR_VALUE), (dict(normalize=2), LA_ERR_VALUE), (dict(eps=-1.0), LA_ERR_VALUE),
+    (dict(eps=float("nan")), LA_ERR_VALUE), (dict(in_dtype=5), LA_ERR_VALUE),
+    (dict(chunk=48), LA_ERR_UNSUPPORTED), (dict(d_k=96, d_v=96, n_psi=96), LA_ERR_UNSUPPORTED),
+    (dict(out_dtype=LA_BF16), LA_ERR_UNSUPPORTED),
+    (dict(in_dtype=LA_F32, chunk=128), LA_ERR_UNSUPPORTED),
+    (dict(), LA_OK), (dict(chunk=128), LA_OK), (dict(d_k=64, d_v=64, n_psi=64), LA_OK),
+    (dict(in_dtype=LA_F32, d_k=64, d_v=64, n_psi=64, chunk=64), LA_OK),
+])
+def test_prefill_validation(kw, status):
+    st, _ = _ws(_desc(**kw))
+    assert st == status, (kw, st, binding.status_string(st))
+
+
+def test_workspace_size_planner():
+    st, n1 = _ws(_desc(T=1000))
+    assert st == LA_OK and n1 > 0
+    # one summary (n_psi*d_v + n_psi fp32) per segment per sequence
+    E = 128 * 128 + 128
+    assert n1 % (4 * E) == 0
+    st, n_big = _ws(_desc(T=131035, H=64, chunk=128, psi=0, normalize=0))
+    assert st == LA_OK and n_big % (4 * E) == 0
+    segs = n_big // (4 * E) // 64
+    assert 1 <= segs <= 1024
+    # never more segments than chunks
+    st, n_small = _ws(_desc(T=1, H=1))
+    assert st == LA_OK and n_small == 4 * E
+    assert binding.load().lin_attn_prefill_workspace_size(None, None) == LA_ERR_NULL
+
+
+def test_prefill_rejects_bad_pointers_before_launch():
+    lib = binding.load()
+    d = _desc()
+    _, ws = _ws(d)
+    fake = ctypes.c_void_p(1 << 20)            # never dereferenced: validation fails first
+    odd = ctypes.c_void_p((1 << 20) + 4)
+    call = lambda q, k, v, o, w, wb, prf=None: lib.lin_attn_prefill(ctypes.byref(d), q, k, v, None, prf, None, None,
+                                                                     o, None, None, w, wb, None)
+    assert call(None, fake, fake, fake, fake, ws) == LA_ERR_NULL
+    assert call(fake, fake, fake, None, fake, ws) == LA_ERR_NULL
+    assert call(odd, fake, fake, fake, fake, ws) == LA_ERR_ALIGN
+    assert call(fake, fake, fake, fake, None, ws) == LA_ERR_WORKSPACE
+    assert call(fake, fake, fake, fake, fake, ws - 1) == LA_ERR_WORKSPACE
+    # gamma outside (0, 1]
+    bad_gamma = (ctypes.c_float * 2)(0.5, 1.5)
+    assert lib.lin_attn_prefill(ctypes.byref(d), fake, fake, fake, bad_gamma, None, None, None, fake, None, None,
+                                fake, ws, None) == LA_ERR_VALUE
+    zero_gamma = (ctypes.c_float * 2)(0.0, 1.0)
+    assert lib.lin_attn_prefill(ctypes.byref(d), fake, fake, fake, zero_gamma, None, None, None, fake, None, None,
+                                fake, ws, None) == LA_ERR_VALUE
+    # PRF needs its bank
+    dp = _desc(psi=2, n_psi=256)
+    st, wsp = _ws(dp)
+    if st == LA_OK:
+        assert lib.lin_attn_prefill(ctypes.byref(dp), fake, fake, fake, None, None, None, None, fake, None, None,
+                                    fake, wsp, None) == LA_ERR_NULL
+
+
+def test_decode_validation():
+    lib = binding.load()
+    fake = ctypes.c_void_p(1 << 20)
+
+    def call(desc, Z=fake, prf=None, S=fake):
+        return lib.lin_attn_decode_step(ctypes.byref(desc), fake, fake, fake, None, prf, S, Z, fake, None)
+
+    ok = dict(N=32, H=64, d_k=128, d_v=128, n_psi=128, psi=1, normalize=1, eps=1e-6, in_dtype=LA_BF16,
+              out_dtype=LA_F32)
+    assert call(DecodeDesc(**dict(ok, N=0))) == LA_ERR_SHAPE
+    assert call(DecodeDesc(**dict(ok, psi=7))) == LA_ERR_VALUE
+    assert call(DecodeDesc(**dict(ok, d_k=96, d_v=96, n_psi=96))) == LA_ERR_UNSUPPORTED
+    assert call(DecodeDesc(**ok), Z=None) == LA_ERR_NULL
+    assert call(DecodeDesc(**ok), S=None) == LA_ERR_NULL
+    assert call(DecodeDesc(**dict(ok, psi=2, n_psi=256))) == LA_ERR_NULL  # PRF without bank
+    assert call(DecodeDesc(**ok), S=ctypes.c_void_p((1 << 20) + 8)) == LA_ERR_ALIGN
+    assert lib.lin_attn_decode_step(None, fake, fake, fake, None, None, fake, fake, fake, None) == LA_ERR_NULL
