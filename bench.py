@@ -67,6 +67,9 @@ def bench_prefill(w: workloads.Workload, steps: int, warmup: int):
         binding.lin_attn_prefill(inp["q"], inp["k"], inp["v"], **kw)
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    for row in evs:  # torch creates the HIP event on first record; the library re-records it
+        for e in row:
+            e.record()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -135,7 +138,10 @@ def bench_decode(w: workloads.DecodeWorkload, steps: int, warmup: int):
 def cpu_baseline(w: workloads.Workload, budget_s: float):
     """The fp64 oracle on this host's cores over whole heads of the same workload, until budget_s."""
     import oracle
+    # the host's CPU share: the affinity set, capped by OMP_NUM_THREADS when the environment sets it
     nthreads = len(os.sched_getaffinity(0))
+    if os.environ.get("OMP_NUM_THREADS", "").isdigit():
+        nthreads = max(1, min(nthreads, int(os.environ["OMP_NUM_THREADS"])))
     log(f"cpu baseline: fp64 oracle on {nthreads} threads, budget ~{budget_s:.0f}s")
     inp = inputs.make_prefill_inputs(w, device="cuda")
     gam = inp["gamma"]

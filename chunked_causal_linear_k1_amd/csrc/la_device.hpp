@@ -100,6 +100,17 @@ __device__ __forceinline__ bf16x8 ld_cols8_perm(const __bf16* X, int pitch, int 
   return cat8(a, b);
 }
 
+// Buffer resource over [p, p + bytes) (gfx9 family: raw buffer, no stride). A buffer
+// load at an offset past `bytes` returns zeros instead of touching memory, which is
+// how ragged tails are read without branches.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
 // Row index (within a 32x32 D-tile) of accumulator register r in lane l.
 __device__ __forceinline__ int dtile_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
 
