@@ -46,6 +46,25 @@ __device__ __forceinline__ bf16_pair split_bf16(float x) {
   return {hi, to_bf16(x - from_bf16(hi))};
 }
 
+// Eight fp32 values as two bf16x8 MFMA operands hi + lo, cheaply: hi keeps the top 16
+// bits of each value (truncation, exact as a bf16), the residual x - hi is exact in
+// fp32 and is rounded once to bf16. hi + lo carries about 16 significant bits.
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void split8_trunc(const float* x, bf16x8& hi, bf16x8& lo) {
+  u32x4v h, l;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const unsigned a = __float_as_uint(x[2 * k]), b = __float_as_uint(x[2 * k + 1]);
+    const float ra = x[2 * k] - __uint_as_float(a & 0xffff0000u);
+    const float rb = x[2 * k + 1] - __uint_as_float(b & 0xffff0000u);
+    h[k] = __builtin_amdgcn_perm(b, a, 0x07060302u);  // {hi16(b), hi16(a)}
+    const __bf16 la = to_bf16(ra), lb = to_bf16(rb);
+    l[k] = (unsigned)__builtin_bit_cast(unsigned short, la) | ((unsigned)__builtin_bit_cast(unsigned short, lb) << 16);
+  }
+  hi = __builtin_bit_cast(bf16x8, h);
+  lo = __builtin_bit_cast(bf16x8, l);
+}
+
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -110,6 +129,54 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
 __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
+
+// XOR-swizzled row-major tiles (no padding, pitch = D elements): the 16-byte chunk c of
+// row r is stored at chunk c ^ swz<D>(r). The pattern keeps both access kinds free of
+// LDS bank conflicts -- 16 rows read at one chunk (row operands) and 4 consecutive rows
+// read at one 32-byte pair of chunks (transpose reads).
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) return ((r & 7) << 1) | ((r >> 3) & 1);
+  else return (((r >> 1) & 3) << 1) | ((r >> 3) & 1);
+}
+template <int D>
+__device__ __forceinline__ int swz_off(int row, int col) {
+  return row * D + ((((col >> 3) ^ swz<D>(row)) << 3) | (col & 7));
+}
+// Swizzled-tile versions of the operand loaders above.
+template <int D>
+__device__ __forceinline__ bf16x8 ld_cols8_swz(const __bf16* X, int r0, int k0, int lane) {
+  const int m = lane & 31, h = lane >> 5;
+  return *(const bf16x8*)(X + swz_off<D>(r0 + m, k0 + 8 * h));
+}
+template <int D>
+__device__ __forceinline__ bf16x8 ld_rows8_swz(const __bf16* X, int r0, int c0, int lane) {
+  const int L = lane & 15, g = lane >> 4;
+  const int col = c0 + 16 * (g & 1) + 4 * (L & 3);
+  const int row = r0 + 8 * (g >> 1) + (L >> 2);
+  bf16x4 lo = lds_read_tr4(X + swz_off<D>(row, col));
+  bf16x4 hi = lds_read_tr4(X + swz_off<D>(row + 4, col));
+  return cat8(lo, hi);
+}
+
+// Workgroup barrier for LDS hand-offs only. __syncthreads() also orders global memory,
+// which makes every wave wait for all of its outstanding global loads and stores
+// (s_waitcnt vmcnt(0)) -- including the next chunk's prefetched tiles and this chunk's
+// output stores, which would serialise memory traffic with the matrix work. Here each
+// wave only waits for its own LDS operations (lgkmcnt(0); vmcnt and expcnt left at
+// their maxima) before the hardware barrier; the empty asm statements keep the
+// compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Wait for every outstanding vector-memory access of this wave (vmcnt 0; lgkmcnt and
+// expcnt left at their maxima). Used where a loop is entered with loads in flight, so the
+// wait the compiler inserts at the loop header only has to cover the loop's own accesses.
+__device__ __forceinline__ void vm_drain() { __builtin_amdgcn_s_waitcnt(0x0f70); }
 
 // Row index (within a 32x32 D-tile) of accumulator register r in lane l.
 __device__ __forceinline__ int dtile_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }

@@ -5,7 +5,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include "../../include/linattn.h"
+#include "linattn.h"
 
 namespace la {
 

@@ -182,37 +182,29 @@ __device__ __forceinline__ void state_mfma(f32x16 (&S)[D / 32], const __bf16* sK
 }
 
 // One score tile A^T[i-tile it][j-tile jt] (M = i, N = j, k = feature) with the causal
-// mask (DIAG) and decay D_ji = gamma^(j-i); adds its row sums to rsum and A V to num.
-// qk holds the j-tile's Q operands (k = feature); lane column j = 32 jt + n, register
-// row i = 32 it + dtile_row(r).
-template <int C, int D, bool DECAY, bool NORM, bool DIAG>
+// mask and decay D_ji = gamma^(j-i); adds its row sums to rsum and A V to num. qk holds
+// the j-tile's Q operands (k = feature). fac[r] is this lane's factor for register r:
+// for the diagonal tile gamma^(n - i_r) masked to i_r <= n, for the others
+// gamma^(n + 32 - i_r) * gamma^(32 (jt - it - 1)) (lane column j = 32 jt + n, register
+// row i = 32 it + i_r).
+template <int C, int D, bool NORM>
 __device__ __forceinline__ void score_tile(int it, int jt, const bf16x8 (&qk)[D / 16], const __bf16* sK,
-                                           const __bf16* sV, f32x16& num, float& rsum, float lg, int Ew,
-                                           int lane) {
+                                           const __bf16* sV, f32x16& num, float& rsum, const float (&fac)[16],
+                                           float tf, int Ew, int lane) {
   constexpr int PK = Geo<C, D, true>::PK;
-  const int n = lane & 31;
   f32x16 acc = f32x16{};
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) acc = mfma32(ld_cols8(sK, PK, it * 32, kk * 16, lane), qk[kk], acc);
+  float a[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    const int ir = dtile_row(r, lane);
-    if (DIAG) {
-      acc[r] = ir <= n ? (DECAY ? acc[r] * exp2f((float)(n - ir) * lg) : acc[r]) : 0.f;
-    } else if (DECAY) {
-      acc[r] *= exp2f((float)(32 * (jt - it) + n - ir) * lg);
-    }
-    if (NORM) rsum += acc[r];
+    a[r] = acc[r] * (fac[r] * tf);
+    if (NORM) rsum += a[r];
   }
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     bf16x8 ah, al;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const bf16_pair sp = split_bf16(acc[8 * q + j]);
-      ah[j] = sp.hi;
-      al[j] = sp.lo;
-    }
+    split8_trunc(a + 8 * q, ah, al);
     const bf16x8 vv = ld_rows8_perm(sV, PK, it * 32, q, Ew, lane);
     num = mfma32(ah, vv, num);
     num = mfma32(al, vv, num);
@@ -249,7 +241,7 @@ __global__ __launch_bounds__(2 * D) void k_summary(PrefillParams p) {
   for (int c = c0; c < c1; ++c) {
     const int L = min(C, p.T - c * C);
     const float a = DECAY ? exp2f((float)L * lg) : 1.f;
-    __syncthreads();  // the previous chunk is done with LDS
+    lds_barrier();  // the previous chunk is done with LDS
     float zp[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) zp[j] = 0.f;
@@ -262,7 +254,7 @@ __global__ __launch_bounds__(2 * D) void k_summary(PrefillParams p) {
       load_pieces<C, D>(pk, kb + (size_t)(c + 1) * C * D, Ln);
       load_pieces<C, D>(pv, vb + (size_t)(c + 1) * C * D, Ln);
     }
-    __syncthreads();
+    lds_barrier();
     if (DECAY) {
 #pragma unroll
       for (int pt = 0; pt < D / 32; ++pt) S[pt] *= a;
@@ -278,9 +270,9 @@ __global__ __launch_bounds__(2 * D) void k_summary(PrefillParams p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) out[(size_t)(pt * 32 + dtile_row(r, lane)) * D + Ew + n] = S[pt][r];
   if (NORM) {
-    __syncthreads();
+    lds_barrier();
     reduce_zp<D>(zrun, sF + G::F_ZRED);
-    __syncthreads();
+    lds_barrier();
     if (tid < D) {
       float z = 0.f;
 #pragma unroll
@@ -319,6 +311,16 @@ __global__ __launch_bounds__(2 * D) void k_output(PrefillParams p) {
   if (tid < D) sF[G::F_Z + tid] = NORM ? pre[(size_t)D * D + tid] : 0.f;
   for (int j = tid; j < C; j += G::NT) sF[G::F_THETA + j] = DECAY ? exp2f((float)(j + 1) * lg) : 1.f;
 
+  // this lane's score-tile factors (its column j%32 = n and register rows are fixed):
+  // diagonal tile gamma^(n - i_r) masked to i_r <= n; off-diagonal base gamma^(n + 32 - i_r)
+  float fdiag[16], foff[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int ir = dtile_row(r, lane);
+    fdiag[r] = ir <= n ? (DECAY ? exp2f((float)(n - ir) * lg) : 1.f) : 0.f;
+    foff[r] = DECAY ? exp2f((float)(n + 32 - ir) * lg) : 1.f;
+  }
+
   const uint16_t* qb = (const uint16_t*)p.q + (size_t)bh * p.T * D;
   const uint16_t* kb = (const uint16_t*)p.k + (size_t)bh * p.T * D;
   const uint16_t* vb = (const uint16_t*)p.v + (size_t)bh * p.T * D;
@@ -331,11 +333,12 @@ __global__ __launch_bounds__(2 * D) void k_output(PrefillParams p) {
     load_pieces<C, D>(pq, qb + (size_t)c0 * C * D, L0);
     load_pieces<C, D>(pk, kb + (size_t)c0 * C * D, L0);
     load_pieces<C, D>(pv, vb + (size_t)c0 * C * D, L0);
+    vm_drain();  // entering the loop with nothing in flight, see the prefetch below
   }
   for (int c = c0; c < c1; ++c) {
     const int t0 = c * C, L = min(C, p.T - t0);
     const float a = DECAY ? exp2f((float)L * lg) : 1.f;
-    __syncthreads();  // the previous chunk is done with LDS (and Z is updated)
+    lds_barrier();  // the previous chunk is done with LDS (and Z is updated)
     float zp[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) zp[j] = 0.f;
@@ -348,29 +351,34 @@ __global__ __launch_bounds__(2 * D) void k_output(PrefillParams p) {
     // Ln, including every row when there is no next chunk, read as zeros)
     load_pieces<C, D>(pk, kb + (size_t)(c + 1) * C * D, Ln);
     load_pieces<C, D>(pv, vb + (size_t)(c + 1) * C * D, Ln);
-    __syncthreads();
+    lds_barrier();
     // stores of this chunk's outputs: rows past L are dropped by the buffer bound
     const __amdgpu_buffer_rsrc_t ors = make_rsrc(ob + (size_t)t0 * D, (uint32_t)L * D * 4);
 
+    // S as the B operand of psi(Q) S: straight from its accumulator layout (D-tile
+    // feedback order), split once per chunk into hi + lo
+    bf16x8 sh[D / 32][2], sl[D / 32][2];
+#pragma unroll
+    for (int pt = 0; pt < D / 32; ++pt)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        float x[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = S[pt][8 * q + j];
+        split8_trunc(x, sh[pt][q], sl[pt][q]);
+      }
+
 #pragma unroll 1
     for (int jt = 0; jt < NJ; ++jt) {
-      // num = gamma^(j+1) psi(q_j) S_prev   (M = j, N = e, k = state row p); S enters as
-      // the B operand straight from its accumulator layout (D-tile feedback order), hi + lo
+      // num = gamma^(j+1) psi(q_j) S_prev   (M = j, N = e, k = state row p)
       f32x16 num = f32x16{};
 #pragma unroll
       for (int pt = 0; pt < D / 32; ++pt)
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-          bf16x8 sh, sl;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const bf16_pair sp = split_bf16(S[pt][8 * q + j]);
-            sh[j] = sp.hi;
-            sl[j] = sp.lo;
-          }
           const bf16x8 qa = ld_cols8_perm(sQ, G::PQ, jt * 32, pt * 32, q, lane);
-          num = mfma32(qa, sh, num);
-          num = mfma32(qa, sl, num);
+          num = mfma32(qa, sh[pt][q], num);
+          num = mfma32(qa, sl[pt][q], num);
         }
       if (DECAY) {
 #pragma unroll
@@ -395,12 +403,14 @@ __global__ __launch_bounds__(2 * D) void k_output(PrefillParams p) {
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) qk[kk] = ld_cols8(sQ, G::PQ, jt * 32, kk * 16, lane);
       // scores A^T (M = i, N = j, k = feature), masked and decayed; then num += A V.
-      // Off-diagonal tiles (it < jt) first, in a loop whose body is one basic block; the
-      // diagonal tile (causal mask) last.
+      // Off-diagonal tiles (it < jt) first, then the diagonal tile (causal mask).
       float rsum = 0.f;
 #pragma unroll 1
-      for (int it = 0; it < jt; ++it) score_tile<C, D, DECAY, NORM, false>(it, jt, qk, sK, sV, num, rsum, lg, Ew, lane);
-      score_tile<C, D, DECAY, NORM, true>(jt, jt, qk, sK, sV, num, rsum, lg, Ew, lane);
+      for (int it = 0; it < jt; ++it) {
+        const float tf = DECAY ? exp2f((float)(32 * (jt - it - 1)) * lg) : 1.f;
+        score_tile<C, D, NORM>(it, jt, qk, sK, sV, num, rsum, foff, tf, Ew, lane);
+      }
+      score_tile<C, D, NORM>(jt, jt, qk, sK, sV, num, rsum, fdiag, 1.f, Ew, lane);
       // o_j = num_j / den_j; den_j is formed in lane j%32 and fetched by the lanes holding row j
       float den = 1.f;
       if (NORM) den = sF[G::F_THETA + jt * 32 + n] * qz + (rsum + __shfl_xor(rsum, 32)) + p.eps;
@@ -417,7 +427,7 @@ __global__ __launch_bounds__(2 * D) void k_output(PrefillParams p) {
     // state update: K~ = Xi psi(K) as hi + lo, S <- gamma^L S + K~^T V, Z <- gamma^L Z + K~^T 1
     if (NORM) reduce_zp<D>(zp, sF + G::F_ZRED);
     if (DECAY) {
-      __syncthreads();  // every wave is done reading psi(K) for scores
+      lds_barrier();  // every wave is done reading psi(K) for scores
 #pragma unroll
       for (int i = 0; i < G::NPC; ++i) {
         const int row = piece_row<C, D>(i), c8 = piece_cols<C, D>(i);
@@ -436,7 +446,7 @@ __global__ __launch_bounds__(2 * D) void k_output(PrefillParams p) {
         *(bf16x8*)(sKlo + row * G::PK + c8) = lo;
       }
     }
-    __syncthreads();
+    lds_barrier();
     if (NORM && tid < D) {
       float z = 0.f;
 #pragma unroll
@@ -451,10 +461,347 @@ __global__ __launch_bounds__(2 * D) void k_output(PrefillParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// Output kernel with the score tiles computed once per workgroup.
+//
+// Each wave produces a share of the C/32 x (C/32 + 1)/2 score tiles A^T (masked, decayed,
+// split into bf16 hi + lo) and writes them to LDS; after a barrier every wave reads the
+// tiles it needs as MFMA operands for its value columns. Compared with every wave
+// computing every tile, this removes 3/4 of the score MFMAs and of the score epilogue
+// (mask, decay, split). For identity psi the score tiles share LDS with the K~ lo tile,
+// which is only needed afterwards, in the state update.
+template <int C, int D, bool ELU>
+struct ShGeo {
+  static constexpr int NW = D / 32;
+  static constexpr int NJ = C / 32;
+  static constexpr int NTILE = NJ * (NJ + 1) / 2;
+  static constexpr int PQ = D + 8;          // Q: row reads
+  static constexpr int PK = D;              // K (and K lo): XOR-swizzled, see swz_off
+  static constexpr int PV = D + 16;         // V: transpose reads
+  static constexpr int PA = 40;             // score tiles: 32 x 32, row pitch 40
+  static constexpr int A_TILE = 2 * 32 * PA * 2;  // hi + lo, bytes
+  static constexpr int Q_BYTES = C * PQ * 2;
+  static constexpr int K_BYTES = C * PK * 2;
+  static constexpr int V_BYTES = C * PV * 2;
+  static constexpr int A_BYTES = NTILE * A_TILE;
+  static constexpr int OFF_Q = 0;
+  static constexpr int OFF_K = Q_BYTES;
+  static constexpr int OFF_V = OFF_K + K_BYTES;
+  static constexpr int OFF_KLO = OFF_V + V_BYTES;  // psi(k) lo (elu+1) or K~ lo (decay)
+  static constexpr int OFF_A = ELU ? OFF_KLO + K_BYTES : OFF_KLO;  // aliases K lo for identity psi
+  static constexpr int X_END = ELU ? OFF_A + A_BYTES : OFF_KLO + (A_BYTES > K_BYTES ? A_BYTES : K_BYTES);
+  static constexpr int OFF_F = X_END;
+  static constexpr int F_Z = 0;               // Z [D]
+  static constexpr int F_ZRED = D;            // per-wave Z partials [NW][D]
+  static constexpr int F_THETA = D + NW * D;  // gamma^(j+1) [C]
+  static constexpr int F_R = F_THETA + C;     // per-tile score row sums [NTILE][32]
+  static constexpr int LDS_BYTES = OFF_F + 4 * (F_R + NTILE * 32);
+  static constexpr bool FITS = LDS_BYTES <= 160 * 1024;
+};
+
+// tile t <-> (it, jt) with it <= jt, t = jt (jt + 1) / 2 + it
+__device__ __forceinline__ int tile_jt(int t) {
+  int jt = 0;
+  while ((jt + 1) * (jt + 2) / 2 <= t) ++jt;
+  return jt;
+}
+
+// S[pt] += K~^T V over the chunk, K~ = hi (+ lo) in LDS with pitch PK, V with pitch PV.
+template <int C, int D, bool SPLIT, int PK, int PV>
+__device__ __forceinline__ void state_mfma_p(f32x16 (&S)[D / 32], const __bf16* sK, const __bf16* sKlo,
+                                             const __bf16* sV, int Ew, int lane) {
+#pragma unroll 2
+  for (int ik = 0; ik < C / 16; ++ik) {
+    const bf16x8 vb = ld_rows8(sV, PV, ik * 16, Ew, lane);
+#pragma unroll
+    for (int pt = 0; pt < D / 32; ++pt) {
+      S[pt] = mfma32(ld_rows8(sK, PK, ik * 16, pt * 32, lane), vb, S[pt]);
+      if (SPLIT) S[pt] = mfma32(ld_rows8(sKlo, PK, ik * 16, pt * 32, lane), vb, S[pt]);
+    }
+  }
+}
+
+// S[pt] += K~^T V over the chunk, K~ = hi (+ lo) in swizzled LDS tiles, V with pitch PV.
+template <int C, int D, bool SPLIT, int PV>
+__device__ __forceinline__ void state_mfma_swz(f32x16 (&S)[D / 32], const __bf16* sK, const __bf16* sKlo,
+                                               const __bf16* sV, int Ew, int lane) {
+#pragma unroll 2
+  for (int ik = 0; ik < C / 16; ++ik) {
+    const bf16x8 vb = ld_rows8(sV, PV, ik * 16, Ew, lane);
+#pragma unroll
+    for (int pt = 0; pt < D / 32; ++pt) {
+      S[pt] = mfma32(ld_rows8_swz<D>(sK, ik * 16, pt * 32, lane), vb, S[pt]);
+      if (SPLIT) S[pt] = mfma32(ld_rows8_swz<D>(sKlo, ik * 16, pt * 32, lane), vb, S[pt]);
+    }
+  }
+}
+
+// K into swizzled LDS: identity psi stores the raw keys (rows past T are zero from the
+// bounded load); elu+1 stores psi(k) as hi + lo. zp += Xi_i psi(k_i) when NORM.
+template <int C, int D, bool ELU, bool DECAY, bool NORM>
+__device__ __forceinline__ void commit_k_swz(const Pieces<C, D>& P, __bf16* sK, __bf16* sKlo, int L, float lg,
+                                             float (&zp)[8]) {
+#pragma unroll
+  for (int i = 0; i < Geo<C, D, true>::NPC; ++i) {
+    const int row = piece_row<C, D>(i), c8 = piece_cols<C, D>(i);
+    const int off = swz_off<D>(row, c8);
+    if (!ELU && !NORM) {
+      *(uint4*)(sK + off) = P.r[i];
+      continue;
+    }
+    const float live = row < L ? 1.f : 0.f;
+    const float xi = DECAY ? live * exp2f((float)(L - 1 - row) * lg) : live;
+    const bf16x8 x = __builtin_bit_cast(bf16x8, P.r[i]);
+    float f[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      f[j] = ELU ? elu1(from_bf16(x[j])) * live : from_bf16(x[j]);
+      if (NORM) zp[j] += f[j] * xi;
+    }
+    if (ELU) {
+      bf16x8 hi, lo;
+      split8_trunc(f, hi, lo);
+      *(bf16x8*)(sK + off) = hi;
+      *(bf16x8*)(sKlo + off) = lo;
+    } else {
+      *(uint4*)(sK + off) = P.r[i];
+    }
+  }
+}
+
+template <int C, int D, bool DECAY, bool NORM, bool ELU>
+__global__ __launch_bounds__(2 * D) void k_output_sh(PrefillParams p) {
+  using G = ShGeo<C, D, ELU>;
+  static_assert(G::FITS, "LDS budget");
+  constexpr bool SPLIT = DECAY || ELU;
+  constexpr int NJ = G::NJ, NW = G::NW;
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int seg = blockIdx.x, bh = blockIdx.y, head = bh % p.H;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, n = lane & 31, hh = lane >> 5;
+  const int Ew = 32 * w;
+  const float lg = DECAY ? p.log2g[head] : 0.f;
+  __bf16* sQ = (__bf16*)(smem + G::OFF_Q);
+  __bf16* sK = (__bf16*)(smem + G::OFF_K);
+  __bf16* sV = (__bf16*)(smem + G::OFF_V);
+  __bf16* sKlo = (__bf16*)(smem + G::OFF_KLO);
+  __bf16* sA = (__bf16*)(smem + G::OFF_A);
+  float* sF = (float*)(smem + G::OFF_F);
+
+  // exclusive prefix state of this segment (written by the scan)
+  const size_t E = (size_t)D * D + D;
+  const float* pre = p.ws + ((size_t)bh * p.n_seg + seg) * E;
+  f32x16 S[D / 32];
+#pragma unroll
+  for (int pt = 0; pt < D / 32; ++pt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) S[pt][r] = pre[(size_t)(pt * 32 + dtile_row(r, lane)) * D + Ew + n];
+  if (tid < D) sF[G::F_Z + tid] = NORM ? pre[(size_t)D * D + tid] : 0.f;
+  for (int j = tid; j < C; j += 2 * D) sF[G::F_THETA + j] = DECAY ? exp2f((float)(j + 1) * lg) : 1.f;
+
+  // this lane's score-tile factors (column j%32 = n and register rows fixed):
+  // diagonal tile gamma^(n - i_r) masked to i_r <= n; off-diagonal base gamma^(n + 32 - i_r)
+  float fdiag[16], foff[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int ir = dtile_row(r, lane);
+    fdiag[r] = ir <= n ? (DECAY ? exp2f((float)(n - ir) * lg) : 1.f) : 0.f;
+    foff[r] = DECAY ? exp2f((float)(n + 32 - ir) * lg) : 1.f;
+  }
+
+  const uint16_t* qb = (const uint16_t*)p.q + (size_t)bh * p.T * D;
+  const uint16_t* kb = (const uint16_t*)p.k + (size_t)bh * p.T * D;
+  const uint16_t* vb = (const uint16_t*)p.v + (size_t)bh * p.T * D;
+  float* ob = (float*)p.o + (size_t)bh * p.T * D;
+  const int c0 = seg * p.seg_chunks, c1 = min(c0 + p.seg_chunks, p.n_chunks);
+
+  Pieces<C, D> pq, pk, pv;
+  {
+    const int L0 = min(C, p.T - c0 * C);
+    load_pieces<C, D>(pq, qb + (size_t)c0 * C * D, L0);
+    load_pieces<C, D>(pk, kb + (size_t)c0 * C * D, L0);
+    load_pieces<C, D>(pv, vb + (size_t)c0 * C * D, L0);
+    vm_drain();  // entering the loop with nothing in flight, see the prefetch below
+  }
+  for (int c = c0; c < c1; ++c) {
+    const int t0 = c * C, L = min(C, p.T - t0);
+    const float a = DECAY ? exp2f((float)L * lg) : 1.f;
+    lds_barrier();  // the previous chunk is done with LDS (and Z is updated)
+    float zp[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) zp[j] = 0.f;
+    commit_q<C, D, ELU>(pq, sQ, G::PQ);
+    commit_k_swz<C, D, ELU, DECAY, NORM>(pk, sK, sKlo, L, lg, zp);
+    commit_v<C, D>(pv, sV, G::PV);
+    const bool more = c + 1 < c1;
+    const int Ln = more ? min(C, p.T - (c + 1) * C) : 0;
+    // next chunk's tiles stream in during this chunk's matrix work (rows past Ln read as
+    // zero). All three are issued before this chunk's output stores: the vmcnt wait at the
+    // next commit then covers only these loads, not the stores.
+    load_pieces<C, D>(pq, qb + (size_t)(c + 1) * C * D, Ln);
+    load_pieces<C, D>(pk, kb + (size_t)(c + 1) * C * D, Ln);
+    load_pieces<C, D>(pv, vb + (size_t)(c + 1) * C * D, Ln);
+    lds_barrier();
+
+    // ---- score tiles, shared: wave w computes tiles w, w + NW, ...
+    for (int t = w; t < G::NTILE; t += NW) {
+      const int jt = tile_jt(t), it = t - jt * (jt + 1) / 2;
+      f32x16 acc = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk)
+        acc = mfma32(ld_cols8_swz<D>(sK, it * 32, kk * 16, lane), ld_cols8(sQ, G::PQ, jt * 32, kk * 16, lane), acc);
+      const bool diag = it == jt;
+      const float tf = (DECAY && !diag) ? exp2f((float)(32 * (jt - it - 1)) * lg) : 1.f;
+      float av[16];
+      float rs = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        av[r] = acc[r] * ((diag ? fdiag[r] : foff[r]) * tf);
+        if (NORM) rs += av[r];
+      }
+      if (NORM) {
+        rs += __shfl_xor(rs, 32);
+        if (hh == 0) sF[G::F_R + t * 32 + n] = rs;
+      }
+      // A[j = n][i = 8 q4 + 4 hh + 0..3] as 8-byte runs, hi and lo
+      __bf16* ahi = sA + t * (2 * 32 * G::PA);
+      __bf16* alo = ahi + 32 * G::PA;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        bf16x8 h8, l8;
+        split8_trunc(av + 8 * q, h8, l8);
+        const u32x4 hv = __builtin_bit_cast(u32x4, h8), lv = __builtin_bit_cast(u32x4, l8);
+        // registers 8q..8q+3 -> cols 16q + 4hh + 0..3; 8q+4..8q+7 -> cols 16q + 8 + 4hh + 0..3
+        *(uint2*)(ahi + n * G::PA + 16 * q + 4 * hh) = make_uint2(hv[0], hv[1]);
+        *(uint2*)(ahi + n * G::PA + 16 * q + 8 + 4 * hh) = make_uint2(hv[2], hv[3]);
+        *(uint2*)(alo + n * G::PA + 16 * q + 4 * hh) = make_uint2(lv[0], lv[1]);
+        *(uint2*)(alo + n * G::PA + 16 * q + 8 + 4 * hh) = make_uint2(lv[2], lv[3]);
+      }
+    }
+    lds_barrier();
+
+    // ---- outputs for this wave's value columns, computed transposed: numT[e][j] (M = value
+    // column e, N = token j), so each lane ends up with 4 consecutive columns of one token
+    // row (16-byte stores) and the per-token factors are lane scalars.
+    const __amdgpu_buffer_rsrc_t ors = make_rsrc(ob + (size_t)t0 * D, (uint32_t)L * D * 4);
+    bf16x8 sh[D / 32][2], sl[D / 32][2];
+#pragma unroll
+    for (int pt = 0; pt < D / 32; ++pt)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        float x[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = S[pt][8 * q + j];
+        split8_trunc(x, sh[pt][q], sl[pt][q]);
+      }
+    // unrolled so the store count per chunk is static: the wait for the prefetched tiles
+    // at the next commit then leaves this chunk's output stores in flight
+#pragma unroll
+    for (int jt = 0; jt < NJ; ++jt) {
+      // numT = S_prev^T psi(Q)^T   (k = state row p; S straight from its accumulator layout)
+      f32x16 num = f32x16{};
+#pragma unroll
+      for (int pt = 0; pt < D / 32; ++pt)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const bf16x8 qa = ld_cols8_perm(sQ, G::PQ, jt * 32, pt * 32, q, lane);
+          num = mfma32(sh[pt][q], qa, num);
+          num = mfma32(sl[pt][q], qa, num);
+        }
+      if (DECAY) num *= sF[G::F_THETA + jt * 32 + n];  // gamma^(j+1), j = this lane's token
+      // numT += V^T A^T for it <= jt   (k = token i; A from LDS)
+#pragma unroll 1
+      for (int it = 0; it <= jt; ++it) {
+        const __bf16* ahi = sA + (jt * (jt + 1) / 2 + it) * (2 * 32 * G::PA);
+        const __bf16* alo = ahi + 32 * G::PA;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const bf16x8 vv = ld_rows8(sV, G::PV, it * 32 + 16 * q, Ew, lane);
+          num = mfma32(vv, ld_cols8(ahi, G::PA, 0, 16 * q, lane), num);
+          num = mfma32(vv, ld_cols8(alo, G::PA, 0, 16 * q, lane), num);
+        }
+      }
+      float inv = 1.f;
+      if (NORM) {
+        // psi(q_j) . Z_prev and the score row sums for j = jt*32 + n
+        float qz = 0.f;
+        const __bf16* qr = sQ + (jt * 32 + n) * G::PQ + hh * (D / 2);
+        const f32x4* zr = (const f32x4*)(sF + G::F_Z + hh * (D / 2));
+#pragma unroll
+        for (int e8 = 0; e8 < D / 2; e8 += 8) {
+          const bf16x8 qv = *(const bf16x8*)(qr + e8);
+          const f32x4 z0 = zr[e8 / 4], z1 = zr[e8 / 4 + 1];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) qz += from_bf16(qv[j]) * z0[j] + from_bf16(qv[4 + j]) * z1[j];
+        }
+        qz += __shfl_xor(qz, 32);
+        float r = 0.f;
+        for (int it = 0; it <= jt; ++it) r += sF[G::F_R + (jt * (jt + 1) / 2 + it) * 32 + n];
+        inv = 1.f / (sF[G::F_THETA + jt * 32 + n] * qz + r + p.eps);
+      }
+      // registers 4 q4 .. 4 q4 + 3 hold columns Ew + 8 q4 + 4 hh + 0..3 of token row j
+      const uint32_t row_off = (uint32_t)((jt * 32 + n) * D + Ew + 4 * hh) * 4;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const u32x4 v4 = {__float_as_uint(num[4 * q4] * inv), __float_as_uint(num[4 * q4 + 1] * inv),
+                          __float_as_uint(num[4 * q4 + 2] * inv), __float_as_uint(num[4 * q4 + 3] * inv)};
+        __builtin_amdgcn_raw_buffer_store_b128(v4, ors, row_off + 32 * q4, 0, 0);
+      }
+    }
+
+    // state update: K~ = Xi psi(K) as hi + lo, S <- gamma^L S + K~^T V, Z <- gamma^L Z + K~^T 1
+    if (NORM) reduce_zp<D>(zp, sF + G::F_ZRED);
+    if (DECAY) {
+      lds_barrier();  // every wave is done with the score tiles (K lo aliases them) and K
+#pragma unroll
+      for (int i = 0; i < Geo<C, D, true>::NPC; ++i) {
+        const int row = piece_row<C, D>(i), c8 = piece_cols<C, D>(i);
+        const float xi = row < L ? exp2f((float)(L - 1 - row) * lg) : 0.f;
+        const int off = swz_off<D>(row, c8);
+        const bf16x8 h8 = *(const bf16x8*)(sK + off);
+        float x[8];
+        if (ELU) {
+          const bf16x8 l8 = *(const bf16x8*)(sKlo + off);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) x[j] = (from_bf16(h8[j]) + from_bf16(l8[j])) * xi;
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) x[j] = from_bf16(h8[j]) * xi;
+        }
+        bf16x8 hi, lo;
+        split8_trunc(x, hi, lo);
+        *(bf16x8*)(sK + off) = hi;
+        *(bf16x8*)(sKlo + off) = lo;
+      }
+    }
+    lds_barrier();
+    if (NORM && tid < D) {
+      float z = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) z += sF[G::F_ZRED + ww * D + tid];
+      sF[G::F_Z + tid] = a * sF[G::F_Z + tid] + z;
+    }
+    if (DECAY) {
+#pragma unroll
+      for (int pt = 0; pt < D / 32; ++pt) S[pt] *= a;
+    }
+    state_mfma_swz<C, D, SPLIT, G::PV>(S, sK, sKlo, sV, Ew, lane);
+  }
+}
+
 template <int C, int D, bool DECAY, bool NORM, bool ELU>
 hipError_t launch_flags(const PrefillParams& p, hipStream_t s, bool out) {
-  const void* kern = out ? (const void*)k_output<C, D, DECAY, NORM, ELU> : (const void*)k_summary<C, D, DECAY, NORM, ELU>;
-  const int lds = out ? Geo<C, D, true>::LDS_BYTES : Geo<C, D, false>::LDS_BYTES;
+  const void* kern = (const void*)k_summary<C, D, DECAY, NORM, ELU>;
+  int lds = Geo<C, D, false>::LDS_BYTES;
+  if (out) {
+    // the shared-score kernel where its LDS fits, else every wave computes its own scores
+    if constexpr (ShGeo<C, D, ELU>::FITS) {
+      kern = (const void*)k_output_sh<C, D, DECAY, NORM, ELU>;
+      lds = ShGeo<C, D, ELU>::LDS_BYTES;
+    } else {
+      kern = (const void*)k_output<C, D, DECAY, NORM, ELU>;
+      lds = Geo<C, D, true>::LDS_BYTES;
+    }
+  }
   hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
   dim3 grid(p.n_seg, p.B * p.H);
