@@ -25,6 +25,8 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 #define LA_LDS __attribute__((address_space(3)))
 
@@ -58,8 +60,9 @@ __device__ __forceinline__ void split8_trunc(const float* x, bf16x8& hi, bf16x8&
     const float ra = x[2 * k] - __uint_as_float(a & 0xffff0000u);
     const float rb = x[2 * k + 1] - __uint_as_float(b & 0xffff0000u);
     h[k] = __builtin_amdgcn_perm(b, a, 0x07060302u);  // {hi16(b), hi16(a)}
-    const __bf16 la = to_bf16(ra), lb = to_bf16(rb);
-    l[k] = (unsigned)__builtin_bit_cast(unsigned short, la) | ((unsigned)__builtin_bit_cast(unsigned short, lb) << 16);
+    // one packed round-to-nearest-even conversion, element 0 in the low half
+    const bf16x2 lp = __builtin_convertvector((f32x2){ra, rb}, bf16x2);
+    l[k] = __builtin_bit_cast(unsigned, lp);
   }
   hi = __builtin_bit_cast(bf16x8, h);
   lo = __builtin_bit_cast(bf16x8, l);
@@ -128,6 +131,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
 }
 __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+// Same with a wave-uniform part of the offset in the scalar offset operand, so loads
+// that differ only by a constant stride share one offset register.
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+// An integer the optimiser must treat as unknown. Used for per-lane LDS base addresses:
+// kept in one register each, with every access a base plus an immediate offset, rather
+// than the constant parts folded back in and a register materialised per access (the
+// DS immediate only reaches 64 KiB, less than the LDS image of the prefill kernels).
+__device__ __forceinline__ int pin(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
 }
 
 // XOR-swizzled row-major tiles (no padding, pitch = D elements): the 16-byte chunk c of

@@ -92,10 +92,12 @@ __device__ __forceinline__ int piece_row(int i) {
 // Rows >= valid read as zeros (bounded buffer resource, no branches).
 template <int C, int D>
 __device__ __forceinline__ void load_pieces(Pieces<C, D>& P, const uint16_t* __restrict__ g, int valid) {
+  using G = Geo<C, D, true>;
+  static_assert(G::NT % G::PPR == 0, "piece i of a thread is i * NT / PPR rows below piece 0");
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(g, (uint32_t)valid * D * 2);
+  const uint32_t v0 = (uint32_t)(piece_row<C, D>(0) * D + piece_cols<C, D>(0)) * 2;
 #pragma unroll
-  for (int i = 0; i < Geo<C, D, true>::NPC; ++i)
-    P.r[i] = buf_load16(rs, (uint32_t)(piece_row<C, D>(i) * D + piece_cols<C, D>(i)) * 2);
+  for (int i = 0; i < G::NPC; ++i) P.r[i] = buf_load16(rs, v0, (uint32_t)(i * (G::NT / G::PPR) * D * 2));
 }
 
 // Q: psi applied, rounded once to bf16.
@@ -484,13 +486,13 @@ struct ShGeo {
   static constexpr int K_BYTES = C * PK * 2;
   static constexpr int V_BYTES = C * PV * 2;
   static constexpr int A_BYTES = NTILE * A_TILE;
+  // K lo directly after K, so one register addresses both (offsets stay below 64 KiB)
   static constexpr int OFF_Q = 0;
   static constexpr int OFF_K = Q_BYTES;
-  static constexpr int OFF_V = OFF_K + K_BYTES;
-  static constexpr int OFF_KLO = OFF_V + V_BYTES;  // psi(k) lo (elu+1) or K~ lo (decay)
+  static constexpr int OFF_KLO = OFF_K + K_BYTES;  // psi(k) lo (elu+1) or K~ lo (decay)
   static constexpr int OFF_A = ELU ? OFF_KLO + K_BYTES : OFF_KLO;  // aliases K lo for identity psi
-  static constexpr int X_END = ELU ? OFF_A + A_BYTES : OFF_KLO + (A_BYTES > K_BYTES ? A_BYTES : K_BYTES);
-  static constexpr int OFF_F = X_END;
+  static constexpr int OFF_V = ELU ? OFF_A + A_BYTES : OFF_KLO + (A_BYTES > K_BYTES ? A_BYTES : K_BYTES);
+  static constexpr int OFF_F = OFF_V + V_BYTES;
   static constexpr int F_Z = 0;               // Z [D]
   static constexpr int F_ZRED = D;            // per-wave Z partials [NW][D]
   static constexpr int F_THETA = D + NW * D;  // gamma^(j+1) [C]
@@ -521,71 +523,54 @@ __device__ __forceinline__ void state_mfma_p(f32x16 (&S)[D / 32], const __bf16* 
   }
 }
 
-// S[pt] += K~^T V over the chunk, K~ = hi (+ lo) in swizzled LDS tiles, V with pitch PV.
-template <int C, int D, bool SPLIT, int PV>
-__device__ __forceinline__ void state_mfma_swz(f32x16 (&S)[D / 32], const __bf16* sK, const __bf16* sKlo,
-                                               const __bf16* sV, int Ew, int lane) {
-#pragma unroll 2
-  for (int ik = 0; ik < C / 16; ++ik) {
-    const bf16x8 vb = ld_rows8(sV, PV, ik * 16, Ew, lane);
-#pragma unroll
-    for (int pt = 0; pt < D / 32; ++pt) {
-      S[pt] = mfma32(ld_rows8_swz<D>(sK, ik * 16, pt * 32, lane), vb, S[pt]);
-      if (SPLIT) S[pt] = mfma32(ld_rows8_swz<D>(sKlo, ik * 16, pt * 32, lane), vb, S[pt]);
-    }
-  }
-}
-
-// K into swizzled LDS: identity psi stores the raw keys (rows past T are zero from the
-// bounded load); elu+1 stores psi(k) as hi + lo. zp += Xi_i psi(k_i) when NORM.
-template <int C, int D, bool ELU, bool DECAY, bool NORM>
-__device__ __forceinline__ void commit_k_swz(const Pieces<C, D>& P, __bf16* sK, __bf16* sKlo, int L, float lg,
-                                             float (&zp)[8]) {
-#pragma unroll
-  for (int i = 0; i < Geo<C, D, true>::NPC; ++i) {
-    const int row = piece_row<C, D>(i), c8 = piece_cols<C, D>(i);
-    const int off = swz_off<D>(row, c8);
-    if (!ELU && !NORM) {
-      *(uint4*)(sK + off) = P.r[i];
-      continue;
-    }
-    const float live = row < L ? 1.f : 0.f;
-    const float xi = DECAY ? live * exp2f((float)(L - 1 - row) * lg) : live;
-    const bf16x8 x = __builtin_bit_cast(bf16x8, P.r[i]);
-    float f[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      f[j] = ELU ? elu1(from_bf16(x[j])) * live : from_bf16(x[j]);
-      if (NORM) zp[j] += f[j] * xi;
-    }
-    if (ELU) {
-      bf16x8 hi, lo;
-      split8_trunc(f, hi, lo);
-      *(bf16x8*)(sK + off) = hi;
-      *(bf16x8*)(sKlo + off) = lo;
-    } else {
-      *(uint4*)(sK + off) = P.r[i];
-    }
-  }
-}
-
+// Output kernel addressing. The LDS image (up to 160 KiB) is larger than the 64 KiB reach
+// of a DS instruction's immediate offset, so each region is addressed from per-lane
+// byte bases pinned in registers (see pin) plus compile-time immediates below 64 KiB.
+// K and K lo are XOR-swizzled (swz_off); since swz<D>(r0 + x) == swz<D>(x) whenever r0
+// is a multiple of 16 and x < 32, a swizzled read of any row block is one of a few
+// per-lane bases plus the row block's constant offset.
 template <int C, int D, bool DECAY, bool NORM, bool ELU>
 __global__ __launch_bounds__(2 * D) void k_output_sh(PrefillParams p) {
   using G = ShGeo<C, D, ELU>;
+  using PG = Geo<C, D, true>;  // piece geometry of the global -> LDS copies
   static_assert(G::FITS, "LDS budget");
+  static_assert(PG::NT / PG::PPR == 16, "piece i of a thread covers row 16 i + tid / PPR");
   constexpr bool SPLIT = DECAY || ELU;
-  constexpr int NJ = G::NJ, NW = G::NW;
+  constexpr int NJ = G::NJ, NW = G::NW, NPC = PG::NPC;
+  constexpr int TPW = (G::NTILE + NW - 1) / NW;  // score tiles per wave (the last round partial)
+  constexpr int PQ = G::PQ, PV = G::PV, PA = G::PA;
+  constexpr int KLO = G::K_BYTES;    // K lo, relative to K
+  constexpr int ALO = 32 * PA * 2;   // a score tile's lo half, relative to its hi half
   extern __shared__ __align__(16) unsigned char smem[];
   const int seg = blockIdx.x, bh = blockIdx.y, head = bh % p.H;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, n = lane & 31, hh = lane >> 5;
+  const int L16 = lane & 15, g = lane >> 4;
   const int Ew = 32 * w;
   const float lg = DECAY ? p.log2g[head] : 0.f;
-  __bf16* sQ = (__bf16*)(smem + G::OFF_Q);
-  __bf16* sK = (__bf16*)(smem + G::OFF_K);
-  __bf16* sV = (__bf16*)(smem + G::OFF_V);
-  __bf16* sKlo = (__bf16*)(smem + G::OFF_KLO);
-  __bf16* sA = (__bf16*)(smem + G::OFF_A);
-  float* sF = (float*)(smem + G::OFF_F);
+
+  // per-lane LDS bases (bytes); pieces of this thread: row prow + 16 i, columns pcol..+7
+  const int prow = tid / PG::PPR, pcol = (tid % PG::PPR) * 8;
+  const int trow = 8 * (g >> 1) + (L16 >> 2), tcol = 16 * (g & 1) + 4 * (L16 & 3);  // transpose reads
+  unsigned char* const qP = smem + pin(G::OFF_Q + (prow * PQ + pcol) * 2);
+  const unsigned char* const qC = smem + pin(G::OFF_Q + (n * PQ + 4 * hh) * 2);  // psi(Q) S operand
+  const unsigned char* const qS = smem + pin(G::OFF_Q + (n * PQ + 8 * hh) * 2);  // score operand
+  const unsigned char* const qZ = smem + pin(G::OFF_Q + (n * PQ + hh * (D / 2)) * 2);  // psi(q) . Z
+  unsigned char* const kP = smem + pin(G::OFF_K + swz_off<D>(prow, pcol) * 2);
+  const unsigned char* kR[D / 16];     // score operand: row n, features 16 kk + 8 hh
+  const unsigned char* kT[D / 32][2];  // state-update operand: rows trow (+4), columns 32 pt + tcol
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) kR[kk] = smem + pin(G::OFF_K + swz_off<D>(n, 16 * kk + 8 * hh) * 2);
+#pragma unroll
+  for (int pt = 0; pt < D / 32; ++pt) {
+    kT[pt][0] = smem + pin(G::OFF_K + swz_off<D>(trow, 32 * pt + tcol) * 2);
+    kT[pt][1] = smem + pin(G::OFF_K + swz_off<D>(trow + 4, 32 * pt + tcol) * 2);
+  }
+  unsigned char* const vP = smem + pin(G::OFF_V + (prow * PV + pcol) * 2);
+  const unsigned char* const vT = smem + pin(G::OFF_V + (trow * PV + Ew + tcol) * 2);
+  unsigned char* const aW = smem + pin(G::OFF_A + (n * PA + 4 * hh) * 2);
+  const unsigned char* const aR = smem + pin(G::OFF_A + (n * PA + 8 * hh) * 2);
+  float* const sF = (float*)(smem + pin(G::OFF_F));
+  float* const fN = (float*)(smem + pin(G::OFF_F + 4 * n));  // per-token entries of this lane's column
 
   // exclusive prefix state of this segment (written by the scan)
   const size_t E = (size_t)D * D + D;
@@ -626,12 +611,52 @@ __global__ __launch_bounds__(2 * D) void k_output_sh(PrefillParams p) {
     const int t0 = c * C, L = min(C, p.T - t0);
     const float a = DECAY ? exp2f((float)L * lg) : 1.f;
     lds_barrier();  // the previous chunk is done with LDS (and Z is updated)
+
+    // ---- commit this chunk's tiles: psi(Q) rounded to bf16; K swizzled (psi(k) as hi + lo
+    // for elu+1; raw keys for identity, rows past T zero from the bounded load); V raw
     float zp[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) zp[j] = 0.f;
-    commit_q<C, D, ELU>(pq, sQ, G::PQ);
-    commit_k_swz<C, D, ELU, DECAY, NORM>(pk, sK, sKlo, L, lg, zp);
-    commit_v<C, D>(pv, sV, G::PV);
+#pragma unroll
+    for (int i = 0; i < NPC; ++i) {
+      uint4 raw = pq.r[i];
+      if (ELU) {
+        const bf16x8 x = __builtin_bit_cast(bf16x8, raw);
+        bf16x8 y;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) y[j] = to_bf16(elu1(from_bf16(x[j])));
+        raw = __builtin_bit_cast(uint4, y);
+      }
+      *(uint4*)(qP + i * 16 * PQ * 2) = raw;
+    }
+#pragma unroll
+    for (int i = 0; i < NPC; ++i) {
+      const int off = i * 16 * D * 2;
+      if (!ELU && !NORM) {
+        *(uint4*)(kP + off) = pk.r[i];
+        continue;
+      }
+      const int row = prow + 16 * i;
+      const float live = row < L ? 1.f : 0.f;
+      const float xi = DECAY ? live * exp2f((float)(L - 1 - row) * lg) : live;
+      const bf16x8 x = __builtin_bit_cast(bf16x8, pk.r[i]);
+      float f[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        f[j] = ELU ? elu1(from_bf16(x[j])) * live : from_bf16(x[j]);
+        if (NORM) zp[j] += f[j] * xi;
+      }
+      if (ELU) {
+        bf16x8 hi, lo;
+        split8_trunc(f, hi, lo);
+        *(bf16x8*)(kP + off) = hi;
+        *(bf16x8*)(kP + off + KLO) = lo;
+      } else {
+        *(uint4*)(kP + off) = pk.r[i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NPC; ++i) *(uint4*)(vP + i * 16 * PV * 2) = pv.r[i];
     const bool more = c + 1 < c1;
     const int Ln = more ? min(C, p.T - (c + 1) * C) : 0;
     // next chunk's tiles stream in during this chunk's matrix work (rows past Ln read as
@@ -642,13 +667,22 @@ __global__ __launch_bounds__(2 * D) void k_output_sh(PrefillParams p) {
     load_pieces<C, D>(pv, vb + (size_t)(c + 1) * C * D, Ln);
     lds_barrier();
 
-    // ---- score tiles, shared: wave w computes tiles w, w + NW, ...
-    for (int t = w; t < G::NTILE; t += NW) {
+    // ---- score tiles A^T (M = i, N = j, k = feature), masked, decayed, split into hi + lo
+    // and shared through LDS: wave w computes tiles w, w + NW, ...
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      const int t = w + u * NW;
+      if (t >= G::NTILE) break;
       const int jt = tile_jt(t), it = t - jt * (jt + 1) / 2;
+      bf16x8 ka[D / 16], qv[D / 16];
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        ka[kk] = *(const bf16x8*)(kR[kk] + it * 32 * D * 2);
+        qv[kk] = *(const bf16x8*)(qS + (jt * 32 * PQ + kk * 16) * 2);
+      }
       f32x16 acc = f32x16{};
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk)
-        acc = mfma32(ld_cols8_swz<D>(sK, it * 32, kk * 16, lane), ld_cols8(sQ, G::PQ, jt * 32, kk * 16, lane), acc);
+      for (int kk = 0; kk < D / 16; ++kk) acc = mfma32(ka[kk], qv[kk], acc);
       const bool diag = it == jt;
       const float tf = (DECAY && !diag) ? exp2f((float)(32 * (jt - it - 1)) * lg) : 1.f;
       float av[16];
@@ -660,21 +694,20 @@ __global__ __launch_bounds__(2 * D) void k_output_sh(PrefillParams p) {
       }
       if (NORM) {
         rs += __shfl_xor(rs, 32);
-        if (hh == 0) sF[G::F_R + t * 32 + n] = rs;
+        if (hh == 0) fN[G::F_R + t * 32] = rs;
       }
-      // A[j = n][i = 8 q4 + 4 hh + 0..3] as 8-byte runs, hi and lo
-      __bf16* ahi = sA + t * (2 * 32 * G::PA);
-      __bf16* alo = ahi + 32 * G::PA;
+      // A[j = n][i = 8 q4 + 4 hh + 0..3] as 8-byte runs: registers 8q..8q+3 are columns
+      // 16q + 4hh + 0..3, registers 8q+4..8q+7 columns 16q + 8 + 4hh + 0..3
+      unsigned char* at = aW + t * G::A_TILE;
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         bf16x8 h8, l8;
         split8_trunc(av + 8 * q, h8, l8);
         const u32x4 hv = __builtin_bit_cast(u32x4, h8), lv = __builtin_bit_cast(u32x4, l8);
-        // registers 8q..8q+3 -> cols 16q + 4hh + 0..3; 8q+4..8q+7 -> cols 16q + 8 + 4hh + 0..3
-        *(uint2*)(ahi + n * G::PA + 16 * q + 4 * hh) = make_uint2(hv[0], hv[1]);
-        *(uint2*)(ahi + n * G::PA + 16 * q + 8 + 4 * hh) = make_uint2(hv[2], hv[3]);
-        *(uint2*)(alo + n * G::PA + 16 * q + 4 * hh) = make_uint2(lv[0], lv[1]);
-        *(uint2*)(alo + n * G::PA + 16 * q + 8 + 4 * hh) = make_uint2(lv[2], lv[3]);
+        *(uint2*)(at + 32 * q) = make_uint2(hv[0], hv[1]);
+        *(uint2*)(at + 32 * q + 16) = make_uint2(hv[2], hv[3]);
+        *(uint2*)(at + 32 * q + ALO) = make_uint2(lv[0], lv[1]);
+        *(uint2*)(at + 32 * q + 16 + ALO) = make_uint2(lv[2], lv[3]);
       }
     }
     lds_barrier();
@@ -683,7 +716,7 @@ __global__ __launch_bounds__(2 * D) void k_output_sh(PrefillParams p) {
     // column e, N = token j), so each lane ends up with 4 consecutive columns of one token
     // row (16-byte stores) and the per-token factors are lane scalars.
     const __amdgpu_buffer_rsrc_t ors = make_rsrc(ob + (size_t)t0 * D, (uint32_t)L * D * 4);
-    bf16x8 sh[D / 32][2], sl[D / 32][2];
+    bf16x8 sh[D / 32][2], sl[D / 32][2];  // S_prev as hi + lo, straight from its accumulator layout
 #pragma unroll
     for (int pt = 0; pt < D / 32; ++pt)
 #pragma unroll
@@ -697,46 +730,49 @@ __global__ __launch_bounds__(2 * D) void k_output_sh(PrefillParams p) {
     // at the next commit then leaves this chunk's output stores in flight
 #pragma unroll
     for (int jt = 0; jt < NJ; ++jt) {
-      // numT = S_prev^T psi(Q)^T   (k = state row p; S straight from its accumulator layout)
+      // numT = S_prev^T psi(Q)^T (k = state row p, in the D-tile feedback order)
       f32x16 num = f32x16{};
 #pragma unroll
       for (int pt = 0; pt < D / 32; ++pt)
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-          const bf16x8 qa = ld_cols8_perm(sQ, G::PQ, jt * 32, pt * 32, q, lane);
-          num = mfma32(sh[pt][q], qa, num);
-          num = mfma32(sl[pt][q], qa, num);
+          const unsigned char* qa = qC + (jt * 32 * PQ + pt * 32 + 16 * q) * 2;
+          const bf16x8 qo = cat8(*(const bf16x4*)qa, *(const bf16x4*)(qa + 16));
+          num = mfma32(sh[pt][q], qo, num);
+          num = mfma32(sl[pt][q], qo, num);
         }
-      if (DECAY) num *= sF[G::F_THETA + jt * 32 + n];  // gamma^(j+1), j = this lane's token
-      // numT += V^T A^T for it <= jt   (k = token i; A from LDS)
-#pragma unroll 1
+      if (DECAY) num *= fN[G::F_THETA + jt * 32];  // gamma^(j+1), j = this lane's token
+      // numT += V^T A^T for it <= jt (k = token i)
+#pragma unroll
       for (int it = 0; it <= jt; ++it) {
-        const __bf16* ahi = sA + (jt * (jt + 1) / 2 + it) * (2 * 32 * G::PA);
-        const __bf16* alo = ahi + 32 * G::PA;
+        const unsigned char* at = aR + (jt * (jt + 1) / 2 + it) * G::A_TILE;
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-          const bf16x8 vv = ld_rows8(sV, G::PV, it * 32 + 16 * q, Ew, lane);
-          num = mfma32(vv, ld_cols8(ahi, G::PA, 0, 16 * q, lane), num);
-          num = mfma32(vv, ld_cols8(alo, G::PA, 0, 16 * q, lane), num);
+          const int r0 = it * 32 + 16 * q;
+          const bf16x8 vv = cat8(lds_read_tr4((const __bf16*)(vT + r0 * PV * 2)),
+                                 lds_read_tr4((const __bf16*)(vT + (r0 + 4) * PV * 2)));
+          num = mfma32(vv, *(const bf16x8*)(at + 32 * q), num);
+          num = mfma32(vv, *(const bf16x8*)(at + 32 * q + ALO), num);
         }
       }
       float inv = 1.f;
       if (NORM) {
-        // psi(q_j) . Z_prev and the score row sums for j = jt*32 + n
+        // psi(q_j) . Z_prev (the lane halves split the features) and the score row sums
         float qz = 0.f;
-        const __bf16* qr = sQ + (jt * 32 + n) * G::PQ + hh * (D / 2);
+        const unsigned char* qr = qZ + jt * 32 * PQ * 2;
         const f32x4* zr = (const f32x4*)(sF + G::F_Z + hh * (D / 2));
 #pragma unroll
         for (int e8 = 0; e8 < D / 2; e8 += 8) {
-          const bf16x8 qv = *(const bf16x8*)(qr + e8);
+          const bf16x8 qv = *(const bf16x8*)(qr + e8 * 2);
           const f32x4 z0 = zr[e8 / 4], z1 = zr[e8 / 4 + 1];
 #pragma unroll
           for (int j = 0; j < 4; ++j) qz += from_bf16(qv[j]) * z0[j] + from_bf16(qv[4 + j]) * z1[j];
         }
         qz += __shfl_xor(qz, 32);
         float r = 0.f;
-        for (int it = 0; it <= jt; ++it) r += sF[G::F_R + (jt * (jt + 1) / 2 + it) * 32 + n];
-        inv = 1.f / (sF[G::F_THETA + jt * 32 + n] * qz + r + p.eps);
+#pragma unroll
+        for (int it = 0; it <= jt; ++it) r += fN[G::F_R + (jt * (jt + 1) / 2 + it) * 32];
+        inv = 1.f / (fN[G::F_THETA + jt * 32] * qz + r + p.eps);
       }
       // registers 4 q4 .. 4 q4 + 3 hold columns Ew + 8 q4 + 4 hh + 0..3 of token row j
       const uint32_t row_off = (uint32_t)((jt * 32 + n) * D + Ew + 4 * hh) * 4;
@@ -748,19 +784,18 @@ __global__ __launch_bounds__(2 * D) void k_output_sh(PrefillParams p) {
       }
     }
 
-    // state update: K~ = Xi psi(K) as hi + lo, S <- gamma^L S + K~^T V, Z <- gamma^L Z + K~^T 1
+    // ---- state update: K~ = Xi psi(K) as hi + lo, S <- gamma^L S + K~^T V, Z <- gamma^L Z + K~^T 1
     if (NORM) reduce_zp<D>(zp, sF + G::F_ZRED);
     if (DECAY) {
       lds_barrier();  // every wave is done with the score tiles (K lo aliases them) and K
 #pragma unroll
-      for (int i = 0; i < Geo<C, D, true>::NPC; ++i) {
-        const int row = piece_row<C, D>(i), c8 = piece_cols<C, D>(i);
+      for (int i = 0; i < NPC; ++i) {
+        const int row = prow + 16 * i, off = i * 16 * D * 2;
         const float xi = row < L ? exp2f((float)(L - 1 - row) * lg) : 0.f;
-        const int off = swz_off<D>(row, c8);
-        const bf16x8 h8 = *(const bf16x8*)(sK + off);
+        const bf16x8 h8 = *(const bf16x8*)(kP + off);
         float x[8];
         if (ELU) {
-          const bf16x8 l8 = *(const bf16x8*)(sKlo + off);
+          const bf16x8 l8 = *(const bf16x8*)(kP + off + KLO);
 #pragma unroll
           for (int j = 0; j < 8; ++j) x[j] = (from_bf16(h8[j]) + from_bf16(l8[j])) * xi;
         } else {
@@ -769,8 +804,8 @@ __global__ __launch_bounds__(2 * D) void k_output_sh(PrefillParams p) {
         }
         bf16x8 hi, lo;
         split8_trunc(x, hi, lo);
-        *(bf16x8*)(sK + off) = hi;
-        *(bf16x8*)(sKlo + off) = lo;
+        *(bf16x8*)(kP + off) = hi;
+        *(bf16x8*)(kP + off + KLO) = lo;
       }
     }
     lds_barrier();
@@ -784,7 +819,23 @@ __global__ __launch_bounds__(2 * D) void k_output_sh(PrefillParams p) {
 #pragma unroll
       for (int pt = 0; pt < D / 32; ++pt) S[pt] *= a;
     }
-    state_mfma_swz<C, D, SPLIT, G::PV>(S, sK, sKlo, sV, Ew, lane);
+    // S[pt] += K~^T V (M = state row, N = value column, k = token)
+#pragma unroll
+    for (int ik = 0; ik < C / 16; ++ik) {
+      const int r0 = ik * 16;
+      const bf16x8 vb8 = cat8(lds_read_tr4((const __bf16*)(vT + r0 * PV * 2)),
+                              lds_read_tr4((const __bf16*)(vT + (r0 + 4) * PV * 2)));
+#pragma unroll
+      for (int pt = 0; pt < D / 32; ++pt) {
+        const int ko = r0 * D * 2;
+        S[pt] = mfma32(cat8(lds_read_tr4((const __bf16*)(kT[pt][0] + ko)), lds_read_tr4((const __bf16*)(kT[pt][1] + ko))),
+                       vb8, S[pt]);
+        if (SPLIT)
+          S[pt] = mfma32(cat8(lds_read_tr4((const __bf16*)(kT[pt][0] + ko + KLO)),
+                              lds_read_tr4((const __bf16*)(kT[pt][1] + ko + KLO))),
+                         vb8, S[pt]);
+      }
+    }
   }
 }
 
