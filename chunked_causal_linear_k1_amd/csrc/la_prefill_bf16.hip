@@ -1,16 +1,22 @@
-// la_prefill_bf16.hip -- dispatch of the bf16 prefill kernels (see la_prefill_bf16.hpp)
-// over the supported chunk sizes and head widths.
+// la_prefill_bf16.hip -- dispatch of the bf16 prefill kernels (la_prefill_bf16.hpp for the
+// identity and elu+1 feature maps, la_prefill_prf.hip for positive random features) over the
+// supported chunk sizes and head widths.
 #include "la_prefill_bf16.hpp"
 
 namespace la {
 
+bool prefill_prf_bf16_supported(int C, int d_k, int d_v, int n_psi);
+hipError_t launch_prefill_prf_bf16(const PrefillParams& p, hipStream_t s, bool out);
+
 bool prefill_bf16_supported(int C, int d_k, int d_v, int n_psi, int psi) {
+  if (psi == LA_PSI_PRF) return prefill_prf_bf16_supported(C, d_k, d_v, n_psi);
   if (psi != LA_PSI_IDENTITY && psi != LA_PSI_ELU1) return false;
   if (d_k != d_v || n_psi != d_k) return false;
   return (d_k == 64 || d_k == 128) && (C == 64 || C == 128);
 }
 
 static hipError_t dispatch(const PrefillParams& p, hipStream_t s, bool out) {
+  if (p.psi == LA_PSI_PRF) return launch_prefill_prf_bf16(p, s, out);
   if (p.C == 64 && p.d_k == 64) return launch_prefill_bf16_c64_d64(p, s, out);
   if (p.C == 64 && p.d_k == 128) return launch_prefill_bf16_c64_d128(p, s, out);
   if (p.C == 128 && p.d_k == 64) return launch_prefill_bf16_c128_d64(p, s, out);

@@ -195,3 +195,72 @@ def test_full_prefill_8k_elu1_sampled():
 def test_full_retnet_128k_sampled():
     # the fastest-decaying head, the slowest, and two in between
     _full_size(workloads.RETNET_128K, heads=[0, 21, 42, 63])
+
+
+# positive random features (psi = exp(W x - |x|^2/2) / sqrt(n_psi), one bf16 bank per head)
+PRF_SMALL = [
+    # name, B, H, T, n_psi, normalize, decay, v_scale
+    ("prf256_ragged", 1, 2, 450, 256, 1, "none", 1.0),
+    ("prf128_ragged", 2, 1, 333, 128, 1, "none", 1.0),
+    ("prf256_decay_norm", 1, 2, 400, 256, 1, "const:0.99", 1.0),
+    ("prf128_decay_norm_spread", 1, 3, 260, 128, 1, "retnet_spread", 1.0),
+    ("prf256_decay_nonorm", 1, 2, 300, 256, 0, "retnet_spread", 0.05),
+]
+
+
+@pytest.mark.parametrize("case", PRF_SMALL, ids=[c[0] for c in PRF_SMALL])
+def test_prf_small_elementwise(case):
+    name, B, H, T, n_psi, normalize, decay, vs = case
+    w = Workload(name=name, B=B, H=H, T=T, d_k=128, d_v=128, n_psi=n_psi, chunk=64, psi=PSI_PRF,
+                 normalize=normalize, eps=1e-6, dtype="bf16", seed=13, qk_scale=128 ** -0.25, v_scale=vs,
+                 decay=decay)
+    announce(f"prefill prf small {name}")
+    inp = inputs.make_prefill_inputs(w, device="cpu")
+    o = _run(w, inp).cpu().reshape(B * H, T, 128).numpy()
+    ref = _oracle_o(w, inp)
+    if normalize:
+        assert_close(o, ref, "bf16", name)
+    else:
+        # unnormalised sums of exponential features have no fixed scale (here |o| ~ 1e3):
+        # rel-L2 as is, max-abs on outputs scaled by the largest reference magnitude
+        scale = float(np.abs(ref).max())
+        assert_close(o / scale, ref / scale, "bf16", f"{name} (scaled by max |o| = {scale:.3g})")
+
+
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 129])
+def test_prf_edge_lengths(T):
+    w = Workload(name=f"prf_edge_T{T}", B=1, H=2, T=T, d_k=128, d_v=128, n_psi=256, chunk=64, psi=PSI_PRF,
+                 normalize=1, eps=1e-6, dtype="bf16", seed=40 + T, qk_scale=128 ** -0.25, v_scale=1.0)
+    announce(f"prefill prf edge T={T}")
+    inp = inputs.make_prefill_inputs(w, device="cpu")
+    o = _run(w, inp)
+    ref = _oracle_o(w, inp)
+    assert_close(o.cpu().reshape(2, T, 128).numpy(), ref, "bf16", w.name)
+
+
+def test_prf_initial_and_final_state():
+    """n_psi = 256 != d_v: the 256 x 128 state and 256-long normaliser in and out."""
+    B, H, T, NP = 1, 2, 301, 256
+    w = Workload(name="prf_state", B=B, H=H, T=T, d_k=128, d_v=128, n_psi=NP, chunk=64, psi=PSI_PRF,
+                 normalize=1, eps=1e-6, dtype="bf16", seed=17, qk_scale=128 ** -0.25, v_scale=1.0,
+                 decay="const:0.995")
+    announce("prefill prf init/final state")
+    inp = inputs.make_prefill_inputs(w, device="cpu")
+    rng = np.random.default_rng(4)
+    S0 = (rng.standard_normal((B, H, NP, 128)) * 0.5).astype(np.float32)
+    Z0 = (np.abs(rng.standard_normal((B, H, NP))) * 5 + 1).astype(np.float32)
+    fS = torch.empty((B, H, NP, 128), dtype=torch.float32, device=DEV)
+    fZ = torch.empty((B, H, NP), dtype=torch.float32, device=DEV)
+    o = _run(w, inp, init_S=torch.from_numpy(S0).to(DEV), init_Z=torch.from_numpy(Z0).to(DEV), final_S=fS,
+             final_Z=fZ)
+    ref, rS, rZ = _oracle_o(w, inp, S0=S0.reshape(B * H, NP, 128).astype(np.float64),
+                            Z0=Z0.reshape(B * H, NP).astype(np.float64), want_state=True)
+    assert_close(o.cpu().reshape(B * H, T, 128).numpy(), ref, "bf16", "prf o with init state")
+    assert_close(fS.cpu().reshape(B * H, NP, 128).numpy() / np.abs(rS).max(), rS / np.abs(rS).max(), "bf16",
+                 "prf final S (scaled to max 1)")
+    assert_close(fZ.cpu().reshape(B * H, NP).numpy() / np.abs(rZ).max(), rZ / np.abs(rZ).max(), "bf16",
+                 "prf final Z (scaled to max 1)")
+
+
+def test_full_prf_4k_sampled():
+    _full_size(workloads.PRF_4K, heads=[0, 37, 81, 127])
