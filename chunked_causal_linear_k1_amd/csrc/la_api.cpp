@@ -17,7 +17,11 @@ namespace {
 using la::PrefillParams;
 using la::ScanParams;
 
-constexpr int kTargetWorkgroups = 2048;  // prefill parallelism target (8 per CU on 256 CUs)
+// Prefill decomposition (segments of consecutive chunks, one workgroup each):
+constexpr int kTargetWorkgroups = 2048;  // enough to fill 256 CUs several times over
+constexpr int kMinWorkgroups = 256;      // at least one per CU where the sequences allow it
+constexpr int kMinSegTokens = 2048;      // per-segment state traffic (n_psi*d_v floats written,
+                                         // scanned, read back) small next to the token traffic
 
 bool aligned16(const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -53,6 +57,7 @@ la_status validate_prefill_desc(const la_prefill_desc* d) {
   if (d->in_dtype != LA_BF16 && d->in_dtype != LA_F32) return LA_ERR_VALUE;
   if (d->out_dtype != LA_BF16 && d->out_dtype != LA_F32) return LA_ERR_VALUE;
   if (d->psi != LA_PSI_PRF && d->n_psi != d->d_k) return LA_ERR_SHAPE;
+  if (d->d_v % 4 != 0 || d->n_psi % 4 != 0) return LA_ERR_UNSUPPORTED;  // 16-byte state rows
   // element counts must fit comfortably in 64-bit offsets and the grid's y extent
   const double tokens = (double)d->B * d->H * d->T;
   if (tokens * std::max(d->d_k, d->d_v) > 9.0e15) return LA_ERR_SHAPE;
@@ -74,6 +79,8 @@ Plan make_plan(const la_prefill_desc* d) {
   const long long BH = (long long)d->B * d->H;
   pl.n_chunks = (int)((d->T + (long long)d->chunk - 1) / d->chunk);
   long long want = (kTargetWorkgroups + BH - 1) / BH;  // segments per sequence
+  want = std::min<long long>(want, std::max(1LL, (long long)d->T / kMinSegTokens));
+  if (want * BH < kMinWorkgroups) want = (kMinWorkgroups + BH - 1) / BH;
   want = std::max(1LL, std::min<long long>(want, pl.n_chunks));
   pl.seg_chunks = (int)((pl.n_chunks + want - 1) / want);
   pl.n_seg = (pl.n_chunks + pl.seg_chunks - 1) / pl.seg_chunks;

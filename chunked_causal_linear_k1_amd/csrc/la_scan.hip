@@ -9,14 +9,14 @@
 // X_s with init (+) X_0 (+) ... (+) X_{s-1} and writes init (+) X_0 (+) ... as the
 // final state.
 //
-// The state elements (n_psi*d_v + n_psi per sequence) are independent, so a
-// workgroup takes 64 consecutive elements (one per lane) and spreads the segment
-// axis over W waves: each wave folds its run of segments, the W wave totals are
-// scanned with a Blelloch up-sweep/down-sweep in LDS (log2 W levels each; the
-// down-sweep combines parent-prefix (+) left-sum in that order because the monoid
-// does not commute), and each wave then rewrites its run with exclusive prefixes.
-// Every element is read twice and written once, coalesced; the order of all
-// floating-point operations is fixed, so results are deterministic.
+// The state elements (n_psi*d_v + n_psi per sequence) are independent. A workgroup
+// takes 256 consecutive elements (4 per lane, 16-byte accesses) and spreads the segment
+// axis over W waves: each wave folds its run of segments (holding the run in registers
+// when it is at most RUN long, so every element is read once and written once), the W
+// wave totals are scanned with a Blelloch up-sweep/down-sweep in LDS (log2 W levels
+// each; the down-sweep combines parent-prefix (+) left-sum in that order because the
+// monoid does not commute), and each wave then writes its run's exclusive prefixes.
+// The order of all floating-point operations is fixed: results are deterministic.
 #include "la_device.hpp"
 #include "la_kernels.hpp"
 
@@ -25,15 +25,21 @@ namespace {
 
 constexpr int kMaxWaves = 16;
 
+__device__ __forceinline__ f32x4 ld4(const float* p) { return *(const f32x4*)p; }
+__device__ __forceinline__ void st4(float* p, const f32x4& v) { *(f32x4*)p = v; }
+
+// RUN > 0: runs of up to RUN segments are kept in registers between the fold and the
+// rewrite; RUN == 0: the rewrite reads the run again (any run length).
+template <int RUN>
 __global__ __launch_bounds__(64 * kMaxWaves) void k_segment_scan(ScanParams p) {
-  __shared__ float sx[kMaxWaves][64];
+  __shared__ f32x4 sx[kMaxWaves][64];
   __shared__ float sa[kMaxWaves];
   const int W = blockDim.x >> 6;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int bh = blockIdx.y, head = bh % p.H;
   const size_t SE = (size_t)p.n_psi * p.d_v;
-  const size_t E = SE + p.n_psi;
-  const size_t e = (size_t)blockIdx.x * 64 + lane;
+  const size_t E = SE + p.n_psi;  // a multiple of 4 (n_psi and d_v are multiples of 4)
+  const size_t e = ((size_t)blockIdx.x * 64 + lane) * 4;
   const bool live = e < E;
   const float lg = p.has_decay ? p.log2g[head] : 0.f;
   float* base = p.ws + (size_t)bh * p.n_seg * E + e;
@@ -41,19 +47,33 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_segment_scan(ScanParams p) {
   // this wave's run of segments
   const int per = (p.n_seg + W - 1) / W;
   const int s0 = min(w * per, p.n_seg), s1 = min(s0 + per, p.n_seg);
-
   auto seg_decay = [&](int s) {
     const int len = min(p.seg_len, p.T - s * p.seg_len);
     return gpow(lg, (float)len);
   };
 
   // 1. fold the run: total = X_s0 (+) ... (+) X_{s1-1}
-  float tx = 0.f, ta = 1.f;
-  for (int s = s0; s < s1; ++s) {
-    const float as = seg_decay(s);
-    const float xs = live ? base[(size_t)s * E] : 0.f;
-    tx = as * tx + xs;
-    ta *= as;
+  f32x4 run[RUN > 0 ? RUN : 1];
+  f32x4 tx = {0.f, 0.f, 0.f, 0.f};
+  float ta = 1.f;
+  if (RUN > 0) {
+#pragma unroll
+    for (int i = 0; i < (RUN > 0 ? RUN : 1); ++i)
+      run[i] = (live && s0 + i < s1) ? ld4(base + (size_t)(s0 + i) * E) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < (RUN > 0 ? RUN : 1); ++i) {
+      if (s0 + i < s1) {
+        const float as = seg_decay(s0 + i);
+        tx = as * tx + run[i];
+        ta *= as;
+      }
+    }
+  } else {
+    for (int s = s0; s < s1; ++s) {
+      const float as = seg_decay(s);
+      if (live) tx = as * tx + ld4(base + (size_t)s * E);
+      ta *= as;
+    }
   }
   sx[w][lane] = tx;
   if (lane == 0) sa[w] = ta;
@@ -63,7 +83,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_segment_scan(ScanParams p) {
   for (int d = 1; d < W; d <<= 1) {  // up-sweep: node right <- left (+) right
     const int right = (w + 1) * 2 * d - 1;
     const bool act = right < W;
-    float nx = 0.f, na = 1.f;
+    f32x4 nx = {0.f, 0.f, 0.f, 0.f};
+    float na = 1.f;
     if (act) {
       const int left = right - d;
       nx = sa[right] * sx[left][lane] + sx[right][lane];
@@ -77,13 +98,14 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_segment_scan(ScanParams p) {
     __syncthreads();
   }
   if (w == W - 1) {
-    sx[W - 1][lane] = 0.f;
+    sx[W - 1][lane] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (lane == 0) sa[W - 1] = 1.f;
   }
   __syncthreads();
   for (int d = W >> 1; d >= 1; d >>= 1) {  // down-sweep
     const int right = (w + 1) * 2 * d - 1;
-    float lx = 0.f, la_ = 1.f, px = 0.f, pa = 1.f;
+    f32x4 lx = {0.f, 0.f, 0.f, 0.f}, px = {0.f, 0.f, 0.f, 0.f};
+    float la_ = 1.f, pa = 1.f;
     const bool act = right < W;
     if (act) {
       const int left = right - d;
@@ -95,7 +117,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_segment_scan(ScanParams p) {
     __syncthreads();
     if (act) {
       const int left = right - d;
-      sx[left][lane] = px;  // left child gets the parent's prefix
+      sx[left][lane] = px;              // left child gets the parent's prefix
       sx[right][lane] = la_ * px + lx;  // right child: prefix (+) left sum
       if (lane == 0) {
         sa[left] = pa;
@@ -106,32 +128,43 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_segment_scan(ScanParams p) {
   }
 
   // 3. carry into this run: init (+) prefix_w
-  float cx = sx[w][lane];
+  f32x4 cx = sx[w][lane];
   const float ca = sa[w];
   if (live) {
-    float init = 0.f;
+    f32x4 init = {0.f, 0.f, 0.f, 0.f};
     if (e < SE) {
-      if (p.init_S) init = p.init_S[(size_t)bh * SE + e];
+      if (p.init_S) init = ld4(p.init_S + (size_t)bh * SE + e);
     } else if (p.init_Z) {
-      init = p.init_Z[(size_t)bh * p.n_psi + (e - SE)];
+      init = ld4(p.init_Z + (size_t)bh * p.n_psi + (e - SE));
     }
     cx = ca * init + cx;
   }
   // 4. rewrite the run with exclusive prefixes
-  for (int s = s0; s < s1; ++s) {
-    const float as = seg_decay(s);
-    if (live) {
-      const float xs = base[(size_t)s * E];
-      base[(size_t)s * E] = cx;
-      cx = as * cx + xs;
+  if (RUN > 0) {
+#pragma unroll
+    for (int i = 0; i < (RUN > 0 ? RUN : 1); ++i) {
+      if (s0 + i < s1) {
+        const float as = seg_decay(s0 + i);
+        if (live) st4(base + (size_t)(s0 + i) * E, cx);
+        cx = as * cx + run[i];
+      }
+    }
+  } else {
+    for (int s = s0; s < s1; ++s) {
+      const float as = seg_decay(s);
+      if (live) {
+        const f32x4 xs = ld4(base + (size_t)s * E);
+        st4(base + (size_t)s * E, cx);
+        cx = as * cx + xs;
+      }
     }
   }
   // 5. the wave holding the last segment writes the final state
   if (live && s1 == p.n_seg && s0 < s1) {
     if (e < SE) {
-      if (p.final_S) p.final_S[(size_t)bh * SE + e] = cx;
+      if (p.final_S) st4(p.final_S + (size_t)bh * SE + e, cx);
     } else if (p.final_Z) {
-      p.final_Z[(size_t)bh * p.n_psi + (e - SE)] = cx;
+      st4(p.final_Z + (size_t)bh * p.n_psi + (e - SE), cx);
     }
   }
 }
@@ -139,11 +172,18 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_segment_scan(ScanParams p) {
 }  // namespace
 
 hipError_t launch_segment_scan(const ScanParams& p, hipStream_t s) {
+  // waves per workgroup: a power of two, runs of ~4 segments per wave, at most kMaxWaves
   int W = 1;
-  while (W < p.n_seg && W < kMaxWaves) W <<= 1;
+  while (W < kMaxWaves && W * 4 < p.n_seg) W <<= 1;
+  const int per = (p.n_seg + W - 1) / W;
   const size_t E = (size_t)p.n_psi * p.d_v + p.n_psi;
-  dim3 grid((unsigned)((E + 63) / 64), p.BH);
-  hipLaunchKernelGGL(k_segment_scan, grid, dim3(64 * W), 0, s, p);
+  dim3 grid((unsigned)((E + 255) / 256), p.BH);
+  if (per <= 4)
+    hipLaunchKernelGGL(k_segment_scan<4>, grid, dim3(64 * W), 0, s, p);
+  else if (per <= 8)
+    hipLaunchKernelGGL(k_segment_scan<8>, grid, dim3(64 * W), 0, s, p);
+  else
+    hipLaunchKernelGGL(k_segment_scan<0>, grid, dim3(64 * W), 0, s, p);
   return hipGetLastError();
 }
 

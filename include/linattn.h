@@ -87,10 +87,12 @@ typedef struct {
 } la_prefill_desc;
 
 /* Supported sizes in this build (anything else: LA_ERR_UNSUPPORTED):
- *   in_dtype LA_BF16: d_k == d_v in {64, 128}; chunk in {64, 128};
- *                     psi identity/elu1 (n_psi == d_k), or PRF with n_psi in
- *                     {64, 128, 256} and chunk == 64.
- *   in_dtype LA_F32 : d_k, d_v, n_psi <= 128, chunk in {16, 32, 64}, any psi.
+ *   in_dtype LA_BF16: psi identity/elu1: d_k == d_v == n_psi in {64, 128},
+ *                     chunk in {64, 128};
+ *                     psi PRF: d_k == d_v == 128, n_psi in {128, 256}, chunk 64.
+ *   in_dtype LA_F32 : d_k, d_v <= 128, n_psi <= 256 (LDS permitting),
+ *                     chunk in {16, 32, 64}, any psi.
+ *   always: d_v and n_psi multiples of 4 (16-byte state rows in the workspace).
  *   gamma: when given, at most LA_MAX_DECAY_HEADS heads.                        */
 #define LA_MAX_DECAY_HEADS 256
 

@@ -70,6 +70,12 @@ def _ws(desc):
     (dict(in_dtype=LA_F32, chunk=128), LA_ERR_UNSUPPORTED),
     (dict(), LA_OK), (dict(chunk=128), LA_OK), (dict(d_k=64, d_v=64, n_psi=64), LA_OK),
     (dict(in_dtype=LA_F32, d_k=64, d_v=64, n_psi=64, chunk=64), LA_OK),
+    # state rows must be whole 16-byte groups (the scan moves 4 floats per access)
+    (dict(in_dtype=LA_F32, d_k=30, d_v=30, n_psi=30, chunk=32, psi=0), LA_ERR_UNSUPPORTED),
+    (dict(in_dtype=LA_F32, d_k=32, d_v=32, n_psi=32, chunk=32, psi=0), LA_OK),
+    # positive random features: bf16 needs d 128, n_psi 128 or 256, chunk 64
+    (dict(psi=2, n_psi=256), LA_OK), (dict(psi=2, n_psi=128), LA_OK),
+    (dict(psi=2, n_psi=64), LA_ERR_UNSUPPORTED), (dict(psi=2, n_psi=256, chunk=128), LA_ERR_UNSUPPORTED),
 ])
 def test_prefill_validation(kw, status):
     st, _ = _ws(_desc(**kw))
@@ -86,6 +92,13 @@ def test_workspace_size_planner():
     assert st == LA_OK and n_big % (4 * E) == 0
     segs = n_big // (4 * E) // 64
     assert 1 <= segs <= 1024
+    # segments of at least 2048 tokens unless that leaves fewer than 256 workgroups:
+    # the 8k x 64-sequence shape gets 4 segments of 2048 tokens (256 workgroups)
+    st, n8 = _ws(_desc(B=4, H=16, T=8192))
+    assert st == LA_OK and n8 == 4 * E * 64 * 4
+    # a single short sequence still gets one segment per chunk up to 256 workgroups
+    st, n1s = _ws(_desc(B=1, H=1, T=4096))
+    assert st == LA_OK and n1s == 4 * E * 64
     # never more segments than chunks
     st, n_small = _ws(_desc(T=1, H=1))
     assert st == LA_OK and n_small == 4 * E
