@@ -22,8 +22,12 @@ SOURCES = ["la_api.cpp", "la_decode.hip", "la_scan.hip", "la_prefill_bf16.hip", 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
+# -amdgpu-mfma-vgpr-form: MFMA accumulators in ordinary VGPRs. The fp32 states are also
+# scaled and split by VALU code every chunk; with the accumulation-register form the compiler
+# copied every state tile between the two register files around each MFMA chain.
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-amdgpu-mfma-vgpr-form=true",
           "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 
