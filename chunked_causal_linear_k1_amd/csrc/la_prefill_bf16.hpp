@@ -819,21 +819,37 @@ __global__ __launch_bounds__(2 * D) void k_output_sh(PrefillParams p) {
 #pragma unroll
       for (int pt = 0; pt < D / 32; ++pt) S[pt] *= a;
     }
-    // S[pt] += K~^T V (M = state row, N = value column, k = token)
+    // S[pt] += K~^T V (M = state row, N = value column, k = token), software-pipelined:
+    // the operands of token step ik + 1 are read while the MFMAs of step ik run
+    {
+      constexpr int NK = C / 16, NM = (SPLIT ? 2 : 1) * (D / 32);
+      bf16x8 ops[2][1 + NM];  // [buffer][V, then K~ hi (and lo) per state-row tile]
+      auto load_ops = [&](bf16x8 (&o)[1 + NM], int ik) {
+        const int r0 = ik * 16, ko = r0 * D * 2;
+        o[0] = cat8(lds_read_tr4((const __bf16*)(vT + r0 * PV * 2)), lds_read_tr4((const __bf16*)(vT + (r0 + 4) * PV * 2)));
 #pragma unroll
-    for (int ik = 0; ik < C / 16; ++ik) {
-      const int r0 = ik * 16;
-      const bf16x8 vb8 = cat8(lds_read_tr4((const __bf16*)(vT + r0 * PV * 2)),
-                              lds_read_tr4((const __bf16*)(vT + (r0 + 4) * PV * 2)));
+        for (int pt = 0; pt < D / 32; ++pt) {
+          o[1 + (SPLIT ? 2 : 1) * pt] =
+              cat8(lds_read_tr4((const __bf16*)(kT[pt][0] + ko)), lds_read_tr4((const __bf16*)(kT[pt][1] + ko)));
+          if (SPLIT)
+            o[2 + 2 * pt] = cat8(lds_read_tr4((const __bf16*)(kT[pt][0] + ko + KLO)),
+                                 lds_read_tr4((const __bf16*)(kT[pt][1] + ko + KLO)));
+        }
+      };
+      load_ops(ops[0], 0);
 #pragma unroll
-      for (int pt = 0; pt < D / 32; ++pt) {
-        const int ko = r0 * D * 2;
-        S[pt] = mfma32(cat8(lds_read_tr4((const __bf16*)(kT[pt][0] + ko)), lds_read_tr4((const __bf16*)(kT[pt][1] + ko))),
-                       vb8, S[pt]);
-        if (SPLIT)
-          S[pt] = mfma32(cat8(lds_read_tr4((const __bf16*)(kT[pt][0] + ko + KLO)),
-                              lds_read_tr4((const __bf16*)(kT[pt][1] + ko + KLO))),
-                         vb8, S[pt]);
+      for (int ik = 0; ik < NK; ++ik) {
+        if (ik + 1 < NK) load_ops(ops[(ik + 1) & 1], ik + 1);
+        const bf16x8(&o)[1 + NM] = ops[ik & 1];
+#pragma unroll
+        for (int pt = 0; pt < D / 32; ++pt) {
+          S[pt] = mfma32(o[1 + (SPLIT ? 2 : 1) * pt], o[0], S[pt]);
+          if (SPLIT) S[pt] = mfma32(o[2 + 2 * pt], o[0], S[pt]);
+        }
+        if (ik + 1 < NK) {  // keep the next step's reads ahead of this step's MFMAs
+          __builtin_amdgcn_sched_group_barrier(0x100, 2 * (1 + NM), 0);  // LDS reads
+          __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);            // MFMA
+        }
       }
     }
   }
