@@ -24,7 +24,20 @@ static hipError_t dispatch(const PrefillParams& p, hipStream_t s, bool out) {
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_prefill_bf16_summary(const PrefillParams& p, hipStream_t s) { return dispatch(p, s, false); }
+// The segment summary (the decayed sum of psi(k_i) v_i^T over the segment's tokens) does
+// not depend on how the tokens are grouped, so at C = 128 it is folded in 64-token steps:
+// the 64-token kernel needs half the LDS, two workgroups share a CU and hide each other's
+// latency. Segment boundaries (multiples of seg_chunks * C tokens) are unchanged.
+hipError_t launch_prefill_bf16_summary(const PrefillParams& p, hipStream_t s) {
+  if (p.C == 128 && p.psi != LA_PSI_PRF) {
+    PrefillParams q = p;
+    q.C = 64;
+    q.n_chunks = (p.T + 63) / 64;
+    q.seg_chunks = 2 * p.seg_chunks;
+    return dispatch(q, s, false);
+  }
+  return dispatch(p, s, false);
+}
 hipError_t launch_prefill_bf16_output(const PrefillParams& p, hipStream_t s) { return dispatch(p, s, true); }
 
 }  // namespace la
