@@ -200,7 +200,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--no-extra", action="store_true", help="headline workload only (no 8k elu+1 line)")
+    ap.add_argument("--no-extra", action="store_true", help="headline workload only (no 8k elu+1 and PRF lines)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="first run one plain copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -245,15 +245,20 @@ def main():
         "roofline": roofline,
     }
     if not args.no_extra:
-        w8 = workloads.PREFILL_8K
-        p8 = bench_prefill(w8, args.steps, args.warmup)
-        a8 = BYTES_PER_TOKEN_HEAD * p8["units"] / (p8["ms_per_step"] * 1e-3) / 1e9
-        line["prefill_8k"] = {"workload": w8.name, "token_heads_per_s": round(p8["token_heads_per_s"], 1),
-                              "ms_per_step": round(p8["ms_per_step"], 4),
-                              "phase_ms": {k: round(v, 4) for k, v in p8["phase_ms"].items()},
-                              "whole_call_roofline": {"bound": "hbm", "achieved": round(a8, 1),
-                                                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                                      "frac": round(a8 / HBM_PEAK_GBS, 4)}}
+        for key, wx in (("prefill_8k", workloads.PREFILL_8K), ("prefill_prf_4k", workloads.PRF_4K)):
+            px = bench_prefill(wx, args.steps, args.warmup)
+            ax = BYTES_PER_TOKEN_HEAD * px["units"] / (px["ms_per_step"] * 1e-3) / 1e9
+            line[key] = {"workload": wx.name, "token_heads_per_s": round(px["token_heads_per_s"], 1),
+                         "ms_per_step": round(px["ms_per_step"], 4),
+                         "phase_ms": {k: round(v, 4) for k, v in px["phase_ms"].items()},
+                         "whole_call_roofline": {"bound": "hbm", "achieved": round(ax, 1), "peak": HBM_PEAK_GBS,
+                                                 "unit": "GB/s", "frac": round(ax / HBM_PEAK_GBS, 4)}}
+            if wx.psi == workloads.PSI_PRF:
+                # 286,720 algorithmic FLOP per token-head (features 4*256*128, local pass C*(256+128),
+                # state and output 4*256*128); bf16 MFMA dense peak 2.5 PFLOP/s
+                tf = 286720 * px["units"] / (px["ms_per_step"] * 1e-3) / 1e12
+                line[key]["mfma_roofline"] = {"bound": "mfma", "achieved": round(tf, 1), "peak": 2500.0,
+                                              "unit": "TFLOP/s", "frac": round(tf / 2500.0, 4)}
     if not args.no_decode:
         dw = workloads.DECODE_32x64
         for key, reps, note in (("decode", 1, "as configured: the 129 MiB state is re-read every step and can "

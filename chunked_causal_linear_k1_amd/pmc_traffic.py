@@ -23,12 +23,13 @@ from collections import defaultdict
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-KERNEL_SOURCES = ["la_prefill_bf16.hpp", "la_device.hpp", "la_scan.hip", "la_decode.hip"]
+KERNEL_SOURCES = ["la_prefill_bf16.hpp", "la_prefill_bf16.hip", "la_prefill_prf.hpp", "la_device.hpp", "la_scan.hip",
+                  "la_decode.hip", "la_api.cpp"]
 
 # kernel-name substring -> key in traffic.json
 KERNELS = {
     "k_output_sh<128, 128, true, false, false>": "k_output_retnet_128k",
-    "k_summary<128, 128, true, false, false>": "k_summary_retnet_128k",
+    "k_summary<64, 128, true, false, false>": "k_summary_retnet_128k",  # 128k summaries fold 64-token steps
     "k_segment_scan": "k_segment_scan",
     "k_decode": "k_decode_32x64",
 }
