@@ -855,13 +855,375 @@ __global__ __launch_bounds__(2 * D) void k_output_sh(PrefillParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// Output kernel with two waves per SIMD (8 waves per workgroup, d = 128, chunk 64).
+//
+// The LDS image of a 128-token chunk fills the CU, so occupancy must come from within the
+// workgroup. Waves w and w + 4 share value-column block cb = w % 4: each holds the full
+// 128 x 32 state slice S[:, cb] and performs the same state update (bitwise identical
+// results), and they split the output row tiles between them (tiles {0, 3} and {1, 2} at
+// C = 128, so both do the same amount of work). The score tiles are shared as before. The
+// duplicated state update costs MFMA issue slots, which are cheap here; in exchange the
+// second wave on each SIMD hides the LDS and MFMA latencies that a lone wave exposes.
+// Register diet for 256 per wave: decay factors of the score tiles are computed per tile,
+// S is split into hi + lo one state-row tile at a time, and each thread carries half as
+// many prefetched pieces.
+template <int C, int D, bool ELU>
+struct W8Geo {
+  using B = ShGeo<C, D, ELU>;
+  static constexpr int NWV = 8, NT = 64 * NWV;
+  static constexpr int NJ = B::NJ, NTILE = B::NTILE, JPR = NJ / 2;  // row tiles per wave
+  static constexpr int PQ = B::PQ, PV = B::PV, PA = B::PA, A_TILE = B::A_TILE, K_BYTES = B::K_BYTES;
+  static constexpr int OFF_Q = B::OFF_Q, OFF_K = B::OFF_K, OFF_A = B::OFF_A, OFF_V = B::OFF_V, OFF_F = B::OFF_F;
+  static constexpr int F_Z = 0;                 // Z [D]
+  static constexpr int F_ZRED = D;              // per-wave Z partials [NWV][D]
+  static constexpr int F_THETA = D + NWV * D;   // gamma^(j+1) [C]
+  static constexpr int F_R = F_THETA + C;       // per-tile score row sums [NTILE][32]
+  static constexpr int LDS_BYTES = OFF_F + 4 * (F_R + NTILE * 32);
+  static constexpr int PPR = D / 8;             // 16-byte pieces per token row
+  static constexpr int RSTEP = NT / PPR;        // rows between a thread's pieces
+  static constexpr int NPC = C * PPR / NT;      // pieces per thread per tile
+  // Used at C = 64 only: at C = 128 the duplicated state update's LDS reads (each wave
+  // reads all of K~ and its V columns) cost more than the second wave per SIMD saves
+  // (measured on the 128k retention workload: 3.36 ms against 3.03 ms with four waves).
+  static constexpr bool FITS = B::FITS && LDS_BYTES <= 160 * 1024 && D == 128 && C == 64;
+};
+
+template <int NPC>
+struct PiecesN {
+  uint4 r[NPC];
+};
+
+// Rows >= valid read as zeros (bounded buffer resource, no branches); piece i of the thread
+// at row prow + RSTEP i, columns pcol .. pcol + 7.
+template <int D, int NPC, int RSTEP>
+__device__ __forceinline__ void load_pieces_n(PiecesN<NPC>& P, const uint16_t* __restrict__ g, int valid, int prow,
+                                              int pcol) {
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(g, (uint32_t)valid * D * 2);
+  const uint32_t v0 = (uint32_t)(prow * D + pcol) * 2;
+#pragma unroll
+  for (int i = 0; i < NPC; ++i) P.r[i] = buf_load16(rs, v0, (uint32_t)(i * RSTEP * D * 2));
+}
+
+template <int C, int D, bool DECAY, bool NORM, bool ELU>
+__global__ __launch_bounds__(512) void k_output_w8(PrefillParams p) {
+  using G = W8Geo<C, D, ELU>;
+  static_assert(G::FITS, "8-wave layout");
+  static_assert(G::RSTEP % 16 == 0, "piece rows advance in multiples of 16 (swizzle period)");
+  constexpr bool SPLIT = DECAY || ELU;
+  constexpr int NJ = G::NJ, NWV = G::NWV, NPC = G::NPC, JPR = G::JPR, RSTEP = G::RSTEP;
+  constexpr int TPW = (G::NTILE + NWV - 1) / NWV;
+  constexpr int PQ = G::PQ, PV = G::PV, PA = G::PA;
+  constexpr int KLO = G::K_BYTES;
+  constexpr int ALO = 32 * PA * 2;
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int seg = blockIdx.x, bh = blockIdx.y, head = bh % p.H;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, n = lane & 31, hh = lane >> 5;
+  const int cb = w & 3, role = w >> 2;
+  const int L16 = lane & 15, g = lane >> 4;
+  const int Ew = 32 * cb;
+  const float lg = DECAY ? p.log2g[head] : 0.f;
+
+  const int prow = tid / G::PPR, pcol = (tid % G::PPR) * 8;
+  const int trow = 8 * (g >> 1) + (L16 >> 2), tcol = 16 * (g & 1) + 4 * (L16 & 3);
+  unsigned char* const qP = smem + pin(G::OFF_Q + (prow * PQ + pcol) * 2);
+  const unsigned char* const qC = smem + pin(G::OFF_Q + (n * PQ + 4 * hh) * 2);
+  const unsigned char* const qS = smem + pin(G::OFF_Q + (n * PQ + 8 * hh) * 2);
+  const unsigned char* const qZ = smem + pin(G::OFF_Q + (n * PQ + hh * (D / 2)) * 2);
+  unsigned char* const kP = smem + pin(G::OFF_K + swz_off<D>(prow, pcol) * 2);
+  const unsigned char* kR[D / 16];
+  const unsigned char* kT[D / 32][2];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) kR[kk] = smem + pin(G::OFF_K + swz_off<D>(n, 16 * kk + 8 * hh) * 2);
+#pragma unroll
+  for (int pt = 0; pt < D / 32; ++pt) {
+    kT[pt][0] = smem + pin(G::OFF_K + swz_off<D>(trow, 32 * pt + tcol) * 2);
+    kT[pt][1] = smem + pin(G::OFF_K + swz_off<D>(trow + 4, 32 * pt + tcol) * 2);
+  }
+  unsigned char* const vP = smem + pin(G::OFF_V + (prow * PV + pcol) * 2);
+  const unsigned char* const vT = smem + pin(G::OFF_V + (trow * PV + Ew + tcol) * 2);
+  unsigned char* const aW = smem + pin(G::OFF_A + (n * PA + 4 * hh) * 2);
+  const unsigned char* const aR = smem + pin(G::OFF_A + (n * PA + 8 * hh) * 2);
+  float* const sF = (float*)(smem + pin(G::OFF_F));
+  float* const fN = (float*)(smem + pin(G::OFF_F + 4 * n));
+
+  const size_t E = (size_t)D * D + D;
+  const float* pre = p.ws + ((size_t)bh * p.n_seg + seg) * E;
+  f32x16 S[D / 32];
+#pragma unroll
+  for (int pt = 0; pt < D / 32; ++pt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) S[pt][r] = pre[(size_t)(pt * 32 + dtile_row(r, lane)) * D + Ew + n];
+  if (tid < D) sF[G::F_Z + tid] = NORM ? pre[(size_t)D * D + tid] : 0.f;
+  for (int j = tid; j < C; j += G::NT) sF[G::F_THETA + j] = DECAY ? exp2f((float)(j + 1) * lg) : 1.f;
+
+  const uint16_t* qb = (const uint16_t*)p.q + (size_t)bh * p.T * D;
+  const uint16_t* kb = (const uint16_t*)p.k + (size_t)bh * p.T * D;
+  const uint16_t* vb = (const uint16_t*)p.v + (size_t)bh * p.T * D;
+  float* ob = (float*)p.o + (size_t)bh * p.T * D;
+  const int c0 = seg * p.seg_chunks, c1 = min(c0 + p.seg_chunks, p.n_chunks);
+
+  PiecesN<NPC> pq, pk, pv;
+  {
+    const int L0 = min(C, p.T - c0 * C);
+    load_pieces_n<D, NPC, RSTEP>(pq, qb + (size_t)c0 * C * D, L0, prow, pcol);
+    load_pieces_n<D, NPC, RSTEP>(pk, kb + (size_t)c0 * C * D, L0, prow, pcol);
+    load_pieces_n<D, NPC, RSTEP>(pv, vb + (size_t)c0 * C * D, L0, prow, pcol);
+    vm_drain();
+  }
+  for (int c = c0; c < c1; ++c) {
+    const int t0 = c * C, L = min(C, p.T - t0);
+    const float a = DECAY ? exp2f((float)L * lg) : 1.f;
+    lds_barrier();  // the previous chunk is done with LDS (and Z is updated)
+
+    // ---- commit (see k_output_sh)
+    float zp[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) zp[j] = 0.f;
+#pragma unroll
+    for (int i = 0; i < NPC; ++i) {
+      uint4 raw = pq.r[i];
+      if (ELU) {
+        const bf16x8 x = __builtin_bit_cast(bf16x8, raw);
+        bf16x8 y;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) y[j] = to_bf16(elu1(from_bf16(x[j])));
+        raw = __builtin_bit_cast(uint4, y);
+      }
+      *(uint4*)(qP + i * RSTEP * PQ * 2) = raw;
+    }
+#pragma unroll
+    for (int i = 0; i < NPC; ++i) {
+      const int off = i * RSTEP * D * 2;
+      if (!ELU && !NORM) {
+        *(uint4*)(kP + off) = pk.r[i];
+        continue;
+      }
+      const int row = prow + RSTEP * i;
+      const float live = row < L ? 1.f : 0.f;
+      const float xi = DECAY ? live * exp2f((float)(L - 1 - row) * lg) : live;
+      const bf16x8 x = __builtin_bit_cast(bf16x8, pk.r[i]);
+      float f[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        f[j] = ELU ? elu1(from_bf16(x[j])) * live : from_bf16(x[j]);
+        if (NORM) zp[j] += f[j] * xi;
+      }
+      if (ELU) {
+        bf16x8 hi, lo;
+        split8_trunc(f, hi, lo);
+        *(bf16x8*)(kP + off) = hi;
+        *(bf16x8*)(kP + off + KLO) = lo;
+      } else {
+        *(uint4*)(kP + off) = pk.r[i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NPC; ++i) *(uint4*)(vP + i * RSTEP * PV * 2) = pv.r[i];
+    const bool more = c + 1 < c1;
+    const int Ln = more ? min(C, p.T - (c + 1) * C) : 0;
+    load_pieces_n<D, NPC, RSTEP>(pq, qb + (size_t)(c + 1) * C * D, Ln, prow, pcol);
+    load_pieces_n<D, NPC, RSTEP>(pk, kb + (size_t)(c + 1) * C * D, Ln, prow, pcol);
+    load_pieces_n<D, NPC, RSTEP>(pv, vb + (size_t)(c + 1) * C * D, Ln, prow, pcol);
+    lds_barrier();
+
+    // ---- score tiles (shared): wave w computes tiles w, w + 8, ...; decay factors per tile
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      const int t = w + u * NWV;
+      if (t >= G::NTILE) break;
+      const int jt = tile_jt(t), it = t - jt * (jt + 1) / 2;
+      bf16x8 ka[D / 16], qv[D / 16];
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        ka[kk] = *(const bf16x8*)(kR[kk] + it * 32 * D * 2);
+        qv[kk] = *(const bf16x8*)(qS + (jt * 32 * PQ + kk * 16) * 2);
+      }
+      f32x16 acc = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) acc = mfma32(ka[kk], qv[kk], acc);
+      const bool diag = it == jt;
+      float av[16];
+      float rs = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int ir = dtile_row(r, lane);
+        float f;
+        if constexpr (DECAY) f = (diag && ir > n) ? 0.f : exp2f((float)(32 * (jt - it) + n - ir) * lg);
+        else f = (diag && ir > n) ? 0.f : 1.f;
+        av[r] = acc[r] * f;
+        if (NORM) rs += av[r];
+      }
+      if (NORM) {
+        rs += __shfl_xor(rs, 32);
+        if (hh == 0) fN[G::F_R + t * 32] = rs;
+      }
+      unsigned char* at = aW + t * G::A_TILE;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        bf16x8 h8, l8;
+        split8_trunc(av + 8 * q, h8, l8);
+        const u32x4 hv = __builtin_bit_cast(u32x4, h8), lv = __builtin_bit_cast(u32x4, l8);
+        *(uint2*)(at + 32 * q) = make_uint2(hv[0], hv[1]);
+        *(uint2*)(at + 32 * q + 16) = make_uint2(hv[2], hv[3]);
+        *(uint2*)(at + 32 * q + ALO) = make_uint2(lv[0], lv[1]);
+        *(uint2*)(at + 32 * q + 16 + ALO) = make_uint2(lv[2], lv[3]);
+      }
+    }
+    lds_barrier();
+
+    // ---- outputs of this wave's row tiles jt(role, j) = role, NJ - 1 - role for its value
+    // columns, transposed as in k_output_sh; S split one state-row tile at a time
+    const __amdgpu_buffer_rsrc_t ors = make_rsrc(ob + (size_t)t0 * D, (uint32_t)L * D * 4);
+    f32x16 num[JPR];
+#pragma unroll
+    for (int j = 0; j < JPR; ++j) num[j] = f32x16{};
+#pragma unroll
+    for (int pt = 0; pt < D / 32; ++pt) {
+      bf16x8 sh[2], sl[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        float x[8];
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) x[jj] = S[pt][8 * q + jj];
+        split8_trunc(x, sh[q], sl[q]);
+      }
+#pragma unroll
+      for (int j = 0; j < JPR; ++j) {
+        const int jt = j == 0 ? role : NJ - 1 - role;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const unsigned char* qa = qC + (jt * 32 * PQ + pt * 32 + 16 * q) * 2;
+          const bf16x8 qo = cat8(*(const bf16x4*)qa, *(const bf16x4*)(qa + 16));
+          num[j] = mfma32(sh[q], qo, num[j]);
+          num[j] = mfma32(sl[q], qo, num[j]);
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < JPR; ++j) {
+      const int jt = j == 0 ? role : NJ - 1 - role;
+      if (DECAY) num[j] *= fN[G::F_THETA + jt * 32];
+      // numT += V^T A^T for it <= jt (the trip count depends on the role: a wave-uniform loop)
+      for (int it = 0; it <= jt; ++it) {
+        const unsigned char* at = aR + (jt * (jt + 1) / 2 + it) * G::A_TILE;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int r0 = it * 32 + 16 * q;
+          const bf16x8 vv = cat8(lds_read_tr4((const __bf16*)(vT + r0 * PV * 2)),
+                                 lds_read_tr4((const __bf16*)(vT + (r0 + 4) * PV * 2)));
+          num[j] = mfma32(vv, *(const bf16x8*)(at + 32 * q), num[j]);
+          num[j] = mfma32(vv, *(const bf16x8*)(at + 32 * q + ALO), num[j]);
+        }
+      }
+      float inv = 1.f;
+      if (NORM) {
+        float qz = 0.f;
+        const unsigned char* qr = qZ + jt * 32 * PQ * 2;
+        const f32x4* zr = (const f32x4*)(sF + G::F_Z + hh * (D / 2));
+#pragma unroll
+        for (int e8 = 0; e8 < D / 2; e8 += 8) {
+          const bf16x8 qv = *(const bf16x8*)(qr + e8 * 2);
+          const f32x4 z0 = zr[e8 / 4], z1 = zr[e8 / 4 + 1];
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) qz += from_bf16(qv[jj]) * z0[jj] + from_bf16(qv[4 + jj]) * z1[jj];
+        }
+        qz += __shfl_xor(qz, 32);
+        float r = 0.f;
+        for (int it = 0; it <= jt; ++it) r += fN[G::F_R + (jt * (jt + 1) / 2 + it) * 32];
+        inv = 1.f / (fN[G::F_THETA + jt * 32] * qz + r + p.eps);
+      }
+      const uint32_t row_off = (uint32_t)((jt * 32 + n) * D + Ew + 4 * hh) * 4;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const u32x4 v4 = {__float_as_uint(num[j][4 * q4] * inv), __float_as_uint(num[j][4 * q4 + 1] * inv),
+                          __float_as_uint(num[j][4 * q4 + 2] * inv), __float_as_uint(num[j][4 * q4 + 3] * inv)};
+        __builtin_amdgcn_raw_buffer_store_b128(v4, ors, row_off + 32 * q4, 0, 0);
+      }
+    }
+
+    // ---- state update (every wave: its value columns, all state rows)
+    if (NORM) reduce_zp<D>(zp, sF + G::F_ZRED);
+    if (DECAY) {
+      lds_barrier();  // every wave is done with the score tiles (K lo aliases them) and K
+#pragma unroll
+      for (int i = 0; i < NPC; ++i) {
+        const int row = prow + RSTEP * i, off = i * RSTEP * D * 2;
+        const float xi = row < L ? exp2f((float)(L - 1 - row) * lg) : 0.f;
+        const bf16x8 h8 = *(const bf16x8*)(kP + off);
+        float x[8];
+        if (ELU) {
+          const bf16x8 l8 = *(const bf16x8*)(kP + off + KLO);
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) x[jj] = (from_bf16(h8[jj]) + from_bf16(l8[jj])) * xi;
+        } else {
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) x[jj] = from_bf16(h8[jj]) * xi;
+        }
+        bf16x8 hi, lo;
+        split8_trunc(x, hi, lo);
+        *(bf16x8*)(kP + off) = hi;
+        *(bf16x8*)(kP + off + KLO) = lo;
+      }
+    }
+    lds_barrier();
+    if (NORM && tid < D) {
+      float z = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < NWV; ++ww) z += sF[G::F_ZRED + ww * D + tid];
+      sF[G::F_Z + tid] = a * sF[G::F_Z + tid] + z;
+    }
+    if (DECAY) {
+#pragma unroll
+      for (int pt = 0; pt < D / 32; ++pt) S[pt] *= a;
+    }
+    {
+      constexpr int NK = C / 16, NM = (SPLIT ? 2 : 1) * (D / 32);
+      bf16x8 ops[2][1 + NM];
+      auto load_ops = [&](bf16x8 (&o)[1 + NM], int ik) {
+        const int r0 = ik * 16, ko = r0 * D * 2;
+        o[0] = cat8(lds_read_tr4((const __bf16*)(vT + r0 * PV * 2)), lds_read_tr4((const __bf16*)(vT + (r0 + 4) * PV * 2)));
+#pragma unroll
+        for (int pt = 0; pt < D / 32; ++pt) {
+          o[1 + (SPLIT ? 2 : 1) * pt] =
+              cat8(lds_read_tr4((const __bf16*)(kT[pt][0] + ko)), lds_read_tr4((const __bf16*)(kT[pt][1] + ko)));
+          if (SPLIT)
+            o[2 + 2 * pt] = cat8(lds_read_tr4((const __bf16*)(kT[pt][0] + ko + KLO)),
+                                 lds_read_tr4((const __bf16*)(kT[pt][1] + ko + KLO)));
+        }
+      };
+      load_ops(ops[0], 0);
+#pragma unroll
+      for (int ik = 0; ik < NK; ++ik) {
+        if (ik + 1 < NK) load_ops(ops[(ik + 1) & 1], ik + 1);
+        const bf16x8(&o)[1 + NM] = ops[ik & 1];
+#pragma unroll
+        for (int pt = 0; pt < D / 32; ++pt) {
+          S[pt] = mfma32(o[1 + (SPLIT ? 2 : 1) * pt], o[0], S[pt]);
+          if (SPLIT) S[pt] = mfma32(o[2 + 2 * pt], o[0], S[pt]);
+        }
+        if (ik + 1 < NK) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 2 * (1 + NM), 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
+        }
+      }
+    }
+  }
+}
+
 template <int C, int D, bool DECAY, bool NORM, bool ELU>
 hipError_t launch_flags(const PrefillParams& p, hipStream_t s, bool out) {
   const void* kern = (const void*)k_summary<C, D, DECAY, NORM, ELU>;
   int lds = Geo<C, D, false>::LDS_BYTES;
+  int threads = 2 * D;
   if (out) {
-    // the shared-score kernel where its LDS fits, else every wave computes its own scores
-    if constexpr (ShGeo<C, D, ELU>::FITS) {
+    // the two-waves-per-SIMD kernel where it applies, else the shared-score kernel where its
+    // LDS fits, else every wave computes its own scores
+    if constexpr (W8Geo<C, D, ELU>::FITS) {
+      kern = (const void*)k_output_w8<C, D, DECAY, NORM, ELU>;
+      lds = W8Geo<C, D, ELU>::LDS_BYTES;
+      threads = W8Geo<C, D, ELU>::NT;
+    } else if constexpr (ShGeo<C, D, ELU>::FITS) {
       kern = (const void*)k_output_sh<C, D, DECAY, NORM, ELU>;
       lds = ShGeo<C, D, ELU>::LDS_BYTES;
     } else {
@@ -873,7 +1235,7 @@ hipError_t launch_flags(const PrefillParams& p, hipStream_t s, bool out) {
   if (e != hipSuccess) return e;
   dim3 grid(p.n_seg, p.B * p.H);
   void* args[] = {(void*)&p};
-  e = hipLaunchKernel(kern, grid, dim3(2 * D), args, lds, s);
+  e = hipLaunchKernel(kern, grid, dim3(threads), args, lds, s);
   if (e != hipSuccess) return e;
   return hipGetLastError();
 }
