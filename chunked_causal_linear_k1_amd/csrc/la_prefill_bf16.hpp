@@ -479,7 +479,7 @@ struct ShGeo {
   static constexpr int NTILE = NJ * (NJ + 1) / 2;
   static constexpr int PQ = D + 8;          // Q: row reads
   static constexpr int PK = D;              // K (and K lo): XOR-swizzled, see swz_off
-  static constexpr int PV = D + 16;         // V: transpose reads
+  static constexpr int PV = D;              // V: XOR-swizzled like K (transpose reads)
   static constexpr int PA = 40;             // score tiles: 32 x 32, row pitch 40
   static constexpr int A_TILE = 2 * 32 * PA * 2;  // hi + lo, bytes
   static constexpr int Q_BYTES = C * PQ * 2;
@@ -565,8 +565,9 @@ __global__ __launch_bounds__(2 * D) void k_output_sh(PrefillParams p) {
     kT[pt][0] = smem + pin(G::OFF_K + swz_off<D>(trow, 32 * pt + tcol) * 2);
     kT[pt][1] = smem + pin(G::OFF_K + swz_off<D>(trow + 4, 32 * pt + tcol) * 2);
   }
-  unsigned char* const vP = smem + pin(G::OFF_V + (prow * PV + pcol) * 2);
-  const unsigned char* const vT = smem + pin(G::OFF_V + (trow * PV + Ew + tcol) * 2);
+  unsigned char* const vP = smem + pin(G::OFF_V + swz_off<D>(prow, pcol) * 2);
+  const unsigned char* const vT0 = smem + pin(G::OFF_V + swz_off<D>(trow, Ew + tcol) * 2);
+  const unsigned char* const vT1 = smem + pin(G::OFF_V + swz_off<D>(trow + 4, Ew + tcol) * 2);
   unsigned char* const aW = smem + pin(G::OFF_A + (n * PA + 4 * hh) * 2);
   const unsigned char* const aR = smem + pin(G::OFF_A + (n * PA + 8 * hh) * 2);
   float* const sF = (float*)(smem + pin(G::OFF_F));
@@ -656,7 +657,7 @@ __global__ __launch_bounds__(2 * D) void k_output_sh(PrefillParams p) {
       }
     }
 #pragma unroll
-    for (int i = 0; i < NPC; ++i) *(uint4*)(vP + i * 16 * PV * 2) = pv.r[i];
+    for (int i = 0; i < NPC; ++i) *(uint4*)(vP + i * 16 * D * 2) = pv.r[i];
     const bool more = c + 1 < c1;
     const int Ln = more ? min(C, p.T - (c + 1) * C) : 0;
     // next chunk's tiles stream in during this chunk's matrix work (rows past Ln read as
@@ -749,8 +750,8 @@ __global__ __launch_bounds__(2 * D) void k_output_sh(PrefillParams p) {
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
           const int r0 = it * 32 + 16 * q;
-          const bf16x8 vv = cat8(lds_read_tr4((const __bf16*)(vT + r0 * PV * 2)),
-                                 lds_read_tr4((const __bf16*)(vT + (r0 + 4) * PV * 2)));
+          const bf16x8 vv = cat8(lds_read_tr4((const __bf16*)(vT0 + r0 * D * 2)),
+                                 lds_read_tr4((const __bf16*)(vT1 + r0 * D * 2)));
           num = mfma32(vv, *(const bf16x8*)(at + 32 * q), num);
           num = mfma32(vv, *(const bf16x8*)(at + 32 * q + ALO), num);
         }
@@ -826,7 +827,7 @@ __global__ __launch_bounds__(2 * D) void k_output_sh(PrefillParams p) {
       bf16x8 ops[2][1 + NM];  // [buffer][V, then K~ hi (and lo) per state-row tile]
       auto load_ops = [&](bf16x8 (&o)[1 + NM], int ik) {
         const int r0 = ik * 16, ko = r0 * D * 2;
-        o[0] = cat8(lds_read_tr4((const __bf16*)(vT + r0 * PV * 2)), lds_read_tr4((const __bf16*)(vT + (r0 + 4) * PV * 2)));
+        o[0] = cat8(lds_read_tr4((const __bf16*)(vT0 + r0 * D * 2)), lds_read_tr4((const __bf16*)(vT1 + r0 * D * 2)));
 #pragma unroll
         for (int pt = 0; pt < D / 32; ++pt) {
           o[1 + (SPLIT ? 2 : 1) * pt] =
@@ -940,8 +941,9 @@ __global__ __launch_bounds__(512) void k_output_w8(PrefillParams p) {
     kT[pt][0] = smem + pin(G::OFF_K + swz_off<D>(trow, 32 * pt + tcol) * 2);
     kT[pt][1] = smem + pin(G::OFF_K + swz_off<D>(trow + 4, 32 * pt + tcol) * 2);
   }
-  unsigned char* const vP = smem + pin(G::OFF_V + (prow * PV + pcol) * 2);
-  const unsigned char* const vT = smem + pin(G::OFF_V + (trow * PV + Ew + tcol) * 2);
+  unsigned char* const vP = smem + pin(G::OFF_V + swz_off<D>(prow, pcol) * 2);
+  const unsigned char* const vT0 = smem + pin(G::OFF_V + swz_off<D>(trow, Ew + tcol) * 2);
+  const unsigned char* const vT1 = smem + pin(G::OFF_V + swz_off<D>(trow + 4, Ew + tcol) * 2);
   unsigned char* const aW = smem + pin(G::OFF_A + (n * PA + 4 * hh) * 2);
   const unsigned char* const aR = smem + pin(G::OFF_A + (n * PA + 8 * hh) * 2);
   float* const sF = (float*)(smem + pin(G::OFF_F));
@@ -1019,7 +1021,7 @@ __global__ __launch_bounds__(512) void k_output_w8(PrefillParams p) {
       }
     }
 #pragma unroll
-    for (int i = 0; i < NPC; ++i) *(uint4*)(vP + i * RSTEP * PV * 2) = pv.r[i];
+    for (int i = 0; i < NPC; ++i) *(uint4*)(vP + i * RSTEP * D * 2) = pv.r[i];
     const bool more = c + 1 < c1;
     const int Ln = more ? min(C, p.T - (c + 1) * C) : 0;
     load_pieces_n<D, NPC, RSTEP>(pq, qb + (size_t)(c + 1) * C * D, Ln, prow, pcol);
@@ -1110,8 +1112,8 @@ __global__ __launch_bounds__(512) void k_output_w8(PrefillParams p) {
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
           const int r0 = it * 32 + 16 * q;
-          const bf16x8 vv = cat8(lds_read_tr4((const __bf16*)(vT + r0 * PV * 2)),
-                                 lds_read_tr4((const __bf16*)(vT + (r0 + 4) * PV * 2)));
+          const bf16x8 vv = cat8(lds_read_tr4((const __bf16*)(vT0 + r0 * D * 2)),
+                                 lds_read_tr4((const __bf16*)(vT1 + r0 * D * 2)));
           num[j] = mfma32(vv, *(const bf16x8*)(at + 32 * q), num[j]);
           num[j] = mfma32(vv, *(const bf16x8*)(at + 32 * q + ALO), num[j]);
         }
@@ -1182,7 +1184,7 @@ __global__ __launch_bounds__(512) void k_output_w8(PrefillParams p) {
       bf16x8 ops[2][1 + NM];
       auto load_ops = [&](bf16x8 (&o)[1 + NM], int ik) {
         const int r0 = ik * 16, ko = r0 * D * 2;
-        o[0] = cat8(lds_read_tr4((const __bf16*)(vT + r0 * PV * 2)), lds_read_tr4((const __bf16*)(vT + (r0 + 4) * PV * 2)));
+        o[0] = cat8(lds_read_tr4((const __bf16*)(vT0 + r0 * D * 2)), lds_read_tr4((const __bf16*)(vT1 + r0 * D * 2)));
 #pragma unroll
         for (int pt = 0; pt < D / 32; ++pt) {
           o[1 + (SPLIT ? 2 : 1) * pt] =
