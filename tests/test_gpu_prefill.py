@@ -62,6 +62,9 @@ SMALL = [
     ("elu1_decay_norm_d64_c128", 1, 2, 700, 64, 128, PSI_ELU1, 1, "const:0.99", "bf16"),
     ("elu1_decay_norm_c64", 1, 2, 1500, 128, 64, PSI_ELU1, 1, "const:0.999", "bf16"),
     ("identity_norm_nodecay", 1, 2, 333, 128, 64, PSI_IDENTITY, 0, "none", "bf16"),
+    # identity features with a denominator are ill-conditioned (psi(q).Z can cross zero), so
+    # the retention form is the identity case tested at C = 64, d = 128 as well
+    ("identity_decay_c64_d128", 1, 3, 901, 128, 64, PSI_IDENTITY, 0, "retnet_spread", "bf16"),
     ("f32_elu1_c32", 1, 2, 300, 64, 32, PSI_ELU1, 1, "none", "f32"),
     ("f32_identity_decay_c16", 1, 2, 200, 32, 16, PSI_IDENTITY, 0, "const:0.9", "f32"),
 ]
@@ -122,6 +125,26 @@ def test_initial_and_final_state():
     assert_close(o.cpu().reshape(4, w.T, 128).numpy(), ref, "bf16", "o with init state")
     assert_close(fS.cpu().reshape(4, 128, 128).numpy(), rS, "bf16", "final S")
     assert_close(fZ.cpu().reshape(4, 128).numpy(), rZ, "bf16", "final Z")
+
+
+def test_initial_and_final_state_c64():
+    """The same hand-off at C = 64 (the two-waves-per-SIMD output kernel), per-head decay."""
+    w = Workload(name="state_c64", B=2, H=3, T=777, d_k=128, d_v=128, n_psi=128, chunk=64, psi=PSI_ELU1,
+                 normalize=1, eps=1e-6, dtype="bf16", seed=6, qk_scale=0.5, v_scale=1.0, decay="retnet_spread")
+    announce("prefill init/final state C=64")
+    inp = inputs.make_prefill_inputs(w, device="cpu")
+    rng = np.random.default_rng(8)
+    S0 = (rng.standard_normal((2, 3, 128, 128)) * 0.5).astype(np.float32)
+    Z0 = (np.abs(rng.standard_normal((2, 3, 128))) * 10 + 1).astype(np.float32)
+    fS = torch.empty((2, 3, 128, 128), dtype=torch.float32, device=DEV)
+    fZ = torch.empty((2, 3, 128), dtype=torch.float32, device=DEV)
+    o = _run(w, inp, init_S=torch.from_numpy(S0).to(DEV), init_Z=torch.from_numpy(Z0).to(DEV), final_S=fS,
+             final_Z=fZ)
+    ref, rS, rZ = _oracle_o(w, inp, S0=S0.reshape(6, 128, 128).astype(np.float64),
+                            Z0=Z0.reshape(6, 128).astype(np.float64), want_state=True)
+    assert_close(o.cpu().reshape(6, w.T, 128).numpy(), ref, "bf16", "o with init state, C=64")
+    assert_close(fS.cpu().reshape(6, 128, 128).numpy(), rS, "bf16", "final S, C=64")
+    assert_close(fZ.cpu().reshape(6, 128).numpy(), rZ, "bf16", "final Z, C=64")
 
 
 def test_causality_and_determinism():
