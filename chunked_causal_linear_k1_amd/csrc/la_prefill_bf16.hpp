@@ -501,10 +501,11 @@ struct ShGeo {
   static constexpr bool FITS = LDS_BYTES <= 160 * 1024;
 };
 
-// tile t <-> (it, jt) with it <= jt, t = jt (jt + 1) / 2 + it
+// tile t <-> (it, jt) with it <= jt, t = jt (jt + 1) / 2 + it; branch-free (up to 16 row tiles)
 __device__ __forceinline__ int tile_jt(int t) {
   int jt = 0;
-  while ((jt + 1) * (jt + 2) / 2 <= t) ++jt;
+#pragma unroll
+  for (int k = 1; k < 16; ++k) jt += t >= k * (k + 1) / 2;
   return jt;
 }
 
@@ -669,11 +670,10 @@ __global__ __launch_bounds__(2 * D) void k_output_sh(PrefillParams p) {
     lds_barrier();
 
     // ---- score tiles A^T (M = i, N = j, k = feature), masked, decayed, split into hi + lo
-    // and shared through LDS: wave w computes tiles w, w + NW, ...
-#pragma unroll
-    for (int u = 0; u < TPW; ++u) {
-      const int t = w + u * NW;
-      if (t >= G::NTILE) break;
+    // and shared through LDS: wave w computes tiles w, w + NW, ... Software-pipelined: the
+    // MFMA chain of the next tile is interleaved with the epilogue (mask, decay, split, LDS
+    // writes) of the current one, so the VALU work fills the chain's latency.
+    auto score_chain = [&](int t) {
       const int jt = tile_jt(t), it = t - jt * (jt + 1) / 2;
       bf16x8 ka[D / 16], qv[D / 16];
 #pragma unroll
@@ -684,6 +684,10 @@ __global__ __launch_bounds__(2 * D) void k_output_sh(PrefillParams p) {
       f32x16 acc = f32x16{};
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) acc = mfma32(ka[kk], qv[kk], acc);
+      return acc;
+    };
+    auto score_epilogue = [&](int t, const f32x16& acc) {
+      const int jt = tile_jt(t), it = t - jt * (jt + 1) / 2;
       const bool diag = it == jt;
       const float tf = (DECAY && !diag) ? exp2f((float)(32 * (jt - it - 1)) * lg) : 1.f;
       float av[16];
@@ -710,6 +714,30 @@ __global__ __launch_bounds__(2 * D) void k_output_sh(PrefillParams p) {
         *(uint2*)(at + 32 * q + ALO) = make_uint2(lv[0], lv[1]);
         *(uint2*)(at + 32 * q + 16 + ALO) = make_uint2(lv[2], lv[3]);
       }
+    };
+    // Every wave runs TPW tiles, so the phase is straight-line code the schedule can
+    // interleave: a wave with fewer tiles recomputes the last tile and writes the same
+    // bytes to the same place as the wave that owns it (it would wait at the barrier anyway).
+    static_assert(G::NTILE >= NW, "every wave has a score tile");
+    {
+      f32x16 prev = score_chain(w);
+      int tp = w;
+#pragma unroll
+      for (int u = 1; u < TPW; ++u) {
+        const int t = min(w + u * NW, G::NTILE - 1);
+        const f32x16 cur = score_chain(t);
+        score_epilogue(tp, prev);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * (D / 16), 0);  // the next tile's operands
+#pragma unroll
+        for (int i = 0; i < D / 16; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA of the next tile
+          __builtin_amdgcn_sched_group_barrier(0x002, 14, 0);  // epilogue VALU of this one
+        }
+        __builtin_amdgcn_sched_group_barrier(0x200, 8, 0);     // its LDS writes
+        prev = cur;
+        tp = t;
+      }
+      score_epilogue(tp, prev);
     }
     lds_barrier();
 
