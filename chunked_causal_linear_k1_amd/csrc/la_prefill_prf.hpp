@@ -183,6 +183,41 @@ __device__ __forceinline__ bf16x8 psik_tr(const PsiKBases<NP>& b, int row0, int 
   return cat8(lds_read_tr4((const __bf16*)(b.tr[pt & 3][0] + o)), lds_read_tr4((const __bf16*)(b.tr[pt & 3][1] + o)));
 }
 
+// S[pt] += K~^T V over the chunk (M = feature, N = value column, k = token), software-
+// pipelined in steps of (16 tokens, up to 4 feature tiles): the operands of the next step
+// are read from LDS while the current step's MFMAs run.
+template <int C, int D, int NP, int LO, int PV>
+__device__ __forceinline__ void state_update_prf(f32x16 (&S)[NP / 32], const PsiKBases<NP>& kb8,
+                                                 const unsigned char* vT) {
+  constexpr int NFT = NP / 32, PTS = NFT < 4 ? NFT : 4, HALVES = NFT / PTS, NSTEP = (C / 16) * HALVES;
+  bf16x8 ops[2][1 + 2 * PTS];  // [buffer][V, then psi(K) hi, lo per feature tile of the step]
+  auto load_step = [&](bf16x8 (&o)[1 + 2 * PTS], int st) {
+    const int r0 = (st / HALVES) * 16, p0 = (st % HALVES) * PTS;
+    o[0] = cat8(lds_read_tr4((const __bf16*)(vT + r0 * PV * 2)), lds_read_tr4((const __bf16*)(vT + (r0 + 4) * PV * 2)));
+#pragma unroll
+    for (int j = 0; j < PTS; ++j) {
+      o[1 + 2 * j] = psik_tr<NP>(kb8, r0, p0 + j, 0);
+      o[2 + 2 * j] = psik_tr<NP>(kb8, r0, p0 + j, LO);
+    }
+  };
+  load_step(ops[0], 0);
+#pragma unroll
+  for (int st = 0; st < NSTEP; ++st) {
+    if (st + 1 < NSTEP) load_step(ops[(st + 1) & 1], st + 1);
+    const bf16x8(&o)[1 + 2 * PTS] = ops[st & 1];
+    const int p0 = (st % HALVES) * PTS;
+#pragma unroll
+    for (int j = 0; j < PTS; ++j) {
+      S[p0 + j] = mfma32(o[1 + 2 * j], o[0], S[p0 + j]);
+      S[p0 + j] = mfma32(o[2 + 2 * j], o[0], S[p0 + j]);
+    }
+    if (st + 1 < NSTEP) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * (1 + 2 * PTS), 0);  // next step's reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * PTS, 0);            // this step's MFMAs
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------------------
 // Segment summaries: per (sequence, segment), S = sum over the segment's tokens of
 // gamma^(seg_end-1-i) psi(k_i) v_i^T and Z likewise, written to the workspace.
@@ -283,17 +318,7 @@ __global__ __launch_bounds__(2 * D) void k_summary_prf(PrefillParams p) {
       for (int pt = 0; pt < NFT; ++pt) S[pt] *= a;
     }
     // S[pt] += K~^T V (M = feature, N = value column, k = token)
-#pragma unroll
-    for (int ik = 0; ik < C / 16; ++ik) {
-      const int r0 = ik * 16;
-      const bf16x8 vb8 = cat8(lds_read_tr4((const __bf16*)(vT + r0 * PV * 2)),
-                              lds_read_tr4((const __bf16*)(vT + (r0 + 4) * PV * 2)));
-#pragma unroll
-      for (int pt = 0; pt < NFT; ++pt) {
-        S[pt] = mfma32(psik_tr<NP>(kb8, r0, pt, 0), vb8, S[pt]);
-        S[pt] = mfma32(psik_tr<NP>(kb8, r0, pt, LO), vb8, S[pt]);
-      }
-    }
+    state_update_prf<C, D, NP, LO, PV>(S, kb8, vT);
   }
   // segment summary -> workspace [bh][seg][E], E = NP*D + NP
   const size_t E = (size_t)NP * D + NP;
@@ -584,17 +609,7 @@ __global__ __launch_bounds__(2 * D) void k_output_prf(PrefillParams p) {
 #pragma unroll
       for (int pt = 0; pt < NFT; ++pt) S[pt] *= a;
     }
-#pragma unroll
-    for (int ik = 0; ik < C / 16; ++ik) {
-      const int r0 = ik * 16;
-      const bf16x8 vb8 = cat8(lds_read_tr4((const __bf16*)(vT + r0 * PV * 2)),
-                              lds_read_tr4((const __bf16*)(vT + (r0 + 4) * PV * 2)));
-#pragma unroll
-      for (int pt = 0; pt < NFT; ++pt) {
-        S[pt] = mfma32(psik_tr<NP>(kb8, r0, pt, 0), vb8, S[pt]);
-        S[pt] = mfma32(psik_tr<NP>(kb8, r0, pt, LO), vb8, S[pt]);
-      }
-    }
+    state_update_prf<C, D, NP, LO, PV>(S, kb8, vT);
   }
 }
 
