@@ -57,6 +57,24 @@ def traffic_from_profiles(kernel_key: str):
     return rec[kernel_key]["bytes"]
 
 
+def mfma_from_profiles(kernel_key: str):
+    """rocprofv3 MFMA figures for one launch of a prefill kernel (profiles/mfma.json, written by
+    chunked_causal_linear_k1_amd.pmc_mfma): busy percentage and executed bf16 MFMA flops, or None
+    when absent or taken on kernel sources other than the current ones."""
+    from chunked_causal_linear_k1_amd import pmc_traffic
+    path = os.path.join(PROFILE_DIR, "mfma.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != pmc_traffic.source_hash() or kernel_key not in rec:
+        return None
+    r = rec[kernel_key]
+    return {"kernel": kernel_key, "mfma_busy_pct": r["mfma_busy_pct"], "mfma_bf16_flops": r["mfma_bf16_flops"]}
+
+
 def bench_prefill(w: workloads.Workload, steps: int, warmup: int):
     log(f"prefill {w.name}: generating inputs on the GPU")
     inp = inputs.make_prefill_inputs(w, device="cuda")
@@ -243,16 +261,21 @@ def main():
                    "state": "fp32", "output": "fp32"},
         "phase_ms": {k: round(v, 4) for k, v in pre["phase_ms"].items()},
         "roofline": roofline,
+        "mfma_counters": {"output": mfma_from_profiles("k_output_retnet_128k"),
+                          "summary": mfma_from_profiles("k_summary_retnet_128k")},
     }
     if not args.no_extra:
-        for key, wx in (("prefill_8k", workloads.PREFILL_8K), ("prefill_prf_4k", workloads.PRF_4K)):
+        for key, wx, tag in (("prefill_8k", workloads.PREFILL_8K, "elu1_8k"),
+                             ("prefill_prf_4k", workloads.PRF_4K, "prf256_4k")):
             px = bench_prefill(wx, args.steps, args.warmup)
             ax = BYTES_PER_TOKEN_HEAD * px["units"] / (px["ms_per_step"] * 1e-3) / 1e9
             line[key] = {"workload": wx.name, "token_heads_per_s": round(px["token_heads_per_s"], 1),
                          "ms_per_step": round(px["ms_per_step"], 4),
                          "phase_ms": {k: round(v, 4) for k, v in px["phase_ms"].items()},
                          "whole_call_roofline": {"bound": "hbm", "achieved": round(ax, 1), "peak": HBM_PEAK_GBS,
-                                                 "unit": "GB/s", "frac": round(ax / HBM_PEAK_GBS, 4)}}
+                                                 "unit": "GB/s", "frac": round(ax / HBM_PEAK_GBS, 4)},
+                         "mfma_counters": {"output": mfma_from_profiles(f"k_output_{tag}"),
+                                           "summary": mfma_from_profiles(f"k_summary_{tag}")}}
             if wx.psi == workloads.PSI_PRF:
                 # 286,720 algorithmic FLOP per token-head (features 4*256*128, local pass C*(256+128),
                 # state and output 4*256*128); bf16 MFMA dense peak 2.5 PFLOP/s

@@ -23,8 +23,6 @@ from collections import defaultdict
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-KERNEL_SOURCES = ["la_prefill_bf16.hpp", "la_prefill_bf16.hip", "la_prefill_prf.hpp", "la_device.hpp", "la_scan.hip",
-                  "la_decode.hip", "la_api.cpp"]
 
 # kernel-name substring -> key in traffic.json
 KERNELS = {
@@ -37,10 +35,14 @@ COPY_KERNEL = "neg"  # the --copy-probe kernel of bench.py (torch.neg of an fp32
 
 
 def source_hash() -> str:
+    """Hash of every kernel and dispatch source (csrc/), in name order."""
     h = hashlib.sha1()
-    for f in KERNEL_SOURCES:
-        with open(os.path.join(HERE, "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    src = os.path.join(HERE, "csrc")
+    for f in sorted(os.listdir(src)):
+        if f.endswith((".hip", ".hpp", ".cpp", ".h")):
+            h.update(f.encode())
+            with open(os.path.join(src, f), "rb") as fh:
+                h.update(fh.read())
     return h.hexdigest()[:16]
 
 
