@@ -21,17 +21,19 @@ LIB_PATH = os.path.join(_HERE, "liblinattn.so")
 
 LA_OK, LA_ERR_NULL, LA_ERR_SHAPE, LA_ERR_UNSUPPORTED, LA_ERR_WORKSPACE, LA_ERR_ALIGN, LA_ERR_VALUE, LA_ERR_HIP = range(8)
 LA_BF16, LA_F32 = 0, 1
+LA_LAYOUT_BHTD, LA_LAYOUT_BTHD = 0, 1
 MAX_DECAY_HEADS = 256
 
 EXPORTED = ("lin_attn_prefill_workspace_size", "lin_attn_prefill", "lin_attn_prefill_profiled",
-            "lin_attn_decode_step", "lin_attn_status_string", "lin_attn_version")
+            "lin_attn_prefill_varlen", "lin_attn_decode_step", "lin_attn_status_string", "lin_attn_version")
 
 
 class PrefillDesc(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("T", ctypes.c_int32),
                 ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32), ("n_psi", ctypes.c_int32),
                 ("chunk", ctypes.c_int32), ("psi", ctypes.c_int32), ("normalize", ctypes.c_int32),
-                ("eps", ctypes.c_float), ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32)]
+                ("eps", ctypes.c_float), ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+                ("layout", ctypes.c_int32)]
 
 
 class DecodeDesc(ctypes.Structure):
@@ -65,6 +67,9 @@ def load() -> ctypes.CDLL:
                                          ctypes.c_size_t, vp]
         lib.lin_attn_prefill_profiled.restype = ctypes.c_int
         lib.lin_attn_prefill_profiled.argtypes = lib.lin_attn_prefill.argtypes + [ctypes.POINTER(ctypes.c_void_p)]
+        lib.lin_attn_prefill_varlen.restype = ctypes.c_int
+        lib.lin_attn_prefill_varlen.argtypes = [ctypes.POINTER(PrefillDesc), vp, ctypes.c_int32, vp, vp, vp, fp, vp,
+                                                vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         lib.lin_attn_decode_step.restype = ctypes.c_int
         lib.lin_attn_decode_step.argtypes = [ctypes.POINTER(DecodeDesc), vp, vp, vp, fp, vp, vp, vp, vp, vp]
         lib.lin_attn_status_string.restype = ctypes.c_char_p
@@ -110,8 +115,9 @@ def _stream(stream) -> Optional[int]:
     return stream.cuda_stream
 
 
-def prefill_desc(B, H, T, d_k, d_v, n_psi, chunk, psi, normalize, eps, in_dtype, out_dtype=LA_F32) -> PrefillDesc:
-    return PrefillDesc(B, H, T, d_k, d_v, n_psi, chunk, psi, normalize, eps, in_dtype, out_dtype)
+def prefill_desc(B, H, T, d_k, d_v, n_psi, chunk, psi, normalize, eps, in_dtype, out_dtype=LA_F32,
+                 layout=LA_LAYOUT_BHTD) -> PrefillDesc:
+    return PrefillDesc(B, H, T, d_k, d_v, n_psi, chunk, psi, normalize, eps, in_dtype, out_dtype, layout)
 
 
 def workspace_size(desc: PrefillDesc) -> int:
@@ -127,20 +133,31 @@ def lin_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, psi: 
                      prf_w: Optional[torch.Tensor] = None, init_S: Optional[torch.Tensor] = None,
                      init_Z: Optional[torch.Tensor] = None, o: Optional[torch.Tensor] = None,
                      final_S: Optional[torch.Tensor] = None, final_Z: Optional[torch.Tensor] = None,
-                     workspace: Optional[torch.Tensor] = None, stream=None, events=None) -> torch.Tensor:
-    """o = chunkwise causal linear attention of q, k, v [B, H, T, d] on the GPU (C ABI call).
+                     workspace: Optional[torch.Tensor] = None, stream=None, events=None, layout: str = "bhtd",
+                     out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
+    """o = chunkwise causal linear attention of q, k, v on the GPU (C ABI call).
 
+    layout "bhtd": q, k, v, o are [B, H, T, d]; "bthd": [B, T, H, d]. o is allocated in
+    out_dtype (float32, or bfloat16 = the fp32 result rounded to nearest even) unless given.
     events: optional sequence of 4 torch.cuda.Event (timing enabled) recorded at the phase
     boundaries through lin_attn_prefill_profiled."""
-    B, H, T, d_k = q.shape
+    if layout == "bhtd":
+        B, H, T, d_k = q.shape
+        lay = LA_LAYOUT_BHTD
+    elif layout == "bthd":
+        B, T, H, d_k = q.shape
+        lay = LA_LAYOUT_BTHD
+    else:
+        raise ValueError(f"layout must be 'bhtd' or 'bthd', not {layout!r}")
     d_v = v.shape[-1]
     n_psi = prf_w.shape[1] if prf_w is not None else d_k
     for t in (q, k, v):
         if not t.is_contiguous():
-            raise ValueError("q, k, v must be contiguous [B, H, T, d]")
-    desc = prefill_desc(B, H, T, d_k, d_v, n_psi, chunk, psi, normalize, eps, _dtype_code(q))
+            raise ValueError(f"q, k, v must be contiguous ({layout})")
     if o is None:
-        o = torch.empty((B, H, T, d_v), dtype=torch.float32, device=q.device)
+        shape = (B, H, T, d_v) if lay == LA_LAYOUT_BHTD else (B, T, H, d_v)
+        o = torch.empty(shape, dtype=out_dtype, device=q.device)
+    desc = prefill_desc(B, H, T, d_k, d_v, n_psi, chunk, psi, normalize, eps, _dtype_code(q), _dtype_code(o), lay)
     ws_bytes = workspace_size(desc)
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
@@ -155,6 +172,43 @@ def lin_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, psi: 
         st = load().lin_attn_prefill_profiled(*args, ev)
     if st != LA_OK:
         raise LinAttnError(st, "lin_attn_prefill")
+    return o
+
+
+def lin_attn_prefill_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor,
+                            max_seqlen: int, *, psi: int, chunk: int, normalize: int = 1, eps: float = 1e-6,
+                            gamma: Optional[Sequence[float]] = None, prf_w: Optional[torch.Tensor] = None,
+                            init_S: Optional[torch.Tensor] = None, init_Z: Optional[torch.Tensor] = None,
+                            o: Optional[torch.Tensor] = None, final_S: Optional[torch.Tensor] = None,
+                            final_Z: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                            stream=None, out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
+    """Prefill of N packed sequences: q, k, v [total, H, d]; cu_seqlens int32 [N + 1] on the device
+    (sequence b is tokens cu_seqlens[b] .. cu_seqlens[b+1] - 1); max_seqlen >= every length.
+    States are per sequence: [N, H, n_psi, d_v] and [N, H, n_psi]."""
+    total, H, d_k = q.shape
+    d_v = v.shape[-1]
+    N = cu_seqlens.numel() - 1
+    n_psi = prf_w.shape[1] if prf_w is not None else d_k
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.device != q.device:
+        raise ValueError("cu_seqlens must be an int32 tensor on the inputs' device")
+    for t in (q, k, v, cu_seqlens):
+        if not t.is_contiguous():
+            raise ValueError("q, k, v [total, H, d] and cu_seqlens must be contiguous")
+    if o is None:
+        o = torch.empty((total, H, d_v), dtype=out_dtype, device=q.device)
+    desc = prefill_desc(N, H, max_seqlen, d_k, d_v, n_psi, chunk, psi, normalize, eps, _dtype_code(q),
+                        _dtype_code(o), LA_LAYOUT_BTHD)
+    ws_bytes = workspace_size(desc)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    g = _gamma_array(gamma, H)
+    st = load().lin_attn_prefill_varlen(ctypes.byref(desc), _ptr(cu_seqlens), total, _ptr(q), _ptr(k), _ptr(v), g,
+                                        _ptr(prf_w), _ptr(init_S), _ptr(init_Z), _ptr(o), _ptr(final_S),
+                                        _ptr(final_Z), _ptr(workspace),
+                                        0 if workspace is None else workspace.numel() * workspace.element_size(),
+                                        _stream(stream))
+    if st != LA_OK:
+        raise LinAttnError(st, "lin_attn_prefill_varlen")
     return o
 
 

@@ -56,13 +56,18 @@ la_status validate_prefill_desc(const la_prefill_desc* d) {
   if (!(d->eps >= 0.f) || !isfinite(d->eps)) return LA_ERR_VALUE;
   if (d->in_dtype != LA_BF16 && d->in_dtype != LA_F32) return LA_ERR_VALUE;
   if (d->out_dtype != LA_BF16 && d->out_dtype != LA_F32) return LA_ERR_VALUE;
+  if (d->layout != LA_LAYOUT_BHTD && d->layout != LA_LAYOUT_BTHD) return LA_ERR_VALUE;
   if (d->psi != LA_PSI_PRF && d->n_psi != d->d_k) return LA_ERR_SHAPE;
   if (d->d_v % 4 != 0 || d->n_psi % 4 != 0) return LA_ERR_UNSUPPORTED;  // 16-byte state rows
   // element counts must fit comfortably in 64-bit offsets and the grid's y extent
   const double tokens = (double)d->B * d->H * d->T;
   if (tokens * std::max(d->d_k, d->d_v) > 9.0e15) return LA_ERR_SHAPE;
   if ((long long)d->B * d->H > 65535) return LA_ERR_UNSUPPORTED;
-  if (d->out_dtype != LA_F32) return LA_ERR_UNSUPPORTED;
+  // one chunk of one head spans (C - 1) * H + 1 rows in the interleaved layout: its byte
+  // extent must fit a buffer resource's 32-bit range
+  if (d->layout == LA_LAYOUT_BTHD && (double)d->chunk * d->H * std::max(d->d_k, d->d_v) * 4 >= 2147483648.0)
+    return LA_ERR_UNSUPPORTED;
+  if (d->out_dtype == LA_BF16 && d->in_dtype != LA_BF16) return LA_ERR_UNSUPPORTED;
   const bool ok = d->in_dtype == LA_BF16
                       ? la::prefill_bf16_supported(d->chunk, d->d_k, d->d_v, d->n_psi, d->psi)
                       : la::prefill_f32_supported(d->chunk, d->d_k, d->d_v, d->n_psi, d->psi);
@@ -107,7 +112,7 @@ const char* lin_attn_status_string(la_status s) {
   return "unknown status";
 }
 
-const char* lin_attn_version(void) { return "0.1.0"; }
+const char* lin_attn_version(void) { return "0.2.0"; }
 
 la_status lin_attn_prefill_workspace_size(const la_prefill_desc* d, size_t* bytes) {
   if (!bytes) return LA_ERR_NULL;
@@ -117,12 +122,23 @@ la_status lin_attn_prefill_workspace_size(const la_prefill_desc* d, size_t* byte
   return LA_OK;
 }
 
-la_status lin_attn_prefill_profiled(const la_prefill_desc* d, const void* q, const void* k, const void* v,
-                                    const float* gamma, const void* prf_w, const float* init_S,
-                                    const float* init_Z, void* o, float* final_S, float* final_Z, void* workspace,
-                                    size_t workspace_bytes, hipStream_t stream, hipEvent_t* events) {
+}  // extern "C"
+
+namespace {
+
+// Both prefill entry points: fixed-length batches (cu_seqlens == nullptr) and packed
+// variable-length batches.
+la_status prefill_impl(const la_prefill_desc* d, const int32_t* cu_seqlens, int32_t total_tokens, const void* q,
+                       const void* k, const void* v, const float* gamma, const void* prf_w, const float* init_S,
+                       const float* init_Z, void* o, float* final_S, float* final_Z, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream, hipEvent_t* events) {
   la_status st = validate_prefill_desc(d);
   if (st != LA_OK) return st;
+  if (cu_seqlens) {
+    if (d->layout != LA_LAYOUT_BTHD) return LA_ERR_VALUE;
+    if (total_tokens < 0) return LA_ERR_SHAPE;
+    if ((reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0) return LA_ERR_ALIGN;
+  }
   if (!q || !k || !v || !o) return LA_ERR_NULL;
   if (d->psi == LA_PSI_PRF && !prf_w) return LA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(prf_w) ||
@@ -138,9 +154,17 @@ la_status lin_attn_prefill_profiled(const la_prefill_desc* d, const void* q, con
   memset(&p, 0, sizeof p);
   p.q = q; p.k = k; p.v = v; p.prf_w = prf_w; p.o = o;
   p.ws = (float*)workspace;
+  p.cu_seqlens = cu_seqlens;
+  p.total = cu_seqlens ? total_tokens : 0;
   p.B = d->B; p.H = d->H; p.T = d->T;
+  if (d->layout == LA_LAYOUT_BTHD) {
+    p.tok_rows = d->H; p.head_rows = 1; p.seq_rows = (long long)d->T * d->H;
+  } else {
+    p.tok_rows = 1; p.head_rows = d->T; p.seq_rows = (long long)d->H * d->T;
+  }
   p.d_k = d->d_k; p.d_v = d->d_v; p.n_psi = d->n_psi; p.C = d->chunk;
   p.psi = d->psi; p.normalize = d->normalize; p.eps = d->eps;
+  p.out_bf16 = d->out_dtype == LA_BF16;
   p.n_chunks = pl.n_chunks; p.seg_chunks = pl.seg_chunks; p.n_seg = pl.n_seg;
   p.has_decay = fill_log2g(gamma, d->H, p.log2g);
 
@@ -151,6 +175,7 @@ la_status lin_attn_prefill_profiled(const la_prefill_desc* d, const void* q, con
   // without normalisation the normaliser is not maintained: init_Z / final_Z are ignored
   sp.init_Z = d->normalize ? init_Z : nullptr;
   sp.final_Z = d->normalize ? final_Z : nullptr;
+  sp.cu_seqlens = cu_seqlens; sp.total = p.total;
   sp.BH = d->B * d->H; sp.H = d->H; sp.T = d->T;
   sp.n_psi = d->n_psi; sp.d_v = d->d_v;
   sp.n_seg = pl.n_seg; sp.seg_len = pl.seg_chunks * d->chunk;
@@ -169,6 +194,28 @@ la_status lin_attn_prefill_profiled(const la_prefill_desc* d, const void* q, con
   if (e == hipSuccess) e = bf ? la::launch_prefill_bf16_output(p, stream) : la::launch_prefill_f32_output(p, stream);
   if (e == hipSuccess) e = mark(3);
   return e == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+la_status lin_attn_prefill_profiled(const la_prefill_desc* d, const void* q, const void* k, const void* v,
+                                    const float* gamma, const void* prf_w, const float* init_S,
+                                    const float* init_Z, void* o, float* final_S, float* final_Z, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream, hipEvent_t* events) {
+  return prefill_impl(d, nullptr, 0, q, k, v, gamma, prf_w, init_S, init_Z, o, final_S, final_Z, workspace,
+                      workspace_bytes, stream, events);
+}
+
+la_status lin_attn_prefill_varlen(const la_prefill_desc* d, const int32_t* cu_seqlens, int32_t total_tokens,
+                                  const void* q, const void* k, const void* v, const float* gamma,
+                                  const void* prf_w, const float* init_S, const float* init_Z, void* o,
+                                  float* final_S, float* final_Z, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream) {
+  if (!cu_seqlens) return LA_ERR_NULL;
+  return prefill_impl(d, cu_seqlens, total_tokens, q, k, v, gamma, prf_w, init_S, init_Z, o, final_S, final_Z,
+                      workspace, workspace_bytes, stream, nullptr);
 }
 
 la_status lin_attn_prefill(const la_prefill_desc* d, const void* q, const void* k, const void* v,

@@ -138,6 +138,37 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t v
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
 
+// Bound of a buffer resource over `rows` token rows spaced `stride` bytes apart, each
+// `row_bytes` long: 0 when rows <= 0, so every load reads zero and no store lands. A row
+// at or past `rows` starts at or beyond the bound (stride >= row_bytes).
+__device__ __forceinline__ uint32_t rows_extent(int rows, uint32_t stride, uint32_t row_bytes) {
+  return rows > 0 ? (uint32_t)(rows - 1) * stride + row_bytes : 0u;
+}
+
+// Four consecutive outputs at element offset `elem` of an fp32 (OBF false) or bf16 (OBF
+// true, each value rounded to nearest even) output tensor.
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+template <bool OBF>
+__device__ __forceinline__ void store_out4(__amdgpu_buffer_rsrc_t r, uint32_t elem, float a, float b, float c,
+                                           float d) {
+  if (OBF) {
+    const bf16x2 ab = __builtin_convertvector((f32x2){a, b}, bf16x2);
+    const bf16x2 cd = __builtin_convertvector((f32x2){c, d}, bf16x2);
+    const u32x2 w = {__builtin_bit_cast(uint32_t, ab), __builtin_bit_cast(uint32_t, cd)};
+    __builtin_amdgcn_raw_buffer_store_b64(w, r, elem * 2, 0, 0);
+  } else {
+    const u32x4 w = {__float_as_uint(a), __float_as_uint(b), __float_as_uint(c), __float_as_uint(d)};
+    __builtin_amdgcn_raw_buffer_store_b128(w, r, elem * 4, 0, 0);
+  }
+}
+template <bool OBF>
+__device__ __forceinline__ void store_out1(__amdgpu_buffer_rsrc_t r, uint32_t elem, float x) {
+  if (OBF)
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (__bf16)x), r, elem * 2, 0, 0);
+  else
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, elem * 4, 0, 0);
+}
+
 // An integer the optimiser must treat as unknown. Used for per-lane LDS base addresses:
 // kept in one register each, with every access a base plus an immediate offset, rather
 // than the constant parts folded back in and a register materialised per access (the

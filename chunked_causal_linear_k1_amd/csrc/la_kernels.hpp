@@ -15,6 +15,14 @@ namespace la {
 // n_chunks = ceil(T / C) chunks, and consecutive chunks are grouped into n_seg
 // segments of seg_chunks chunks (the last segment and the last chunk may be
 // short). The workspace holds one summary (a, S, Z) per segment, scanned in place.
+// With per-sequence lengths (cu_seqlens) T is the longest sequence: segments that
+// start past a shorter sequence's end are empty (identity summaries, no outputs).
+//
+// Token tensors are seen as rows of d elements, one row per (token, head). Token t of
+// sequence (b, h) is row row0(b, h) + t * tok_rows, where row0 = b * seq_rows + h * head_rows
+// for fixed-length batches ([B,H,T,d]: tok_rows 1, head_rows T, seq_rows H*T; [B,T,H,d]:
+// tok_rows H, head_rows 1, seq_rows T*H) and row0 = cu_seqlens[b] * H + h for packed
+// sequences ([total, H, d]).
 struct PrefillParams {
   const void* q;
   const void* k;
@@ -22,10 +30,15 @@ struct PrefillParams {
   const void* prf_w;     // [H, n_psi, d_k] or null
   void* o;
   float* ws;             // [BH, n_seg, E] with E = n_psi*d_v + n_psi (segment summaries)
+  const int* cu_seqlens; // [B + 1] first token of each packed sequence, or null
   int B, H, T;
+  int total;             // tokens in the packed tensors (cu_seqlens only)
+  int tok_rows;
+  long long seq_rows, head_rows;
   int d_k, d_v, n_psi, C;
   int psi;               // la_psi
   int normalize;
+  int out_bf16;          // o is bf16 (round to nearest even of the fp32 result)
   float eps;
   int n_chunks, seg_chunks, n_seg;
   int has_decay;
@@ -38,6 +51,8 @@ struct ScanParams {
   const float* init_Z;   // [BH, n_psi] or null
   float* final_S;        // [BH, n_psi, d_v] or null
   float* final_Z;        // [BH, n_psi] or null
+  const int* cu_seqlens; // [B + 1] or null (then every sequence has T tokens)
+  int total;             // tokens in the packed tensors (cu_seqlens only)
   int BH, H, T;
   int n_psi, d_v;
   int n_seg, seg_len;    // segment length in tokens (the last one may be short)
@@ -62,6 +77,34 @@ struct DecodeParams {
   int has_decay;
   float gamma[LA_MAX_DECAY_HEADS];
 };
+
+// Length of packed sequence b, clamped so that malformed offsets never address rows
+// outside [0, total) and no sequence exceeds max_len; its first token is *start.
+__device__ __forceinline__ int packed_len(const int* cu, int b, int total, int max_len, int* start) {
+  const int s0 = min(max(cu[b], 0), total);
+  const int s1 = min(max(cu[b + 1], s0), total);
+  *start = s0;
+  return min(s1 - s0, max_len);
+}
+
+// Where the sequence of (batch, head) bh lives: its length and its first token row.
+struct SeqSpan {
+  int T;
+  long long row0;
+};
+__device__ __forceinline__ SeqSpan seq_span(const PrefillParams& p, int bh) {
+  const int b = bh / p.H, h = bh - b * p.H;
+  SeqSpan s;
+  if (p.cu_seqlens) {
+    int start;
+    s.T = packed_len(p.cu_seqlens, b, p.total, p.T, &start);
+    s.row0 = (long long)start * p.H + h;
+  } else {
+    s.T = p.T;
+    s.row0 = (long long)b * p.seq_rows + (long long)h * p.head_rows;
+  }
+  return s;
+}
 
 // Launchers: return hipSuccess or the launch error. Shapes are validated by the caller.
 bool prefill_bf16_supported(int C, int d_k, int d_v, int n_psi, int psi);

@@ -32,7 +32,7 @@ hipError_t launch_prefill_bf16_summary(const PrefillParams& p, hipStream_t s) {
   if (p.C == 128 && p.psi != LA_PSI_PRF) {
     PrefillParams q = p;
     q.C = 64;
-    q.n_chunks = (p.T + 63) / 64;
+    q.n_chunks = 2 * p.n_chunks;  // kernels count each sequence's chunks from its own length
     q.seg_chunks = 2 * p.seg_chunks;
     return dispatch(q, s, false);
   }

@@ -89,15 +89,17 @@ __device__ __forceinline__ int piece_row(int i) {
   return (threadIdx.x + i * G::NT) / G::PPR;
 }
 
-// Rows >= valid read as zeros (bounded buffer resource, no branches).
+// Token rows are rsb bytes apart (D * 2 when a head's tokens are contiguous). Rows >= valid
+// read as zeros (bounded buffer resource, no branches).
 template <int C, int D>
-__device__ __forceinline__ void load_pieces(Pieces<C, D>& P, const uint16_t* __restrict__ g, int valid) {
+__device__ __forceinline__ void load_pieces(Pieces<C, D>& P, const uint16_t* __restrict__ g, int valid,
+                                            uint32_t rsb) {
   using G = Geo<C, D, true>;
   static_assert(G::NT % G::PPR == 0, "piece i of a thread is i * NT / PPR rows below piece 0");
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(g, (uint32_t)valid * D * 2);
-  const uint32_t v0 = (uint32_t)(piece_row<C, D>(0) * D + piece_cols<C, D>(0)) * 2;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(g, rows_extent(valid, rsb, D * 2));
+  const uint32_t v0 = (uint32_t)piece_row<C, D>(0) * rsb + (uint32_t)piece_cols<C, D>(0) * 2;
 #pragma unroll
-  for (int i = 0; i < G::NPC; ++i) P.r[i] = buf_load16(rs, v0, (uint32_t)(i * (G::NT / G::PPR) * D * 2));
+  for (int i = 0; i < G::NPC; ++i) P.r[i] = buf_load16(rs, v0, (uint32_t)(i * (G::NT / G::PPR)) * rsb);
 }
 
 // Q: psi applied, rounded once to bf16.
@@ -234,14 +236,17 @@ __global__ __launch_bounds__(2 * D) void k_summary(PrefillParams p) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) zrun[j] = 0.f;
 
-  const uint16_t* kb = (const uint16_t*)p.k + (size_t)bh * p.T * D;
-  const uint16_t* vb = (const uint16_t*)p.v + (size_t)bh * p.T * D;
-  const int c0 = seg * p.seg_chunks, c1 = min(c0 + p.seg_chunks, p.n_chunks);
+  const SeqSpan sq = seq_span(p, bh);
+  const int T = sq.T, n_chunks = (T + C - 1) / C;
+  const uint32_t rse = (uint32_t)p.tok_rows * D, rsb = rse * 2;  // elements / bytes between token rows
+  const uint16_t* kb = (const uint16_t*)p.k + sq.row0 * D;
+  const uint16_t* vb = (const uint16_t*)p.v + sq.row0 * D;
+  const int c0 = seg * p.seg_chunks, c1 = min(c0 + p.seg_chunks, n_chunks);
   Pieces<C, D> pk, pv;
-  load_pieces<C, D>(pk, kb + (size_t)c0 * C * D, min(C, p.T - c0 * C));
-  load_pieces<C, D>(pv, vb + (size_t)c0 * C * D, min(C, p.T - c0 * C));
+  load_pieces<C, D>(pk, kb + (size_t)c0 * C * rse, min(C, T - c0 * C), rsb);
+  load_pieces<C, D>(pv, vb + (size_t)c0 * C * rse, min(C, T - c0 * C), rsb);
   for (int c = c0; c < c1; ++c) {
-    const int L = min(C, p.T - c * C);
+    const int L = min(C, T - c * C);
     const float a = DECAY ? exp2f((float)L * lg) : 1.f;
     lds_barrier();  // the previous chunk is done with LDS
     float zp[8];
@@ -252,9 +257,9 @@ __global__ __launch_bounds__(2 * D) void k_summary(PrefillParams p) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) zrun[j] = a * zrun[j] + zp[j];
     if (c + 1 < c1) {  // next chunk's loads overlap this chunk's matrix work
-      const int Ln = min(C, p.T - (c + 1) * C);
-      load_pieces<C, D>(pk, kb + (size_t)(c + 1) * C * D, Ln);
-      load_pieces<C, D>(pv, vb + (size_t)(c + 1) * C * D, Ln);
+      const int Ln = min(C, T - (c + 1) * C);
+      load_pieces<C, D>(pk, kb + (size_t)(c + 1) * C * rse, Ln, rsb);
+      load_pieces<C, D>(pv, vb + (size_t)(c + 1) * C * rse, Ln, rsb);
     }
     lds_barrier();
     if (DECAY) {
@@ -286,7 +291,7 @@ __global__ __launch_bounds__(2 * D) void k_summary(PrefillParams p) {
   }
 }
 
-template <int C, int D, bool DECAY, bool NORM, bool ELU>
+template <int C, int D, bool DECAY, bool NORM, bool ELU, bool OBF>
 __global__ __launch_bounds__(2 * D) void k_output(PrefillParams p) {
   using G = Geo<C, D, true>;
   constexpr bool SPLIT = DECAY || ELU;
@@ -323,22 +328,27 @@ __global__ __launch_bounds__(2 * D) void k_output(PrefillParams p) {
     foff[r] = DECAY ? exp2f((float)(n + 32 - ir) * lg) : 1.f;
   }
 
-  const uint16_t* qb = (const uint16_t*)p.q + (size_t)bh * p.T * D;
-  const uint16_t* kb = (const uint16_t*)p.k + (size_t)bh * p.T * D;
-  const uint16_t* vb = (const uint16_t*)p.v + (size_t)bh * p.T * D;
-  float* ob = (float*)p.o + (size_t)bh * p.T * D;
-  const int c0 = seg * p.seg_chunks, c1 = min(c0 + p.seg_chunks, p.n_chunks);
+  const SeqSpan sq = seq_span(p, bh);
+  const int T = sq.T, n_chunks = (T + C - 1) / C;
+  const uint32_t rse = (uint32_t)p.tok_rows * D, rsb = rse * 2;  // elements / bytes between token rows
+  constexpr int OES = OBF ? 2 : 4;  // output element bytes
+  const uint16_t* qb = (const uint16_t*)p.q + sq.row0 * D;
+  const uint16_t* kb = (const uint16_t*)p.k + sq.row0 * D;
+  const uint16_t* vb = (const uint16_t*)p.v + sq.row0 * D;
+  unsigned char* ob = (unsigned char*)p.o + sq.row0 * D * OES;
+  const int c0 = seg * p.seg_chunks, c1 = min(c0 + p.seg_chunks, n_chunks);
+  if (c0 >= c1) return;  // segment past the end of a shorter sequence: nothing to write
 
   Pieces<C, D> pq, pk, pv;
   {
-    const int L0 = min(C, p.T - c0 * C);
-    load_pieces<C, D>(pq, qb + (size_t)c0 * C * D, L0);
-    load_pieces<C, D>(pk, kb + (size_t)c0 * C * D, L0);
-    load_pieces<C, D>(pv, vb + (size_t)c0 * C * D, L0);
+    const int L0 = min(C, T - c0 * C);
+    load_pieces<C, D>(pq, qb + (size_t)c0 * C * rse, L0, rsb);
+    load_pieces<C, D>(pk, kb + (size_t)c0 * C * rse, L0, rsb);
+    load_pieces<C, D>(pv, vb + (size_t)c0 * C * rse, L0, rsb);
     vm_drain();  // entering the loop with nothing in flight, see the prefetch below
   }
   for (int c = c0; c < c1; ++c) {
-    const int t0 = c * C, L = min(C, p.T - t0);
+    const int t0 = c * C, L = min(C, T - t0);
     const float a = DECAY ? exp2f((float)L * lg) : 1.f;
     lds_barrier();  // the previous chunk is done with LDS (and Z is updated)
     float zp[8];
@@ -348,14 +358,14 @@ __global__ __launch_bounds__(2 * D) void k_output(PrefillParams p) {
     commit_k<C, D, ELU, DECAY, false, ELU>(pk, sK, sKlo, G::PK, L, lg, zp);
     commit_v<C, D>(pv, sV, G::PK);
     const bool more = c + 1 < c1;
-    const int Ln = more ? min(C, p.T - (c + 1) * C) : 0;
+    const int Ln = more ? min(C, T - (c + 1) * C) : 0;
     // next chunk's keys and values stream in during this chunk's matrix work (rows past
     // Ln, including every row when there is no next chunk, read as zeros)
-    load_pieces<C, D>(pk, kb + (size_t)(c + 1) * C * D, Ln);
-    load_pieces<C, D>(pv, vb + (size_t)(c + 1) * C * D, Ln);
+    load_pieces<C, D>(pk, kb + (size_t)(c + 1) * C * rse, Ln, rsb);
+    load_pieces<C, D>(pv, vb + (size_t)(c + 1) * C * rse, Ln, rsb);
     lds_barrier();
     // stores of this chunk's outputs: rows past L are dropped by the buffer bound
-    const __amdgpu_buffer_rsrc_t ors = make_rsrc(ob + (size_t)t0 * D, (uint32_t)L * D * 4);
+    const __amdgpu_buffer_rsrc_t ors = make_rsrc(ob + (size_t)t0 * rse * OES, rows_extent(L, rse * OES, D * OES));
 
     // S as the B operand of psi(Q) S: straight from its accumulator layout (D-tile
     // feedback order), split once per chunk into hi + lo
@@ -420,12 +430,12 @@ __global__ __launch_bounds__(2 * D) void k_output(PrefillParams p) {
       for (int r = 0; r < 16; ++r) {
         const int j = jt * 32 + dtile_row(r, lane);
         const float val = NORM ? num[r] / __shfl(den, dtile_row(r, lane)) : num[r];
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), ors, (uint32_t)(j * D + Ew + n) * 4, 0, 0);
+        store_out1<OBF>(ors, (uint32_t)j * rse + Ew + n, val);
       }
     }
 
     // next chunk's queries: issued once this chunk's queries are no longer read
-    load_pieces<C, D>(pq, qb + (size_t)(c + 1) * C * D, Ln);
+    load_pieces<C, D>(pq, qb + (size_t)(c + 1) * C * rse, Ln, rsb);
     // state update: K~ = Xi psi(K) as hi + lo, S <- gamma^L S + K~^T V, Z <- gamma^L Z + K~^T 1
     if (NORM) reduce_zp<D>(zp, sF + G::F_ZRED);
     if (DECAY) {
@@ -530,7 +540,7 @@ __device__ __forceinline__ void state_mfma_p(f32x16 (&S)[D / 32], const __bf16* 
 // K and K lo are XOR-swizzled (swz_off); since swz<D>(r0 + x) == swz<D>(x) whenever r0
 // is a multiple of 16 and x < 32, a swizzled read of any row block is one of a few
 // per-lane bases plus the row block's constant offset.
-template <int C, int D, bool DECAY, bool NORM, bool ELU>
+template <int C, int D, bool DECAY, bool NORM, bool ELU, bool OBF>
 __global__ __launch_bounds__(2 * D) void k_output_sh(PrefillParams p) {
   using G = ShGeo<C, D, ELU>;
   using PG = Geo<C, D, true>;  // piece geometry of the global -> LDS copies
@@ -595,22 +605,27 @@ __global__ __launch_bounds__(2 * D) void k_output_sh(PrefillParams p) {
     foff[r] = DECAY ? exp2f((float)(n + 32 - ir) * lg) : 1.f;
   }
 
-  const uint16_t* qb = (const uint16_t*)p.q + (size_t)bh * p.T * D;
-  const uint16_t* kb = (const uint16_t*)p.k + (size_t)bh * p.T * D;
-  const uint16_t* vb = (const uint16_t*)p.v + (size_t)bh * p.T * D;
-  float* ob = (float*)p.o + (size_t)bh * p.T * D;
-  const int c0 = seg * p.seg_chunks, c1 = min(c0 + p.seg_chunks, p.n_chunks);
+  const SeqSpan sq = seq_span(p, bh);
+  const int T = sq.T, n_chunks = (T + C - 1) / C;
+  const uint32_t rse = (uint32_t)p.tok_rows * D, rsb = rse * 2;  // elements / bytes between token rows
+  constexpr int OES = OBF ? 2 : 4;  // output element bytes
+  const uint16_t* qb = (const uint16_t*)p.q + sq.row0 * D;
+  const uint16_t* kb = (const uint16_t*)p.k + sq.row0 * D;
+  const uint16_t* vb = (const uint16_t*)p.v + sq.row0 * D;
+  unsigned char* ob = (unsigned char*)p.o + sq.row0 * D * OES;
+  const int c0 = seg * p.seg_chunks, c1 = min(c0 + p.seg_chunks, n_chunks);
+  if (c0 >= c1) return;  // segment past the end of a shorter sequence: nothing to write
 
   Pieces<C, D> pq, pk, pv;
   {
-    const int L0 = min(C, p.T - c0 * C);
-    load_pieces<C, D>(pq, qb + (size_t)c0 * C * D, L0);
-    load_pieces<C, D>(pk, kb + (size_t)c0 * C * D, L0);
-    load_pieces<C, D>(pv, vb + (size_t)c0 * C * D, L0);
+    const int L0 = min(C, T - c0 * C);
+    load_pieces<C, D>(pq, qb + (size_t)c0 * C * rse, L0, rsb);
+    load_pieces<C, D>(pk, kb + (size_t)c0 * C * rse, L0, rsb);
+    load_pieces<C, D>(pv, vb + (size_t)c0 * C * rse, L0, rsb);
     vm_drain();  // entering the loop with nothing in flight, see the prefetch below
   }
   for (int c = c0; c < c1; ++c) {
-    const int t0 = c * C, L = min(C, p.T - t0);
+    const int t0 = c * C, L = min(C, T - t0);
     const float a = DECAY ? exp2f((float)L * lg) : 1.f;
     lds_barrier();  // the previous chunk is done with LDS (and Z is updated)
 
@@ -660,13 +675,13 @@ __global__ __launch_bounds__(2 * D) void k_output_sh(PrefillParams p) {
 #pragma unroll
     for (int i = 0; i < NPC; ++i) *(uint4*)(vP + i * 16 * D * 2) = pv.r[i];
     const bool more = c + 1 < c1;
-    const int Ln = more ? min(C, p.T - (c + 1) * C) : 0;
+    const int Ln = more ? min(C, T - (c + 1) * C) : 0;
     // next chunk's tiles stream in during this chunk's matrix work (rows past Ln read as
     // zero). All three are issued before this chunk's output stores: the vmcnt wait at the
     // next commit then covers only these loads, not the stores.
-    load_pieces<C, D>(pq, qb + (size_t)(c + 1) * C * D, Ln);
-    load_pieces<C, D>(pk, kb + (size_t)(c + 1) * C * D, Ln);
-    load_pieces<C, D>(pv, vb + (size_t)(c + 1) * C * D, Ln);
+    load_pieces<C, D>(pq, qb + (size_t)(c + 1) * C * rse, Ln, rsb);
+    load_pieces<C, D>(pk, kb + (size_t)(c + 1) * C * rse, Ln, rsb);
+    load_pieces<C, D>(pv, vb + (size_t)(c + 1) * C * rse, Ln, rsb);
     lds_barrier();
 
     // ---- score tiles A^T (M = i, N = j, k = feature), masked, decayed, split into hi + lo
@@ -744,7 +759,7 @@ __global__ __launch_bounds__(2 * D) void k_output_sh(PrefillParams p) {
     // ---- outputs for this wave's value columns, computed transposed: numT[e][j] (M = value
     // column e, N = token j), so each lane ends up with 4 consecutive columns of one token
     // row (16-byte stores) and the per-token factors are lane scalars.
-    const __amdgpu_buffer_rsrc_t ors = make_rsrc(ob + (size_t)t0 * D, (uint32_t)L * D * 4);
+    const __amdgpu_buffer_rsrc_t ors = make_rsrc(ob + (size_t)t0 * rse * OES, rows_extent(L, rse * OES, D * OES));
     bf16x8 sh[D / 32][2], sl[D / 32][2];  // S_prev as hi + lo, straight from its accumulator layout
 #pragma unroll
     for (int pt = 0; pt < D / 32; ++pt)
@@ -804,13 +819,11 @@ __global__ __launch_bounds__(2 * D) void k_output_sh(PrefillParams p) {
         inv = 1.f / (fN[G::F_THETA + jt * 32] * qz + r + p.eps);
       }
       // registers 4 q4 .. 4 q4 + 3 hold columns Ew + 8 q4 + 4 hh + 0..3 of token row j
-      const uint32_t row_off = (uint32_t)((jt * 32 + n) * D + Ew + 4 * hh) * 4;
+      const uint32_t row_el = (uint32_t)(jt * 32 + n) * rse + Ew + 4 * hh;
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const u32x4 v4 = {__float_as_uint(num[4 * q4] * inv), __float_as_uint(num[4 * q4 + 1] * inv),
-                          __float_as_uint(num[4 * q4 + 2] * inv), __float_as_uint(num[4 * q4 + 3] * inv)};
-        __builtin_amdgcn_raw_buffer_store_b128(v4, ors, row_off + 32 * q4, 0, 0);
-      }
+      for (int q4 = 0; q4 < 4; ++q4)
+        store_out4<OBF>(ors, row_el + 8 * q4, num[4 * q4] * inv, num[4 * q4 + 1] * inv, num[4 * q4 + 2] * inv,
+                        num[4 * q4 + 3] * inv);
     }
 
     // ---- state update: K~ = Xi psi(K) as hi + lo, S <- gamma^L S + K~^T V, Z <- gamma^L Z + K~^T 1
@@ -924,17 +937,17 @@ struct PiecesN {
 };
 
 // Rows >= valid read as zeros (bounded buffer resource, no branches); piece i of the thread
-// at row prow + RSTEP i, columns pcol .. pcol + 7.
+// at row prow + RSTEP i, columns pcol .. pcol + 7; token rows rsb bytes apart.
 template <int D, int NPC, int RSTEP>
 __device__ __forceinline__ void load_pieces_n(PiecesN<NPC>& P, const uint16_t* __restrict__ g, int valid, int prow,
-                                              int pcol) {
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(g, (uint32_t)valid * D * 2);
-  const uint32_t v0 = (uint32_t)(prow * D + pcol) * 2;
+                                              int pcol, uint32_t rsb) {
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(g, rows_extent(valid, rsb, D * 2));
+  const uint32_t v0 = (uint32_t)prow * rsb + (uint32_t)pcol * 2;
 #pragma unroll
-  for (int i = 0; i < NPC; ++i) P.r[i] = buf_load16(rs, v0, (uint32_t)(i * RSTEP * D * 2));
+  for (int i = 0; i < NPC; ++i) P.r[i] = buf_load16(rs, v0, (uint32_t)(i * RSTEP) * rsb);
 }
 
-template <int C, int D, bool DECAY, bool NORM, bool ELU>
+template <int C, int D, bool DECAY, bool NORM, bool ELU, bool OBF>
 __global__ __launch_bounds__(512) void k_output_w8(PrefillParams p) {
   using G = W8Geo<C, D, ELU>;
   static_assert(G::FITS, "8-wave layout");
@@ -987,22 +1000,27 @@ __global__ __launch_bounds__(512) void k_output_w8(PrefillParams p) {
   if (tid < D) sF[G::F_Z + tid] = NORM ? pre[(size_t)D * D + tid] : 0.f;
   for (int j = tid; j < C; j += G::NT) sF[G::F_THETA + j] = DECAY ? exp2f((float)(j + 1) * lg) : 1.f;
 
-  const uint16_t* qb = (const uint16_t*)p.q + (size_t)bh * p.T * D;
-  const uint16_t* kb = (const uint16_t*)p.k + (size_t)bh * p.T * D;
-  const uint16_t* vb = (const uint16_t*)p.v + (size_t)bh * p.T * D;
-  float* ob = (float*)p.o + (size_t)bh * p.T * D;
-  const int c0 = seg * p.seg_chunks, c1 = min(c0 + p.seg_chunks, p.n_chunks);
+  const SeqSpan sq = seq_span(p, bh);
+  const int T = sq.T, n_chunks = (T + C - 1) / C;
+  const uint32_t rse = (uint32_t)p.tok_rows * D, rsb = rse * 2;  // elements / bytes between token rows
+  constexpr int OES = OBF ? 2 : 4;  // output element bytes
+  const uint16_t* qb = (const uint16_t*)p.q + sq.row0 * D;
+  const uint16_t* kb = (const uint16_t*)p.k + sq.row0 * D;
+  const uint16_t* vb = (const uint16_t*)p.v + sq.row0 * D;
+  unsigned char* ob = (unsigned char*)p.o + sq.row0 * D * OES;
+  const int c0 = seg * p.seg_chunks, c1 = min(c0 + p.seg_chunks, n_chunks);
+  if (c0 >= c1) return;  // segment past the end of a shorter sequence: nothing to write
 
   PiecesN<NPC> pq, pk, pv;
   {
-    const int L0 = min(C, p.T - c0 * C);
-    load_pieces_n<D, NPC, RSTEP>(pq, qb + (size_t)c0 * C * D, L0, prow, pcol);
-    load_pieces_n<D, NPC, RSTEP>(pk, kb + (size_t)c0 * C * D, L0, prow, pcol);
-    load_pieces_n<D, NPC, RSTEP>(pv, vb + (size_t)c0 * C * D, L0, prow, pcol);
+    const int L0 = min(C, T - c0 * C);
+    load_pieces_n<D, NPC, RSTEP>(pq, qb + (size_t)c0 * C * rse, L0, prow, pcol, rsb);
+    load_pieces_n<D, NPC, RSTEP>(pk, kb + (size_t)c0 * C * rse, L0, prow, pcol, rsb);
+    load_pieces_n<D, NPC, RSTEP>(pv, vb + (size_t)c0 * C * rse, L0, prow, pcol, rsb);
     vm_drain();
   }
   for (int c = c0; c < c1; ++c) {
-    const int t0 = c * C, L = min(C, p.T - t0);
+    const int t0 = c * C, L = min(C, T - t0);
     const float a = DECAY ? exp2f((float)L * lg) : 1.f;
     lds_barrier();  // the previous chunk is done with LDS (and Z is updated)
 
@@ -1051,10 +1069,10 @@ __global__ __launch_bounds__(512) void k_output_w8(PrefillParams p) {
 #pragma unroll
     for (int i = 0; i < NPC; ++i) *(uint4*)(vP + i * RSTEP * D * 2) = pv.r[i];
     const bool more = c + 1 < c1;
-    const int Ln = more ? min(C, p.T - (c + 1) * C) : 0;
-    load_pieces_n<D, NPC, RSTEP>(pq, qb + (size_t)(c + 1) * C * D, Ln, prow, pcol);
-    load_pieces_n<D, NPC, RSTEP>(pk, kb + (size_t)(c + 1) * C * D, Ln, prow, pcol);
-    load_pieces_n<D, NPC, RSTEP>(pv, vb + (size_t)(c + 1) * C * D, Ln, prow, pcol);
+    const int Ln = more ? min(C, T - (c + 1) * C) : 0;
+    load_pieces_n<D, NPC, RSTEP>(pq, qb + (size_t)(c + 1) * C * rse, Ln, prow, pcol, rsb);
+    load_pieces_n<D, NPC, RSTEP>(pk, kb + (size_t)(c + 1) * C * rse, Ln, prow, pcol, rsb);
+    load_pieces_n<D, NPC, RSTEP>(pv, vb + (size_t)(c + 1) * C * rse, Ln, prow, pcol, rsb);
     lds_barrier();
 
     // ---- score tiles (shared): wave w computes tiles w, w + 8, ...; decay factors per tile
@@ -1104,7 +1122,7 @@ __global__ __launch_bounds__(512) void k_output_w8(PrefillParams p) {
 
     // ---- outputs of this wave's row tiles jt(role, j) = role, NJ - 1 - role for its value
     // columns, transposed as in k_output_sh; S split one state-row tile at a time
-    const __amdgpu_buffer_rsrc_t ors = make_rsrc(ob + (size_t)t0 * D, (uint32_t)L * D * 4);
+    const __amdgpu_buffer_rsrc_t ors = make_rsrc(ob + (size_t)t0 * rse * OES, rows_extent(L, rse * OES, D * OES));
     f32x16 num[JPR];
 #pragma unroll
     for (int j = 0; j < JPR; ++j) num[j] = f32x16{};
@@ -1163,13 +1181,11 @@ __global__ __launch_bounds__(512) void k_output_w8(PrefillParams p) {
         for (int it = 0; it <= jt; ++it) r += fN[G::F_R + (jt * (jt + 1) / 2 + it) * 32];
         inv = 1.f / (fN[G::F_THETA + jt * 32] * qz + r + p.eps);
       }
-      const uint32_t row_off = (uint32_t)((jt * 32 + n) * D + Ew + 4 * hh) * 4;
+      const uint32_t row_el = (uint32_t)(jt * 32 + n) * rse + Ew + 4 * hh;
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const u32x4 v4 = {__float_as_uint(num[j][4 * q4] * inv), __float_as_uint(num[j][4 * q4 + 1] * inv),
-                          __float_as_uint(num[j][4 * q4 + 2] * inv), __float_as_uint(num[j][4 * q4 + 3] * inv)};
-        __builtin_amdgcn_raw_buffer_store_b128(v4, ors, row_off + 32 * q4, 0, 0);
-      }
+      for (int q4 = 0; q4 < 4; ++q4)
+        store_out4<OBF>(ors, row_el + 8 * q4, num[j][4 * q4] * inv, num[j][4 * q4 + 1] * inv,
+                        num[j][4 * q4 + 2] * inv, num[j][4 * q4 + 3] * inv);
     }
 
     // ---- state update (every wave: its value columns, all state rows)
@@ -1241,26 +1257,31 @@ __global__ __launch_bounds__(512) void k_output_w8(PrefillParams p) {
   }
 }
 
+// The output kernel for (C, D, flags): the two-waves-per-SIMD kernel where it applies, else
+// the shared-score kernel where its LDS fits, else every wave computes its own scores.
+template <int C, int D, bool DECAY, bool NORM, bool ELU, bool OBF>
+const void* output_kernel(int& lds, int& threads) {
+  if constexpr (W8Geo<C, D, ELU>::FITS) {
+    lds = W8Geo<C, D, ELU>::LDS_BYTES;
+    threads = W8Geo<C, D, ELU>::NT;
+    return (const void*)k_output_w8<C, D, DECAY, NORM, ELU, OBF>;
+  } else if constexpr (ShGeo<C, D, ELU>::FITS) {
+    lds = ShGeo<C, D, ELU>::LDS_BYTES;
+    return (const void*)k_output_sh<C, D, DECAY, NORM, ELU, OBF>;
+  } else {
+    lds = Geo<C, D, true>::LDS_BYTES;
+    return (const void*)k_output<C, D, DECAY, NORM, ELU, OBF>;
+  }
+}
+
 template <int C, int D, bool DECAY, bool NORM, bool ELU>
 hipError_t launch_flags(const PrefillParams& p, hipStream_t s, bool out) {
   const void* kern = (const void*)k_summary<C, D, DECAY, NORM, ELU>;
   int lds = Geo<C, D, false>::LDS_BYTES;
   int threads = 2 * D;
-  if (out) {
-    // the two-waves-per-SIMD kernel where it applies, else the shared-score kernel where its
-    // LDS fits, else every wave computes its own scores
-    if constexpr (W8Geo<C, D, ELU>::FITS) {
-      kern = (const void*)k_output_w8<C, D, DECAY, NORM, ELU>;
-      lds = W8Geo<C, D, ELU>::LDS_BYTES;
-      threads = W8Geo<C, D, ELU>::NT;
-    } else if constexpr (ShGeo<C, D, ELU>::FITS) {
-      kern = (const void*)k_output_sh<C, D, DECAY, NORM, ELU>;
-      lds = ShGeo<C, D, ELU>::LDS_BYTES;
-    } else {
-      kern = (const void*)k_output<C, D, DECAY, NORM, ELU>;
-      lds = Geo<C, D, true>::LDS_BYTES;
-    }
-  }
+  if (out)
+    kern = p.out_bf16 ? output_kernel<C, D, DECAY, NORM, ELU, true>(lds, threads)
+                      : output_kernel<C, D, DECAY, NORM, ELU, false>(lds, threads);
   hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
   dim3 grid(p.n_seg, p.B * p.H);

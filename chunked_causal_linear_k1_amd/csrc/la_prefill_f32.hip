@@ -39,12 +39,13 @@ __host__ __device__ inline F32Layout f32_layout(int C, int d_k, int d_v, int n_p
   return L;
 }
 
-// psi of the chunk rows [0, valid) of x (fp32, row length d_k) into out[C][n_psi]; rows >= valid -> 0.
-__device__ void features_f32(const float* __restrict__ x, float* raw, float* out, int C, int valid, int d_k,
-                             int n_psi, int psi, const float* __restrict__ w) {
+// psi of the chunk rows [0, valid) of x (fp32, row length d_k, rows rs elements apart) into
+// out[C][n_psi]; rows >= valid -> 0.
+__device__ void features_f32(const float* __restrict__ x, size_t rs, float* raw, float* out, int C, int valid,
+                             int d_k, int n_psi, int psi, const float* __restrict__ w) {
   for (int idx = threadIdx.x; idx < C * d_k; idx += kThreads) {
     const int r = idx / d_k;
-    raw[idx] = r < valid ? x[(size_t)idx] : 0.f;
+    raw[idx] = r < valid ? x[(size_t)r * rs + (idx - r * d_k)] : 0.f;
   }
   __syncthreads();
   for (int idx = threadIdx.x; idx < C * n_psi; idx += kThreads) {
@@ -71,8 +72,11 @@ __device__ void features_f32(const float* __restrict__ x, float* raw, float* out
   __syncthreads();
 }
 
-__device__ void load_rows_f32(const float* __restrict__ x, float* out, int C, int valid, int d) {
-  for (int idx = threadIdx.x; idx < C * d; idx += kThreads) out[idx] = (idx / d) < valid ? x[(size_t)idx] : 0.f;
+__device__ void load_rows_f32(const float* __restrict__ x, size_t rs, float* out, int C, int valid, int d) {
+  for (int idx = threadIdx.x; idx < C * d; idx += kThreads) {
+    const int r = idx / d;
+    out[idx] = r < valid ? x[(size_t)r * rs + (idx - r * d)] : 0.f;
+  }
 }
 
 // S <- a S + sum_i xi_i fK_i v_i^T ; Z likewise. Needs FK, V, XI in LDS.
@@ -101,14 +105,17 @@ __global__ __launch_bounds__(kThreads) void k_summary_f32(PrefillParams p) {
   const float lg = p.has_decay ? p.log2g[head] : 0.f;
   const float* w = p.psi == LA_PSI_PRF ? (const float*)p.prf_w + (size_t)head * p.n_psi * p.d_k : nullptr;
   for (int idx = threadIdx.x; idx < p.n_psi * p.d_v + p.n_psi; idx += kThreads) sm[Ly.S + idx] = 0.f;  // S then Z
-  const float* kb = (const float*)p.k + (size_t)bh * p.T * p.d_k;
-  const float* vb = (const float*)p.v + (size_t)bh * p.T * p.d_v;
-  const int c0 = seg * p.seg_chunks, c1 = min(c0 + p.seg_chunks, p.n_chunks);
+  const SeqSpan sq = seq_span(p, bh);
+  const int T = sq.T, n_chunks = (T + p.C - 1) / p.C;
+  const size_t rk = (size_t)p.tok_rows * p.d_k, rv = (size_t)p.tok_rows * p.d_v;  // elements between token rows
+  const float* kb = (const float*)p.k + sq.row0 * p.d_k;
+  const float* vb = (const float*)p.v + sq.row0 * p.d_v;
+  const int c0 = seg * p.seg_chunks, c1 = min(c0 + p.seg_chunks, n_chunks);
   for (int c = c0; c < c1; ++c) {
-    const int t0 = c * p.C, L = min(p.C, p.T - t0);
+    const int t0 = c * p.C, L = min(p.C, T - t0);
     __syncthreads();
-    load_rows_f32(vb + (size_t)t0 * p.d_v, sm + Ly.V, p.C, L, p.d_v);
-    features_f32(kb + (size_t)t0 * p.d_k, sm + Ly.RAW, sm + Ly.FK, p.C, L, p.d_k, p.n_psi, p.psi, w);
+    load_rows_f32(vb + (size_t)t0 * rv, rv, sm + Ly.V, p.C, L, p.d_v);
+    features_f32(kb + (size_t)t0 * rk, rk, sm + Ly.RAW, sm + Ly.FK, p.C, L, p.d_k, p.n_psi, p.psi, w);
     state_update_f32(sm, Ly, p.C, L, p.d_v, p.n_psi, lg);
   }
   __syncthreads();
@@ -128,17 +135,20 @@ __global__ __launch_bounds__(kThreads) void k_output_f32(PrefillParams p) {
   const float* pre = p.ws + ((size_t)bh * p.n_seg + seg) * E;
   for (int idx = threadIdx.x; idx < (int)E; idx += kThreads) sm[Ly.S + idx] = pre[idx];  // S then Z
   for (int j = threadIdx.x; j < C; j += kThreads) sm[Ly.THETA + j] = gpow(lg, (float)(j + 1));
-  const float* qb = (const float*)p.q + (size_t)bh * p.T * p.d_k;
-  const float* kb = (const float*)p.k + (size_t)bh * p.T * p.d_k;
-  const float* vb = (const float*)p.v + (size_t)bh * p.T * d_v;
-  float* ob = (float*)p.o + (size_t)bh * p.T * d_v;
-  const int c0 = seg * p.seg_chunks, c1 = min(c0 + p.seg_chunks, p.n_chunks);
+  const SeqSpan sq = seq_span(p, bh);
+  const int T = sq.T, n_chunks = (T + C - 1) / C;
+  const size_t rk = (size_t)p.tok_rows * p.d_k, rv = (size_t)p.tok_rows * d_v;  // elements between token rows
+  const float* qb = (const float*)p.q + sq.row0 * p.d_k;
+  const float* kb = (const float*)p.k + sq.row0 * p.d_k;
+  const float* vb = (const float*)p.v + sq.row0 * d_v;
+  float* ob = (float*)p.o + sq.row0 * d_v;
+  const int c0 = seg * p.seg_chunks, c1 = min(c0 + p.seg_chunks, n_chunks);
   for (int c = c0; c < c1; ++c) {
-    const int t0 = c * C, L = min(C, p.T - t0);
+    const int t0 = c * C, L = min(C, T - t0);
     __syncthreads();
-    load_rows_f32(vb + (size_t)t0 * d_v, sm + Ly.V, C, L, d_v);
-    features_f32(qb + (size_t)t0 * p.d_k, sm + Ly.RAW, sm + Ly.FQ, C, L, p.d_k, n_psi, p.psi, w);
-    features_f32(kb + (size_t)t0 * p.d_k, sm + Ly.RAW, sm + Ly.FK, C, L, p.d_k, n_psi, p.psi, w);
+    load_rows_f32(vb + (size_t)t0 * rv, rv, sm + Ly.V, C, L, d_v);
+    features_f32(qb + (size_t)t0 * rk, rk, sm + Ly.RAW, sm + Ly.FQ, C, L, p.d_k, n_psi, p.psi, w);
+    features_f32(kb + (size_t)t0 * rk, rk, sm + Ly.RAW, sm + Ly.FK, C, L, p.d_k, n_psi, p.psi, w);
     // scores
     for (int idx = threadIdx.x; idx < C * C; idx += kThreads) {
       const int j = idx / C, i = idx % C;
@@ -167,7 +177,7 @@ __global__ __launch_bounds__(kThreads) void k_output_f32(PrefillParams p) {
       for (int i = 0; i <= j; ++i) intra += sm[Ly.A + j * C + i] * sm[Ly.V + i * d_v + e];
       float num = sm[Ly.THETA + j] * inter + intra;
       if (p.normalize) num = num / sm[Ly.DEN + j];
-      ob[(size_t)(t0 + j) * d_v + e] = num;
+      ob[(size_t)(t0 + j) * rv + e] = num;
     }
     __syncthreads();
     state_update_f32(sm, Ly, C, L, d_v, n_psi, lg);

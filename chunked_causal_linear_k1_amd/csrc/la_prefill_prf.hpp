@@ -264,18 +264,21 @@ __global__ __launch_bounds__(2 * D) void k_summary_prf(PrefillParams p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) zacc[f][r] = 0.f;
 
-  const uint16_t* kg = (const uint16_t*)p.k + (size_t)bh * p.T * D;
-  const uint16_t* vg = (const uint16_t*)p.v + (size_t)bh * p.T * D;
-  const int c0 = seg * p.seg_chunks, c1 = min(c0 + p.seg_chunks, p.n_chunks);
+  const SeqSpan sq = seq_span(p, bh);
+  const int T = sq.T, n_chunks = (T + C - 1) / C;
+  const uint32_t rse = (uint32_t)p.tok_rows * D, rsb = rse * 2;  // elements / bytes between token rows
+  const uint16_t* kg = (const uint16_t*)p.k + sq.row0 * D;
+  const uint16_t* vg = (const uint16_t*)p.v + sq.row0 * D;
+  const int c0 = seg * p.seg_chunks, c1 = min(c0 + p.seg_chunks, n_chunks);
   pf::Pieces<C, D> pk_, pv_;
   {
-    const int L0 = min(C, p.T - c0 * C);
-    pf::load_pieces<C, D>(pk_, kg + (size_t)c0 * C * D, L0);
-    pf::load_pieces<C, D>(pv_, vg + (size_t)c0 * C * D, L0);
+    const int L0 = min(C, T - c0 * C);
+    pf::load_pieces<C, D>(pk_, kg + (size_t)c0 * C * rse, L0, rsb);
+    pf::load_pieces<C, D>(pv_, vg + (size_t)c0 * C * rse, L0, rsb);
     vm_drain();
   }
   for (int c = c0; c < c1; ++c) {
-    const int L = min(C, p.T - c * C);
+    const int L = min(C, T - c * C);
     const float a = DECAY ? exp2f((float)L * lg) : 1.f;
     lds_barrier();  // the previous chunk is done with LDS
     commit_raw_norm<C, D>(pk_, rkP, PR * 2, sF + G::F_NK, prow, tid);
@@ -283,9 +286,9 @@ __global__ __launch_bounds__(2 * D) void k_summary_prf(PrefillParams p) {
     for (int i = 0; i < NPC; ++i) *(uint4*)(vP + i * 16 * PV * 2) = pv_.r[i];
     {
       const bool more = c + 1 < c1;
-      const int Ln = more ? min(C, p.T - (c + 1) * C) : 0;
-      pf::load_pieces<C, D>(pk_, kg + (size_t)(c + 1) * C * D, Ln);
-      pf::load_pieces<C, D>(pv_, vg + (size_t)(c + 1) * C * D, Ln);
+      const int Ln = more ? min(C, T - (c + 1) * C) : 0;
+      pf::load_pieces<C, D>(pk_, kg + (size_t)(c + 1) * C * rse, Ln, rsb);
+      pf::load_pieces<C, D>(pv_, vg + (size_t)(c + 1) * C * rse, Ln, rsb);
     }
     lds_barrier();
     // K~_t = Xi_t psi(k_t) for this wave's features; padded tokens give exactly zero
@@ -338,7 +341,7 @@ __global__ __launch_bounds__(2 * D) void k_summary_prf(PrefillParams p) {
 // ---------------------------------------------------------------------------------------
 // Output pass: per (sequence, segment), from the segment's exclusive prefix (written by
 // the scan), walk the chunks: features, shared score tiles, outputs, state update.
-template <int C, int D, int NP, bool DECAY, bool NORM>
+template <int C, int D, int NP, bool DECAY, bool NORM, bool OBF>
 __global__ __launch_bounds__(2 * D) void k_output_prf(PrefillParams p) {
   using G = Geo<C, D, NP, true>;
   using PG = pf::Geo<C, D, true>;
@@ -401,21 +404,26 @@ __global__ __launch_bounds__(2 * D) void k_output_prf(PrefillParams p) {
     }
   }
 
-  const uint16_t* qg = (const uint16_t*)p.q + (size_t)bh * p.T * D;
-  const uint16_t* kg = (const uint16_t*)p.k + (size_t)bh * p.T * D;
-  const uint16_t* vg = (const uint16_t*)p.v + (size_t)bh * p.T * D;
-  float* ob = (float*)p.o + (size_t)bh * p.T * D;
-  const int c0 = seg * p.seg_chunks, c1 = min(c0 + p.seg_chunks, p.n_chunks);
+  const SeqSpan sq = seq_span(p, bh);
+  const int T = sq.T, n_chunks = (T + C - 1) / C;
+  const uint32_t rse = (uint32_t)p.tok_rows * D, rsb = rse * 2;  // elements / bytes between token rows
+  constexpr int OES = OBF ? 2 : 4;  // output element bytes
+  const uint16_t* qg = (const uint16_t*)p.q + sq.row0 * D;
+  const uint16_t* kg = (const uint16_t*)p.k + sq.row0 * D;
+  const uint16_t* vg = (const uint16_t*)p.v + sq.row0 * D;
+  unsigned char* ob = (unsigned char*)p.o + sq.row0 * D * OES;
+  const int c0 = seg * p.seg_chunks, c1 = min(c0 + p.seg_chunks, n_chunks);
+  if (c0 >= c1) return;  // segment past the end of a shorter sequence: nothing to write
   pf::Pieces<C, D> pq_, pk_, pv_;
   {
-    const int L0 = min(C, p.T - c0 * C);
-    pf::load_pieces<C, D>(pq_, qg + (size_t)c0 * C * D, L0);
-    pf::load_pieces<C, D>(pk_, kg + (size_t)c0 * C * D, L0);
-    pf::load_pieces<C, D>(pv_, vg + (size_t)c0 * C * D, L0);
+    const int L0 = min(C, T - c0 * C);
+    pf::load_pieces<C, D>(pq_, qg + (size_t)c0 * C * rse, L0, rsb);
+    pf::load_pieces<C, D>(pk_, kg + (size_t)c0 * C * rse, L0, rsb);
+    pf::load_pieces<C, D>(pv_, vg + (size_t)c0 * C * rse, L0, rsb);
     vm_drain();
   }
   for (int c = c0; c < c1; ++c) {
-    const int t0 = c * C, L = min(C, p.T - t0);
+    const int t0 = c * C, L = min(C, T - t0);
     const float a = DECAY ? exp2f((float)L * lg) : 1.f;
     lds_barrier();  // the previous chunk is done with LDS (and Z is updated)
     commit_raw_norm<C, D>(pq_, rqP, PR * 2, sF + G::F_NQ, prow, tid);
@@ -424,10 +432,10 @@ __global__ __launch_bounds__(2 * D) void k_output_prf(PrefillParams p) {
     for (int i = 0; i < NPC; ++i) *(uint4*)(vP + i * 16 * PV * 2) = pv_.r[i];
     {
       const bool more = c + 1 < c1;
-      const int Ln = more ? min(C, p.T - (c + 1) * C) : 0;
-      pf::load_pieces<C, D>(pq_, qg + (size_t)(c + 1) * C * D, Ln);
-      pf::load_pieces<C, D>(pk_, kg + (size_t)(c + 1) * C * D, Ln);
-      pf::load_pieces<C, D>(pv_, vg + (size_t)(c + 1) * C * D, Ln);
+      const int Ln = more ? min(C, T - (c + 1) * C) : 0;
+      pf::load_pieces<C, D>(pq_, qg + (size_t)(c + 1) * C * rse, Ln, rsb);
+      pf::load_pieces<C, D>(pk_, kg + (size_t)(c + 1) * C * rse, Ln, rsb);
+      pf::load_pieces<C, D>(pv_, vg + (size_t)(c + 1) * C * rse, Ln, rsb);
     }
     lds_barrier();
 
@@ -510,7 +518,7 @@ __global__ __launch_bounds__(2 * D) void k_output_prf(PrefillParams p) {
     lds_barrier();
 
     // ---- outputs, transposed as in k_output_sh: numT[e][j] (M = value column, N = token)
-    const __amdgpu_buffer_rsrc_t ors = make_rsrc(ob + (size_t)t0 * D, (uint32_t)L * D * 4);
+    const __amdgpu_buffer_rsrc_t ors = make_rsrc(ob + (size_t)t0 * rse * OES, rows_extent(L, rse * OES, D * OES));
     f32x16 num[NJ];
 #pragma unroll
     for (int jt = 0; jt < NJ; ++jt) num[jt] = f32x16{};
@@ -567,13 +575,11 @@ __global__ __launch_bounds__(2 * D) void k_output_prf(PrefillParams p) {
         for (int it = 0; it <= jt; ++it) r += fN[G::F_R + (jt * (jt + 1) / 2 + it) * 32];
         inv = 1.f / (fN[G::F_THETA + jt * 32] * qz + r + p.eps);
       }
-      const uint32_t row_off = (uint32_t)((jt * 32 + n) * D + Ew + 4 * hh) * 4;
+      const uint32_t row_el = (uint32_t)(jt * 32 + n) * rse + Ew + 4 * hh;
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const u32x4 v4 = {__float_as_uint(num[jt][4 * q4] * inv), __float_as_uint(num[jt][4 * q4 + 1] * inv),
-                          __float_as_uint(num[jt][4 * q4 + 2] * inv), __float_as_uint(num[jt][4 * q4 + 3] * inv)};
-        __builtin_amdgcn_raw_buffer_store_b128(v4, ors, row_off + 32 * q4, 0, 0);
-      }
+      for (int q4 = 0; q4 < 4; ++q4)
+        store_out4<OBF>(ors, row_el + 8 * q4, num[jt][4 * q4] * inv, num[jt][4 * q4 + 1] * inv,
+                        num[jt][4 * q4 + 2] * inv, num[jt][4 * q4 + 3] * inv);
     }
 
     // ---- state update: S <- gamma^L S + K~^T V, Z <- gamma^L Z + sum_i Xi_i psi(k_i)
@@ -615,7 +621,9 @@ __global__ __launch_bounds__(2 * D) void k_output_prf(PrefillParams p) {
 
 template <int C, int D, int NP, bool DECAY, bool NORM>
 hipError_t launch_flags(const PrefillParams& p, hipStream_t s, bool out) {
-  const void* kern = out ? (const void*)k_output_prf<C, D, NP, DECAY, NORM> : (const void*)k_summary_prf<C, D, NP, DECAY, NORM>;
+  const void* kern = !out ? (const void*)k_summary_prf<C, D, NP, DECAY, NORM>
+                     : p.out_bf16 ? (const void*)k_output_prf<C, D, NP, DECAY, NORM, true>
+                                  : (const void*)k_output_prf<C, D, NP, DECAY, NORM, false>;
   const int lds = out ? Geo<C, D, NP, true>::LDS_BYTES : Geo<C, D, NP, false>::LDS_BYTES;
   hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;

@@ -43,12 +43,17 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_segment_scan(ScanParams p) {
   const bool live = e < E;
   const float lg = p.has_decay ? p.log2g[head] : 0.f;
   float* base = p.ws + (size_t)bh * p.n_seg * E + e;
+  int T = p.T;  // this sequence's length
+  if (p.cu_seqlens) {
+    int start;
+    T = packed_len(p.cu_seqlens, bh / p.H, p.total, p.T, &start);
+  }
 
   // this wave's run of segments
   const int per = (p.n_seg + W - 1) / W;
   const int s0 = min(w * per, p.n_seg), s1 = min(s0 + per, p.n_seg);
   auto seg_decay = [&](int s) {
-    const int len = min(p.seg_len, p.T - s * p.seg_len);
+    const int len = max(0, min(p.seg_len, T - s * p.seg_len));  // 0 past a shorter sequence's end
     return gpow(lg, (float)len);
   };
 

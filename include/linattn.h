@@ -71,6 +71,13 @@ typedef enum {
 
 typedef enum { LA_BF16 = 0, LA_F32 = 1 } la_dtype;
 
+/* Layout of the token tensors q, k, v and o of lin_attn_prefill (d is d_k or d_v). */
+typedef enum {
+  LA_LAYOUT_BHTD = 0, /* [B, H, T, d]: each head's tokens contiguous                  */
+  LA_LAYOUT_BTHD = 1  /* [B, T, H, d]: heads interleaved per token, the layout of a   *
+                       * projection output viewed as (B, T, H, d), no transpose needed */
+} la_layout;
+
 /* Prefill (training / prompt) problem description. All fields are int32 so the
  * struct has the same layout from C, C++ and ctypes. */
 typedef struct {
@@ -83,7 +90,10 @@ typedef struct {
   int32_t normalize;     /* 1: divide by psi(q).Z + eps; 0: numerator only       */
   float eps;             /* >= 0; used only when normalize == 1                  */
   int32_t in_dtype;      /* la_dtype of q, k, v and prf_w                        */
-  int32_t out_dtype;     /* la_dtype of o (LA_F32 only in this build)            */
+  int32_t out_dtype;     /* la_dtype of o: LA_F32, or LA_BF16 = the fp32 result
+                            rounded to nearest even (in_dtype LA_BF16 only)      */
+  int32_t layout;        /* la_layout of q, k, v, o (0 = [B, H, T, d]); states
+                            are [B, H, n_psi, d_v] in every layout               */
 } la_prefill_desc;
 
 /* Supported sizes in this build (anything else: LA_ERR_UNSUPPORTED):
@@ -93,10 +103,12 @@ typedef struct {
  *   in_dtype LA_F32 : d_k, d_v <= 128, n_psi <= 256 (LDS permitting),
  *                     chunk in {16, 32, 64}, any psi.
  *   always: d_v and n_psi multiples of 4 (16-byte state rows in the workspace).
+ *   out_dtype LA_BF16 with in_dtype LA_BF16 only.
  *   gamma: when given, at most LA_MAX_DECAY_HEADS heads.                        */
 #define LA_MAX_DECAY_HEADS 256
 
-/* Device workspace bytes lin_attn_prefill needs for `d` (0 is possible).
+/* Device workspace bytes lin_attn_prefill (or lin_attn_prefill_varlen, with B the
+ * number of sequences and T the longest length) needs for `d` (0 is possible).
  * Pure host function. Returns LA_OK and writes *bytes, or a validation error. */
 la_status lin_attn_prefill_workspace_size(const la_prefill_desc* d, size_t* bytes);
 
@@ -108,14 +120,15 @@ la_status lin_attn_prefill_workspace_size(const la_prefill_desc* d, size_t* byte
  * Retentive Networks", section C, whose summaries combine as
  * (a1, S1) (+) (a2, S2) = (a1 a2, a2 S1 + S2)).
  *
- *   q, k      device [B, H, T, d_k] in_dtype
- *   v         device [B, H, T, d_v] in_dtype
+ *   q, k      device [B, H, T, d_k] in_dtype ([B, T, H, d_k] for LA_LAYOUT_BTHD)
+ *   v         device [B, H, T, d_v] in_dtype (likewise)
  *   gamma     host   [H] fp32 per-head decay, 0 < gamma <= 1; NULL means 1
  *   prf_w     device [H, n_psi, d_k] in_dtype (the PRF bank, one per head,
  *             shared over the batch); required iff psi == LA_PSI_PRF
  *   init_S    device [B, H, n_psi, d_v] fp32 state before token 1, or NULL (zero)
  *   init_Z    device [B, H, n_psi] fp32, or NULL (zero); ignored when normalize == 0
- *   o         device [B, H, T, d_v] out_dtype, written for every t < T
+ *   o         device [B, H, T, d_v] out_dtype ([B, T, H, d_v] for LA_LAYOUT_BTHD),
+ *             written for every t < T
  *   final_S   device [B, H, n_psi, d_v] fp32 state after token T, or NULL
  *   final_Z   device [B, H, n_psi] fp32, or NULL; not written when normalize == 0
  *             (without a denominator the normaliser is not maintained)
@@ -127,6 +140,34 @@ la_status lin_attn_prefill(const la_prefill_desc* d, const void* q, const void* 
                            const float* gamma, const void* prf_w, const float* init_S,
                            const float* init_Z, void* o, float* final_S, float* final_Z,
                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * lin_attn_prefill over a batch of sequences of different lengths packed end to end
+ * (the variable-length batches of serving, where prompts of many lengths are
+ * prefilled together; "Log-Depth Chunked Linear-Attention Scan", Implementation
+ * notes: every sequence's ragged tail contributes zero). Each sequence is an
+ * independent problem with its own state; no token attends across a boundary.
+ *
+ *   d           as for lin_attn_prefill with B = number of sequences and
+ *               T = the longest sequence length (host value, >= every length);
+ *               layout must be LA_LAYOUT_BTHD (tokens of all heads interleaved)
+ *   cu_seqlens  device [B + 1] int32: sequence b is tokens
+ *               [cu_seqlens[b], cu_seqlens[b+1]) of the packed tensors;
+ *               cu_seqlens[0] = 0, non-decreasing, cu_seqlens[B] = total_tokens.
+ *               Lengths may be 0 (no output; final state = initial state).
+ *               Offsets outside these rules give unspecified outputs but are
+ *               clamped, so no access falls outside the tensors.
+ *   total_tokens host, >= 0: tokens in the packed tensors
+ *   q, k        device [total_tokens, H, d_k];  v device [total_tokens, H, d_v]
+ *   o           device [total_tokens, H, d_v] out_dtype
+ *   init_S, init_Z, final_S, final_Z: per sequence, [B, H, n_psi, d_v] / [B, H, n_psi]
+ *   other arguments as for lin_attn_prefill.
+ */
+la_status lin_attn_prefill_varlen(const la_prefill_desc* d, const int32_t* cu_seqlens, int32_t total_tokens,
+                                  const void* q, const void* k, const void* v, const float* gamma,
+                                  const void* prf_w, const float* init_S, const float* init_Z, void* o,
+                                  float* final_S, float* final_Z, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream);
 
 /*
  * lin_attn_prefill with phase timing for profilers and benchmarks: identical work

@@ -66,7 +66,14 @@ def _ws(desc):
     (dict(psi=3), LA_ERR_VALUE), (dict(normalize=2), LA_ERR_VALUE), (dict(eps=-1.0), LA_ERR_VALUE),
     (dict(eps=float("nan")), LA_ERR_VALUE), (dict(in_dtype=5), LA_ERR_VALUE),
     (dict(chunk=48), LA_ERR_UNSUPPORTED), (dict(d_k=96, d_v=96, n_psi=96), LA_ERR_UNSUPPORTED),
-    (dict(out_dtype=LA_BF16), LA_ERR_UNSUPPORTED),
+    (dict(out_dtype=LA_BF16), LA_OK),                      # bf16 output = RNE of the fp32 result
+    (dict(out_dtype=LA_BF16, in_dtype=LA_F32, d_k=64, d_v=64, n_psi=64), LA_ERR_UNSUPPORTED),
+    (dict(out_dtype=7), LA_ERR_VALUE),
+    # token layout: [B, H, T, d] or [B, T, H, d]
+    (dict(layout=1), LA_OK), (dict(layout=1, in_dtype=LA_F32, d_k=64, d_v=64, n_psi=64), LA_OK),
+    (dict(layout=2), LA_ERR_VALUE), (dict(layout=-1), LA_ERR_VALUE),
+    # one interleaved chunk of one head must fit a 32-bit buffer range: C * H * d * 4 < 2^31
+    (dict(layout=1, H=32768, chunk=128), LA_ERR_UNSUPPORTED), (dict(layout=1, H=512, chunk=128), LA_OK),
     (dict(in_dtype=LA_F32, chunk=128), LA_ERR_UNSUPPORTED),
     (dict(), LA_OK), (dict(chunk=128), LA_OK), (dict(d_k=64, d_v=64, n_psi=64), LA_OK),
     (dict(in_dtype=LA_F32, d_k=64, d_v=64, n_psi=64, chunk=64), LA_OK),
@@ -131,6 +138,27 @@ def test_prefill_rejects_bad_pointers_before_launch():
     if st == LA_OK:
         assert lib.lin_attn_prefill(ctypes.byref(dp), fake, fake, fake, None, None, None, None, fake, None, None,
                                     fake, wsp, None) == LA_ERR_NULL
+
+
+def test_varlen_rejects_bad_arguments_before_launch():
+    lib = binding.load()
+    d = _desc(B=3, T=700, layout=1)   # 3 packed sequences, longest 700 tokens
+    _, ws = _ws(d)
+    fake = ctypes.c_void_p(1 << 20)
+    cu = ctypes.c_void_p(1 << 21)
+
+    def call(desc=d, cu_=cu, total=1200, q=fake, o=fake, w=fake, wb=ws):
+        return lib.lin_attn_prefill_varlen(ctypes.byref(desc), cu_, total, q, fake, fake, None, None, None, None, o,
+                                           None, None, w, wb, None)
+    assert call(cu_=None) == LA_ERR_NULL
+    assert call(total=-1) == LA_ERR_SHAPE
+    assert call(cu_=ctypes.c_void_p((1 << 21) + 2)) == LA_ERR_ALIGN   # int32 offsets: 4-byte aligned
+    assert call(desc=_desc(B=3, T=700, layout=0)) == LA_ERR_VALUE    # packed tokens interleave the heads
+    assert call(q=None) == LA_ERR_NULL
+    assert call(w=None) == LA_ERR_WORKSPACE
+    # the workspace is sized like a fixed-length call with B sequences of the longest length
+    st, ws_fixed = _ws(_desc(B=3, T=700))
+    assert st == LA_OK and ws_fixed == ws
 
 
 def test_decode_validation():

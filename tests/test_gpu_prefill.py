@@ -83,6 +83,23 @@ def test_small_elementwise(case):
     assert_close(o.cpu().reshape(B * H, T, d).numpy(), ref, dt, name)
 
 
+@pytest.mark.parametrize("d,C,decay", [(128, 128, "retnet_spread"), (128, 64, "retnet_spread"), (64, 64, "none"),
+                                       (64, 128, "const:0.97")])
+def test_identity_with_denominator(d, C, decay):
+    """Identity features with the denominator. With signed q and k the dot psi(q).Z can pass
+    through zero and the output has no bound, so here q and k are made non-negative: the
+    denominator is then a positive sum and the normalised output a weighted mean of v."""
+    T = 601
+    w = Workload(name=f"identity_norm_d{d}_c{C}", B=1, H=3, T=T, d_k=d, d_v=d, n_psi=d, chunk=C, psi=PSI_IDENTITY,
+                 normalize=1, eps=1e-6, dtype="bf16", seed=d + C, qk_scale=d ** -0.5, v_scale=1.0, decay=decay)
+    announce(f"prefill identity with denominator d={d} C={C}")
+    inp = inputs.make_prefill_inputs(w, device="cpu")
+    inp["q"], inp["k"] = inp["q"].abs(), inp["k"].abs()
+    o = _run(w, inp)
+    ref = _oracle_o(w, inp)
+    assert_close(o.cpu().reshape(3, T, d).numpy(), ref, "bf16", w.name)
+
+
 def test_tiny_f32_workload_full():
     """The 1 x 1 x 1024, d = 64, C = 64, elu+1 fp32 workload, every output."""
     w = workloads.TINY_F32
