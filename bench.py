@@ -75,17 +75,23 @@ def mfma_from_profiles(kernel_key: str):
     return {"kernel": kernel_key, "mfma_busy_pct": r["mfma_busy_pct"], "mfma_bf16_flops": r["mfma_bf16_flops"]}
 
 
-def bench_prefill(w: workloads.Workload, steps: int, warmup: int):
-    log(f"prefill {w.name}: generating inputs on the GPU")
+def bench_prefill(w: workloads.Workload, steps: int, warmup: int, layout: str = "bhtd",
+                  out_dtype: torch.dtype = torch.float32):
+    log(f"prefill {w.name} ({layout}, {out_dtype}): generating inputs on the GPU")
     inp = inputs.make_prefill_inputs(w, device="cuda")
+    if layout == "bthd":  # the same tokens in [B, T, H, d]
+        for key in ("q", "k", "v"):
+            inp[key] = inp[key].transpose(1, 2).contiguous()
     g = inp["gamma"]
     gam = None if g is None else list(g)
-    o = torch.empty((w.B, w.H, w.T, w.d_v), dtype=torch.float32, device="cuda")
+    shape = (w.B, w.H, w.T, w.d_v) if layout == "bhtd" else (w.B, w.T, w.H, w.d_v)
+    o = torch.empty(shape, dtype=out_dtype, device="cuda")
     desc = binding.prefill_desc(w.B, w.H, w.T, w.d_k, w.d_v, w.n_psi, w.chunk, w.psi, w.normalize, w.eps,
-                                binding.LA_BF16)
+                                binding.LA_BF16, binding.LA_BF16 if out_dtype == torch.bfloat16 else binding.LA_F32,
+                                binding.LA_LAYOUT_BHTD if layout == "bhtd" else binding.LA_LAYOUT_BTHD)
     ws = torch.empty(max(binding.workspace_size(desc), 16), dtype=torch.uint8, device="cuda")
     kw = dict(psi=w.psi, chunk=w.chunk, normalize=w.normalize, eps=w.eps, gamma=gam, prf_w=inp["prf_w"], o=o,
-              workspace=ws)
+              workspace=ws, layout=layout)
     for _ in range(warmup):
         binding.lin_attn_prefill(inp["q"], inp["k"], inp["v"], **kw)
     torch.cuda.synchronize()
@@ -112,6 +118,37 @@ def bench_prefill(w: workloads.Workload, steps: int, warmup: int):
                      "output": float(phases[:, 2].mean())},
         "units": units,
     }
+    del inp, o, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_varlen(w: workloads.VarlenWorkload, steps: int, warmup: int):
+    """Whole lin_attn_prefill_varlen calls on a packed batch, event-timed on the current stream."""
+    log(f"prefill {w.name}: generating packed inputs on the GPU")
+    inp = inputs.make_varlen_inputs(w, device="cuda")
+    g = inp["gamma"]
+    kw = dict(psi=w.psi, chunk=w.chunk, normalize=w.normalize, eps=w.eps, gamma=None if g is None else list(g))
+    o = torch.empty((inp["q"].shape[0], w.H, w.d_v), dtype=torch.float32, device="cuda")
+    desc = binding.prefill_desc(w.N, w.H, inp["max_len"], w.d_k, w.d_v, w.n_psi, w.chunk, w.psi, w.normalize, w.eps,
+                                binding.LA_BF16, binding.LA_F32, binding.LA_LAYOUT_BTHD)
+    ws = torch.empty(max(binding.varlen_workspace_size(desc, inp["q"].shape[0]), 16), dtype=torch.uint8,
+                     device="cuda")
+    args = (inp["q"], inp["k"], inp["v"], inp["cu_seqlens"], inp["max_len"])
+    for _ in range(warmup):
+        binding.lin_attn_prefill_varlen(*args, o=o, workspace=ws, **kw)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        binding.lin_attn_prefill_varlen(*args, o=o, workspace=ws, **kw)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    units = sum(inp["lengths"]) * w.H
+    res = {"ms_per_step": ms, "token_heads_per_s": units / (ms * 1e-3), "units": units,
+           "lengths": {"n": w.N, "min": min(inp["lengths"]), "max": inp["max_len"], "total": sum(inp["lengths"])}}
     del inp, o, ws
     torch.cuda.empty_cache()
     return res
@@ -218,7 +255,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--no-extra", action="store_true", help="headline workload only (no 8k elu+1 and PRF lines)")
+    ap.add_argument("--no-extra", action="store_true", help="headline workload only (no 8k elu+1, PRF, layout, bf16-output and packed-batch lines)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="first run one plain copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -282,6 +319,31 @@ def main():
                 tf = 286720 * px["units"] / (px["ms_per_step"] * 1e-3) / 1e12
                 line[key]["mfma_roofline"] = {"bound": "mfma", "achieved": round(tf, 1), "peak": 2500.0,
                                               "unit": "TFLOP/s", "frac": round(tf / 2500.0, 4)}
+        # the 128k workload in the other token layout and with bf16 output (o = the fp32 result
+        # rounded to nearest even: 768 + 256 algorithmic bytes per token-head)
+        for key, layout, odt, bpt in (("prefill_128k_bthd", "bthd", torch.float32, BYTES_PER_TOKEN_HEAD),
+                                      ("prefill_128k_bf16_out", "bhtd", torch.bfloat16, 3 * 128 * 2 + 128 * 2)):
+            px = bench_prefill(w, args.steps, args.warmup, layout=layout, out_dtype=odt)
+            ao = bpt * px["units"] / (px["phase_ms"]["output"] * 1e-3) / 1e9
+            ax = bpt * px["units"] / (px["ms_per_step"] * 1e-3) / 1e9
+            line[key] = {"workload": w.name, "layout": layout, "output": str(odt).replace("torch.", ""),
+                         "token_heads_per_s": round(px["token_heads_per_s"], 1),
+                         "ms_per_step": round(px["ms_per_step"], 4),
+                         "phase_ms": {k: round(v, 4) for k, v in px["phase_ms"].items()},
+                         "roofline": {"kernel": "output pass", "bound": "hbm", "achieved": round(ao, 1),
+                                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ao / HBM_PEAK_GBS, 4),
+                                      "bytes_per_token_head": bpt},
+                         "whole_call_roofline": {"bound": "hbm", "achieved": round(ax, 1), "peak": HBM_PEAK_GBS,
+                                                 "unit": "GB/s", "frac": round(ax / HBM_PEAK_GBS, 4)}}
+        vw = workloads.VARLEN_32
+        pv = bench_varlen(vw, args.steps, args.warmup)
+        av = BYTES_PER_TOKEN_HEAD * pv["units"] / (pv["ms_per_step"] * 1e-3) / 1e9
+        line["prefill_varlen"] = {"workload": vw.name, "sequences": pv["lengths"], "H": vw.H, "chunk": vw.chunk,
+                                  "token_heads_per_s": round(pv["token_heads_per_s"], 1),
+                                  "ms_per_step": round(pv["ms_per_step"], 4),
+                                  "whole_call_roofline": {"bound": "hbm", "achieved": round(av, 1),
+                                                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                                          "frac": round(av / HBM_PEAK_GBS, 4)}}
     if not args.no_decode:
         dw = workloads.DECODE_32x64
         for key, reps, note in (("decode", 1, "as configured: the 129 MiB state is re-read every step and can "

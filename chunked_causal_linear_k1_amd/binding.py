@@ -25,7 +25,7 @@ LA_LAYOUT_BHTD, LA_LAYOUT_BTHD = 0, 1
 MAX_DECAY_HEADS = 256
 
 EXPORTED = ("lin_attn_prefill_workspace_size", "lin_attn_prefill", "lin_attn_prefill_profiled",
-            "lin_attn_prefill_varlen", "lin_attn_decode_step", "lin_attn_status_string", "lin_attn_version")
+            "lin_attn_prefill_varlen", "lin_attn_prefill_varlen_workspace_size", "lin_attn_decode_step", "lin_attn_status_string", "lin_attn_version")
 
 
 class PrefillDesc(ctypes.Structure):
@@ -68,6 +68,9 @@ def load() -> ctypes.CDLL:
         lib.lin_attn_prefill_profiled.restype = ctypes.c_int
         lib.lin_attn_prefill_profiled.argtypes = lib.lin_attn_prefill.argtypes + [ctypes.POINTER(ctypes.c_void_p)]
         lib.lin_attn_prefill_varlen.restype = ctypes.c_int
+        lib.lin_attn_prefill_varlen_workspace_size.restype = ctypes.c_int
+        lib.lin_attn_prefill_varlen_workspace_size.argtypes = [ctypes.POINTER(PrefillDesc), ctypes.c_int32,
+                                                               ctypes.POINTER(ctypes.c_size_t)]
         lib.lin_attn_prefill_varlen.argtypes = [ctypes.POINTER(PrefillDesc), vp, ctypes.c_int32, vp, vp, vp, fp, vp,
                                                 vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         lib.lin_attn_decode_step.restype = ctypes.c_int
@@ -125,6 +128,14 @@ def workspace_size(desc: PrefillDesc) -> int:
     st = load().lin_attn_prefill_workspace_size(ctypes.byref(desc), ctypes.byref(n))
     if st != LA_OK:
         raise LinAttnError(st, "lin_attn_prefill_workspace_size")
+    return int(n.value)
+
+
+def varlen_workspace_size(desc: PrefillDesc, total_tokens: int) -> int:
+    n = ctypes.c_size_t(0)
+    st = load().lin_attn_prefill_varlen_workspace_size(ctypes.byref(desc), int(total_tokens), ctypes.byref(n))
+    if st != LA_OK:
+        raise LinAttnError(st, "lin_attn_prefill_varlen_workspace_size")
     return int(n.value)
 
 
@@ -198,7 +209,7 @@ def lin_attn_prefill_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, c
         o = torch.empty((total, H, d_v), dtype=out_dtype, device=q.device)
     desc = prefill_desc(N, H, max_seqlen, d_k, d_v, n_psi, chunk, psi, normalize, eps, _dtype_code(q),
                         _dtype_code(o), LA_LAYOUT_BTHD)
-    ws_bytes = workspace_size(desc)
+    ws_bytes = varlen_workspace_size(desc, total)
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     g = _gamma_array(gamma, H)

@@ -79,16 +79,31 @@ struct Plan {
   size_t ws_bytes;
 };
 
-Plan make_plan(const la_prefill_desc* d) {
+// total_tokens < 0: a fixed-length batch (every sequence T tokens), cut into the same number
+// of segments per sequence. total_tokens >= 0: a packed batch whose lengths only the device
+// knows (T is the longest); segments then have a fixed token count sized from the batch's
+// total, so the non-empty workgroups number about kTargetWorkgroups and carry similar work
+// whatever the length mix (segments past a shorter sequence's end are empty and exit at once).
+Plan make_plan(const la_prefill_desc* d, long long total_tokens = -1) {
   Plan pl;
   const long long BH = (long long)d->B * d->H;
   pl.n_chunks = (int)((d->T + (long long)d->chunk - 1) / d->chunk);
-  long long want = (kTargetWorkgroups + BH - 1) / BH;  // segments per sequence
-  want = std::min<long long>(want, std::max(1LL, (long long)d->T / kMinSegTokens));
-  if (want * BH < kMinWorkgroups) want = (kMinWorkgroups + BH - 1) / BH;
-  want = std::max(1LL, std::min<long long>(want, pl.n_chunks));
-  pl.seg_chunks = (int)((pl.n_chunks + want - 1) / want);
+  if (total_tokens < 0) {
+    long long want = (kTargetWorkgroups + BH - 1) / BH;  // segments per sequence
+    want = std::min<long long>(want, std::max(1LL, (long long)d->T / kMinSegTokens));
+    if (want * BH < kMinWorkgroups) want = (kMinWorkgroups + BH - 1) / BH;
+    want = std::max(1LL, std::min<long long>(want, pl.n_chunks));
+    pl.seg_chunks = (int)((pl.n_chunks + want - 1) / want);
+  } else {
+    const long long work = total_tokens * d->H;  // token-heads in the batch
+    const long long seg_tokens = std::max<long long>(kMinSegTokens, (work + kTargetWorkgroups - 1) / kTargetWorkgroups);
+    pl.seg_chunks = (int)std::min<long long>(pl.n_chunks, (seg_tokens + d->chunk - 1) / d->chunk);
+  }
   pl.n_seg = (pl.n_chunks + pl.seg_chunks - 1) / pl.seg_chunks;
+  if (pl.n_seg > 65535) {  // the grid's y extent
+    pl.seg_chunks = (pl.n_chunks + 65534) / 65535;
+    pl.n_seg = (pl.n_chunks + pl.seg_chunks - 1) / pl.seg_chunks;
+  }
   const size_t E = (size_t)d->n_psi * d->d_v + d->n_psi;
   pl.ws_bytes = (size_t)BH * pl.n_seg * E * sizeof(float);
   return pl;
@@ -122,6 +137,15 @@ la_status lin_attn_prefill_workspace_size(const la_prefill_desc* d, size_t* byte
   return LA_OK;
 }
 
+la_status lin_attn_prefill_varlen_workspace_size(const la_prefill_desc* d, int32_t total_tokens, size_t* bytes) {
+  if (!bytes) return LA_ERR_NULL;
+  const la_status st = validate_prefill_desc(d);
+  if (st != LA_OK) return st;
+  if (total_tokens < 0) return LA_ERR_SHAPE;
+  *bytes = make_plan(d, total_tokens).ws_bytes;
+  return LA_OK;
+}
+
 }  // extern "C"
 
 namespace {
@@ -147,7 +171,7 @@ la_status prefill_impl(const la_prefill_desc* d, const int32_t* cu_seqlens, int3
     return LA_ERR_ALIGN;
   st = check_gamma(gamma, d->H);
   if (st != LA_OK) return st;
-  const Plan pl = make_plan(d);
+  const Plan pl = cu_seqlens ? make_plan(d, total_tokens) : make_plan(d);
   if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes)) return LA_ERR_WORKSPACE;
 
   PrefillParams p;

@@ -15,6 +15,7 @@ namespace la {
 // n_chunks = ceil(T / C) chunks, and consecutive chunks are grouped into n_seg
 // segments of seg_chunks chunks (the last segment and the last chunk may be
 // short). The workspace holds one summary (a, S, Z) per segment, scanned in place.
+// One workgroup per (sequence, segment): blockIdx.x = b * H + h, blockIdx.y = segment.
 // With per-sequence lengths (cu_seqlens) T is the longest sequence: segments that
 // start past a shorter sequence's end are empty (identity summaries, no outputs).
 //

@@ -220,7 +220,7 @@ __global__ __launch_bounds__(2 * D) void k_summary(PrefillParams p) {
   using G = Geo<C, D, false>;
   constexpr bool SPLIT = DECAY || ELU;  // K~ inexact in bf16: keep a lo part
   extern __shared__ __align__(16) unsigned char smem[];
-  const int seg = blockIdx.x, bh = blockIdx.y, head = bh % p.H;
+  const int bh = blockIdx.x, seg = blockIdx.y, head = bh % p.H;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const float lg = DECAY ? p.log2g[head] : 0.f;
   __bf16* sK = (__bf16*)(smem + G::OFF_K);
@@ -297,7 +297,7 @@ __global__ __launch_bounds__(2 * D) void k_output(PrefillParams p) {
   constexpr bool SPLIT = DECAY || ELU;
   constexpr int NJ = C / 32;
   extern __shared__ __align__(16) unsigned char smem[];
-  const int seg = blockIdx.x, bh = blockIdx.y, head = bh % p.H;
+  const int bh = blockIdx.x, seg = blockIdx.y, head = bh % p.H;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, n = lane & 31, hh = lane >> 5;
   const int Ew = 32 * w;
   const float lg = DECAY ? p.log2g[head] : 0.f;
@@ -553,7 +553,7 @@ __global__ __launch_bounds__(2 * D) void k_output_sh(PrefillParams p) {
   constexpr int KLO = G::K_BYTES;    // K lo, relative to K
   constexpr int ALO = 32 * PA * 2;   // a score tile's lo half, relative to its hi half
   extern __shared__ __align__(16) unsigned char smem[];
-  const int seg = blockIdx.x, bh = blockIdx.y, head = bh % p.H;
+  const int bh = blockIdx.x, seg = blockIdx.y, head = bh % p.H;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, n = lane & 31, hh = lane >> 5;
   const int L16 = lane & 15, g = lane >> 4;
   const int Ew = 32 * w;
@@ -959,7 +959,7 @@ __global__ __launch_bounds__(512) void k_output_w8(PrefillParams p) {
   constexpr int KLO = G::K_BYTES;
   constexpr int ALO = 32 * PA * 2;
   extern __shared__ __align__(16) unsigned char smem[];
-  const int seg = blockIdx.x, bh = blockIdx.y, head = bh % p.H;
+  const int bh = blockIdx.x, seg = blockIdx.y, head = bh % p.H;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, n = lane & 31, hh = lane >> 5;
   const int cb = w & 3, role = w >> 2;
   const int L16 = lane & 15, g = lane >> 4;
@@ -1284,7 +1284,11 @@ hipError_t launch_flags(const PrefillParams& p, hipStream_t s, bool out) {
                       : output_kernel<C, D, DECAY, NORM, ELU, false>(lds, threads);
   hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
-  dim3 grid(p.n_seg, p.B * p.H);
+  // x = (batch, head), y = segment: workgroups are dealt to the 8 XCDs round-robin by linear id
+  // x + y * B * H, so every XCD gets a share of the sequences with all their segments. With the
+  // segment on x, segment s would always land on the same XCDs: for variable-length batches the
+  // heavy first segments would pile onto a few of them.
+  dim3 grid(p.B * p.H, p.n_seg);
   void* args[] = {(void*)&p};
   e = hipLaunchKernel(kern, grid, dim3(threads), args, lds, s);
   if (e != hipSuccess) return e;

@@ -101,7 +101,7 @@ __device__ void state_update_f32(float* sm, const F32Layout& Ly, int C, int L, i
 __global__ __launch_bounds__(kThreads) void k_summary_f32(PrefillParams p) {
   extern __shared__ __align__(16) float sm[];
   const F32Layout Ly = f32_layout(p.C, p.d_k, p.d_v, p.n_psi);
-  const int seg = blockIdx.x, bh = blockIdx.y, head = bh % p.H;
+  const int bh = blockIdx.x, seg = blockIdx.y, head = bh % p.H;
   const float lg = p.has_decay ? p.log2g[head] : 0.f;
   const float* w = p.psi == LA_PSI_PRF ? (const float*)p.prf_w + (size_t)head * p.n_psi * p.d_k : nullptr;
   for (int idx = threadIdx.x; idx < p.n_psi * p.d_v + p.n_psi; idx += kThreads) sm[Ly.S + idx] = 0.f;  // S then Z
@@ -127,7 +127,7 @@ __global__ __launch_bounds__(kThreads) void k_summary_f32(PrefillParams p) {
 __global__ __launch_bounds__(kThreads) void k_output_f32(PrefillParams p) {
   extern __shared__ __align__(16) float sm[];
   const F32Layout Ly = f32_layout(p.C, p.d_k, p.d_v, p.n_psi);
-  const int seg = blockIdx.x, bh = blockIdx.y, head = bh % p.H;
+  const int bh = blockIdx.x, seg = blockIdx.y, head = bh % p.H;
   const float lg = p.has_decay ? p.log2g[head] : 0.f;
   const int C = p.C, n_psi = p.n_psi, d_v = p.d_v;
   const float* w = p.psi == LA_PSI_PRF ? (const float*)p.prf_w + (size_t)head * n_psi * p.d_k : nullptr;
@@ -202,7 +202,11 @@ static hipError_t launch_f32(const void* kern, const PrefillParams& p, hipStream
   const size_t lds = f32_lds_bytes(p.C, p.d_k, p.d_v, p.n_psi);
   hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  dim3 grid(p.n_seg, p.B * p.H);
+  // x = (batch, head), y = segment: workgroups are dealt to the 8 XCDs round-robin by linear id
+  // x + y * B * H, so every XCD gets a share of the sequences with all their segments. With the
+  // segment on x, segment s would always land on the same XCDs: for variable-length batches the
+  // heavy first segments would pile onto a few of them.
+  dim3 grid(p.B * p.H, p.n_seg);
   void* args[] = {(void*)&p};
   e = hipLaunchKernel(kern, grid, dim3(kThreads), args, lds, s);
   if (e != hipSuccess) return e;

@@ -229,7 +229,7 @@ __global__ __launch_bounds__(2 * D) void k_summary_prf(PrefillParams p) {
   constexpr int PR = G::PR, PV = G::PV, LO = G::PSIK;
   constexpr float LOG2E = 1.4426950408889634f;
   extern __shared__ __align__(16) unsigned char smem[];
-  const int seg = blockIdx.x, bh = blockIdx.y, head = bh % p.H;
+  const int bh = blockIdx.x, seg = blockIdx.y, head = bh % p.H;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, n = lane & 31, hh = lane >> 5;
   const int L16 = lane & 15, g = lane >> 4;
   const int Ew = 32 * w;
@@ -350,7 +350,7 @@ __global__ __launch_bounds__(2 * D) void k_output_prf(PrefillParams p) {
   constexpr int LO = G::PSIK, ALO = 32 * PA * 2;
   constexpr float LOG2E = 1.4426950408889634f;
   extern __shared__ __align__(16) unsigned char smem[];
-  const int seg = blockIdx.x, bh = blockIdx.y, head = bh % p.H;
+  const int bh = blockIdx.x, seg = blockIdx.y, head = bh % p.H;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, n = lane & 31, hh = lane >> 5;
   const int L16 = lane & 15, g = lane >> 4;
   const int Ew = 32 * w;
@@ -627,7 +627,11 @@ hipError_t launch_flags(const PrefillParams& p, hipStream_t s, bool out) {
   const int lds = out ? Geo<C, D, NP, true>::LDS_BYTES : Geo<C, D, NP, false>::LDS_BYTES;
   hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
-  dim3 grid(p.n_seg, p.B * p.H);
+  // x = (batch, head), y = segment: workgroups are dealt to the 8 XCDs round-robin by linear id
+  // x + y * B * H, so every XCD gets a share of the sequences with all their segments. With the
+  // segment on x, segment s would always land on the same XCDs: for variable-length batches the
+  // heavy first segments would pile onto a few of them.
+  dim3 grid(p.B * p.H, p.n_seg);
   void* args[] = {(void*)&p};
   e = hipLaunchKernel(kern, grid, dim3(2 * D), args, lds, s);
   if (e != hipSuccess) return e;

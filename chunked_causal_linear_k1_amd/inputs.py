@@ -20,7 +20,7 @@ Recipe (also stated in the design notes):
 from __future__ import annotations
 
 import math
-from typing import Dict, Optional
+from typing import Dict, List, Optional
 
 import numpy as np
 import torch
@@ -67,6 +67,28 @@ def make_prefill_inputs(w: Workload, device: str = "cpu", seed: Optional[int] = 
     if w.psi == PSI_PRF:
         prf_w = _randn((w.H, w.n_psi, w.d_k), gen, device, 1.0, dt)
     return {"q": q, "k": k, "v": v, "prf_w": prf_w, "gamma": gammas(w)}
+
+
+def varlen_lengths(w) -> List[int]:
+    """The sequence lengths of a VarlenWorkload: uniform in [len_min, len_max], seeded."""
+    rng = np.random.default_rng(w.seed)
+    return [int(x) for x in rng.integers(w.len_min, w.len_max + 1, size=w.N)]
+
+
+def make_varlen_inputs(w, device: str = "cpu") -> Dict[str, object]:
+    """Packed q, k, v [total, H, d] of a VarlenWorkload, cu_seqlens (int32 [N + 1], on device),
+    the lengths, the longest length and gamma (fp32 numpy or None)."""
+    lengths = varlen_lengths(w)
+    total = int(sum(lengths))
+    gen = torch.Generator(device=device)
+    gen.manual_seed(w.seed + 1)
+    dt = torch_dtype(w.dtype)
+    q = _randn((total, w.H, w.d_k), gen, device, w.qk_scale, dt)
+    k = _randn((total, w.H, w.d_k), gen, device, w.qk_scale, dt)
+    v = _randn((total, w.H, w.d_v), gen, device, w.v_scale, dt)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32), device=device)
+    return {"q": q, "k": k, "v": v, "prf_w": None, "gamma": gammas(w), "cu_seqlens": cu, "lengths": lengths,
+            "max_len": max(lengths)}
 
 
 def make_decode_prefix(w: DecodeWorkload, device: str = "cpu") -> Dict[str, torch.Tensor]:

@@ -74,6 +74,31 @@ class DecodeWorkload:
     dtype: str = "bf16"
 
 
+@dataclass(frozen=True)
+class VarlenWorkload:
+    """A packed batch of N sequences of seeded lengths (a serving prefill): q, k, v are
+    [total, H, d] with sequence b at tokens cu_seqlens[b] .. cu_seqlens[b+1] - 1. Lengths are
+    drawn uniformly from [len_min, len_max] (inputs.varlen_lengths)."""
+
+    name: str
+    N: int
+    H: int
+    len_min: int
+    len_max: int
+    d_k: int
+    d_v: int
+    n_psi: int
+    chunk: int
+    psi: int
+    normalize: int
+    eps: float
+    dtype: str
+    seed: int
+    qk_scale: float
+    v_scale: float
+    decay: str = "none"
+
+
 # Tiny fp32 case the oracle finishes in well under a second.
 TINY_F32 = Workload(
     name="tiny_f32_elu1", B=1, H=1, T=1024, d_k=64, d_v=64, n_psi=64, chunk=64,
@@ -99,5 +124,11 @@ RETNET_128K = Workload(
 DECODE_32x64 = DecodeWorkload(
     name="decode_32x64", N=32, H=64, d_k=128, d_v=128, n_psi=128, psi=PSI_ELU1, normalize=1,
     eps=1e-6, gamma=0.999, prefix_len=4096, steps=256, seed=4)
+
+# Serving prefill: 32 prompts of 1k..16k tokens packed in one call, retention form as above.
+VARLEN_32 = VarlenWorkload(
+    name="varlen_32x1k_16k_retention", N=32, H=32, len_min=1024, len_max=16384, d_k=128, d_v=128, n_psi=128,
+    chunk=128, psi=PSI_IDENTITY, normalize=0, eps=1e-6, dtype="bf16", seed=5, qk_scale=128 ** -0.5, v_scale=1.0,
+    decay="retnet_spread")
 
 PREFILL_WORKLOADS = {w.name: w for w in (TINY_F32, PREFILL_8K, PRF_4K, RETNET_128K)}

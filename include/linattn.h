@@ -107,10 +107,14 @@ typedef struct {
  *   gamma: when given, at most LA_MAX_DECAY_HEADS heads.                        */
 #define LA_MAX_DECAY_HEADS 256
 
-/* Device workspace bytes lin_attn_prefill (or lin_attn_prefill_varlen, with B the
- * number of sequences and T the longest length) needs for `d` (0 is possible).
+/* Device workspace bytes lin_attn_prefill needs for `d` (0 is possible).
  * Pure host function. Returns LA_OK and writes *bytes, or a validation error. */
 la_status lin_attn_prefill_workspace_size(const la_prefill_desc* d, size_t* bytes);
+
+/* The same for lin_attn_prefill_varlen with this `d` (B = number of sequences,
+ * T = longest length) and total_tokens >= 0 packed tokens: segments are sized from
+ * the total, so the workspace depends on it. */
+la_status lin_attn_prefill_varlen_workspace_size(const la_prefill_desc* d, int32_t total_tokens, size_t* bytes);
 
 /*
  * Chunkwise causal linear attention over whole sequences ("Log-Depth Chunked
@@ -161,6 +165,7 @@ la_status lin_attn_prefill(const la_prefill_desc* d, const void* q, const void* 
  *   q, k        device [total_tokens, H, d_k];  v device [total_tokens, H, d_v]
  *   o           device [total_tokens, H, d_v] out_dtype
  *   init_S, init_Z, final_S, final_Z: per sequence, [B, H, n_psi, d_v] / [B, H, n_psi]
+ *   workspace   at least lin_attn_prefill_varlen_workspace_size(d, total_tokens) bytes
  *   other arguments as for lin_attn_prefill.
  */
 la_status lin_attn_prefill_varlen(const la_prefill_desc* d, const int32_t* cu_seqlens, int32_t total_tokens,

@@ -143,7 +143,7 @@ def test_prefill_rejects_bad_pointers_before_launch():
 def test_varlen_rejects_bad_arguments_before_launch():
     lib = binding.load()
     d = _desc(B=3, T=700, layout=1)   # 3 packed sequences, longest 700 tokens
-    _, ws = _ws(d)
+    ws = 1 << 30
     fake = ctypes.c_void_p(1 << 20)
     cu = ctypes.c_void_p(1 << 21)
 
@@ -156,9 +156,29 @@ def test_varlen_rejects_bad_arguments_before_launch():
     assert call(desc=_desc(B=3, T=700, layout=0)) == LA_ERR_VALUE    # packed tokens interleave the heads
     assert call(q=None) == LA_ERR_NULL
     assert call(w=None) == LA_ERR_WORKSPACE
-    # the workspace is sized like a fixed-length call with B sequences of the longest length
-    st, ws_fixed = _ws(_desc(B=3, T=700))
-    assert st == LA_OK and ws_fixed == ws
+    n = ctypes.c_size_t(0)
+    assert lib.lin_attn_prefill_varlen_workspace_size(ctypes.byref(d), -1, ctypes.byref(n)) == LA_ERR_SHAPE
+    assert lib.lin_attn_prefill_varlen_workspace_size(ctypes.byref(d), 1200, None) == LA_ERR_NULL
+
+
+def test_varlen_planner():
+    """Packed batches: segments of a fixed token count sized from the batch total (at least 2048
+    tokens; about 2048 non-empty workgroups), one summary per (sequence, head, segment)."""
+    lib = binding.load()
+    E = 128 * 128 + 128
+
+    def ws(total, **kw):
+        n = ctypes.c_size_t(0)
+        st = lib.lin_attn_prefill_varlen_workspace_size(ctypes.byref(_desc(layout=1, **kw)), total, ctypes.byref(n))
+        assert st == LA_OK, binding.status_string(st)
+        return n.value
+    # 32 sequences x 32 heads, longest 16372, 259406 tokens: 8.3M token-heads / 2048 -> 4096-token segments
+    assert ws(259406, B=32, H=32, T=16372, chunk=128, psi=0, normalize=0) == 32 * 32 * 4 * E * 4
+    # small batches keep segments of 2048 tokens
+    assert ws(3000, B=3, H=2, T=1000, chunk=64) == 3 * 2 * 1 * E * 4
+    assert ws(30000, B=3, H=2, T=20000, chunk=64) == 3 * 2 * 10 * E * 4
+    # an empty batch still plans one segment per sequence
+    assert ws(0, B=3, H=2, T=1, chunk=64) == 3 * 2 * 1 * E * 4
 
 
 def test_decode_validation():

@@ -233,3 +233,27 @@ def test_varlen_prefill_then_decode(psi, d, normalize, decay):
                     for x in ("q", "k", "v")}
             ref = _oracle_blocks(w, full["q"], full["k"], full["v"], inp, list(range(H)))
             assert_close(o[b].cpu().numpy(), ref[:, -1, :], "bf16", f"handoff seq {b} step {t}")
+
+
+def test_full_varlen_serving_sampled():
+    """The packed serving batch at full size (32 prompts of 1k..16k tokens, 32 heads, retention
+    form), in the launch configuration the benchmark times; sampled (sequence, head) pairs
+    against the oracle: the shortest, the longest and a middle sequence."""
+    from chunked_causal_linear_k1_amd import workloads
+    w = workloads.VARLEN_32
+    announce(f"varlen full {w.name}")
+    inp = inputs.make_varlen_inputs(w, device=DEV)
+    g = inp["gamma"]
+    o = binding.lin_attn_prefill_varlen(inp["q"], inp["k"], inp["v"], inp["cu_seqlens"], inp["max_len"], psi=w.psi,
+                                        chunk=w.chunk, normalize=w.normalize, eps=w.eps, gamma=list(g))
+    torch.cuda.synchronize()
+    lengths = inp["lengths"]
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    order = np.argsort(lengths)
+    for b in (int(order[0]), int(order[len(order) // 2]), int(order[-1])):
+        for h in (0, w.H - 1):
+            sl = slice(int(cu[b]), int(cu[b + 1]))
+            q, k, v = (inp[x][sl, h].cpu().unsqueeze(0) for x in ("q", "k", "v"))
+            ref = oracle.prefill(q, k, v, w.psi, gamma=[float(g[h])], normalize=w.normalize,
+                                 eps=float(np.float32(w.eps)))
+            assert_close(o[sl, h].cpu().unsqueeze(0).numpy(), ref, "bf16", f"varlen full seq {b} (T={lengths[b]}) head {h}")
