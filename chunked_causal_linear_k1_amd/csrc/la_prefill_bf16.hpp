@@ -507,7 +507,8 @@ struct ShGeo {
   static constexpr int F_ZRED = D;            // per-wave Z partials [NW][D]
   static constexpr int F_THETA = D + NW * D;  // gamma^(j+1) [C]
   static constexpr int F_R = F_THETA + C;     // per-tile score row sums [NTILE][32]
-  static constexpr int LDS_BYTES = OFF_F + 4 * (F_R + NTILE * 32);
+  static constexpr int F_XI = F_R + NTILE * 32;  // Xi_i = gamma^(L-1-i), 0 past L [C] (decay on V)
+  static constexpr int LDS_BYTES = OFF_F + 4 * (F_XI + C);
   static constexpr bool FITS = LDS_BYTES <= 160 * 1024;
 };
 
@@ -547,6 +548,11 @@ __global__ __launch_bounds__(2 * D) void k_output_sh(PrefillParams p) {
   static_assert(G::FITS, "LDS budget");
   static_assert(PG::NT / PG::PPR == 16, "piece i of a thread covers row 16 i + tid / PPR");
   constexpr bool SPLIT = DECAY || ELU;
+  // Identity keys are exact in bf16, so the decay of the state update goes on the values:
+  // S += K^T (Xi V), with Xi V split into hi + lo in registers from the transpose reads of V.
+  // K stays as committed: no K~ pass, no barrier around it. (elu+1 keys are already two-term,
+  // and decayed values would make that four MFMAs per step, so elu+1 keeps K~ = Xi psi(K).)
+  constexpr bool VDEC = DECAY && !ELU;
   constexpr int NJ = G::NJ, NW = G::NW, NPC = PG::NPC;
   constexpr int TPW = (G::NTILE + NW - 1) / NW;  // score tiles per wave (the last round partial)
   constexpr int PQ = G::PQ, PV = G::PV, PA = G::PA;
@@ -674,6 +680,9 @@ __global__ __launch_bounds__(2 * D) void k_output_sh(PrefillParams p) {
     }
 #pragma unroll
     for (int i = 0; i < NPC; ++i) *(uint4*)(vP + i * 16 * D * 2) = pv.r[i];
+    if (VDEC) {  // Xi of this chunk (the previous chunk's state update is done: barrier above)
+      for (int j = tid; j < C; j += 2 * D) sF[G::F_XI + j] = j < L ? exp2f((float)(L - 1 - j) * lg) : 0.f;
+    }
     const bool more = c + 1 < c1;
     const int Ln = more ? min(C, T - (c + 1) * C) : 0;
     // next chunk's tiles stream in during this chunk's matrix work (rows past Ln read as
@@ -826,9 +835,10 @@ __global__ __launch_bounds__(2 * D) void k_output_sh(PrefillParams p) {
                         num[4 * q4 + 3] * inv);
     }
 
-    // ---- state update: K~ = Xi psi(K) as hi + lo, S <- gamma^L S + K~^T V, Z <- gamma^L Z + K~^T 1
+    // ---- state update: S <- gamma^L S + K~^T V with K~ = Xi psi(K) as hi + lo (elu+1), or
+    // S <- gamma^L S + K^T (Xi V) (identity); Z <- gamma^L Z + sum_i Xi_i psi(k_i)
     if (NORM) reduce_zp<D>(zp, sF + G::F_ZRED);
-    if (DECAY) {
+    if (DECAY && !VDEC) {
       lds_barrier();  // every wave is done with the score tiles (K lo aliases them) and K
 #pragma unroll
       for (int i = 0; i < NPC; ++i) {
@@ -850,7 +860,9 @@ __global__ __launch_bounds__(2 * D) void k_output_sh(PrefillParams p) {
         *(bf16x8*)(kP + off + KLO) = lo;
       }
     }
-    lds_barrier();
+    // the Z partials (and a rewritten K~) must be complete; K, V and Xi were published before
+    // the score tiles, and nothing else changes LDS until the next chunk's commit
+    if (NORM || (DECAY && !VDEC)) lds_barrier();
     if (NORM && tid < D) {
       float z = 0.f;
 #pragma unroll
@@ -861,36 +873,62 @@ __global__ __launch_bounds__(2 * D) void k_output_sh(PrefillParams p) {
 #pragma unroll
       for (int pt = 0; pt < D / 32; ++pt) S[pt] *= a;
     }
-    // S[pt] += K~^T V (M = state row, N = value column, k = token), software-pipelined:
-    // the operands of token step ik + 1 are read while the MFMAs of step ik run
+    // S[pt] += K~^T V, or K^T (Xi V) (M = state row, N = value column, k = token),
+    // software-pipelined: the operands of token step ik + 1 are read while the MFMAs of
+    // step ik run. Element j of this lane's V operand at step ik is token 16 ik + 8 hh + j.
     {
-      constexpr int NK = C / 16, NM = (SPLIT ? 2 : 1) * (D / 32);
-      bf16x8 ops[2][1 + NM];  // [buffer][V, then K~ hi (and lo) per state-row tile]
-      auto load_ops = [&](bf16x8 (&o)[1 + NM], int ik) {
+      constexpr int NK = C / 16;
+      constexpr int KP = (SPLIT && !VDEC) ? 2 : 1;  // key operand parts per state-row tile
+      constexpr int NM = KP * (D / 32);
+      bf16x8 ops[2][1 + NM];  // [buffer][V, then K (K~ hi and lo) per state-row tile]
+      f32x4 xis[2][2];        // VDEC: Xi of this lane's 8 tokens of the step
+      const float* const xiR = sF + G::F_XI + 8 * hh;
+      auto load_ops = [&](bf16x8 (&o)[1 + NM], f32x4 (&x)[2], int ik) {
         const int r0 = ik * 16, ko = r0 * D * 2;
         o[0] = cat8(lds_read_tr4((const __bf16*)(vT0 + r0 * D * 2)), lds_read_tr4((const __bf16*)(vT1 + r0 * D * 2)));
 #pragma unroll
         for (int pt = 0; pt < D / 32; ++pt) {
-          o[1 + (SPLIT ? 2 : 1) * pt] =
+          o[1 + KP * pt] =
               cat8(lds_read_tr4((const __bf16*)(kT[pt][0] + ko)), lds_read_tr4((const __bf16*)(kT[pt][1] + ko)));
-          if (SPLIT)
+          if (KP == 2)
             o[2 + 2 * pt] = cat8(lds_read_tr4((const __bf16*)(kT[pt][0] + ko + KLO)),
                                  lds_read_tr4((const __bf16*)(kT[pt][1] + ko + KLO)));
         }
+        if (VDEC) {
+          x[0] = *(const f32x4*)(xiR + r0);
+          x[1] = *(const f32x4*)(xiR + r0 + 4);
+        }
       };
-      load_ops(ops[0], 0);
+      load_ops(ops[0], xis[0], 0);
 #pragma unroll
       for (int ik = 0; ik < NK; ++ik) {
-        if (ik + 1 < NK) load_ops(ops[(ik + 1) & 1], ik + 1);
+        if (ik + 1 < NK) load_ops(ops[(ik + 1) & 1], xis[(ik + 1) & 1], ik + 1);
         const bf16x8(&o)[1 + NM] = ops[ik & 1];
+        if (VDEC) {
+          const f32x4(&x)[2] = xis[ik & 1];
+          float vx[8];
 #pragma unroll
-        for (int pt = 0; pt < D / 32; ++pt) {
-          S[pt] = mfma32(o[1 + (SPLIT ? 2 : 1) * pt], o[0], S[pt]);
-          if (SPLIT) S[pt] = mfma32(o[2 + 2 * pt], o[0], S[pt]);
+          for (int j = 0; j < 4; ++j) {
+            vx[j] = from_bf16(o[0][j]) * x[0][j];
+            vx[4 + j] = from_bf16(o[0][4 + j]) * x[1][j];
+          }
+          bf16x8 vh, vl;
+          split8_trunc(vx, vh, vl);
+#pragma unroll
+          for (int pt = 0; pt < D / 32; ++pt) {
+            S[pt] = mfma32(o[1 + pt], vh, S[pt]);
+            S[pt] = mfma32(o[1 + pt], vl, S[pt]);
+          }
+        } else {
+#pragma unroll
+          for (int pt = 0; pt < D / 32; ++pt) {
+            S[pt] = mfma32(o[1 + KP * pt], o[0], S[pt]);
+            if (KP == 2) S[pt] = mfma32(o[2 + 2 * pt], o[0], S[pt]);
+          }
         }
         if (ik + 1 < NK) {  // keep the next step's reads ahead of this step's MFMAs
-          __builtin_amdgcn_sched_group_barrier(0x100, 2 * (1 + NM), 0);  // LDS reads
-          __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);            // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 2 * (1 + NM) + (VDEC ? 2 : 0), 0);  // LDS reads
+          __builtin_amdgcn_sched_group_barrier(0x008, VDEC ? 2 * (D / 32) : NM, 0);       // MFMA
         }
       }
     }
