@@ -185,6 +185,35 @@ __device__ __forceinline__ void state_mfma(f32x16 (&S)[D / 32], const __bf16* sK
   }
 }
 
+// S[pt] += K^T (Xi V) over the chunk: keys exact (no lo part), the values of this wave's
+// columns scaled by Xi (table sXi, per token) and split into hi + lo in registers. Element j
+// of the V operand at step ik is token 16 ik + 8 h + j (h = lane / 32).
+template <int C, int D>
+__device__ __forceinline__ void state_mfma_vdec(f32x16 (&S)[D / 32], const __bf16* sK, const __bf16* sV,
+                                                const float* sXi, int Ew, int lane) {
+  constexpr int PK = Geo<C, D, true>::PK;
+  const float* xr = sXi + 8 * (lane >> 5);
+#pragma unroll 2
+  for (int ik = 0; ik < C / 16; ++ik) {
+    const bf16x8 vb = ld_rows8(sV, PK, ik * 16, Ew, lane);
+    const f32x4 x0 = *(const f32x4*)(xr + ik * 16), x1 = *(const f32x4*)(xr + ik * 16 + 4);
+    float vx[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      vx[j] = from_bf16(vb[j]) * x0[j];
+      vx[4 + j] = from_bf16(vb[4 + j]) * x1[j];
+    }
+    bf16x8 vh, vl;
+    split8_trunc(vx, vh, vl);
+#pragma unroll
+    for (int pt = 0; pt < D / 32; ++pt) {
+      const bf16x8 ka = ld_rows8(sK, PK, ik * 16, pt * 32, lane);
+      S[pt] = mfma32(ka, vh, S[pt]);
+      S[pt] = mfma32(ka, vl, S[pt]);
+    }
+  }
+}
+
 // One score tile A^T[i-tile it][j-tile jt] (M = i, N = j, k = feature) with the causal
 // mask and decay D_ji = gamma^(j-i); adds its row sums to rsum and A V to num. qk holds
 // the j-tile's Q operands (k = feature). fac[r] is this lane's factor for register r:
@@ -215,10 +244,29 @@ __device__ __forceinline__ void score_tile(int it, int jt, const bf16x8 (&qk)[D 
   }
 }
 
+// Summary-pass LDS image. With identity keys and decay the decay goes on the values (see
+// k_summary), so there is no K lo tile and V moves up: about 40 KiB at C = 64, d = 128, so
+// three workgroups share a CU instead of two.
+template <int C, int D, bool VDEC>
+struct SumGeo {
+  using B = Geo<C, D, false>;
+  static constexpr int NW = B::NW, PK = B::PK;
+  static constexpr int OFF_K = B::OFF_K, OFF_KLO = B::OFF_KLO;
+  static constexpr int OFF_V = VDEC ? B::OFF_KLO : B::OFF_V;
+  static constexpr int OFF_F = OFF_V + B::K_BYTES;
+  static constexpr int F_ZRED = B::F_ZRED;  // per-wave Z partials [NW][D]
+  static constexpr int F_XI = B::F_THETA;   // Xi_i = gamma^(L-1-i), 0 past L [C]
+  static constexpr int LDS_BYTES = OFF_F + 4 * (F_XI + C);
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+};
+
 template <int C, int D, bool DECAY, bool NORM, bool ELU>
 __global__ __launch_bounds__(2 * D) void k_summary(PrefillParams p) {
-  using G = Geo<C, D, false>;
-  constexpr bool SPLIT = DECAY || ELU;  // K~ inexact in bf16: keep a lo part
+  // Identity keys are exact in bf16: the decay goes on the values, S += K^T (Xi V), with Xi V
+  // split hi + lo in registers. elu+1 keys keep K~ = Xi psi(K) as hi + lo.
+  constexpr bool VDEC = DECAY && !ELU;
+  constexpr bool SPLIT = (DECAY || ELU) && !VDEC;  // K~ inexact in bf16: keep a lo part
+  using G = SumGeo<C, D, VDEC>;
   extern __shared__ __align__(16) unsigned char smem[];
   const int bh = blockIdx.x, seg = blockIdx.y, head = bh % p.H;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -252,8 +300,11 @@ __global__ __launch_bounds__(2 * D) void k_summary(PrefillParams p) {
     float zp[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) zp[j] = 0.f;
-    commit_k<C, D, ELU, DECAY, true, SPLIT>(pk, sK, sKlo, G::PK, L, lg, zp);
+    commit_k<C, D, ELU, DECAY, !VDEC, SPLIT>(pk, sK, sKlo, G::PK, L, lg, zp);
     commit_v<C, D>(pv, sV, G::PK);
+    if (VDEC) {
+      for (int j = tid; j < C; j += 2 * D) sF[G::F_XI + j] = j < L ? exp2f((float)(L - 1 - j) * lg) : 0.f;
+    }
 #pragma unroll
     for (int j = 0; j < 8; ++j) zrun[j] = a * zrun[j] + zp[j];
     if (c + 1 < c1) {  // next chunk's loads overlap this chunk's matrix work
@@ -266,7 +317,10 @@ __global__ __launch_bounds__(2 * D) void k_summary(PrefillParams p) {
 #pragma unroll
       for (int pt = 0; pt < D / 32; ++pt) S[pt] *= a;
     }
-    state_mfma<C, D, SPLIT>(S, sK, sKlo, sV, Ew, lane);
+    if (VDEC)
+      state_mfma_vdec<C, D>(S, sK, sV, sF + G::F_XI, Ew, lane);
+    else
+      state_mfma<C, D, SPLIT>(S, sK, sKlo, sV, Ew, lane);
   }
   // segment summary -> workspace [bh][seg][E], E = D*D + D
   const size_t E = (size_t)D * D + D;
@@ -1315,7 +1369,7 @@ const void* output_kernel(int& lds, int& threads) {
 template <int C, int D, bool DECAY, bool NORM, bool ELU>
 hipError_t launch_flags(const PrefillParams& p, hipStream_t s, bool out) {
   const void* kern = (const void*)k_summary<C, D, DECAY, NORM, ELU>;
-  int lds = Geo<C, D, false>::LDS_BYTES;
+  int lds = SumGeo<C, D, DECAY && !ELU>::LDS_BYTES;
   int threads = 2 * D;
   if (out)
     kern = p.out_bf16 ? output_kernel<C, D, DECAY, NORM, ELU, true>(lds, threads)
