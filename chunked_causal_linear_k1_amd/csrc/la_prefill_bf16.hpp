@@ -739,13 +739,15 @@ __global__ __launch_bounds__(2 * D) void k_output_sh(PrefillParams p) {
     }
     const bool more = c + 1 < c1;
     const int Ln = more ? min(C, T - (c + 1) * C) : 0;
+    lds_barrier();
     // next chunk's tiles stream in during this chunk's matrix work (rows past Ln read as
-    // zero). All three are issued before this chunk's output stores: the vmcnt wait at the
-    // next commit then covers only these loads, not the stores.
+    // zero). They are issued among the score MFMAs (one load after each, see below), so the
+    // wave keeps the MFMA pipe fed while the vector memory unit accepts them, and before
+    // this chunk's output stores: the vmcnt wait at the next commit then covers only these
+    // loads, not the stores.
     load_pieces<C, D>(pq, qb + (size_t)(c + 1) * C * rse, Ln, rsb);
     load_pieces<C, D>(pk, kb + (size_t)(c + 1) * C * rse, Ln, rsb);
     load_pieces<C, D>(pv, vb + (size_t)(c + 1) * C * rse, Ln, rsb);
-    lds_barrier();
 
     // ---- score tiles A^T (M = i, N = j, k = feature), masked, decayed, split into hi + lo
     // and shared through LDS: wave w computes tiles w, w + NW, ... Software-pipelined: the
@@ -798,8 +800,16 @@ __global__ __launch_bounds__(2 * D) void k_output_sh(PrefillParams p) {
     // bytes to the same place as the wave that owns it (it would wait at the barrier anyway).
     static_assert(G::NTILE >= NW, "every wave has a score tile");
     {
+      // next-chunk loads per score MFMA (3 NPC loads over TPW tiles of D / 16 MFMAs)
+      constexpr int LPM = (3 * NPC + TPW * (D / 16) - 1) / (TPW * (D / 16));
       f32x16 prev = score_chain(w);
       int tp = w;
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * (D / 16), 0);  // the first tile's operands
+#pragma unroll
+      for (int i = 0; i < D / 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x020, LPM, 0);  // next-chunk loads
+      }
 #pragma unroll
       for (int u = 1; u < TPW; ++u) {
         const int t = min(w + u * NW, G::NTILE - 1);
@@ -808,8 +818,9 @@ __global__ __launch_bounds__(2 * D) void k_output_sh(PrefillParams p) {
         __builtin_amdgcn_sched_group_barrier(0x100, 2 * (D / 16), 0);  // the next tile's operands
 #pragma unroll
         for (int i = 0; i < D / 16; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA of the next tile
-          __builtin_amdgcn_sched_group_barrier(0x002, 14, 0);  // epilogue VALU of this one
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // one MFMA of the next tile
+          __builtin_amdgcn_sched_group_barrier(0x020, LPM, 0);  // next-chunk loads
+          __builtin_amdgcn_sched_group_barrier(0x002, 14, 0);   // epilogue VALU of this one
         }
         __builtin_amdgcn_sched_group_barrier(0x200, 8, 0);     // its LDS writes
         prev = cur;
