@@ -29,7 +29,7 @@ _LIB_PATH = os.path.join(_HERE, "liblinattn_oracle.so")
 # A test that plants a mistake in a copy of the oracle points this at the copy.
 _LIB_OVERRIDE = os.environ.get("LINATTN_ORACLE_LIB")
 
-PSI_IDENTITY, PSI_ELU1, PSI_PRF = 0, 1, 2
+PSI_IDENTITY, PSI_ELU1, PSI_PRF, PSI_PRF_QSHIFT = 0, 1, 2, 3
 BF16, F32 = 0, 1
 
 _lib = None

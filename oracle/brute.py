@@ -25,11 +25,14 @@ def feature_np(x: np.ndarray, psi: int, w: np.ndarray | None = None) -> np.ndarr
         return x.copy()
     if psi == 1:
         return np.where(x > 0, x + 1.0, np.exp(np.minimum(x, 0.0)))
-    if psi == 2:
+    if psi in (2, 3):
         m = w.shape[0]
         lin = x @ w.T  # [..., m]
         half_sq = 0.5 * np.sum(x * x, axis=-1, keepdims=True)
-        return np.exp(lin - half_sq) / np.sqrt(m)
+        logf = lin - half_sq
+        if psi == 3:  # query-row shift: the row's largest log-feature becomes 0
+            logf = logf - logf.max(axis=-1, keepdims=True)
+        return np.exp(logf) / np.sqrt(m)
     raise ValueError(psi)
 
 
@@ -39,7 +42,7 @@ def quadratic(q: np.ndarray, k: np.ndarray, v: np.ndarray, psi: int, gamma: floa
     """One (batch, head): q, k [T, d_k], v [T, d_v] fp64 -> o [T, d_v] fp64."""
     T = q.shape[0]
     fq = feature_np(q, psi, w)
-    fk = feature_np(k, psi, w)
+    fk = feature_np(k, 2 if psi == 3 else psi, w)  # keys never take the query-row shift
     A = fq @ fk.T  # [T, T], A[t, i] = psi(q_t) . psi(k_i)
     t_idx = np.arange(T)[:, None]
     i_idx = np.arange(T)[None, :]

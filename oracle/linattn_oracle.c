@@ -26,7 +26,11 @@
  *    "The Associative Property and Linear Kernel Formulation"); positive random
  *    features psi(x)_p = exp(w_p . x - |x|^2/2) / sqrt(m) ("Linearized 2-Simplicial
  *    Attention", section 3.2 and appendix "Feature scaling": the m^{-1/2} factor
- *    sits on each feature vector).
+ *    sits on each feature vector);
+ *  - the same features with the log-space shift of the query row (same page,
+ *    appendix B.2): psi(q)_p = exp(l_p - max_r l_r) / sqrt(m) with
+ *    l_p = w_p . q - |q|^2/2, the shift depending on the query row only and shared by
+ *    numerator and denominator; key features unshifted.
  *
  * Build: gcc -O2 -std=c99 -ffp-contract=off -fopenmp -shared -fPIC
  */
@@ -38,7 +42,8 @@
 #include <omp.h>
 #endif
 
-enum { ORC_PSI_IDENTITY = 0, ORC_PSI_ELU1 = 1, ORC_PSI_PRF = 2 };
+enum { ORC_PSI_IDENTITY = 0, ORC_PSI_ELU1 = 1, ORC_PSI_PRF = 2, ORC_PSI_PRF_QSHIFT = 3 };
+#define ORC_IS_PRF(psi) ((psi) == ORC_PSI_PRF || (psi) == ORC_PSI_PRF_QSHIFT)
 enum { ORC_BF16 = 0, ORC_F32 = 1 };
 
 /* Exact upcast of one stored element. bf16 is the top half of an IEEE fp32. */
@@ -62,14 +67,21 @@ void oracle_feature_f64(int psi, int d_k, int n_psi, const double* x, const doub
     /* elu(x) = x for x > 0, exp(x) - 1 otherwise; plus one. */
     for (int j = 0; j < d_k; ++j) out[j] = x[j] > 0.0 ? x[j] + 1.0 : exp(x[j]);
   } else {
+    /* log-features l_p = w_p . x - |x|^2/2; PRF_QSHIFT subtracts their maximum */
     double sq = 0.0;
     for (int j = 0; j < d_k; ++j) sq += x[j] * x[j];
     double inv_sqrt_m = 1.0 / sqrt((double)n_psi);
     for (int p = 0; p < n_psi; ++p) {
       double dot = 0.0;
       for (int j = 0; j < d_k; ++j) dot += w[(size_t)p * d_k + j] * x[j];
-      out[p] = exp(dot - 0.5 * sq) * inv_sqrt_m;
+      out[p] = dot - 0.5 * sq;
     }
+    double shift = 0.0;
+    if (psi == ORC_PSI_PRF_QSHIFT) {
+      shift = out[0];
+      for (int p = 1; p < n_psi; ++p) shift = out[p] > shift ? out[p] : shift;
+    }
+    for (int p = 0; p < n_psi; ++p) out[p] = exp(out[p] - shift) * inv_sqrt_m;
   }
 }
 
@@ -79,7 +91,8 @@ static void recurrence_step(int psi, int d_k, int d_v, int n_psi, const double* 
                             int normalize, double eps, const double* kt, const double* vt,
                             const double* qt, double* S, double* Z, double* f, double* g,
                             double* ot) {
-  oracle_feature_f64(psi, d_k, n_psi, kt, w, f);
+  /* keys never take the query-row shift */
+  oracle_feature_f64(psi == ORC_PSI_PRF_QSHIFT ? ORC_PSI_PRF : psi, d_k, n_psi, kt, w, f);
   for (int p = 0; p < n_psi; ++p) {
     double* row = S + (size_t)p * d_v;
     for (int e = 0; e < d_v; ++e) row[e] = gamma * row[e] + f[p] * vt[e];
@@ -119,8 +132,8 @@ int oracle_prefill_f64(int nblk, int T, int d_k, int d_v, int n_psi, int psi, in
                        const double* S0, const double* Z0, double* o, double* S_out,
                        double* Z_out, int nthreads) {
   if (nblk < 0 || T < 0 || d_k <= 0 || d_v <= 0 || n_psi <= 0) return -1;
-  if (psi != ORC_PSI_PRF && n_psi != d_k) return -1;
-  if (psi == ORC_PSI_PRF && !w) return -1;
+  if (!ORC_IS_PRF(psi) && n_psi != d_k) return -1;
+  if (ORC_IS_PRF(psi) && !w) return -1;
   if (q && !o) return -1;
   int err = 0;
 #ifdef _OPENMP
@@ -136,8 +149,8 @@ int oracle_prefill_f64(int nblk, int T, int d_k, int d_v, int n_psi, int psi, in
     double* qt = (double*)malloc(sizeof(double) * (size_t)d_k);
     double* vt = (double*)malloc(sizeof(double) * (size_t)d_v);
     double* wd = NULL;
-    if (psi == ORC_PSI_PRF) wd = (double*)malloc(sizeof(double) * (size_t)n_psi * d_k);
-    if (!S || !Z || !f || !g || !kt || !qt || !vt || (psi == ORC_PSI_PRF && !wd)) {
+    if (ORC_IS_PRF(psi)) wd = (double*)malloc(sizeof(double) * (size_t)n_psi * d_k);
+    if (!S || !Z || !f || !g || !kt || !qt || !vt || (ORC_IS_PRF(psi) && !wd)) {
       err |= 1;
     } else {
       if (wd) {
@@ -175,8 +188,8 @@ int oracle_decode_step_f64(int nblk, int d_k, int d_v, int n_psi, int psi, int i
                            const int32_t* w_head, const double* gamma, int normalize, double eps,
                            double* S, double* Z, double* o, int nthreads) {
   if (nblk < 0 || d_k <= 0 || d_v <= 0 || n_psi <= 0 || !q || !k || !v || !S || !o) return -1;
-  if (psi != ORC_PSI_PRF && n_psi != d_k) return -1;
-  if (psi == ORC_PSI_PRF && !w) return -1;
+  if (!ORC_IS_PRF(psi) && n_psi != d_k) return -1;
+  if (ORC_IS_PRF(psi) && !w) return -1;
   if (normalize && !Z) return -1;
   int err = 0;
 #ifdef _OPENMP
@@ -190,8 +203,8 @@ int oracle_decode_step_f64(int nblk, int d_k, int d_v, int n_psi, int psi, int i
     double* qt = (double*)malloc(sizeof(double) * (size_t)d_k);
     double* vt = (double*)malloc(sizeof(double) * (size_t)d_v);
     double* wd = NULL;
-    if (psi == ORC_PSI_PRF) wd = (double*)malloc(sizeof(double) * (size_t)n_psi * d_k);
-    if (!f || !g || !kt || !qt || !vt || (psi == ORC_PSI_PRF && !wd)) {
+    if (ORC_IS_PRF(psi)) wd = (double*)malloc(sizeof(double) * (size_t)n_psi * d_k);
+    if (!f || !g || !kt || !qt || !vt || (ORC_IS_PRF(psi) && !wd)) {
       err |= 1;
     } else {
       if (wd) {

@@ -28,8 +28,12 @@ MUTATIONS = {
     "eps_sign": [("den += eps;", "den -= eps;")],
     "elu_missing_plus_one": [("x[j] > 0.0 ? x[j] + 1.0 : exp(x[j])", "x[j] > 0.0 ? x[j] : exp(x[j])")],
     "elu_wrong_branch": [("x[j] > 0.0 ? x[j] + 1.0 : exp(x[j])", "x[j] > 0.0 ? exp(x[j]) : x[j] + 1.0")],
-    "prf_norm_not_halved": [("exp(dot - 0.5 * sq)", "exp(dot - sq)")],
-    "prf_norm_sign": [("exp(dot - 0.5 * sq)", "exp(dot + 0.5 * sq)")],
+    "prf_norm_not_halved": [("out[p] = dot - 0.5 * sq;", "out[p] = dot - sq;")],
+    "prf_norm_sign": [("out[p] = dot - 0.5 * sq;", "out[p] = dot + 0.5 * sq;")],
+    "qshift_on_keys_too": [("oracle_feature_f64(psi == ORC_PSI_PRF_QSHIFT ? ORC_PSI_PRF : psi, d_k, n_psi, kt, w, f);",
+                            "oracle_feature_f64(psi, d_k, n_psi, kt, w, f);")],
+    "qshift_missing": [("if (psi == ORC_PSI_PRF_QSHIFT) {", "if (0) {")],
+    "qshift_min_not_max": [("shift = out[p] > shift ? out[p] : shift;", "shift = out[p] < shift ? out[p] : shift;")],
     "prf_scale_1_over_m": [("1.0 / sqrt((double)n_psi)", "1.0 / (double)n_psi")],
     "state_transposed": [("ot[e] += g[p] * row[e];",
                           "ot[e] += g[p] * S[(size_t)(e % n_psi) * d_v + (size_t)(p % d_v)];")],

@@ -57,7 +57,8 @@ def _rand(shape, seed, scale=1.0):
     return (torch.randn(shape, generator=g) * scale).to(torch.float32)
 
 
-PSI = {"identity": oracle.PSI_IDENTITY, "elu1": oracle.PSI_ELU1, "prf": oracle.PSI_PRF}
+PSI = {"identity": oracle.PSI_IDENTITY, "elu1": oracle.PSI_ELU1, "prf": oracle.PSI_PRF,
+       "prf_qshift": oracle.PSI_PRF_QSHIFT}
 
 
 # ----------------------------------------------------------------------------- golden
@@ -132,6 +133,40 @@ def test_prf_expectation_is_softmax_kernel():
     assert abs(float(fx @ fy) - est) < 1e-12 * abs(est)
 
 
+def test_qshift_largest_query_feature_is_one_over_sqrt_m():
+    """The log-space shift of "Linearized 2-Simplicial Attention" (appendix B.2) subtracts the
+    query row's largest log-feature, so that feature becomes exp(0) / sqrt(m) and every other
+    is smaller; the ratios between features are those of the unshifted map."""
+    rng = np.random.default_rng(3)
+    m, d = 64, 8
+    w = rng.standard_normal((m, d))
+    for scale in (0.3, 3.0, 30.0):  # at 30 the unshifted features underflow or overflow in fp64
+        x = rng.standard_normal(d) * scale
+        f = oracle.feature(x, oracle.PSI_PRF_QSHIFT, m, w)
+        assert np.all(np.isfinite(f)) and np.all(f > 0)
+        assert abs(f.max() * math.sqrt(m) - 1.0) < 1e-15
+        if scale < 10:
+            g = oracle.feature(x, oracle.PSI_PRF, m, w)
+            np.testing.assert_allclose(f / f.max(), g / g.max(), rtol=1e-12)
+
+
+@pytest.mark.parametrize("gamma", [1.0, 0.9])
+def test_qshift_cancels_without_eps(gamma):
+    """The shift depends on the query row only and multiplies numerator and denominator alike:
+    with eps = 0 the output equals that of the unshifted features."""
+    T, d_k, d_v, m = 40, 8, 6, 24
+    q, k = _rand((2, T, d_k), 5, 0.8), _rand((2, T, d_k), 6, 0.8)
+    v = _rand((2, T, d_v), 7)
+    w = _rand((1, m, d_k), 8)
+    a = oracle.prefill(q, k, v, oracle.PSI_PRF_QSHIFT, n_psi=m, prf_w=w, gamma=[gamma, gamma], normalize=1, eps=0.0)
+    b = oracle.prefill(q, k, v, oracle.PSI_PRF, n_psi=m, prf_w=w, gamma=[gamma, gamma], normalize=1, eps=0.0)
+    np.testing.assert_allclose(a, b, rtol=1e-12, atol=0)
+    # the states are those of the keys, which take no shift
+    _, Sa, Za = oracle.prefill(None, k, v, oracle.PSI_PRF_QSHIFT, n_psi=m, prf_w=w, want_state=True)
+    _, Sb, Zb = oracle.prefill(None, k, v, oracle.PSI_PRF, n_psi=m, prf_w=w, want_state=True)
+    assert np.array_equal(Sa, Sb) and np.array_equal(Za, Zb)
+
+
 # ----------------------------------------------------------------------------- brute force
 CASES = [
     # psi, gamma, normalize, T, d_k, d_v, n_psi, scale
@@ -143,6 +178,9 @@ CASES = [
     ("elu1", 1.0, 0, 17, 8, 8, 8, 1.0),
     ("prf", 1.0, 1, 40, 8, 8, 16, 0.6),
     ("prf", 0.95, 1, 33, 6, 4, 12, 0.6),
+    ("prf_qshift", 1.0, 1, 40, 8, 8, 16, 0.6),
+    ("prf_qshift", 0.95, 1, 33, 6, 4, 12, 1.5),
+    ("prf_qshift", 0.9, 0, 21, 6, 4, 12, 1.0),
 ]
 
 
@@ -152,7 +190,7 @@ def test_recurrence_matches_quadratic_form(psi, gamma, normalize, T, d_k, d_v, n
     q = _rand((1, T, d_k), seed, scale)
     k = _rand((1, T, d_k), seed + 1, scale)
     v = _rand((1, T, d_v), seed + 2)
-    w = _rand((n_psi, d_k), seed + 3) if psi == "prf" else None
+    w = _rand((n_psi, d_k), seed + 3) if psi.startswith("prf") else None
     eps = 1e-3
     o = oracle.prefill(q, k, v, PSI[psi], n_psi=n_psi, prf_w=None if w is None else w[None],
                        gamma=[gamma], normalize=normalize, eps=eps)[0]
@@ -161,13 +199,13 @@ def test_recurrence_matches_quadratic_form(psi, gamma, normalize, T, d_k, d_v, n
     np.testing.assert_allclose(o, ref, rtol=1e-11, atol=1e-11 * np.abs(ref).max())
 
 
-@pytest.mark.parametrize("psi", ["identity", "elu1", "prf"])
+@pytest.mark.parametrize("psi", ["identity", "elu1", "prf", "prf_qshift"])
 def test_initial_state_matches_quadratic_form(psi):
     T, d_k, d_v = 23, 6, 5
-    n_psi = 10 if psi == "prf" else d_k
+    n_psi = 10 if psi.startswith("prf") else d_k
     q, k = _rand((1, T, d_k), 1, 0.5), _rand((1, T, d_k), 2, 0.5)
     v = _rand((1, T, d_v), 3)
-    w = _rand((n_psi, d_k), 4) if psi == "prf" else None
+    w = _rand((n_psi, d_k), 4) if psi.startswith("prf") else None
     rng = np.random.default_rng(0)
     S0 = rng.standard_normal((n_psi, d_v))
     Z0 = np.abs(rng.standard_normal(n_psi)) + 1.0
