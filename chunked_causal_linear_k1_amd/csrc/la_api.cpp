@@ -51,13 +51,13 @@ la_status validate_prefill_desc(const la_prefill_desc* d) {
   if (!d) return LA_ERR_NULL;
   if (d->B < 1 || d->H < 1 || d->T < 1 || d->d_k < 1 || d->d_v < 1 || d->n_psi < 1 || d->chunk < 1)
     return LA_ERR_SHAPE;
-  if (d->psi < LA_PSI_IDENTITY || d->psi > LA_PSI_PRF) return LA_ERR_VALUE;
+  if (d->psi < LA_PSI_IDENTITY || d->psi > LA_PSI_PRF_QSHIFT) return LA_ERR_VALUE;
   if (d->normalize != 0 && d->normalize != 1) return LA_ERR_VALUE;
   if (!(d->eps >= 0.f) || !isfinite(d->eps)) return LA_ERR_VALUE;
   if (d->in_dtype != LA_BF16 && d->in_dtype != LA_F32) return LA_ERR_VALUE;
   if (d->out_dtype != LA_BF16 && d->out_dtype != LA_F32) return LA_ERR_VALUE;
   if (d->layout != LA_LAYOUT_BHTD && d->layout != LA_LAYOUT_BTHD) return LA_ERR_VALUE;
-  if (d->psi != LA_PSI_PRF && d->n_psi != d->d_k) return LA_ERR_SHAPE;
+  if (!la::is_prf(d->psi) && d->n_psi != d->d_k) return LA_ERR_SHAPE;
   if (d->d_v % 4 != 0 || d->n_psi % 4 != 0) return LA_ERR_UNSUPPORTED;  // 16-byte state rows
   // element counts must fit comfortably in 64-bit offsets and the grid's y extent
   const double tokens = (double)d->B * d->H * d->T;
@@ -164,7 +164,7 @@ la_status prefill_impl(const la_prefill_desc* d, const int32_t* cu_seqlens, int3
     if ((reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0) return LA_ERR_ALIGN;
   }
   if (!q || !k || !v || !o) return LA_ERR_NULL;
-  if (d->psi == LA_PSI_PRF && !prf_w) return LA_ERR_NULL;
+  if (la::is_prf(d->psi) && !prf_w) return LA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(prf_w) ||
       !aligned16(init_S) || !aligned16(init_Z) || !aligned16(final_S) || !aligned16(final_Z) ||
       !aligned16(workspace))
@@ -255,18 +255,18 @@ la_status lin_attn_decode_step(const la_decode_desc* d, const void* q, const voi
                                hipStream_t stream) {
   if (!d) return LA_ERR_NULL;
   if (d->N < 1 || d->H < 1 || d->d_k < 1 || d->d_v < 1 || d->n_psi < 1) return LA_ERR_SHAPE;
-  if (d->psi < LA_PSI_IDENTITY || d->psi > LA_PSI_PRF) return LA_ERR_VALUE;
+  if (d->psi < LA_PSI_IDENTITY || d->psi > LA_PSI_PRF_QSHIFT) return LA_ERR_VALUE;
   if (d->normalize != 0 && d->normalize != 1) return LA_ERR_VALUE;
   if (!(d->eps >= 0.f) || !isfinite(d->eps)) return LA_ERR_VALUE;
   if (d->in_dtype != LA_BF16 && d->in_dtype != LA_F32) return LA_ERR_VALUE;
   if (d->out_dtype != LA_BF16 && d->out_dtype != LA_F32) return LA_ERR_VALUE;
-  if (d->psi != LA_PSI_PRF && d->n_psi != d->d_k) return LA_ERR_SHAPE;
+  if (!la::is_prf(d->psi) && d->n_psi != d->d_k) return LA_ERR_SHAPE;
   if ((long long)d->N * d->H > 2147483647LL) return LA_ERR_SHAPE;
   if (d->out_dtype != LA_F32) return LA_ERR_UNSUPPORTED;
   if (!la::decode_supported(d->d_k, d->d_v, d->n_psi, d->psi)) return LA_ERR_UNSUPPORTED;
   if (!q || !k || !v || !S || !o) return LA_ERR_NULL;
   if (d->normalize && !Z) return LA_ERR_NULL;
-  if (d->psi == LA_PSI_PRF && !prf_w) return LA_ERR_NULL;
+  if (la::is_prf(d->psi) && !prf_w) return LA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(S) || !aligned16(Z) || !aligned16(o) ||
       !aligned16(prf_w))
     return LA_ERR_ALIGN;

@@ -60,11 +60,27 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeParams p) {
         dot += wj * x[j];
         sq += x[j] * x[j];
       }
-      val = expf(dot - 0.5f * sq) * rsqrtf((float)n_psi);
+      const float l = dot - 0.5f * sq;
+      // with the query-row shift the query's log-features are exponentiated below
+      val = (which == 1 && p.psi == LA_PSI_PRF_QSHIFT) ? l : expf(l) * rsqrtf((float)n_psi);
     }
     (which == 0 ? sf : sg)[f] = val;
   }
   __syncthreads();
+  if (p.psi == LA_PSI_PRF_QSHIFT) {  // psi(q)_p = exp(l_p - max_r l_r) / sqrt(m)
+    float mx = -__builtin_huge_valf();
+    for (int f = tid; f < n_psi; f += kDecThreads) mx = fmaxf(mx, sg[f]);
+    sred[tid] = mx;
+    __syncthreads();
+    for (int s = kDecThreads / 2; s > 0; s >>= 1) {
+      if (tid < s) sred[tid] = fmaxf(sred[tid], sred[tid + s]);
+      __syncthreads();
+    }
+    const float shift = sred[0];
+    __syncthreads();  // every thread has the shift before sred is reused
+    for (int f = tid; f < n_psi; f += kDecThreads) sg[f] = expf(sg[f] - shift) * rsqrtf((float)n_psi);
+    __syncthreads();
+  }
 
   // normaliser: Z <- gamma Z + f, den = g . Z + eps
   if (p.normalize) {
@@ -112,7 +128,7 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeParams p) {
 bool decode_supported(int d_k, int d_v, int n_psi, int psi) {
   if (d_k != 64 && d_k != 128) return false;
   if (d_v != 64 && d_v != 128) return false;
-  if (psi == LA_PSI_PRF) return n_psi == 64 || n_psi == 128 || n_psi == 256;
+  if (is_prf(psi)) return n_psi == 64 || n_psi == 128 || n_psi == 256;
   return (psi == LA_PSI_IDENTITY || psi == LA_PSI_ELU1) && n_psi == d_k;
 }
 

@@ -79,6 +79,9 @@ struct DecodeParams {
   float gamma[LA_MAX_DECAY_HEADS];
 };
 
+// Positive random features, with or without the query-row shift.
+__host__ __device__ inline bool is_prf(int psi) { return psi == LA_PSI_PRF || psi == LA_PSI_PRF_QSHIFT; }
+
 // Length of packed sequence b, clamped so that malformed offsets never address rows
 // outside [0, total) and no sequence exceeds max_len; its first token is *start.
 __device__ __forceinline__ int packed_len(const int* cu, int b, int total, int max_len, int* start) {

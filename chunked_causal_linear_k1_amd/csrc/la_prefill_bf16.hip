@@ -9,14 +9,14 @@ bool prefill_prf_bf16_supported(int C, int d_k, int d_v, int n_psi);
 hipError_t launch_prefill_prf_bf16(const PrefillParams& p, hipStream_t s, bool out);
 
 bool prefill_bf16_supported(int C, int d_k, int d_v, int n_psi, int psi) {
-  if (psi == LA_PSI_PRF) return prefill_prf_bf16_supported(C, d_k, d_v, n_psi);
+  if (is_prf(psi)) return prefill_prf_bf16_supported(C, d_k, d_v, n_psi);
   if (psi != LA_PSI_IDENTITY && psi != LA_PSI_ELU1) return false;
   if (d_k != d_v || n_psi != d_k) return false;
   return (d_k == 64 || d_k == 128) && (C == 64 || C == 128);
 }
 
 static hipError_t dispatch(const PrefillParams& p, hipStream_t s, bool out) {
-  if (p.psi == LA_PSI_PRF) return launch_prefill_prf_bf16(p, s, out);
+  if (is_prf(p.psi)) return launch_prefill_prf_bf16(p, s, out);
   if (p.C == 64 && p.d_k == 64) return launch_prefill_bf16_c64_d64(p, s, out);
   if (p.C == 64 && p.d_k == 128) return launch_prefill_bf16_c64_d128(p, s, out);
   if (p.C == 128 && p.d_k == 64) return launch_prefill_bf16_c128_d64(p, s, out);
@@ -29,7 +29,7 @@ static hipError_t dispatch(const PrefillParams& p, hipStream_t s, bool out) {
 // the 64-token kernel needs half the LDS, two workgroups share a CU and hide each other's
 // latency. Segment boundaries (multiples of seg_chunks * C tokens) are unchanged.
 hipError_t launch_prefill_bf16_summary(const PrefillParams& p, hipStream_t s) {
-  if (p.C == 128 && p.psi != LA_PSI_PRF) {
+  if (p.C == 128 && !is_prf(p.psi)) {
     PrefillParams q = p;
     q.C = 64;
     q.n_chunks = 2 * p.n_chunks;  // kernels count each sequence's chunks from its own length

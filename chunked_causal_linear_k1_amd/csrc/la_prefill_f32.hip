@@ -64,12 +64,26 @@ __device__ void features_f32(const float* __restrict__ x, size_t rs, float* raw,
           dot += wr[j] * xr[j];
           sq += xr[j] * xr[j];
         }
-        val = expf(dot - 0.5f * sq) * rsqrtf((float)n_psi);
+        val = dot - 0.5f * sq;  // log-feature; exponentiated below
       }
     }
     out[idx] = val;
   }
   __syncthreads();
+  if (is_prf(psi)) {
+    // PRF_QSHIFT: subtract each row's largest log-feature (rows past `valid` stay zero)
+    if (psi == LA_PSI_PRF_QSHIFT) {
+      for (int r = threadIdx.x; r < valid; r += kThreads) {
+        float mx = out[r * n_psi];
+        for (int f = 1; f < n_psi; ++f) mx = fmaxf(mx, out[r * n_psi + f]);
+        for (int f = 0; f < n_psi; ++f) out[r * n_psi + f] -= mx;
+      }
+      __syncthreads();
+    }
+    for (int idx = threadIdx.x; idx < C * n_psi; idx += kThreads)
+      if (idx / n_psi < valid) out[idx] = expf(out[idx]) * rsqrtf((float)n_psi);
+    __syncthreads();
+  }
 }
 
 __device__ void load_rows_f32(const float* __restrict__ x, size_t rs, float* out, int C, int valid, int d) {
@@ -103,7 +117,8 @@ __global__ __launch_bounds__(kThreads) void k_summary_f32(PrefillParams p) {
   const F32Layout Ly = f32_layout(p.C, p.d_k, p.d_v, p.n_psi);
   const int bh = blockIdx.x, seg = blockIdx.y, head = bh % p.H;
   const float lg = p.has_decay ? p.log2g[head] : 0.f;
-  const float* w = p.psi == LA_PSI_PRF ? (const float*)p.prf_w + (size_t)head * p.n_psi * p.d_k : nullptr;
+  const float* w = is_prf(p.psi) ? (const float*)p.prf_w + (size_t)head * p.n_psi * p.d_k : nullptr;
+  const int kpsi = p.psi == LA_PSI_PRF_QSHIFT ? LA_PSI_PRF : p.psi;  // keys take no query shift
   for (int idx = threadIdx.x; idx < p.n_psi * p.d_v + p.n_psi; idx += kThreads) sm[Ly.S + idx] = 0.f;  // S then Z
   const SeqSpan sq = seq_span(p, bh);
   const int T = sq.T, n_chunks = (T + p.C - 1) / p.C;
@@ -115,7 +130,7 @@ __global__ __launch_bounds__(kThreads) void k_summary_f32(PrefillParams p) {
     const int t0 = c * p.C, L = min(p.C, T - t0);
     __syncthreads();
     load_rows_f32(vb + (size_t)t0 * rv, rv, sm + Ly.V, p.C, L, p.d_v);
-    features_f32(kb + (size_t)t0 * rk, rk, sm + Ly.RAW, sm + Ly.FK, p.C, L, p.d_k, p.n_psi, p.psi, w);
+    features_f32(kb + (size_t)t0 * rk, rk, sm + Ly.RAW, sm + Ly.FK, p.C, L, p.d_k, p.n_psi, kpsi, w);
     state_update_f32(sm, Ly, p.C, L, p.d_v, p.n_psi, lg);
   }
   __syncthreads();
@@ -130,7 +145,8 @@ __global__ __launch_bounds__(kThreads) void k_output_f32(PrefillParams p) {
   const int bh = blockIdx.x, seg = blockIdx.y, head = bh % p.H;
   const float lg = p.has_decay ? p.log2g[head] : 0.f;
   const int C = p.C, n_psi = p.n_psi, d_v = p.d_v;
-  const float* w = p.psi == LA_PSI_PRF ? (const float*)p.prf_w + (size_t)head * n_psi * p.d_k : nullptr;
+  const float* w = is_prf(p.psi) ? (const float*)p.prf_w + (size_t)head * n_psi * p.d_k : nullptr;
+  const int kpsi = p.psi == LA_PSI_PRF_QSHIFT ? LA_PSI_PRF : p.psi;  // keys take no query shift
   const size_t E = (size_t)n_psi * d_v + n_psi;
   const float* pre = p.ws + ((size_t)bh * p.n_seg + seg) * E;
   for (int idx = threadIdx.x; idx < (int)E; idx += kThreads) sm[Ly.S + idx] = pre[idx];  // S then Z
@@ -148,7 +164,7 @@ __global__ __launch_bounds__(kThreads) void k_output_f32(PrefillParams p) {
     __syncthreads();
     load_rows_f32(vb + (size_t)t0 * rv, rv, sm + Ly.V, C, L, d_v);
     features_f32(qb + (size_t)t0 * rk, rk, sm + Ly.RAW, sm + Ly.FQ, C, L, p.d_k, n_psi, p.psi, w);
-    features_f32(kb + (size_t)t0 * rk, rk, sm + Ly.RAW, sm + Ly.FK, C, L, p.d_k, n_psi, p.psi, w);
+    features_f32(kb + (size_t)t0 * rk, rk, sm + Ly.RAW, sm + Ly.FK, C, L, p.d_k, n_psi, kpsi, w);
     // scores
     for (int idx = threadIdx.x; idx < C * C; idx += kThreads) {
       const int j = idx / C, i = idx % C;
@@ -191,8 +207,8 @@ static size_t f32_lds_bytes(int C, int d_k, int d_v, int n_psi) {
 }
 
 bool prefill_f32_supported(int C, int d_k, int d_v, int n_psi, int psi) {
-  if (psi < LA_PSI_IDENTITY || psi > LA_PSI_PRF) return false;
-  if (psi != LA_PSI_PRF && n_psi != d_k) return false;
+  if (psi < LA_PSI_IDENTITY || psi > LA_PSI_PRF_QSHIFT) return false;
+  if (!is_prf(psi) && n_psi != d_k) return false;
   if (d_k > 128 || d_v > 128 || n_psi > 256) return false;
   if (C != 16 && C != 32 && C != 64) return false;
   return f32_lds_bytes(C, d_k, d_v, n_psi) <= 160 * 1024;

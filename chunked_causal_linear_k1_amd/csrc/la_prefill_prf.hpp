@@ -56,7 +56,8 @@ struct Geo {
   static constexpr int F_R = F_THETA + C;         // score row sums [NTILE][32]
   static constexpr int F_NQ = F_R + NTILE * 32;   // |q_t|^2 [C]
   static constexpr int F_NK = F_NQ + C;           // |k_t|^2 [C]
-  static constexpr int LDS_BYTES = OFF_F + 4 * (F_NK + C);
+  static constexpr int F_QMAX = F_NK + C;         // per-wave max_p w_p . q_t [NW][C] (query shift)
+  static constexpr int LDS_BYTES = OFF_F + 4 * (F_QMAX + (WITH_Q ? NW * C : 0));
   static_assert(FPW * NW == NFT, "feature tiles split evenly over the waves");
   static_assert(NTILE <= NW, "one score tile per wave");
   static_assert(!WITH_Q || NTILE * A_TILE <= 2 * RAW, "score tiles fit in the raw-tile region");
@@ -341,7 +342,7 @@ __global__ __launch_bounds__(2 * D) void k_summary_prf(PrefillParams p) {
 // ---------------------------------------------------------------------------------------
 // Output pass: per (sequence, segment), from the segment's exclusive prefix (written by
 // the scan), walk the chunks: features, shared score tiles, outputs, state update.
-template <int C, int D, int NP, bool DECAY, bool NORM, bool OBF>
+template <int C, int D, int NP, bool DECAY, bool NORM, bool OBF, bool QS>
 __global__ __launch_bounds__(2 * D) void k_output_prf(PrefillParams p) {
   using G = Geo<C, D, NP, true>;
   using PG = pf::Geo<C, D, true>;
@@ -439,6 +440,26 @@ __global__ __launch_bounds__(2 * D) void k_output_prf(PrefillParams p) {
     }
     lds_barrier();
 
+    // ---- QS: the query-row shift. l_p = w_p . q - |q|^2/2 and its maximum differ by the
+    // same |q|^2/2, so the shifted feature is exp(w_p . q - max_r w_r . q) / sqrt(m). Each
+    // wave takes the maximum over its features (the GEMM is recomputed below), the waves'
+    // maxima meet in LDS.
+    if (QS) {
+#pragma unroll
+      for (int jt = 0; jt < NJ; ++jt) {
+        float mx = -__builtin_huge_valf();
+#pragma unroll
+        for (int f = 0; f < FPW; ++f) {
+          const f32x16 acc = feature_gemm<D>(wop[f], rR, jt, PR * 2);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[r]);
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 32));  // the other half of the lane pair holds the other rows
+        if (hh == 0) sF[G::F_QMAX + w * C + jt * 32 + n] = mx;
+      }
+      lds_barrier();
+    }
+
     // ---- features of this wave's feature tiles: psi(Q) rounded to bf16; psi(K) as hi + lo
     // (zero past the sequence end); zt = sum_i Xi_i psi(k_i) for the feature of register
     // (n >> 1) & 15 (see lane_total16)
@@ -452,7 +473,13 @@ __global__ __launch_bounds__(2 * D) void k_output_prf(PrefillParams p) {
         const int t = jt * 32 + n;
         {
           const f32x16 acc = feature_gemm<D>(wop[f], rR, jt, PR * 2);
-          const float h = 0.5f * sF[G::F_NQ + t] * LOG2E - log2_rsqrt;
+          float qshift = 0.5f * sF[G::F_NQ + t];  // |q|^2 / 2, or the row's largest w_p . q (QS)
+          if (QS) {
+            qshift = sF[G::F_QMAX + t];
+#pragma unroll
+            for (int ww = 1; ww < G::NW; ++ww) qshift = fmaxf(qshift, sF[G::F_QMAX + ww * C + t]);
+          }
+          const float h = qshift * LOG2E - log2_rsqrt;
           float v[16];
 #pragma unroll
           for (int r = 0; r < 16; ++r) v[r] = exp2f(acc[r] * LOG2E - h);
@@ -621,9 +648,12 @@ __global__ __launch_bounds__(2 * D) void k_output_prf(PrefillParams p) {
 
 template <int C, int D, int NP, bool DECAY, bool NORM>
 hipError_t launch_flags(const PrefillParams& p, hipStream_t s, bool out) {
+  const bool qs = p.psi == LA_PSI_PRF_QSHIFT;
   const void* kern = !out ? (const void*)k_summary_prf<C, D, NP, DECAY, NORM>
-                     : p.out_bf16 ? (const void*)k_output_prf<C, D, NP, DECAY, NORM, true>
-                                  : (const void*)k_output_prf<C, D, NP, DECAY, NORM, false>;
+                     : p.out_bf16 ? (qs ? (const void*)k_output_prf<C, D, NP, DECAY, NORM, true, true>
+                                        : (const void*)k_output_prf<C, D, NP, DECAY, NORM, true, false>)
+                                  : (qs ? (const void*)k_output_prf<C, D, NP, DECAY, NORM, false, true>
+                                        : (const void*)k_output_prf<C, D, NP, DECAY, NORM, false, false>);
   const int lds = out ? Geo<C, D, NP, true>::LDS_BYTES : Geo<C, D, NP, false>::LDS_BYTES;
   hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;

@@ -25,7 +25,7 @@ from typing import Dict, List, Optional
 import numpy as np
 import torch
 
-from .workloads import DecodeWorkload, Workload, PSI_PRF
+from .workloads import DecodeWorkload, Workload, PSI_PRF, PSI_PRF_QSHIFT
 
 _TORCH_DTYPE = {"bf16": torch.bfloat16, "f32": torch.float32}
 
@@ -64,7 +64,7 @@ def make_prefill_inputs(w: Workload, device: str = "cpu", seed: Optional[int] = 
     k = _randn((w.B, w.H, w.T, w.d_k), gen, device, w.qk_scale, dt)
     v = _randn((w.B, w.H, w.T, w.d_v), gen, device, w.v_scale, dt)
     prf_w = None
-    if w.psi == PSI_PRF:
+    if w.psi in (PSI_PRF, PSI_PRF_QSHIFT):
         prf_w = _randn((w.H, w.n_psi, w.d_k), gen, device, 1.0, dt)
     return {"q": q, "k": k, "v": v, "prf_w": prf_w, "gamma": gammas(w)}
 

@@ -16,8 +16,9 @@ from typing import Optional
 PSI_IDENTITY = 0
 PSI_ELU1 = 1
 PSI_PRF = 2
+PSI_PRF_QSHIFT = 3  # positive random features with the query-row log-space shift
 
-PSI_NAMES = {PSI_IDENTITY: "identity", PSI_ELU1: "elu+1", PSI_PRF: "prf"}
+PSI_NAMES = {PSI_IDENTITY: "identity", PSI_ELU1: "elu+1", PSI_PRF: "prf", PSI_PRF_QSHIFT: "prf+qshift"}
 
 
 @dataclass(frozen=True)

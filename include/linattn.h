@@ -66,7 +66,14 @@ typedef enum {
 typedef enum {
   LA_PSI_IDENTITY = 0, /* psi(x) = x; requires n_psi == d_k                        */
   LA_PSI_ELU1 = 1,     /* psi(x)_j = x_j + 1 if x_j > 0 else exp(x_j); n_psi == d_k */
-  LA_PSI_PRF = 2       /* psi(x)_p = exp(w_p . x - |x|^2/2) / sqrt(n_psi)           */
+  LA_PSI_PRF = 2,      /* psi(x)_p = exp(w_p . x - |x|^2/2) / sqrt(n_psi)           */
+  LA_PSI_PRF_QSHIFT = 3 /* the same features with the log-space shift of the query
+                         * row ("Linearized 2-Simplicial Attention", appendix B.2):
+                         * psi(q)_p = exp(l_p - max_r l_r) / sqrt(n_psi), l_p = w_p . q
+                         * - |q|^2/2; keys unshifted. The shift depends on the query
+                         * row only and scales numerator and denominator alike, so the
+                         * output equals LA_PSI_PRF's with eps weighted by exp(max_r l_r);
+                         * it keeps psi(q) . S finite for large-magnitude queries.   */
 } la_psi;
 
 typedef enum { LA_BF16 = 0, LA_F32 = 1 } la_dtype;
@@ -84,7 +91,7 @@ typedef struct {
   int32_t B, H, T;       /* batch, heads, sequence length (T >= 1, any value:
                             the last chunk may be ragged)                        */
   int32_t d_k, d_v;      /* key/query and value widths                           */
-  int32_t n_psi;         /* feature width: == d_k unless psi == LA_PSI_PRF       */
+  int32_t n_psi;         /* feature width: == d_k unless psi is a PRF map        */
   int32_t chunk;         /* chunk size C                                         */
   int32_t psi;           /* la_psi                                               */
   int32_t normalize;     /* 1: divide by psi(q).Z + eps; 0: numerator only       */
@@ -99,7 +106,8 @@ typedef struct {
 /* Supported sizes in this build (anything else: LA_ERR_UNSUPPORTED):
  *   in_dtype LA_BF16: psi identity/elu1: d_k == d_v == n_psi in {64, 128},
  *                     chunk in {64, 128};
- *                     psi PRF: d_k == d_v == 128, n_psi in {128, 256}, chunk 64.
+ *                     psi PRF, PRF_QSHIFT: d_k == d_v == 128, n_psi in {128, 256},
+ *                     chunk 64.
  *   in_dtype LA_F32 : d_k, d_v <= 128, n_psi <= 256 (LDS permitting),
  *                     chunk in {16, 32, 64}, any psi.
  *   always: d_v and n_psi multiples of 4 (16-byte state rows in the workspace).
@@ -128,7 +136,8 @@ la_status lin_attn_prefill_varlen_workspace_size(const la_prefill_desc* d, int32
  *   v         device [B, H, T, d_v] in_dtype (likewise)
  *   gamma     host   [H] fp32 per-head decay, 0 < gamma <= 1; NULL means 1
  *   prf_w     device [H, n_psi, d_k] in_dtype (the PRF bank, one per head,
- *             shared over the batch); required iff psi == LA_PSI_PRF
+ *             shared over the batch); required iff psi is LA_PSI_PRF or
+ *             LA_PSI_PRF_QSHIFT
  *   init_S    device [B, H, n_psi, d_v] fp32 state before token 1, or NULL (zero)
  *   init_Z    device [B, H, n_psi] fp32, or NULL (zero); ignored when normalize == 0
  *   o         device [B, H, T, d_v] out_dtype ([B, T, H, d_v] for LA_LAYOUT_BTHD),

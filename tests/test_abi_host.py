@@ -63,7 +63,7 @@ def _ws(desc):
     (dict(T=0), LA_ERR_SHAPE), (dict(B=0), LA_ERR_SHAPE), (dict(H=-1), LA_ERR_SHAPE),
     (dict(d_k=0), LA_ERR_SHAPE), (dict(chunk=0), LA_ERR_SHAPE),
     (dict(n_psi=64), LA_ERR_SHAPE),                       # n_psi != d_k without PRF
-    (dict(psi=3), LA_ERR_VALUE), (dict(normalize=2), LA_ERR_VALUE), (dict(eps=-1.0), LA_ERR_VALUE),
+    (dict(psi=5), LA_ERR_VALUE), (dict(normalize=2), LA_ERR_VALUE), (dict(eps=-1.0), LA_ERR_VALUE),
     (dict(eps=float("nan")), LA_ERR_VALUE), (dict(in_dtype=5), LA_ERR_VALUE),
     (dict(chunk=48), LA_ERR_UNSUPPORTED), (dict(d_k=96, d_v=96, n_psi=96), LA_ERR_UNSUPPORTED),
     (dict(out_dtype=LA_BF16), LA_OK),                      # bf16 output = RNE of the fp32 result
@@ -83,6 +83,9 @@ def _ws(desc):
     # positive random features: bf16 needs d 128, n_psi 128 or 256, chunk 64
     (dict(psi=2, n_psi=256), LA_OK), (dict(psi=2, n_psi=128), LA_OK),
     (dict(psi=2, n_psi=64), LA_ERR_UNSUPPORTED), (dict(psi=2, n_psi=256, chunk=128), LA_ERR_UNSUPPORTED),
+    # the same features with the query-row shift; anything past it is not a feature map
+    (dict(psi=3, n_psi=256), LA_OK), (dict(psi=3, n_psi=128), LA_OK), (dict(psi=3, n_psi=64), LA_ERR_UNSUPPORTED),
+    (dict(psi=3, in_dtype=LA_F32, d_k=64, d_v=64, n_psi=96, chunk=32), LA_OK), (dict(psi=4), LA_ERR_VALUE),
 ])
 def test_prefill_validation(kw, status):
     st, _ = _ws(_desc(**kw))

@@ -7,7 +7,8 @@ import torch
 
 import oracle
 from chunked_causal_linear_k1_amd import binding, inputs, workloads
-from chunked_causal_linear_k1_amd.workloads import PSI_ELU1, PSI_IDENTITY, PSI_PRF, DecodeWorkload, Workload
+from chunked_causal_linear_k1_amd.workloads import (PSI_ELU1, PSI_IDENTITY, PSI_PRF, PSI_PRF_QSHIFT, DecodeWorkload,
+                                                    Workload)
 
 from gpu_common import announce, assert_close
 
@@ -63,10 +64,13 @@ def test_decode_small(psi, d, normalize, gamma):
     _run_steps(w, S, Z, steps, w.steps)
 
 
-def test_decode_prf():
-    w = DecodeWorkload(name="dec_prf", N=2, H=3, d_k=128, d_v=128, n_psi=256, psi=PSI_PRF, normalize=1, eps=1e-6,
+@pytest.mark.parametrize("psi,q_mult", [(PSI_PRF, 1.0), (PSI_PRF_QSHIFT, 1.0), (PSI_PRF_QSHIFT, 8.0)])
+def test_decode_prf(psi, q_mult):
+    """PRF decode; with the query-row shift also for queries 8x larger, whose unshifted
+    log-features (about -300) underflow in fp32."""
+    w = DecodeWorkload(name=f"dec_prf{psi}", N=2, H=3, d_k=128, d_v=128, n_psi=256, psi=psi, normalize=1, eps=1e-6,
                        gamma=0.99, prefix_len=64, steps=4, seed=8)
-    announce("decode prf")
+    announce(f"decode prf psi={psi} q x{q_mult}")
     g = torch.Generator().manual_seed(99)
     prf = torch.randn((3, 256, 128), generator=g).to(torch.bfloat16)
     # prefix state from the oracle, with keys scaled like the PRF workload
@@ -76,6 +80,7 @@ def test_decode_prf():
                              w_head=[b % 3 for b in range(6)], gamma=[0.99] * 6, normalize=1, want_state=True)
     steps = {n: (torch.randn((4, 2, 3, 128), generator=g) * (128 ** -0.25 if n != "v" else 1.0)).to(torch.bfloat16)
              for n in ("q", "k", "v")}
+    steps["q"] = (steps["q"].float() * q_mult).to(torch.bfloat16)  # a power of two: exact
     _run_steps(w, S, Z, steps, 4, prf=prf)
 
 

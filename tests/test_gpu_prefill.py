@@ -14,7 +14,7 @@ import torch
 
 import oracle
 from chunked_causal_linear_k1_amd import binding, inputs, workloads
-from chunked_causal_linear_k1_amd.workloads import PSI_ELU1, PSI_IDENTITY, PSI_PRF, Workload
+from chunked_causal_linear_k1_amd.workloads import PSI_ELU1, PSI_IDENTITY, PSI_PRF, PSI_PRF_QSHIFT, Workload
 
 from gpu_common import announce, assert_close
 
@@ -265,6 +265,49 @@ def test_prf_small_elementwise(case):
         # rel-L2 as is, max-abs on outputs scaled by the largest reference magnitude
         scale = float(np.abs(ref).max())
         assert_close(o / scale, ref / scale, "bf16", f"{name} (scaled by max |o| = {scale:.3g})")
+
+
+# the same features with the query-row log-space shift (psi(q)_p = exp(l_p - max_r l_r) / sqrt(m))
+PRF_QSHIFT = [
+    # name, T, n_psi, normalize, decay, query multiplier
+    ("qshift256", 450, 256, 1, "none", 1.0),
+    ("qshift128_decay", 333, 128, 1, "const:0.99", 1.0),
+    ("qshift256_nonorm_spread", 300, 256, 0, "retnet_spread", 1.0),
+    # queries 8x larger: unshifted log-features near -300 underflow in fp32, shifted ones peak at 0
+    ("qshift256_large_queries", 400, 256, 1, "none", 8.0),
+    ("qshift128_large_queries_decay", 200, 128, 1, "const:0.98", 8.0),
+]
+
+
+@pytest.mark.parametrize("case", PRF_QSHIFT, ids=[c[0] for c in PRF_QSHIFT])
+def test_prf_qshift(case):
+    name, T, n_psi, normalize, decay, q_mult = case
+    B, H = 1, 2
+    w = Workload(name=name, B=B, H=H, T=T, d_k=128, d_v=128, n_psi=n_psi, chunk=64, psi=PSI_PRF_QSHIFT,
+                 normalize=normalize, eps=1e-6, dtype="bf16", seed=19, qk_scale=128 ** -0.25, v_scale=1.0,
+                 decay=decay)
+    announce(f"prefill prf query shift {name}")
+    inp = inputs.make_prefill_inputs(w, device="cpu")
+    inp["q"] = (inp["q"].float() * q_mult).to(torch.bfloat16)  # a power of two: exact
+    o = _run(w, inp).cpu().reshape(B * H, T, 128).numpy()
+    ref = _oracle_o(w, inp)
+    if normalize:
+        assert_close(o, ref, "bf16", name)
+    else:
+        scale = float(np.abs(ref).max())
+        assert_close(o / scale, ref / scale, "bf16", f"{name} (scaled by max |o| = {scale:.3g})")
+
+
+def test_prf_qshift_f32_path():
+    """The fp32 path with the query-row shift (d 64, n_psi 96, chunk 32)."""
+    w = Workload(name="f32_qshift", B=1, H=2, T=150, d_k=64, d_v=64, n_psi=96, chunk=32, psi=PSI_PRF_QSHIFT,
+                 normalize=1, eps=1e-6, dtype="f32", seed=23, qk_scale=64 ** -0.25, v_scale=1.0,
+                 decay="const:0.97")
+    announce("prefill prf query shift fp32")
+    inp = inputs.make_prefill_inputs(w, device="cpu")
+    o = _run(w, inp).cpu().reshape(2, 150, 64).numpy()
+    ref = _oracle_o(w, inp)
+    assert_close(o, ref, "f32", w.name)
 
 
 @pytest.mark.parametrize("T", [1, 63, 64, 65, 129])
