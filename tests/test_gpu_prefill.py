@@ -298,6 +298,22 @@ def test_prf_qshift(case):
         assert_close(o / scale, ref / scale, "bf16", f"{name} (scaled by max |o| = {scale:.3g})")
 
 
+@pytest.mark.parametrize("psi", [PSI_PRF, PSI_PRF_QSHIFT])
+def test_prf_orthogonal_bank(psi):
+    """The orthogonal Gaussian bank ("Linearized 2-Simplicial Attention", appendix B.1: Haar
+    blocks of 128 rows with chi_128 radii) in place of the independent one."""
+    from chunked_causal_linear_k1_amd import prf_bank
+    w = Workload(name="prf_orthogonal", B=1, H=2, T=350, d_k=128, d_v=128, n_psi=256, chunk=64, psi=psi,
+                 normalize=1, eps=1e-6, dtype="bf16", seed=29, qk_scale=128 ** -0.25, v_scale=1.0,
+                 decay="const:0.995")
+    announce(f"prefill prf orthogonal bank psi={psi}")
+    inp = inputs.make_prefill_inputs(w, device="cpu")
+    inp["prf_w"] = prf_bank.orthogonal_bank(2, 256, 128, seed=5)
+    o = _run(w, inp)
+    ref = _oracle_o(w, inp)
+    assert_close(o.cpu().reshape(2, 350, 128).numpy(), ref, "bf16", f"orthogonal bank psi={psi}")
+
+
 def test_prf_qshift_f32_path():
     """The fp32 path with the query-row shift (d 64, n_psi 96, chunk 32)."""
     w = Workload(name="f32_qshift", B=1, H=2, T=150, d_k=64, d_v=64, n_psi=96, chunk=32, psi=PSI_PRF_QSHIFT,
