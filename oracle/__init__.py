@@ -64,6 +64,15 @@ def _load():
         lib.oracle_decode_step_f64.argtypes = [ctypes.c_int] * 6 + [vp, vp, vp, vp, ip, dp, ctypes.c_int,
                                                                       ctypes.c_double, dp, dp, dp,
                                                                       ctypes.c_int]
+        fp = ctypes.POINTER(ctypes.c_float)
+        lib.oracle_prefill_gated_f64.restype = ctypes.c_int
+        lib.oracle_prefill_gated_f64.argtypes = [ctypes.c_int] * 7 + [vp, vp, vp, vp, ip, fp, ctypes.c_int,
+                                                                        ctypes.c_double, dp, dp, dp, dp, dp,
+                                                                        ctypes.c_int]
+        lib.oracle_decode_step_gated_f64.restype = ctypes.c_int
+        lib.oracle_decode_step_gated_f64.argtypes = [ctypes.c_int] * 6 + [vp, vp, vp, vp, ip, fp, ctypes.c_int,
+                                                                            ctypes.c_double, dp, dp, dp,
+                                                                            ctypes.c_int]
         lib.oracle_feature_f64.restype = None
         lib.oracle_feature_f64.argtypes = [ctypes.c_int] * 3 + [dp, dp, dp]
         lib.oracle_max_threads.restype = ctypes.c_int
@@ -104,7 +113,7 @@ def max_threads() -> int:
 
 def prefill(q, k, v, psi: int, n_psi: Optional[int] = None, prf_w=None, w_head=None, gamma=None,
             normalize: int = 1, eps: float = 1e-6, S0=None, Z0=None, want_state: bool = False,
-            nthreads: int = 0):
+            nthreads: int = 0, log_gate=None):
     """Oracle prefill for blocks [nblk, T, d] (leading dims are flattened into blocks).
 
     gamma: per-block decay values (anything array-like; each is used as given, in fp64) or None.
@@ -139,13 +148,24 @@ def prefill(q, k, v, psi: int, n_psi: Optional[int] = None, prf_w=None, w_head=N
     o = np.empty(lead + (T, d_v), dtype=np.float64) if qq is not None else None
     S = np.empty((nblk, n_psi, d_v), dtype=np.float64) if want_state else None
     Z = np.empty((nblk, n_psi), dtype=np.float64) if want_state else None
-    rc = lib.oracle_prefill_f64(
-        nblk, T, d_k, d_v, n_psi, psi, dt,
-        None if qq is None else qq.ctypes.data, kk.ctypes.data, vv.ctypes.data,
-        None if ww is None else ww.ctypes.data,
-        None if wh is None else wh.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
-        _dptr(g), int(normalize), float(eps), _dptr(s0), _dptr(z0), _dptr(o), _dptr(S), _dptr(Z),
-        int(nthreads))
+    if log_gate is not None:
+        # per-token, per-state-row forget gates exp(log_gate) in place of gamma (fp32 values)
+        lgt = _gate_f32(log_gate, (nblk, T, n_psi))
+        rc = lib.oracle_prefill_gated_f64(
+            nblk, T, d_k, d_v, n_psi, psi, dt,
+            None if qq is None else qq.ctypes.data, kk.ctypes.data, vv.ctypes.data,
+            None if ww is None else ww.ctypes.data,
+            None if wh is None else wh.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+            lgt.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), int(normalize), float(eps), _dptr(s0), _dptr(z0),
+            _dptr(o), _dptr(S), _dptr(Z), int(nthreads))
+    else:
+        rc = lib.oracle_prefill_f64(
+            nblk, T, d_k, d_v, n_psi, psi, dt,
+            None if qq is None else qq.ctypes.data, kk.ctypes.data, vv.ctypes.data,
+            None if ww is None else ww.ctypes.data,
+            None if wh is None else wh.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+            _dptr(g), int(normalize), float(eps), _dptr(s0), _dptr(z0), _dptr(o), _dptr(S), _dptr(Z),
+            int(nthreads))
     if rc != 0:
         raise RuntimeError("oracle_prefill_f64 failed")
     if want_state:
@@ -153,8 +173,22 @@ def prefill(q, k, v, psi: int, n_psi: Optional[int] = None, prf_w=None, w_head=N
     return o
 
 
+def _gate_f32(log_gate, shape) -> np.ndarray:
+    """log gates as a contiguous fp32 array of the given shape (fp32 values kept exactly)."""
+    try:
+        import torch
+        if isinstance(log_gate, torch.Tensor):
+            log_gate = log_gate.detach().cpu().float().numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    a = np.ascontiguousarray(np.asarray(log_gate, dtype=np.float32))
+    if a.size != int(np.prod(shape)):
+        raise ValueError(f"log_gate has {a.size} values, expected {shape}")
+    return a.reshape(shape)
+
+
 def decode_step(q, k, v, S, Z, psi: int, prf_w=None, w_head=None, gamma=None, normalize: int = 1,
-                eps: float = 1e-6, nthreads: int = 0):
+                eps: float = 1e-6, nthreads: int = 0, log_gate=None):
     """One in-place decode step on fp64 state S [nblk, n_psi, d_v], Z [nblk, n_psi]. Returns o (fp64)."""
     lib = _load()
     qq, dt = _stored(q)
@@ -172,11 +206,20 @@ def decode_step(q, k, v, S, Z, psi: int, prf_w=None, w_head=None, gamma=None, no
     if Z is not None:
         assert Z.dtype == np.float64 and Z.flags.c_contiguous
     o = np.empty(kk.shape[:-1] + (d_v,), dtype=np.float64)
-    rc = lib.oracle_decode_step_f64(
-        nblk, d_k, d_v, n_psi, psi, dt, qq.ctypes.data, kk.ctypes.data, vv.ctypes.data,
-        None if ww is None else ww.ctypes.data,
-        None if wh is None else wh.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
-        _dptr(g), int(normalize), float(eps), _dptr(S), _dptr(Z), _dptr(o), int(nthreads))
+    if log_gate is not None:
+        lgt = _gate_f32(log_gate, (nblk, n_psi))
+        rc = lib.oracle_decode_step_gated_f64(
+            nblk, d_k, d_v, n_psi, psi, dt, qq.ctypes.data, kk.ctypes.data, vv.ctypes.data,
+            None if ww is None else ww.ctypes.data,
+            None if wh is None else wh.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+            lgt.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), int(normalize), float(eps), _dptr(S), _dptr(Z),
+            _dptr(o), int(nthreads))
+    else:
+        rc = lib.oracle_decode_step_f64(
+            nblk, d_k, d_v, n_psi, psi, dt, qq.ctypes.data, kk.ctypes.data, vv.ctypes.data,
+            None if ww is None else ww.ctypes.data,
+            None if wh is None else wh.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+            _dptr(g), int(normalize), float(eps), _dptr(S), _dptr(Z), _dptr(o), int(nthreads))
     if rc != 0:
         raise RuntimeError("oracle_decode_step_f64 failed")
     return o

@@ -59,3 +59,33 @@ def quadratic(q: np.ndarray, k: np.ndarray, v: np.ndarray, psi: int, gamma: floa
     if not normalize:
         return num
     return num / (den + eps)[:, None]
+
+
+def quadratic_gated(q: np.ndarray, k: np.ndarray, v: np.ndarray, psi: int, log_gate: np.ndarray,
+                    normalize: int = 1, eps: float = 1e-6, w: np.ndarray | None = None,
+                    S0: np.ndarray | None = None, Z0: np.ndarray | None = None) -> np.ndarray:
+    """One (batch, head) with per-token, per-feature forget gates alpha_t = exp(log_gate_t)
+    [T, n_psi], in the parallel form: with G_t = sum_{s <= t} log_gate_s,
+        A[t, i] = sum_p psi(q_t)_p psi(k_i)_p exp(G_t[p] - G_i[p])    (i <= t)
+        num_t   = sum_i A[t, i] v_i + sum_p psi(q_t)_p exp(G_t[p]) S0[p, :]
+        den_t   = sum_i A[t, i]     + sum_p psi(q_t)_p exp(G_t[p]) Z0[p]
+    ("Linear Attention and Retentive Networks", Data-Dependent Gating Mechanism: the product
+    of the gates between token i and t scales what token i wrote)."""
+    T = q.shape[0]
+    fq = feature_np(q, psi, w)
+    fk = feature_np(k, 2 if psi == 3 else psi, w)
+    G = np.cumsum(np.asarray(log_gate, dtype=np.float64), axis=0)  # [T, n_psi]
+    A = np.zeros((T, T))
+    for t in range(T):
+        dec = np.exp(G[t][None, :] - G[: t + 1])  # [t+1, n_psi]
+        A[t, : t + 1] = (fk[: t + 1] * dec) @ fq[t]
+    num = A @ v
+    den = A.sum(axis=1)
+    if S0 is not None:
+        fqd = fq * np.exp(G)
+        num = num + fqd @ S0
+        if Z0 is not None:
+            den = den + fqd @ Z0
+    if not normalize:
+        return num
+    return num / (den + eps)[:, None]

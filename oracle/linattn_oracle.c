@@ -223,6 +223,131 @@ int oracle_decode_step_f64(int nblk, int d_k, int d_v, int n_psi, int psi, int i
   return err ? -1 : 0;
 }
 
+/*
+ * Gated recurrence ("Linear Attention and Retentive Networks", Data-Dependent Gating
+ * Mechanism: S_t = G_t . S_{t-1} + k_t^T v_t with G_t = alpha_t 1^T, one forget gate per
+ * state row, i.e. per key feature): for every token t,
+ *   alpha = exp(log_gate_t)                                  (n_psi gates)
+ *   S[p][:] = alpha[p] S[p][:] + psi(k_t)[p] v_t^T;  Z[p] = alpha[p] Z[p] + psi(k_t)[p]
+ *   o_t = psi(q_t)^T S / (psi(q_t) . Z + eps)   (or the numerator alone)
+ * log_gate: fp32 [nblk][T][n_psi] (fp32 values used exactly); other arguments as for
+ * oracle_prefill_f64. Update first, then read, as in the ungated recurrence.
+ */
+static void gated_step(int psi, int d_k, int d_v, int n_psi, const double* w, const float* lg,
+                       int normalize, double eps, const double* kt, const double* vt, const double* qt,
+                       double* S, double* Z, double* f, double* g, double* ot) {
+  oracle_feature_f64(psi == ORC_PSI_PRF_QSHIFT ? ORC_PSI_PRF : psi, d_k, n_psi, kt, w, f);
+  for (int p = 0; p < n_psi; ++p) {
+    const double alpha = exp((double)lg[p]);
+    double* row = S + (size_t)p * d_v;
+    for (int e = 0; e < d_v; ++e) row[e] = alpha * row[e] + f[p] * vt[e];
+    if (Z) Z[p] = alpha * Z[p] + f[p];
+  }
+  if (!qt) return;
+  oracle_feature_f64(psi, d_k, n_psi, qt, w, g);
+  double den = 0.0;
+  if (normalize) {
+    for (int p = 0; p < n_psi; ++p) den += g[p] * Z[p];
+    den += eps;
+  }
+  for (int e = 0; e < d_v; ++e) ot[e] = 0.0;
+  for (int p = 0; p < n_psi; ++p) {
+    const double* row = S + (size_t)p * d_v;
+    for (int e = 0; e < d_v; ++e) ot[e] += g[p] * row[e];
+  }
+  if (normalize)
+    for (int e = 0; e < d_v; ++e) ot[e] = ot[e] / den;
+}
+
+int oracle_prefill_gated_f64(int nblk, int T, int d_k, int d_v, int n_psi, int psi, int in_dtype,
+                             const void* q, const void* k, const void* v, const void* w,
+                             const int32_t* w_head, const float* log_gate, int normalize, double eps,
+                             const double* S0, const double* Z0, double* o, double* S_out,
+                             double* Z_out, int nthreads) {
+  if (nblk < 0 || T < 0 || d_k <= 0 || d_v <= 0 || n_psi <= 0 || !log_gate) return -1;
+  if (!ORC_IS_PRF(psi) && n_psi != d_k) return -1;
+  if (ORC_IS_PRF(psi) && !w) return -1;
+  if (q && !o) return -1;
+  int err = 0;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : err)
+#endif
+  for (int b = 0; b < nblk; ++b) {
+    double* S = (double*)calloc((size_t)n_psi * d_v, sizeof(double));
+    double* Z = (double*)calloc((size_t)n_psi, sizeof(double));
+    double* f = (double*)malloc(sizeof(double) * (size_t)n_psi);
+    double* g = (double*)malloc(sizeof(double) * (size_t)n_psi);
+    double* kt = (double*)malloc(sizeof(double) * (size_t)d_k);
+    double* qt = (double*)malloc(sizeof(double) * (size_t)d_k);
+    double* vt = (double*)malloc(sizeof(double) * (size_t)d_v);
+    double* wd = NULL;
+    if (ORC_IS_PRF(psi)) wd = (double*)malloc(sizeof(double) * (size_t)n_psi * d_k);
+    if (!S || !Z || !f || !g || !kt || !qt || !vt || (ORC_IS_PRF(psi) && !wd)) {
+      err |= 1;
+    } else {
+      if (wd) {
+        size_t hw = w_head ? (size_t)w_head[b] : 0;
+        load_vec(w, in_dtype, hw * (size_t)n_psi * d_k, n_psi * d_k, wd);
+      }
+      if (S0) memcpy(S, S0 + (size_t)b * n_psi * d_v, sizeof(double) * (size_t)n_psi * d_v);
+      if (Z0) memcpy(Z, Z0 + (size_t)b * n_psi, sizeof(double) * (size_t)n_psi);
+      for (int t = 0; t < T; ++t) {
+        size_t rowk = ((size_t)b * T + t) * d_k, rowv = ((size_t)b * T + t) * d_v;
+        load_vec(k, in_dtype, rowk, d_k, kt);
+        load_vec(v, in_dtype, rowv, d_v, vt);
+        if (q) load_vec(q, in_dtype, rowk, d_k, qt);
+        gated_step(psi, d_k, d_v, n_psi, wd, log_gate + ((size_t)b * T + t) * n_psi, normalize, eps, kt, vt,
+                   q ? qt : NULL, S, Z, f, g, q ? o + rowv : NULL);
+      }
+      if (S_out) memcpy(S_out + (size_t)b * n_psi * d_v, S, sizeof(double) * (size_t)n_psi * d_v);
+      if (Z_out) memcpy(Z_out + (size_t)b * n_psi, Z, sizeof(double) * (size_t)n_psi);
+    }
+    free(S); free(Z); free(f); free(g); free(kt); free(qt); free(vt); free(wd);
+  }
+  return err ? -1 : 0;
+}
+
+/* One gated decode step for nblk states in place (log_gate: fp32 [nblk][n_psi]). */
+int oracle_decode_step_gated_f64(int nblk, int d_k, int d_v, int n_psi, int psi, int in_dtype,
+                                 const void* q, const void* k, const void* v, const void* w,
+                                 const int32_t* w_head, const float* log_gate, int normalize, double eps,
+                                 double* S, double* Z, double* o, int nthreads) {
+  if (nblk < 0 || d_k <= 0 || d_v <= 0 || n_psi <= 0 || !q || !k || !v || !S || !o || !log_gate) return -1;
+  if (!ORC_IS_PRF(psi) && n_psi != d_k) return -1;
+  if (ORC_IS_PRF(psi) && !w) return -1;
+  if (normalize && !Z) return -1;
+  int err = 0;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(static) reduction(| : err)
+#endif
+  for (int b = 0; b < nblk; ++b) {
+    double* f = (double*)malloc(sizeof(double) * (size_t)n_psi);
+    double* g = (double*)malloc(sizeof(double) * (size_t)n_psi);
+    double* kt = (double*)malloc(sizeof(double) * (size_t)d_k);
+    double* qt = (double*)malloc(sizeof(double) * (size_t)d_k);
+    double* vt = (double*)malloc(sizeof(double) * (size_t)d_v);
+    double* wd = NULL;
+    if (ORC_IS_PRF(psi)) wd = (double*)malloc(sizeof(double) * (size_t)n_psi * d_k);
+    if (!f || !g || !kt || !qt || !vt || (ORC_IS_PRF(psi) && !wd)) {
+      err |= 1;
+    } else {
+      if (wd) {
+        size_t hw = w_head ? (size_t)w_head[b] : 0;
+        load_vec(w, in_dtype, hw * (size_t)n_psi * d_k, n_psi * d_k, wd);
+      }
+      load_vec(k, in_dtype, (size_t)b * d_k, d_k, kt);
+      load_vec(q, in_dtype, (size_t)b * d_k, d_k, qt);
+      load_vec(v, in_dtype, (size_t)b * d_v, d_v, vt);
+      gated_step(psi, d_k, d_v, n_psi, wd, log_gate + (size_t)b * n_psi, normalize, eps, kt, vt, qt,
+                 S + (size_t)b * n_psi * d_v, Z ? Z + (size_t)b * n_psi : NULL, f, g, o + (size_t)b * d_v);
+    }
+    free(f); free(g); free(kt); free(qt); free(vt); free(wd);
+  }
+  return err ? -1 : 0;
+}
+
 int oracle_max_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

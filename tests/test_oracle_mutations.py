@@ -33,6 +33,14 @@ MUTATIONS = {
     "qshift_on_keys_too": [("oracle_feature_f64(psi == ORC_PSI_PRF_QSHIFT ? ORC_PSI_PRF : psi, d_k, n_psi, kt, w, f);",
                             "oracle_feature_f64(psi, d_k, n_psi, kt, w, f);")],
     "qshift_missing": [("if (psi == ORC_PSI_PRF_QSHIFT) {", "if (0) {")],
+    "gate_after_write": [("for (int e = 0; e < d_v; ++e) row[e] = alpha * row[e] + f[p] * vt[e];",
+                          "for (int e = 0; e < d_v; ++e) row[e] = alpha * (row[e] + f[p] * vt[e]);")],
+    "gate_not_on_Z": [("if (Z) Z[p] = alpha * Z[p] + f[p];", "if (Z) Z[p] = Z[p] + f[p];")],
+    "gate_of_previous_token": [("log_gate + ((size_t)b * T + t) * n_psi,",
+                                "log_gate + ((size_t)b * T + (t > 0 ? t - 1 : 0)) * n_psi,")],
+    "gate_exp_sign": [("const double alpha = exp((double)lg[p]);", "const double alpha = exp(-(double)lg[p]);")],
+    "gate_channel_reversed": [("const double alpha = exp((double)lg[p]);",
+                               "const double alpha = exp((double)lg[n_psi - 1 - p]);")],
     "qshift_min_not_max": [("shift = out[p] > shift ? out[p] : shift;", "shift = out[p] < shift ? out[p] : shift;")],
     "prf_scale_1_over_m": [("1.0 / sqrt((double)n_psi)", "1.0 / (double)n_psi")],
     "state_transposed": [("ot[e] += g[p] * row[e];",

@@ -380,3 +380,82 @@ def test_bf16_inputs_upcast_exactly():
     o = oracle.prefill(x, x, x, oracle.PSI_IDENTITY, normalize=0)
     xd = x.to(torch.float64).numpy()[0, 0]
     np.testing.assert_array_equal(o[0, 0], (xd @ xd) * xd)
+
+
+# ----------------------------------------------------------------------------- gated recurrence
+def _gates(shape, seed, lo=-3.0):
+    """log forget gates in [lo, 0): log-sigmoid of a scaled Gaussian, fp32 (the values both
+    sides receive)."""
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(shape, generator=g) * 2.0 + 1.0
+    return torch.clamp(torch.nn.functional.logsigmoid(x), min=lo).to(torch.float32)
+
+
+@pytest.mark.parametrize("psi,normalize,with_state", [("identity", 0, False), ("identity", 0, True),
+                                                       ("elu1", 1, False), ("elu1", 1, True),
+                                                       ("prf", 1, True)])
+def test_gated_recurrence_matches_quadratic_form(psi, normalize, with_state):
+    """S_t = diag(alpha_t) S_{t-1} + psi(k_t) v_t^T against the parallel form with the
+    products of the gates between writer and reader ("Linear Attention and Retentive
+    Networks", Data-Dependent Gating Mechanism)."""
+    T, d_k, d_v = 45, 6, 5
+    n_psi = 9 if psi == "prf" else d_k
+    q, k = _rand((1, T, d_k), 21, 0.7), _rand((1, T, d_k), 22, 0.7)
+    v = _rand((1, T, d_v), 23)
+    w = _rand((n_psi, d_k), 24) if psi == "prf" else None
+    lg = _gates((1, T, n_psi), 25)
+    rng = np.random.default_rng(1)
+    S0 = rng.standard_normal((n_psi, d_v)) if with_state else None
+    Z0 = np.abs(rng.standard_normal(n_psi)) + 1.0 if with_state else None
+    o = oracle.prefill(q, k, v, PSI[psi], n_psi=n_psi, prf_w=None if w is None else w[None], normalize=normalize,
+                       eps=1e-3, log_gate=lg, S0=None if S0 is None else S0[None],
+                       Z0=None if Z0 is None else Z0[None])[0]
+    ref = brute.quadratic_gated(oracle.as_f64(q[0]), oracle.as_f64(k[0]), oracle.as_f64(v[0]), PSI[psi],
+                                lg[0].double().numpy(), normalize, 1e-3, None if w is None else oracle.as_f64(w),
+                                S0=S0, Z0=Z0)
+    np.testing.assert_allclose(o, ref, rtol=1e-10, atol=1e-11 * np.abs(ref).max())
+
+
+def test_constant_gate_is_scalar_decay():
+    """The same gate in every channel and at every token is the per-head decay gamma."""
+    T, d = 60, 8
+    q, k, v = _rand((2, T, d), 31, 0.5), _rand((2, T, d), 32, 0.5), _rand((2, T, d), 33)
+    lg = torch.full((2, T, d), math.log(0.93), dtype=torch.float32)
+    gam = math.exp(float(lg[0, 0, 0]))  # the decay the stored fp32 log gate stands for
+    for normalize in (0, 1):
+        a = oracle.prefill(q, k, v, oracle.PSI_ELU1, normalize=normalize, log_gate=lg)
+        b = oracle.prefill(q, k, v, oracle.PSI_ELU1, normalize=normalize, gamma=[gam, gam])
+        np.testing.assert_allclose(a, b, rtol=1e-12, atol=0)
+
+
+def test_zero_log_gate_is_no_decay():
+    T, d = 40, 8
+    q, k, v = _rand((1, T, d), 41, 0.5), _rand((1, T, d), 42, 0.5), _rand((1, T, d), 43)
+    a = oracle.prefill(q, k, v, oracle.PSI_ELU1, log_gate=torch.zeros((1, T, d)))
+    b = oracle.prefill(q, k, v, oracle.PSI_ELU1)
+    assert np.array_equal(a, b)
+
+
+def test_gated_decode_equals_prefill():
+    T, d = 30, 8
+    q, k, v = _rand((3, T, d), 51, 0.5), _rand((3, T, d), 52, 0.5), _rand((3, T, d), 53)
+    lg = _gates((3, T, d), 54)
+    ref = oracle.prefill(q, k, v, oracle.PSI_ELU1, log_gate=lg)
+    S, Z = np.zeros((3, d, d)), np.zeros((3, d))
+    for t in range(T):
+        o = oracle.decode_step(q[:, t].contiguous(), k[:, t].contiguous(), v[:, t].contiguous(), S, Z,
+                               oracle.PSI_ELU1, log_gate=lg[:, t].contiguous())
+        assert np.array_equal(o, ref[:, t])
+
+
+def test_strong_gate_forgets_the_past():
+    """A gate of exp(-60) in every channel at token r wipes what came before (to e^-60):
+    afterwards the outputs are those of the sequence that starts at r."""
+    T, d, r = 50, 8, 20
+    q, k, v = _rand((1, T, d), 61, 0.5), _rand((1, T, d), 62, 0.5), _rand((1, T, d), 63)
+    lg = _gates((1, T, d), 64, lo=-1.0)
+    lg[0, r] = -60.0
+    full = oracle.prefill(q, k, v, oracle.PSI_ELU1, log_gate=lg)[0]
+    tail = oracle.prefill(q[:, r:].contiguous(), k[:, r:].contiguous(), v[:, r:].contiguous(), oracle.PSI_ELU1,
+                          log_gate=lg[:, r:].contiguous())[0]
+    np.testing.assert_allclose(full[r:], tail, rtol=1e-20 + 1e-12, atol=1e-20)
