@@ -25,7 +25,8 @@ LA_LAYOUT_BHTD, LA_LAYOUT_BTHD = 0, 1
 MAX_DECAY_HEADS = 256
 
 EXPORTED = ("lin_attn_prefill_workspace_size", "lin_attn_prefill", "lin_attn_prefill_profiled",
-            "lin_attn_prefill_varlen", "lin_attn_prefill_varlen_workspace_size", "lin_attn_decode_step", "lin_attn_status_string", "lin_attn_version")
+            "lin_attn_prefill_varlen", "lin_attn_prefill_varlen_workspace_size", "lin_attn_prefill_gated",
+            "lin_attn_prefill_gated_workspace_size", "lin_attn_decode_step", "lin_attn_decode_step_gated", "lin_attn_status_string", "lin_attn_version")
 
 
 class PrefillDesc(ctypes.Structure):
@@ -73,6 +74,14 @@ def load() -> ctypes.CDLL:
                                                                ctypes.POINTER(ctypes.c_size_t)]
         lib.lin_attn_prefill_varlen.argtypes = [ctypes.POINTER(PrefillDesc), vp, ctypes.c_int32, vp, vp, vp, fp, vp,
                                                 vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        lib.lin_attn_prefill_gated.restype = ctypes.c_int
+        lib.lin_attn_prefill_gated.argtypes = [ctypes.POINTER(PrefillDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                               ctypes.c_size_t, vp]
+        lib.lin_attn_prefill_gated_workspace_size.restype = ctypes.c_int
+        lib.lin_attn_prefill_gated_workspace_size.argtypes = [ctypes.POINTER(PrefillDesc),
+                                                              ctypes.POINTER(ctypes.c_size_t)]
+        lib.lin_attn_decode_step_gated.restype = ctypes.c_int
+        lib.lin_attn_decode_step_gated.argtypes = [ctypes.POINTER(DecodeDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.lin_attn_decode_step.restype = ctypes.c_int
         lib.lin_attn_decode_step.argtypes = [ctypes.POINTER(DecodeDesc), vp, vp, vp, fp, vp, vp, vp, vp, vp]
         lib.lin_attn_status_string.restype = ctypes.c_char_p
@@ -220,6 +229,70 @@ def lin_attn_prefill_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, c
                                         _stream(stream))
     if st != LA_OK:
         raise LinAttnError(st, "lin_attn_prefill_varlen")
+    return o
+
+
+def gated_workspace_size(desc: PrefillDesc) -> int:
+    n = ctypes.c_size_t(0)
+    st = load().lin_attn_prefill_gated_workspace_size(ctypes.byref(desc), ctypes.byref(n))
+    if st != LA_OK:
+        raise LinAttnError(st, "lin_attn_prefill_gated_workspace_size")
+    return int(n.value)
+
+
+def lin_attn_prefill_gated(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_gate: torch.Tensor, *,
+                           psi: int, chunk: int = 16, normalize: int = 0, eps: float = 1e-6,
+                           init_S: Optional[torch.Tensor] = None, init_Z: Optional[torch.Tensor] = None,
+                           o: Optional[torch.Tensor] = None, final_S: Optional[torch.Tensor] = None,
+                           final_Z: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                           stream=None, layout: str = "bhtd", out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
+    """Gated prefill: q, k, v and the fp32 log forget gates (laid out like k) in layout "bhtd"
+    [B, H, T, d] or "bthd" [B, T, H, d]."""
+    if layout == "bhtd":
+        B, H, T, d_k = q.shape
+        lay = LA_LAYOUT_BHTD
+    elif layout == "bthd":
+        B, T, H, d_k = q.shape
+        lay = LA_LAYOUT_BTHD
+    else:
+        raise ValueError(f"layout must be 'bhtd' or 'bthd', not {layout!r}")
+    d_v = v.shape[-1]
+    if log_gate.dtype != torch.float32 or log_gate.shape != k.shape:
+        raise ValueError("log_gate must be fp32 and shaped like k")
+    for t in (q, k, v, log_gate):
+        if not t.is_contiguous():
+            raise ValueError(f"q, k, v, log_gate must be contiguous ({layout})")
+    if o is None:
+        shape = (B, H, T, d_v) if lay == LA_LAYOUT_BHTD else (B, T, H, d_v)
+        o = torch.empty(shape, dtype=out_dtype, device=q.device)
+    desc = prefill_desc(B, H, T, d_k, d_v, d_k, chunk, psi, normalize, eps, _dtype_code(q), _dtype_code(o), lay)
+    ws_bytes = gated_workspace_size(desc)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    st = load().lin_attn_prefill_gated(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_gate), _ptr(init_S),
+                                       _ptr(init_Z), _ptr(o), _ptr(final_S), _ptr(final_Z), _ptr(workspace),
+                                       0 if workspace is None else workspace.numel() * workspace.element_size(),
+                                       _stream(stream))
+    if st != LA_OK:
+        raise LinAttnError(st, "lin_attn_prefill_gated")
+    return o
+
+
+def lin_attn_decode_step_gated(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_gate: torch.Tensor,
+                               S: torch.Tensor, Z: Optional[torch.Tensor], *, psi: int, normalize: int = 1,
+                               eps: float = 1e-6, prf_w: Optional[torch.Tensor] = None,
+                               o: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """One gated decode step: q, k, v [N, H, d], log_gate fp32 [N, H, n_psi]; S, Z in place."""
+    N, H, d_k = q.shape
+    d_v = v.shape[-1]
+    n_psi = S.shape[-2]
+    desc = DecodeDesc(N, H, d_k, d_v, n_psi, psi, normalize, eps, _dtype_code(q), LA_F32)
+    if o is None:
+        o = torch.empty((N, H, d_v), dtype=torch.float32, device=q.device)
+    st = load().lin_attn_decode_step_gated(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_gate),
+                                           _ptr(prf_w), _ptr(S), _ptr(Z), _ptr(o), _stream(stream))
+    if st != LA_OK:
+        raise LinAttnError(st, "lin_attn_decode_step_gated")
     return o
 
 

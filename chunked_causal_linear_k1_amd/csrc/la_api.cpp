@@ -47,7 +47,7 @@ int fill_log2g(const float* gamma, int H, float* out) {
   return any;
 }
 
-la_status validate_prefill_desc(const la_prefill_desc* d) {
+la_status validate_prefill_desc(const la_prefill_desc* d, bool gated = false) {
   if (!d) return LA_ERR_NULL;
   if (d->B < 1 || d->H < 1 || d->T < 1 || d->d_k < 1 || d->d_v < 1 || d->n_psi < 1 || d->chunk < 1)
     return LA_ERR_SHAPE;
@@ -68,6 +68,8 @@ la_status validate_prefill_desc(const la_prefill_desc* d) {
   if (d->layout == LA_LAYOUT_BTHD && (double)d->chunk * d->H * std::max(d->d_k, d->d_v) * 4 >= 2147483648.0)
     return LA_ERR_UNSUPPORTED;
   if (d->out_dtype == LA_BF16 && d->in_dtype != LA_BF16) return LA_ERR_UNSUPPORTED;
+  if (gated) return la::prefill_gated_supported(d->chunk, d->d_k, d->d_v, d->n_psi, d->psi) ? LA_OK
+                                                                                           : LA_ERR_UNSUPPORTED;
   const bool ok = d->in_dtype == LA_BF16
                       ? la::prefill_bf16_supported(d->chunk, d->d_k, d->d_v, d->n_psi, d->psi)
                       : la::prefill_f32_supported(d->chunk, d->d_k, d->d_v, d->n_psi, d->psi);
@@ -84,7 +86,7 @@ struct Plan {
 // knows (T is the longest); segments then have a fixed token count sized from the batch's
 // total, so the non-empty workgroups number about kTargetWorkgroups and carry similar work
 // whatever the length mix (segments past a shorter sequence's end are empty and exit at once).
-Plan make_plan(const la_prefill_desc* d, long long total_tokens = -1) {
+Plan make_plan(const la_prefill_desc* d, long long total_tokens = -1, bool gated = false) {
   Plan pl;
   const long long BH = (long long)d->B * d->H;
   pl.n_chunks = (int)((d->T + (long long)d->chunk - 1) / d->chunk);
@@ -104,7 +106,8 @@ Plan make_plan(const la_prefill_desc* d, long long total_tokens = -1) {
     pl.seg_chunks = (pl.n_chunks + 65534) / 65535;
     pl.n_seg = (pl.n_chunks + pl.seg_chunks - 1) / pl.seg_chunks;
   }
-  const size_t E = (size_t)d->n_psi * d->d_v + d->n_psi;
+  // one record per segment: S, Z (and, gated, the segment's per-row decay)
+  const size_t E = (size_t)d->n_psi * d->d_v + (gated ? 2 : 1) * (size_t)d->n_psi;
   pl.ws_bytes = (size_t)BH * pl.n_seg * E * sizeof(float);
   return pl;
 }
@@ -137,6 +140,14 @@ la_status lin_attn_prefill_workspace_size(const la_prefill_desc* d, size_t* byte
   return LA_OK;
 }
 
+la_status lin_attn_prefill_gated_workspace_size(const la_prefill_desc* d, size_t* bytes) {
+  if (!bytes) return LA_ERR_NULL;
+  const la_status st = validate_prefill_desc(d, true);
+  if (st != LA_OK) return st;
+  *bytes = make_plan(d, -1, true).ws_bytes;
+  return LA_OK;
+}
+
 la_status lin_attn_prefill_varlen_workspace_size(const la_prefill_desc* d, int32_t total_tokens, size_t* bytes) {
   if (!bytes) return LA_ERR_NULL;
   const la_status st = validate_prefill_desc(d);
@@ -155,8 +166,10 @@ namespace {
 la_status prefill_impl(const la_prefill_desc* d, const int32_t* cu_seqlens, int32_t total_tokens, const void* q,
                        const void* k, const void* v, const float* gamma, const void* prf_w, const float* init_S,
                        const float* init_Z, void* o, float* final_S, float* final_Z, void* workspace,
-                       size_t workspace_bytes, hipStream_t stream, hipEvent_t* events) {
-  la_status st = validate_prefill_desc(d);
+                       size_t workspace_bytes, hipStream_t stream, hipEvent_t* events,
+                       const float* log_gate = nullptr) {
+  const bool gated = log_gate != nullptr;
+  la_status st = validate_prefill_desc(d, gated);
   if (st != LA_OK) return st;
   if (cu_seqlens) {
     if (d->layout != LA_LAYOUT_BTHD) return LA_ERR_VALUE;
@@ -171,7 +184,8 @@ la_status prefill_impl(const la_prefill_desc* d, const int32_t* cu_seqlens, int3
     return LA_ERR_ALIGN;
   st = check_gamma(gamma, d->H);
   if (st != LA_OK) return st;
-  const Plan pl = cu_seqlens ? make_plan(d, total_tokens) : make_plan(d);
+  if (gated && !aligned16(log_gate)) return LA_ERR_ALIGN;
+  const Plan pl = make_plan(d, cu_seqlens ? (long long)total_tokens : -1LL, gated);
   if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes)) return LA_ERR_WORKSPACE;
 
   PrefillParams p;
@@ -179,6 +193,8 @@ la_status prefill_impl(const la_prefill_desc* d, const int32_t* cu_seqlens, int3
   p.q = q; p.k = k; p.v = v; p.prf_w = prf_w; p.o = o;
   p.ws = (float*)workspace;
   p.cu_seqlens = cu_seqlens;
+  p.log_gate = log_gate;
+  p.in_f32 = d->in_dtype == LA_F32;
   p.total = cu_seqlens ? total_tokens : 0;
   p.B = d->B; p.H = d->H; p.T = d->T;
   if (d->layout == LA_LAYOUT_BTHD) {
@@ -200,6 +216,7 @@ la_status prefill_impl(const la_prefill_desc* d, const int32_t* cu_seqlens, int3
   sp.init_Z = d->normalize ? init_Z : nullptr;
   sp.final_Z = d->normalize ? final_Z : nullptr;
   sp.cu_seqlens = cu_seqlens; sp.total = p.total;
+  sp.gated = gated;
   sp.BH = d->B * d->H; sp.H = d->H; sp.T = d->T;
   sp.n_psi = d->n_psi; sp.d_v = d->d_v;
   sp.n_seg = pl.n_seg; sp.seg_len = pl.seg_chunks * d->chunk;
@@ -211,11 +228,15 @@ la_status prefill_impl(const la_prefill_desc* d, const int32_t* cu_seqlens, int3
   };
   const bool bf = d->in_dtype == LA_BF16;
   hipError_t e = mark(0);
-  if (e == hipSuccess) e = bf ? la::launch_prefill_bf16_summary(p, stream) : la::launch_prefill_f32_summary(p, stream);
+  if (e == hipSuccess)
+    e = gated ? la::launch_prefill_gated(p, stream, false)
+              : bf ? la::launch_prefill_bf16_summary(p, stream) : la::launch_prefill_f32_summary(p, stream);
   if (e == hipSuccess) e = mark(1);
   if (e == hipSuccess) e = la::launch_segment_scan(sp, stream);
   if (e == hipSuccess) e = mark(2);
-  if (e == hipSuccess) e = bf ? la::launch_prefill_bf16_output(p, stream) : la::launch_prefill_f32_output(p, stream);
+  if (e == hipSuccess)
+    e = gated ? la::launch_prefill_gated(p, stream, true)
+              : bf ? la::launch_prefill_bf16_output(p, stream) : la::launch_prefill_f32_output(p, stream);
   if (e == hipSuccess) e = mark(3);
   return e == hipSuccess ? LA_OK : LA_ERR_HIP;
 }
@@ -250,9 +271,12 @@ la_status lin_attn_prefill(const la_prefill_desc* d, const void* q, const void* 
                                    workspace_bytes, stream, nullptr);
 }
 
-la_status lin_attn_decode_step(const la_decode_desc* d, const void* q, const void* k, const void* v,
-                               const float* gamma, const void* prf_w, float* S, float* Z, void* o,
-                               hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+la_status decode_impl(const la_decode_desc* d, const void* q, const void* k, const void* v, const float* gamma,
+                      const float* log_gate, const void* prf_w, float* S, float* Z, void* o, hipStream_t stream) {
   if (!d) return LA_ERR_NULL;
   if (d->N < 1 || d->H < 1 || d->d_k < 1 || d->d_v < 1 || d->n_psi < 1) return LA_ERR_SHAPE;
   if (d->psi < LA_PSI_IDENTITY || d->psi > LA_PSI_PRF_QSHIFT) return LA_ERR_VALUE;
@@ -268,7 +292,7 @@ la_status lin_attn_decode_step(const la_decode_desc* d, const void* q, const voi
   if (d->normalize && !Z) return LA_ERR_NULL;
   if (la::is_prf(d->psi) && !prf_w) return LA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(S) || !aligned16(Z) || !aligned16(o) ||
-      !aligned16(prf_w))
+      !aligned16(prf_w) || !aligned16(log_gate))
     return LA_ERR_ALIGN;
   la_status st = check_gamma(gamma, d->H);
   if (st != LA_OK) return st;
@@ -279,6 +303,7 @@ la_status lin_attn_decode_step(const la_decode_desc* d, const void* q, const voi
   p.N = d->N; p.H = d->H; p.d_k = d->d_k; p.d_v = d->d_v; p.n_psi = d->n_psi;
   p.psi = d->psi; p.normalize = d->normalize; p.eps = d->eps;
   p.in_f32 = d->in_dtype == LA_F32;
+  p.log_gate = log_gate;
   if (gamma) {
     for (int h = 0; h < d->H; ++h) {
       p.gamma[h] = gamma[h];
@@ -286,6 +311,32 @@ la_status lin_attn_decode_step(const la_decode_desc* d, const void* q, const voi
     }
   }
   return la::launch_decode_step(p, stream) == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+la_status lin_attn_decode_step(const la_decode_desc* d, const void* q, const void* k, const void* v,
+                               const float* gamma, const void* prf_w, float* S, float* Z, void* o,
+                               hipStream_t stream) {
+  return decode_impl(d, q, k, v, gamma, nullptr, prf_w, S, Z, o, stream);
+}
+
+la_status lin_attn_decode_step_gated(const la_decode_desc* d, const void* q, const void* k, const void* v,
+                                     const float* log_gate, const void* prf_w, float* S, float* Z, void* o,
+                                     hipStream_t stream) {
+  if (!log_gate) return LA_ERR_NULL;
+  return decode_impl(d, q, k, v, nullptr, log_gate, prf_w, S, Z, o, stream);
+}
+
+la_status lin_attn_prefill_gated(const la_prefill_desc* d, const void* q, const void* k, const void* v,
+                                 const float* log_gate, const float* init_S, const float* init_Z, void* o,
+                                 float* final_S, float* final_Z, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream) {
+  if (!log_gate) return LA_ERR_NULL;
+  return prefill_impl(d, nullptr, 0, q, k, v, nullptr, nullptr, init_S, init_Z, o, final_S, final_Z, workspace,
+                      workspace_bytes, stream, nullptr, log_gate);
 }
 
 }  // extern "C"

@@ -5,7 +5,9 @@
 // step is a rank-1 update plus a vector-matrix product, independent of how many
 // tokens came before:
 //   S <- gamma S + psi(k) v^T,  Z <- gamma Z + psi(k),  o = psi(q)^T S / (psi(q).Z + eps)
-// (update first, then read: the new token attends to itself).
+// (update first, then read: the new token attends to itself). With per-row forget gates
+// ("Linear Attention and Retentive Networks", Data-Dependent Gating Mechanism) gamma is
+// replaced, row by row, by alpha[p] = exp(log_gate[p]).
 //
 // The step is a pure stream over the fp32 state (n_psi*d_v*4 bytes read and written
 // per head). One workgroup per (stream, head): psi(k), psi(q) go to LDS, then every
@@ -87,7 +89,8 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeParams p) {
     float part = 0.f;
     for (int f = tid; f < n_psi; f += kDecThreads) {
       float* zp = p.Z + (size_t)b * n_psi + f;
-      const float z = gam * *zp + sf[f];
+      const float gz = p.log_gate ? expf(p.log_gate[(size_t)b * n_psi + f]) : gam;
+      const float z = gz * *zp + sf[f];
       *zp = z;
       part += sg[f] * z;
     }
@@ -110,7 +113,8 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeParams p) {
     f32x4* sp = (f32x4*)(Sb + (size_t)row * d_v + 4 * cg);
     f32x4 s = *sp;
     const float fk = sf[row], gq = sg[row];
-    s = gam * s + fk * v4;
+    const float gr = p.log_gate ? expf(p.log_gate[(size_t)b * n_psi + row]) : gam;  // this row's forget gate
+    s = gr * s + fk * v4;
     *sp = s;
     acc += gq * s;
   }

@@ -32,6 +32,7 @@ struct PrefillParams {
   void* o;
   float* ws;             // [BH, n_seg, E] with E = n_psi*d_v + n_psi (segment summaries)
   const int* cu_seqlens; // [B + 1] first token of each packed sequence, or null
+  const float* log_gate; // per-token, per-feature log forget gates (gated prefill), rows like k; or null
   int B, H, T;
   int total;             // tokens in the packed tensors (cu_seqlens only)
   int tok_rows;
@@ -40,6 +41,7 @@ struct PrefillParams {
   int psi;               // la_psi
   int normalize;
   int out_bf16;          // o is bf16 (round to nearest even of the fp32 result)
+  int in_f32;            // q, k, v are fp32 (gated path; the other paths dispatch on dtype)
   float eps;
   int n_chunks, seg_chunks, n_seg;
   int has_decay;
@@ -57,6 +59,7 @@ struct ScanParams {
   int BH, H, T;
   int n_psi, d_v;
   int n_seg, seg_len;    // segment length in tokens (the last one may be short)
+  int gated;             // 1: per-row decays stored after each segment's S and Z (gated prefill)
   int has_decay;
   float log2g[LA_MAX_DECAY_HEADS];
 };
@@ -77,6 +80,7 @@ struct DecodeParams {
   int in_f32;            // 1: q, k, v, prf_w are fp32; 0: bf16
   int has_decay;
   float gamma[LA_MAX_DECAY_HEADS];
+  const float* log_gate; // [N, H, n_psi] per-row log forget gates (gated step), or null
 };
 
 // Positive random features, with or without the query-row shift.
@@ -120,6 +124,9 @@ hipError_t launch_prefill_f32_summary(const PrefillParams& p, hipStream_t s);
 hipError_t launch_prefill_f32_output(const PrefillParams& p, hipStream_t s);
 
 hipError_t launch_segment_scan(const ScanParams& p, hipStream_t s);
+
+bool prefill_gated_supported(int C, int d_k, int d_v, int n_psi, int psi);
+hipError_t launch_prefill_gated(const PrefillParams& p, hipStream_t s, bool out);
 
 bool decode_supported(int d_k, int d_v, int n_psi, int psi);
 hipError_t launch_decode_step(const DecodeParams& p, hipStream_t s);

@@ -33,16 +33,23 @@ __device__ __forceinline__ void st4(float* p, const f32x4& v) { *(f32x4*)p = v; 
 template <int RUN>
 __global__ __launch_bounds__(64 * kMaxWaves) void k_segment_scan(ScanParams p) {
   __shared__ f32x4 sx[kMaxWaves][64];
-  __shared__ float sa[kMaxWaves];
+  __shared__ f32x4 sa[kMaxWaves][64];  // decays per element: rows differ under per-row gates
   const int W = blockDim.x >> 6;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int bh = blockIdx.y, head = bh % p.H;
   const size_t SE = (size_t)p.n_psi * p.d_v;
-  const size_t E = SE + p.n_psi;  // a multiple of 4 (n_psi and d_v are multiples of 4)
+  const size_t E = SE + p.n_psi;  // scanned elements; a multiple of 4 (n_psi and d_v are)
+  // segment record: S, Z, then (gated) the segment's per-row decay vector
+  const size_t REC = E + (p.gated ? p.n_psi : 0);
   const size_t e = ((size_t)blockIdx.x * 64 + lane) * 4;
   const bool live = e < E;
   const float lg = p.has_decay ? p.log2g[head] : 0.f;
-  float* base = p.ws + (size_t)bh * p.n_seg * E + e;
+  float* base = p.ws + (size_t)bh * p.n_seg * REC + e;
+  // the state rows of this lane's 4 elements: one row (S part, d_v a multiple of 4) or four
+  // consecutive rows (Z part); their decays under per-row gates
+  const bool zpart = e >= SE;
+  const size_t row = zpart ? e - SE : e / p.d_v;
+  const float* gvec = p.ws + (size_t)bh * p.n_seg * REC + E + (live ? row : 0);
   int T = p.T;  // this sequence's length
   if (p.cu_seqlens) {
     int start;
@@ -52,36 +59,43 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_segment_scan(ScanParams p) {
   // this wave's run of segments
   const int per = (p.n_seg + W - 1) / W;
   const int s0 = min(w * per, p.n_seg), s1 = min(s0 + per, p.n_seg);
-  auto seg_decay = [&](int s) {
+  auto seg_decay = [&](int s) -> f32x4 {
+    if (p.gated) {  // products of the segment's gates for these rows
+      if (!live) return f32x4{1.f, 1.f, 1.f, 1.f};
+      if (zpart) return ld4(gvec + (size_t)s * REC);
+      const float a = gvec[(size_t)s * REC];
+      return f32x4{a, a, a, a};
+    }
     const int len = max(0, min(p.seg_len, T - s * p.seg_len));  // 0 past a shorter sequence's end
-    return gpow(lg, (float)len);
+    const float a = gpow(lg, (float)len);
+    return f32x4{a, a, a, a};
   };
 
   // 1. fold the run: total = X_s0 (+) ... (+) X_{s1-1}
   f32x4 run[RUN > 0 ? RUN : 1];
   f32x4 tx = {0.f, 0.f, 0.f, 0.f};
-  float ta = 1.f;
+  f32x4 ta = {1.f, 1.f, 1.f, 1.f};
   if (RUN > 0) {
 #pragma unroll
     for (int i = 0; i < (RUN > 0 ? RUN : 1); ++i)
-      run[i] = (live && s0 + i < s1) ? ld4(base + (size_t)(s0 + i) * E) : f32x4{0.f, 0.f, 0.f, 0.f};
+      run[i] = (live && s0 + i < s1) ? ld4(base + (size_t)(s0 + i) * REC) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < (RUN > 0 ? RUN : 1); ++i) {
       if (s0 + i < s1) {
-        const float as = seg_decay(s0 + i);
+        const f32x4 as = seg_decay(s0 + i);
         tx = as * tx + run[i];
         ta *= as;
       }
     }
   } else {
     for (int s = s0; s < s1; ++s) {
-      const float as = seg_decay(s);
-      if (live) tx = as * tx + ld4(base + (size_t)s * E);
+      const f32x4 as = seg_decay(s);
+      if (live) tx = as * tx + ld4(base + (size_t)s * REC);
       ta *= as;
     }
   }
   sx[w][lane] = tx;
-  if (lane == 0) sa[w] = ta;
+  sa[w][lane] = ta;
   __syncthreads();
 
   // 2. Blelloch over the W wave totals (W is a power of two)
@@ -89,52 +103,50 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_segment_scan(ScanParams p) {
     const int right = (w + 1) * 2 * d - 1;
     const bool act = right < W;
     f32x4 nx = {0.f, 0.f, 0.f, 0.f};
-    float na = 1.f;
+    f32x4 na = {1.f, 1.f, 1.f, 1.f};
     if (act) {
       const int left = right - d;
-      nx = sa[right] * sx[left][lane] + sx[right][lane];
-      na = sa[left] * sa[right];
+      nx = sa[right][lane] * sx[left][lane] + sx[right][lane];
+      na = sa[left][lane] * sa[right][lane];
     }
     __syncthreads();
     if (act) {
       sx[right][lane] = nx;
-      if (lane == 0) sa[right] = na;
+      sa[right][lane] = na;
     }
     __syncthreads();
   }
   if (w == W - 1) {
     sx[W - 1][lane] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (lane == 0) sa[W - 1] = 1.f;
+    sa[W - 1][lane] = f32x4{1.f, 1.f, 1.f, 1.f};
   }
   __syncthreads();
   for (int d = W >> 1; d >= 1; d >>= 1) {  // down-sweep
     const int right = (w + 1) * 2 * d - 1;
     f32x4 lx = {0.f, 0.f, 0.f, 0.f}, px = {0.f, 0.f, 0.f, 0.f};
-    float la_ = 1.f, pa = 1.f;
+    f32x4 la_ = {1.f, 1.f, 1.f, 1.f}, pa = {1.f, 1.f, 1.f, 1.f};
     const bool act = right < W;
     if (act) {
       const int left = right - d;
       lx = sx[left][lane];
-      la_ = sa[left];
+      la_ = sa[left][lane];
       px = sx[right][lane];
-      pa = sa[right];
+      pa = sa[right][lane];
     }
     __syncthreads();
     if (act) {
       const int left = right - d;
       sx[left][lane] = px;              // left child gets the parent's prefix
       sx[right][lane] = la_ * px + lx;  // right child: prefix (+) left sum
-      if (lane == 0) {
-        sa[left] = pa;
-        sa[right] = pa * la_;
-      }
+      sa[left][lane] = pa;
+      sa[right][lane] = pa * la_;
     }
     __syncthreads();
   }
 
   // 3. carry into this run: init (+) prefix_w
   f32x4 cx = sx[w][lane];
-  const float ca = sa[w];
+  const f32x4 ca = sa[w][lane];
   if (live) {
     f32x4 init = {0.f, 0.f, 0.f, 0.f};
     if (e < SE) {
@@ -149,17 +161,17 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_segment_scan(ScanParams p) {
 #pragma unroll
     for (int i = 0; i < (RUN > 0 ? RUN : 1); ++i) {
       if (s0 + i < s1) {
-        const float as = seg_decay(s0 + i);
-        if (live) st4(base + (size_t)(s0 + i) * E, cx);
+        const f32x4 as = seg_decay(s0 + i);
+        if (live) st4(base + (size_t)(s0 + i) * REC, cx);
         cx = as * cx + run[i];
       }
     }
   } else {
     for (int s = s0; s < s1; ++s) {
-      const float as = seg_decay(s);
+      const f32x4 as = seg_decay(s);
       if (live) {
-        const f32x4 xs = ld4(base + (size_t)s * E);
-        st4(base + (size_t)s * E, cx);
+        const f32x4 xs = ld4(base + (size_t)s * REC);
+        st4(base + (size_t)s * REC, cx);
         cx = as * cx + xs;
       }
     }

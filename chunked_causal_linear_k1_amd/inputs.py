@@ -69,6 +69,15 @@ def make_prefill_inputs(w: Workload, device: str = "cpu", seed: Optional[int] = 
     return {"q": q, "k": k, "v": v, "prf_w": prf_w, "gamma": gammas(w)}
 
 
+def make_log_gates(shape, seed: int, temp: float = 16.0, device: str = "cpu") -> torch.Tensor:
+    """fp32 log forget gates logsigmoid(z) / temp with z ~ N(0, 1): the gate form of gated linear
+    attention (a sigmoid of a projection, sharpened by a temperature), all in (-inf, 0)."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    z = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+    return torch.nn.functional.logsigmoid(z) / temp
+
+
 def varlen_lengths(w) -> List[int]:
     """The sequence lengths of a VarlenWorkload: uniform in [len_min, len_max], seeded."""
     rng = np.random.default_rng(w.seed)

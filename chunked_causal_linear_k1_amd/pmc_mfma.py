@@ -33,7 +33,8 @@ KERNELS = {
     "k_summary<64, 128, true, false, false>": "k_summary_retnet_128k",
     "k_output_w8<64, 128, false, true, true, false>": "k_output_elu1_8k",
     "k_summary<64, 128, false, true, true>": "k_summary_elu1_8k",
-    "k_output_prf<64, 128, 256, false, true, false>": "k_output_prf256_4k",
+    "k_output_prf<64, 128, 256, false, true, false, false>": "k_output_prf256_4k",
+    "k_output_prf<64, 128, 256, false, true, false, true>": "k_output_prf256_4k_qshift",
     "k_summary_prf<64, 128, 256, false, true>": "k_summary_prf256_4k",
 }
 

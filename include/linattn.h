@@ -197,6 +197,33 @@ la_status lin_attn_prefill_profiled(const la_prefill_desc* d, const void* q, con
                                     size_t workspace_bytes, hipStream_t stream,
                                     hipEvent_t* events);
 
+/*
+ * Chunkwise causal linear attention with data-dependent forget gates ("Linear Attention
+ * and Retentive Networks", Data-Dependent Gating Mechanism: S_t = G_t . S_{t-1} + k_t^T v_t
+ * with G_t = alpha_t 1^T, one gate per state row and token):
+ *   S_t[p][:] = alpha_t[p] S_{t-1}[p][:] + psi(k_t)[p] v_t^T,   alpha_t = exp(log_gate_t)
+ *   Z_t[p]    = alpha_t[p] Z_{t-1}[p]    + psi(k_t)[p]
+ *   o_t       = psi(q_t)^T S_t / (psi(q_t) . Z_t + eps)   (numerator alone if !normalize)
+ * The gates replace gamma. Chunks combine under (a1, X1) (+) (a2, X2) = (a1 a2,
+ * diag(a2) X1 + X2) with a the per-row product of a chunk's gates.
+ *
+ *   d         as for lin_attn_prefill; supported: psi identity or elu1, d_k == d_v ==
+ *             n_psi in {64, 128}, chunk 16, in_dtype LA_BF16 or LA_F32, either layout
+ *   log_gate  device fp32, laid out like k ([B, H, T, d_k] or [B, T, H, d_k]): the log of
+ *             each token's gate per state row, <= 0 (gates in (0, 1]). Values must be
+ *             finite; an exact reset between documents is a sequence boundary (separate
+ *             batch entries), not a gate.
+ *   workspace at least lin_attn_prefill_gated_workspace_size bytes
+ *   other arguments as for lin_attn_prefill (no gamma, no PRF bank).
+ * This path computes in fp32 on the vector ALUs (the gate factors make every operand
+ * inexact in bf16).
+ */
+la_status lin_attn_prefill_gated_workspace_size(const la_prefill_desc* d, size_t* bytes);
+la_status lin_attn_prefill_gated(const la_prefill_desc* d, const void* q, const void* k, const void* v,
+                                 const float* log_gate, const float* init_S, const float* init_Z, void* o,
+                                 float* final_S, float* final_Z, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
+
 /* Batched single-token decode description: N independent streams x H heads. */
 typedef struct {
   int32_t N, H;
@@ -229,6 +256,16 @@ typedef struct {
 la_status lin_attn_decode_step(const la_decode_desc* d, const void* q, const void* k, const void* v,
                                const float* gamma, const void* prf_w, float* S, float* Z, void* o,
                                hipStream_t stream);
+
+/*
+ * lin_attn_decode_step with per-row forget gates in place of gamma (same page, Data-
+ * Dependent Gating Mechanism): S[p][:] <- alpha[p] S[p][:] + psi(k)[p] v^T, Z[p] <- alpha[p]
+ * Z[p] + psi(k)[p], alpha = exp(log_gate), then o as above. log_gate: device fp32
+ * [N, H, n_psi], <= 0, finite. Other arguments as for lin_attn_decode_step (no gamma).
+ */
+la_status lin_attn_decode_step_gated(const la_decode_desc* d, const void* q, const void* k, const void* v,
+                                     const float* log_gate, const void* prf_w, float* S, float* Z, void* o,
+                                     hipStream_t stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char* lin_attn_status_string(la_status s);

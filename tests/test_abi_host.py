@@ -184,6 +184,35 @@ def test_varlen_planner():
     assert ws(0, B=3, H=2, T=1, chunk=64) == 3 * 2 * 1 * E * 4
 
 
+def test_gated_validation_and_workspace():
+    lib = binding.load()
+
+    def ws(**kw):
+        n = ctypes.c_size_t(0)
+        st = lib.lin_attn_prefill_gated_workspace_size(ctypes.byref(_desc(**kw)), ctypes.byref(n))
+        return st, n.value
+    base = dict(chunk=16, psi=0, normalize=0)
+    st, n = ws(**base)
+    assert st == LA_OK
+    # one record per segment: S, Z and the segment's per-row decay
+    E = 128 * 128 + 2 * 128
+    assert n % (4 * E) == 0
+    for kw in (dict(chunk=64), dict(psi=2, n_psi=256), dict(d_v=64), dict(d_k=96, d_v=96, n_psi=96)):
+        assert ws(**{**base, **kw})[0] == LA_ERR_UNSUPPORTED, kw
+    assert ws(**{**base, "psi": 1, "normalize": 1, "d_k": 64, "d_v": 64, "n_psi": 64})[0] == LA_OK
+    assert ws(**{**base, "in_dtype": LA_F32, "layout": 1})[0] == LA_OK
+    d = _desc(**base)
+    fake, odd = ctypes.c_void_p(1 << 20), ctypes.c_void_p((1 << 20) + 4)
+    call = lambda g, w=fake: lib.lin_attn_prefill_gated(ctypes.byref(d), fake, fake, fake, g, None, None, fake, None,
+                                                        None, w, n, None)
+    assert call(None) == LA_ERR_NULL
+    assert call(odd) == LA_ERR_ALIGN
+    assert call(fake, None) == LA_ERR_WORKSPACE
+    dd = DecodeDesc(2, 2, 64, 64, 64, 1, 1, 1e-6, LA_BF16, LA_F32)
+    assert lib.lin_attn_decode_step_gated(ctypes.byref(dd), fake, fake, fake, None, None, fake, fake, fake,
+                                          None) == LA_ERR_NULL
+
+
 def test_decode_validation():
     lib = binding.load()
     fake = ctypes.c_void_p(1 << 20)

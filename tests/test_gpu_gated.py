@@ -1,0 +1,173 @@
+"""GPU parity of the gated path (lin_attn_prefill_gated, lin_attn_decode_step_gated) against
+the fp64 oracle's gated recurrence, through the C ABI: small cases spanning several chunks
+and segments with ragged tails, both layouts, fp32 and bf16 inputs, strong and mild gates,
+initial and final states, decode steps, the prefill -> decode hand-off, and the full-size
+gated workload on sampled (batch, head) sequences."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from chunked_causal_linear_k1_amd import binding, inputs, workloads
+from chunked_causal_linear_k1_amd.workloads import PSI_ELU1, PSI_IDENTITY, PSI_PRF, Workload
+
+from gpu_common import announce, assert_close
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _inputs(w: Workload, temp: float, layout: str = "bhtd"):
+    inp = inputs.make_prefill_inputs(w, device="cpu")
+    lg = inputs.make_log_gates((w.B, w.H, w.T, w.d_k), w.seed + 2, temp)
+    return inp["q"], inp["k"], inp["v"], lg
+
+
+def _oracle(w: Workload, q, k, v, lg, S0=None, Z0=None, want_state=False):
+    BH = w.B * w.H
+    return oracle.prefill(q.reshape(BH, w.T, -1), k.reshape(BH, w.T, -1), v.reshape(BH, w.T, -1), w.psi,
+                          normalize=w.normalize, eps=float(np.float32(w.eps)), log_gate=lg.reshape(BH, w.T, -1),
+                          S0=S0, Z0=Z0, want_state=want_state)
+
+
+def _bthd(x):
+    return x.transpose(1, 2).contiguous()
+
+
+CASES = [
+    # name, B, H, T, d, psi, normalize, dtype, gate temperature, layout
+    ("identity_d128_mild", 2, 2, 301, 128, PSI_IDENTITY, 0, "bf16", 16.0, "bhtd"),
+    ("identity_d128_strong_bthd", 1, 3, 250, 128, PSI_IDENTITY, 0, "bf16", 1.0, "bthd"),
+    ("elu1_norm_d64", 2, 2, 333, 64, PSI_ELU1, 1, "bf16", 4.0, "bhtd"),
+    ("elu1_norm_d128_bthd", 1, 2, 200, 128, PSI_ELU1, 1, "bf16", 16.0, "bthd"),
+    ("f32_identity_d64_strong", 1, 2, 190, 64, PSI_IDENTITY, 0, "f32", 1.0, "bhtd"),
+    ("f32_elu1_norm_d128", 1, 2, 130, 128, PSI_ELU1, 1, "f32", 8.0, "bthd"),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_gated_small(case):
+    name, B, H, T, d, psi, normalize, dt, temp, layout = case
+    scale = d ** -0.5 if psi == PSI_IDENTITY else 0.5
+    w = Workload(name=name, B=B, H=H, T=T, d_k=d, d_v=d, n_psi=d, chunk=16, psi=psi, normalize=normalize, eps=1e-6,
+                 dtype=dt, seed=71, qk_scale=scale, v_scale=1.0)
+    announce(f"gated prefill {name}")
+    q, k, v, lg = _inputs(w, temp)
+    args = (q, k, v, lg) if layout == "bhtd" else tuple(_bthd(x) for x in (q, k, v, lg))
+    o = binding.lin_attn_prefill_gated(*(x.to(DEV) for x in args), psi=psi, normalize=normalize, eps=w.eps,
+                                       layout=layout)
+    torch.cuda.synchronize()
+    if layout == "bthd":
+        o = o.transpose(1, 2)
+    ref = _oracle(w, q, k, v, lg)
+    assert_close(o.cpu().reshape(B * H, T, d).numpy(), ref, dt, name)
+
+
+@pytest.mark.parametrize("T", [1, 15, 16, 17, 47])
+def test_gated_edge_lengths(T):
+    w = Workload(name=f"gated_T{T}", B=1, H=2, T=T, d_k=64, d_v=64, n_psi=64, chunk=16, psi=PSI_ELU1, normalize=1,
+                 eps=1e-6, dtype="bf16", seed=73 + T, qk_scale=0.5, v_scale=1.0)
+    announce(f"gated prefill edge T={T}")
+    q, k, v, lg = _inputs(w, 4.0)
+    o = binding.lin_attn_prefill_gated(q.to(DEV), k.to(DEV), v.to(DEV), lg.to(DEV), psi=w.psi, normalize=1, eps=w.eps)
+    torch.cuda.synchronize()
+    assert_close(o.cpu().reshape(2, T, 64).numpy(), _oracle(w, q, k, v, lg), "bf16", w.name)
+
+
+def test_gated_initial_and_final_state():
+    """Prefill from an initial state (the state of a gated prefix) and the final state after
+    the last token, against the oracle continuing from the same state."""
+    B, H, T, d = 2, 2, 277, 128
+    w = Workload(name="gated_state", B=B, H=H, T=T, d_k=d, d_v=d, n_psi=d, chunk=16, psi=PSI_ELU1, normalize=1,
+                 eps=1e-6, dtype="bf16", seed=79, qk_scale=0.5, v_scale=1.0)
+    announce("gated prefill init/final state")
+    q, k, v, lg = _inputs(w, 8.0)
+    # initial state: the oracle's state after a seeded 64-token gated prefix
+    wp = Workload(name="prefix", B=B, H=H, T=64, d_k=d, d_v=d, n_psi=d, chunk=16, psi=PSI_ELU1, normalize=1,
+                  eps=1e-6, dtype="bf16", seed=80, qk_scale=0.5, v_scale=1.0)
+    _, kp, vp, lgp = _inputs(wp, 8.0)
+    _, S0, Z0 = oracle.prefill(None, kp.reshape(B * H, 64, d), vp.reshape(B * H, 64, d), PSI_ELU1,
+                               log_gate=lgp.reshape(B * H, 64, d), want_state=True)
+    S0f, Z0f = S0.astype(np.float32), Z0.astype(np.float32)
+    fS = torch.empty((B, H, d, d), dtype=torch.float32, device=DEV)
+    fZ = torch.empty((B, H, d), dtype=torch.float32, device=DEV)
+    o = binding.lin_attn_prefill_gated(q.to(DEV), k.to(DEV), v.to(DEV), lg.to(DEV), psi=PSI_ELU1, normalize=1,
+                                       eps=w.eps, init_S=torch.from_numpy(S0f).reshape(B, H, d, d).to(DEV),
+                                       init_Z=torch.from_numpy(Z0f).reshape(B, H, d).to(DEV), final_S=fS, final_Z=fZ)
+    torch.cuda.synchronize()
+    ref, rS, rZ = _oracle(w, q, k, v, lg, S0=S0f.astype(np.float64), Z0=Z0f.astype(np.float64), want_state=True)
+    assert_close(o.cpu().reshape(B * H, T, d).numpy(), ref, "bf16", "gated o with init state")
+    assert_close(fS.cpu().reshape(B * H, d, d).numpy(), rS, "bf16", "gated final S")
+    assert_close(fZ.cpu().reshape(B * H, d).numpy(), rZ, "bf16", "gated final Z")
+
+
+@pytest.mark.parametrize("psi,d,normalize", [(PSI_IDENTITY, 128, 0), (PSI_ELU1, 64, 1), (PSI_PRF, 128, 1)])
+def test_gated_decode(psi, d, normalize):
+    """Decode steps with per-row gates from a gated prefix state, every step against the oracle."""
+    N, H, P, steps = 2, 3, 40, 5
+    n_psi = 256 if psi == PSI_PRF else d
+    g = torch.Generator().manual_seed(83)
+    sc = 128 ** -0.25 if psi == PSI_PRF else (d ** -0.5 if psi == PSI_IDENTITY else 0.5)
+    prf = torch.randn((H, n_psi, d), generator=g).to(torch.bfloat16) if psi == PSI_PRF else None
+    kp = (torch.randn((N * H, P, d), generator=g) * sc).to(torch.bfloat16)
+    vp = torch.randn((N * H, P, d), generator=g).to(torch.bfloat16)
+    lgp = inputs.make_log_gates((N * H, P, n_psi), 84, 4.0)
+    heads = [b % H for b in range(N * H)]
+    _, S, Z = oracle.prefill(None, kp, vp, psi, n_psi=n_psi, prf_w=prf, w_head=heads, log_gate=lgp, want_state=True)
+    Sg = torch.from_numpy(S.astype(np.float32)).reshape(N, H, n_psi, d).to(DEV)
+    Zg = torch.from_numpy(Z.astype(np.float32)).reshape(N, H, n_psi).to(DEV)
+    So = Sg.cpu().double().numpy().reshape(N * H, n_psi, d).copy()
+    Zo = Zg.cpu().double().numpy().reshape(N * H, n_psi).copy()
+    announce(f"gated decode psi={psi} d={d}")
+    for t in range(steps):
+        q, k, v = ((torch.randn((N, H, d), generator=g) * (sc if x != "v" else 1.0)).to(torch.bfloat16)
+                   for x in ("q", "k", "v"))
+        lg = inputs.make_log_gates((N, H, n_psi), 90 + t, 4.0)
+        o = binding.lin_attn_decode_step_gated(q.to(DEV), k.to(DEV), v.to(DEV), lg.to(DEV), Sg,
+                                               Zg if normalize else None, psi=psi, normalize=normalize,
+                                               prf_w=None if prf is None else prf.to(DEV))
+        ref = oracle.decode_step(q.reshape(-1, d), k.reshape(-1, d), v.reshape(-1, d), So, Zo, psi, prf_w=prf,
+                                 w_head=heads if prf is not None else None, normalize=normalize,
+                                 eps=float(np.float32(1e-6)), log_gate=lg.reshape(-1, n_psi))
+        torch.cuda.synchronize()
+        assert_close(o.cpu().reshape(-1, d).numpy(), ref, "bf16", f"gated decode step {t}")
+    assert_close(Sg.cpu().reshape(-1, n_psi, d).numpy() / np.abs(So).max(), So / np.abs(So).max(), "bf16",
+                 "gated decode final S (scaled to max 1)")
+
+
+def test_gated_prefill_then_decode():
+    """The gated prefill's final state continues in gated decode: outputs match the oracle
+    over the whole sequence."""
+    B, H, T, d, n = 1, 2, 150, 64, 4
+    w = Workload(name="gated_handoff", B=B, H=H, T=T + n, d_k=d, d_v=d, n_psi=d, chunk=16, psi=PSI_ELU1,
+                 normalize=1, eps=1e-6, dtype="bf16", seed=85, qk_scale=0.5, v_scale=1.0)
+    announce("gated prefill -> decode")
+    q, k, v, lg = _inputs(w, 4.0)
+    S = torch.empty((B, H, d, d), dtype=torch.float32, device=DEV)
+    Z = torch.empty((B, H, d), dtype=torch.float32, device=DEV)
+    binding.lin_attn_prefill_gated(*(x[:, :, :T].contiguous().to(DEV) for x in (q, k, v, lg)), psi=PSI_ELU1,
+                                   normalize=1, eps=w.eps, final_S=S, final_Z=Z)
+    ref = _oracle(w, q, k, v, lg)  # [B*H, T+n, d]
+    for t in range(n):
+        o = binding.lin_attn_decode_step_gated(*(x[:, :, T + t].contiguous().to(DEV) for x in (q, k, v, lg)), S, Z,
+                                               psi=PSI_ELU1, normalize=1, eps=w.eps)
+        torch.cuda.synchronize()
+        assert_close(o.cpu().reshape(B * H, d).numpy(), ref[:, T + t], "bf16", f"hand-off step {t}")
+
+
+def test_full_gated_8k_sampled():
+    """The 4 x 16 x 8192 gated workload in the benchmark's launch configuration; sampled
+    (batch, head) sequences against the oracle."""
+    w = workloads.GATED_8K
+    announce("gated full size 8k")
+    inp = inputs.make_prefill_inputs(w, device=DEV)
+    lg = inputs.make_log_gates((w.B, w.H, w.T, w.d_k), w.seed + 2, w.extra["gate_temp"], device=DEV)
+    o = binding.lin_attn_prefill_gated(inp["q"], inp["k"], inp["v"], lg, psi=w.psi, normalize=w.normalize, eps=w.eps)
+    torch.cuda.synchronize()
+    for b, h in ((0, 0), (1, 7), (3, 15)):
+        ref = oracle.prefill(inp["q"][b, h:h + 1].cpu(), inp["k"][b, h:h + 1].cpu(), inp["v"][b, h:h + 1].cpu(),
+                             w.psi, normalize=w.normalize, log_gate=lg[b, h:h + 1].cpu())
+        assert_close(o[b, h:h + 1].cpu().numpy(), ref, "bf16", f"gated 8k (b={b}, h={h})")
