@@ -123,6 +123,33 @@ def bench_prefill(w: workloads.Workload, steps: int, warmup: int, layout: str = 
     return res
 
 
+def bench_gated(w: workloads.Workload, steps: int, warmup: int):
+    """Whole lin_attn_prefill_gated calls (fp32 vector-ALU path), event-timed on the current stream."""
+    log(f"prefill {w.name}: generating inputs and log gates on the GPU")
+    inp = inputs.make_prefill_inputs(w, device="cuda")
+    lg = inputs.make_log_gates((w.B, w.H, w.T, w.d_k), w.seed + 2, w.extra["gate_temp"], device="cuda")
+    o = torch.empty((w.B, w.H, w.T, w.d_v), dtype=torch.float32, device="cuda")
+    desc = binding.prefill_desc(w.B, w.H, w.T, w.d_k, w.d_v, w.n_psi, w.chunk, w.psi, w.normalize, w.eps,
+                                binding.LA_BF16)
+    ws = torch.empty(max(binding.gated_workspace_size(desc), 16), dtype=torch.uint8, device="cuda")
+    kw = dict(psi=w.psi, chunk=w.chunk, normalize=w.normalize, eps=w.eps, o=o, workspace=ws)
+    for _ in range(warmup):
+        binding.lin_attn_prefill_gated(inp["q"], inp["k"], inp["v"], lg, **kw)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        binding.lin_attn_prefill_gated(inp["q"], inp["k"], inp["v"], lg, **kw)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    res = {"ms_per_step": ms, "token_heads_per_s": w.token_heads / (ms * 1e-3), "units": w.token_heads}
+    del inp, lg, o, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_varlen(w: workloads.VarlenWorkload, steps: int, warmup: int):
     """Whole lin_attn_prefill_varlen calls on a packed batch, event-timed on the current stream."""
     log(f"prefill {w.name}: generating packed inputs on the GPU")
@@ -255,7 +282,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--no-extra", action="store_true", help="headline workload only (no 8k elu+1, PRF, layout, bf16-output and packed-batch lines)")
+    ap.add_argument("--no-extra", action="store_true", help="headline workload only (no 8k elu+1, PRF, layout, bf16-output, gated and packed-batch lines)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="first run one plain copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -302,8 +329,10 @@ def main():
                           "summary": mfma_from_profiles("k_summary_retnet_128k")},
     }
     if not args.no_extra:
+        prf_qs = workloads.PRF_4K.with_(name="prf256_4k_qshift", psi=workloads.PSI_PRF_QSHIFT)
         for key, wx, tag in (("prefill_8k", workloads.PREFILL_8K, "elu1_8k"),
-                             ("prefill_prf_4k", workloads.PRF_4K, "prf256_4k")):
+                             ("prefill_prf_4k", workloads.PRF_4K, "prf256_4k"),
+                             ("prefill_prf_4k_qshift", prf_qs, "prf256_4k_qshift")):
             px = bench_prefill(wx, args.steps, args.warmup)
             ax = BYTES_PER_TOKEN_HEAD * px["units"] / (px["ms_per_step"] * 1e-3) / 1e9
             line[key] = {"workload": wx.name, "token_heads_per_s": round(px["token_heads_per_s"], 1),
@@ -313,7 +342,7 @@ def main():
                                                  "unit": "GB/s", "frac": round(ax / HBM_PEAK_GBS, 4)},
                          "mfma_counters": {"output": mfma_from_profiles(f"k_output_{tag}"),
                                            "summary": mfma_from_profiles(f"k_summary_{tag}")}}
-            if wx.psi == workloads.PSI_PRF:
+            if wx.psi in (workloads.PSI_PRF, workloads.PSI_PRF_QSHIFT):
                 # 286,720 algorithmic FLOP per token-head (features 4*256*128, local pass C*(256+128),
                 # state and output 4*256*128); bf16 MFMA dense peak 2.5 PFLOP/s
                 tf = 286720 * px["units"] / (px["ms_per_step"] * 1e-3) / 1e12
@@ -335,6 +364,22 @@ def main():
                                       "bytes_per_token_head": bpt},
                          "whole_call_roofline": {"bound": "hbm", "achieved": round(ax, 1), "peak": HBM_PEAK_GBS,
                                                  "unit": "GB/s", "frac": round(ax / HBM_PEAK_GBS, 4)}}
+        gw = workloads.GATED_8K
+        pg = bench_gated(gw, args.steps, args.warmup)
+        # algorithmic work per token-head: scores C*n (causal half), A V C*d_v, state read and
+        # update 4*n*d_v; bytes: q, k, v bf16, the fp32 log gates, o fp32
+        flop = gw.chunk * gw.n_psi + gw.chunk * gw.d_v + 4 * gw.n_psi * gw.d_v
+        gbytes = 3 * 128 * 2 + 128 * 4 + 128 * 4
+        tf = flop * pg["units"] / (pg["ms_per_step"] * 1e-3) / 1e12
+        gb = gbytes * pg["units"] / (pg["ms_per_step"] * 1e-3) / 1e9
+        line["prefill_gated_8k"] = {"workload": gw.name, "token_heads_per_s": round(pg["token_heads_per_s"], 1),
+                                    "ms_per_step": round(pg["ms_per_step"], 4),
+                                    "roofline": {"kernel": "whole call (fp32 vector ALU)", "bound": "alu",
+                                                 "achieved": round(tf, 1), "peak": 157.3, "unit": "TFLOP/s",
+                                                 "frac": round(tf / 157.3, 4), "flop_per_token_head": flop},
+                                    "whole_call_hbm": {"achieved": round(gb, 1), "peak": HBM_PEAK_GBS,
+                                                       "unit": "GB/s", "frac": round(gb / HBM_PEAK_GBS, 4),
+                                                       "bytes_per_token_head": gbytes}}
         vw = workloads.VARLEN_32
         pv = bench_varlen(vw, args.steps, args.warmup)
         av = BYTES_PER_TOKEN_HEAD * pv["units"] / (pv["ms_per_step"] * 1e-3) / 1e9
