@@ -7,7 +7,11 @@ product package.
 
 Contents
   * ``linattn_oracle.c`` -> ``liblinattn_oracle.so``: the token-by-token fp64
-    recurrence (the definition; pinned by the tests listed in each function).
+    recurrence (the definition; pinned by the tests listed in each function), and
+    its adjoint for the backward pass (``prefill_backward``: a forward sweep for the
+    query gradients and a reverse sweep over the adjoint state for the key and
+    value gradients; pinned by finite differences of the forward oracle, autograd of
+    the quadratic form and exact dyadic cases in tests/test_oracle_backward_pins.py).
   * ``brute.py``: the masked quadratic ("parallel") form, a second definition
     used to pin the recurrence on tiny inputs.
   * ``chunked.py``: an fp64 statement of the chunked method (chunk summaries,
@@ -73,6 +77,10 @@ def _load():
         lib.oracle_decode_step_gated_f64.argtypes = [ctypes.c_int] * 6 + [vp, vp, vp, vp, ip, fp, ctypes.c_int,
                                                                             ctypes.c_double, dp, dp, dp,
                                                                             ctypes.c_int]
+        lib.oracle_prefill_backward_f64.restype = ctypes.c_int
+        lib.oracle_prefill_backward_f64.argtypes = [ctypes.c_int] * 7 + [vp, vp, vp, vp, ip, dp, ctypes.c_int,
+                                                                           ctypes.c_double, dp, dp, dp, dp, dp,
+                                                                           dp, dp, dp, ctypes.c_int]
         lib.oracle_feature_f64.restype = None
         lib.oracle_feature_f64.argtypes = [ctypes.c_int] * 3 + [dp, dp, dp]
         lib.oracle_max_threads.restype = ctypes.c_int
@@ -171,6 +179,46 @@ def prefill(q, k, v, psi: int, n_psi: Optional[int] = None, prf_w=None, w_head=N
     if want_state:
         return o, S.reshape(lead + (n_psi, d_v)), Z.reshape(lead + (n_psi,))
     return o
+
+
+def prefill_backward(q, k, v, dout, psi: int, n_psi: Optional[int] = None, prf_w=None, w_head=None,
+                     gamma=None, normalize: int = 1, eps: float = 1e-6, S0=None, Z0=None, nthreads: int = 0):
+    """Gradients of sum_t dout_t . o_t for the prefill of ``prefill`` (same arguments; dout is
+    [..., T, d_v], any float type, used exactly in fp64). Returns fp64 (dq, dk, dv, dS0, dZ0)
+    with the shapes of q, k, v and of the state [..., n_psi, d_v], [..., n_psi]."""
+    lib = _load()
+    qq, dt = _stored(q)
+    kk, dt2 = _stored(k)
+    vv, dt3 = _stored(v)
+    assert dt == dt2 == dt3 and qq.shape == kk.shape
+    lead = kk.shape[:-2]
+    T, d_k = kk.shape[-2], kk.shape[-1]
+    d_v = vv.shape[-1]
+    nblk = int(np.prod(lead)) if len(lead) else 1
+    n_psi = d_k if n_psi is None else n_psi
+    ww = None
+    if prf_w is not None:
+        ww, dtw = _stored(prf_w)
+        assert dtw == dt, "PRF bank must be stored like q/k/v"
+    wh = None if w_head is None else np.ascontiguousarray(np.asarray(w_head, dtype=np.int32).reshape(nblk))
+    g = None if gamma is None else np.ascontiguousarray(np.asarray(gamma, dtype=np.float64).reshape(nblk))
+    s0 = None if S0 is None else np.ascontiguousarray(np.asarray(S0, dtype=np.float64).reshape(nblk, n_psi, d_v))
+    z0 = None if Z0 is None else np.ascontiguousarray(np.asarray(Z0, dtype=np.float64).reshape(nblk, n_psi))
+    do = np.ascontiguousarray(as_f64(dout).reshape(nblk, T, d_v))
+    dq = np.empty(lead + (T, d_k), dtype=np.float64)
+    dk = np.empty(lead + (T, d_k), dtype=np.float64)
+    dv = np.empty(lead + (T, d_v), dtype=np.float64)
+    dS0 = np.empty((nblk, n_psi, d_v), dtype=np.float64)
+    dZ0 = np.empty((nblk, n_psi), dtype=np.float64)
+    rc = lib.oracle_prefill_backward_f64(
+        nblk, T, d_k, d_v, n_psi, psi, dt, qq.ctypes.data, kk.ctypes.data, vv.ctypes.data,
+        None if ww is None else ww.ctypes.data,
+        None if wh is None else wh.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+        _dptr(g), int(normalize), float(eps), _dptr(s0), _dptr(z0), _dptr(do), _dptr(dq), _dptr(dk), _dptr(dv),
+        _dptr(dS0), _dptr(dZ0), int(nthreads))
+    if rc != 0:
+        raise RuntimeError("oracle_prefill_backward_f64 failed")
+    return dq, dk, dv, dS0.reshape(lead + (n_psi, d_v)), dZ0.reshape(lead + (n_psi,))
 
 
 def _gate_f32(log_gate, shape) -> np.ndarray:

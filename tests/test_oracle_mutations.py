@@ -18,7 +18,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "linattn_oracle.c")
-PINS = os.path.join(ROOT, "tests", "test_oracle_pins.py")
+PINS = [os.path.join(ROOT, "tests", "test_oracle_pins.py"), os.path.join(ROOT, "tests", "test_oracle_backward_pins.py")]
 
 MUTATIONS = {
     "S_not_decayed": [("row[e] = gamma * row[e] + f[p] * vt[e];", "row[e] = row[e] + f[p] * vt[e];")],
@@ -51,6 +51,24 @@ MUTATIONS = {
     "initial_Z_ignored": [("if (Z0) memcpy(Z, Z0", "if (0) memcpy(Z, Z0")],
     "query_feature_from_key": [("oracle_feature_f64(psi, d_k, n_psi, qt, w, g);",
                                 "oracle_feature_f64(psi, d_k, n_psi, kt, w, g);")],
+    # backward
+    "bwd_dden_sign": [("dden = -a / den;", "dden = a / den;")],
+    "bwd_dnum_not_scaled": [("dn[e] = dot_[e] / den;", "dn[e] = dot_[e];")],
+    "bwd_adjoint_not_decayed": [("row[e] = gm * row[e] + g[p] * dn[e];", "row[e] = row[e] + g[p] * dn[e];")],
+    "bwd_adjoint_Z_dropped": [("dg[p] = a + RZ[p];", "dg[p] = a;")],
+    "bwd_dS0_missing_gamma": [("dS0[(size_t)b * nS + i] = gm * R[i];", "dS0[(size_t)b * nS + i] = R[i];")],
+    "bwd_dv_from_query_feature": [("a += R[(size_t)p * d_v + e] * f[p];", "a += R[(size_t)p * d_v + e] * g[p];")],
+    "bwd_dq_state_without_Z": [("dg[p] = a + Z[p] * dden;", "dg[p] = a;")],
+    "bwd_elu_derivative_branch": [("dx[j] = dpsi[j] * (x[j] > 0.0 ? 1.0 : exp(x[j]));",
+                                   "dx[j] = dpsi[j] * (x[j] > 0.0 ? exp(x[j]) : 1.0);")],
+    "bwd_prf_norm_term_dropped": [("dx[j] -= c * (rstar >= 0 ? w[(size_t)rstar * d_k + j] : x[j]);",
+                                   "dx[j] -= c * (rstar >= 0 ? w[(size_t)rstar * d_k + j] : 0.0);")],
+    "bwd_qshift_argmax_ignored": [("if (psi == ORC_PSI_PRF_QSHIFT) {\n      /* argmax", "if (0) {\n      /* argmax")],
+    "bwd_keys_take_the_shift": [("feature_vjp(psi_k, d_k, n_psi, kt, wd, dg, dk + rowk, buf);",
+                                 "feature_vjp(psi, d_k, n_psi, kt, wd, dg, dk + rowk, buf);")],
+    "bwd_adjoint_read_before_write": [
+        ("        load_vec(k, in_dtype, rowk, d_k, kt);\n        load_vec(v, in_dtype, rowv, d_v, vt);\n        oracle_feature_f64(psi_k, d_k, n_psi, kt, wd, f);\n        for (int p = 0; p < n_psi; ++p) {\n          double a = 0.0;\n          for (int e = 0; e < d_v; ++e) a += R[(size_t)p * d_v + e] * vt[e];",
+         "        load_vec(k, in_dtype, rowk, d_k, kt);\n        load_vec(v, in_dtype, rowv, d_v, vt);\n        oracle_feature_f64(psi_k, d_k, n_psi, kt, wd, f);\n        for (int p = 0; p < n_psi; ++p) {\n          double a = 0.0;\n          for (int e = 0; e < d_v; ++e) a += (R[(size_t)p * d_v + e] - g[p] * dn[e]) * vt[e];")],
 }
 
 
@@ -67,7 +85,7 @@ def _run_mutation(name, edits, workdir):
     subprocess.run(["gcc", "-O2", "-std=c99", "-ffp-contract=off", "-fopenmp", "-shared", "-fPIC", c_path,
                     "-o", so_path, "-lm"], check=True, capture_output=True)
     env = dict(os.environ, LINATTN_ORACLE_LIB=so_path, OMP_NUM_THREADS="1")
-    r = subprocess.run([sys.executable, "-m", "pytest", PINS, "-x", "-q", "-p", "no:cacheprovider"],
+    r = subprocess.run([sys.executable, "-m", "pytest", *PINS, "-x", "-q", "-p", "no:cacheprovider"],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
     return name, r.returncode, r.stdout[-400:]
 
