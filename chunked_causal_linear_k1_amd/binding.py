@@ -26,7 +26,9 @@ MAX_DECAY_HEADS = 256
 
 EXPORTED = ("lin_attn_prefill_workspace_size", "lin_attn_prefill", "lin_attn_prefill_profiled",
             "lin_attn_prefill_varlen", "lin_attn_prefill_varlen_workspace_size", "lin_attn_prefill_gated",
-            "lin_attn_prefill_gated_workspace_size", "lin_attn_decode_step", "lin_attn_decode_step_gated", "lin_attn_status_string", "lin_attn_version")
+            "lin_attn_prefill_gated_workspace_size", "lin_attn_prefill_backward",
+            "lin_attn_prefill_backward_workspace_size", "lin_attn_decode_step", "lin_attn_decode_step_gated",
+            "lin_attn_status_string", "lin_attn_version")
 
 
 class PrefillDesc(ctypes.Structure):
@@ -80,6 +82,12 @@ def load() -> ctypes.CDLL:
         lib.lin_attn_prefill_gated_workspace_size.restype = ctypes.c_int
         lib.lin_attn_prefill_gated_workspace_size.argtypes = [ctypes.POINTER(PrefillDesc),
                                                               ctypes.POINTER(ctypes.c_size_t)]
+        lib.lin_attn_prefill_backward.restype = ctypes.c_int
+        lib.lin_attn_prefill_backward.argtypes = [ctypes.POINTER(PrefillDesc), vp, vp, vp, fp, vp, vp, vp, vp, vp,
+                                                  vp, vp, vp, vp, ctypes.c_size_t, vp]
+        lib.lin_attn_prefill_backward_workspace_size.restype = ctypes.c_int
+        lib.lin_attn_prefill_backward_workspace_size.argtypes = [ctypes.POINTER(PrefillDesc),
+                                                                 ctypes.POINTER(ctypes.c_size_t)]
         lib.lin_attn_decode_step_gated.restype = ctypes.c_int
         lib.lin_attn_decode_step_gated.argtypes = [ctypes.POINTER(DecodeDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.lin_attn_decode_step.restype = ctypes.c_int
@@ -230,6 +238,53 @@ def lin_attn_prefill_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, c
     if st != LA_OK:
         raise LinAttnError(st, "lin_attn_prefill_varlen")
     return o
+
+
+def backward_workspace_size(desc: PrefillDesc) -> int:
+    n = ctypes.c_size_t(0)
+    st = load().lin_attn_prefill_backward_workspace_size(ctypes.byref(desc), ctypes.byref(n))
+    if st != LA_OK:
+        raise LinAttnError(st, "lin_attn_prefill_backward_workspace_size")
+    return int(n.value)
+
+
+def lin_attn_prefill_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch.Tensor, *, psi: int,
+                              chunk: int, normalize: int = 1, eps: float = 1e-6,
+                              gamma: Optional[Sequence[float]] = None, init_S: Optional[torch.Tensor] = None,
+                              init_Z: Optional[torch.Tensor] = None, dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
+                              dv: Optional[torch.Tensor] = None, dinit_S: Optional[torch.Tensor] = None,
+                              dinit_Z: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                              stream=None, layout: str = "bhtd"):
+    """(dq, dk, dv) of L = sum dout . o for lin_attn_prefill with the same arguments (C ABI call).
+
+    dout is float32 or bfloat16, laid out like o. Gradients are float32 in the layouts of q, k,
+    v; dinit_S / dinit_Z are written when given."""
+    if layout == "bhtd":
+        B, H, T, d_k = q.shape
+        lay = LA_LAYOUT_BHTD
+    elif layout == "bthd":
+        B, T, H, d_k = q.shape
+        lay = LA_LAYOUT_BTHD
+    else:
+        raise ValueError(f"layout must be 'bhtd' or 'bthd', not {layout!r}")
+    d_v = v.shape[-1]
+    for t in (q, k, v, dout):
+        if not t.is_contiguous():
+            raise ValueError(f"q, k, v, dout must be contiguous ({layout})")
+    dq = torch.empty(q.shape, dtype=torch.float32, device=q.device) if dq is None else dq
+    dk = torch.empty(k.shape, dtype=torch.float32, device=q.device) if dk is None else dk
+    dv = torch.empty(v.shape, dtype=torch.float32, device=q.device) if dv is None else dv
+    desc = prefill_desc(B, H, T, d_k, d_v, d_k, chunk, psi, normalize, eps, _dtype_code(q), _dtype_code(dout), lay)
+    ws_bytes = backward_workspace_size(desc)
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    st = load().lin_attn_prefill_backward(
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _gamma_array(gamma, H), _ptr(init_S), _ptr(init_Z),
+        _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dinit_S), _ptr(dinit_Z), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    if st != LA_OK:
+        raise LinAttnError(st, "lin_attn_prefill_backward")
+    return dq, dk, dv
 
 
 def gated_workspace_size(desc: PrefillDesc) -> int:

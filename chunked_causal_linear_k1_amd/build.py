@@ -17,6 +17,7 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "liblinattn.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 SOURCES = ["la_api.cpp", "la_decode.hip", "la_scan.hip", "la_prefill_bf16.hip", "la_prefill_f32.hip", "la_gla.hip",
+           "la_backward.hip",
            "la_prefill_bf16_c64_d64.hip", "la_prefill_bf16_c64_d128.hip", "la_prefill_bf16_c128_d64.hip",
            "la_prefill_bf16_c128_d128.hip", "la_prefill_prf.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -31,10 +32,20 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 
+# The backward kernels keep two states and their operands live at once: with the VGPR form
+# their accumulators would share the 256 architectural VGPRs with everything else (and this
+# compiler's AGPR-copy rewrite pass crashes on them), so they keep the accumulation registers.
+NO_VGPR_FORM = {"la_backward.hip"}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [HIPCC] + COMMON + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+    flags = COMMON
+    if src in NO_VGPR_FORM:  # drop "-mllvm -amdgpu-mfma-vgpr-form=true"
+        i = COMMON.index("-amdgpu-mfma-vgpr-form=true")
+        flags = COMMON[:i - 1] + COMMON[i + 1:]
+    cmd = [HIPCC] + flags + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

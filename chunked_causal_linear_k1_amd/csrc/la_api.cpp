@@ -130,7 +130,7 @@ const char* lin_attn_status_string(la_status s) {
   return "unknown status";
 }
 
-const char* lin_attn_version(void) { return "0.2.0"; }
+const char* lin_attn_version(void) { return "0.3.0"; }
 
 la_status lin_attn_prefill_workspace_size(const la_prefill_desc* d, size_t* bytes) {
   if (!bytes) return LA_ERR_NULL;
@@ -145,6 +145,28 @@ la_status lin_attn_prefill_gated_workspace_size(const la_prefill_desc* d, size_t
   const la_status st = validate_prefill_desc(d, true);
   if (st != LA_OK) return st;
   *bytes = make_plan(d, -1, true).ws_bytes;
+  return LA_OK;
+}
+
+// The backward pass: the forward segment prefixes, the adjoint segment records (same size) and,
+// with a denominator, two floats per token (1/den and dden).
+la_status validate_backward_desc(const la_prefill_desc* d) {
+  const la_status st = validate_prefill_desc(d);
+  if (st != LA_OK) return st;
+  if (d->in_dtype != LA_BF16) return LA_ERR_UNSUPPORTED;
+  return la::prefill_backward_supported(d->chunk, d->d_k, d->d_v, d->n_psi, d->psi) ? LA_OK : LA_ERR_UNSUPPORTED;
+}
+
+size_t backward_ws_bytes(const la_prefill_desc* d) {
+  const size_t tok = d->normalize ? (size_t)d->B * d->H * d->T * 2 * sizeof(float) : 0;
+  return 2 * make_plan(d).ws_bytes + tok;
+}
+
+la_status lin_attn_prefill_backward_workspace_size(const la_prefill_desc* d, size_t* bytes) {
+  if (!bytes) return LA_ERR_NULL;
+  const la_status st = validate_backward_desc(d);
+  if (st != LA_OK) return st;
+  *bytes = backward_ws_bytes(d);
   return LA_OK;
 }
 
@@ -328,6 +350,69 @@ la_status lin_attn_decode_step_gated(const la_decode_desc* d, const void* q, con
                                      hipStream_t stream) {
   if (!log_gate) return LA_ERR_NULL;
   return decode_impl(d, q, k, v, nullptr, log_gate, prf_w, S, Z, o, stream);
+}
+
+la_status lin_attn_prefill_backward(const la_prefill_desc* d, const void* q, const void* k, const void* v,
+                                    const float* gamma, const float* init_S, const float* init_Z, const void* dout,
+                                    float* dq, float* dk, float* dv, float* dinit_S, float* dinit_Z,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  la_status st = validate_backward_desc(d);
+  if (st != LA_OK) return st;
+  if (!q || !k || !v || !dout || !dq || !dk || !dv) return LA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned16(dq) ||
+      !aligned16(dk) || !aligned16(dv) || !aligned16(init_S) || !aligned16(init_Z) || !aligned16(dinit_S) ||
+      !aligned16(dinit_Z) || !aligned16(workspace))
+    return LA_ERR_ALIGN;
+  st = check_gamma(gamma, d->H);
+  if (st != LA_OK) return st;
+  const Plan pl = make_plan(d);
+  const size_t need = backward_ws_bytes(d);
+  if (!workspace || workspace_bytes < need) return LA_ERR_WORKSPACE;
+
+  la::BackwardParams bp;
+  memset(&bp, 0, sizeof bp);
+  PrefillParams& p = bp.f;
+  p.q = q; p.k = k; p.v = v;
+  p.ws = (float*)workspace;
+  p.B = d->B; p.H = d->H; p.T = d->T;
+  if (d->layout == LA_LAYOUT_BTHD) {
+    p.tok_rows = d->H; p.head_rows = 1; p.seq_rows = (long long)d->T * d->H;
+  } else {
+    p.tok_rows = 1; p.head_rows = d->T; p.seq_rows = (long long)d->H * d->T;
+  }
+  p.d_k = d->d_k; p.d_v = d->d_v; p.n_psi = d->n_psi; p.C = d->chunk;
+  p.psi = d->psi; p.normalize = d->normalize; p.eps = d->eps;
+  p.n_chunks = pl.n_chunks; p.seg_chunks = pl.seg_chunks; p.n_seg = pl.n_seg;
+  p.has_decay = fill_log2g(gamma, d->H, p.log2g);
+  bp.dout = dout;
+  bp.dq = dq; bp.dk = dk; bp.dv = dv;
+  bp.rev = (float*)((char*)workspace + pl.ws_bytes);
+  bp.tok = d->normalize ? (float*)((char*)workspace + 2 * pl.ws_bytes) : nullptr;
+  bp.dout_bf16 = d->out_dtype == LA_BF16;
+
+  ScanParams sp;
+  memset(&sp, 0, sizeof sp);
+  sp.ws = p.ws;
+  sp.init_S = init_S;
+  sp.init_Z = d->normalize ? init_Z : nullptr;
+  sp.BH = d->B * d->H; sp.H = d->H; sp.T = d->T;
+  sp.n_psi = d->n_psi; sp.d_v = d->d_v;
+  sp.n_seg = pl.n_seg; sp.seg_len = pl.seg_chunks * d->chunk;
+  sp.has_decay = p.has_decay;
+  memcpy(sp.log2g, p.log2g, sizeof sp.log2g);
+  ScanParams rp = sp;  // the adjoint state: no initial element; its total is the initial state's gradient
+  rp.ws = bp.rev;
+  rp.init_S = nullptr; rp.init_Z = nullptr;
+  rp.final_S = dinit_S;
+  rp.final_Z = d->normalize ? dinit_Z : nullptr;
+  rp.reverse = 1;
+
+  hipError_t e = la::launch_prefill_bf16_summary(p, stream);            // forward segment summaries
+  if (e == hipSuccess) e = la::launch_segment_scan(sp, stream);          // forward prefixes
+  if (e == hipSuccess) e = la::launch_prefill_backward(bp, stream, false);  // query sweep: dq, adjoint summaries
+  if (e == hipSuccess) e = la::launch_segment_scan(rp, stream);          // adjoint state after each segment
+  if (e == hipSuccess) e = la::launch_prefill_backward(bp, stream, true);   // state sweep: dk, dv
+  return e == hipSuccess ? LA_OK : LA_ERR_HIP;
 }
 
 la_status lin_attn_prefill_gated(const la_prefill_desc* d, const void* q, const void* k, const void* v,

@@ -1,0 +1,770 @@
+// la_backward.hip -- backward pass of the chunked prefill: the gradients of
+// L = sum_t dout_t . o_t with respect to q, k, v (and, through the scan, the initial state).
+//
+// Two sweeps, as in "Linearized 2-Simplicial Attention" (4.2 Custom Triton kernel, Backward;
+// appendix "Backward query sweep" and "Backward state sweep"): a query sweep that recomputes
+// the prefix state and produces dq, and a state sweep that produces the key and value
+// gradients from the adjoint state. With g_t = psi(q_t), f_t = psi(k_t) and the read
+// o_t = g_t^T S_t / (g_t . Z_t + eps) of the inclusive state ("Log-Depth Chunked
+// Linear-Attention Scan", Mathematical statement), the chain rule gives
+//   dnum_t = dout_t / den_t,  dden_t = -(dout_t . num_t) / den_t^2   (normalize = 0: dout_t, 0)
+//   dg_t   = S_t dnum_t + Z_t dden_t
+//   R_t    = sum_{u >= t} gamma^(u-t) g_u dnum_u^T,  RZ_t likewise with dden_u  (adjoint state)
+//   df_t   = R_t v_t + RZ_t,  dv_t = R_t^T f_t.
+// Per step of BC tokens (j, i inside the step; theta_j = gamma^(j+1), xi_i = gamma^(L-1-i),
+// D_ji = gamma^(j-i) [i <= j]; the chunk algebra of the same page's Implementation notes and of
+// "Linear Attention and Retentive Networks", Retentive Networks, representation C):
+//   Bm  = (dNum V^T + dden 1^T) (.) D                       C x C
+//   dG  = Bm F + theta (.) (dNum S_<^T + dden Z_<^T)        query sweep; S_< the state before the step
+//   A   = (G F^T) (.) D
+//   dV  = A^T dNum + xi (.) (F R_>)                         state sweep; R_> the adjoint after the step
+//   dF  = Bm^T G + xi (.) (V R_>^T + RZ_>)
+//   R_> of the previous step = gamma^L R_> + (theta (.) G)^T dNum
+// The query sweep recomputes dout_t . num_t from the same tiles (X = dout V^T, Y = dout S_<^T):
+//   dout_j . num_j = sum_i A_ji X_ji + theta_j g_j . Y_j,  den_j = sum_i A_ji + theta_j g_j . Z_< + eps,
+// so only the inputs are needed (no saved output), and dden does not inherit the rounding of a
+// stored o: the terms S dnum and Z dden nearly cancel for a normalised average, which would
+// amplify it. Segments: the query sweep starts from the forward scan's prefix and accumulates
+// each segment's adjoint summary sum_t gamma^(t - start + 1) g_t dnum_t^T; the segment scan
+// run in reverse order turns those into the adjoint state after each segment.
+//
+// Both kernels: one workgroup of four waves per (sequence, segment), d_k = d_v = n_psi =
+// 128, bf16 operands on MFMA 32x32x16 with fp32 accumulation; every operand that is not
+// exact in bf16 (the states, scaled features, dNum, the C x C tiles, elu+1 keys) is a
+// two-term hi + lo expansion (psi(q) included, unlike the forward output pass: the adjoint
+// state sums psi(q) against signed upstream gradients without averaging the rounding out).
+// Wave w owns the 32 columns [32w, 32w + 32) of each output.
+#include "la_device.hpp"
+#include "la_kernels.hpp"
+
+namespace la {
+namespace {
+
+constexpr int BC = 64;    // tokens per step
+constexpr int BD = 128;   // d_k = d_v = n_psi
+constexpr int BNT = 256;  // four waves
+constexpr int TP = BD + 8;  // pitch (elements) of the C x D bf16 tiles
+constexpr int SQ = BC + 8;  // pitch of the C x C bf16 tiles
+
+// LDS image (bf16 element offsets, then float tables).
+struct BG {
+  static constexpr int TILE = BC * TP, STILE = BC * SQ;
+  static constexpr int QH = 0, QL = TILE, KH = 2 * TILE, KL = 3 * TILE, V = 4 * TILE, NH = 5 * TILE, NL = 6 * TILE;
+  static constexpr int AH = 7 * TILE, AL = AH + STILE, BH = AL + STILE, BL = BH + STILE;
+  static constexpr int HALVES = BL + STILE;
+  static constexpr int F0 = HALVES / 2;      // first float
+  static constexpr int TH = F0, XI = TH + BC, DD = XI + BC, IV = DD + BC, WT = IV + BC, ZV = WT + BC;
+  static constexpr int FEND = ZV + BD;
+  static constexpr int BYTES = FEND * 4;
+};
+static_assert(BG::HALVES % 8 == 0, "float tables 16-byte aligned");
+static_assert(BG::BYTES <= 160 * 1024, "LDS image fits a CU");
+// the query sweep's row partials (8 x BC floats) sit in the AH region, unused there
+static_assert(9 * BC * 2 <= BG::STILE, "row partials and weights fit one bf16 C x C tile");
+
+// ---- global tiles ----------------------------------------------------------------------
+
+// A step of BC token rows x BD bf16: 4 pieces of 8 elements per thread (row t/16 + 16i).
+struct Tile16 {
+  uint4 r[4];
+};
+__device__ __forceinline__ void load_tile16(Tile16& P, const void* base, int valid, uint32_t rsb) {
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, rows_extent(valid, rsb, BD * 2));
+  const int t = threadIdx.x;
+  const uint32_t v0 = (uint32_t)(t >> 4) * rsb + (uint32_t)(t & 15) * 16;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) P.r[i] = buf_load16(rs, v0, (uint32_t)(16 * i) * rsb);
+}
+__device__ __forceinline__ int t16_row(int i) { return (threadIdx.x >> 4) + 16 * i; }
+__device__ __forceinline__ int t16_col(int) { return (threadIdx.x & 15) * 8; }
+
+// A step of BC token rows x BD fp32 (or bf16) values: thread t holds token t/4, columns
+// 4 (t%4) + 16 i + 0..3 for i = 0..7.
+struct TileF {
+  f32x4 r[8];
+};
+template <bool BF>
+__device__ __forceinline__ void load_tileF(TileF& P, const void* base, int valid, uint32_t rsb) {
+  constexpr int ES = BF ? 2 : 4;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, rows_extent(valid, rsb, BD * ES));
+  const int t = threadIdx.x;
+  const uint32_t v0 = (uint32_t)(t >> 2) * rsb + (uint32_t)(4 * (t & 3)) * ES;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if (BF) {
+      const u32x2 w = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, v0, 16 * i * ES, 0));
+      P.r[i] = f32x4{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xffff0000u), __uint_as_float(w[1] << 16),
+                     __uint_as_float(w[1] & 0xffff0000u)};
+    } else {
+      P.r[i] = __builtin_bit_cast(f32x4, buf_load16(rs, v0, 16 * i * ES));
+    }
+  }
+}
+__device__ __forceinline__ int tf_tok() { return threadIdx.x >> 2; }
+__device__ __forceinline__ int tf_col(int i) { return 4 * (threadIdx.x & 3) + 16 * i; }
+
+// Sum over the four threads of a token (lanes t, t^1, t^2, t^3 of one wave).
+__device__ __forceinline__ float quad_sum(float x) {
+  x += __shfl_xor(x, 1);
+  x += __shfl_xor(x, 2);
+  return x;
+}
+
+// ---- commits ---------------------------------------------------------------------------
+
+// psi(x) of a bf16 tile to LDS as hi (+ lo when LO): rows >= L are zero (padded positions
+// are the monoid identity). ELU: elu+1.
+template <bool ELU, bool LO>
+__device__ __forceinline__ void commit_feat(const Tile16& P, __bf16* hi, __bf16* lo, int L) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = t16_row(i), col = t16_col(i);
+    const bf16x8 x = __builtin_bit_cast(bf16x8, P.r[i]);
+    bf16x8 h, l;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float xf = from_bf16(x[j]);
+      const float f = row < L ? (ELU ? elu1(xf) : xf) : 0.f;
+      const bf16_pair pr = split_bf16(f);
+      h[j] = pr.hi;
+      l[j] = pr.lo;
+    }
+    *(bf16x8*)(hi + row * TP + col) = h;
+    if (LO) *(bf16x8*)(lo + row * TP + col) = l;
+  }
+}
+
+__device__ __forceinline__ void commit_raw(const Tile16& P, __bf16* dst) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) *(uint4*)(dst + t16_row(i) * TP + t16_col(i)) = P.r[i];
+}
+
+// s * x (x from a TileF, s the token's scale) as hi + lo.
+__device__ __forceinline__ void commit_scaled(const TileF& P, float s, __bf16* hi, __bf16* lo) {
+  const int j = tf_tok();
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int col = tf_col(i);
+    bf16x4 h, l;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bf16_pair pr = split_bf16(s * P.r[i][e]);
+      h[e] = pr.hi;
+      l[e] = pr.lo;
+    }
+    *(bf16x4*)(hi + j * TP + col) = h;
+    *(bf16x4*)(lo + j * TP + col) = l;
+  }
+}
+
+// ---- helpers ---------------------------------------------------------------------------
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) z[r] = 0.f;
+  return z;
+}
+
+// (hi + lo) * f per element, 8 values, re-split as hi + lo (LO false: lo ignored).
+template <bool LO>
+__device__ __forceinline__ void scale_split(const bf16x8& xh, const bf16x8& xl, const float* f, bf16x8& hi,
+                                            bf16x8& lo) {
+  float y[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) y[j] = (from_bf16(xh[j]) + (LO ? from_bf16(xl[j]) : 0.f)) * f[j];
+  split8_trunc(y, hi, lo);
+}
+
+// Registers 8q..8q+7 of a D-tile (rows in the feedback order of k-half q) as hi + lo operands.
+__device__ __forceinline__ void split_dtile(const f32x16& D, bf16x8 (&hi)[2], bf16x8 (&lo)[2]) {
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    float x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = D[8 * q + j];
+    split8_trunc(x, hi[q], lo[q]);
+  }
+}
+
+// Row sums of a D-tile over its 32 columns (the 32 lanes of each half-wave), by recursive
+// halving (16 exchanges): lane l ends with the sum of row dtile_row((l >> 1) & 15, l).
+__device__ __forceinline__ float rowsum16(const f32x16& v, int lane) {
+  float a[8], b[4], c[2];
+  const bool b4 = lane & 16, b3 = lane & 8, b2 = lane & 4, b1 = lane & 2;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a[i] = (b4 ? v[8 + i] : v[i]) + __shfl_xor(b4 ? v[i] : v[8 + i], 16);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) b[i] = (b3 ? a[4 + i] : a[i]) + __shfl_xor(b3 ? a[i] : a[4 + i], 8);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) c[i] = (b2 ? b[2 + i] : b[i]) + __shfl_xor(b2 ? b[i] : b[2 + i], 4);
+  const float d = (b1 ? c[1] : c[0]) + __shfl_xor(b1 ? c[0] : c[1], 2);
+  return d + __shfl_xor(d, 1);
+}
+__device__ __forceinline__ int rowsum16_row(int lane) { return dtile_row((lane >> 1) & 15, lane); }
+
+// The causal decay mask D_ji (0 above the diagonal).
+template <bool DECAY>
+__device__ __forceinline__ float dmask(int j, int i, float lg) {
+  return i <= j ? (DECAY ? exp2f((float)(j - i) * lg) : 1.f) : 0.f;
+}
+
+// Tile (jt, it) of the lower block triangle of a C x C matrix: job 0 -> (0,0), 1 -> (1,0), 2 -> (1,1).
+__device__ __forceinline__ int job_jt(int job) { return job == 0 ? 0 : 1; }
+__device__ __forceinline__ int job_it(int job) { return job == 2 ? 1 : 0; }
+
+// A = G F^T tile (jt, it), unmasked: G and F as hi + lo (lo only for elu+1).
+template <bool ELU>
+__device__ __forceinline__ f32x16 a_tile_acc(const __bf16* sh, int jt, int it, int lane) {
+  f32x16 acc = zero16();
+#pragma unroll
+  for (int k0 = 0; k0 < BD; k0 += 16) {
+    const bf16x8 gh = ld_cols8(sh + BG::QH, TP, 32 * jt, k0, lane);  // A[m=j][k=p] = G[j][p]
+    const bf16x8 fh = ld_cols8(sh + BG::KH, TP, 32 * it, k0, lane);  // B[k=p][n=i] = F[i][p]
+    acc = mfma32(gh, fh, acc);
+    if (ELU) {
+      acc = mfma32(gh, ld_cols8(sh + BG::KL, TP, 32 * it, k0, lane), acc);
+      acc = mfma32(ld_cols8(sh + BG::QL, TP, 32 * jt, k0, lane), fh, acc);
+    }
+  }
+  return acc;
+}
+
+// X = N V^T tile (jt, it), N = the hi + lo tile in NH/NL (unmasked).
+__device__ __forceinline__ f32x16 x_tile_acc(const __bf16* sh, int jt, int it, int lane) {
+  f32x16 acc = zero16();
+#pragma unroll
+  for (int k0 = 0; k0 < BD; k0 += 16) {
+    const bf16x8 b = ld_cols8(sh + BG::V, TP, 32 * it, k0, lane);  // B[k=e][n=i] = V[i][e]
+    acc = mfma32(ld_cols8(sh + BG::NH, TP, 32 * jt, k0, lane), b, acc);
+    acc = mfma32(ld_cols8(sh + BG::NL, TP, 32 * jt, k0, lane), b, acc);
+  }
+  return acc;
+}
+
+// Bm tile (jt, it) = (X inv_j + dden_j) (.) D, split hi + lo into LDS. INV: X was formed
+// from dout (query sweep) and takes inv_j here; otherwise from dNum (state sweep).
+template <bool DECAY, bool NORM, bool INV>
+__device__ __forceinline__ void store_bm(__bf16* sh, const float* sf, const f32x16& X, int jt, int it, int L,
+                                         float lg, int lane) {
+  const int i = 32 * it + (lane & 31);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int j = 32 * jt + dtile_row(r, lane);
+    const float x = NORM ? (INV ? X[r] * sf[BG::IV + j] : X[r]) + sf[BG::DD + j] : X[r];
+    const bf16_pair pr = split_bf16(i < L ? x * dmask<DECAY>(j, i, lg) : 0.f);
+    sh[BG::BH + j * SQ + i] = pr.hi;
+    sh[BG::BL + j * SQ + i] = pr.lo;
+  }
+}
+
+// psi'(x) from psi(x) for elu+1: 1 where x > 0 (psi > 1), exp(x) = psi where x <= 0.
+__device__ __forceinline__ float dpsi_from_feat(float f) { return fminf(f, 1.f); }
+
+// ---- query sweep -----------------------------------------------------------------------
+
+template <bool ELU, bool DECAY, bool NORM, bool DBF>
+__global__ __launch_bounds__(BNT) void k_bwd_query(BackwardParams bp) {
+  const PrefillParams& p = bp.f;
+  extern __shared__ __align__(16) unsigned char smem[];
+  __bf16* sh = (__bf16*)smem;
+  float* sf = (float*)smem;
+  float* part = sf + BG::AH / 2;  // row partials: A sums [2][BC], A.X sums [2][BC], g.Y sums [4][BC]
+  float* wi = part + 8 * BC;      // W_j / den_j, the adjoint summary's token weights
+  const int bh = blockIdx.x, seg = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const SeqSpan sq = seq_span(p, bh);
+  const int T = sq.T;
+  const int seg_tok = p.seg_chunks * p.C;
+  const int tb = seg * seg_tok, te = min(tb + seg_tok, T);
+  const size_t E = (size_t)BD * BD + BD;
+  float* rrec = bp.rev + ((size_t)bh * p.n_seg + seg) * E;
+  const int col = 32 * w + (lane & 31);  // this lane's output column
+  f32x16 RS[4];                          // adjoint summary [p][e]: rows p in tile pt, column e = col
+#pragma unroll
+  for (int pt = 0; pt < 4; ++pt) RS[pt] = zero16();
+  float rz = 0.f;  // thread p < BD: the adjoint summary's Z part
+  if (tb < te) {
+    const float lg = DECAY ? p.log2g[bh % p.H] : 0.f;
+    const uint32_t rsb = (uint32_t)p.tok_rows * BD * 2, rsb4 = (uint32_t)p.tok_rows * BD * 4;
+    const uint32_t rsbd = (uint32_t)p.tok_rows * BD * (DBF ? 2 : 4);
+    const float* pre = p.ws + ((size_t)bh * p.n_seg + seg) * E;
+    // the state before the step, transposed: ST[et] rows e in [32et, 32et + 32), column p = col
+    f32x16 ST[4];
+#pragma unroll
+    for (int et = 0; et < 4; ++et)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ST[et][r] = pre[(size_t)col * BD + 32 * et + dtile_row(r, lane)];
+    float zreg = (NORM && tid < BD) ? pre[(size_t)BD * BD + tid] : 0.f;  // Z_<[p] of thread p
+
+    for (int t0 = tb; t0 < te; t0 += BC) {
+      const int L = min(BC, te - t0);
+      const long long r0 = sq.row0 + (long long)t0 * p.tok_rows;
+      Tile16 tq, tk, tv;
+      load_tile16(tq, (const uint16_t*)p.q + r0 * BD, L, rsb);
+      load_tile16(tk, (const uint16_t*)p.k + r0 * BD, L, rsb);
+      load_tile16(tv, (const uint16_t*)p.v + r0 * BD, L, rsb);
+      TileF tdo;
+      load_tileF<DBF>(tdo, (const unsigned char*)bp.dout + r0 * BD * (DBF ? 2 : 4), L, rsbd);
+      lds_barrier();  // the previous step is done with LDS
+      commit_feat<ELU, ELU>(tq, sh + BG::QH, sh + BG::QL, L);
+      commit_feat<ELU, ELU>(tk, sh + BG::KH, sh + BG::KL, L);
+      commit_raw(tv, sh + BG::V);
+      commit_scaled(tdo, 1.f, sh + BG::NH, sh + BG::NL);  // dout as hi + lo
+      if (tid < BC) {
+        const int j = tid;
+        sf[BG::TH + j] = DECAY ? exp2f((float)(j + 1) * lg) : 1.f;
+        sf[BG::XI + j] = j < L ? (DECAY ? exp2f((float)(L - 1 - j) * lg) : 1.f) : 0.f;
+        sf[BG::WT + j] = DECAY ? exp2f((float)(t0 - tb + j + 1) * lg) : 1.f;
+        if (!NORM) {
+          sf[BG::IV + j] = 1.f;
+          sf[BG::DD + j] = 0.f;
+          wi[j] = sf[BG::WT + j];
+        }
+      }
+      if (NORM && tid < BD) sf[BG::ZV + tid] = zreg;
+      lds_barrier();
+
+      // X = dout V^T tiles (lower block triangle, waves 0..2), kept in registers; with a
+      // denominator also A = G F^T and the row partials sum_i A_ji and sum_i A_ji X_ji
+      f32x16 X = zero16();
+      if (w < 3) {
+        const int jt = job_jt(w), it = job_it(w);
+        X = x_tile_acc(sh, jt, it, lane);
+        if (NORM) {
+          const f32x16 A = a_tile_acc<ELU>(sh, jt, it, lane);
+          f32x16 Am, AX;
+          const int i = 32 * it + (lane & 31);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            Am[r] = A[r] * dmask<DECAY>(32 * jt + dtile_row(r, lane), i, lg);
+            AX[r] = Am[r] * X[r];
+          }
+          const float sa = rowsum16(Am, lane), sx = rowsum16(AX, lane);
+          if ((lane & 1) == 0) {
+            const int j = 32 * jt + rowsum16_row(lane);
+            part[it * BC + j] = sa;
+            part[2 * BC + it * BC + j] = sx;
+          }
+        }
+      } else if (NORM && lane < 32) {  // the upper tile (0, 1) is zero
+        part[BC + lane] = 0.f;
+        part[3 * BC + lane] = 0.f;
+      }
+      // Y = dout S_<^T (rows j, column p = col), kept in registers
+      f32x16 Y[2] = {zero16(), zero16()};
+#pragma unroll
+      for (int et = 0; et < 4; ++et) {
+        bf16x8 sth[2], stl[2];
+        split_dtile(ST[et], sth, stl);
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+          for (int jt = 0; jt < 2; ++jt) {
+            const bf16x8 nh = ld_cols8_perm(sh + BG::NH, TP, 32 * jt, 32 * et, q, lane);
+            const bf16x8 nl = ld_cols8_perm(sh + BG::NL, TP, 32 * jt, 32 * et, q, lane);
+            Y[jt] = mfma32(nh, sth[q], Y[jt]);
+            Y[jt] = mfma32(nh, stl[q], Y[jt]);
+            Y[jt] = mfma32(nl, sth[q], Y[jt]);
+          }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (NORM) {
+        // row partials of g_j . Y_j over this wave's 32 features
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt) {
+          f32x16 gy;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int j = 32 * jt + dtile_row(r, lane);
+            const float g = from_bf16(sh[BG::QH + j * TP + col]) + (ELU ? from_bf16(sh[BG::QL + j * TP + col]) : 0.f);
+            gy[r] = g * Y[jt][r];
+          }
+          const float sy = rowsum16(gy, lane);
+          if ((lane & 1) == 0) part[(4 + w) * BC + 32 * jt + rowsum16_row(lane)] = sy;
+        }
+        lds_barrier();
+        // per token: den, dout . num, 1/den and dden = -(dout . num) / den^2
+        const int j = tf_tok(), qq = tid & 3;
+        float zs = 0.f;
+        for (int pp = 32 * qq; pp < 32 * qq + 32; ++pp) {
+          const float g = from_bf16(sh[BG::QH + j * TP + pp]) + (ELU ? from_bf16(sh[BG::QL + j * TP + pp]) : 0.f);
+          zs += g * sf[BG::ZV + pp];
+        }
+        zs = quad_sum(zs);
+        if (qq == 0) {
+          const float th = sf[BG::TH + j];
+          const float den = part[j] + part[BC + j] + th * zs + p.eps;
+          const float dn = part[2 * BC + j] + part[3 * BC + j] +
+                           th * (part[4 * BC + j] + part[5 * BC + j] + part[6 * BC + j] + part[7 * BC + j]);
+          // padded rows: dnum = dden = 0 (their den may be 0 when eps is)
+          const float inv = j < L ? 1.f / den : 0.f;
+          const float dden = -dn * inv * inv;
+          sf[BG::IV + j] = inv;
+          sf[BG::DD + j] = dden;
+          wi[j] = sf[BG::WT + j] * inv;
+          if (j < L) {
+            float* tk2 = bp.tok + ((size_t)bh * p.T + (t0 + j)) * 2;
+            tk2[0] = inv;
+            tk2[1] = dden;
+          }
+        }
+        lds_barrier();
+      }
+
+      // Bm tiles as hi + lo
+      if (w < 3) store_bm<DECAY, NORM, true>(sh, sf, X, job_jt(w), job_it(w), L, lg, lane);
+      lds_barrier();
+
+      // dG = Bm F + theta (inv Y + dden Z_<): rows j, column p = col
+      const __amdgpu_buffer_rsrc_t rdq = make_rsrc(bp.dq + r0 * BD, rows_extent(L, rsb4, BD * 4));
+      const float zp = NORM ? sf[BG::ZV + col] : 0.f;
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt) {
+        f32x16 a1 = zero16();
+#pragma unroll
+        for (int k0 = 0; k0 < 32 * (jt + 1); k0 += 16) {
+          const bf16x8 kh = ld_rows8(sh + BG::KH, TP, k0, 32 * w, lane);  // B[k=i][n=p] = F[i][p]
+          const bf16x8 bmh = ld_cols8(sh + BG::BH, SQ, 32 * jt, k0, lane);  // A[m=j][k=i] = Bm[j][i]
+          const bf16x8 bml = ld_cols8(sh + BG::BL, SQ, 32 * jt, k0, lane);
+          a1 = mfma32(bmh, kh, a1);
+          a1 = mfma32(bml, kh, a1);
+          if (ELU) a1 = mfma32(bmh, ld_rows8(sh + BG::KL, TP, k0, 32 * w, lane), a1);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = 32 * jt + dtile_row(r, lane);
+          const float st = NORM ? sf[BG::IV + j] * Y[jt][r] + sf[BG::DD + j] * zp : Y[jt][r];
+          float g = a1[r] + sf[BG::TH + j] * st;
+          if (ELU)
+            g *= dpsi_from_feat(from_bf16(sh[BG::QH + j * TP + col]) + from_bf16(sh[BG::QL + j * TP + col]));
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(g), rdq, (uint32_t)j * rsb4 + (uint32_t)col * 4, 0, 0);
+        }
+      }
+
+      // adjoint summary: RS[p][e] += sum_j (W_j inv_j G[j][p]) dout[j][e]
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+        for (int k0 = 0; k0 < BC; k0 += 16) {
+          const bf16x8 gh = ld_rows8(sh + BG::QH, TP, k0, 32 * pt, lane);  // A[m=p][k=j] = G[j][p]
+          const bf16x8 nh = ld_rows8(sh + BG::NH, TP, k0, 32 * w, lane);   // B[k=j][n=e]
+          const bf16x8 nl = ld_rows8(sh + BG::NL, TP, k0, 32 * w, lane);
+          if (DECAY || NORM) {
+            bf16x8 sh2, sl2;
+            const bf16x8 gl = ELU ? ld_rows8(sh + BG::QL, TP, k0, 32 * pt, lane) : gh;
+            scale_split<ELU>(gh, gl, wi + k0 + 8 * (lane >> 5), sh2, sl2);
+            RS[pt] = mfma32(sh2, nh, RS[pt]);
+            RS[pt] = mfma32(sh2, nl, RS[pt]);
+            RS[pt] = mfma32(sl2, nh, RS[pt]);
+          } else {
+            RS[pt] = mfma32(gh, nh, RS[pt]);
+            RS[pt] = mfma32(gh, nl, RS[pt]);
+            if (ELU) RS[pt] = mfma32(ld_rows8(sh + BG::QL, TP, k0, 32 * pt, lane), nh, RS[pt]);
+          }
+        }
+      if (NORM && tid < BD) {
+        for (int j = 0; j < L; ++j) {
+          const float g = from_bf16(sh[BG::QH + j * TP + tid]) + (ELU ? from_bf16(sh[BG::QL + j * TP + tid]) : 0.f);
+          rz += sf[BG::WT + j] * g * sf[BG::DD + j];
+        }
+      }
+
+      // state: S_< <- gamma^L S_< + F^T (xi V), held transposed: ST[e][p] += sum_i (xi_i V[i][e]) F[i][p]
+      const float a = DECAY ? exp2f((float)L * lg) : 1.f;
+#pragma unroll
+      for (int et = 0; et < 4; ++et) {
+        if (DECAY) ST[et] *= a;
+#pragma unroll
+        for (int k0 = 0; k0 < BC; k0 += 16) {
+          const bf16x8 va = ld_rows8(sh + BG::V, TP, k0, 32 * et, lane);  // A[m=e][k=i] = V[i][e]
+          const bf16x8 kh = ld_rows8(sh + BG::KH, TP, k0, 32 * w, lane);  // B[k=i][n=p] = F[i][p]
+          if (DECAY) {
+            bf16x8 vh, vl;
+            scale_split<false>(va, va, sf + BG::XI + k0 + 8 * (lane >> 5), vh, vl);
+            ST[et] = mfma32(vh, kh, ST[et]);
+            ST[et] = mfma32(vl, kh, ST[et]);
+            if (ELU) ST[et] = mfma32(vh, ld_rows8(sh + BG::KL, TP, k0, 32 * w, lane), ST[et]);
+          } else {
+            ST[et] = mfma32(va, kh, ST[et]);  // rows past L are zero in F
+            if (ELU) ST[et] = mfma32(va, ld_rows8(sh + BG::KL, TP, k0, 32 * w, lane), ST[et]);
+          }
+        }
+      }
+      if (NORM && tid < BD) {
+        float zn = a * zreg;
+        for (int i = 0; i < L; ++i)
+          zn += sf[BG::XI + i] * (from_bf16(sh[BG::KH + i * TP + tid]) + (ELU ? from_bf16(sh[BG::KL + i * TP + tid]) : 0.f));
+        zreg = zn;
+      }
+    }
+  }
+  // the segment's adjoint summary [S (p, e)][Z (p)]
+#pragma unroll
+  for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) rrec[(size_t)(32 * pt + dtile_row(r, lane)) * BD + col] = RS[pt][r];
+  if (tid < BD) rrec[(size_t)BD * BD + tid] = rz;
+}
+
+// ---- state sweep -----------------------------------------------------------------------
+
+template <bool ELU, bool DECAY, bool NORM, bool DBF>
+__global__ __launch_bounds__(BNT) void k_bwd_key(BackwardParams bp) {
+  const PrefillParams& p = bp.f;
+  extern __shared__ __align__(16) unsigned char smem[];
+  __bf16* sh = (__bf16*)smem;
+  float* sf = (float*)smem;
+  const int bh = blockIdx.x, seg = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const SeqSpan sq = seq_span(p, bh);
+  const int T = sq.T;
+  const int seg_tok = p.seg_chunks * p.C;
+  const int tb = seg * seg_tok, te = min(tb + seg_tok, T);
+  if (tb >= te) return;
+  const size_t E = (size_t)BD * BD + BD;
+  const float* rpre = bp.rev + ((size_t)bh * p.n_seg + seg) * E;  // the adjoint state after this segment
+  const float lg = DECAY ? p.log2g[bh % p.H] : 0.f;
+  const uint32_t rsb = (uint32_t)p.tok_rows * BD * 2, rsb4 = (uint32_t)p.tok_rows * BD * 4;
+  const uint32_t rsbd = (uint32_t)p.tok_rows * BD * (DBF ? 2 : 4);
+  const int col = 32 * w + (lane & 31);
+  // R[p][e]: rows p in tile pt, column e = col;  RT[e][p]: rows e in tile et, column p = col
+  f32x16 R[4], RT[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      R[t][r] = rpre[(size_t)(32 * t + dtile_row(r, lane)) * BD + col];
+      RT[t][r] = rpre[(size_t)col * BD + 32 * t + dtile_row(r, lane)];
+    }
+  float rz = (NORM && tid < BD) ? rpre[(size_t)BD * BD + tid] : 0.f;  // RZ[p] of thread p
+
+  const int nsteps = (te - tb + BC - 1) / BC;
+  for (int s = nsteps - 1; s >= 0; --s) {
+    const int t0 = tb + s * BC, L = min(BC, te - t0);
+    const long long r0 = sq.row0 + (long long)t0 * p.tok_rows;
+    Tile16 tq, tk, tv;
+    load_tile16(tq, (const uint16_t*)p.q + r0 * BD, L, rsb);
+    load_tile16(tk, (const uint16_t*)p.k + r0 * BD, L, rsb);
+    load_tile16(tv, (const uint16_t*)p.v + r0 * BD, L, rsb);
+    TileF tdo;
+    load_tileF<DBF>(tdo, (const unsigned char*)bp.dout + r0 * BD * (DBF ? 2 : 4), L, rsbd);
+    float inv = 1.f, dden = 0.f;
+    if (NORM) {
+      const int j = tf_tok();
+      if (j < L) {
+        const float* tk2 = bp.tok + ((size_t)bh * p.T + (t0 + j)) * 2;
+        inv = tk2[0];
+        dden = tk2[1];
+      }
+    }
+    lds_barrier();
+    commit_feat<ELU, ELU>(tq, sh + BG::QH, sh + BG::QL, L);
+    commit_feat<ELU, ELU>(tk, sh + BG::KH, sh + BG::KL, L);
+    commit_raw(tv, sh + BG::V);
+    commit_scaled(tdo, inv, sh + BG::NH, sh + BG::NL);
+    if (tid < BC) {
+      const int j = tid;
+      sf[BG::TH + j] = DECAY ? exp2f((float)(j + 1) * lg) : 1.f;
+      sf[BG::XI + j] = j < L ? (DECAY ? exp2f((float)(L - 1 - j) * lg) : 1.f) : 0.f;
+    }
+    if (NORM && (tid & 3) == 0) sf[BG::DD + tf_tok()] = dden;
+    if (NORM && tid < BD) sf[BG::ZV + tid] = rz;
+    lds_barrier();
+
+    // A and Bm tiles (lower block triangle), hi + lo; jobs 0..2 are A, 3..5 are Bm
+    for (int job = w; job < 6; job += 4) {
+      if (job < 3) {
+        const int jt = job_jt(job), it = job_it(job);
+        const f32x16 acc = a_tile_acc<ELU>(sh, jt, it, lane);
+        const int i = 32 * it + (lane & 31);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = 32 * jt + dtile_row(r, lane);
+          const bf16_pair pr = split_bf16(acc[r] * dmask<DECAY>(j, i, lg));
+          sh[BG::AH + j * SQ + i] = pr.hi;
+          sh[BG::AL + j * SQ + i] = pr.lo;
+        }
+      } else {
+        const int jt = job_jt(job - 3), it = job_it(job - 3);
+        store_bm<DECAY, NORM, false>(sh, sf, x_tile_acc(sh, jt, it, lane), jt, it, L, lg, lane);
+      }
+    }
+    lds_barrier();
+
+    // dV = A^T dNum + xi (F R): rows i, column e = col
+    {
+      f32x16 a2[2] = {zero16(), zero16()};
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) {
+        bf16x8 rh[2], rl[2];
+        split_dtile(R[pt], rh, rl);
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+          for (int it = 0; it < 2; ++it) {
+            const bf16x8 kh = ld_cols8_perm(sh + BG::KH, TP, 32 * it, 32 * pt, q, lane);  // A[m=i][k=p]
+            a2[it] = mfma32(kh, rh[q], a2[it]);
+            a2[it] = mfma32(kh, rl[q], a2[it]);
+            if (ELU) a2[it] = mfma32(ld_cols8_perm(sh + BG::KL, TP, 32 * it, 32 * pt, q, lane), rh[q], a2[it]);
+          }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const __amdgpu_buffer_rsrc_t rdv = make_rsrc(bp.dv + r0 * BD, rows_extent(L, rsb4, BD * 4));
+#pragma unroll
+      for (int it = 0; it < 2; ++it) {
+        f32x16 a1 = zero16();
+#pragma unroll
+        for (int k0 = 32 * it; k0 < BC; k0 += 16) {
+          const bf16x8 ah = ld_rows8(sh + BG::AH, SQ, k0, 32 * it, lane);  // A[m=i][k=j] = A[j][i]
+          const bf16x8 al = ld_rows8(sh + BG::AL, SQ, k0, 32 * it, lane);
+          const bf16x8 nh = ld_rows8(sh + BG::NH, TP, k0, 32 * w, lane);  // B[k=j][n=e]
+          const bf16x8 nl = ld_rows8(sh + BG::NL, TP, k0, 32 * w, lane);
+          a1 = mfma32(ah, nh, a1);
+          a1 = mfma32(ah, nl, a1);
+          a1 = mfma32(al, nh, a1);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int i = 32 * it + dtile_row(r, lane);
+          const float g = a1[r] + sf[BG::XI + i] * a2[it][r];
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(g), rdv, (uint32_t)i * rsb4 + (uint32_t)col * 4, 0, 0);
+        }
+      }
+    }
+
+    // dF = Bm^T G + xi (V R^T + RZ): rows i, column p = col
+    __builtin_amdgcn_sched_barrier(0);
+    {
+      f32x16 a2[2] = {zero16(), zero16()};
+#pragma unroll
+      for (int et = 0; et < 4; ++et) {
+        bf16x8 th[2], tl[2];
+        split_dtile(RT[et], th, tl);
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+          for (int it = 0; it < 2; ++it) {
+            const bf16x8 va = ld_cols8_perm(sh + BG::V, TP, 32 * it, 32 * et, q, lane);  // A[m=i][k=e]
+            a2[it] = mfma32(va, th[q], a2[it]);
+            a2[it] = mfma32(va, tl[q], a2[it]);
+          }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const __amdgpu_buffer_rsrc_t rdk = make_rsrc(bp.dk + r0 * BD, rows_extent(L, rsb4, BD * 4));
+      const float rzp = NORM ? sf[BG::ZV + col] : 0.f;
+#pragma unroll
+      for (int it = 0; it < 2; ++it) {
+        f32x16 a1 = zero16();
+#pragma unroll
+        for (int k0 = 32 * it; k0 < BC; k0 += 16) {
+          const bf16x8 bmh = ld_rows8(sh + BG::BH, SQ, k0, 32 * it, lane);  // A[m=i][k=j] = Bm[j][i]
+          const bf16x8 bml = ld_rows8(sh + BG::BL, SQ, k0, 32 * it, lane);
+          const bf16x8 gq = ld_rows8(sh + BG::QH, TP, k0, 32 * w, lane);  // B[k=j][n=p] = G[j][p]
+          a1 = mfma32(bmh, gq, a1);
+          a1 = mfma32(bml, gq, a1);
+          if (ELU) a1 = mfma32(bmh, ld_rows8(sh + BG::QL, TP, k0, 32 * w, lane), a1);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int i = 32 * it + dtile_row(r, lane);
+          float g = a1[r] + sf[BG::XI + i] * (a2[it][r] + rzp);
+          if (ELU)
+            g *= dpsi_from_feat(from_bf16(sh[BG::KH + i * TP + col]) + from_bf16(sh[BG::KL + i * TP + col]));
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(g), rdk, (uint32_t)i * rsb4 + (uint32_t)col * 4, 0, 0);
+        }
+      }
+    }
+
+    // adjoint state before this step: R <- gamma^L R + (theta G)^T dNum, RT likewise
+    const float a = DECAY ? exp2f((float)L * lg) : 1.f;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      if (DECAY) {
+        R[t] *= a;
+        RT[t] *= a;
+      }
+#pragma unroll
+      for (int k0 = 0; k0 < BC; k0 += 16) {
+        const float* th = sf + BG::TH + k0 + 8 * (lane >> 5);
+        // R[p][e] += sum_j (theta_j G[j][p]) dNum[j][e]: tile pt = t, column e = col
+        {
+          const bf16x8 ga = ld_rows8(sh + BG::QH, TP, k0, 32 * t, lane);  // A[m=p][k=j]
+          const bf16x8 nh = ld_rows8(sh + BG::NH, TP, k0, 32 * w, lane);
+          const bf16x8 nl = ld_rows8(sh + BG::NL, TP, k0, 32 * w, lane);
+          if (DECAY) {
+            bf16x8 gh, gl;
+            scale_split<ELU>(ga, ELU ? ld_rows8(sh + BG::QL, TP, k0, 32 * t, lane) : ga, th, gh, gl);
+            R[t] = mfma32(gh, nh, R[t]);
+            R[t] = mfma32(gh, nl, R[t]);
+            R[t] = mfma32(gl, nh, R[t]);
+          } else {
+            R[t] = mfma32(ga, nh, R[t]);
+            R[t] = mfma32(ga, nl, R[t]);
+            if (ELU) R[t] = mfma32(ld_rows8(sh + BG::QL, TP, k0, 32 * t, lane), nh, R[t]);
+          }
+        }
+        // RT[e][p] += sum_j dNum[j][e] (theta_j G[j][p]): tile et = t, column p = col
+        {
+          const bf16x8 nh = ld_rows8(sh + BG::NH, TP, k0, 32 * t, lane);  // A[m=e][k=j] = dNum[j][e]
+          const bf16x8 nl = ld_rows8(sh + BG::NL, TP, k0, 32 * t, lane);
+          const bf16x8 gb = ld_rows8(sh + BG::QH, TP, k0, 32 * w, lane);  // B[k=j][n=p]
+          if (DECAY) {
+            bf16x8 gh, gl;
+            scale_split<ELU>(gb, ELU ? ld_rows8(sh + BG::QL, TP, k0, 32 * w, lane) : gb, th, gh, gl);
+            RT[t] = mfma32(nh, gh, RT[t]);
+            RT[t] = mfma32(nl, gh, RT[t]);
+            RT[t] = mfma32(nh, gl, RT[t]);
+          } else {
+            RT[t] = mfma32(nh, gb, RT[t]);
+            RT[t] = mfma32(nl, gb, RT[t]);
+            if (ELU) RT[t] = mfma32(nh, ld_rows8(sh + BG::QL, TP, k0, 32 * w, lane), RT[t]);
+          }
+        }
+      }
+    }
+    if (NORM && tid < BD) {
+      float zn = a * rz;
+      for (int j = 0; j < L; ++j) {
+        const float g = from_bf16(sh[BG::QH + j * TP + tid]) + (ELU ? from_bf16(sh[BG::QL + j * TP + tid]) : 0.f);
+        zn += sf[BG::TH + j] * g * sf[BG::DD + j];
+      }
+      rz = zn;
+    }
+  }
+}
+
+template <bool ELU, bool DECAY, bool NORM, bool DBF>
+hipError_t launch4(const BackwardParams& p, hipStream_t s, bool key_sweep) {
+  const void* kern = key_sweep ? (const void*)k_bwd_key<ELU, DECAY, NORM, DBF>
+                               : (const void*)k_bwd_query<ELU, DECAY, NORM, DBF>;
+  hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, BG::BYTES);
+  if (e != hipSuccess) return e;
+  dim3 grid(p.f.B * p.f.H, p.f.n_seg);  // sequences on x: every XCD gets all segments of its sequences
+  void* args[] = {(void*)&p};
+  e = hipLaunchKernel(kern, grid, dim3(BNT), args, BG::BYTES, s);
+  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+template <bool ELU, bool DECAY>
+hipError_t launch2(const BackwardParams& p, hipStream_t s, bool key_sweep) {
+  const bool norm = p.f.normalize != 0, dbf = p.dout_bf16 != 0;
+  if (norm) return dbf ? launch4<ELU, DECAY, true, true>(p, s, key_sweep) : launch4<ELU, DECAY, true, false>(p, s, key_sweep);
+  return dbf ? launch4<ELU, DECAY, false, true>(p, s, key_sweep) : launch4<ELU, DECAY, false, false>(p, s, key_sweep);
+}
+
+}  // namespace
+
+bool prefill_backward_supported(int C, int d_k, int d_v, int n_psi, int psi) {
+  if (psi != LA_PSI_IDENTITY && psi != LA_PSI_ELU1) return false;
+  if (d_k != BD || d_v != BD || n_psi != BD) return false;
+  return C == 64 || C == 128;  // segments are whole multiples of the 64-token step
+}
+
+hipError_t launch_prefill_backward(const BackwardParams& p, hipStream_t s, bool key_sweep) {
+  const bool elu = p.f.psi == LA_PSI_ELU1, decay = p.f.has_decay != 0;
+  if (elu) return decay ? launch2<true, true>(p, s, key_sweep) : launch2<true, false>(p, s, key_sweep);
+  return decay ? launch2<false, true>(p, s, key_sweep) : launch2<false, false>(p, s, key_sweep);
+}
+
+}  // namespace la

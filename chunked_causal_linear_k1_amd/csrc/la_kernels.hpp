@@ -60,8 +60,23 @@ struct ScanParams {
   int n_psi, d_v;
   int n_seg, seg_len;    // segment length in tokens (the last one may be short)
   int gated;             // 1: per-row decays stored after each segment's S and Z (gated prefill)
+  int reverse;           // 1: scan the segments from the last to the first (the adjoint state of
+                         // the backward pass); the prefix of segment s then folds segments > s
   int has_decay;
   float log2g[LA_MAX_DECAY_HEADS];
+};
+
+// Backward pass of the prefill: the forward problem plus the upstream gradient, the gradient
+// outputs and three workspace regions.
+struct BackwardParams {
+  PrefillParams f;       // q, k, v, spans, chunking, decay (f.ws: the forward segment prefixes)
+  const void* dout;      // dL/do, rows like o, dout_bf16 ? bf16 : fp32
+  float* dq;             // fp32, rows like q
+  float* dk;             // fp32, rows like k
+  float* dv;             // fp32, rows like v
+  float* rev;            // [BH, n_seg, E] segment summaries of the adjoint state, then their reverse prefixes
+  float* tok;            // [BH, T, 2]: 1/den and dden per token (normalize only)
+  int dout_bf16;
 };
 
 struct DecodeParams {
@@ -127,6 +142,9 @@ hipError_t launch_segment_scan(const ScanParams& p, hipStream_t s);
 
 bool prefill_gated_supported(int C, int d_k, int d_v, int n_psi, int psi);
 hipError_t launch_prefill_gated(const PrefillParams& p, hipStream_t s, bool out);
+
+bool prefill_backward_supported(int C, int d_k, int d_v, int n_psi, int psi);
+hipError_t launch_prefill_backward(const BackwardParams& p, hipStream_t s, bool key_sweep);
 
 bool decode_supported(int d_k, int d_v, int n_psi, int psi);
 hipError_t launch_decode_step(const DecodeParams& p, hipStream_t s);

@@ -9,6 +9,11 @@
 // X_s with init (+) X_0 (+) ... (+) X_{s-1} and writes init (+) X_0 (+) ... as the
 // final state.
 //
+// With `reverse` the segment order is reversed: segment s receives the fold of segments
+// n_seg-1, ..., s+1 (each decayed by the segments between it and s) and the final state is
+// the fold of all of them. This is the adjoint state of the backward pass, which gathers
+// every later read of a state and decays the same way on its way back.
+//
 // The state elements (n_psi*d_v + n_psi per sequence) are independent. A workgroup
 // takes 256 consecutive elements (4 per lane, 16-byte accesses) and spreads the segment
 // axis over W waves: each wave folds its run of segments (holding the run in registers
@@ -44,6 +49,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_segment_scan(ScanParams p) {
   const size_t e = ((size_t)blockIdx.x * 64 + lane) * 4;
   const bool live = e < E;
   const float lg = p.has_decay ? p.log2g[head] : 0.f;
+  // scan position i is segment seg_of(i): the same segment in forward order, mirrored in reverse
+  auto seg_of = [&](int i) -> int { return p.reverse ? p.n_seg - 1 - i : i; };
   float* base = p.ws + (size_t)bh * p.n_seg * REC + e;
   // the state rows of this lane's 4 elements: one row (S part, d_v a multiple of 4) or four
   // consecutive rows (Z part); their decays under per-row gates
@@ -78,19 +85,19 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_segment_scan(ScanParams p) {
   if (RUN > 0) {
 #pragma unroll
     for (int i = 0; i < (RUN > 0 ? RUN : 1); ++i)
-      run[i] = (live && s0 + i < s1) ? ld4(base + (size_t)(s0 + i) * REC) : f32x4{0.f, 0.f, 0.f, 0.f};
+      run[i] = (live && s0 + i < s1) ? ld4(base + (size_t)seg_of(s0 + i) * REC) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < (RUN > 0 ? RUN : 1); ++i) {
       if (s0 + i < s1) {
-        const f32x4 as = seg_decay(s0 + i);
+        const f32x4 as = seg_decay(seg_of(s0 + i));
         tx = as * tx + run[i];
         ta *= as;
       }
     }
   } else {
     for (int s = s0; s < s1; ++s) {
-      const f32x4 as = seg_decay(s);
-      if (live) tx = as * tx + ld4(base + (size_t)s * REC);
+      const f32x4 as = seg_decay(seg_of(s));
+      if (live) tx = as * tx + ld4(base + (size_t)seg_of(s) * REC);
       ta *= as;
     }
   }
@@ -161,17 +168,17 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_segment_scan(ScanParams p) {
 #pragma unroll
     for (int i = 0; i < (RUN > 0 ? RUN : 1); ++i) {
       if (s0 + i < s1) {
-        const f32x4 as = seg_decay(s0 + i);
-        if (live) st4(base + (size_t)(s0 + i) * REC, cx);
+        const f32x4 as = seg_decay(seg_of(s0 + i));
+        if (live) st4(base + (size_t)seg_of(s0 + i) * REC, cx);
         cx = as * cx + run[i];
       }
     }
   } else {
     for (int s = s0; s < s1; ++s) {
-      const f32x4 as = seg_decay(s);
+      const f32x4 as = seg_decay(seg_of(s));
       if (live) {
-        const f32x4 xs = ld4(base + (size_t)s * REC);
-        st4(base + (size_t)s * REC, cx);
+        const f32x4 xs = ld4(base + (size_t)seg_of(s) * REC);
+        st4(base + (size_t)seg_of(s) * REC, cx);
         cx = as * cx + xs;
       }
     }

@@ -78,6 +78,13 @@ def make_log_gates(shape, seed: int, temp: float = 16.0, device: str = "cpu") ->
     return torch.nn.functional.logsigmoid(z) / temp
 
 
+def make_upstream_grad(shape, seed: int, device: str = "cpu", dtype: torch.dtype = torch.float32) -> torch.Tensor:
+    """dL/do for a backward pass: N(0, 1) drawn in fp32 from a seeded generator, then stored in dtype."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    return torch.randn(shape, generator=gen, device=device, dtype=torch.float32).to(dtype)
+
+
 def varlen_lengths(w) -> List[int]:
     """The sequence lengths of a VarlenWorkload: uniform in [len_min, len_max], seeded."""
     rng = np.random.default_rng(w.seed)

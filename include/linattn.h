@@ -224,6 +224,36 @@ la_status lin_attn_prefill_gated(const la_prefill_desc* d, const void* q, const 
                                  float* final_S, float* final_Z, void* workspace, size_t workspace_bytes,
                                  hipStream_t stream);
 
+/*
+ * Backward pass of lin_attn_prefill: for L = sum_t dout_t . o_t, the gradients of L with
+ * respect to q, k, v and the initial state of the same prefill (same d, q, k, v, gamma,
+ * init_S, init_Z). Two sweeps ("Linearized 2-Simplicial Attention", 4.2 Custom Triton
+ * kernel, Backward, and the appendix's backward query and state sweeps): a query sweep that
+ * recomputes the prefix state (and, with a denominator, dout_t . o_t from it, so no forward
+ * output is needed) and gives dq, then a state sweep over the adjoint state
+ * R_t = sum_{u >= t} gamma^(u-t) psi(q_u) dnum_u^T (dnum_u = dout_u / den_u) that gives dk and dv;
+ * across segments the adjoint state is the forward scan's monoid run in reverse order.
+ * gamma, eps and the feature map are constants (no gradient for them).
+ *
+ *   d         as for lin_attn_prefill; supported: in_dtype LA_BF16, psi identity or elu1,
+ *             d_k == d_v == n_psi == 128, chunk 64 or 128 (walked in steps of 64 tokens:
+ *             the gradient does not depend on the grouping), either layout. out_dtype is
+ *             the type of dout (LA_F32 or LA_BF16).
+ *   dout      device, dL/do, laid out like lin_attn_prefill's o, out_dtype
+ *   dq, dk    device fp32, laid out like q and k
+ *   dv        device fp32, laid out like v
+ *   dinit_S   device fp32 [B, H, n_psi, d_v] or NULL; dinit_Z [B, H, n_psi] or NULL (not
+ *             written when normalize == 0)
+ *   workspace at least lin_attn_prefill_backward_workspace_size bytes (two segment-summary
+ *             regions, plus 8 bytes per token-head when normalize == 1)
+ * Errors as for lin_attn_prefill. Rows past T are neither read nor written.
+ */
+la_status lin_attn_prefill_backward_workspace_size(const la_prefill_desc* d, size_t* bytes);
+la_status lin_attn_prefill_backward(const la_prefill_desc* d, const void* q, const void* k, const void* v,
+                                    const float* gamma, const float* init_S, const float* init_Z, const void* dout,
+                                    float* dq, float* dk, float* dv, float* dinit_S, float* dinit_Z,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Batched single-token decode description: N independent streams x H heads. */
 typedef struct {
   int32_t N, H;

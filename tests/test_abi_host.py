@@ -213,6 +213,43 @@ def test_gated_validation_and_workspace():
                                           None) == LA_ERR_NULL
 
 
+def test_backward_validation_and_workspace():
+    """Host-side checks of lin_attn_prefill_backward: supported shapes, workspace size, NULL and
+    alignment errors and a gamma outside (0, 1] are all reported before anything is launched."""
+    lib = binding.load()
+
+    def ws(**kw):
+        n = ctypes.c_size_t(0)
+        st = lib.lin_attn_prefill_backward_workspace_size(ctypes.byref(_desc(**kw)), ctypes.byref(n))
+        return st, n.value
+    base = dict(B=2, H=4, T=1000, chunk=64, psi=1, normalize=1)
+    st, n = ws(**base)
+    assert st == LA_OK
+    fwd = ctypes.c_size_t(0)
+    assert lib.lin_attn_prefill_workspace_size(ctypes.byref(_desc(**base)), ctypes.byref(fwd)) == LA_OK
+    # two segment-record regions plus 1/den and dden per token-head
+    assert n == 2 * fwd.value + 2 * 4 * 1000 * 8
+    st0, n0 = ws(**{**base, "normalize": 0})
+    assert st0 == LA_OK and n0 == 2 * fwd.value
+    assert ws(**{**base, "chunk": 128, "psi": 0})[0] == LA_OK
+    assert ws(**{**base, "layout": 1})[0] == LA_OK
+    for kw in (dict(chunk=32), dict(psi=2, n_psi=256), dict(d_k=64, d_v=64, n_psi=64), dict(in_dtype=LA_F32),
+               dict(psi=3, n_psi=256)):
+        assert ws(**{**base, **kw})[0] == LA_ERR_UNSUPPORTED, kw
+    d = _desc(**base)
+    fake, odd = ctypes.c_void_p(1 << 20), ctypes.c_void_p((1 << 20) + 4)
+
+    def call(q=fake, dout=fake, dq=fake, w=fake, gamma=None, size=n):
+        return lib.lin_attn_prefill_backward(ctypes.byref(d), q, fake, fake, gamma, None, None, dout, dq, fake, fake,
+                                             None, None, w, size, None)
+    assert call(q=None) == LA_ERR_NULL
+    assert call(dout=None) == LA_ERR_NULL
+    assert call(dq=odd) == LA_ERR_ALIGN
+    assert call(w=None) == LA_ERR_WORKSPACE
+    assert call(size=n - 16) == LA_ERR_WORKSPACE
+    assert call(gamma=(ctypes.c_float * 4)(1.0, 0.5, 0.0, 1.0)) == LA_ERR_VALUE
+
+
 def test_decode_validation():
     lib = binding.load()
     fake = ctypes.c_void_p(1 << 20)

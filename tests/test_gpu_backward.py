@@ -1,0 +1,149 @@
+"""GPU parity of the backward pass (lin_attn_prefill_backward, through the C ABI) against the
+fp64 backward oracle (oracle.prefill_backward, the adjoint of the token loop, pinned on the CPU).
+
+Cases span both sweeps' paths: identity features with per-head decay and no denominator (the
+retention form), elu+1 with and without decay and a denominator, identity with a denominator
+(non-negative q and k, so the denominator is a positive sum), chunk 64 and 128, ragged tails,
+sequences shorter than one step, many segments (the reverse scan), long segments of many steps,
+initial states (and their gradients), bf16 upstream gradients and the [B, T, H, d] layout.
+
+Tolerances: those of the forward pass for bf16 inputs (rel-L2 <= 2e-3), with max-abs applied
+after scaling by the largest reference magnitude: gradients have no fixed scale (a query's
+gradient grows with the state it reads).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from chunked_causal_linear_k1_amd import binding, inputs
+from chunked_causal_linear_k1_amd.workloads import PSI_ELU1, PSI_IDENTITY, Workload
+
+from gpu_common import BF16_MAX_ABS, BF16_REL_L2, announce, metrics
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _check(got, ref, label):
+    rel, mx = metrics(got, ref)
+    scale = max(float(np.abs(ref).max()), 1e-30)
+    print(f"[parity] {label} rel_l2={rel:.3e} max_abs/scale={mx / scale:.3e} scale={scale:.3e}", flush=True)
+    assert rel <= BF16_REL_L2 and mx <= BF16_MAX_ABS * scale, f"{label}: rel_l2={rel:.3e} max_abs/scale={mx / scale:.3e}"
+
+
+def _workload(psi, normalize, decay, B, H, T, C, seed):
+    scale = 128 ** -0.5 if psi == PSI_IDENTITY else 0.5
+    return Workload(name="bwd", B=B, H=H, T=T, d_k=128, d_v=128, n_psi=128, chunk=C, psi=psi, normalize=normalize,
+                    eps=1e-6, dtype="bf16", seed=seed, qk_scale=scale, v_scale=1.0, decay=decay)
+
+
+def _prefix_state(w, inp, T0, seed):
+    """The state after a seeded T0-token prefix (oracle), as a hand-off would give it."""
+    gen = torch.Generator().manual_seed(seed)
+    k0 = (torch.randn((w.B, w.H, T0, w.d_k), generator=gen) * w.qk_scale).to(torch.bfloat16)
+    v0 = torch.randn((w.B, w.H, T0, w.d_v), generator=gen).to(torch.bfloat16)
+    if w.psi == PSI_IDENTITY and w.normalize:
+        k0 = k0.abs()
+    g = inp["gamma"]
+    _, S, Z = oracle.prefill(None, k0, v0, w.psi, gamma=None if g is None else np.repeat(g[None], w.B, 0),
+                             normalize=w.normalize, want_state=True)
+    return S, Z
+
+
+# name, psi, normalize, decay, B, H, T, C, init state, dout dtype, layout
+CASES = [
+    ("retention_decay", PSI_IDENTITY, 0, "retnet_spread", 1, 4, 300, 64, False, "f32", "bhtd"),
+    ("retention_c128_state", PSI_IDENTITY, 0, "const:0.99", 1, 2, 1000, 128, True, "f32", "bhtd"),
+    ("elu1_norm", PSI_ELU1, 1, "none", 2, 2, 333, 64, False, "f32", "bhtd"),
+    ("elu1_norm_decay_state", PSI_ELU1, 1, "const:0.995", 1, 3, 517, 64, True, "f32", "bhtd"),
+    ("identity_norm_nonneg", PSI_IDENTITY, 1, "const:0.98", 1, 2, 257, 64, False, "f32", "bhtd"),
+    ("elu1_short", PSI_ELU1, 1, "none", 1, 2, 37, 64, False, "f32", "bhtd"),
+    ("elu1_bf16_dout_bthd", PSI_ELU1, 1, "const:0.99", 2, 3, 200, 128, True, "bf16", "bthd"),
+    ("retention_bthd_bf16", PSI_IDENTITY, 0, "retnet_spread", 1, 4, 450, 64, False, "bf16", "bthd"),
+]
+
+
+def _run(case):
+    name, psi, normalize, decay, B, H, T, C, with_state, dt, layout = case
+    w = _workload(psi, normalize, decay, B, H, T, C, seed=100 + [c[0] for c in CASES].index(name))
+    announce(f"backward {name} B={B} H={H} T={T} C={C} layout={layout}")
+    inp = inputs.make_prefill_inputs(w)
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    if psi == PSI_IDENTITY and normalize:
+        q, k = q.abs(), k.abs()
+    ddt = torch.float32 if dt == "f32" else torch.bfloat16
+    dout = inputs.make_upstream_grad((B, H, T, 128), w.seed + 11, dtype=ddt)
+    g = inp["gamma"]
+    gam = None if g is None else list(g)
+    S0 = Z0 = None
+    if with_state:
+        S0, Z0 = _prefix_state(w, inp, 96, w.seed + 5)
+    tr = (lambda x: x.transpose(1, 2).contiguous()) if layout == "bthd" else (lambda x: x.contiguous())
+    qd, kd, vd, dod = (tr(x).to(DEV) for x in (q, k, v, dout))
+    kw = dict(psi=psi, chunk=C, normalize=normalize, eps=w.eps, gamma=gam, layout=layout)
+    S0d = None if S0 is None else torch.from_numpy(S0).float().to(DEV)
+    Z0d = None if Z0 is None else torch.from_numpy(Z0).float().to(DEV)
+    dS0 = torch.zeros((B, H, 128, 128), device=DEV) if with_state else None
+    dZ0 = torch.zeros((B, H, 128), device=DEV) if with_state else None
+    dq, dk, dv = binding.lin_attn_prefill_backward(qd, kd, vd, dod, init_S=S0d, init_Z=Z0d, dinit_S=dS0,
+                                                   dinit_Z=dZ0, **kw)
+    torch.cuda.synchronize()
+    untr = (lambda x: x.transpose(1, 2)) if layout == "bthd" else (lambda x: x)
+    got = [untr(x.cpu()).numpy() for x in (dq, dk, dv)]
+    # the oracle takes S0 / Z0 as the same fp32 values the GPU received
+    S0r = None if S0 is None else S0d.cpu().double().numpy()
+    Z0r = None if Z0 is None else Z0d.cpu().double().numpy()
+    ref = oracle.prefill_backward(q, k, v, dout, psi, gamma=None if g is None else np.repeat(g[None], B, 0),
+                                  normalize=normalize, eps=w.eps, S0=S0r, Z0=Z0r)
+    for lab, a, b in zip(("dq", "dk", "dv"), got, ref[:3]):
+        _check(a, b, f"{name} {lab}")
+    if with_state:
+        _check(dS0.cpu().numpy(), ref[3], f"{name} dS0")
+        if normalize:
+            _check(dZ0.cpu().numpy(), ref[4], f"{name} dZ0")
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_backward_matches_oracle(case):
+    _run(case)
+
+
+@pytest.mark.parametrize("psi,normalize,decay", [(PSI_IDENTITY, 0, "retnet_spread"), (PSI_ELU1, 1, "const:0.999")])
+def test_backward_long_segments(psi, normalize, decay):
+    """B*H = 256 sequences of 4100 tokens: segments of 2048 tokens (32 steps each) and a ragged
+    third one; sampled heads against the oracle (each head's gradients depend on its own inputs)."""
+    B, H, T = 2, 128, 4100
+    w = _workload(psi, normalize, decay, B, H, T, 64, seed=21)
+    announce(f"backward long segments psi={psi} norm={normalize} B={B} H={H} T={T}")
+    inp = inputs.make_prefill_inputs(w, device=DEV)
+    dout = inputs.make_upstream_grad((B, H, T, 128), 31, device=DEV)
+    g = inp["gamma"]
+    kw = dict(psi=psi, chunk=64, normalize=normalize, eps=w.eps, gamma=None if g is None else list(g))
+    dq, dk, dv = binding.lin_attn_prefill_backward(inp["q"], inp["k"], inp["v"], dout, **kw)
+    torch.cuda.synchronize()
+    for b, h in ((0, 0), (1, 77), (1, 127)):
+        ref = oracle.prefill_backward(inp["q"][b, h].cpu(), inp["k"][b, h].cpu(), inp["v"][b, h].cpu(),
+                                      dout[b, h].cpu(), psi, gamma=None if g is None else [g[h]],
+                                      normalize=normalize, eps=w.eps)
+        for lab, a, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref[:3]):
+            _check(a[b, h].cpu().numpy(), r, f"long b={b} h={h} {lab}")
+
+
+def test_backward_chunk_invariance():
+    """chunk 64 and chunk 128 describe the same function: their gradients agree to rounding."""
+    w = _workload(PSI_ELU1, 1, "const:0.99", 1, 2, 700, 64, seed=3)
+    announce("backward chunk 64 vs 128")
+    inp = inputs.make_prefill_inputs(w, device=DEV)
+    dout = inputs.make_upstream_grad((1, 2, 700, 128), 4, device=DEV)
+    res = []
+    for C in (64, 128):
+        kw = dict(psi=PSI_ELU1, chunk=C, normalize=1, eps=w.eps, gamma=list(inp["gamma"]))
+        res.append(binding.lin_attn_prefill_backward(inp["q"], inp["k"], inp["v"], dout, **kw))
+    torch.cuda.synchronize()
+    for lab, a, b in zip(("dq", "dk", "dv"), res[0], res[1]):
+        rel, _ = metrics(a.cpu().numpy(), b.cpu().numpy())
+        assert rel < 1e-3, (lab, rel)
