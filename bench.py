@@ -150,6 +150,36 @@ def bench_gated(w: workloads.Workload, steps: int, warmup: int):
     return res
 
 
+def bench_backward(w: workloads.Workload, steps: int, warmup: int):
+    """Whole lin_attn_prefill_backward calls (forward summaries, scan, query sweep, reverse scan,
+    state sweep) for an upstream gradient of o's shape, event-timed on the current stream."""
+    log(f"backward {w.name}: generating inputs and the upstream gradient on the GPU")
+    inp = inputs.make_prefill_inputs(w, device="cuda")
+    dout = inputs.make_upstream_grad((w.B, w.H, w.T, w.d_v), w.seed + 11, device="cuda")
+    g = inp["gamma"]
+    desc = binding.prefill_desc(w.B, w.H, w.T, w.d_k, w.d_v, w.n_psi, w.chunk, w.psi, w.normalize, w.eps,
+                                binding.LA_BF16, binding.LA_F32)
+    ws = torch.empty(binding.backward_workspace_size(desc), dtype=torch.uint8, device="cuda")
+    grads = [torch.empty((w.B, w.H, w.T, d), dtype=torch.float32, device="cuda") for d in (w.d_k, w.d_k, w.d_v)]
+    kw = dict(psi=w.psi, chunk=w.chunk, normalize=w.normalize, eps=w.eps, gamma=None if g is None else list(g),
+              dq=grads[0], dk=grads[1], dv=grads[2], workspace=ws)
+    for _ in range(warmup):
+        binding.lin_attn_prefill_backward(inp["q"], inp["k"], inp["v"], dout, **kw)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        binding.lin_attn_prefill_backward(inp["q"], inp["k"], inp["v"], dout, **kw)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    res = {"ms_per_step": ms, "token_heads_per_s": w.token_heads / (ms * 1e-3), "units": w.token_heads}
+    del inp, dout, ws, grads
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_varlen(w: workloads.VarlenWorkload, steps: int, warmup: int):
     """Whole lin_attn_prefill_varlen calls on a packed batch, event-timed on the current stream."""
     log(f"prefill {w.name}: generating packed inputs on the GPU")
@@ -282,7 +312,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--no-extra", action="store_true", help="headline workload only (no 8k elu+1, PRF, layout, bf16-output, gated and packed-batch lines)")
+    ap.add_argument("--no-extra", action="store_true", help="headline workload only (no 8k elu+1, PRF, layout, bf16-output, gated, backward and packed-batch lines)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="first run one plain copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -380,6 +410,16 @@ def main():
                                     "whole_call_hbm": {"achieved": round(gb, 1), "peak": HBM_PEAK_GBS,
                                                        "unit": "GB/s", "frac": round(gb / HBM_PEAK_GBS, 4),
                                                        "bytes_per_token_head": gbytes}}
+        # backward: compulsory bytes per token-head (q, k, v bf16 and dout fp32 read; dq, dk, dv fp32 written)
+        bwd_bytes = 3 * 128 * 2 + 128 * 4 + 3 * 128 * 4
+        for key, bw in (("backward_8k", workloads.PREFILL_8K), ("backward_128k", workloads.RETNET_128K)):
+            pb = bench_backward(bw, args.steps, args.warmup)
+            ab = bwd_bytes * pb["units"] / (pb["ms_per_step"] * 1e-3) / 1e9
+            line[key] = {"workload": bw.name, "token_heads_per_s": round(pb["token_heads_per_s"], 1),
+                         "ms_per_step": round(pb["ms_per_step"], 4),
+                         "whole_call_roofline": {"bound": "hbm", "achieved": round(ab, 1), "peak": HBM_PEAK_GBS,
+                                                 "unit": "GB/s", "frac": round(ab / HBM_PEAK_GBS, 4),
+                                                 "bytes_per_token_head": bwd_bytes}}
         vw = workloads.VARLEN_32
         pv = bench_varlen(vw, args.steps, args.warmup)
         av = BYTES_PER_TOKEN_HEAD * pv["units"] / (pv["ms_per_step"] * 1e-3) / 1e9
