@@ -296,7 +296,7 @@ def gated_workspace_size(desc: PrefillDesc) -> int:
 
 
 def lin_attn_prefill_gated(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_gate: torch.Tensor, *,
-                           psi: int, chunk: int = 16, normalize: int = 0, eps: float = 1e-6,
+                           psi: int, chunk: int = 32, normalize: int = 0, eps: float = 1e-6,
                            init_S: Optional[torch.Tensor] = None, init_Z: Optional[torch.Tensor] = None,
                            o: Optional[torch.Tensor] = None, final_S: Optional[torch.Tensor] = None,
                            final_Z: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,

@@ -15,17 +15,23 @@
 // it is <= 0 whatever the gates: nothing overflows. Segments combine as
 // (a1, X1) (+) (a2, X2) = (a1 a2, diag(a2) X1 + X2) with vector a (the scan, la_scan.hip).
 //
-// This path runs in fp32 on the vector ALUs: the gate factors make every operand inexact
-// in bf16. Chunks of 16 tokens; each thread keeps an 8 x 8 block of the state in
-// registers (rows 8 pb.., columns 8 eb..; the pb lanes of a column block are adjacent,
-// so the sums over state rows reduce across 16 (or 8) consecutive lanes).
+// Two implementations, both with chunks of 32 tokens:
+//  - bf16 inputs: the state terms on MFMA (outputs psi(q_j) e^{G_j} S_prev and the update
+//    psi(k_i) e^{G - G_i} v_i^T, both factors carried as bf16 hi + lo), the intra-chunk
+//    scores A on the vector ALUs as running products of the gates (for a fixed key i the
+//    factor exp(G_j - G_i) is the product of the gates of tokens i+1..j, so it is built by
+//    one multiply per token with every factor <= 1: no exponential per pair, no overflow).
+//  - fp32 inputs: fp32 on the vector ALUs throughout (the fp32 tolerance leaves no room for
+//    two-term bf16 products); each thread keeps an 8 x 8 block of the state in registers
+//    (rows 8 pb.., columns 8 eb..; the pb lanes of a column block are adjacent, so the sums
+//    over state rows reduce across 16 (or 8) consecutive lanes).
 #include "la_device.hpp"
 #include "la_kernels.hpp"
 
 namespace la {
 namespace {
 
-constexpr int GC = 16;  // chunk
+constexpr int GC = 32;  // chunk
 
 template <int NP, int DV>
 struct GlaGeo {
@@ -294,6 +300,355 @@ __global__ __launch_bounds__((GlaGeo<NP, DV>::NT)) void k_output_gla(PrefillPara
   }
 }
 
+// ======================= bf16 inputs: state terms on MFMA ===============================
+
+// LDS image of the MFMA kernels (D = n_psi = d_k = d_v). bf16 tiles have pitch D + 8.
+template <int D>
+struct MGeo {
+  static constexpr int NT = 2 * D, NW = D / 32, P = D + 8, AP = GC + 8;
+  // fp32 regions (float offsets)
+  static constexpr int PQ = 0;              // psi(q) [GC][D]
+  static constexpr int PK = PQ + GC * D;    // psi(k) [GC][D]
+  static constexpr int AL = PK + GC * D;    // log gates, then the gates exp(log_gate) [GC][D]
+  static constexpr int APART = AL + GC * D; // score partials [NW][GC][GC]
+  static constexpr int AEND = APART + NW * GC * GC;  // exp(G) [D]
+  static constexpr int ZV = AEND + D;       // Z_prev [D]
+  static constexpr int DEN = ZV + D;        // [GC]
+  static constexpr int FEND = DEN + GC;
+  // bf16 regions (element offsets from the end of the fp32 image)
+  static constexpr int H0 = 2 * FEND;
+  static constexpr int QH = H0, QL = QH + GC * P, KH = QL + GC * P, KL = KH + GC * P, V = KL + GC * P;
+  static constexpr int SAH = V + GC * P, SAL = SAH + GC * AP;  // A hi / lo [GC][AP]
+  static constexpr int HEND = SAL + GC * AP;
+  static constexpr int BYTES = HEND * 2;
+  static_assert(FEND % 4 == 0 && (GC * P) % 8 == 0 && (GC * AP) % 8 == 0, "16-byte aligned regions");
+};
+
+// Global tile of GC token rows x D bf16 (16-byte pieces) / fp32 log gates.
+template <int D>
+struct MLoad {
+  static constexpr int NT = 2 * D;
+  static constexpr int PB = GC * D / 8 / NT;   // bf16 pieces per thread per tensor (2)
+  static constexpr int PF = GC * D / 4 / NT;   // fp32 pieces per thread (4)
+  uint4 q[PB], k[PB], v[PB];
+  uint4 g[PF];
+};
+template <int D>
+__device__ __forceinline__ void mload(MLoad<D>& T, const PrefillParams& p, long long r0, int L) {
+  constexpr int NT = 2 * D, RP = D / 8, RPF = D / 4;  // pieces per row
+  const uint32_t rsb = (uint32_t)p.tok_rows * D * 2, rsf = (uint32_t)p.tok_rows * D * 4;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc((const uint16_t*)p.q + r0 * D, rows_extent(L, rsb, D * 2));
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const uint16_t*)p.k + r0 * D, rows_extent(L, rsb, D * 2));
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const uint16_t*)p.v + r0 * D, rows_extent(L, rsb, D * 2));
+  const __amdgpu_buffer_rsrc_t rg = make_rsrc(p.log_gate + r0 * D, rows_extent(L, rsf, D * 4));
+#pragma unroll
+  for (int i = 0; i < MLoad<D>::PB; ++i) {
+    const int pc = threadIdx.x + i * NT, row = pc / RP, col = (pc % RP) * 8;
+    const uint32_t off = (uint32_t)row * rsb + (uint32_t)col * 2;
+    T.q[i] = buf_load16(rq, off);
+    T.k[i] = buf_load16(rk, off);
+    T.v[i] = buf_load16(rv, off);
+  }
+#pragma unroll
+  for (int i = 0; i < MLoad<D>::PF; ++i) {
+    const int pc = threadIdx.x + i * NT, row = pc / RPF, col = (pc % RPF) * 4;
+    T.g[i] = buf_load16(rg, (uint32_t)row * rsf + (uint32_t)col * 4);
+  }
+}
+
+// Commit: psi(q), psi(k) as fp32 (rows >= L zero), log gates (rows >= L zero: gate 1), v.
+template <int D, bool Q>
+__device__ __forceinline__ void mcommit(const MLoad<D>& T, float* sf, __bf16* sh, int L, bool elu) {
+  using G = MGeo<D>;
+  constexpr int NT = 2 * D, RP = D / 8, RPF = D / 4;
+#pragma unroll
+  for (int i = 0; i < MLoad<D>::PB; ++i) {
+    const int pc = threadIdx.x + i * NT, row = pc / RP, col = (pc % RP) * 8;
+    const bf16x8 kx = __builtin_bit_cast(bf16x8, T.k[i]);
+    f32x4 k0, k1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float a = from_bf16(kx[j]), b = from_bf16(kx[4 + j]);
+      k0[j] = row < L ? (elu ? elu1(a) : a) : 0.f;
+      k1[j] = row < L ? (elu ? elu1(b) : b) : 0.f;
+    }
+    *(f32x4*)(sf + G::PK + row * D + col) = k0;
+    *(f32x4*)(sf + G::PK + row * D + col + 4) = k1;
+    if (Q) {
+      const bf16x8 qx = __builtin_bit_cast(bf16x8, T.q[i]);
+      f32x4 q0, q1;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float a = from_bf16(qx[j]), b = from_bf16(qx[4 + j]);
+        q0[j] = row < L ? (elu ? elu1(a) : a) : 0.f;
+        q1[j] = row < L ? (elu ? elu1(b) : b) : 0.f;
+      }
+      *(f32x4*)(sf + G::PQ + row * D + col) = q0;
+      *(f32x4*)(sf + G::PQ + row * D + col + 4) = q1;
+    }
+    *(uint4*)(sh + G::V + row * G::P + col) = T.v[i];
+  }
+#pragma unroll
+  for (int i = 0; i < MLoad<D>::PF; ++i) {
+    const int pc = threadIdx.x + i * NT, row = pc / RPF, col = (pc % RPF) * 4;
+    const f32x4 g = __builtin_bit_cast(f32x4, T.g[i]);
+    *(f32x4*)(sf + G::AL + row * D + col) = row < L ? g : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+}
+
+// Per feature p (threads p < D): G_j = cumulative log gate, k^_i = psi(k_i) e^{G_end - G_i}
+// (hi + lo), and with Q also q^_j = psi(q_j) e^{G_j} (hi + lo) and the gates exp(log_gate)
+// in place of the log gates. Returns G_end (this feature's summed log gate over the chunk)
+// and adds sum_i k^_i to *ksum.
+template <int D, bool Q>
+__device__ __forceinline__ float feature_pass(float* sf, __bf16* sh, float* ksum) {
+  using G = MGeo<D>;
+  const int p = threadIdx.x;
+  float g[GC];
+  float c = 0.f;
+#pragma unroll
+  for (int j = 0; j < GC; ++j) {
+    const float lg = sf[G::AL + j * D + p];
+    c += lg;
+    g[j] = c;
+    if (Q) {
+      sf[G::AL + j * D + p] = __expf(lg);
+      const bf16_pair pr = split_bf16(sf[G::PQ + j * D + p] * __expf(c));
+      sh[G::QH + j * G::P + p] = pr.hi;
+      sh[G::QL + j * G::P + p] = pr.lo;
+    }
+  }
+  float ks = 0.f;
+#pragma unroll
+  for (int i = 0; i < GC; ++i) {
+    const float kh = sf[G::PK + i * D + p] * __expf(c - g[i]);
+    ks += kh;
+    const bf16_pair pr = split_bf16(kh);
+    sh[G::KH + i * G::P + p] = pr.hi;
+    sh[G::KL + i * G::P + p] = pr.lo;
+  }
+  *ksum = ks;
+  return c;
+}
+
+// State update of wave w's columns: S[p][e] = e^{G_end[p]} S[p][e] + sum_i k^_i[p] v_i[e].
+template <int D>
+__device__ __forceinline__ void mstate(f32x16 (&S)[D / 32], const float* sf, const __bf16* sh, int w, int lane) {
+  using G = MGeo<D>;
+#pragma unroll
+  for (int pt = 0; pt < D / 32; ++pt) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) S[pt][r] *= sf[G::AEND + 32 * pt + dtile_row(r, lane)];
+#pragma unroll
+    for (int i0 = 0; i0 < GC; i0 += 16) {
+      const bf16x8 v = ld_rows8(sh + G::V, G::P, i0, 32 * w, lane);    // B[k=i][n=e] = v_i[e]
+      S[pt] = mfma32(ld_rows8(sh + G::KH, G::P, i0, 32 * pt, lane), v, S[pt]);  // A[m=p][k=i] = k^_i[p]
+      S[pt] = mfma32(ld_rows8(sh + G::KL, G::P, i0, 32 * pt, lane), v, S[pt]);
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(2 * D) void k_summary_gla_m(PrefillParams p) {
+  using G = MGeo<D>;
+  extern __shared__ __align__(16) unsigned char smem[];
+  float* sf = (float*)smem;
+  __bf16* sh = (__bf16*)smem;
+  const int bh = blockIdx.x, seg = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const bool elu = p.psi == LA_PSI_ELU1, norm = p.normalize != 0;
+  const SeqSpan sq = seq_span(p, bh);
+  const int T = sq.T, n_chunks = (T + GC - 1) / GC;
+  const int c0 = seg * p.seg_chunks, c1 = min(c0 + p.seg_chunks, n_chunks);
+  f32x16 S[D / 32];
+#pragma unroll
+  for (int pt = 0; pt < D / 32; ++pt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) S[pt][r] = 0.f;
+  float z = 0.f, segtot = 0.f;  // thread p < D: Z[p] and the segment's summed log gate
+  MLoad<D> T0;
+  if (c0 < c1) mload<D>(T0, p, sq.row0 + (long long)c0 * GC * p.tok_rows, min(GC, T - c0 * GC));
+  for (int c = c0; c < c1; ++c) {
+    const int L = min(GC, T - c * GC);
+    lds_barrier();
+    mcommit<D, false>(T0, sf, sh, L, elu);
+    if (c + 1 < c1) mload<D>(T0, p, sq.row0 + (long long)(c + 1) * GC * p.tok_rows, min(GC, T - (c + 1) * GC));
+    lds_barrier();
+    if (tid < D) {
+      float ks;
+      const float ge = feature_pass<D, false>(sf, sh, &ks);
+      const float ae = __expf(ge);
+      sf[G::AEND + tid] = ae;
+      z = ae * z + ks;
+      segtot += ge;
+    }
+    lds_barrier();
+    mstate<D>(S, sf, sh, w, lane);
+  }
+  const size_t REC = (size_t)D * D + 2 * D;
+  float* out = p.ws + ((size_t)bh * p.n_seg + seg) * REC;
+#pragma unroll
+  for (int pt = 0; pt < D / 32; ++pt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) out[(size_t)(32 * pt + dtile_row(r, lane)) * D + 32 * w + (lane & 31)] = S[pt][r];
+  if (tid < D) {
+    out[(size_t)D * D + tid] = norm ? z : 0.f;
+    out[(size_t)D * D + D + tid] = __expf(segtot);
+  }
+}
+
+template <int D, bool OBF>
+__global__ __launch_bounds__(2 * D) void k_output_gla_m(PrefillParams p) {
+  using G = MGeo<D>;
+  constexpr int NT = 2 * D, NW = D / 32, TPT = NT / GC;  // threads per token in the reductions
+  extern __shared__ __align__(16) unsigned char smem[];
+  float* sf = (float*)smem;
+  __bf16* sh = (__bf16*)smem;
+  const int bh = blockIdx.x, seg = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const bool elu = p.psi == LA_PSI_ELU1, norm = p.normalize != 0;
+  const SeqSpan sq = seq_span(p, bh);
+  const int T = sq.T, n_chunks = (T + GC - 1) / GC;
+  const int c0 = seg * p.seg_chunks, c1 = min(c0 + p.seg_chunks, n_chunks);
+  if (c0 >= c1) return;
+  const size_t REC = (size_t)D * D + 2 * D;
+  const float* pre = p.ws + ((size_t)bh * p.n_seg + seg) * REC;
+  f32x16 S[D / 32];  // S[p][e]: rows p in tile pt, column e = 32 w + lane % 32
+#pragma unroll
+  for (int pt = 0; pt < D / 32; ++pt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) S[pt][r] = pre[(size_t)(32 * pt + dtile_row(r, lane)) * D + 32 * w + (lane & 31)];
+  float z = (norm && tid < D) ? pre[(size_t)D * D + tid] : 0.f;  // Z_prev[p] of thread p
+  constexpr int OES = OBF ? 2 : 4;
+  const uint32_t rso = (uint32_t)p.tok_rows * D * OES;
+  MLoad<D> T0;
+  mload<D>(T0, p, sq.row0 + (long long)c0 * GC * p.tok_rows, min(GC, T - c0 * GC));
+  for (int c = c0; c < c1; ++c) {
+    const int L = min(GC, T - c * GC);
+    const long long r0 = sq.row0 + (long long)c * GC * p.tok_rows;
+    lds_barrier();
+    mcommit<D, true>(T0, sf, sh, L, elu);
+    if (tid < D) sf[G::ZV + tid] = z;
+    if (c + 1 < c1) mload<D>(T0, p, sq.row0 + (long long)(c + 1) * GC * p.tok_rows, min(GC, T - (c + 1) * GC));
+    lds_barrier();
+    float ks = 0.f;
+    if (tid < D) sf[G::AEND + tid] = __expf(feature_pass<D, true>(sf, sh, &ks));
+    lds_barrier();
+
+    // scores A_ji = sum_p psi(q_j)[p] psi(k_i)[p] prod_{s=i+1..j} alpha_s[p]: thread (i, slice of
+    // 16 features) walks j upwards, multiplying its running key features by each token's gates
+    {
+      const int i = tid & 31, f0 = (tid >> 5) * 16;
+      float kk[16];
+#pragma unroll
+      for (int f = 0; f < 16; f += 4) *(f32x4*)(kk + f) = *(const f32x4*)(sf + G::PK + i * D + f0 + f);
+#pragma unroll 2
+      for (int j = 0; j < GC; ++j) {
+        if (j > i) {
+#pragma unroll
+          for (int f = 0; f < 16; f += 4) {
+            const f32x4 a = *(const f32x4*)(sf + G::AL + j * D + f0 + f);
+            kk[f] *= a[0]; kk[f + 1] *= a[1]; kk[f + 2] *= a[2]; kk[f + 3] *= a[3];
+          }
+        }
+        float acc = 0.f;
+#pragma unroll
+        for (int f = 0; f < 16; f += 4) {
+          const f32x4 qv = *(const f32x4*)(sf + G::PQ + j * D + f0 + f);
+          acc += qv[0] * kk[f] + qv[1] * kk[f + 1] + qv[2] * kk[f + 2] + qv[3] * kk[f + 3];
+        }
+        acc = j >= i ? acc : 0.f;
+        // lanes l and l + 32 hold the same key i: combine, then one partial per wave to LDS
+        acc += __shfl_xor(acc, 32);
+        if (lane < 32) sf[G::APART + (w * GC + j) * GC + i] = acc;
+      }
+    }
+    lds_barrier();
+    // A as hi + lo; den_j = q^_j . Z_prev + sum_i A_ji + eps (TPT threads per token)
+    {
+      const int j = tid / TPT, r = tid % TPT;
+      constexpr int IW = GC / TPT, FW = D / TPT;
+      float rs = 0.f;
+#pragma unroll
+      for (int ii = 0; ii < IW; ++ii) {
+        const int i = r * IW + ii;
+        float a = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) a += sf[G::APART + (ww * GC + j) * GC + i];
+        rs += a;
+        const bf16_pair pr = split_bf16(a);
+        sh[G::SAH + j * G::AP + i] = pr.hi;
+        sh[G::SAL + j * G::AP + i] = pr.lo;
+      }
+      if (norm) {
+        float zs = 0.f;
+        for (int f = r * FW; f < r * FW + FW; ++f)
+          zs += (from_bf16(sh[G::QH + j * G::P + f]) + from_bf16(sh[G::QL + j * G::P + f])) * sf[G::ZV + f];
+        rs += zs;
+#pragma unroll
+        for (int o = 1; o < TPT; o <<= 1) rs += __shfl_xor(rs, o);
+        if (r == 0) sf[G::DEN + j] = rs + p.eps;
+      }
+    }
+    if (norm && tid < D) z = sf[G::AEND + tid] * z + ks;  // Z_prev read above; written at the next commit
+    lds_barrier();
+
+    // outputs, transposed: num^T[e][j] = sum_p S[p][e] q^_j[p] + sum_i v_i[e] A_ji (M = e, N = j)
+    {
+      f32x16 acc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+      for (int pt = 0; pt < D / 32; ++pt) {
+        bf16x8 shi[2], slo[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          float x[8];
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) x[jj] = S[pt][8 * q + jj];
+          split8_trunc(x, shi[q], slo[q]);
+        }
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const bf16x8 qh = ld_cols8_perm(sh + G::QH, G::P, 0, 32 * pt, q, lane);  // B[k=p][n=j] = q^_j[p]
+          const bf16x8 ql = ld_cols8_perm(sh + G::QL, G::P, 0, 32 * pt, q, lane);
+          acc = mfma32(shi[q], qh, acc);  // A[m=e][k=p] = S[p][e] (the D-tile, transposed)
+          acc = mfma32(shi[q], ql, acc);
+          acc = mfma32(slo[q], qh, acc);
+        }
+      }
+#pragma unroll
+      for (int i0 = 0; i0 < GC; i0 += 16) {
+        const bf16x8 va = ld_rows8(sh + G::V, G::P, i0, 32 * w, lane);  // A[m=e][k=i] = v_i[e]
+        acc = mfma32(va, ld_cols8(sh + G::SAH, G::AP, 0, i0, lane), acc);  // B[k=i][n=j] = A_ji
+        acc = mfma32(va, ld_cols8(sh + G::SAL, G::AP, 0, i0, lane), acc);
+      }
+      const int j = lane & 31;
+      const float inv = norm ? 1.f / sf[G::DEN + j] : 1.f;
+      const __amdgpu_buffer_rsrc_t ro = make_rsrc((unsigned char*)p.o + r0 * D * OES, rows_extent(L, rso, D * OES));
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int e = 32 * w + dtile_row(4 * g, lane);  // four consecutive columns
+        store_out4<OBF>(ro, (uint32_t)j * (rso / OES) + e, acc[4 * g] * inv, acc[4 * g + 1] * inv,
+                        acc[4 * g + 2] * inv, acc[4 * g + 3] * inv);
+      }
+    }
+    mstate<D>(S, sf, sh, w, lane);
+  }
+}
+
+template <int D>
+hipError_t launch_m(const PrefillParams& p, hipStream_t s, bool out) {
+  using G = MGeo<D>;
+  const void* kern = !out ? (const void*)k_summary_gla_m<D>
+                     : p.out_bf16 ? (const void*)k_output_gla_m<D, true> : (const void*)k_output_gla_m<D, false>;
+  hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, G::BYTES);
+  if (e != hipSuccess) return e;
+  dim3 grid(p.B * p.H, p.n_seg);
+  void* args[] = {(void*)&p};
+  e = hipLaunchKernel(kern, grid, dim3(G::NT), args, G::BYTES, s);
+  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
 template <int NP, int DV>
 hipError_t launch_nd(const PrefillParams& p, hipStream_t s, bool out) {
   using G = GlaGeo<NP, DV>;
@@ -318,6 +673,11 @@ bool prefill_gated_supported(int C, int d_k, int d_v, int n_psi, int psi) {
 }
 
 hipError_t launch_prefill_gated(const PrefillParams& p, hipStream_t s, bool out) {
+  if (!p.in_f32) {
+    if (p.d_k == 64) return launch_m<64>(p, s, out);
+    if (p.d_k == 128) return launch_m<128>(p, s, out);
+    return hipErrorInvalidValue;
+  }
   if (p.d_k == 64) return launch_nd<64, 64>(p, s, out);
   if (p.d_k == 128) return launch_nd<128, 128>(p, s, out);
   return hipErrorInvalidValue;

@@ -130,7 +130,7 @@ DECODE_32x64 = DecodeWorkload(
 # feature, log alpha = logsigmoid(z) / 16 with z ~ N(0, 1) (inputs.make_log_gates), no
 # denominator, chunks of 16 on the fp32 path.
 GATED_8K = Workload(
-    name="gated_8k", B=4, H=16, T=8192, d_k=128, d_v=128, n_psi=128, chunk=16, psi=PSI_IDENTITY, normalize=0,
+    name="gated_8k", B=4, H=16, T=8192, d_k=128, d_v=128, n_psi=128, chunk=32, psi=PSI_IDENTITY, normalize=0,
     eps=1e-6, dtype="bf16", seed=7, qk_scale=128 ** -0.5, v_scale=1.0, extra={"gate_temp": 16.0})
 
 # Serving prefill: 32 prompts of 1k..16k tokens packed in one call, retention form as above.

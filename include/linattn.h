@@ -208,7 +208,7 @@ la_status lin_attn_prefill_profiled(const la_prefill_desc* d, const void* q, con
  * diag(a2) X1 + X2) with a the per-row product of a chunk's gates.
  *
  *   d         as for lin_attn_prefill; supported: psi identity or elu1, d_k == d_v ==
- *             n_psi in {64, 128}, chunk 16, in_dtype LA_BF16 or LA_F32, either layout
+ *             n_psi in {64, 128}, chunk 32, in_dtype LA_BF16 or LA_F32, either layout
  *   log_gate  device fp32, laid out like k ([B, H, T, d_k] or [B, T, H, d_k]): the log of
  *             each token's gate per state row, <= 0 (gates in (0, 1]). Values must be
  *             finite; an exact reset between documents is a sequence boundary (separate

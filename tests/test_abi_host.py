@@ -191,13 +191,13 @@ def test_gated_validation_and_workspace():
         n = ctypes.c_size_t(0)
         st = lib.lin_attn_prefill_gated_workspace_size(ctypes.byref(_desc(**kw)), ctypes.byref(n))
         return st, n.value
-    base = dict(chunk=16, psi=0, normalize=0)
+    base = dict(chunk=32, psi=0, normalize=0)
     st, n = ws(**base)
     assert st == LA_OK
     # one record per segment: S, Z and the segment's per-row decay
     E = 128 * 128 + 2 * 128
     assert n % (4 * E) == 0
-    for kw in (dict(chunk=64), dict(psi=2, n_psi=256), dict(d_v=64), dict(d_k=96, d_v=96, n_psi=96)):
+    for kw in (dict(chunk=64), dict(chunk=16), dict(psi=2, n_psi=256), dict(d_v=64), dict(d_k=96, d_v=96, n_psi=96)):
         assert ws(**{**base, **kw})[0] == LA_ERR_UNSUPPORTED, kw
     assert ws(**{**base, "psi": 1, "normalize": 1, "d_k": 64, "d_v": 64, "n_psi": 64})[0] == LA_OK
     assert ws(**{**base, "in_dtype": LA_F32, "layout": 1})[0] == LA_OK

@@ -52,7 +52,7 @@ CASES = [
 def test_gated_small(case):
     name, B, H, T, d, psi, normalize, dt, temp, layout = case
     scale = d ** -0.5 if psi == PSI_IDENTITY else 0.5
-    w = Workload(name=name, B=B, H=H, T=T, d_k=d, d_v=d, n_psi=d, chunk=16, psi=psi, normalize=normalize, eps=1e-6,
+    w = Workload(name=name, B=B, H=H, T=T, d_k=d, d_v=d, n_psi=d, chunk=32, psi=psi, normalize=normalize, eps=1e-6,
                  dtype=dt, seed=71, qk_scale=scale, v_scale=1.0)
     announce(f"gated prefill {name}")
     q, k, v, lg = _inputs(w, temp)
@@ -68,7 +68,7 @@ def test_gated_small(case):
 
 @pytest.mark.parametrize("T", [1, 15, 16, 17, 47])
 def test_gated_edge_lengths(T):
-    w = Workload(name=f"gated_T{T}", B=1, H=2, T=T, d_k=64, d_v=64, n_psi=64, chunk=16, psi=PSI_ELU1, normalize=1,
+    w = Workload(name=f"gated_T{T}", B=1, H=2, T=T, d_k=64, d_v=64, n_psi=64, chunk=32, psi=PSI_ELU1, normalize=1,
                  eps=1e-6, dtype="bf16", seed=73 + T, qk_scale=0.5, v_scale=1.0)
     announce(f"gated prefill edge T={T}")
     q, k, v, lg = _inputs(w, 4.0)
@@ -81,12 +81,12 @@ def test_gated_initial_and_final_state():
     """Prefill from an initial state (the state of a gated prefix) and the final state after
     the last token, against the oracle continuing from the same state."""
     B, H, T, d = 2, 2, 277, 128
-    w = Workload(name="gated_state", B=B, H=H, T=T, d_k=d, d_v=d, n_psi=d, chunk=16, psi=PSI_ELU1, normalize=1,
+    w = Workload(name="gated_state", B=B, H=H, T=T, d_k=d, d_v=d, n_psi=d, chunk=32, psi=PSI_ELU1, normalize=1,
                  eps=1e-6, dtype="bf16", seed=79, qk_scale=0.5, v_scale=1.0)
     announce("gated prefill init/final state")
     q, k, v, lg = _inputs(w, 8.0)
     # initial state: the oracle's state after a seeded 64-token gated prefix
-    wp = Workload(name="prefix", B=B, H=H, T=64, d_k=d, d_v=d, n_psi=d, chunk=16, psi=PSI_ELU1, normalize=1,
+    wp = Workload(name="prefix", B=B, H=H, T=64, d_k=d, d_v=d, n_psi=d, chunk=32, psi=PSI_ELU1, normalize=1,
                   eps=1e-6, dtype="bf16", seed=80, qk_scale=0.5, v_scale=1.0)
     _, kp, vp, lgp = _inputs(wp, 8.0)
     _, S0, Z0 = oracle.prefill(None, kp.reshape(B * H, 64, d), vp.reshape(B * H, 64, d), PSI_ELU1,
@@ -142,7 +142,7 @@ def test_gated_prefill_then_decode():
     """The gated prefill's final state continues in gated decode: outputs match the oracle
     over the whole sequence."""
     B, H, T, d, n = 1, 2, 150, 64, 4
-    w = Workload(name="gated_handoff", B=B, H=H, T=T + n, d_k=d, d_v=d, n_psi=d, chunk=16, psi=PSI_ELU1,
+    w = Workload(name="gated_handoff", B=B, H=H, T=T + n, d_k=d, d_v=d, n_psi=d, chunk=32, psi=PSI_ELU1,
                  normalize=1, eps=1e-6, dtype="bf16", seed=85, qk_scale=0.5, v_scale=1.0)
     announce("gated prefill -> decode")
     q, k, v, lg = _inputs(w, 4.0)
