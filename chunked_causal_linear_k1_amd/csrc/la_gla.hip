@@ -356,7 +356,8 @@ __device__ __forceinline__ void mload(MLoad<D>& T, const PrefillParams& p, long 
   }
 }
 
-// Commit: psi(q), psi(k) as fp32 (rows >= L zero), log gates (rows >= L zero: gate 1), v.
+// Commit: psi(q), psi(k) as fp32 (rows >= L zero), v, and the log gates (summary) or the
+// gates exp(log_gate) (output pass, Q); padded rows have gate 1.
 template <int D, bool Q>
 __device__ __forceinline__ void mcommit(const MLoad<D>& T, float* sf, __bf16* sh, int L, bool elu) {
   using G = MGeo<D>;
@@ -392,7 +393,9 @@ __device__ __forceinline__ void mcommit(const MLoad<D>& T, float* sf, __bf16* sh
   for (int i = 0; i < MLoad<D>::PF; ++i) {
     const int pc = threadIdx.x + i * NT, row = pc / RPF, col = (pc % RPF) * 4;
     const f32x4 g = __builtin_bit_cast(f32x4, T.g[i]);
-    *(f32x4*)(sf + G::AL + row * D + col) = row < L ? g : f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 x = row < L ? g : f32x4{0.f, 0.f, 0.f, 0.f};  // padded tokens: log gate 0, gate 1
+    if (Q) x = f32x4{__expf(x[0]), __expf(x[1]), __expf(x[2]), __expf(x[3])};
+    *(f32x4*)(sf + G::AL + row * D + col) = x;
   }
 }
 
@@ -516,7 +519,7 @@ __global__ __launch_bounds__(2 * D) void k_output_gla_m(PrefillParams p) {
   for (int pt = 0; pt < D / 32; ++pt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) S[pt][r] = pre[(size_t)(32 * pt + dtile_row(r, lane)) * D + 32 * w + (lane & 31)];
-  float z = (norm && tid < D) ? pre[(size_t)D * D + tid] : 0.f;  // Z_prev[p] of thread p
+  float z = (norm && tid >= D) ? pre[(size_t)D * D + tid - D] : 0.f;  // Z_prev[p] of thread D + p
   constexpr int OES = OBF ? 2 : 4;
   const uint32_t rso = (uint32_t)p.tok_rows * D * OES;
   MLoad<D> T0;
@@ -526,11 +529,36 @@ __global__ __launch_bounds__(2 * D) void k_output_gla_m(PrefillParams p) {
     const long long r0 = sq.row0 + (long long)c * GC * p.tok_rows;
     lds_barrier();
     mcommit<D, true>(T0, sf, sh, L, elu);
-    if (tid < D) sf[G::ZV + tid] = z;
+    if (tid >= D) sf[G::ZV + tid - D] = z;
     if (c + 1 < c1) mload<D>(T0, p, sq.row0 + (long long)(c + 1) * GC * p.tok_rows, min(GC, T - (c + 1) * GC));
     lds_barrier();
+    // q^_j = psi(q_j) prod_{s<=j} alpha_s (threads p < D) and k^_i = psi(k_i) prod_{s>i} alpha_s
+    // (threads D + p): running products of the gates, every factor <= 1
     float ks = 0.f;
-    if (tid < D) sf[G::AEND + tid] = __expf(feature_pass<D, true>(sf, sh, &ks));
+    if (tid < D) {
+      const int pf = tid;
+      float eg = 1.f;
+#pragma unroll 4
+      for (int j = 0; j < GC; ++j) {
+        eg *= sf[G::AL + j * D + pf];
+        const bf16_pair pr = split_bf16(sf[G::PQ + j * D + pf] * eg);
+        sh[G::QH + j * G::P + pf] = pr.hi;
+        sh[G::QL + j * G::P + pf] = pr.lo;
+      }
+      sf[G::AEND + pf] = eg;
+    } else {
+      const int pf = tid - D;
+      float f = 1.f;
+#pragma unroll 4
+      for (int i = GC - 1; i >= 0; --i) {
+        const float kh = sf[G::PK + i * D + pf] * f;
+        ks += kh;
+        const bf16_pair pr = split_bf16(kh);
+        sh[G::KH + i * G::P + pf] = pr.hi;
+        sh[G::KL + i * G::P + pf] = pr.lo;
+        f *= sf[G::AL + i * D + pf];
+      }
+    }
     lds_barrier();
 
     // scores A_ji = sum_p psi(q_j)[p] psi(k_i)[p] prod_{s=i+1..j} alpha_s[p]: thread (i, slice of
@@ -540,25 +568,33 @@ __global__ __launch_bounds__(2 * D) void k_output_gla_m(PrefillParams p) {
       float kk[16];
 #pragma unroll
       for (int f = 0; f < 16; f += 4) *(f32x4*)(kk + f) = *(const f32x4*)(sf + G::PK + i * D + f0 + f);
-#pragma unroll 2
-      for (int j = 0; j < GC; ++j) {
-        if (j > i) {
+      for (int j0 = 0; j0 < GC; j0 += 4) {
+        float part[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int j = j0 + jj;
+          if (j > i) {
+#pragma unroll
+            for (int f = 0; f < 16; f += 4) {
+              const f32x4 a = *(const f32x4*)(sf + G::AL + j * D + f0 + f);
+              kk[f] *= a[0]; kk[f + 1] *= a[1]; kk[f + 2] *= a[2]; kk[f + 3] *= a[3];
+            }
+          }
+          float acc[4];
 #pragma unroll
           for (int f = 0; f < 16; f += 4) {
-            const f32x4 a = *(const f32x4*)(sf + G::AL + j * D + f0 + f);
-            kk[f] *= a[0]; kk[f + 1] *= a[1]; kk[f + 2] *= a[2]; kk[f + 3] *= a[3];
+            const f32x4 qv = *(const f32x4*)(sf + G::PQ + j * D + f0 + f);
+            acc[f / 4] = qv[0] * kk[f] + qv[1] * kk[f + 1] + qv[2] * kk[f + 2] + qv[3] * kk[f + 3];
           }
+          part[jj] = j >= i ? (acc[0] + acc[1]) + (acc[2] + acc[3]) : 0.f;
         }
-        float acc = 0.f;
-#pragma unroll
-        for (int f = 0; f < 16; f += 4) {
-          const f32x4 qv = *(const f32x4*)(sf + G::PQ + j * D + f0 + f);
-          acc += qv[0] * kk[f] + qv[1] * kk[f + 1] + qv[2] * kk[f + 2] + qv[3] * kk[f + 3];
-        }
-        acc = j >= i ? acc : 0.f;
         // lanes l and l + 32 hold the same key i: combine, then one partial per wave to LDS
-        acc += __shfl_xor(acc, 32);
-        if (lane < 32) sf[G::APART + (w * GC + j) * GC + i] = acc;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) part[jj] += __shfl_xor(part[jj], 32);
+        if (lane < 32) {
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) sf[G::APART + (w * GC + j0 + jj) * GC + i] = part[jj];
+        }
       }
     }
     lds_barrier();
@@ -588,7 +624,7 @@ __global__ __launch_bounds__(2 * D) void k_output_gla_m(PrefillParams p) {
         if (r == 0) sf[G::DEN + j] = rs + p.eps;
       }
     }
-    if (norm && tid < D) z = sf[G::AEND + tid] * z + ks;  // Z_prev read above; written at the next commit
+    if (norm && tid >= D) z = sf[G::AEND + tid - D] * z + ks;  // Z_prev read above; written at the next commit
     lds_barrier();
 
     // outputs, transposed: num^T[e][j] = sum_p S[p][e] q^_j[p] + sum_i v_i[e] A_ji (M = e, N = j)
