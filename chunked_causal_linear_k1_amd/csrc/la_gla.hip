@@ -319,7 +319,10 @@ struct MGeo {
   static constexpr int H0 = 2 * FEND;
   static constexpr int QH = H0, QL = QH + GC * P, KH = QL + GC * P, KL = KH + GC * P, V = KL + GC * P;
   static constexpr int SAH = V + GC * P, SAL = SAH + GC * AP;  // A hi / lo [GC][AP]
-  static constexpr int HEND = SAL + GC * AP;
+  // the off-diagonal half block of the scores: q~ (rows GC/2.., zero above) and k~ (rows
+  // ..GC/2, zero below), referenced to the last token of the first half
+  static constexpr int XQH = SAL + GC * AP, XQL = XQH + GC * P, XKH = XQL + GC * P, XKL = XKH + GC * P;
+  static constexpr int HEND = XKL + GC * P;
   static constexpr int BYTES = HEND * 2;
   static_assert(FEND % 4 == 0 && (GC * P) % 8 == 0 && (GC * AP) % 8 == 0, "16-byte aligned regions");
 };
@@ -521,7 +524,16 @@ __global__ __launch_bounds__(2 * D) void k_output_gla_m(PrefillParams p) {
     for (int r = 0; r < 16; ++r) S[pt][r] = pre[(size_t)(32 * pt + dtile_row(r, lane)) * D + 32 * w + (lane & 31)];
   float z = (norm && tid >= D) ? pre[(size_t)D * D + tid - D] : 0.f;  // Z_prev[p] of thread D + p
   constexpr int OES = OBF ? 2 : 4;
+  constexpr int HC = GC / 2;
   const uint32_t rso = (uint32_t)p.tok_rows * D * OES;
+  // rows 0..HC-1 of q~ and HC.. of k~ stay zero: the MFMA over the full tile then yields the
+  // off-diagonal half block only
+  for (int x = tid; x < HC * G::P; x += NT) {
+    sh[G::XQH + x] = to_bf16(0.f);
+    sh[G::XQL + x] = to_bf16(0.f);
+    sh[G::XKH + HC * G::P + x] = to_bf16(0.f);
+    sh[G::XKL + HC * G::P + x] = to_bf16(0.f);
+  }
   MLoad<D> T0;
   mload<D>(T0, p, sq.row0 + (long long)c0 * GC * p.tok_rows, min(GC, T - c0 * GC));
   for (int c = c0; c < c1; ++c) {
@@ -537,42 +549,59 @@ __global__ __launch_bounds__(2 * D) void k_output_gla_m(PrefillParams p) {
     float ks = 0.f;
     if (tid < D) {
       const int pf = tid;
-      float eg = 1.f;
+      float eg = 1.f, ex = 1.f;  // prod_{s<=j} alpha_s, and prod_{HC<=s<=j} alpha_s
 #pragma unroll 4
       for (int j = 0; j < GC; ++j) {
-        eg *= sf[G::AL + j * D + pf];
-        const bf16_pair pr = split_bf16(sf[G::PQ + j * D + pf] * eg);
+        const float a = sf[G::AL + j * D + pf], q = sf[G::PQ + j * D + pf];
+        eg *= a;
+        const bf16_pair pr = split_bf16(q * eg);
         sh[G::QH + j * G::P + pf] = pr.hi;
         sh[G::QL + j * G::P + pf] = pr.lo;
+        if (j >= HC) {
+          ex *= a;
+          const bf16_pair px = split_bf16(q * ex);
+          sh[G::XQH + j * G::P + pf] = px.hi;
+          sh[G::XQL + j * G::P + pf] = px.lo;
+        }
       }
       sf[G::AEND + pf] = eg;
     } else {
       const int pf = tid - D;
-      float f = 1.f;
+      float f = 1.f, fx = 1.f;  // prod_{s>i} alpha_s, and prod_{i<s<HC} alpha_s
 #pragma unroll 4
       for (int i = GC - 1; i >= 0; --i) {
-        const float kh = sf[G::PK + i * D + pf] * f;
+        const float k = sf[G::PK + i * D + pf], a = sf[G::AL + i * D + pf];
+        const float kh = k * f;
         ks += kh;
         const bf16_pair pr = split_bf16(kh);
         sh[G::KH + i * G::P + pf] = pr.hi;
         sh[G::KL + i * G::P + pf] = pr.lo;
-        f *= sf[G::AL + i * D + pf];
+        f *= a;
+        if (i < HC) {
+          const bf16_pair px = split_bf16(k * fx);
+          sh[G::XKH + i * G::P + pf] = px.hi;
+          sh[G::XKL + i * G::P + pf] = px.lo;
+          fx *= a;
+        }
       }
     }
     lds_barrier();
 
-    // scores A_ji = sum_p psi(q_j)[p] psi(k_i)[p] prod_{s=i+1..j} alpha_s[p]: thread (i, slice of
-    // 16 features) walks j upwards, multiplying its running key features by each token's gates
+    // scores A_ji = sum_p psi(q_j)[p] psi(k_i)[p] prod_{s=i+1..j} alpha_s[p]
+    //  - i, j in the same half: thread (i, slice of 16 features) walks j upwards through its
+    //    half, multiplying its running key features by each token's gates (every factor <= 1)
+    //  - j in the second half, i in the first: sum_p q~_j[p] k~_i[p] with both factors
+    //    referenced to token HC - 1 (so both <= 1), one MFMA tile per wave over its features
     {
-      const int i = tid & 31, f0 = (tid >> 5) * 16;
+      const int i = tid & 31, f0 = (tid >> 5) * 16, jb = i & HC;
       float kk[16];
 #pragma unroll
       for (int f = 0; f < 16; f += 4) *(f32x4*)(kk + f) = *(const f32x4*)(sf + G::PK + i * D + f0 + f);
-      for (int j0 = 0; j0 < GC; j0 += 4) {
+      for (int j0 = 0; j0 < HC; j0 += 4) {
         float part[4];
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
-          const int j = j0 + jj;
+          const int j = jb + j0 + jj;
           if (j > i) {
 #pragma unroll
             for (int f = 0; f < 16; f += 4) {
@@ -593,8 +622,25 @@ __global__ __launch_bounds__(2 * D) void k_output_gla_m(PrefillParams p) {
         for (int jj = 0; jj < 4; ++jj) part[jj] += __shfl_xor(part[jj], 32);
         if (lane < 32) {
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj) sf[G::APART + (w * GC + j0 + jj) * GC + i] = part[jj];
+          for (int jj = 0; jj < 4; ++jj) sf[G::APART + (w * GC + jb + j0 + jj) * GC + i] = part[jj];
         }
+      }
+      f32x16 x;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x[r] = 0.f;
+#pragma unroll
+      for (int k0 = 0; k0 < 32; k0 += 16) {
+        const bf16x8 qh = ld_cols8(sh + G::XQH, G::P, 0, 32 * w + k0, lane);  // A[m=j][k=p] = q~_j[p]
+        const bf16x8 ql = ld_cols8(sh + G::XQL, G::P, 0, 32 * w + k0, lane);
+        const bf16x8 kh = ld_cols8(sh + G::XKH, G::P, 0, 32 * w + k0, lane);  // B[k=p][n=i] = k~_i[p]
+        const bf16x8 kl = ld_cols8(sh + G::XKL, G::P, 0, 32 * w + k0, lane);
+        x = mfma32(qh, kh, x);
+        x = mfma32(qh, kl, x);
+        x = mfma32(ql, kh, x);
+      }
+      if (i < HC) {  // rows j >= HC: registers 8..15
+#pragma unroll
+        for (int r = 8; r < 16; ++r) sf[G::APART + (w * GC + dtile_row(r, lane)) * GC + i] = x[r];
       }
     }
     lds_barrier();
@@ -609,6 +655,7 @@ __global__ __launch_bounds__(2 * D) void k_output_gla_m(PrefillParams p) {
         float a = 0.f;
 #pragma unroll
         for (int ww = 0; ww < NW; ++ww) a += sf[G::APART + (ww * GC + j) * GC + i];
+        a = i <= j ? a : 0.f;  // the first half's rows against the second half's keys are never written
         rs += a;
         const bf16_pair pr = split_bf16(a);
         sh[G::SAH + j * G::AP + i] = pr.hi;
