@@ -54,7 +54,8 @@ struct BG {
   static constexpr int HALVES = BL + STILE;
   static constexpr int F0 = HALVES / 2;      // first float
   static constexpr int TH = F0, XI = TH + BC, DD = XI + BC, IV = DD + BC, WT = IV + BC, ZV = WT + BC;
-  static constexpr int FEND = ZV + BD;
+  static constexpr int DM = ZV + BD;  // gamma^n, n = 0..BC-1 (the causal decay mask by lag)
+  static constexpr int FEND = DM + BC;
   static constexpr int BYTES = FEND * 4;
 };
 static_assert(BG::HALVES % 8 == 0, "float tables 16-byte aligned");
@@ -64,49 +65,59 @@ static_assert(9 * BC * 2 <= BG::STILE, "row partials and weights fit one bf16 C 
 
 // ---- global tiles ----------------------------------------------------------------------
 
-// A step of BC token rows x BD bf16: 4 pieces of 8 elements per thread (row t/16 + 16i).
+// A step of BC token rows x BD bf16 over NT threads: BC*BD/8/NT pieces of 8 elements per
+// thread (row t/16 + (NT/16) i).
+template <int NT>
 struct Tile16 {
-  uint4 r[4];
+  static constexpr int N = BC * BD / 8 / NT;
+  uint4 r[N];
 };
-__device__ __forceinline__ void load_tile16(Tile16& P, const void* base, int valid, uint32_t rsb) {
+template <int NT>
+__device__ __forceinline__ void load_tile16(Tile16<NT>& P, const void* base, int valid, uint32_t rsb) {
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, rows_extent(valid, rsb, BD * 2));
   const int t = threadIdx.x;
   const uint32_t v0 = (uint32_t)(t >> 4) * rsb + (uint32_t)(t & 15) * 16;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) P.r[i] = buf_load16(rs, v0, (uint32_t)(16 * i) * rsb);
+  for (int i = 0; i < Tile16<NT>::N; ++i) P.r[i] = buf_load16(rs, v0, (uint32_t)((NT / 16) * i) * rsb);
 }
-__device__ __forceinline__ int t16_row(int i) { return (threadIdx.x >> 4) + 16 * i; }
-__device__ __forceinline__ int t16_col(int) { return (threadIdx.x & 15) * 8; }
+template <int NT>
+__device__ __forceinline__ int t16_row(int i) { return (threadIdx.x >> 4) + (NT / 16) * i; }
+__device__ __forceinline__ int t16_col() { return (threadIdx.x & 15) * 8; }
 
-// A step of BC token rows x BD fp32 (or bf16) values: thread t holds token t/4, columns
-// 4 (t%4) + 16 i + 0..3 for i = 0..7.
+// A step of BC token rows x BD fp32 (or bf16) values over NT threads: TPT = NT / BC threads per
+// token; thread t holds token t / TPT, columns 4 (t % TPT) + 4 TPT i + 0..3.
+template <int NT>
 struct TileF {
-  f32x4 r[8];
+  static constexpr int TPT = NT / BC, N = BD / (4 * TPT);
+  f32x4 r[N];
 };
-template <bool BF>
-__device__ __forceinline__ void load_tileF(TileF& P, const void* base, int valid, uint32_t rsb) {
-  constexpr int ES = BF ? 2 : 4;
+template <int NT, bool BF>
+__device__ __forceinline__ void load_tileF(TileF<NT>& P, const void* base, int valid, uint32_t rsb) {
+  constexpr int ES = BF ? 2 : 4, TPT = TileF<NT>::TPT;
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, rows_extent(valid, rsb, BD * ES));
   const int t = threadIdx.x;
-  const uint32_t v0 = (uint32_t)(t >> 2) * rsb + (uint32_t)(4 * (t & 3)) * ES;
+  const uint32_t v0 = (uint32_t)(t / TPT) * rsb + (uint32_t)(4 * (t % TPT)) * ES;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < TileF<NT>::N; ++i) {
     if (BF) {
-      const u32x2 w = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, v0, 16 * i * ES, 0));
+      const u32x2 w = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, v0, 4 * TPT * i * ES, 0));
       P.r[i] = f32x4{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xffff0000u), __uint_as_float(w[1] << 16),
                      __uint_as_float(w[1] & 0xffff0000u)};
     } else {
-      P.r[i] = __builtin_bit_cast(f32x4, buf_load16(rs, v0, 16 * i * ES));
+      P.r[i] = __builtin_bit_cast(f32x4, buf_load16(rs, v0, 4 * TPT * i * ES));
     }
   }
 }
-__device__ __forceinline__ int tf_tok() { return threadIdx.x >> 2; }
-__device__ __forceinline__ int tf_col(int i) { return 4 * (threadIdx.x & 3) + 16 * i; }
+template <int NT>
+__device__ __forceinline__ int tf_tok() { return threadIdx.x / TileF<NT>::TPT; }
+template <int NT>
+__device__ __forceinline__ int tf_col(int i) { return 4 * (threadIdx.x % TileF<NT>::TPT) + 4 * TileF<NT>::TPT * i; }
 
-// Sum over the four threads of a token (lanes t, t^1, t^2, t^3 of one wave).
-__device__ __forceinline__ float quad_sum(float x) {
-  x += __shfl_xor(x, 1);
-  x += __shfl_xor(x, 2);
+// Sum over the threads of a token (TPT adjacent lanes of one wave).
+template <int NT>
+__device__ __forceinline__ float token_sum(float x) {
+#pragma unroll
+  for (int o = 1; o < TileF<NT>::TPT; o <<= 1) x += __shfl_xor(x, o);
   return x;
 }
 
@@ -114,11 +125,11 @@ __device__ __forceinline__ float quad_sum(float x) {
 
 // psi(x) of a bf16 tile to LDS as hi (+ lo when LO): rows >= L are zero (padded positions
 // are the monoid identity). ELU: elu+1.
-template <bool ELU, bool LO>
-__device__ __forceinline__ void commit_feat(const Tile16& P, __bf16* hi, __bf16* lo, int L) {
+template <int NT, bool ELU, bool LO>
+__device__ __forceinline__ void commit_feat(const Tile16<NT>& P, __bf16* hi, __bf16* lo, int L) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = t16_row(i), col = t16_col(i);
+  for (int i = 0; i < Tile16<NT>::N; ++i) {
+    const int row = t16_row<NT>(i), col = t16_col();
     const bf16x8 x = __builtin_bit_cast(bf16x8, P.r[i]);
     bf16x8 h, l;
 #pragma unroll
@@ -134,17 +145,19 @@ __device__ __forceinline__ void commit_feat(const Tile16& P, __bf16* hi, __bf16*
   }
 }
 
-__device__ __forceinline__ void commit_raw(const Tile16& P, __bf16* dst) {
+template <int NT>
+__device__ __forceinline__ void commit_raw(const Tile16<NT>& P, __bf16* dst) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) *(uint4*)(dst + t16_row(i) * TP + t16_col(i)) = P.r[i];
+  for (int i = 0; i < Tile16<NT>::N; ++i) *(uint4*)(dst + t16_row<NT>(i) * TP + t16_col()) = P.r[i];
 }
 
 // s * x (x from a TileF, s the token's scale) as hi + lo.
-__device__ __forceinline__ void commit_scaled(const TileF& P, float s, __bf16* hi, __bf16* lo) {
-  const int j = tf_tok();
+template <int NT>
+__device__ __forceinline__ void commit_scaled(const TileF<NT>& P, float s, __bf16* hi, __bf16* lo) {
+  const int j = tf_tok<NT>();
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int col = tf_col(i);
+  for (int i = 0; i < TileF<NT>::N; ++i) {
+    const int col = tf_col<NT>(i);
     bf16x4 h, l;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -203,10 +216,12 @@ __device__ __forceinline__ float rowsum16(const f32x16& v, int lane) {
 }
 __device__ __forceinline__ int rowsum16_row(int lane) { return dtile_row((lane >> 1) & 15, lane); }
 
-// The causal decay mask D_ji (0 above the diagonal).
+// The causal decay mask D_ji (0 above the diagonal), gamma^(j-i) read from the step's table:
+// read from LDS rather than recomputed, so the compiler cannot hoist one live value per
+// element out of the step loop.
 template <bool DECAY>
-__device__ __forceinline__ float dmask(int j, int i, float lg) {
-  return i <= j ? (DECAY ? exp2f((float)(j - i) * lg) : 1.f) : 0.f;
+__device__ __forceinline__ float dmask(int j, int i, const float* sf) {
+  return i <= j ? (DECAY ? sf[BG::DM + j - i] : 1.f) : 0.f;
 }
 
 // Tile (jt, it) of the lower block triangle of a C x C matrix: job 0 -> (0,0), 1 -> (1,0), 2 -> (1,1).
@@ -217,7 +232,7 @@ __device__ __forceinline__ int job_it(int job) { return job == 2 ? 1 : 0; }
 template <bool ELU>
 __device__ __forceinline__ f32x16 a_tile_acc(const __bf16* sh, int jt, int it, int lane) {
   f32x16 acc = zero16();
-#pragma unroll
+#pragma unroll 2
   for (int k0 = 0; k0 < BD; k0 += 16) {
     const bf16x8 gh = ld_cols8(sh + BG::QH, TP, 32 * jt, k0, lane);  // A[m=j][k=p] = G[j][p]
     const bf16x8 fh = ld_cols8(sh + BG::KH, TP, 32 * it, k0, lane);  // B[k=p][n=i] = F[i][p]
@@ -233,7 +248,7 @@ __device__ __forceinline__ f32x16 a_tile_acc(const __bf16* sh, int jt, int it, i
 // X = N V^T tile (jt, it), N = the hi + lo tile in NH/NL (unmasked).
 __device__ __forceinline__ f32x16 x_tile_acc(const __bf16* sh, int jt, int it, int lane) {
   f32x16 acc = zero16();
-#pragma unroll
+#pragma unroll 2
   for (int k0 = 0; k0 < BD; k0 += 16) {
     const bf16x8 b = ld_cols8(sh + BG::V, TP, 32 * it, k0, lane);  // B[k=e][n=i] = V[i][e]
     acc = mfma32(ld_cols8(sh + BG::NH, TP, 32 * jt, k0, lane), b, acc);
@@ -252,7 +267,7 @@ __device__ __forceinline__ void store_bm(__bf16* sh, const float* sf, const f32x
   for (int r = 0; r < 16; ++r) {
     const int j = 32 * jt + dtile_row(r, lane);
     const float x = NORM ? (INV ? X[r] * sf[BG::IV + j] : X[r]) + sf[BG::DD + j] : X[r];
-    const bf16_pair pr = split_bf16(i < L ? x * dmask<DECAY>(j, i, lg) : 0.f);
+    const bf16_pair pr = split_bf16(i < L ? x * dmask<DECAY>(j, i, sf) : 0.f);
     sh[BG::BH + j * SQ + i] = pr.hi;
     sh[BG::BL + j * SQ + i] = pr.lo;
   }
@@ -271,14 +286,14 @@ __global__ __launch_bounds__(BNT) void k_bwd_query(BackwardParams bp) {
   float* sf = (float*)smem;
   float* part = sf + BG::AH / 2;  // row partials: A sums [2][BC], A.X sums [2][BC], g.Y sums [4][BC]
   float* wi = part + 8 * BC;      // W_j / den_j, the adjoint summary's token weights
-  const int bh = blockIdx.x, seg = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int bh = blockIdx.x, seg = blockIdx.y, tid = threadIdx.x, lane0 = tid & 63, w = tid >> 6;
   const SeqSpan sq = seq_span(p, bh);
   const int T = sq.T;
   const int seg_tok = p.seg_chunks * p.C;
   const int tb = seg * seg_tok, te = min(tb + seg_tok, T);
   const size_t E = (size_t)BD * BD + BD;
   float* rrec = bp.rev + ((size_t)bh * p.n_seg + seg) * E;
-  const int col = 32 * w + (lane & 31);  // this lane's output column
+  const int col0 = 32 * w + (lane0 & 31);  // this lane's output column
   f32x16 RS[4];                          // adjoint summary [p][e]: rows p in tile pt, column e = col
 #pragma unroll
   for (int pt = 0; pt < 4; ++pt) RS[pt] = zero16();
@@ -293,28 +308,33 @@ __global__ __launch_bounds__(BNT) void k_bwd_query(BackwardParams bp) {
 #pragma unroll
     for (int et = 0; et < 4; ++et)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) ST[et][r] = pre[(size_t)col * BD + 32 * et + dtile_row(r, lane)];
+      for (int r = 0; r < 16; ++r) ST[et][r] = pre[(size_t)col0 * BD + 32 * et + dtile_row(r, lane0)];
     float zreg = (NORM && tid < BD) ? pre[(size_t)BD * BD + tid] : 0.f;  // Z_<[p] of thread p
 
     for (int t0 = tb; t0 < te; t0 += BC) {
+      // the lane index, opaque once per step (see the state sweep) where the denominator's extra
+      // row reductions would otherwise leave hoisted addresses spilling; without it the hoisted
+      // addresses fit and are cheaper
+      const int lane = NORM ? pin(lane0) : lane0, col = 32 * w + (lane & 31);
       const int L = min(BC, te - t0);
       const long long r0 = sq.row0 + (long long)t0 * p.tok_rows;
-      Tile16 tq, tk, tv;
-      load_tile16(tq, (const uint16_t*)p.q + r0 * BD, L, rsb);
-      load_tile16(tk, (const uint16_t*)p.k + r0 * BD, L, rsb);
-      load_tile16(tv, (const uint16_t*)p.v + r0 * BD, L, rsb);
-      TileF tdo;
-      load_tileF<DBF>(tdo, (const unsigned char*)bp.dout + r0 * BD * (DBF ? 2 : 4), L, rsbd);
+      Tile16<BNT> tq, tk, tv;
+      load_tile16<BNT>(tq, (const uint16_t*)p.q + r0 * BD, L, rsb);
+      load_tile16<BNT>(tk, (const uint16_t*)p.k + r0 * BD, L, rsb);
+      load_tile16<BNT>(tv, (const uint16_t*)p.v + r0 * BD, L, rsb);
+      TileF<BNT> tdo;
+      load_tileF<BNT, DBF>(tdo, (const unsigned char*)bp.dout + r0 * BD * (DBF ? 2 : 4), L, rsbd);
       lds_barrier();  // the previous step is done with LDS
-      commit_feat<ELU, ELU>(tq, sh + BG::QH, sh + BG::QL, L);
-      commit_feat<ELU, ELU>(tk, sh + BG::KH, sh + BG::KL, L);
-      commit_raw(tv, sh + BG::V);
-      commit_scaled(tdo, 1.f, sh + BG::NH, sh + BG::NL);  // dout as hi + lo
+      commit_feat<BNT, ELU, ELU>(tq, sh + BG::QH, sh + BG::QL, L);
+      commit_feat<BNT, ELU, ELU>(tk, sh + BG::KH, sh + BG::KL, L);
+      commit_raw<BNT>(tv, sh + BG::V);
+      commit_scaled<BNT>(tdo, 1.f, sh + BG::NH, sh + BG::NL);  // dout as hi + lo
       if (tid < BC) {
         const int j = tid;
         sf[BG::TH + j] = DECAY ? exp2f((float)(j + 1) * lg) : 1.f;
         sf[BG::XI + j] = j < L ? (DECAY ? exp2f((float)(L - 1 - j) * lg) : 1.f) : 0.f;
         sf[BG::WT + j] = DECAY ? exp2f((float)(t0 - tb + j + 1) * lg) : 1.f;
+        sf[BG::DM + j] = DECAY ? exp2f((float)j * lg) : 1.f;
         if (!NORM) {
           sf[BG::IV + j] = 1.f;
           sf[BG::DD + j] = 0.f;
@@ -336,7 +356,7 @@ __global__ __launch_bounds__(BNT) void k_bwd_query(BackwardParams bp) {
           const int i = 32 * it + (lane & 31);
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            Am[r] = A[r] * dmask<DECAY>(32 * jt + dtile_row(r, lane), i, lg);
+            Am[r] = A[r] * dmask<DECAY>(32 * jt + dtile_row(r, lane), i, sf);
             AX[r] = Am[r] * X[r];
           }
           const float sa = rowsum16(Am, lane), sx = rowsum16(AX, lane);
@@ -384,13 +404,13 @@ __global__ __launch_bounds__(BNT) void k_bwd_query(BackwardParams bp) {
         }
         lds_barrier();
         // per token: den, dout . num, 1/den and dden = -(dout . num) / den^2
-        const int j = tf_tok(), qq = tid & 3;
+        const int j = tf_tok<BNT>(), qq = tid & 3;
         float zs = 0.f;
         for (int pp = 32 * qq; pp < 32 * qq + 32; ++pp) {
           const float g = from_bf16(sh[BG::QH + j * TP + pp]) + (ELU ? from_bf16(sh[BG::QL + j * TP + pp]) : 0.f);
           zs += g * sf[BG::ZV + pp];
         }
-        zs = quad_sum(zs);
+        zs = token_sum<BNT>(zs);
         if (qq == 0) {
           const float th = sf[BG::TH + j];
           const float den = part[j] + part[BC + j] + th * zs + p.eps;
@@ -502,19 +522,26 @@ __global__ __launch_bounds__(BNT) void k_bwd_query(BackwardParams bp) {
 #pragma unroll
   for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) rrec[(size_t)(32 * pt + dtile_row(r, lane)) * BD + col] = RS[pt][r];
+    for (int r = 0; r < 16; ++r) rrec[(size_t)(32 * pt + dtile_row(r, lane0)) * BD + col0] = RS[pt][r];
   if (tid < BD) rrec[(size_t)BD * BD + tid] = rz;
 }
 
 // ---- state sweep -----------------------------------------------------------------------
 
+// Eight waves, specialised by the state they hold (two waves per SIMD): waves 0..3 hold R
+// (value columns 32 cw..) and produce dv, waves 4..7 hold R^T (feature columns 32 cw..) and
+// produce dk. Each wave then carries one 128 x 32 state instead of two, and the second wave
+// on each SIMD hides the other's LDS and MFMA latencies.
+constexpr int KNT = 512;
+
 template <bool ELU, bool DECAY, bool NORM, bool DBF>
-__global__ __launch_bounds__(BNT) void k_bwd_key(BackwardParams bp) {
+__global__ __launch_bounds__(KNT) void k_bwd_key(BackwardParams bp) {
   const PrefillParams& p = bp.f;
   extern __shared__ __align__(16) unsigned char smem[];
   __bf16* sh = (__bf16*)smem;
   float* sf = (float*)smem;
-  const int bh = blockIdx.x, seg = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int bh = blockIdx.x, seg = blockIdx.y, tid = threadIdx.x, lane0 = tid & 63, w = tid >> 6;
+  const int role = w >> 2, cw = w & 3;  // role 0: R and dv; role 1: R^T and dk
   const SeqSpan sq = seq_span(p, bh);
   const int T = sq.T;
   const int seg_tok = p.seg_chunks * p.C;
@@ -525,31 +552,36 @@ __global__ __launch_bounds__(BNT) void k_bwd_key(BackwardParams bp) {
   const float lg = DECAY ? p.log2g[bh % p.H] : 0.f;
   const uint32_t rsb = (uint32_t)p.tok_rows * BD * 2, rsb4 = (uint32_t)p.tok_rows * BD * 4;
   const uint32_t rsbd = (uint32_t)p.tok_rows * BD * (DBF ? 2 : 4);
-  const int col = 32 * w + (lane & 31);
-  // R[p][e]: rows p in tile pt, column e = col;  RT[e][p]: rows e in tile et, column p = col
-  f32x16 R[4], RT[4];
+  const int col0 = 32 * cw + (lane0 & 31);
+  // role 0: St[t] = R[p][e], rows p in tile t, column e = col
+  // role 1: St[t] = R^T[e][p], rows e in tile t, column p = col
+  f32x16 St[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      R[t][r] = rpre[(size_t)(32 * t + dtile_row(r, lane)) * BD + col];
-      RT[t][r] = rpre[(size_t)col * BD + 32 * t + dtile_row(r, lane)];
-    }
-  float rz = (NORM && tid < BD) ? rpre[(size_t)BD * BD + tid] : 0.f;  // RZ[p] of thread p
+    for (int r = 0; r < 16; ++r)
+      St[t][r] = role == 0 ? rpre[(size_t)(32 * t + dtile_row(r, lane0)) * BD + col0]
+                           : rpre[(size_t)col0 * BD + 32 * t + dtile_row(r, lane0)];
+  const int zp = tid - KNT / 2;  // role-1 thread zp < BD holds RZ[zp]
+  float rz = (NORM && role == 1 && zp < BD) ? rpre[(size_t)BD * BD + zp] : 0.f;
 
   const int nsteps = (te - tb + BC - 1) / BC;
   for (int s = nsteps - 1; s >= 0; --s) {
+    // the lane index, opaque to the optimiser once per step: every per-lane LDS address is then
+    // formed inside the step (a few bases plus immediates) rather than hoisted out of the loop
+    // as one live register per access
+    const int lane = pin(lane0), col = 32 * cw + (lane & 31);
     const int t0 = tb + s * BC, L = min(BC, te - t0);
     const long long r0 = sq.row0 + (long long)t0 * p.tok_rows;
-    Tile16 tq, tk, tv;
-    load_tile16(tq, (const uint16_t*)p.q + r0 * BD, L, rsb);
-    load_tile16(tk, (const uint16_t*)p.k + r0 * BD, L, rsb);
-    load_tile16(tv, (const uint16_t*)p.v + r0 * BD, L, rsb);
-    TileF tdo;
-    load_tileF<DBF>(tdo, (const unsigned char*)bp.dout + r0 * BD * (DBF ? 2 : 4), L, rsbd);
+    Tile16<KNT> tq, tk, tv;
+    load_tile16<KNT>(tq, (const uint16_t*)p.q + r0 * BD, L, rsb);
+    load_tile16<KNT>(tk, (const uint16_t*)p.k + r0 * BD, L, rsb);
+    load_tile16<KNT>(tv, (const uint16_t*)p.v + r0 * BD, L, rsb);
+    TileF<KNT> tdo;
+    load_tileF<KNT, DBF>(tdo, (const unsigned char*)bp.dout + r0 * BD * (DBF ? 2 : 4), L, rsbd);
     float inv = 1.f, dden = 0.f;
     if (NORM) {
-      const int j = tf_tok();
+      const int j = tf_tok<KNT>();
       if (j < L) {
         const float* tk2 = bp.tok + ((size_t)bh * p.T + (t0 + j)) * 2;
         inv = tk2[0];
@@ -557,46 +589,48 @@ __global__ __launch_bounds__(BNT) void k_bwd_key(BackwardParams bp) {
       }
     }
     lds_barrier();
-    commit_feat<ELU, ELU>(tq, sh + BG::QH, sh + BG::QL, L);
-    commit_feat<ELU, ELU>(tk, sh + BG::KH, sh + BG::KL, L);
-    commit_raw(tv, sh + BG::V);
-    commit_scaled(tdo, inv, sh + BG::NH, sh + BG::NL);
+    commit_feat<KNT, ELU, ELU>(tq, sh + BG::QH, sh + BG::QL, L);
+    commit_feat<KNT, ELU, ELU>(tk, sh + BG::KH, sh + BG::KL, L);
+    commit_raw<KNT>(tv, sh + BG::V);
+    commit_scaled<KNT>(tdo, inv, sh + BG::NH, sh + BG::NL);
     if (tid < BC) {
       const int j = tid;
       sf[BG::TH + j] = DECAY ? exp2f((float)(j + 1) * lg) : 1.f;
       sf[BG::XI + j] = j < L ? (DECAY ? exp2f((float)(L - 1 - j) * lg) : 1.f) : 0.f;
+      sf[BG::DM + j] = DECAY ? exp2f((float)j * lg) : 1.f;
     }
-    if (NORM && (tid & 3) == 0) sf[BG::DD + tf_tok()] = dden;
-    if (NORM && tid < BD) sf[BG::ZV + tid] = rz;
+    if (NORM && (tid % TileF<KNT>::TPT) == 0) sf[BG::DD + tf_tok<KNT>()] = dden;
+    if (NORM && role == 1 && zp < BD) sf[BG::ZV + zp] = rz;
     lds_barrier();
 
-    // A and Bm tiles (lower block triangle), hi + lo; jobs 0..2 are A, 3..5 are Bm
-    for (int job = w; job < 6; job += 4) {
-      if (job < 3) {
-        const int jt = job_jt(job), it = job_it(job);
+    // A tiles (role 0) and Bm tiles (role 1) of the lower block triangle, hi + lo
+    if (cw < 3) {
+      const int jt = job_jt(cw), it = job_it(cw);
+      if (role == 0) {
         const f32x16 acc = a_tile_acc<ELU>(sh, jt, it, lane);
         const int i = 32 * it + (lane & 31);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int j = 32 * jt + dtile_row(r, lane);
-          const bf16_pair pr = split_bf16(acc[r] * dmask<DECAY>(j, i, lg));
+          const bf16_pair pr = split_bf16(acc[r] * dmask<DECAY>(j, i, sf));
           sh[BG::AH + j * SQ + i] = pr.hi;
           sh[BG::AL + j * SQ + i] = pr.lo;
         }
       } else {
-        const int jt = job_jt(job - 3), it = job_it(job - 3);
         store_bm<DECAY, NORM, false>(sh, sf, x_tile_acc(sh, jt, it, lane), jt, it, L, lg, lane);
       }
     }
     lds_barrier();
+    const float a = DECAY ? exp2f((float)L * lg) : 1.f;
+    __builtin_amdgcn_sched_barrier(0);
 
-    // dV = A^T dNum + xi (F R): rows i, column e = col
-    {
+    if (role == 0) {
+      // dV = A^T dNum + xi (F R): rows i, column e = col
       f32x16 a2[2] = {zero16(), zero16()};
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt) {
         bf16x8 rh[2], rl[2];
-        split_dtile(R[pt], rh, rl);
+        split_dtile(St[pt], rh, rl);
 #pragma unroll
         for (int q = 0; q < 2; ++q)
 #pragma unroll
@@ -616,8 +650,8 @@ __global__ __launch_bounds__(BNT) void k_bwd_key(BackwardParams bp) {
         for (int k0 = 32 * it; k0 < BC; k0 += 16) {
           const bf16x8 ah = ld_rows8(sh + BG::AH, SQ, k0, 32 * it, lane);  // A[m=i][k=j] = A[j][i]
           const bf16x8 al = ld_rows8(sh + BG::AL, SQ, k0, 32 * it, lane);
-          const bf16x8 nh = ld_rows8(sh + BG::NH, TP, k0, 32 * w, lane);  // B[k=j][n=e]
-          const bf16x8 nl = ld_rows8(sh + BG::NL, TP, k0, 32 * w, lane);
+          const bf16x8 nh = ld_rows8(sh + BG::NH, TP, k0, 32 * cw, lane);  // B[k=j][n=e]
+          const bf16x8 nl = ld_rows8(sh + BG::NL, TP, k0, 32 * cw, lane);
           a1 = mfma32(ah, nh, a1);
           a1 = mfma32(ah, nl, a1);
           a1 = mfma32(al, nh, a1);
@@ -629,23 +663,44 @@ __global__ __launch_bounds__(BNT) void k_bwd_key(BackwardParams bp) {
           __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(g), rdv, (uint32_t)i * rsb4 + (uint32_t)col * 4, 0, 0);
         }
       }
-    }
-
-    // dF = Bm^T G + xi (V R^T + RZ): rows i, column p = col
-    __builtin_amdgcn_sched_barrier(0);
-    {
+      // R <- gamma^L R + (theta G)^T dNum: R[p][e] += sum_j (theta_j G[j][p]) dNum[j][e]
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        if (DECAY) St[t] *= a;
+#pragma unroll
+        for (int k0 = 0; k0 < BC; k0 += 16) {
+          const float* th = sf + BG::TH + k0 + 8 * (lane >> 5);
+          const bf16x8 ga = ld_rows8(sh + BG::QH, TP, k0, 32 * t, lane);  // A[m=p][k=j]
+          const bf16x8 nh = ld_rows8(sh + BG::NH, TP, k0, 32 * cw, lane);
+          const bf16x8 nl = ld_rows8(sh + BG::NL, TP, k0, 32 * cw, lane);
+          if (DECAY) {
+            bf16x8 gh, gl;
+            scale_split<ELU>(ga, ELU ? ld_rows8(sh + BG::QL, TP, k0, 32 * t, lane) : ga, th, gh, gl);
+            St[t] = mfma32(gh, nh, St[t]);
+            St[t] = mfma32(gh, nl, St[t]);
+            St[t] = mfma32(gl, nh, St[t]);
+          } else {
+            St[t] = mfma32(ga, nh, St[t]);
+            St[t] = mfma32(ga, nl, St[t]);
+            if (ELU) St[t] = mfma32(ld_rows8(sh + BG::QL, TP, k0, 32 * t, lane), nh, St[t]);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      // dF = Bm^T G + xi (V R^T + RZ): rows i, column p = col
       f32x16 a2[2] = {zero16(), zero16()};
 #pragma unroll
       for (int et = 0; et < 4; ++et) {
-        bf16x8 th[2], tl[2];
-        split_dtile(RT[et], th, tl);
+        bf16x8 th2[2], tl2[2];
+        split_dtile(St[et], th2, tl2);
 #pragma unroll
         for (int q = 0; q < 2; ++q)
 #pragma unroll
           for (int it = 0; it < 2; ++it) {
             const bf16x8 va = ld_cols8_perm(sh + BG::V, TP, 32 * it, 32 * et, q, lane);  // A[m=i][k=e]
-            a2[it] = mfma32(va, th[q], a2[it]);
-            a2[it] = mfma32(va, tl[q], a2[it]);
+            a2[it] = mfma32(va, th2[q], a2[it]);
+            a2[it] = mfma32(va, tl2[q], a2[it]);
           }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -658,10 +713,10 @@ __global__ __launch_bounds__(BNT) void k_bwd_key(BackwardParams bp) {
         for (int k0 = 32 * it; k0 < BC; k0 += 16) {
           const bf16x8 bmh = ld_rows8(sh + BG::BH, SQ, k0, 32 * it, lane);  // A[m=i][k=j] = Bm[j][i]
           const bf16x8 bml = ld_rows8(sh + BG::BL, SQ, k0, 32 * it, lane);
-          const bf16x8 gq = ld_rows8(sh + BG::QH, TP, k0, 32 * w, lane);  // B[k=j][n=p] = G[j][p]
+          const bf16x8 gq = ld_rows8(sh + BG::QH, TP, k0, 32 * cw, lane);  // B[k=j][n=p] = G[j][p]
           a1 = mfma32(bmh, gq, a1);
           a1 = mfma32(bml, gq, a1);
-          if (ELU) a1 = mfma32(bmh, ld_rows8(sh + BG::QL, TP, k0, 32 * w, lane), a1);
+          if (ELU) a1 = mfma32(bmh, ld_rows8(sh + BG::QL, TP, k0, 32 * cw, lane), a1);
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -672,63 +727,38 @@ __global__ __launch_bounds__(BNT) void k_bwd_key(BackwardParams bp) {
           __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(g), rdk, (uint32_t)i * rsb4 + (uint32_t)col * 4, 0, 0);
         }
       }
-    }
-
-    // adjoint state before this step: R <- gamma^L R + (theta G)^T dNum, RT likewise
-    const float a = DECAY ? exp2f((float)L * lg) : 1.f;
-    __builtin_amdgcn_sched_barrier(0);
+      // R^T <- gamma^L R^T + dNum^T (theta G): R^T[e][p] += sum_j dNum[j][e] (theta_j G[j][p])
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      if (DECAY) {
-        R[t] *= a;
-        RT[t] *= a;
-      }
+      for (int t = 0; t < 4; ++t) {
+        if (DECAY) St[t] *= a;
 #pragma unroll
-      for (int k0 = 0; k0 < BC; k0 += 16) {
-        const float* th = sf + BG::TH + k0 + 8 * (lane >> 5);
-        // R[p][e] += sum_j (theta_j G[j][p]) dNum[j][e]: tile pt = t, column e = col
-        {
-          const bf16x8 ga = ld_rows8(sh + BG::QH, TP, k0, 32 * t, lane);  // A[m=p][k=j]
-          const bf16x8 nh = ld_rows8(sh + BG::NH, TP, k0, 32 * w, lane);
-          const bf16x8 nl = ld_rows8(sh + BG::NL, TP, k0, 32 * w, lane);
-          if (DECAY) {
-            bf16x8 gh, gl;
-            scale_split<ELU>(ga, ELU ? ld_rows8(sh + BG::QL, TP, k0, 32 * t, lane) : ga, th, gh, gl);
-            R[t] = mfma32(gh, nh, R[t]);
-            R[t] = mfma32(gh, nl, R[t]);
-            R[t] = mfma32(gl, nh, R[t]);
-          } else {
-            R[t] = mfma32(ga, nh, R[t]);
-            R[t] = mfma32(ga, nl, R[t]);
-            if (ELU) R[t] = mfma32(ld_rows8(sh + BG::QL, TP, k0, 32 * t, lane), nh, R[t]);
-          }
-        }
-        // RT[e][p] += sum_j dNum[j][e] (theta_j G[j][p]): tile et = t, column p = col
-        {
+        for (int k0 = 0; k0 < BC; k0 += 16) {
+          const float* th = sf + BG::TH + k0 + 8 * (lane >> 5);
           const bf16x8 nh = ld_rows8(sh + BG::NH, TP, k0, 32 * t, lane);  // A[m=e][k=j] = dNum[j][e]
           const bf16x8 nl = ld_rows8(sh + BG::NL, TP, k0, 32 * t, lane);
-          const bf16x8 gb = ld_rows8(sh + BG::QH, TP, k0, 32 * w, lane);  // B[k=j][n=p]
+          const bf16x8 gb = ld_rows8(sh + BG::QH, TP, k0, 32 * cw, lane);  // B[k=j][n=p]
           if (DECAY) {
             bf16x8 gh, gl;
-            scale_split<ELU>(gb, ELU ? ld_rows8(sh + BG::QL, TP, k0, 32 * w, lane) : gb, th, gh, gl);
-            RT[t] = mfma32(nh, gh, RT[t]);
-            RT[t] = mfma32(nl, gh, RT[t]);
-            RT[t] = mfma32(nh, gl, RT[t]);
+            scale_split<ELU>(gb, ELU ? ld_rows8(sh + BG::QL, TP, k0, 32 * cw, lane) : gb, th, gh, gl);
+            St[t] = mfma32(nh, gh, St[t]);
+            St[t] = mfma32(nl, gh, St[t]);
+            St[t] = mfma32(nh, gl, St[t]);
           } else {
-            RT[t] = mfma32(nh, gb, RT[t]);
-            RT[t] = mfma32(nl, gb, RT[t]);
-            if (ELU) RT[t] = mfma32(nh, ld_rows8(sh + BG::QL, TP, k0, 32 * w, lane), RT[t]);
+            St[t] = mfma32(nh, gb, St[t]);
+            St[t] = mfma32(nl, gb, St[t]);
+            if (ELU) St[t] = mfma32(nh, ld_rows8(sh + BG::QL, TP, k0, 32 * cw, lane), St[t]);
           }
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
-    }
-    if (NORM && tid < BD) {
-      float zn = a * rz;
-      for (int j = 0; j < L; ++j) {
-        const float g = from_bf16(sh[BG::QH + j * TP + tid]) + (ELU ? from_bf16(sh[BG::QL + j * TP + tid]) : 0.f);
-        zn += sf[BG::TH + j] * g * sf[BG::DD + j];
+      if (NORM && zp < BD) {
+        float zn = a * rz;
+        for (int j = 0; j < L; ++j) {
+          const float g = from_bf16(sh[BG::QH + j * TP + zp]) + (ELU ? from_bf16(sh[BG::QL + j * TP + zp]) : 0.f);
+          zn += sf[BG::TH + j] * g * sf[BG::DD + j];
+        }
+        rz = zn;
       }
-      rz = zn;
     }
   }
 }
@@ -741,7 +771,7 @@ hipError_t launch4(const BackwardParams& p, hipStream_t s, bool key_sweep) {
   if (e != hipSuccess) return e;
   dim3 grid(p.f.B * p.f.H, p.f.n_seg);  // sequences on x: every XCD gets all segments of its sequences
   void* args[] = {(void*)&p};
-  e = hipLaunchKernel(kern, grid, dim3(BNT), args, BG::BYTES, s);
+  e = hipLaunchKernel(kern, grid, dim3(key_sweep ? KNT : BNT), args, BG::BYTES, s);
   if (e != hipSuccess) return e;
   return hipGetLastError();
 }
