@@ -278,8 +278,14 @@ __device__ __forceinline__ float dpsi_from_feat(float f) { return fminf(f, 1.f);
 
 // ---- query sweep -----------------------------------------------------------------------
 
+// Eight waves, specialised like the state sweep's: waves 0..3 hold S_<^T (feature columns
+// 32 cw..) and produce Y = dout S_<^T, dG and the state update; waves 4..7 hold the segment's
+// adjoint summary (value columns 32 cw..) and produce the X = dout V^T and A tiles, Bm and the
+// summary's update.
+constexpr int QNT = 512;
+
 template <bool ELU, bool DECAY, bool NORM, bool DBF>
-__global__ __launch_bounds__(BNT) void k_bwd_query(BackwardParams bp) {
+__global__ __launch_bounds__(QNT) void k_bwd_query(BackwardParams bp) {
   const PrefillParams& p = bp.f;
   extern __shared__ __align__(16) unsigned char smem[];
   __bf16* sh = (__bf16*)smem;
@@ -287,48 +293,46 @@ __global__ __launch_bounds__(BNT) void k_bwd_query(BackwardParams bp) {
   float* part = sf + BG::AH / 2;  // row partials: A sums [2][BC], A.X sums [2][BC], g.Y sums [4][BC]
   float* wi = part + 8 * BC;      // W_j / den_j, the adjoint summary's token weights
   const int bh = blockIdx.x, seg = blockIdx.y, tid = threadIdx.x, lane0 = tid & 63, w = tid >> 6;
+  const int role = w >> 2, cw = w & 3;
   const SeqSpan sq = seq_span(p, bh);
   const int T = sq.T;
   const int seg_tok = p.seg_chunks * p.C;
   const int tb = seg * seg_tok, te = min(tb + seg_tok, T);
   const size_t E = (size_t)BD * BD + BD;
   float* rrec = bp.rev + ((size_t)bh * p.n_seg + seg) * E;
-  const int col0 = 32 * w + (lane0 & 31);  // this lane's output column
-  f32x16 RS[4];                          // adjoint summary [p][e]: rows p in tile pt, column e = col
+  const int col0 = 32 * cw + (lane0 & 31);
+  // role 0: St[t] = S_<^T[e][p], rows e in tile t, column p = col
+  // role 1: St[t] = adjoint summary [p][e], rows p in tile t, column e = col
+  f32x16 St[4];
+  const float* pre = p.ws + ((size_t)bh * p.n_seg + seg) * E;
 #pragma unroll
-  for (int pt = 0; pt < 4; ++pt) RS[pt] = zero16();
-  float rz = 0.f;  // thread p < BD: the adjoint summary's Z part
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) St[t][r] = role == 0 && tb < te ? pre[(size_t)col0 * BD + 32 * t + dtile_row(r, lane0)] : 0.f;
+  const int zp = tid - QNT / 2;                                          // role-1 thread zp < BD: RZ[zp]
+  float zreg = (NORM && tid < BD && tb < te) ? pre[(size_t)BD * BD + tid] : 0.f;  // role-0 thread p: Z_<[p]
+  float rz = 0.f;
   if (tb < te) {
     const float lg = DECAY ? p.log2g[bh % p.H] : 0.f;
     const uint32_t rsb = (uint32_t)p.tok_rows * BD * 2, rsb4 = (uint32_t)p.tok_rows * BD * 4;
     const uint32_t rsbd = (uint32_t)p.tok_rows * BD * (DBF ? 2 : 4);
-    const float* pre = p.ws + ((size_t)bh * p.n_seg + seg) * E;
-    // the state before the step, transposed: ST[et] rows e in [32et, 32et + 32), column p = col
-    f32x16 ST[4];
-#pragma unroll
-    for (int et = 0; et < 4; ++et)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) ST[et][r] = pre[(size_t)col0 * BD + 32 * et + dtile_row(r, lane0)];
-    float zreg = (NORM && tid < BD) ? pre[(size_t)BD * BD + tid] : 0.f;  // Z_<[p] of thread p
 
     for (int t0 = tb; t0 < te; t0 += BC) {
-      // the lane index, opaque once per step (see the state sweep) where the denominator's extra
-      // row reductions would otherwise leave hoisted addresses spilling; without it the hoisted
-      // addresses fit and are cheaper
-      const int lane = NORM ? pin(lane0) : lane0, col = 32 * w + (lane & 31);
+      // the lane index, opaque once per step (see the state sweep)
+      const int lane = pin(lane0), col = 32 * cw + (lane & 31);
       const int L = min(BC, te - t0);
       const long long r0 = sq.row0 + (long long)t0 * p.tok_rows;
-      Tile16<BNT> tq, tk, tv;
-      load_tile16<BNT>(tq, (const uint16_t*)p.q + r0 * BD, L, rsb);
-      load_tile16<BNT>(tk, (const uint16_t*)p.k + r0 * BD, L, rsb);
-      load_tile16<BNT>(tv, (const uint16_t*)p.v + r0 * BD, L, rsb);
-      TileF<BNT> tdo;
-      load_tileF<BNT, DBF>(tdo, (const unsigned char*)bp.dout + r0 * BD * (DBF ? 2 : 4), L, rsbd);
+      Tile16<QNT> tq, tk, tv;
+      load_tile16<QNT>(tq, (const uint16_t*)p.q + r0 * BD, L, rsb);
+      load_tile16<QNT>(tk, (const uint16_t*)p.k + r0 * BD, L, rsb);
+      load_tile16<QNT>(tv, (const uint16_t*)p.v + r0 * BD, L, rsb);
+      TileF<QNT> tdo;
+      load_tileF<QNT, DBF>(tdo, (const unsigned char*)bp.dout + r0 * BD * (DBF ? 2 : 4), L, rsbd);
       lds_barrier();  // the previous step is done with LDS
-      commit_feat<BNT, ELU, ELU>(tq, sh + BG::QH, sh + BG::QL, L);
-      commit_feat<BNT, ELU, ELU>(tk, sh + BG::KH, sh + BG::KL, L);
-      commit_raw<BNT>(tv, sh + BG::V);
-      commit_scaled<BNT>(tdo, 1.f, sh + BG::NH, sh + BG::NL);  // dout as hi + lo
+      commit_feat<QNT, ELU, ELU>(tq, sh + BG::QH, sh + BG::QL, L);
+      commit_feat<QNT, ELU, ELU>(tk, sh + BG::KH, sh + BG::KL, L);
+      commit_raw<QNT>(tv, sh + BG::V);
+      commit_scaled<QNT>(tdo, 1.f, sh + BG::NH, sh + BG::NL);  // dout as hi + lo
       if (tid < BC) {
         const int j = tid;
         sf[BG::TH + j] = DECAY ? exp2f((float)(j + 1) * lg) : 1.f;
@@ -344,73 +348,77 @@ __global__ __launch_bounds__(BNT) void k_bwd_query(BackwardParams bp) {
       if (NORM && tid < BD) sf[BG::ZV + tid] = zreg;
       lds_barrier();
 
-      // X = dout V^T tiles (lower block triangle, waves 0..2), kept in registers; with a
-      // denominator also A = G F^T and the row partials sum_i A_ji and sum_i A_ji X_ji
-      f32x16 X = zero16();
-      if (w < 3) {
-        const int jt = job_jt(w), it = job_it(w);
-        X = x_tile_acc(sh, jt, it, lane);
-        if (NORM) {
-          const f32x16 A = a_tile_acc<ELU>(sh, jt, it, lane);
-          f32x16 Am, AX;
-          const int i = 32 * it + (lane & 31);
+      f32x16 X = zero16();  // role 1, cw < 3: the X = dout V^T tile of the lower block triangle
+      f32x16 Y[2];          // role 0: Y = dout S_<^T, rows j, column p = col
+      if (role == 1) {
+        if (cw < 3) {
+          const int jt = job_jt(cw), it = job_it(cw);
+          X = x_tile_acc(sh, jt, it, lane);
+          if (NORM) {  // A = G F^T and the row partials sum_i A_ji, sum_i A_ji X_ji
+            const f32x16 A = a_tile_acc<ELU>(sh, jt, it, lane);
+            f32x16 Am, AX;
+            const int i = 32 * it + (lane & 31);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            Am[r] = A[r] * dmask<DECAY>(32 * jt + dtile_row(r, lane), i, sf);
-            AX[r] = Am[r] * X[r];
+            for (int r = 0; r < 16; ++r) {
+              Am[r] = A[r] * dmask<DECAY>(32 * jt + dtile_row(r, lane), i, sf);
+              AX[r] = Am[r] * X[r];
+            }
+            const float sa = rowsum16(Am, lane), sx = rowsum16(AX, lane);
+            if ((lane & 1) == 0) {
+              const int j = 32 * jt + rowsum16_row(lane);
+              part[it * BC + j] = sa;
+              part[2 * BC + it * BC + j] = sx;
+            }
           }
-          const float sa = rowsum16(Am, lane), sx = rowsum16(AX, lane);
-          if ((lane & 1) == 0) {
-            const int j = 32 * jt + rowsum16_row(lane);
-            part[it * BC + j] = sa;
-            part[2 * BC + it * BC + j] = sx;
-          }
+        } else if (NORM && lane < 32) {  // the upper tile (0, 1) is zero
+          part[BC + lane] = 0.f;
+          part[3 * BC + lane] = 0.f;
         }
-      } else if (NORM && lane < 32) {  // the upper tile (0, 1) is zero
-        part[BC + lane] = 0.f;
-        part[3 * BC + lane] = 0.f;
-      }
-      // Y = dout S_<^T (rows j, column p = col), kept in registers
-      f32x16 Y[2] = {zero16(), zero16()};
+      } else {
+        Y[0] = zero16();
+        Y[1] = zero16();
 #pragma unroll
-      for (int et = 0; et < 4; ++et) {
-        bf16x8 sth[2], stl[2];
-        split_dtile(ST[et], sth, stl);
+        for (int et = 0; et < 4; ++et) {
+          bf16x8 sth[2], stl[2];
+          split_dtile(St[et], sth, stl);
 #pragma unroll
-        for (int q = 0; q < 2; ++q)
+          for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+            for (int jt = 0; jt < 2; ++jt) {
+              const bf16x8 nh = ld_cols8_perm(sh + BG::NH, TP, 32 * jt, 32 * et, qq, lane);
+              const bf16x8 nl = ld_cols8_perm(sh + BG::NL, TP, 32 * jt, 32 * et, qq, lane);
+              Y[jt] = mfma32(nh, sth[qq], Y[jt]);
+              Y[jt] = mfma32(nh, stl[qq], Y[jt]);
+              Y[jt] = mfma32(nl, sth[qq], Y[jt]);
+            }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (NORM) {  // row partials of g_j . Y_j over this wave's 32 features
 #pragma unroll
           for (int jt = 0; jt < 2; ++jt) {
-            const bf16x8 nh = ld_cols8_perm(sh + BG::NH, TP, 32 * jt, 32 * et, q, lane);
-            const bf16x8 nl = ld_cols8_perm(sh + BG::NL, TP, 32 * jt, 32 * et, q, lane);
-            Y[jt] = mfma32(nh, sth[q], Y[jt]);
-            Y[jt] = mfma32(nh, stl[q], Y[jt]);
-            Y[jt] = mfma32(nl, sth[q], Y[jt]);
+            f32x16 gy;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int j = 32 * jt + dtile_row(r, lane);
+              const float g = from_bf16(sh[BG::QH + j * TP + col]) + (ELU ? from_bf16(sh[BG::QL + j * TP + col]) : 0.f);
+              gy[r] = g * Y[jt][r];
+            }
+            const float sy = rowsum16(gy, lane);
+            if ((lane & 1) == 0) part[(4 + cw) * BC + 32 * jt + rowsum16_row(lane)] = sy;
           }
-        __builtin_amdgcn_sched_barrier(0);
+        }
       }
       if (NORM) {
-        // row partials of g_j . Y_j over this wave's 32 features
-#pragma unroll
-        for (int jt = 0; jt < 2; ++jt) {
-          f32x16 gy;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int j = 32 * jt + dtile_row(r, lane);
-            const float g = from_bf16(sh[BG::QH + j * TP + col]) + (ELU ? from_bf16(sh[BG::QL + j * TP + col]) : 0.f);
-            gy[r] = g * Y[jt][r];
-          }
-          const float sy = rowsum16(gy, lane);
-          if ((lane & 1) == 0) part[(4 + w) * BC + 32 * jt + rowsum16_row(lane)] = sy;
-        }
         lds_barrier();
         // per token: den, dout . num, 1/den and dden = -(dout . num) / den^2
-        const int j = tf_tok<BNT>(), qq = tid & 3;
+        constexpr int TPT = TileF<QNT>::TPT, FW = BD / TPT;
+        const int j = tf_tok<QNT>(), qq = tid % TPT;
         float zs = 0.f;
-        for (int pp = 32 * qq; pp < 32 * qq + 32; ++pp) {
+        for (int pp = FW * qq; pp < FW * qq + FW; ++pp) {
           const float g = from_bf16(sh[BG::QH + j * TP + pp]) + (ELU ? from_bf16(sh[BG::QL + j * TP + pp]) : 0.f);
           zs += g * sf[BG::ZV + pp];
         }
-        zs = token_sum<BNT>(zs);
+        zs = token_sum<QNT>(zs);
         if (qq == 0) {
           const float th = sf[BG::TH + j];
           const float den = part[j] + part[BC + j] + th * zs + p.eps;
@@ -432,98 +440,106 @@ __global__ __launch_bounds__(BNT) void k_bwd_query(BackwardParams bp) {
       }
 
       // Bm tiles as hi + lo
-      if (w < 3) store_bm<DECAY, NORM, true>(sh, sf, X, job_jt(w), job_it(w), L, lg, lane);
+      if (role == 1 && cw < 3) store_bm<DECAY, NORM, true>(sh, sf, X, job_jt(cw), job_it(cw), L, lg, lane);
       lds_barrier();
 
-      // dG = Bm F + theta (inv Y + dden Z_<): rows j, column p = col
-      const __amdgpu_buffer_rsrc_t rdq = make_rsrc(bp.dq + r0 * BD, rows_extent(L, rsb4, BD * 4));
-      const float zp = NORM ? sf[BG::ZV + col] : 0.f;
+      if (role == 0) {
+        // dG = Bm F + theta (inv Y + dden Z_<): rows j, column p = col
+        const __amdgpu_buffer_rsrc_t rdq = make_rsrc(bp.dq + r0 * BD, rows_extent(L, rsb4, BD * 4));
+        const float zpv = NORM ? sf[BG::ZV + col] : 0.f;
 #pragma unroll
-      for (int jt = 0; jt < 2; ++jt) {
-        f32x16 a1 = zero16();
+        for (int jt = 0; jt < 2; ++jt) {
+          f32x16 a1 = zero16();
 #pragma unroll
-        for (int k0 = 0; k0 < 32 * (jt + 1); k0 += 16) {
-          const bf16x8 kh = ld_rows8(sh + BG::KH, TP, k0, 32 * w, lane);  // B[k=i][n=p] = F[i][p]
-          const bf16x8 bmh = ld_cols8(sh + BG::BH, SQ, 32 * jt, k0, lane);  // A[m=j][k=i] = Bm[j][i]
-          const bf16x8 bml = ld_cols8(sh + BG::BL, SQ, 32 * jt, k0, lane);
-          a1 = mfma32(bmh, kh, a1);
-          a1 = mfma32(bml, kh, a1);
-          if (ELU) a1 = mfma32(bmh, ld_rows8(sh + BG::KL, TP, k0, 32 * w, lane), a1);
-        }
+          for (int k0 = 0; k0 < 32 * (jt + 1); k0 += 16) {
+            const bf16x8 kh = ld_rows8(sh + BG::KH, TP, k0, 32 * cw, lane);  // B[k=i][n=p] = F[i][p]
+            const bf16x8 bmh = ld_cols8(sh + BG::BH, SQ, 32 * jt, k0, lane);  // A[m=j][k=i] = Bm[j][i]
+            const bf16x8 bml = ld_cols8(sh + BG::BL, SQ, 32 * jt, k0, lane);
+            a1 = mfma32(bmh, kh, a1);
+            a1 = mfma32(bml, kh, a1);
+            if (ELU) a1 = mfma32(bmh, ld_rows8(sh + BG::KL, TP, k0, 32 * cw, lane), a1);
+          }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int j = 32 * jt + dtile_row(r, lane);
-          const float st = NORM ? sf[BG::IV + j] * Y[jt][r] + sf[BG::DD + j] * zp : Y[jt][r];
-          float g = a1[r] + sf[BG::TH + j] * st;
-          if (ELU)
-            g *= dpsi_from_feat(from_bf16(sh[BG::QH + j * TP + col]) + from_bf16(sh[BG::QL + j * TP + col]));
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(g), rdq, (uint32_t)j * rsb4 + (uint32_t)col * 4, 0, 0);
-        }
-      }
-
-      // adjoint summary: RS[p][e] += sum_j (W_j inv_j G[j][p]) dout[j][e]
-#pragma unroll
-      for (int pt = 0; pt < 4; ++pt)
-#pragma unroll
-        for (int k0 = 0; k0 < BC; k0 += 16) {
-          const bf16x8 gh = ld_rows8(sh + BG::QH, TP, k0, 32 * pt, lane);  // A[m=p][k=j] = G[j][p]
-          const bf16x8 nh = ld_rows8(sh + BG::NH, TP, k0, 32 * w, lane);   // B[k=j][n=e]
-          const bf16x8 nl = ld_rows8(sh + BG::NL, TP, k0, 32 * w, lane);
-          if (DECAY || NORM) {
-            bf16x8 sh2, sl2;
-            const bf16x8 gl = ELU ? ld_rows8(sh + BG::QL, TP, k0, 32 * pt, lane) : gh;
-            scale_split<ELU>(gh, gl, wi + k0 + 8 * (lane >> 5), sh2, sl2);
-            RS[pt] = mfma32(sh2, nh, RS[pt]);
-            RS[pt] = mfma32(sh2, nl, RS[pt]);
-            RS[pt] = mfma32(sl2, nh, RS[pt]);
-          } else {
-            RS[pt] = mfma32(gh, nh, RS[pt]);
-            RS[pt] = mfma32(gh, nl, RS[pt]);
-            if (ELU) RS[pt] = mfma32(ld_rows8(sh + BG::QL, TP, k0, 32 * pt, lane), nh, RS[pt]);
+          for (int r = 0; r < 16; ++r) {
+            const int j = 32 * jt + dtile_row(r, lane);
+            const float st = NORM ? sf[BG::IV + j] * Y[jt][r] + sf[BG::DD + j] * zpv : Y[jt][r];
+            float g = a1[r] + sf[BG::TH + j] * st;
+            if (ELU)
+              g *= dpsi_from_feat(from_bf16(sh[BG::QH + j * TP + col]) + from_bf16(sh[BG::QL + j * TP + col]));
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(g), rdq, (uint32_t)j * rsb4 + (uint32_t)col * 4, 0, 0);
           }
         }
-      if (NORM && tid < BD) {
-        for (int j = 0; j < L; ++j) {
-          const float g = from_bf16(sh[BG::QH + j * TP + tid]) + (ELU ? from_bf16(sh[BG::QL + j * TP + tid]) : 0.f);
-          rz += sf[BG::WT + j] * g * sf[BG::DD + j];
+        __builtin_amdgcn_sched_barrier(0);
+        // state: S_< <- gamma^L S_< + F^T (xi V), held transposed: S^T[e][p] += sum_i (xi_i V[i][e]) F[i][p]
+        const float a = DECAY ? exp2f((float)L * lg) : 1.f;
+#pragma unroll
+        for (int et = 0; et < 4; ++et) {
+          if (DECAY) St[et] *= a;
+#pragma unroll
+          for (int k0 = 0; k0 < BC; k0 += 16) {
+            const bf16x8 va = ld_rows8(sh + BG::V, TP, k0, 32 * et, lane);  // A[m=e][k=i] = V[i][e]
+            const bf16x8 kh = ld_rows8(sh + BG::KH, TP, k0, 32 * cw, lane);  // B[k=i][n=p] = F[i][p]
+            if (DECAY) {
+              bf16x8 vh, vl;
+              scale_split<false>(va, va, sf + BG::XI + k0 + 8 * (lane >> 5), vh, vl);
+              St[et] = mfma32(vh, kh, St[et]);
+              St[et] = mfma32(vl, kh, St[et]);
+              if (ELU) St[et] = mfma32(vh, ld_rows8(sh + BG::KL, TP, k0, 32 * cw, lane), St[et]);
+            } else {
+              St[et] = mfma32(va, kh, St[et]);  // rows past L are zero in F
+              if (ELU) St[et] = mfma32(va, ld_rows8(sh + BG::KL, TP, k0, 32 * cw, lane), St[et]);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
-      }
-
-      // state: S_< <- gamma^L S_< + F^T (xi V), held transposed: ST[e][p] += sum_i (xi_i V[i][e]) F[i][p]
-      const float a = DECAY ? exp2f((float)L * lg) : 1.f;
+        if (NORM && tid < BD) {
+          float zn = a * zreg;
+          for (int i = 0; i < L; ++i)
+            zn += sf[BG::XI + i] *
+                  (from_bf16(sh[BG::KH + i * TP + tid]) + (ELU ? from_bf16(sh[BG::KL + i * TP + tid]) : 0.f));
+          zreg = zn;
+        }
+      } else {
+        // adjoint summary: [p][e] += sum_j (W_j inv_j G[j][p]) dout[j][e]
 #pragma unroll
-      for (int et = 0; et < 4; ++et) {
-        if (DECAY) ST[et] *= a;
+        for (int pt = 0; pt < 4; ++pt) {
 #pragma unroll
-        for (int k0 = 0; k0 < BC; k0 += 16) {
-          const bf16x8 va = ld_rows8(sh + BG::V, TP, k0, 32 * et, lane);  // A[m=e][k=i] = V[i][e]
-          const bf16x8 kh = ld_rows8(sh + BG::KH, TP, k0, 32 * w, lane);  // B[k=i][n=p] = F[i][p]
-          if (DECAY) {
-            bf16x8 vh, vl;
-            scale_split<false>(va, va, sf + BG::XI + k0 + 8 * (lane >> 5), vh, vl);
-            ST[et] = mfma32(vh, kh, ST[et]);
-            ST[et] = mfma32(vl, kh, ST[et]);
-            if (ELU) ST[et] = mfma32(vh, ld_rows8(sh + BG::KL, TP, k0, 32 * w, lane), ST[et]);
-          } else {
-            ST[et] = mfma32(va, kh, ST[et]);  // rows past L are zero in F
-            if (ELU) ST[et] = mfma32(va, ld_rows8(sh + BG::KL, TP, k0, 32 * w, lane), ST[et]);
+          for (int k0 = 0; k0 < BC; k0 += 16) {
+            const bf16x8 gh = ld_rows8(sh + BG::QH, TP, k0, 32 * pt, lane);  // A[m=p][k=j] = G[j][p]
+            const bf16x8 nh = ld_rows8(sh + BG::NH, TP, k0, 32 * cw, lane);  // B[k=j][n=e]
+            const bf16x8 nl = ld_rows8(sh + BG::NL, TP, k0, 32 * cw, lane);
+            if (DECAY || NORM) {
+              bf16x8 sh2, sl2;
+              const bf16x8 gl = ELU ? ld_rows8(sh + BG::QL, TP, k0, 32 * pt, lane) : gh;
+              scale_split<ELU>(gh, gl, wi + k0 + 8 * (lane >> 5), sh2, sl2);
+              St[pt] = mfma32(sh2, nh, St[pt]);
+              St[pt] = mfma32(sh2, nl, St[pt]);
+              St[pt] = mfma32(sl2, nh, St[pt]);
+            } else {
+              St[pt] = mfma32(gh, nh, St[pt]);
+              St[pt] = mfma32(gh, nl, St[pt]);
+              if (ELU) St[pt] = mfma32(ld_rows8(sh + BG::QL, TP, k0, 32 * pt, lane), nh, St[pt]);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (NORM && zp < BD) {
+          for (int j = 0; j < L; ++j) {
+            const float g = from_bf16(sh[BG::QH + j * TP + zp]) + (ELU ? from_bf16(sh[BG::QL + j * TP + zp]) : 0.f);
+            rz += sf[BG::WT + j] * g * sf[BG::DD + j];
           }
         }
-      }
-      if (NORM && tid < BD) {
-        float zn = a * zreg;
-        for (int i = 0; i < L; ++i)
-          zn += sf[BG::XI + i] * (from_bf16(sh[BG::KH + i * TP + tid]) + (ELU ? from_bf16(sh[BG::KL + i * TP + tid]) : 0.f));
-        zreg = zn;
       }
     }
   }
-  // the segment's adjoint summary [S (p, e)][Z (p)]
+  // the segment's adjoint summary [S (p, e)][Z (p)] (role 1; zero for an empty segment)
+  if (role == 1) {
 #pragma unroll
-  for (int pt = 0; pt < 4; ++pt)
+    for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) rrec[(size_t)(32 * pt + dtile_row(r, lane0)) * BD + col0] = RS[pt][r];
-  if (tid < BD) rrec[(size_t)BD * BD + tid] = rz;
+      for (int r = 0; r < 16; ++r) rrec[(size_t)(32 * pt + dtile_row(r, lane0)) * BD + col0] = St[pt][r];
+    if (zp < BD) rrec[(size_t)BD * BD + zp] = rz;
+  }
 }
 
 // ---- state sweep -----------------------------------------------------------------------
@@ -771,7 +787,7 @@ hipError_t launch4(const BackwardParams& p, hipStream_t s, bool key_sweep) {
   if (e != hipSuccess) return e;
   dim3 grid(p.f.B * p.f.H, p.f.n_seg);  // sequences on x: every XCD gets all segments of its sequences
   void* args[] = {(void*)&p};
-  e = hipLaunchKernel(kern, grid, dim3(key_sweep ? KNT : BNT), args, BG::BYTES, s);
+  e = hipLaunchKernel(kern, grid, dim3(key_sweep ? KNT : QNT), args, BG::BYTES, s);
   if (e != hipSuccess) return e;
   return hipGetLastError();
 }
