@@ -36,6 +36,12 @@ KERNELS = {
     "k_output_prf<64, 128, 256, false, true, false, false>": "k_output_prf256_4k",
     "k_output_prf<64, 128, 256, false, true, false, true>": "k_output_prf256_4k_qshift",
     "k_summary_prf<64, 128, 256, false, true>": "k_summary_prf256_4k",
+    "k_output_gla_m<128, false>": "k_output_gated_8k",
+    "k_summary_gla_m<128>": "k_summary_gated_8k",
+    "k_bwd_query<false, true, false, false>": "k_bwd_query_retnet_128k",
+    "k_bwd_key<false, true, false, false>": "k_bwd_key_retnet_128k",
+    "k_bwd_query<true, false, true, false>": "k_bwd_query_elu1_8k",
+    "k_bwd_key<true, false, true, false>": "k_bwd_key_elu1_8k",
 }
 
 

@@ -45,6 +45,10 @@ CASES = [
     ("elu1_norm_d128_bthd", 1, 2, 200, 128, PSI_ELU1, 1, "bf16", 16.0, "bthd"),
     ("f32_identity_d64_strong", 1, 2, 190, 64, PSI_IDENTITY, 0, "f32", 1.0, "bhtd"),
     ("f32_elu1_norm_d128", 1, 2, 130, 128, PSI_ELU1, 1, "f32", 8.0, "bthd"),
+    # log gates averaging -8 per token: every running product of gates underflows within a
+    # chunk; the path must stay finite and exact (each output is its own token's)
+    ("identity_d128_extreme_gates", 1, 2, 150, 128, PSI_IDENTITY, 0, "bf16", 0.1, "bhtd"),
+    ("elu1_norm_d64_extreme_gates", 1, 2, 100, 64, PSI_ELU1, 1, "bf16", 0.1, "bhtd"),
 ]
 
 
