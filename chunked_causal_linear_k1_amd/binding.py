@@ -27,7 +27,8 @@ MAX_DECAY_HEADS = 256
 EXPORTED = ("lin_attn_prefill_workspace_size", "lin_attn_prefill", "lin_attn_prefill_profiled",
             "lin_attn_prefill_varlen", "lin_attn_prefill_varlen_workspace_size", "lin_attn_prefill_gated",
             "lin_attn_prefill_gated_workspace_size", "lin_attn_prefill_backward",
-            "lin_attn_prefill_backward_workspace_size", "lin_attn_decode_step", "lin_attn_decode_step_gated",
+            "lin_attn_prefill_backward_workspace_size", "lin_attn_prefill_backward_varlen",
+            "lin_attn_prefill_backward_varlen_workspace_size", "lin_attn_decode_step", "lin_attn_decode_step_gated",
             "lin_attn_status_string", "lin_attn_version")
 
 
@@ -88,6 +89,12 @@ def load() -> ctypes.CDLL:
         lib.lin_attn_prefill_backward_workspace_size.restype = ctypes.c_int
         lib.lin_attn_prefill_backward_workspace_size.argtypes = [ctypes.POINTER(PrefillDesc),
                                                                  ctypes.POINTER(ctypes.c_size_t)]
+        lib.lin_attn_prefill_backward_varlen.restype = ctypes.c_int
+        lib.lin_attn_prefill_backward_varlen.argtypes = [ctypes.POINTER(PrefillDesc), vp, ctypes.c_int32, vp, vp, vp,
+                                                         fp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        lib.lin_attn_prefill_backward_varlen_workspace_size.restype = ctypes.c_int
+        lib.lin_attn_prefill_backward_varlen_workspace_size.argtypes = [ctypes.POINTER(PrefillDesc), ctypes.c_int32,
+                                                                        ctypes.POINTER(ctypes.c_size_t)]
         lib.lin_attn_decode_step_gated.restype = ctypes.c_int
         lib.lin_attn_decode_step_gated.argtypes = [ctypes.POINTER(DecodeDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.lin_attn_decode_step.restype = ctypes.c_int
@@ -284,6 +291,51 @@ def lin_attn_prefill_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         workspace.numel() * workspace.element_size(), _stream(stream))
     if st != LA_OK:
         raise LinAttnError(st, "lin_attn_prefill_backward")
+    return dq, dk, dv
+
+
+def backward_varlen_workspace_size(desc: PrefillDesc, total_tokens: int) -> int:
+    n = ctypes.c_size_t(0)
+    st = load().lin_attn_prefill_backward_varlen_workspace_size(ctypes.byref(desc), int(total_tokens),
+                                                                ctypes.byref(n))
+    if st != LA_OK:
+        raise LinAttnError(st, "lin_attn_prefill_backward_varlen_workspace_size")
+    return int(n.value)
+
+
+def lin_attn_prefill_backward_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch.Tensor,
+                                     cu_seqlens: torch.Tensor, max_seqlen: int, *, psi: int, chunk: int,
+                                     normalize: int = 1, eps: float = 1e-6, gamma: Optional[Sequence[float]] = None,
+                                     init_S: Optional[torch.Tensor] = None, init_Z: Optional[torch.Tensor] = None,
+                                     dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
+                                     dv: Optional[torch.Tensor] = None, dinit_S: Optional[torch.Tensor] = None,
+                                     dinit_Z: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                                     stream=None):
+    """(dq, dk, dv) of L = sum dout . o for lin_attn_prefill_varlen with the same arguments: q, k, v,
+    dout [total, H, d]; cu_seqlens int32 [N + 1] on the device. Gradients are float32 [total, H, d];
+    dinit_S [N, H, d_k, d_v] / dinit_Z [N, H, d_k] are written when given."""
+    total, H, d_k = q.shape
+    d_v = v.shape[-1]
+    N = cu_seqlens.numel() - 1
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.device != q.device:
+        raise ValueError("cu_seqlens must be an int32 tensor on the inputs' device")
+    for t in (q, k, v, dout, cu_seqlens):
+        if not t.is_contiguous():
+            raise ValueError("q, k, v, dout [total, H, d] and cu_seqlens must be contiguous")
+    dq = torch.empty(q.shape, dtype=torch.float32, device=q.device) if dq is None else dq
+    dk = torch.empty(k.shape, dtype=torch.float32, device=q.device) if dk is None else dk
+    dv = torch.empty(v.shape, dtype=torch.float32, device=q.device) if dv is None else dv
+    desc = prefill_desc(N, H, max_seqlen, d_k, d_v, d_k, chunk, psi, normalize, eps, _dtype_code(q),
+                        _dtype_code(dout), LA_LAYOUT_BTHD)
+    ws_bytes = backward_varlen_workspace_size(desc, total)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    st = load().lin_attn_prefill_backward_varlen(
+        ctypes.byref(desc), _ptr(cu_seqlens), total, _ptr(q), _ptr(k), _ptr(v), _gamma_array(gamma, H),
+        _ptr(init_S), _ptr(init_Z), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dinit_S), _ptr(dinit_Z),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    if st != LA_OK:
+        raise LinAttnError(st, "lin_attn_prefill_backward_varlen")
     return dq, dk, dv
 
 

@@ -157,9 +157,11 @@ la_status validate_backward_desc(const la_prefill_desc* d) {
   return la::prefill_backward_supported(d->chunk, d->d_k, d->d_v, d->n_psi, d->psi) ? LA_OK : LA_ERR_UNSUPPORTED;
 }
 
-size_t backward_ws_bytes(const la_prefill_desc* d) {
-  const size_t tok = d->normalize ? (size_t)d->B * d->H * d->T * 2 * sizeof(float) : 0;
-  return 2 * make_plan(d).ws_bytes + tok;
+// total_tokens < 0: a fixed-length batch; otherwise a packed batch of that many tokens.
+size_t backward_ws_bytes(const la_prefill_desc* d, long long total_tokens = -1) {
+  const long long rows = total_tokens < 0 ? (long long)d->B * d->T * d->H : total_tokens * d->H;
+  const size_t tok = d->normalize ? (size_t)rows * 2 * sizeof(float) : 0;
+  return 2 * make_plan(d, total_tokens).ws_bytes + tok;
 }
 
 la_status lin_attn_prefill_backward_workspace_size(const la_prefill_desc* d, size_t* bytes) {
@@ -167,6 +169,16 @@ la_status lin_attn_prefill_backward_workspace_size(const la_prefill_desc* d, siz
   const la_status st = validate_backward_desc(d);
   if (st != LA_OK) return st;
   *bytes = backward_ws_bytes(d);
+  return LA_OK;
+}
+
+la_status lin_attn_prefill_backward_varlen_workspace_size(const la_prefill_desc* d, int32_t total_tokens,
+                                                          size_t* bytes) {
+  if (!bytes) return LA_ERR_NULL;
+  const la_status st = validate_backward_desc(d);
+  if (st != LA_OK) return st;
+  if (total_tokens < 0) return LA_ERR_SHAPE;
+  *bytes = backward_ws_bytes(d, total_tokens);
   return LA_OK;
 }
 
@@ -352,12 +364,23 @@ la_status lin_attn_decode_step_gated(const la_decode_desc* d, const void* q, con
   return decode_impl(d, q, k, v, nullptr, log_gate, prf_w, S, Z, o, stream);
 }
 
-la_status lin_attn_prefill_backward(const la_prefill_desc* d, const void* q, const void* k, const void* v,
-                                    const float* gamma, const float* init_S, const float* init_Z, const void* dout,
-                                    float* dq, float* dk, float* dv, float* dinit_S, float* dinit_Z,
-                                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Both backward entry points: fixed-length batches (cu_seqlens == nullptr) and packed
+// variable-length batches.
+la_status backward_impl(const la_prefill_desc* d, const int32_t* cu_seqlens, int32_t total_tokens, const void* q,
+                        const void* k, const void* v, const float* gamma, const float* init_S, const float* init_Z,
+                        const void* dout, float* dq, float* dk, float* dv, float* dinit_S, float* dinit_Z,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
   la_status st = validate_backward_desc(d);
   if (st != LA_OK) return st;
+  if (cu_seqlens) {
+    if (d->layout != LA_LAYOUT_BTHD) return LA_ERR_VALUE;
+    if (total_tokens < 0) return LA_ERR_SHAPE;
+    if ((reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0) return LA_ERR_ALIGN;
+  }
   if (!q || !k || !v || !dout || !dq || !dk || !dv) return LA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned16(dq) ||
       !aligned16(dk) || !aligned16(dv) || !aligned16(init_S) || !aligned16(init_Z) || !aligned16(dinit_S) ||
@@ -365,8 +388,9 @@ la_status lin_attn_prefill_backward(const la_prefill_desc* d, const void* q, con
     return LA_ERR_ALIGN;
   st = check_gamma(gamma, d->H);
   if (st != LA_OK) return st;
-  const Plan pl = make_plan(d);
-  const size_t need = backward_ws_bytes(d);
+  const long long tt = cu_seqlens ? (long long)total_tokens : -1LL;
+  const Plan pl = make_plan(d, tt);
+  const size_t need = backward_ws_bytes(d, tt);
   if (!workspace || workspace_bytes < need) return LA_ERR_WORKSPACE;
 
   la::BackwardParams bp;
@@ -374,6 +398,8 @@ la_status lin_attn_prefill_backward(const la_prefill_desc* d, const void* q, con
   PrefillParams& p = bp.f;
   p.q = q; p.k = k; p.v = v;
   p.ws = (float*)workspace;
+  p.cu_seqlens = cu_seqlens;
+  p.total = cu_seqlens ? total_tokens : 0;
   p.B = d->B; p.H = d->H; p.T = d->T;
   if (d->layout == LA_LAYOUT_BTHD) {
     p.tok_rows = d->H; p.head_rows = 1; p.seq_rows = (long long)d->T * d->H;
@@ -395,6 +421,7 @@ la_status lin_attn_prefill_backward(const la_prefill_desc* d, const void* q, con
   sp.ws = p.ws;
   sp.init_S = init_S;
   sp.init_Z = d->normalize ? init_Z : nullptr;
+  sp.cu_seqlens = cu_seqlens; sp.total = p.total;
   sp.BH = d->B * d->H; sp.H = d->H; sp.T = d->T;
   sp.n_psi = d->n_psi; sp.d_v = d->d_v;
   sp.n_seg = pl.n_seg; sp.seg_len = pl.seg_chunks * d->chunk;
@@ -413,6 +440,28 @@ la_status lin_attn_prefill_backward(const la_prefill_desc* d, const void* q, con
   if (e == hipSuccess) e = la::launch_segment_scan(rp, stream);          // adjoint state after each segment
   if (e == hipSuccess) e = la::launch_prefill_backward(bp, stream, true);   // state sweep: dk, dv
   return e == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+la_status lin_attn_prefill_backward(const la_prefill_desc* d, const void* q, const void* k, const void* v,
+                                    const float* gamma, const float* init_S, const float* init_Z, const void* dout,
+                                    float* dq, float* dk, float* dv, float* dinit_S, float* dinit_Z,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return backward_impl(d, nullptr, 0, q, k, v, gamma, init_S, init_Z, dout, dq, dk, dv, dinit_S, dinit_Z, workspace,
+                       workspace_bytes, stream);
+}
+
+la_status lin_attn_prefill_backward_varlen(const la_prefill_desc* d, const int32_t* cu_seqlens, int32_t total_tokens,
+                                           const void* q, const void* k, const void* v, const float* gamma,
+                                           const float* init_S, const float* init_Z, const void* dout, float* dq,
+                                           float* dk, float* dv, float* dinit_S, float* dinit_Z, void* workspace,
+                                           size_t workspace_bytes, hipStream_t stream) {
+  if (!cu_seqlens) return LA_ERR_NULL;
+  return backward_impl(d, cu_seqlens, total_tokens, q, k, v, gamma, init_S, init_Z, dout, dq, dk, dv, dinit_S,
+                       dinit_Z, workspace, workspace_bytes, stream);
 }
 
 la_status lin_attn_prefill_gated(const la_prefill_desc* d, const void* q, const void* k, const void* v,

@@ -431,7 +431,7 @@ __global__ __launch_bounds__(QNT) void k_bwd_query(BackwardParams bp) {
           sf[BG::DD + j] = dden;
           wi[j] = sf[BG::WT + j] * inv;
           if (j < L) {
-            float* tk2 = bp.tok + ((size_t)bh * p.T + (t0 + j)) * 2;
+            float* tk2 = bp.tok + (size_t)(sq.row0 + (long long)(t0 + j) * p.tok_rows) * 2;  // by token row
             tk2[0] = inv;
             tk2[1] = dden;
           }
@@ -599,7 +599,7 @@ __global__ __launch_bounds__(KNT) void k_bwd_key(BackwardParams bp) {
     if (NORM) {
       const int j = tf_tok<KNT>();
       if (j < L) {
-        const float* tk2 = bp.tok + ((size_t)bh * p.T + (t0 + j)) * 2;
+        const float* tk2 = bp.tok + (size_t)(sq.row0 + (long long)(t0 + j) * p.tok_rows) * 2;
         inv = tk2[0];
         dden = tk2[1];
       }

@@ -75,7 +75,7 @@ struct BackwardParams {
   float* dk;             // fp32, rows like k
   float* dv;             // fp32, rows like v
   float* rev;            // [BH, n_seg, E] segment summaries of the adjoint state, then their reverse prefixes
-  float* tok;            // [BH, T, 2]: 1/den and dden per token (normalize only)
+  float* tok;            // [rows, 2]: 1/den and dden per token row, rows as q's (normalize only)
   int dout_bf16;
 };
 

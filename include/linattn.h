@@ -215,8 +215,9 @@ la_status lin_attn_prefill_profiled(const la_prefill_desc* d, const void* q, con
  *             batch entries), not a gate.
  *   workspace at least lin_attn_prefill_gated_workspace_size bytes
  *   other arguments as for lin_attn_prefill (no gamma, no PRF bank).
- * This path computes in fp32 on the vector ALUs (the gate factors make every operand
- * inexact in bf16).
+ * bf16 inputs run on the matrix cores with every gate-scaled operand carried as a two-term
+ * (hi + lo) bf16 pair, since the gate factors make them inexact in one bf16; fp32 inputs
+ * run on the vector ALUs in fp32.
  */
 la_status lin_attn_prefill_gated_workspace_size(const la_prefill_desc* d, size_t* bytes);
 la_status lin_attn_prefill_gated(const la_prefill_desc* d, const void* q, const void* k, const void* v,
@@ -253,6 +254,28 @@ la_status lin_attn_prefill_backward(const la_prefill_desc* d, const void* q, con
                                     const float* gamma, const float* init_S, const float* init_Z, const void* dout,
                                     float* dq, float* dk, float* dv, float* dinit_S, float* dinit_Z,
                                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * lin_attn_prefill_backward over a packed batch of variable-length sequences: the backward
+ * pass of lin_attn_prefill_varlen with the same d, cu_seqlens, total_tokens, q, k, v, gamma,
+ * init_S and init_Z. Each sequence's gradients depend only on its own tokens and initial state.
+ *
+ *   d, cu_seqlens, total_tokens  as for lin_attn_prefill_varlen (layout LA_LAYOUT_BTHD),
+ *                subject to lin_attn_prefill_backward's support limits
+ *   dout         device [total_tokens, H, d_v] out_dtype
+ *   dq, dk       device fp32 [total_tokens, H, d_k];  dv device fp32 [total_tokens, H, d_v]
+ *   dinit_S, dinit_Z  per sequence, [B, H, n_psi, d_v] / [B, H, n_psi], or NULL; an empty
+ *                sequence's are zero
+ *   workspace    at least lin_attn_prefill_backward_varlen_workspace_size(d, total_tokens) bytes
+ * Errors as for lin_attn_prefill_varlen. Token rows outside every sequence are not written.
+ */
+la_status lin_attn_prefill_backward_varlen_workspace_size(const la_prefill_desc* d, int32_t total_tokens,
+                                                          size_t* bytes);
+la_status lin_attn_prefill_backward_varlen(const la_prefill_desc* d, const int32_t* cu_seqlens, int32_t total_tokens,
+                                           const void* q, const void* k, const void* v, const float* gamma,
+                                           const float* init_S, const float* init_Z, const void* dout, float* dq,
+                                           float* dk, float* dv, float* dinit_S, float* dinit_Z, void* workspace,
+                                           size_t workspace_bytes, hipStream_t stream);
 
 /* Batched single-token decode description: N independent streams x H heads. */
 typedef struct {

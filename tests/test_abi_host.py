@@ -250,6 +250,36 @@ def test_backward_validation_and_workspace():
     assert call(gamma=(ctypes.c_float * 4)(1.0, 0.5, 0.0, 1.0)) == LA_ERR_VALUE
 
 
+def test_backward_varlen_validation_and_workspace():
+    """lin_attn_prefill_backward_varlen: workspace sized by the packed token count (the forward
+    varlen plan twice plus 1/den and dden per token-head), and its argument errors before launch."""
+    lib = binding.load()
+    base = dict(B=5, H=4, T=3000, chunk=64, psi=1, normalize=1, layout=1)
+    total = 4321
+    n, fwd = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    d = _desc(**base)
+    assert lib.lin_attn_prefill_backward_varlen_workspace_size(ctypes.byref(d), total, ctypes.byref(n)) == LA_OK
+    assert lib.lin_attn_prefill_varlen_workspace_size(ctypes.byref(d), total, ctypes.byref(fwd)) == LA_OK
+    assert n.value == 2 * fwd.value + 2 * 4 * total * 4
+    assert lib.lin_attn_prefill_backward_varlen_workspace_size(ctypes.byref(d), -1, ctypes.byref(n)) == LA_ERR_SHAPE
+    assert lib.lin_attn_prefill_backward_varlen_workspace_size(ctypes.byref(d), total, None) == LA_ERR_NULL
+    d32 = _desc(**{**base, "in_dtype": LA_F32})
+    assert lib.lin_attn_prefill_backward_varlen_workspace_size(ctypes.byref(d32), total,
+                                                               ctypes.byref(n)) == LA_ERR_UNSUPPORTED
+    lib.lin_attn_prefill_backward_varlen_workspace_size(ctypes.byref(d), total, ctypes.byref(n))
+    fake, odd = ctypes.c_void_p(1 << 20), ctypes.c_void_p((1 << 20) + 2)
+
+    def call(desc=d, cu=fake, tot=total, q=fake, w=fake, size=n.value):
+        return lib.lin_attn_prefill_backward_varlen(ctypes.byref(desc), cu, tot, q, fake, fake, None, None, None,
+                                                    fake, fake, fake, fake, None, None, w, size, None)
+    assert call(cu=None) == LA_ERR_NULL
+    assert call(cu=odd) == LA_ERR_ALIGN
+    assert call(tot=-1) == LA_ERR_SHAPE
+    assert call(desc=_desc(**{**base, "layout": 0})) == LA_ERR_VALUE
+    assert call(q=None) == LA_ERR_NULL
+    assert call(size=n.value - 16) == LA_ERR_WORKSPACE
+
+
 def test_decode_validation():
     lib = binding.load()
     fake = ctypes.c_void_p(1 << 20)

@@ -13,6 +13,8 @@ gradient grows with the state it reads).
 """
 from __future__ import annotations
 
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -147,3 +149,58 @@ def test_backward_chunk_invariance():
     for lab, a, b in zip(("dq", "dk", "dv"), res[0], res[1]):
         rel, _ = metrics(a.cpu().numpy(), b.cpu().numpy())
         assert rel < 1e-3, (lab, rel)
+
+
+VARLEN_LENGTHS = [200, 0, 1, 63, 64, 65, 777, 128, 1000, 31]
+# name, psi, normalize, decay, chunk, dout dtype
+VARLEN_CASES = [
+    ("elu1_norm_decay", PSI_ELU1, 1, "const:0.995", 64, "f32"),
+    ("retention_spread_bf16", PSI_IDENTITY, 0, "retnet_spread", 128, "bf16"),
+    ("elu1_norm", PSI_ELU1, 1, "none", 128, "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", VARLEN_CASES, ids=[c[0] for c in VARLEN_CASES])
+def test_backward_varlen(case):
+    """Packed sequences of mixed lengths (empty, one token, around a step, several segments) with
+    per-sequence initial states: each sequence's gradients against the oracle on that sequence alone;
+    an empty sequence's initial-state gradients are zero."""
+    name, psi, normalize, decay, C, dt = case
+    H, N, lengths = 2, len(VARLEN_LENGTHS), VARLEN_LENGTHS
+    total = sum(lengths)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    w = _workload(psi, normalize, decay, 1, H, total, C, seed=60 + [c[0] for c in VARLEN_CASES].index(name))
+    announce(f"backward varlen {name} lengths={lengths} C={C}")
+    inp = inputs.make_prefill_inputs(w)  # one [1, H, total, d] stream, cut into sequences below
+    packed = [x[0].transpose(0, 1).contiguous() for x in (inp["q"], inp["k"], inp["v"])]  # [total, H, d]
+    ddt = torch.float32 if dt == "f32" else torch.bfloat16
+    dout = inputs.make_upstream_grad((total, H, 128), w.seed + 11, dtype=ddt)
+    g = inp["gamma"]
+    wn = dataclasses.replace(w, B=N)
+    S0, Z0 = _prefix_state(wn, inp, 96, w.seed + 5)
+    S0d = torch.from_numpy(S0).float().to(DEV)
+    Z0d = torch.from_numpy(Z0).float().to(DEV)
+    dS0 = torch.full((N, H, 128, 128), float("nan"), device=DEV)
+    dZ0 = torch.full((N, H, 128), float("nan"), device=DEV)
+    dq, dk, dv = binding.lin_attn_prefill_backward_varlen(
+        *(x.to(DEV) for x in packed), dout.to(DEV), torch.from_numpy(cu).to(DEV), max(lengths) + 70, psi=psi,
+        chunk=C, normalize=normalize, eps=w.eps, gamma=None if g is None else list(g), init_S=S0d, init_Z=Z0d,
+        dinit_S=dS0, dinit_Z=dZ0)
+    torch.cuda.synchronize()
+    got = [x.cpu() for x in (dq, dk, dv)]
+    S0r, Z0r = S0d.cpu().double().numpy(), Z0d.cpu().double().numpy()
+    for b, L in enumerate(lengths):
+        if L == 0:
+            assert torch.count_nonzero(dS0[b]).item() == 0
+            if normalize:
+                assert torch.count_nonzero(dZ0[b]).item() == 0
+            continue
+        sl = slice(int(cu[b]), int(cu[b + 1]))
+        blk = [x[sl].transpose(0, 1).unsqueeze(0) for x in packed + [dout]]  # [1, H, L, d]
+        ref = oracle.prefill_backward(*blk[:3], blk[3], psi, gamma=None if g is None else g[None],
+                                      normalize=normalize, eps=w.eps, S0=S0r[b:b + 1], Z0=Z0r[b:b + 1])
+        for lab, a, r in zip(("dq", "dk", "dv"), got, ref[:3]):
+            _check(a[sl].transpose(0, 1).unsqueeze(0).numpy(), r, f"varlen {name} seq {b} (T={L}) {lab}")
+        _check(dS0[b:b + 1].cpu().numpy(), ref[3], f"varlen {name} seq {b} dS0")
+        if normalize:
+            _check(dZ0[b:b + 1].cpu().numpy(), ref[4], f"varlen {name} seq {b} dZ0")
