@@ -18,7 +18,20 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace la {
+
+// Calls f(std::integral_constant<int, I>()) for I = B .. E-1 in order: a loop whose index is a
+// constant expression in the body (for builtins that take constant arguments, such as the
+// schedule-group barriers).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>());
+    static_for<B + 1, E>(f);
+  }
+}
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));

@@ -1,6 +1,6 @@
 // la_prefill_bf16.hpp -- chunkwise causal linear attention, bf16 inputs, fp32 state,
-// MFMA 32x32x16 bf16 -> fp32 on gfx950. Kernel templates; instantiated per (C, D) in
-// la_prefill_bf16_c*.hip.
+// MFMA 32x32x16 bf16 -> fp32 on gfx950. Kernel templates; instantiated per head width D
+// in la_prefill_bf16_c64_d*.hip.
 //
 // Method ("Log-Depth Chunked Linear-Attention Scan", Implementation notes; decayed
 // form: "Linear Attention and Retentive Networks", chunkwise recurrent
@@ -11,21 +11,22 @@
 //   S_next  = gamma^L S_prev + sum_i gamma^(L-1-i) psi(k_i) v_i^T   (Z likewise)
 // Padded positions (past T) are zeroed after the feature map, so they add nothing.
 //
-// Two kernels share the chunk machinery:
+// Two passes share the chunk machinery:
 //   k_summary: one workgroup per (sequence, segment of chunks); folds its chunks'
 //              summaries into one segment summary (Kernel 1's summaries, reduced
 //              over the segment) and writes it to the workspace.
-//   k_output : one workgroup per (sequence, segment); starts from the segment's
+//   output   : one workgroup per (sequence, segment); starts from the segment's
 //              exclusive prefix (written there by the scan), walks its chunks,
 //              emits o for every real token (Kernels 1 and 3 fused) and carries the
-//              state from chunk to chunk on chip.
+//              state from chunk to chunk on chip. Two kernels: k_output_sh (D/32
+//              waves, score tiles shared through LDS) and k_output_w8 (two waves per
+//              SIMD within one workgroup, d = 128).
+// Both are instantiated at C = 64: a 128-token chunk is walked in two 64-token steps
+// (la_prefill_bf16.hip), since neither pass depends on how a segment's tokens are grouped.
 //
-// Workgroup = D/32 waves; wave w owns value columns [32w, 32w+32) of the state
-// S (all n_psi rows, fp32 in registers) and of every output tile. Each wave
-// computes every score tile itself, so the score tile goes from the MFMA
-// accumulators straight back into the next MFMA as an operand (no LDS round trip).
-// All LDS tiles are row-major; operands whose k runs over tokens use the gfx950
-// transpose read (ds_read_b64_tr_b16).
+// Wave w owns value columns [32w, 32w+32) of the state S (all n_psi rows, fp32 in
+// registers) and of every output tile. All LDS tiles are row-major; operands whose k
+// runs over tokens use the gfx950 transpose read (ds_read_b64_tr_b16).
 //
 // Scheduling: decay, normalisation and the feature map are template parameters and
 // the tile loops are fully unrolled, so each chunk's matrix work is straight-line
@@ -214,36 +215,6 @@ __device__ __forceinline__ void state_mfma_vdec(f32x16 (&S)[D / 32], const __bf1
   }
 }
 
-// One score tile A^T[i-tile it][j-tile jt] (M = i, N = j, k = feature) with the causal
-// mask and decay D_ji = gamma^(j-i); adds its row sums to rsum and A V to num. qk holds
-// the j-tile's Q operands (k = feature). fac[r] is this lane's factor for register r:
-// for the diagonal tile gamma^(n - i_r) masked to i_r <= n, for the others
-// gamma^(n + 32 - i_r) * gamma^(32 (jt - it - 1)) (lane column j = 32 jt + n, register
-// row i = 32 it + i_r).
-template <int C, int D, bool NORM>
-__device__ __forceinline__ void score_tile(int it, int jt, const bf16x8 (&qk)[D / 16], const __bf16* sK,
-                                           const __bf16* sV, f32x16& num, float& rsum, const float (&fac)[16],
-                                           float tf, int Ew, int lane) {
-  constexpr int PK = Geo<C, D, true>::PK;
-  f32x16 acc = f32x16{};
-#pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) acc = mfma32(ld_cols8(sK, PK, it * 32, kk * 16, lane), qk[kk], acc);
-  float a[16];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    a[r] = acc[r] * (fac[r] * tf);
-    if (NORM) rsum += a[r];
-  }
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    bf16x8 ah, al;
-    split8_trunc(a + 8 * q, ah, al);
-    const bf16x8 vv = ld_rows8_perm(sV, PK, it * 32, q, Ew, lane);
-    num = mfma32(ah, vv, num);
-    num = mfma32(al, vv, num);
-  }
-}
-
 // Summary-pass LDS image. With identity keys and decay the decay goes on the values (see
 // k_summary), so there is no K lo tile and V moves up: about 40 KiB at C = 64, d = 128, so
 // three workgroups share a CU instead of two.
@@ -345,189 +316,6 @@ __global__ __launch_bounds__(2 * D) void k_summary(PrefillParams p) {
   }
 }
 
-template <int C, int D, bool DECAY, bool NORM, bool ELU, bool OBF>
-__global__ __launch_bounds__(2 * D) void k_output(PrefillParams p) {
-  using G = Geo<C, D, true>;
-  constexpr bool SPLIT = DECAY || ELU;
-  constexpr int NJ = C / 32;
-  extern __shared__ __align__(16) unsigned char smem[];
-  const int bh = blockIdx.x, seg = blockIdx.y, head = bh % p.H;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, n = lane & 31, hh = lane >> 5;
-  const int Ew = 32 * w;
-  const float lg = DECAY ? p.log2g[head] : 0.f;
-  __bf16* sQ = (__bf16*)(smem + G::OFF_Q);
-  __bf16* sK = (__bf16*)(smem + G::OFF_K);
-  __bf16* sKlo = (__bf16*)(smem + G::OFF_KLO);
-  __bf16* sV = (__bf16*)(smem + G::OFF_V);
-  float* sF = (float*)(smem + G::OFF_F);
-
-  // exclusive prefix state of this segment (written by the scan)
-  const size_t E = (size_t)D * D + D;
-  const float* pre = p.ws + ((size_t)bh * p.n_seg + seg) * E;
-  f32x16 S[D / 32];
-#pragma unroll
-  for (int pt = 0; pt < D / 32; ++pt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) S[pt][r] = pre[(size_t)(pt * 32 + dtile_row(r, lane)) * D + Ew + n];
-  if (tid < D) sF[G::F_Z + tid] = NORM ? pre[(size_t)D * D + tid] : 0.f;
-  for (int j = tid; j < C; j += G::NT) sF[G::F_THETA + j] = DECAY ? exp2f((float)(j + 1) * lg) : 1.f;
-
-  // this lane's score-tile factors (its column j%32 = n and register rows are fixed):
-  // diagonal tile gamma^(n - i_r) masked to i_r <= n; off-diagonal base gamma^(n + 32 - i_r)
-  float fdiag[16], foff[16];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int ir = dtile_row(r, lane);
-    fdiag[r] = ir <= n ? (DECAY ? exp2f((float)(n - ir) * lg) : 1.f) : 0.f;
-    foff[r] = DECAY ? exp2f((float)(n + 32 - ir) * lg) : 1.f;
-  }
-
-  const SeqSpan sq = seq_span(p, bh);
-  const int T = sq.T, n_chunks = (T + C - 1) / C;
-  const uint32_t rse = (uint32_t)p.tok_rows * D, rsb = rse * 2;  // elements / bytes between token rows
-  constexpr int OES = OBF ? 2 : 4;  // output element bytes
-  const uint16_t* qb = (const uint16_t*)p.q + sq.row0 * D;
-  const uint16_t* kb = (const uint16_t*)p.k + sq.row0 * D;
-  const uint16_t* vb = (const uint16_t*)p.v + sq.row0 * D;
-  unsigned char* ob = (unsigned char*)p.o + sq.row0 * D * OES;
-  const int c0 = seg * p.seg_chunks, c1 = min(c0 + p.seg_chunks, n_chunks);
-  if (c0 >= c1) return;  // segment past the end of a shorter sequence: nothing to write
-
-  Pieces<C, D> pq, pk, pv;
-  {
-    const int L0 = min(C, T - c0 * C);
-    load_pieces<C, D>(pq, qb + (size_t)c0 * C * rse, L0, rsb);
-    load_pieces<C, D>(pk, kb + (size_t)c0 * C * rse, L0, rsb);
-    load_pieces<C, D>(pv, vb + (size_t)c0 * C * rse, L0, rsb);
-    vm_drain();  // entering the loop with nothing in flight, see the prefetch below
-  }
-  for (int c = c0; c < c1; ++c) {
-    const int t0 = c * C, L = min(C, T - t0);
-    const float a = DECAY ? exp2f((float)L * lg) : 1.f;
-    lds_barrier();  // the previous chunk is done with LDS (and Z is updated)
-    float zp[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) zp[j] = 0.f;
-    commit_q<C, D, ELU>(pq, sQ, G::PQ);
-    commit_k<C, D, ELU, DECAY, false, ELU>(pk, sK, sKlo, G::PK, L, lg, zp);
-    commit_v<C, D>(pv, sV, G::PK);
-    const bool more = c + 1 < c1;
-    const int Ln = more ? min(C, T - (c + 1) * C) : 0;
-    // next chunk's keys and values stream in during this chunk's matrix work (rows past
-    // Ln, including every row when there is no next chunk, read as zeros)
-    load_pieces<C, D>(pk, kb + (size_t)(c + 1) * C * rse, Ln, rsb);
-    load_pieces<C, D>(pv, vb + (size_t)(c + 1) * C * rse, Ln, rsb);
-    lds_barrier();
-    // stores of this chunk's outputs: rows past L are dropped by the buffer bound
-    const __amdgpu_buffer_rsrc_t ors = make_rsrc(ob + (size_t)t0 * rse * OES, rows_extent(L, rse * OES, D * OES));
-
-    // S as the B operand of psi(Q) S: straight from its accumulator layout (D-tile
-    // feedback order), split once per chunk into hi + lo
-    bf16x8 sh[D / 32][2], sl[D / 32][2];
-#pragma unroll
-    for (int pt = 0; pt < D / 32; ++pt)
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        float x[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) x[j] = S[pt][8 * q + j];
-        split8_trunc(x, sh[pt][q], sl[pt][q]);
-      }
-
-#pragma unroll 1
-    for (int jt = 0; jt < NJ; ++jt) {
-      // num = gamma^(j+1) psi(q_j) S_prev   (M = j, N = e, k = state row p)
-      f32x16 num = f32x16{};
-#pragma unroll
-      for (int pt = 0; pt < D / 32; ++pt)
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const bf16x8 qa = ld_cols8_perm(sQ, G::PQ, jt * 32, pt * 32, q, lane);
-          num = mfma32(qa, sh[pt][q], num);
-          num = mfma32(qa, sl[pt][q], num);
-        }
-      if (DECAY) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) num[r] *= sF[G::F_THETA + jt * 32 + dtile_row(r, lane)];
-      }
-      // psi(q_j) . Z_prev for j = jt*32 + n (the two lane halves split the features)
-      float qz = 0.f;
-      if (NORM) {
-        const __bf16* qr = sQ + (jt * 32 + n) * G::PQ + hh * (D / 2);
-        const f32x4* zr = (const f32x4*)(sF + G::F_Z + hh * (D / 2));
-#pragma unroll
-        for (int e8 = 0; e8 < D / 2; e8 += 8) {
-          const bf16x8 qv = *(const bf16x8*)(qr + e8);
-          const f32x4 z0 = zr[e8 / 4], z1 = zr[e8 / 4 + 1];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) qz += from_bf16(qv[j]) * z0[j] + from_bf16(qv[4 + j]) * z1[j];
-        }
-        qz += __shfl_xor(qz, 32);
-      }
-      // this row tile's Q operands for the score tiles (k = feature), loaded once
-      bf16x8 qk[D / 16];
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) qk[kk] = ld_cols8(sQ, G::PQ, jt * 32, kk * 16, lane);
-      // scores A^T (M = i, N = j, k = feature), masked and decayed; then num += A V.
-      // Off-diagonal tiles (it < jt) first, then the diagonal tile (causal mask).
-      float rsum = 0.f;
-#pragma unroll 1
-      for (int it = 0; it < jt; ++it) {
-        const float tf = DECAY ? exp2f((float)(32 * (jt - it - 1)) * lg) : 1.f;
-        score_tile<C, D, NORM>(it, jt, qk, sK, sV, num, rsum, foff, tf, Ew, lane);
-      }
-      score_tile<C, D, NORM>(jt, jt, qk, sK, sV, num, rsum, fdiag, 1.f, Ew, lane);
-      // o_j = num_j / den_j; den_j is formed in lane j%32 and fetched by the lanes holding row j
-      float den = 1.f;
-      if (NORM) den = sF[G::F_THETA + jt * 32 + n] * qz + (rsum + __shfl_xor(rsum, 32)) + p.eps;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int j = jt * 32 + dtile_row(r, lane);
-        const float val = NORM ? num[r] / __shfl(den, dtile_row(r, lane)) : num[r];
-        store_out1<OBF>(ors, (uint32_t)j * rse + Ew + n, val);
-      }
-    }
-
-    // next chunk's queries: issued once this chunk's queries are no longer read
-    load_pieces<C, D>(pq, qb + (size_t)(c + 1) * C * rse, Ln, rsb);
-    // state update: K~ = Xi psi(K) as hi + lo, S <- gamma^L S + K~^T V, Z <- gamma^L Z + K~^T 1
-    if (NORM) reduce_zp<D>(zp, sF + G::F_ZRED);
-    if (DECAY) {
-      lds_barrier();  // every wave is done reading psi(K) for scores
-#pragma unroll
-      for (int i = 0; i < G::NPC; ++i) {
-        const int row = piece_row<C, D>(i), c8 = piece_cols<C, D>(i);
-        const float xi = row < L ? exp2f((float)(L - 1 - row) * lg) : 0.f;
-        const bf16x8 h8 = *(const bf16x8*)(sK + row * G::PK + c8);
-        bf16x8 l8 = bf16x8{};
-        if (ELU) l8 = *(const bf16x8*)(sKlo + row * G::PK + c8);
-        bf16x8 hi, lo;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const bf16_pair sp = split_bf16((from_bf16(h8[j]) + from_bf16(l8[j])) * xi);
-          hi[j] = sp.hi;
-          lo[j] = sp.lo;
-        }
-        *(bf16x8*)(sK + row * G::PK + c8) = hi;
-        *(bf16x8*)(sKlo + row * G::PK + c8) = lo;
-      }
-    }
-    lds_barrier();
-    if (NORM && tid < D) {
-      float z = 0.f;
-#pragma unroll
-      for (int ww = 0; ww < G::NW; ++ww) z += sF[G::F_ZRED + ww * D + tid];
-      sF[G::F_Z + tid] = a * sF[G::F_Z + tid] + z;
-    }
-    if (DECAY) {
-#pragma unroll
-      for (int pt = 0; pt < D / 32; ++pt) S[pt] *= a;
-    }
-    state_mfma<C, D, SPLIT>(S, sK, sKlo, sV, Ew, lane);
-  }
-}
-
-// ---------------------------------------------------------------------------------------
 // Output kernel with the score tiles computed once per workgroup.
 //
 // Each wave produces a share of the C/32 x (C/32 + 1)/2 score tiles A^T (masked, decayed,
@@ -564,6 +352,10 @@ struct ShGeo {
   static constexpr int F_XI = F_R + NTILE * 32;  // Xi_i = gamma^(L-1-i), 0 past L [C] (decay on V)
   static constexpr int LDS_BYTES = OFF_F + 4 * (F_XI + C);
   static constexpr bool FITS = LDS_BYTES <= 160 * 1024;
+  // waves per SIMD: two when two workgroups' LDS images fit in the CU (registers are then
+  // capped at 256 per wave), so a second wave computes while the first one's global loads and
+  // stores wait to issue; else one
+  static constexpr int OCC = 2 * LDS_BYTES <= 160 * 1024 ? 2 : 1;
 };
 
 // tile t <-> (it, jt) with it <= jt, t = jt (jt + 1) / 2 + it; branch-free (up to 16 row tiles)
@@ -596,7 +388,8 @@ __device__ __forceinline__ void state_mfma_p(f32x16 (&S)[D / 32], const __bf16* 
 // is a multiple of 16 and x < 32, a swizzled read of any row block is one of a few
 // per-lane bases plus the row block's constant offset.
 template <int C, int D, bool DECAY, bool NORM, bool ELU, bool OBF>
-__global__ __launch_bounds__(2 * D) void k_output_sh(PrefillParams p) {
+__global__ __launch_bounds__(2 * D) __attribute__((amdgpu_waves_per_eu(ShGeo<C, D, ELU>::OCC, ShGeo<C, D, ELU>::OCC)))
+void k_output_sh(PrefillParams p) {
   using G = ShGeo<C, D, ELU>;
   using PG = Geo<C, D, true>;  // piece geometry of the global -> LDS copies
   static_assert(G::FITS, "LDS budget");
@@ -796,14 +589,14 @@ __global__ __launch_bounds__(2 * D) void k_output_sh(PrefillParams p) {
       }
     };
     // Every wave runs TPW tiles, so the phase is straight-line code the schedule can
-    // interleave: a wave with fewer tiles recomputes the last tile and writes the same
-    // bytes to the same place as the wave that owns it (it would wait at the barrier anyway).
-    static_assert(G::NTILE >= NW, "every wave has a score tile");
+    // interleave: a wave with fewer tiles (or none, when there are fewer tiles than waves)
+    // recomputes the last tile and writes the same bytes to the same place as the wave that
+    // owns it (it would wait at the barrier anyway).
     {
       // next-chunk loads per score MFMA (3 NPC loads over TPW tiles of D / 16 MFMAs)
       constexpr int LPM = (3 * NPC + TPW * (D / 16) - 1) / (TPW * (D / 16));
-      f32x16 prev = score_chain(w);
-      int tp = w;
+      int tp = min(w, G::NTILE - 1);
+      f32x16 prev = score_chain(tp);
       __builtin_amdgcn_sched_group_barrier(0x100, 2 * (D / 16), 0);  // the first tile's operands
 #pragma unroll
       for (int i = 0; i < D / 16; ++i) {
@@ -834,45 +627,87 @@ __global__ __launch_bounds__(2 * D) void k_output_sh(PrefillParams p) {
     // column e, N = token j), so each lane ends up with 4 consecutive columns of one token
     // row (16-byte stores) and the per-token factors are lane scalars.
     const __amdgpu_buffer_rsrc_t ors = make_rsrc(ob + (size_t)t0 * rse * OES, rows_extent(L, rse * OES, D * OES));
-    bf16x8 sh[D / 32][2], sl[D / 32][2];  // S_prev as hi + lo, straight from its accumulator layout
+    // All NJ row tiles accumulate together (NJ independent MFMA chains), in steps whose LDS
+    // operands are read one step ahead (double-buffered registers; the schedule barriers keep
+    // the next step's reads above this step's MFMAs). S steps (one per state-row tile pt):
+    // numT[jt] += S_prev^T psi(Q)^T over the tile's 32 state rows (k in the D-tile feedback
+    // order), with only that tile of S held as hi + lo. A V steps (one per 16-token half q of
+    // token tile it): numT[jt] += V^T A^T for every jt >= it, so each V operand is read once.
+    // For each row tile the MFMAs happen in the order one tile at a time would do them.
+    constexpr int NPT = D / 32;
+    f32x16 num[NJ];
 #pragma unroll
-    for (int pt = 0; pt < D / 32; ++pt)
+    for (int jt = 0; jt < NJ; ++jt) num[jt] = f32x16{};
+    bf16x8 qo[2][NJ][2];  // S step operands: psi(Q) rows of every row tile, this state-row tile
+    bf16x8 vo[2];         // A V step operands: V of the half token tile ...
+    bf16x8 ao[2][NJ][2];  // ... and the score tiles (hi, lo) of every row tile jt >= it
+    auto load_s = [&](int pt, int buf) {
+#pragma unroll
+      for (int jt = 0; jt < NJ; ++jt)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const unsigned char* qa = qC + (jt * 32 * PQ + pt * 32 + 16 * q) * 2;
+          qo[buf][jt][q] = cat8(*(const bf16x4*)qa, *(const bf16x4*)(qa + 16));
+        }
+    };
+    auto load_av = [&](int st, int buf) {  // step st: token tile st / 2, half st % 2
+      const int it = st >> 1, q = st & 1, r0 = it * 32 + 16 * q;
+      vo[buf] = cat8(lds_read_tr4((const __bf16*)(vT0 + r0 * D * 2)), lds_read_tr4((const __bf16*)(vT1 + r0 * D * 2)));
+#pragma unroll
+      for (int jt = it; jt < NJ; ++jt) {
+        const unsigned char* at = aR + (jt * (jt + 1) / 2 + it) * G::A_TILE + 32 * q;
+        ao[buf][jt][0] = *(const bf16x8*)at;
+        ao[buf][jt][1] = *(const bf16x8*)(at + ALO);
+      }
+    };
+    // DS read instructions of each step's operands (one read2 per psi(Q) pair; two transpose
+    // reads and two reads per row tile for an A V step)
+    constexpr int RD_S = 2 * NJ;
+    auto rd_av = [](int st) constexpr { return 2 + 2 * (NJ - (st >> 1)); };
+    load_s(0, 0);
+    static_for<0, NPT>([&](auto ipt) {
+      constexpr int pt = decltype(ipt)::value;
+      if constexpr (pt + 1 < NPT) load_s(pt + 1, (pt + 1) & 1);
+      else load_av(0, 0);
+      bf16x8 sh[2], sl[2];  // this state-row tile of S_prev as hi + lo, straight from its accumulator
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         float x[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) x[j] = S[pt][8 * q + j];
-        split8_trunc(x, sh[pt][q], sl[pt][q]);
+        split8_trunc(x, sh[q], sl[q]);
       }
+#pragma unroll
+      for (int jt = 0; jt < NJ; ++jt)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          num[jt] = mfma32(sh[q], qo[pt & 1][jt][q], num[jt]);
+          num[jt] = mfma32(sl[q], qo[pt & 1][jt][q], num[jt]);
+        }
+      __builtin_amdgcn_sched_group_barrier(0x100, pt + 1 < NPT ? RD_S : rd_av(0), 0);  // next step's reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 4 * NJ, 0);                            // this step's MFMAs
+    });
+    if (DECAY) {
+#pragma unroll
+      for (int jt = 0; jt < NJ; ++jt) num[jt] *= fN[G::F_THETA + jt * 32];  // gamma^(j+1), j = this lane's token
+    }
+    static_for<0, 2 * NJ>([&](auto ist) {
+      constexpr int st = decltype(ist)::value, it = st >> 1, b = st & 1;
+      if constexpr (st + 1 < 2 * NJ) load_av(st + 1, b ^ 1);
+#pragma unroll
+      for (int jt = it; jt < NJ; ++jt) {
+        num[jt] = mfma32(vo[b], ao[b][jt][0], num[jt]);
+        num[jt] = mfma32(vo[b], ao[b][jt][1], num[jt]);
+      }
+      if constexpr (st + 1 < 2 * NJ) {
+        __builtin_amdgcn_sched_group_barrier(0x100, rd_av(st + 1), 0);  // next step's reads
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * (NJ - it), 0);  // this step's MFMAs
+      }
+    });
     // unrolled so the store count per chunk is static: the wait for the prefetched tiles
     // at the next commit then leaves this chunk's output stores in flight
 #pragma unroll
     for (int jt = 0; jt < NJ; ++jt) {
-      // numT = S_prev^T psi(Q)^T (k = state row p, in the D-tile feedback order)
-      f32x16 num = f32x16{};
-#pragma unroll
-      for (int pt = 0; pt < D / 32; ++pt)
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const unsigned char* qa = qC + (jt * 32 * PQ + pt * 32 + 16 * q) * 2;
-          const bf16x8 qo = cat8(*(const bf16x4*)qa, *(const bf16x4*)(qa + 16));
-          num = mfma32(sh[pt][q], qo, num);
-          num = mfma32(sl[pt][q], qo, num);
-        }
-      if (DECAY) num *= fN[G::F_THETA + jt * 32];  // gamma^(j+1), j = this lane's token
-      // numT += V^T A^T for it <= jt (k = token i)
-#pragma unroll
-      for (int it = 0; it <= jt; ++it) {
-        const unsigned char* at = aR + (jt * (jt + 1) / 2 + it) * G::A_TILE;
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const int r0 = it * 32 + 16 * q;
-          const bf16x8 vv = cat8(lds_read_tr4((const __bf16*)(vT0 + r0 * D * 2)),
-                                 lds_read_tr4((const __bf16*)(vT1 + r0 * D * 2)));
-          num = mfma32(vv, *(const bf16x8*)(at + 32 * q), num);
-          num = mfma32(vv, *(const bf16x8*)(at + 32 * q + ALO), num);
-        }
-      }
       float inv = 1.f;
       if (NORM) {
         // psi(q_j) . Z_prev (the lane halves split the features) and the score row sums
@@ -896,8 +731,8 @@ __global__ __launch_bounds__(2 * D) void k_output_sh(PrefillParams p) {
       const uint32_t row_el = (uint32_t)(jt * 32 + n) * rse + Ew + 4 * hh;
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4)
-        store_out4<OBF>(ors, row_el + 8 * q4, num[4 * q4] * inv, num[4 * q4 + 1] * inv, num[4 * q4 + 2] * inv,
-                        num[4 * q4 + 3] * inv);
+        store_out4<OBF>(ors, row_el + 8 * q4, num[jt][4 * q4] * inv, num[jt][4 * q4 + 1] * inv,
+                        num[jt][4 * q4 + 2] * inv, num[jt][4 * q4 + 3] * inv);
     }
 
     // ---- state update: S <- gamma^L S + K~^T V with K~ = Xi psi(K) as hi + lo (elu+1), or
@@ -1028,9 +863,9 @@ struct W8Geo {
   static constexpr int PPR = D / 8;             // 16-byte pieces per token row
   static constexpr int RSTEP = NT / PPR;        // rows between a thread's pieces
   static constexpr int NPC = C * PPR / NT;      // pieces per thread per tile
-  // Used at C = 64 only: at C = 128 the duplicated state update's LDS reads (each wave
-  // reads all of K~ and its V columns) cost more than the second wave per SIMD saves
-  // (measured on the 128k retention workload: 3.36 ms against 3.03 ms with four waves).
+  // Laid out for C = 64: at C = 128 the duplicated state update's LDS reads (each wave reads
+  // all of K~ and its V columns) cost more than the second wave per SIMD saves (measured on
+  // the 128k retention workload: 3.36 ms against 3.03 ms with four waves).
   static constexpr bool FITS = B::FITS && LDS_BYTES <= 160 * 1024 && D == 128 && C == 64;
 };
 
@@ -1360,20 +1195,21 @@ __global__ __launch_bounds__(512) void k_output_w8(PrefillParams p) {
   }
 }
 
-// The output kernel for (C, D, flags): the two-waves-per-SIMD kernel where it applies, else
-// the shared-score kernel where its LDS fits, else every wave computes its own scores.
+// The output kernel for (C, D, flags): the two-waves-per-SIMD kernel for elu+1 features or a
+// denominator at d = 128, else the shared-score kernel (two workgroups per CU where their LDS
+// fits). Measured at C = 64, d = 128 on the output pass: identity features with a denominator
+// 0.222 ms (eight waves) against 0.234 ms (shared scores, two workgroups) on 8k x 64 heads;
+// retention without one 2.22 ms (shared scores) against 2.94 ms (eight waves) on 128k x 64.
 template <int C, int D, bool DECAY, bool NORM, bool ELU, bool OBF>
 const void* output_kernel(int& lds, int& threads) {
-  if constexpr (W8Geo<C, D, ELU>::FITS) {
+  if constexpr (W8Geo<C, D, ELU>::FITS && (ELU || NORM)) {
     lds = W8Geo<C, D, ELU>::LDS_BYTES;
     threads = W8Geo<C, D, ELU>::NT;
     return (const void*)k_output_w8<C, D, DECAY, NORM, ELU, OBF>;
-  } else if constexpr (ShGeo<C, D, ELU>::FITS) {
+  } else {
+    static_assert(ShGeo<C, D, ELU>::FITS, "LDS budget of the shared-score output kernel");
     lds = ShGeo<C, D, ELU>::LDS_BYTES;
     return (const void*)k_output_sh<C, D, DECAY, NORM, ELU, OBF>;
-  } else {
-    lds = Geo<C, D, true>::LDS_BYTES;
-    return (const void*)k_output<C, D, DECAY, NORM, ELU, OBF>;
   }
 }
 
@@ -1415,7 +1251,5 @@ hipError_t launch_cd(const PrefillParams& p, hipStream_t s, bool out) {
 // Per-(C, D) entry points, each defined in its own translation unit.
 hipError_t launch_prefill_bf16_c64_d64(const PrefillParams& p, hipStream_t s, bool out);
 hipError_t launch_prefill_bf16_c64_d128(const PrefillParams& p, hipStream_t s, bool out);
-hipError_t launch_prefill_bf16_c128_d64(const PrefillParams& p, hipStream_t s, bool out);
-hipError_t launch_prefill_bf16_c128_d128(const PrefillParams& p, hipStream_t s, bool out);
 
 }  // namespace la
