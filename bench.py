@@ -332,7 +332,7 @@ def main():
     out_ms = pre["phase_ms"]["output"]
     achieved = BYTES_PER_TOKEN_HEAD * pre["units"] / (out_ms * 1e-3) / 1e9
     traffic = traffic_from_profiles("k_output_retnet_128k")
-    roofline = {"kernel": "k_output<128,128>", "bound": "hbm", "achieved": round(achieved, 1),
+    roofline = {"kernel": "k_output_sh<64,128>", "bound": "hbm", "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic,
                 "whole_call_frac": round(BYTES_PER_TOKEN_HEAD * pre["units"] / (pre["ms_per_step"] * 1e-3) / 1e9

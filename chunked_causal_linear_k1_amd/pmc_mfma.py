@@ -29,7 +29,7 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 
 # kernel-name substring -> key
 KERNELS = {
-    "k_output_sh<128, 128, true, false, false, false>": "k_output_retnet_128k",
+    "k_output_sh<64, 128, true, false, false, false>": "k_output_retnet_128k",
     "k_summary<64, 128, true, false, false>": "k_summary_retnet_128k",
     "k_output_w8<64, 128, false, true, true, false>": "k_output_elu1_8k",
     "k_summary<64, 128, false, true, true>": "k_summary_elu1_8k",
