@@ -237,6 +237,47 @@ def test_full_retnet_128k_sampled():
     _full_size(workloads.RETNET_128K, heads=[0, 21, 42, 63])
 
 
+def test_context_parallel_share_128k():
+    """One GPU's view of context parallelism on the 128k retention workload (the method's scan
+    lifted to contiguous T-shards, one per GPU): T is cut into 8 shards; each shard's summary is
+    its final state from a zero initial state, computed independently; the summaries are folded
+    in rank order under the decayed monoid (P_{r+1} = gamma^{L_r} P_r + S_r, what every GPU does
+    after gathering them); and each shard's prefill then starts from its predecessors' fold.
+    Concatenated, the shard outputs must equal the single call's to fp32 rounding, and sampled
+    heads must match the oracle."""
+    w = workloads.RETNET_128K
+    announce("context-parallel share: 128k retention in 8 T-shards")
+    inp = inputs.make_prefill_inputs(w, device=DEV)
+    o_full = binding.prefill_workload(w, inp)
+    gam = torch.tensor(np.asarray(inp["gamma"], dtype=np.float64), device=DEV)  # the fp32 values, exactly
+    P = 8
+    bounds = [r * 16384 for r in range(P)] + [w.T]
+    shards = [{key: inp[key][:, :, lo:hi].contiguous() for key in ("q", "k", "v")}
+              for lo, hi in zip(bounds[:-1], bounds[1:])]
+    g = list(inp["gamma"])
+    kw = dict(psi=w.psi, chunk=w.chunk, normalize=0, eps=w.eps, gamma=g)
+    summaries = []
+    for sh in shards:  # independent: each shard alone from a zero state
+        fS = torch.empty((1, w.H, 128, 128), device=DEV)
+        binding.lin_attn_prefill(sh["q"], sh["k"], sh["v"], final_S=fS, **kw)
+        summaries.append(fS)
+    torch.cuda.synchronize()
+    prefix = torch.zeros((1, w.H, 128, 128), dtype=torch.float64, device=DEV)
+    outs = []
+    for r, sh in enumerate(shards):
+        outs.append(binding.lin_attn_prefill(sh["q"], sh["k"], sh["v"], init_S=prefix.float().contiguous(), **kw))
+        L = bounds[r + 1] - bounds[r]
+        prefix = (gam ** L).view(1, w.H, 1, 1) * prefix + summaries[r].double()
+    torch.cuda.synchronize()
+    o_sh = torch.cat(outs, dim=2)
+    rel = float((o_sh.double() - o_full.double()).norm() / o_full.double().norm())
+    print(f"[parity] sharded vs single call rel_l2={rel:.3e}", flush=True)
+    assert rel <= 1e-5, rel
+    heads = [0, 63]
+    ref = _oracle_o(w, inp, heads=heads)
+    assert_close(o_sh.reshape(w.H, w.T, w.d_v)[heads].cpu().numpy(), ref, "bf16", "sharded 128k heads 0, 63")
+
+
 # positive random features (psi = exp(W x - |x|^2/2) / sqrt(n_psi), one bf16 bank per head)
 PRF_SMALL = [
     # name, B, H, T, n_psi, normalize, decay, v_scale
