@@ -546,13 +546,21 @@ __global__ __launch_bounds__(2 * D) void k_output_gla_m(PrefillParams p) {
     lds_barrier();
     // q^_j = psi(q_j) prod_{s<=j} alpha_s (threads p < D) and k^_i = psi(k_i) prod_{s>i} alpha_s
     // (threads D + p): running products of the gates, every factor <= 1
+    // (the chunk's gates and features of this thread's feature are read into registers first,
+    // so the chains wait on no LDS read)
     float ks = 0.f;
     if (tid < D) {
       const int pf = tid;
-      float eg = 1.f, ex = 1.f;  // prod_{s<=j} alpha_s, and prod_{HC<=s<=j} alpha_s
-#pragma unroll 4
+      float av[GC], qv[GC];
+#pragma unroll
       for (int j = 0; j < GC; ++j) {
-        const float a = sf[G::AL + j * D + pf], q = sf[G::PQ + j * D + pf];
+        av[j] = sf[G::AL + j * D + pf];
+        qv[j] = sf[G::PQ + j * D + pf];
+      }
+      float eg = 1.f, ex = 1.f;  // prod_{s<=j} alpha_s, and prod_{HC<=s<=j} alpha_s
+#pragma unroll
+      for (int j = 0; j < GC; ++j) {
+        const float a = av[j], q = qv[j];
         eg *= a;
         const bf16_pair pr = split_bf16(q * eg);
         sh[G::QH + j * G::P + pf] = pr.hi;
@@ -567,10 +575,16 @@ __global__ __launch_bounds__(2 * D) void k_output_gla_m(PrefillParams p) {
       sf[G::AEND + pf] = eg;
     } else {
       const int pf = tid - D;
+      float av[GC], kv[GC];
+#pragma unroll
+      for (int i = 0; i < GC; ++i) {
+        av[i] = sf[G::AL + i * D + pf];
+        kv[i] = sf[G::PK + i * D + pf];
+      }
       float f = 1.f, fx = 1.f;  // prod_{s>i} alpha_s, and prod_{i<s<HC} alpha_s
-#pragma unroll 4
+#pragma unroll
       for (int i = GC - 1; i >= 0; --i) {
-        const float k = sf[G::PK + i * D + pf], a = sf[G::AL + i * D + pf];
+        const float k = kv[i], a = av[i];
         const float kh = k * f;
         ks += kh;
         const bf16_pair pr = split_bf16(kh);
@@ -597,17 +611,19 @@ __global__ __launch_bounds__(2 * D) void k_output_gla_m(PrefillParams p) {
       float kk[16];
 #pragma unroll
       for (int f = 0; f < 16; f += 4) *(f32x4*)(kk + f) = *(const f32x4*)(sf + G::PK + i * D + f0 + f);
+#pragma unroll
       for (int j0 = 0; j0 < HC; j0 += 4) {
         float part[4];
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
           const int j = jb + j0 + jj;
-          if (j > i) {
+          // branch-free (a select after the product), so the gate reads need not wait on a branch
+          const bool on = j > i;
 #pragma unroll
-            for (int f = 0; f < 16; f += 4) {
-              const f32x4 a = *(const f32x4*)(sf + G::AL + j * D + f0 + f);
-              kk[f] *= a[0]; kk[f + 1] *= a[1]; kk[f + 2] *= a[2]; kk[f + 3] *= a[3];
-            }
+          for (int f = 0; f < 16; f += 4) {
+            const f32x4 a = *(const f32x4*)(sf + G::AL + j * D + f0 + f);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) kk[f + u] = on ? kk[f + u] * a[u] : kk[f + u];
           }
           float acc[4];
 #pragma unroll
