@@ -641,7 +641,10 @@ __global__ __launch_bounds__(KNT) void k_bwd_key(BackwardParams bp) {
     __builtin_amdgcn_sched_barrier(0);
 
     if (role == 0) {
-      // dV = A^T dNum + xi (F R): rows i, column e = col
+      // dV = A^T dNum + xi (F R), computed transposed: dV^T[e][i], rows e (this wave's columns),
+      // column i = 32 it + lane % 32. Operand registers serve either side of an MFMA, so swapping
+      // them transposes the product; each lane then holds four consecutive columns of one token
+      // and stores them with one 16-byte store (a quarter of the store instructions).
       f32x16 a2[2] = {zero16(), zero16()};
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt) {
@@ -651,10 +654,10 @@ __global__ __launch_bounds__(KNT) void k_bwd_key(BackwardParams bp) {
         for (int q = 0; q < 2; ++q)
 #pragma unroll
           for (int it = 0; it < 2; ++it) {
-            const bf16x8 kh = ld_cols8_perm(sh + BG::KH, TP, 32 * it, 32 * pt, q, lane);  // A[m=i][k=p]
-            a2[it] = mfma32(kh, rh[q], a2[it]);
-            a2[it] = mfma32(kh, rl[q], a2[it]);
-            if (ELU) a2[it] = mfma32(ld_cols8_perm(sh + BG::KL, TP, 32 * it, 32 * pt, q, lane), rh[q], a2[it]);
+            const bf16x8 kh = ld_cols8_perm(sh + BG::KH, TP, 32 * it, 32 * pt, q, lane);  // B[k=p][n=i] = F[i][p]
+            a2[it] = mfma32(rh[q], kh, a2[it]);  // A[m=e][k=p] = R[p][e] (the D-tile, transposed)
+            a2[it] = mfma32(rl[q], kh, a2[it]);
+            if (ELU) a2[it] = mfma32(rh[q], ld_cols8_perm(sh + BG::KL, TP, 32 * it, 32 * pt, q, lane), a2[it]);
           }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -664,31 +667,40 @@ __global__ __launch_bounds__(KNT) void k_bwd_key(BackwardParams bp) {
         f32x16 a1 = zero16();
 #pragma unroll
         for (int k0 = 32 * it; k0 < BC; k0 += 16) {
-          const bf16x8 ah = ld_rows8(sh + BG::AH, SQ, k0, 32 * it, lane);  // A[m=i][k=j] = A[j][i]
+          const bf16x8 ah = ld_rows8(sh + BG::AH, SQ, k0, 32 * it, lane);  // B[k=j][n=i] = A[j][i]
           const bf16x8 al = ld_rows8(sh + BG::AL, SQ, k0, 32 * it, lane);
-          const bf16x8 nh = ld_rows8(sh + BG::NH, TP, k0, 32 * cw, lane);  // B[k=j][n=e]
+          const bf16x8 nh = ld_rows8(sh + BG::NH, TP, k0, 32 * cw, lane);  // A[m=e][k=j] = dNum[j][e]
           const bf16x8 nl = ld_rows8(sh + BG::NL, TP, k0, 32 * cw, lane);
-          a1 = mfma32(ah, nh, a1);
-          a1 = mfma32(ah, nl, a1);
-          a1 = mfma32(al, nh, a1);
+          a1 = mfma32(nh, ah, a1);
+          a1 = mfma32(nl, ah, a1);
+          a1 = mfma32(nh, al, a1);
         }
+        const int i = 32 * it + (lane & 31);
+        const float xi = sf[BG::XI + i];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int i = 32 * it + dtile_row(r, lane);
-          const float g = a1[r] + sf[BG::XI + i] * a2[it][r];
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(g), rdv, (uint32_t)i * rsb4 + (uint32_t)col * 4, 0, 0);
+        for (int g4 = 0; g4 < 4; ++g4) {  // registers 4 g4 .. 4 g4 + 3: columns 32 cw + 8 g4 + 4 hh + 0..3
+          f32x4 o;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) o[u] = a1[4 * g4 + u] + xi * a2[it][4 * g4 + u];
+          const uint32_t e = 32 * cw + 8 * g4 + 4 * (lane >> 5);
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), rdv, (uint32_t)i * rsb4 + e * 4, 0, 0);
         }
       }
-      // R <- gamma^L R + (theta G)^T dNum: R[p][e] += sum_j (theta_j G[j][p]) dNum[j][e]
+      // R <- gamma^L R + (theta G)^T dNum: R[p][e] += sum_j (theta_j G[j][p]) dNum[j][e], token
+      // step outermost so that the dNum operands are read once per step (each tile's MFMAs keep
+      // their order)
+      if (DECAY) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        if (DECAY) St[t] *= a;
+        for (int t = 0; t < 4; ++t) St[t] *= a;
+      }
 #pragma unroll
-        for (int k0 = 0; k0 < BC; k0 += 16) {
-          const float* th = sf + BG::TH + k0 + 8 * (lane >> 5);
+      for (int k0 = 0; k0 < BC; k0 += 16) {
+        const float* th = sf + BG::TH + k0 + 8 * (lane >> 5);
+        const bf16x8 nh = ld_rows8(sh + BG::NH, TP, k0, 32 * cw, lane);
+        const bf16x8 nl = ld_rows8(sh + BG::NL, TP, k0, 32 * cw, lane);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
           const bf16x8 ga = ld_rows8(sh + BG::QH, TP, k0, 32 * t, lane);  // A[m=p][k=j]
-          const bf16x8 nh = ld_rows8(sh + BG::NH, TP, k0, 32 * cw, lane);
-          const bf16x8 nl = ld_rows8(sh + BG::NL, TP, k0, 32 * cw, lane);
           if (DECAY) {
             bf16x8 gh, gl;
             scale_split<ELU>(ga, ELU ? ld_rows8(sh + BG::QL, TP, k0, 32 * t, lane) : ga, th, gh, gl);
@@ -704,7 +716,8 @@ __global__ __launch_bounds__(KNT) void k_bwd_key(BackwardParams bp) {
         __builtin_amdgcn_sched_barrier(0);
       }
     } else {
-      // dF = Bm^T G + xi (V R^T + RZ): rows i, column p = col
+      // dF = Bm^T G + xi (V R^T + RZ), computed transposed like dV: dF^T[p][i], rows p (this
+      // wave's features), column i = 32 it + lane % 32, stored 16 bytes at a time
       f32x16 a2[2] = {zero16(), zero16()};
 #pragma unroll
       for (int et = 0; et < 4; ++et) {
@@ -714,55 +727,70 @@ __global__ __launch_bounds__(KNT) void k_bwd_key(BackwardParams bp) {
         for (int q = 0; q < 2; ++q)
 #pragma unroll
           for (int it = 0; it < 2; ++it) {
-            const bf16x8 va = ld_cols8_perm(sh + BG::V, TP, 32 * it, 32 * et, q, lane);  // A[m=i][k=e]
-            a2[it] = mfma32(va, th2[q], a2[it]);
-            a2[it] = mfma32(va, tl2[q], a2[it]);
+            const bf16x8 va = ld_cols8_perm(sh + BG::V, TP, 32 * it, 32 * et, q, lane);  // B[k=e][n=i] = V[i][e]
+            a2[it] = mfma32(th2[q], va, a2[it]);  // A[m=p][k=e] = R^T[e][p] (the D-tile, transposed)
+            a2[it] = mfma32(tl2[q], va, a2[it]);
           }
         __builtin_amdgcn_sched_barrier(0);
       }
       const __amdgpu_buffer_rsrc_t rdk = make_rsrc(bp.dk + r0 * BD, rows_extent(L, rsb4, BD * 4));
-      const float rzp = NORM ? sf[BG::ZV + col] : 0.f;
 #pragma unroll
       for (int it = 0; it < 2; ++it) {
         f32x16 a1 = zero16();
 #pragma unroll
         for (int k0 = 32 * it; k0 < BC; k0 += 16) {
-          const bf16x8 bmh = ld_rows8(sh + BG::BH, SQ, k0, 32 * it, lane);  // A[m=i][k=j] = Bm[j][i]
+          const bf16x8 bmh = ld_rows8(sh + BG::BH, SQ, k0, 32 * it, lane);  // B[k=j][n=i] = Bm[j][i]
           const bf16x8 bml = ld_rows8(sh + BG::BL, SQ, k0, 32 * it, lane);
-          const bf16x8 gq = ld_rows8(sh + BG::QH, TP, k0, 32 * cw, lane);  // B[k=j][n=p] = G[j][p]
-          a1 = mfma32(bmh, gq, a1);
-          a1 = mfma32(bml, gq, a1);
-          if (ELU) a1 = mfma32(bmh, ld_rows8(sh + BG::QL, TP, k0, 32 * cw, lane), a1);
+          const bf16x8 gq = ld_rows8(sh + BG::QH, TP, k0, 32 * cw, lane);  // A[m=p][k=j] = G[j][p]
+          a1 = mfma32(gq, bmh, a1);
+          a1 = mfma32(gq, bml, a1);
+          if (ELU) a1 = mfma32(ld_rows8(sh + BG::QL, TP, k0, 32 * cw, lane), bmh, a1);
         }
+        const int i = 32 * it + (lane & 31);
+        const float xi = sf[BG::XI + i];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int i = 32 * it + dtile_row(r, lane);
-          float g = a1[r] + sf[BG::XI + i] * (a2[it][r] + rzp);
-          if (ELU)
-            g *= dpsi_from_feat(from_bf16(sh[BG::KH + i * TP + col]) + from_bf16(sh[BG::KL + i * TP + col]));
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(g), rdk, (uint32_t)i * rsb4 + (uint32_t)col * 4, 0, 0);
+        for (int g4 = 0; g4 < 4; ++g4) {  // registers 4 g4 .. 4 g4 + 3: features 32 cw + 8 g4 + 4 hh + 0..3
+          const int p0 = 32 * cw + 8 * g4 + 4 * (lane >> 5);
+          const f32x4 rz4 = NORM ? *(const f32x4*)(sf + BG::ZV + p0) : f32x4{0.f, 0.f, 0.f, 0.f};
+          f32x4 o;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) o[u] = a1[4 * g4 + u] + xi * (a2[it][4 * g4 + u] + rz4[u]);
+          if (ELU) {
+            const bf16x4 kh4 = *(const bf16x4*)(sh + BG::KH + i * TP + p0);
+            const bf16x4 kl4 = *(const bf16x4*)(sh + BG::KL + i * TP + p0);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) o[u] *= dpsi_from_feat(from_bf16(kh4[u]) + from_bf16(kl4[u]));
+          }
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), rdk, (uint32_t)i * rsb4 + (uint32_t)p0 * 4,
+                                                 0, 0);
         }
       }
-      // R^T <- gamma^L R^T + dNum^T (theta G): R^T[e][p] += sum_j dNum[j][e] (theta_j G[j][p])
+      // R^T <- gamma^L R^T + dNum^T (theta G): R^T[e][p] += sum_j dNum[j][e] (theta_j G[j][p]), token
+      // step outermost so that theta G (read, scaled and split) is formed once per step for all
+      // four tiles (each tile's MFMAs keep their order)
+      if (DECAY) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        if (DECAY) St[t] *= a;
+        for (int t = 0; t < 4; ++t) St[t] *= a;
+      }
 #pragma unroll
-        for (int k0 = 0; k0 < BC; k0 += 16) {
-          const float* th = sf + BG::TH + k0 + 8 * (lane >> 5);
+      for (int k0 = 0; k0 < BC; k0 += 16) {
+        const float* th = sf + BG::TH + k0 + 8 * (lane >> 5);
+        const bf16x8 gb = ld_rows8(sh + BG::QH, TP, k0, 32 * cw, lane);  // B[k=j][n=p]
+        bf16x8 gh, gl;
+        if (DECAY) scale_split<ELU>(gb, ELU ? ld_rows8(sh + BG::QL, TP, k0, 32 * cw, lane) : gb, th, gh, gl);
+        else gh = gb, gl = ELU ? ld_rows8(sh + BG::QL, TP, k0, 32 * cw, lane) : gb;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
           const bf16x8 nh = ld_rows8(sh + BG::NH, TP, k0, 32 * t, lane);  // A[m=e][k=j] = dNum[j][e]
           const bf16x8 nl = ld_rows8(sh + BG::NL, TP, k0, 32 * t, lane);
-          const bf16x8 gb = ld_rows8(sh + BG::QH, TP, k0, 32 * cw, lane);  // B[k=j][n=p]
           if (DECAY) {
-            bf16x8 gh, gl;
-            scale_split<ELU>(gb, ELU ? ld_rows8(sh + BG::QL, TP, k0, 32 * cw, lane) : gb, th, gh, gl);
             St[t] = mfma32(nh, gh, St[t]);
             St[t] = mfma32(nl, gh, St[t]);
             St[t] = mfma32(nh, gl, St[t]);
           } else {
-            St[t] = mfma32(nh, gb, St[t]);
-            St[t] = mfma32(nl, gb, St[t]);
-            if (ELU) St[t] = mfma32(nh, ld_rows8(sh + BG::QL, TP, k0, 32 * cw, lane), St[t]);
+            St[t] = mfma32(nh, gh, St[t]);
+            St[t] = mfma32(nl, gh, St[t]);
+            if (ELU) St[t] = mfma32(nh, gl, St[t]);
           }
         }
         __builtin_amdgcn_sched_barrier(0);
