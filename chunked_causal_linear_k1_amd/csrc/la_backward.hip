@@ -471,23 +471,29 @@ __global__ __launch_bounds__(QNT) void k_bwd_query(BackwardParams bp) {
         }
         __builtin_amdgcn_sched_barrier(0);
         // state: S_< <- gamma^L S_< + F^T (xi V), held transposed: S^T[e][p] += sum_i (xi_i V[i][e]) F[i][p]
+        // (token step outermost: the F operands are read once per step for all four tiles; each
+        // tile's MFMAs keep their order)
         const float a = DECAY ? exp2f((float)L * lg) : 1.f;
+        if (DECAY) {
 #pragma unroll
-        for (int et = 0; et < 4; ++et) {
-          if (DECAY) St[et] *= a;
+          for (int et = 0; et < 4; ++et) St[et] *= a;
+        }
 #pragma unroll
-          for (int k0 = 0; k0 < BC; k0 += 16) {
+        for (int k0 = 0; k0 < BC; k0 += 16) {
+          const bf16x8 kh = ld_rows8(sh + BG::KH, TP, k0, 32 * cw, lane);  // B[k=i][n=p] = F[i][p]
+          const bf16x8 kl = ELU ? ld_rows8(sh + BG::KL, TP, k0, 32 * cw, lane) : kh;
+#pragma unroll
+          for (int et = 0; et < 4; ++et) {
             const bf16x8 va = ld_rows8(sh + BG::V, TP, k0, 32 * et, lane);  // A[m=e][k=i] = V[i][e]
-            const bf16x8 kh = ld_rows8(sh + BG::KH, TP, k0, 32 * cw, lane);  // B[k=i][n=p] = F[i][p]
             if (DECAY) {
               bf16x8 vh, vl;
               scale_split<false>(va, va, sf + BG::XI + k0 + 8 * (lane >> 5), vh, vl);
               St[et] = mfma32(vh, kh, St[et]);
               St[et] = mfma32(vl, kh, St[et]);
-              if (ELU) St[et] = mfma32(vh, ld_rows8(sh + BG::KL, TP, k0, 32 * cw, lane), St[et]);
+              if (ELU) St[et] = mfma32(vh, kl, St[et]);
             } else {
               St[et] = mfma32(va, kh, St[et]);  // rows past L are zero in F
-              if (ELU) St[et] = mfma32(va, ld_rows8(sh + BG::KL, TP, k0, 32 * cw, lane), St[et]);
+              if (ELU) St[et] = mfma32(va, kl, St[et]);
             }
           }
           __builtin_amdgcn_sched_barrier(0);
@@ -500,14 +506,15 @@ __global__ __launch_bounds__(QNT) void k_bwd_query(BackwardParams bp) {
           zreg = zn;
         }
       } else {
-        // adjoint summary: [p][e] += sum_j (W_j inv_j G[j][p]) dout[j][e]
+        // adjoint summary: [p][e] += sum_j (W_j inv_j G[j][p]) dout[j][e] (token step outermost:
+        // the dout operands are read once per step for all four tiles)
 #pragma unroll
-        for (int pt = 0; pt < 4; ++pt) {
+        for (int k0 = 0; k0 < BC; k0 += 16) {
+          const bf16x8 nh = ld_rows8(sh + BG::NH, TP, k0, 32 * cw, lane);  // B[k=j][n=e]
+          const bf16x8 nl = ld_rows8(sh + BG::NL, TP, k0, 32 * cw, lane);
 #pragma unroll
-          for (int k0 = 0; k0 < BC; k0 += 16) {
+          for (int pt = 0; pt < 4; ++pt) {
             const bf16x8 gh = ld_rows8(sh + BG::QH, TP, k0, 32 * pt, lane);  // A[m=p][k=j] = G[j][p]
-            const bf16x8 nh = ld_rows8(sh + BG::NH, TP, k0, 32 * cw, lane);  // B[k=j][n=e]
-            const bf16x8 nl = ld_rows8(sh + BG::NL, TP, k0, 32 * cw, lane);
             if (DECAY || NORM) {
               bf16x8 sh2, sl2;
               const bf16x8 gl = ELU ? ld_rows8(sh + BG::QL, TP, k0, 32 * pt, lane) : gh;
