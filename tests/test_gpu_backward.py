@@ -20,7 +20,7 @@ import pytest
 import torch
 
 import oracle
-from chunked_causal_linear_k1_amd import binding, inputs
+from chunked_causal_linear_k1_amd import binding, inputs, workloads
 from chunked_causal_linear_k1_amd.workloads import PSI_ELU1, PSI_IDENTITY, Workload
 
 from gpu_common import BF16_MAX_ABS, BF16_REL_L2, announce, metrics
@@ -204,3 +204,66 @@ def test_backward_varlen(case):
         _check(dS0[b:b + 1].cpu().numpy(), ref[3], f"varlen {name} seq {b} dS0")
         if normalize:
             _check(dZ0[b:b + 1].cpu().numpy(), ref[4], f"varlen {name} seq {b} dZ0")
+
+
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 129])
+@pytest.mark.parametrize("psi,normalize,decay", [(PSI_ELU1, 1, "const:0.99"), (PSI_IDENTITY, 0, "retnet_spread")])
+def test_backward_edge_lengths(T, psi, normalize, decay):
+    """One token, one short of a step, exactly a step, one past it, two steps and one: every
+    gradient against the oracle.
+
+    One token with a denominator is the method's degenerate case: o_1 = v_1 w / (w + eps) with
+    w = psi(q_1) . psi(k_1), so o_1 depends on q_1 and k_1 only through eps, and dq, dk are
+    eps-sized differences of O(1) terms (about 1e-9 here). There they are held to an absolute
+    bound at the rounding level of those terms (1e-5 of dv's scale) instead of a relative one."""
+    w = _workload(psi, normalize, decay, 1, 2, T, 64, seed=70 + T)
+    announce(f"backward edge T={T} psi={psi}")
+    inp = inputs.make_prefill_inputs(w)
+    dout = inputs.make_upstream_grad((1, 2, T, 128), w.seed + 1)
+    g = inp["gamma"]
+    dq, dk, dv = binding.lin_attn_prefill_backward(
+        *(inp[x].to(DEV) for x in ("q", "k", "v")), dout.to(DEV), psi=psi, chunk=64, normalize=normalize, eps=w.eps,
+        gamma=None if g is None else list(g))
+    torch.cuda.synchronize()
+    ref = oracle.prefill_backward(inp["q"], inp["k"], inp["v"], dout, psi,
+                                  gamma=None if g is None else np.repeat(g[None], 1, 0), normalize=normalize, eps=w.eps)
+    for lab, a, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref[:3]):
+        if T == 1 and normalize and lab != "dv":
+            err = float(np.abs(a.cpu().numpy() - r).max())
+            bound = 1e-5 * float(np.abs(ref[2]).max())
+            print(f"[parity] edge T=1 {lab} max_abs={err:.3e} bound={bound:.3e}", flush=True)
+            assert err <= bound, (lab, err, bound)
+            continue
+        _check(a.cpu().numpy(), r, f"edge T={T} {lab}")
+
+
+def _full_backward(w, heads):
+    """The timed backward workload at full size: sampled heads against the oracle, and a second
+    call bitwise equal to the first (the backward is deterministic)."""
+    announce(f"backward full-size {w.name} sampled heads {heads}")
+    inp = inputs.make_prefill_inputs(w, device=DEV)
+    dout = inputs.make_upstream_grad((w.B, w.H, w.T, w.d_v), w.seed + 17, device=DEV)
+    g = inp["gamma"]
+    kw = dict(psi=w.psi, chunk=w.chunk, normalize=w.normalize, eps=w.eps, gamma=None if g is None else list(g))
+    first = binding.lin_attn_prefill_backward(inp["q"], inp["k"], inp["v"], dout, **kw)
+    again = binding.lin_attn_prefill_backward(inp["q"], inp["k"], inp["v"], dout, **kw)
+    torch.cuda.synchronize()
+    for a, b in zip(first, again):
+        assert torch.equal(a, b), "backward is not deterministic"
+    del again
+    for hflat in heads:
+        b, h = divmod(hflat, w.H)
+        ref = oracle.prefill_backward(inp["q"][b, h].cpu(), inp["k"][b, h].cpu(), inp["v"][b, h].cpu(),
+                                      dout[b, h].cpu(), w.psi, gamma=None if g is None else [g[h]],
+                                      normalize=w.normalize, eps=w.eps)
+        for lab, a, r in zip(("dq", "dk", "dv"), first, ref[:3]):
+            _check(a[b, h].cpu().numpy(), r, f"{w.name} b={b} h={h} {lab}")
+
+
+def test_full_backward_retnet_128k_sampled():
+    # the fastest-decaying head and the slowest
+    _full_backward(workloads.RETNET_128K, heads=[0, 63])
+
+
+def test_full_backward_8k_elu1_sampled():
+    _full_backward(workloads.PREFILL_8K, heads=[0, 37])
