@@ -64,6 +64,18 @@ def test_decode_small(psi, d, normalize, gamma):
     _run_steps(w, S, Z, steps, w.steps)
 
 
+@pytest.mark.parametrize("psi,d,normalize,gamma", [(PSI_ELU1, 64, 1, 0.99), (PSI_IDENTITY, 128, 0, 0.97)])
+def test_decode_f32(psi, d, normalize, gamma):
+    """fp32 inputs (the prefill's fp32 configuration carried into decode): the fp32 bar."""
+    w = DecodeWorkload(name=f"dec_f32_psi{psi}_d{d}", N=2, H=3, d_k=d, d_v=d, n_psi=d, psi=psi, normalize=normalize,
+                       eps=1e-6, gamma=gamma, prefix_len=100, steps=6, seed=9, dtype="f32")
+    announce(f"decode fp32 {w.name}")
+    prefix = inputs.make_decode_prefix(w)
+    S, Z = _state_from_prefix(w, prefix)
+    steps = inputs.make_decode_steps(w)
+    _run_steps(w, S, Z, steps, w.steps)
+
+
 @pytest.mark.parametrize("psi,q_mult", [(PSI_PRF, 1.0), (PSI_PRF_QSHIFT, 1.0), (PSI_PRF_QSHIFT, 8.0)])
 def test_decode_prf(psi, q_mult):
     """PRF decode; with the query-row shift also for queries 8x larger, whose unshifted
