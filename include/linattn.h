@@ -92,7 +92,12 @@ typedef struct {
                             the last chunk may be ragged)                        */
   int32_t d_k, d_v;      /* key/query and value widths                           */
   int32_t n_psi;         /* feature width: == d_k unless psi is a PRF map        */
-  int32_t chunk;         /* chunk size C                                         */
+  int32_t chunk;         /* chunk size C: the token block of the method; segment
+                            boundaries (where the scanned states apply) fall on
+                            multiples of C. Within a chunk the kernels may group
+                            tokens differently (bf16 identity/elu1 walk 64-token
+                            steps); the result is the same function, C-invariant
+                            up to rounding                                       */
   int32_t psi;           /* la_psi                                               */
   int32_t normalize;     /* 1: divide by psi(q).Z + eps; 0: numerator only       */
   float eps;             /* >= 0; used only when normalize == 1                  */
