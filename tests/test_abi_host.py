@@ -297,3 +297,27 @@ def test_decode_validation():
     assert call(DecodeDesc(**dict(ok, psi=2, n_psi=256))) == LA_ERR_NULL  # PRF without bank
     assert call(DecodeDesc(**ok), S=ctypes.c_void_p((1 << 20) + 8)) == LA_ERR_ALIGN
     assert lib.lin_attn_decode_step(None, fake, fake, fake, None, None, fake, fake, fake, None) == LA_ERR_NULL
+
+
+def test_decay_head_limit():
+    """Per-head decays travel by value in the launch arguments, at most LA_MAX_DECAY_HEADS = 256
+    of them: 257 heads with gamma are rejected (prefill, backward, decode) before any launch. The
+    accepted cases (256 heads with gamma, 257 without) are shown to pass the gamma check by the
+    check that follows it, a workspace of zero bytes, so nothing is launched on these fake
+    pointers."""
+    lib = binding.load()
+    fake = ctypes.c_void_p(1 << 20)
+    g256 = (ctypes.c_float * 256)(*([0.99] * 256))
+    g257 = (ctypes.c_float * 257)(*([0.99] * 257))
+    for H, g, want in ((256, g256, LA_ERR_WORKSPACE), (257, g257, LA_ERR_UNSUPPORTED), (257, None, LA_ERR_WORKSPACE)):
+        d = _desc(B=1, H=H, T=100, chunk=64, psi=0, normalize=0)
+        got = lib.lin_attn_prefill(ctypes.byref(d), fake, fake, fake, g, None, None, None, fake, None, None, fake, 0,
+                                   None)
+        assert got == want, ("prefill", H, got)
+        gotb = lib.lin_attn_prefill_backward(ctypes.byref(d), fake, fake, fake, g, None, None, fake, fake, fake, fake,
+                                             None, None, fake, 0, None)
+        assert gotb == want, ("backward", H, gotb)
+    dd = DecodeDesc(N=1, H=257, d_k=128, d_v=128, n_psi=128, psi=0, normalize=0, eps=1e-6, in_dtype=LA_BF16,
+                    out_dtype=LA_F32)
+    assert lib.lin_attn_decode_step(ctypes.byref(dd), fake, fake, fake, g257, None, fake, None, fake,
+                                    None) == LA_ERR_UNSUPPORTED

@@ -267,3 +267,19 @@ def test_full_backward_retnet_128k_sampled():
 
 def test_full_backward_8k_elu1_sampled():
     _full_backward(workloads.PREFILL_8K, heads=[0, 37])
+
+
+def test_backward_max_decay_heads():
+    """256 heads, each with its own decay: every head's gradients against the oracle."""
+    w = _workload(PSI_IDENTITY, 0, "retnet_spread", 1, 256, 100, 64, seed=43)
+    announce("backward 256 decayed heads")
+    inp = inputs.make_prefill_inputs(w)
+    dout = inputs.make_upstream_grad((1, 256, 100, 128), 44)
+    g = inp["gamma"]
+    dq, dk, dv = binding.lin_attn_prefill_backward(*(inp[x].to(DEV) for x in ("q", "k", "v")), dout.to(DEV),
+                                                   psi=PSI_IDENTITY, chunk=64, normalize=0, eps=w.eps, gamma=list(g))
+    torch.cuda.synchronize()
+    ref = oracle.prefill_backward(inp["q"], inp["k"], inp["v"], dout, PSI_IDENTITY, gamma=np.asarray(g)[None],
+                                  normalize=0, eps=w.eps)
+    for lab, a, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref[:3]):
+        _check(a.cpu().numpy(), r, f"256 heads {lab}")

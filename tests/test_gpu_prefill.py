@@ -404,3 +404,17 @@ def test_prf_initial_and_final_state():
 
 def test_full_prf_4k_sampled():
     _full_size(workloads.PRF_4K, heads=[0, 37, 81, 127])
+
+
+def test_max_decay_heads():
+    """LA_MAX_DECAY_HEADS = 256 heads, each with its own decay (the spread formula over 256 heads),
+    every head against the oracle: the largest per-head table the launch arguments carry."""
+    w = Workload(name="decay256", B=1, H=256, T=200, d_k=64, d_v=64, n_psi=64, chunk=64, psi=PSI_IDENTITY,
+                 normalize=0, eps=1e-6, dtype="bf16", seed=41, qk_scale=64 ** -0.5, v_scale=1.0,
+                 decay="retnet_spread")
+    announce("prefill 256 decayed heads")
+    inp = inputs.make_prefill_inputs(w, device="cpu")
+    assert len(set(np.asarray(inp["gamma"]).tolist())) > 200  # distinct decays
+    o = _run(w, inp)
+    ref = _oracle_o(w, inp)
+    assert_close(o.cpu().reshape(w.H, w.T, w.d_v).numpy(), ref, "bf16", "256 decayed heads")
