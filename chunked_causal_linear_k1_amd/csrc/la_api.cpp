@@ -106,6 +106,11 @@ Plan make_plan(const la_prefill_desc* d, long long total_tokens = -1, bool gated
     pl.seg_chunks = (pl.n_chunks + 65534) / 65535;
     pl.n_seg = (pl.n_chunks + pl.seg_chunks - 1) / pl.seg_chunks;
   }
+  // the bf16 kernels walk 64-token steps: with 32-token chunks a segment holds an even number
+  if (!gated && d->in_dtype == LA_BF16 && d->chunk == 32 && (pl.seg_chunks & 1)) {
+    pl.seg_chunks += 1;
+    pl.n_seg = (pl.n_chunks + pl.seg_chunks - 1) / pl.seg_chunks;
+  }
   // one record per segment: S, Z (and, gated, the segment's per-row decay)
   const size_t E = (size_t)d->n_psi * d->d_v + (gated ? 2 : 1) * (size_t)d->n_psi;
   pl.ws_bytes = (size_t)BH * pl.n_seg * E * sizeof(float);

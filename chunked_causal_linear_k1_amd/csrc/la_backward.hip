@@ -839,7 +839,7 @@ hipError_t launch2(const BackwardParams& p, hipStream_t s, bool key_sweep) {
 bool prefill_backward_supported(int C, int d_k, int d_v, int n_psi, int psi) {
   if (psi != LA_PSI_IDENTITY && psi != LA_PSI_ELU1) return false;
   if (d_k != BD || d_v != BD || n_psi != BD) return false;
-  return C == 64 || C == 128;  // segments are whole multiples of the 64-token step
+  return C == 32 || C == 64 || C == 128;  // segments are whole multiples of the 64-token step
 }
 
 hipError_t launch_prefill_backward(const BackwardParams& p, hipStream_t s, bool key_sweep) {

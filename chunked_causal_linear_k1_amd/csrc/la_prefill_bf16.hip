@@ -8,11 +8,15 @@ namespace la {
 bool prefill_prf_bf16_supported(int C, int d_k, int d_v, int n_psi);
 hipError_t launch_prefill_prf_bf16(const PrefillParams& p, hipStream_t s, bool out);
 
+// Chunks of 32, 64 or 128 tokens: the kernels walk 64-token steps (see in_64_token_steps), so
+// the planner keeps segment boundaries on multiples of 64 tokens (an even chunk count per
+// segment at C = 32).
 bool prefill_bf16_supported(int C, int d_k, int d_v, int n_psi, int psi) {
-  if (is_prf(psi)) return prefill_prf_bf16_supported(C, d_k, d_v, n_psi);
+  if (C != 32 && C != 64 && C != 128) return false;
+  if (is_prf(psi)) return prefill_prf_bf16_supported(64, d_k, d_v, n_psi);
   if (psi != LA_PSI_IDENTITY && psi != LA_PSI_ELU1) return false;
   if (d_k != d_v || n_psi != d_k) return false;
-  return (d_k == 64 || d_k == 128) && (C == 64 || C == 128);
+  return d_k == 64 || d_k == 128;
 }
 
 static hipError_t dispatch(const PrefillParams& p, hipStream_t s, bool out) {
@@ -25,17 +29,20 @@ static hipError_t dispatch(const PrefillParams& p, hipStream_t s, bool out) {
 // Neither pass depends on how a segment's tokens are grouped into chunks: the segment
 // summary is the decayed sum of psi(k_i) v_i^T over the segment's tokens, and each output is
 // the same sum over the tokens before it however the prefix is split between the carried
-// state and the chunk's own scores. So at C = 128 both passes walk the segment in 64-token
-// steps (segment boundaries, multiples of seg_chunks * C tokens, are unchanged): the 64-token
-// kernels need half the LDS, two workgroups share a CU and hide each other's latency. The
-// results differ from a 128-token grouping only by rounding. (128k retention workload: output
-// pass 2.21 ms in 64-token steps against 2.50 ms in 128-token chunks.)
+// state and the chunk's own scores. So both passes walk every segment in 64-token steps
+// (segment boundaries, multiples of seg_chunks * C tokens and of 64, are unchanged): at C =
+// 128 the 64-token kernels need half the LDS, two workgroups share a CU and hide each other's
+// latency, and C = 32 needs no kernels of its own. The results differ from another grouping
+// only by rounding. (128k retention workload: output pass 2.21 ms in 64-token steps against
+// 2.50 ms in 128-token chunks.)
 static PrefillParams in_64_token_steps(const PrefillParams& p) {
-  if (p.C != 128 || is_prf(p.psi)) return p;
+  if (p.C == 64) return p;
   PrefillParams q = p;
   q.C = 64;
-  q.n_chunks = 2 * p.n_chunks;  // kernels count each sequence's chunks from its own length
-  q.seg_chunks = 2 * p.seg_chunks;
+  // kernels count each sequence's steps from its own length; C = 32 segments hold an even
+  // number of chunks (the planner's rule)
+  q.n_chunks = p.C == 128 ? 2 * p.n_chunks : (p.n_chunks + 1) / 2;
+  q.seg_chunks = p.C == 128 ? 2 * p.seg_chunks : p.seg_chunks / 2;
   return q;
 }
 

@@ -95,9 +95,10 @@ typedef struct {
   int32_t chunk;         /* chunk size C: the token block of the method; segment
                             boundaries (where the scanned states apply) fall on
                             multiples of C. Within a chunk the kernels may group
-                            tokens differently (bf16 identity/elu1 walk 64-token
-                            steps); the result is the same function, C-invariant
-                            up to rounding                                       */
+                            tokens differently (the bf16 kernels walk 64-token
+                            steps, and with C = 32 a segment holds an even number
+                            of chunks); the result is the same function,
+                            C-invariant up to rounding                           */
   int32_t psi;           /* la_psi                                               */
   int32_t normalize;     /* 1: divide by psi(q).Z + eps; 0: numerator only       */
   float eps;             /* >= 0; used only when normalize == 1                  */
@@ -110,9 +111,9 @@ typedef struct {
 
 /* Supported sizes in this build (anything else: LA_ERR_UNSUPPORTED):
  *   in_dtype LA_BF16: psi identity/elu1: d_k == d_v == n_psi in {64, 128},
- *                     chunk in {64, 128};
+ *                     chunk in {32, 64, 128};
  *                     psi PRF, PRF_QSHIFT: d_k == d_v == 128, n_psi in {128, 256},
- *                     chunk 64.
+ *                     chunk in {32, 64, 128}.
  *   in_dtype LA_F32 : d_k, d_v <= 128, n_psi <= 256 (LDS permitting),
  *                     chunk in {16, 32, 64}, any psi.
  *   always: d_v and n_psi multiples of 4 (16-byte state rows in the workspace).
@@ -242,7 +243,7 @@ la_status lin_attn_prefill_gated(const la_prefill_desc* d, const void* q, const 
  * gamma, eps and the feature map are constants (no gradient for them).
  *
  *   d         as for lin_attn_prefill; supported: in_dtype LA_BF16, psi identity or elu1,
- *             d_k == d_v == n_psi == 128, chunk 64 or 128 (walked in steps of 64 tokens:
+ *             d_k == d_v == n_psi == 128, chunk 32, 64 or 128 (walked in steps of 64 tokens:
  *             the gradient does not depend on the grouping), either layout. out_dtype is
  *             the type of dout (LA_F32 or LA_BF16).
  *   dout      device, dL/do, laid out like lin_attn_prefill's o, out_dtype

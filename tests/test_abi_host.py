@@ -80,9 +80,14 @@ def _ws(desc):
     # state rows must be whole 16-byte groups (the scan moves 4 floats per access)
     (dict(in_dtype=LA_F32, d_k=30, d_v=30, n_psi=30, chunk=32, psi=0), LA_ERR_UNSUPPORTED),
     (dict(in_dtype=LA_F32, d_k=32, d_v=32, n_psi=32, chunk=32, psi=0), LA_OK),
-    # positive random features: bf16 needs d 128, n_psi 128 or 256, chunk 64
+    # positive random features: bf16 needs d 128, n_psi 128 or 256; chunks 32, 64, 128 (all
+    # walked in 64-token steps)
     (dict(psi=2, n_psi=256), LA_OK), (dict(psi=2, n_psi=128), LA_OK),
-    (dict(psi=2, n_psi=64), LA_ERR_UNSUPPORTED), (dict(psi=2, n_psi=256, chunk=128), LA_ERR_UNSUPPORTED),
+    (dict(psi=2, n_psi=64), LA_ERR_UNSUPPORTED), (dict(psi=2, n_psi=256, chunk=128), LA_OK),
+    (dict(psi=2, n_psi=256, chunk=32), LA_OK), (dict(psi=2, n_psi=256, chunk=16), LA_ERR_UNSUPPORTED),
+    # bf16 identity / elu+1: chunks 32, 64, 128
+    (dict(chunk=32), LA_OK), (dict(chunk=32, d_k=64, d_v=64, n_psi=64, psi=0), LA_OK),
+    (dict(chunk=16), LA_ERR_UNSUPPORTED), (dict(chunk=256), LA_ERR_UNSUPPORTED),
     # the same features with the query-row shift; anything past it is not a feature map
     (dict(psi=3, n_psi=256), LA_OK), (dict(psi=3, n_psi=128), LA_OK), (dict(psi=3, n_psi=64), LA_ERR_UNSUPPORTED),
     (dict(psi=3, in_dtype=LA_F32, d_k=64, d_v=64, n_psi=96, chunk=32), LA_OK), (dict(psi=4), LA_ERR_VALUE),
@@ -112,6 +117,10 @@ def test_workspace_size_planner():
     # never more segments than chunks
     st, n_small = _ws(_desc(T=1, H=1))
     assert st == LA_OK and n_small == 4 * E
+    # chunks of 32 tokens: segments hold an even number of chunks (whole 64-token steps); one
+    # 100-token sequence gets 2 segments of 2 chunks, not 4 of 1
+    st, n32 = _ws(_desc(B=1, H=1, T=100, chunk=32))
+    assert st == LA_OK and n32 == 2 * 4 * E
     assert binding.load().lin_attn_prefill_workspace_size(None, None) == LA_ERR_NULL
 
 
@@ -233,7 +242,8 @@ def test_backward_validation_and_workspace():
     assert st0 == LA_OK and n0 == 2 * fwd.value
     assert ws(**{**base, "chunk": 128, "psi": 0})[0] == LA_OK
     assert ws(**{**base, "layout": 1})[0] == LA_OK
-    for kw in (dict(chunk=32), dict(psi=2, n_psi=256), dict(d_k=64, d_v=64, n_psi=64), dict(in_dtype=LA_F32),
+    assert ws(**{**base, "chunk": 32})[0] == LA_OK
+    for kw in (dict(chunk=16), dict(psi=2, n_psi=256), dict(d_k=64, d_v=64, n_psi=64), dict(in_dtype=LA_F32),
                dict(psi=3, n_psi=256)):
         assert ws(**{**base, **kw})[0] == LA_ERR_UNSUPPORTED, kw
     d = _desc(**base)

@@ -66,6 +66,8 @@ CASES = [
     ("elu1_short", PSI_ELU1, 1, "none", 1, 2, 37, 64, False, "f32", "bhtd"),
     ("elu1_bf16_dout_bthd", PSI_ELU1, 1, "const:0.99", 2, 3, 200, 128, True, "bf16", "bthd"),
     ("retention_bthd_bf16", PSI_IDENTITY, 0, "retnet_spread", 1, 4, 450, 64, False, "bf16", "bthd"),
+    ("elu1_norm_decay_c32_state", PSI_ELU1, 1, "const:0.99", 1, 2, 333, 32, True, "f32", "bhtd"),
+    ("retention_c32_bthd", PSI_IDENTITY, 0, "retnet_spread", 1, 3, 260, 32, False, "bf16", "bthd"),
 ]
 
 
@@ -136,19 +138,20 @@ def test_backward_long_segments(psi, normalize, decay):
 
 
 def test_backward_chunk_invariance():
-    """chunk 64 and chunk 128 describe the same function: their gradients agree to rounding."""
+    """chunks 32, 64 and 128 describe the same function: their gradients agree to rounding."""
     w = _workload(PSI_ELU1, 1, "const:0.99", 1, 2, 700, 64, seed=3)
-    announce("backward chunk 64 vs 128")
+    announce("backward chunk 64 vs 128 vs 32")
     inp = inputs.make_prefill_inputs(w, device=DEV)
     dout = inputs.make_upstream_grad((1, 2, 700, 128), 4, device=DEV)
     res = []
-    for C in (64, 128):
+    for C in (64, 128, 32):
         kw = dict(psi=PSI_ELU1, chunk=C, normalize=1, eps=w.eps, gamma=list(inp["gamma"]))
         res.append(binding.lin_attn_prefill_backward(inp["q"], inp["k"], inp["v"], dout, **kw))
     torch.cuda.synchronize()
-    for lab, a, b in zip(("dq", "dk", "dv"), res[0], res[1]):
-        rel, _ = metrics(a.cpu().numpy(), b.cpu().numpy())
-        assert rel < 1e-3, (lab, rel)
+    for other in (1, 2):
+        for lab, a, b in zip(("dq", "dk", "dv"), res[0], res[other]):
+            rel, _ = metrics(a.cpu().numpy(), b.cpu().numpy())
+            assert rel < 1e-3, (lab, other, rel)
 
 
 VARLEN_LENGTHS = [200, 0, 1, 63, 64, 65, 777, 128, 1000, 31]
@@ -157,6 +160,7 @@ VARLEN_CASES = [
     ("elu1_norm_decay", PSI_ELU1, 1, "const:0.995", 64, "f32"),
     ("retention_spread_bf16", PSI_IDENTITY, 0, "retnet_spread", 128, "bf16"),
     ("elu1_norm", PSI_ELU1, 1, "none", 128, "bf16"),
+    ("retention_decay_c32", PSI_IDENTITY, 0, "const:0.99", 32, "f32"),
 ]
 
 

@@ -39,6 +39,9 @@ CASES = [
     ("elu1_c128_d128", 128, 128, 128, PSI_ELU1, 1, "none", "bf16"),
     ("identity_c64_d64", 64, 64, 64, PSI_IDENTITY, 0, "const:0.97", "bf16"),
     ("prf256_c64", 128, 256, 64, PSI_PRF, 1, "none", "bf16"),
+    # chunks of 32 and PRF at 128: the same 64-token steps, segments on multiples of 64 tokens
+    ("retention_c32_d128", 128, 128, 32, PSI_IDENTITY, 0, "retnet_spread", "bf16"),
+    ("prf256_c128", 128, 256, 128, PSI_PRF, 1, "none", "bf16"),
     ("f32_elu1_c32_d64", 64, 64, 32, PSI_ELU1, 1, "const:0.99", "f32"),
 ]
 

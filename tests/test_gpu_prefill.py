@@ -65,6 +65,9 @@ SMALL = [
     # identity features with a denominator are ill-conditioned (psi(q).Z can cross zero), so
     # the retention form is the identity case tested at C = 64, d = 128 as well
     ("identity_decay_c64_d128", 1, 3, 901, 128, 64, PSI_IDENTITY, 0, "retnet_spread", "bf16"),
+    # chunks of 32 tokens (walked in 64-token steps; segments hold an even number of chunks)
+    ("identity_decay_c32", 1, 3, 777, 128, 32, PSI_IDENTITY, 0, "retnet_spread", "bf16"),
+    ("elu1_norm_c32_d64", 2, 2, 501, 64, 32, PSI_ELU1, 1, "const:0.99", "bf16"),
     ("f32_elu1_c32", 1, 2, 300, 64, 32, PSI_ELU1, 1, "none", "f32"),
     ("f32_identity_decay_c16", 1, 2, 200, 32, 16, PSI_IDENTITY, 0, "const:0.9", "f32"),
 ]
@@ -201,8 +204,8 @@ def test_integer_inputs_bit_exact():
 
 
 def test_chunk_size_invariance():
-    """C = 64 and C = 128 compute the same function: both within tolerance of the oracle
-    and of each other."""
+    """C = 32, 64 and 128 compute the same function: each within tolerance of the oracle
+    and of C = 64."""
     base = dict(B=1, H=2, T=900, d_k=128, d_v=128, n_psi=128, psi=PSI_IDENTITY, normalize=0, eps=1e-6,
                 dtype="bf16", seed=21, qk_scale=128 ** -0.5, v_scale=1.0, decay="retnet_spread")
     announce("prefill chunk-size invariance")
@@ -211,10 +214,13 @@ def test_chunk_size_invariance():
     inp = inputs.make_prefill_inputs(w64, device="cpu")
     o64 = _run(w64, inp).cpu().numpy()
     o128 = _run(w128, inp).cpu().numpy()
+    o32 = _run(Workload(name="c32", chunk=32, **base), inp).cpu().numpy()
     ref = _oracle_o(w64, inp)
     assert_close(o64.reshape(2, 900, 128), ref, "bf16", "C=64")
     assert_close(o128.reshape(2, 900, 128), ref, "bf16", "C=128")
+    assert_close(o32.reshape(2, 900, 128), ref, "bf16", "C=32")
     assert_close(o64, o128, "bf16", "C=64 vs C=128")
+    assert_close(o64, o32, "bf16", "C=64 vs C=32")
 
 
 def _full_size(w: Workload, heads):
@@ -306,6 +312,18 @@ def test_prf_small_elementwise(case):
         # rel-L2 as is, max-abs on outputs scaled by the largest reference magnitude
         scale = float(np.abs(ref).max())
         assert_close(o / scale, ref / scale, "bf16", f"{name} (scaled by max |o| = {scale:.3g})")
+
+
+@pytest.mark.parametrize("C", [32, 128])
+def test_prf_chunk_sizes(C):
+    """Positive random features with chunks of 32 and 128 tokens (the kernels' 64-token steps)."""
+    w = Workload(name=f"prf256_c{C}", B=1, H=2, T=450, d_k=128, d_v=128, n_psi=256, chunk=C, psi=PSI_PRF,
+                 normalize=1, eps=1e-6, dtype="bf16", seed=17, qk_scale=128 ** -0.25, v_scale=1.0,
+                 decay="const:0.99")
+    announce(f"prefill prf chunk {C}")
+    inp = inputs.make_prefill_inputs(w, device="cpu")
+    o = _run(w, inp).cpu().reshape(2, 450, 128).numpy()
+    assert_close(o, _oracle_o(w, inp), "bf16", f"prf chunk {C}")
 
 
 # the same features with the query-row log-space shift (psi(q)_p = exp(l_p - max_r l_r) / sqrt(m))
