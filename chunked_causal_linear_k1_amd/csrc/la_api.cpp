@@ -22,6 +22,8 @@ constexpr int kTargetWorkgroups = 2048;  // enough to fill 256 CUs several times
 constexpr int kMinWorkgroups = 256;      // at least one per CU where the sequences allow it
 constexpr int kMinSegTokens = 2048;      // per-segment state traffic (n_psi*d_v floats written,
                                          // scanned, read back) small next to the token traffic
+constexpr int kMinSubTokens = 1024;      // the same bound for the summary pass's sub-segments
+constexpr int kMaxRecPerSeg = 4;
 
 bool aligned16(const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -78,6 +80,7 @@ la_status validate_prefill_desc(const la_prefill_desc* d, bool gated = false) {
 
 struct Plan {
   int n_chunks, seg_chunks, n_seg;
+  int rec_per_seg, n_rec;  // summary records per segment and per sequence (at most)
   size_t ws_bytes;
 };
 
@@ -86,7 +89,12 @@ struct Plan {
 // knows (T is the longest); segments then have a fixed token count sized from the batch's
 // total, so the non-empty workgroups number about kTargetWorkgroups and carry similar work
 // whatever the length mix (segments past a shorter sequence's end are empty and exit at once).
-Plan make_plan(const la_prefill_desc* d, long long total_tokens = -1, bool gated = false) {
+//
+// sub (fixed-length bf16 forward only): when the segments leave the summary pass short of
+// workgroups, it folds rec_per_seg sub-segments per segment (whole 64-token steps, at least
+// kMinSubTokens each), so that the pass takes a fraction of a segment's time; the scan then
+// runs over the sub-segment records and each segment reads the record at its start.
+Plan make_plan(const la_prefill_desc* d, long long total_tokens = -1, bool gated = false, bool sub = false) {
   Plan pl;
   const long long BH = (long long)d->B * d->H;
   pl.n_chunks = (int)((d->T + (long long)d->chunk - 1) / d->chunk);
@@ -111,9 +119,23 @@ Plan make_plan(const la_prefill_desc* d, long long total_tokens = -1, bool gated
     pl.seg_chunks += 1;
     pl.n_seg = (pl.n_chunks + pl.seg_chunks - 1) / pl.seg_chunks;
   }
-  // one record per segment: S, Z (and, gated, the segment's per-row decay)
+  pl.rec_per_seg = 1;
+  if (sub && !gated && total_tokens < 0 && d->in_dtype == LA_BF16) {
+    const int step = d->chunk == 32 ? 2 : 1;  // chunks per 64-token step
+    // workgroups that fold tokens when the last segment (only the final state needs it) is skipped
+    const long long folded = BH * std::max(1, pl.n_seg - 1);
+    while (pl.rec_per_seg < kMaxRecPerSeg) {
+      const int k2 = 2 * pl.rec_per_seg;
+      if (pl.seg_chunks % (k2 * step) != 0) break;
+      if ((long long)(pl.seg_chunks / k2) * d->chunk < kMinSubTokens) break;
+      if (folded * k2 > kTargetWorkgroups || (long long)pl.n_seg * k2 > 65535) break;
+      pl.rec_per_seg = k2;
+    }
+  }
+  pl.n_rec = pl.n_seg * pl.rec_per_seg;
+  // one record per segment or sub-segment: S, Z (and, gated, the segment's per-row decay)
   const size_t E = (size_t)d->n_psi * d->d_v + (gated ? 2 : 1) * (size_t)d->n_psi;
-  pl.ws_bytes = (size_t)BH * pl.n_seg * E * sizeof(float);
+  pl.ws_bytes = (size_t)BH * pl.n_rec * E * sizeof(float);
   return pl;
 }
 
@@ -141,7 +163,7 @@ la_status lin_attn_prefill_workspace_size(const la_prefill_desc* d, size_t* byte
   if (!bytes) return LA_ERR_NULL;
   const la_status st = validate_prefill_desc(d);
   if (st != LA_OK) return st;
-  *bytes = make_plan(d).ws_bytes;
+  *bytes = make_plan(d, -1, false, true).ws_bytes;
   return LA_OK;
 }
 
@@ -224,7 +246,8 @@ la_status prefill_impl(const la_prefill_desc* d, const int32_t* cu_seqlens, int3
   st = check_gamma(gamma, d->H);
   if (st != LA_OK) return st;
   if (gated && !aligned16(log_gate)) return LA_ERR_ALIGN;
-  const Plan pl = make_plan(d, cu_seqlens ? (long long)total_tokens : -1LL, gated);
+  const bool sub = !gated && !cu_seqlens;
+  const Plan pl = make_plan(d, cu_seqlens ? (long long)total_tokens : -1LL, gated, sub);
   if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes)) return LA_ERR_WORKSPACE;
 
   PrefillParams p;
@@ -245,7 +268,20 @@ la_status prefill_impl(const la_prefill_desc* d, const int32_t* cu_seqlens, int3
   p.psi = d->psi; p.normalize = d->normalize; p.eps = d->eps;
   p.out_bf16 = d->out_dtype == LA_BF16;
   p.n_chunks = pl.n_chunks; p.seg_chunks = pl.seg_chunks; p.n_seg = pl.n_seg;
+  p.n_rec = pl.n_rec; p.rec_per_seg = pl.rec_per_seg; p.sum_end = pl.n_chunks;
   p.has_decay = fill_log2g(gamma, d->H, p.log2g);
+  // The last segment's records feed only the final state: without one, the summary pass stops
+  // at the last segment's start, whose single empty record the scan turns into its prefix.
+  const bool want_final = final_S || (d->normalize && final_Z);
+  if (sub && d->in_dtype == LA_BF16 && !want_final) {  // the bf16 kernels honour sum_end and n_rec
+    p.n_rec = pl.rec_per_seg * (pl.n_seg - 1) + 1;
+    p.sum_end = (pl.n_seg - 1) * pl.seg_chunks;
+  }
+  // the summary pass: one workgroup per record
+  PrefillParams ps = p;
+  ps.seg_chunks = pl.seg_chunks / pl.rec_per_seg;
+  ps.n_seg = p.n_rec;
+  ps.rec_per_seg = 1;
 
   ScanParams sp;
   memset(&sp, 0, sizeof sp);
@@ -258,7 +294,7 @@ la_status prefill_impl(const la_prefill_desc* d, const int32_t* cu_seqlens, int3
   sp.gated = gated;
   sp.BH = d->B * d->H; sp.H = d->H; sp.T = d->T;
   sp.n_psi = d->n_psi; sp.d_v = d->d_v;
-  sp.n_seg = pl.n_seg; sp.seg_len = pl.seg_chunks * d->chunk;
+  sp.n_seg = ps.n_seg; sp.seg_len = ps.seg_chunks * d->chunk;
   sp.has_decay = p.has_decay;
   memcpy(sp.log2g, p.log2g, sizeof sp.log2g);
 
@@ -268,8 +304,8 @@ la_status prefill_impl(const la_prefill_desc* d, const int32_t* cu_seqlens, int3
   const bool bf = d->in_dtype == LA_BF16;
   hipError_t e = mark(0);
   if (e == hipSuccess)
-    e = gated ? la::launch_prefill_gated(p, stream, false)
-              : bf ? la::launch_prefill_bf16_summary(p, stream) : la::launch_prefill_f32_summary(p, stream);
+    e = gated ? la::launch_prefill_gated(ps, stream, false)
+              : bf ? la::launch_prefill_bf16_summary(ps, stream) : la::launch_prefill_f32_summary(ps, stream);
   if (e == hipSuccess) e = mark(1);
   if (e == hipSuccess) e = la::launch_segment_scan(sp, stream);
   if (e == hipSuccess) e = mark(2);
@@ -414,6 +450,7 @@ la_status backward_impl(const la_prefill_desc* d, const int32_t* cu_seqlens, int
   p.d_k = d->d_k; p.d_v = d->d_v; p.n_psi = d->n_psi; p.C = d->chunk;
   p.psi = d->psi; p.normalize = d->normalize; p.eps = d->eps;
   p.n_chunks = pl.n_chunks; p.seg_chunks = pl.seg_chunks; p.n_seg = pl.n_seg;
+  p.n_rec = pl.n_seg; p.rec_per_seg = 1; p.sum_end = pl.n_chunks;
   p.has_decay = fill_log2g(gamma, d->H, p.log2g);
   bp.dout = dout;
   bp.dq = dq; bp.dk = dk; bp.dv = dv;

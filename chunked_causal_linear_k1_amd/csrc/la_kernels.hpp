@@ -14,8 +14,12 @@ namespace la {
 // Work decomposition: each (batch, head) sequence of T tokens is cut into
 // n_chunks = ceil(T / C) chunks, and consecutive chunks are grouped into n_seg
 // segments of seg_chunks chunks (the last segment and the last chunk may be
-// short). The workspace holds one summary (a, S, Z) per segment, scanned in place.
-// One workgroup per (sequence, segment): blockIdx.x = b * H + h, blockIdx.y = segment.
+// short). The workspace holds summary records (a, S, Z), n_rec per sequence, scanned in
+// place into exclusive prefixes; the output pass of segment s starts from record
+// s * rec_per_seg. The summary pass may fold sub-segments (rec_per_seg records per
+// segment) and may stop at chunk sum_end: records past it are empty, which is enough
+// when no final state is asked for (the last segment's records feed only that state).
+// One workgroup per (sequence, segment or record): blockIdx.x = b * H + h.
 // With per-sequence lengths (cu_seqlens) T is the longest sequence: segments that
 // start past a shorter sequence's end are empty (identity summaries, no outputs).
 //
@@ -44,6 +48,9 @@ struct PrefillParams {
   int in_f32;            // q, k, v are fp32 (gated path; the other paths dispatch on dtype)
   float eps;
   int n_chunks, seg_chunks, n_seg;
+  int n_rec;             // summary records per sequence in ws (the record stride)
+  int rec_per_seg;       // records per segment
+  int sum_end;           // the summary pass folds chunks below this index only
   int has_decay;
   float log2g[LA_MAX_DECAY_HEADS];  // log2(gamma_h), 0 when gamma_h == 1
 };
@@ -111,6 +118,12 @@ __device__ __forceinline__ int packed_len(const int* cu, int b, int total, int m
 }
 
 // Where the sequence of (batch, head) bh lives: its length and its first token row.
+// The workspace record that segment seg of sequence bh starts from (output pass), or
+// record seg itself when rec_per_seg is 1 (summary pass).
+__device__ __forceinline__ size_t rec_index(const PrefillParams& p, int bh, int seg) {
+  return (size_t)bh * p.n_rec + (size_t)seg * p.rec_per_seg;
+}
+
 struct SeqSpan {
   int T;
   long long row0;

@@ -43,6 +43,8 @@ static PrefillParams in_64_token_steps(const PrefillParams& p) {
   // number of chunks (the planner's rule)
   q.n_chunks = p.C == 128 ? 2 * p.n_chunks : (p.n_chunks + 1) / 2;
   q.seg_chunks = p.C == 128 ? 2 * p.seg_chunks : p.seg_chunks / 2;
+  // an end that is not the sequence's last chunk is a segment or record boundary: even at C = 32
+  q.sum_end = p.C == 128 ? 2 * p.sum_end : (p.sum_end + 1) / 2;
   return q;
 }
 

@@ -260,10 +260,11 @@ __global__ __launch_bounds__(2 * D) void k_summary(PrefillParams p) {
   const uint32_t rse = (uint32_t)p.tok_rows * D, rsb = rse * 2;  // elements / bytes between token rows
   const uint16_t* kb = (const uint16_t*)p.k + sq.row0 * D;
   const uint16_t* vb = (const uint16_t*)p.v + sq.row0 * D;
-  const int c0 = seg * p.seg_chunks, c1 = min(c0 + p.seg_chunks, n_chunks);
+  const int c0 = seg * p.seg_chunks, c1 = min(min(c0 + p.seg_chunks, n_chunks), p.sum_end);
+  const int L0 = c0 < c1 ? min(C, T - c0 * C) : 0;
   Pieces<C, D> pk, pv;
-  load_pieces<C, D>(pk, kb + (size_t)c0 * C * rse, min(C, T - c0 * C), rsb);
-  load_pieces<C, D>(pv, vb + (size_t)c0 * C * rse, min(C, T - c0 * C), rsb);
+  load_pieces<C, D>(pk, kb + (size_t)c0 * C * rse, L0, rsb);
+  load_pieces<C, D>(pv, vb + (size_t)c0 * C * rse, L0, rsb);
   for (int c = c0; c < c1; ++c) {
     const int L = min(C, T - c * C);
     const float a = DECAY ? exp2f((float)L * lg) : 1.f;
@@ -295,7 +296,7 @@ __global__ __launch_bounds__(2 * D) void k_summary(PrefillParams p) {
   }
   // segment summary -> workspace [bh][seg][E], E = D*D + D
   const size_t E = (size_t)D * D + D;
-  float* out = p.ws + ((size_t)bh * p.n_seg + seg) * E;
+  float* out = p.ws + rec_index(p, bh, seg) * E;
   const int n = lane & 31;
 #pragma unroll
   for (int pt = 0; pt < D / 32; ++pt)
@@ -439,7 +440,7 @@ void k_output_sh(PrefillParams p) {
 
   // exclusive prefix state of this segment (written by the scan)
   const size_t E = (size_t)D * D + D;
-  const float* pre = p.ws + ((size_t)bh * p.n_seg + seg) * E;
+  const float* pre = p.ws + rec_index(p, bh, seg) * E;
   f32x16 S[D / 32];
 #pragma unroll
   for (int pt = 0; pt < D / 32; ++pt)
@@ -929,7 +930,7 @@ __global__ __launch_bounds__(512) void k_output_w8(PrefillParams p) {
   float* const fN = (float*)(smem + pin(G::OFF_F + 4 * n));
 
   const size_t E = (size_t)D * D + D;
-  const float* pre = p.ws + ((size_t)bh * p.n_seg + seg) * E;
+  const float* pre = p.ws + rec_index(p, bh, seg) * E;
   f32x16 S[D / 32];
 #pragma unroll
   for (int pt = 0; pt < D / 32; ++pt)

@@ -270,10 +270,10 @@ __global__ __launch_bounds__(2 * D) void k_summary_prf(PrefillParams p) {
   const uint32_t rse = (uint32_t)p.tok_rows * D, rsb = rse * 2;  // elements / bytes between token rows
   const uint16_t* kg = (const uint16_t*)p.k + sq.row0 * D;
   const uint16_t* vg = (const uint16_t*)p.v + sq.row0 * D;
-  const int c0 = seg * p.seg_chunks, c1 = min(c0 + p.seg_chunks, n_chunks);
+  const int c0 = seg * p.seg_chunks, c1 = min(min(c0 + p.seg_chunks, n_chunks), p.sum_end);
   pf::Pieces<C, D> pk_, pv_;
   {
-    const int L0 = min(C, T - c0 * C);
+    const int L0 = c0 < c1 ? min(C, T - c0 * C) : 0;
     pf::load_pieces<C, D>(pk_, kg + (size_t)c0 * C * rse, L0, rsb);
     pf::load_pieces<C, D>(pv_, vg + (size_t)c0 * C * rse, L0, rsb);
     vm_drain();
@@ -326,7 +326,7 @@ __global__ __launch_bounds__(2 * D) void k_summary_prf(PrefillParams p) {
   }
   // segment summary -> workspace [bh][seg][E], E = NP*D + NP
   const size_t E = (size_t)NP * D + NP;
-  float* out = p.ws + ((size_t)bh * p.n_seg + seg) * E;
+  float* out = p.ws + rec_index(p, bh, seg) * E;
 #pragma unroll
   for (int pt = 0; pt < NFT; ++pt)
 #pragma unroll
@@ -384,7 +384,7 @@ __global__ __launch_bounds__(2 * D) void k_output_prf(PrefillParams p) {
 
   // exclusive prefix state of this segment
   const size_t E = (size_t)NP * D + NP;
-  const float* pre = p.ws + ((size_t)bh * p.n_seg + seg) * E;
+  const float* pre = p.ws + rec_index(p, bh, seg) * E;
   f32x16 S[NFT];
 #pragma unroll
   for (int pt = 0; pt < NFT; ++pt)

@@ -21,6 +21,8 @@
 // wave totals are scanned with a Blelloch up-sweep/down-sweep in LDS (log2 W levels
 // each; the down-sweep combines parent-prefix (+) left-sum in that order because the
 // monoid does not commute), and each wave then writes its run's exclusive prefixes.
+// With few segments (W below 4) a workgroup holds several such groups of W waves, each on
+// its own 256 elements, so that short scans still run four waves per workgroup.
 // The order of all floating-point operations is fixed: results are deterministic.
 #include "la_device.hpp"
 #include "la_kernels.hpp"
@@ -29,6 +31,14 @@ namespace la {
 namespace {
 
 constexpr int kMaxWaves = 16;
+constexpr int kMinGroupWaves = 4;  // waves per workgroup at least (W times the element groups)
+
+// Waves over the segment axis: a power of two, runs of ~4 segments per wave.
+__host__ __device__ inline int scan_seg_waves(int n_seg) {
+  int W = 1;
+  while (W < kMaxWaves && W * 4 < n_seg) W <<= 1;
+  return W;
+}
 
 __device__ __forceinline__ f32x4 ld4(const float* p) { return *(const f32x4*)p; }
 __device__ __forceinline__ void st4(float* p, const f32x4& v) { *(f32x4*)p = v; }
@@ -39,14 +49,16 @@ template <int RUN>
 __global__ __launch_bounds__(64 * kMaxWaves) void k_segment_scan(ScanParams p) {
   __shared__ f32x4 sx[kMaxWaves][64];
   __shared__ f32x4 sa[kMaxWaves][64];  // decays per element: rows differ under per-row gates
-  const int W = blockDim.x >> 6;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int W = scan_seg_waves(p.n_seg);
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int w = wid % W, grp = wid / W, n_grp = (blockDim.x >> 6) / W;
+  const int o = grp * W;  // this element group's LDS slots
   const int bh = blockIdx.y, head = bh % p.H;
   const size_t SE = (size_t)p.n_psi * p.d_v;
   const size_t E = SE + p.n_psi;  // scanned elements; a multiple of 4 (n_psi and d_v are)
   // segment record: S, Z, then (gated) the segment's per-row decay vector
   const size_t REC = E + (p.gated ? p.n_psi : 0);
-  const size_t e = ((size_t)blockIdx.x * 64 + lane) * 4;
+  const size_t e = (((size_t)blockIdx.x * n_grp + grp) * 64 + lane) * 4;
   const bool live = e < E;
   const float lg = p.has_decay ? p.log2g[head] : 0.f;
   // scan position i is segment seg_of(i): the same segment in forward order, mirrored in reverse
@@ -101,8 +113,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_segment_scan(ScanParams p) {
       ta *= as;
     }
   }
-  sx[w][lane] = tx;
-  sa[w][lane] = ta;
+  sx[o + w][lane] = tx;
+  sa[o + w][lane] = ta;
   __syncthreads();
 
   // 2. Blelloch over the W wave totals (W is a power of two)
@@ -113,19 +125,19 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_segment_scan(ScanParams p) {
     f32x4 na = {1.f, 1.f, 1.f, 1.f};
     if (act) {
       const int left = right - d;
-      nx = sa[right][lane] * sx[left][lane] + sx[right][lane];
-      na = sa[left][lane] * sa[right][lane];
+      nx = sa[o + right][lane] * sx[o + left][lane] + sx[o + right][lane];
+      na = sa[o + left][lane] * sa[o + right][lane];
     }
     __syncthreads();
     if (act) {
-      sx[right][lane] = nx;
-      sa[right][lane] = na;
+      sx[o + right][lane] = nx;
+      sa[o + right][lane] = na;
     }
     __syncthreads();
   }
   if (w == W - 1) {
-    sx[W - 1][lane] = f32x4{0.f, 0.f, 0.f, 0.f};
-    sa[W - 1][lane] = f32x4{1.f, 1.f, 1.f, 1.f};
+    sx[o + W - 1][lane] = f32x4{0.f, 0.f, 0.f, 0.f};
+    sa[o + W - 1][lane] = f32x4{1.f, 1.f, 1.f, 1.f};
   }
   __syncthreads();
   for (int d = W >> 1; d >= 1; d >>= 1) {  // down-sweep
@@ -135,25 +147,25 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_segment_scan(ScanParams p) {
     const bool act = right < W;
     if (act) {
       const int left = right - d;
-      lx = sx[left][lane];
-      la_ = sa[left][lane];
-      px = sx[right][lane];
-      pa = sa[right][lane];
+      lx = sx[o + left][lane];
+      la_ = sa[o + left][lane];
+      px = sx[o + right][lane];
+      pa = sa[o + right][lane];
     }
     __syncthreads();
     if (act) {
       const int left = right - d;
-      sx[left][lane] = px;              // left child gets the parent's prefix
-      sx[right][lane] = la_ * px + lx;  // right child: prefix (+) left sum
-      sa[left][lane] = pa;
-      sa[right][lane] = pa * la_;
+      sx[o + left][lane] = px;              // left child gets the parent's prefix
+      sx[o + right][lane] = la_ * px + lx;  // right child: prefix (+) left sum
+      sa[o + left][lane] = pa;
+      sa[o + right][lane] = pa * la_;
     }
     __syncthreads();
   }
 
   // 3. carry into this run: init (+) prefix_w
-  f32x4 cx = sx[w][lane];
-  const f32x4 ca = sa[w][lane];
+  f32x4 cx = sx[o + w][lane];
+  const f32x4 ca = sa[o + w][lane];
   if (live) {
     f32x4 init = {0.f, 0.f, 0.f, 0.f};
     if (e < SE) {
@@ -196,18 +208,18 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_segment_scan(ScanParams p) {
 }  // namespace
 
 hipError_t launch_segment_scan(const ScanParams& p, hipStream_t s) {
-  // waves per workgroup: a power of two, runs of ~4 segments per wave, at most kMaxWaves
-  int W = 1;
-  while (W < kMaxWaves && W * 4 < p.n_seg) W <<= 1;
+  const int W = scan_seg_waves(p.n_seg);
+  const int G = W < kMinGroupWaves ? kMinGroupWaves / W : 1;  // element groups per workgroup
   const int per = (p.n_seg + W - 1) / W;
   const size_t E = (size_t)p.n_psi * p.d_v + p.n_psi;
-  dim3 grid((unsigned)((E + 255) / 256), p.BH);
+  dim3 grid((unsigned)((E + 256 * G - 1) / (256 * G)), p.BH);
+  const dim3 block(64 * W * G);
   if (per <= 4)
-    hipLaunchKernelGGL(k_segment_scan<4>, grid, dim3(64 * W), 0, s, p);
+    hipLaunchKernelGGL(k_segment_scan<4>, grid, block, 0, s, p);
   else if (per <= 8)
-    hipLaunchKernelGGL(k_segment_scan<8>, grid, dim3(64 * W), 0, s, p);
+    hipLaunchKernelGGL(k_segment_scan<8>, grid, block, 0, s, p);
   else
-    hipLaunchKernelGGL(k_segment_scan<0>, grid, dim3(64 * W), 0, s, p);
+    hipLaunchKernelGGL(k_segment_scan<0>, grid, block, 0, s, p);
   return hipGetLastError();
 }
 

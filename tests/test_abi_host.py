@@ -107,10 +107,21 @@ def test_workspace_size_planner():
     assert st == LA_OK and n_big % (4 * E) == 0
     segs = n_big // (4 * E) // 64
     assert 1 <= segs <= 1024
+    # 128k x 64 heads: 32 segments of 4096 tokens (sub-segments would pass 2048 workgroups)
+    assert segs == 32
     # segments of at least 2048 tokens unless that leaves fewer than 256 workgroups:
-    # the 8k x 64-sequence shape gets 4 segments of 2048 tokens (256 workgroups)
+    # the 8k x 64-sequence shape gets 4 segments of 2048 tokens (256 workgroups), whose
+    # summaries are folded as two 1024-token records each (the workspace holds them all)
     st, n8 = _ws(_desc(B=4, H=16, T=8192))
-    assert st == LA_OK and n8 == 4 * E * 64 * 4
+    assert st == LA_OK and n8 == 4 * E * 64 * 4 * 2
+    # the same with PRF features (n_psi 256) at 4k x 128 sequences: 2 segments, 2 records each
+    Ep = 256 * 128 + 256
+    st, n4 = _ws(_desc(B=8, H=16, T=4096, n_psi=256, psi=2))
+    assert st == LA_OK and n4 == 4 * Ep * 128 * 2 * 2
+    # fp32 inputs keep one record per segment
+    Ef = 64 * 64 + 64
+    st, n8f = _ws(_desc(B=4, H=16, T=8192, d_k=64, d_v=64, n_psi=64, in_dtype=binding.LA_F32))
+    assert st == LA_OK and n8f == 4 * Ef * 64 * 4
     # a single short sequence still gets one segment per chunk up to 256 workgroups
     st, n1s = _ws(_desc(B=1, H=1, T=4096))
     assert st == LA_OK and n1s == 4 * E * 64

@@ -147,6 +147,37 @@ def test_initial_and_final_state():
     assert_close(fZ.cpu().reshape(4, 128).numpy(), rZ, "bf16", "final Z")
 
 
+def test_subsegment_records_and_final_state():
+    """Enough sequences for 2048-token segments, so the summary pass folds each segment as two
+    1024-token records: with a final state asked for it folds every segment; without one it
+    stops at the last segment's start. Both against the oracle (sampled heads, initial state
+    given, per-head decay, ragged last chunk)."""
+    B, H, T, d = 2, 64, 4000, 64
+    w = Workload(name="subseg", B=B, H=H, T=T, d_k=d, d_v=d, n_psi=d, chunk=64, psi=PSI_ELU1, normalize=1,
+                 eps=1e-6, dtype="bf16", seed=12, qk_scale=0.5, v_scale=1.0, decay="retnet_spread")
+    desc = binding.prefill_desc(B, H, T, d, d, d, 64, PSI_ELU1, 1, 1e-6, binding.LA_BF16, binding.LA_F32,
+                                binding.LA_LAYOUT_BHTD)
+    assert binding.workspace_size(desc) == 4 * (d * d + d) * B * H * 2 * 2  # 2 segments x 2 records
+    announce("prefill sub-segment records, with and without the final state")
+    inp = inputs.make_prefill_inputs(w, device="cpu")
+    rng = np.random.default_rng(9)
+    S0 = (rng.standard_normal((B, H, d, d)) * 0.5).astype(np.float32)
+    Z0 = (np.abs(rng.standard_normal((B, H, d))) * 10 + 1).astype(np.float32)
+    init = dict(init_S=torch.from_numpy(S0).to(DEV), init_Z=torch.from_numpy(Z0).to(DEV))
+    fS = torch.empty((B, H, d, d), dtype=torch.float32, device=DEV)
+    fZ = torch.empty((B, H, d), dtype=torch.float32, device=DEV)
+    o_fin = _run(w, inp, final_S=fS, final_Z=fZ, **init).cpu().reshape(B * H, T, d).numpy()
+    o_nof = _run(w, inp, **init).cpu().reshape(B * H, T, d).numpy()
+    heads = [0, 45, 64, 127]
+    ref, rS, rZ = _oracle_o(w, inp, heads=heads, S0=S0.reshape(B * H, d, d)[heads].astype(np.float64),
+                            Z0=Z0.reshape(B * H, d)[heads].astype(np.float64), want_state=True)
+    assert_close(o_fin[heads], ref, "bf16", "o, final state asked for")
+    assert_close(o_nof[heads], ref, "bf16", "o, no final state")
+    assert_close(o_nof, o_fin, "bf16", "o with and without the final state")
+    assert_close(fS.cpu().reshape(B * H, d, d).numpy()[heads], rS, "bf16", "final S")
+    assert_close(fZ.cpu().reshape(B * H, d).numpy()[heads], rZ, "bf16", "final Z")
+
+
 def test_initial_and_final_state_c64():
     """The same hand-off at C = 64 (the two-waves-per-SIMD output kernel), per-head decay."""
     w = Workload(name="state_c64", B=2, H=3, T=777, d_k=128, d_v=128, n_psi=128, chunk=64, psi=PSI_ELU1,
