@@ -90,10 +90,11 @@ struct Plan {
 // total, so the non-empty workgroups number about kTargetWorkgroups and carry similar work
 // whatever the length mix (segments past a shorter sequence's end are empty and exit at once).
 //
-// sub (fixed-length bf16 forward only): when the segments leave the summary pass short of
-// workgroups, it folds rec_per_seg sub-segments per segment (whole 64-token steps, at least
-// kMinSubTokens each), so that the pass takes a fraction of a segment's time; the scan then
-// runs over the sub-segment records and each segment reads the record at its start.
+// sub (fixed-length bf16 forward only, gated or not): when the segments leave the summary
+// pass short of workgroups, it folds rec_per_seg sub-segments per segment (whole steps of
+// the kernels: 64 tokens, or the gated path's 32-token chunks; at least kMinSubTokens each),
+// so that the pass takes a fraction of a segment's time; the scan then runs over the
+// sub-segment records and each segment reads the record at its start.
 Plan make_plan(const la_prefill_desc* d, long long total_tokens = -1, bool gated = false, bool sub = false) {
   Plan pl;
   const long long BH = (long long)d->B * d->H;
@@ -120,8 +121,8 @@ Plan make_plan(const la_prefill_desc* d, long long total_tokens = -1, bool gated
     pl.n_seg = (pl.n_chunks + pl.seg_chunks - 1) / pl.seg_chunks;
   }
   pl.rec_per_seg = 1;
-  if (sub && !gated && total_tokens < 0 && d->in_dtype == LA_BF16) {
-    const int step = d->chunk == 32 ? 2 : 1;  // chunks per 64-token step
+  if (sub && total_tokens < 0 && d->in_dtype == LA_BF16) {
+    const int step = !gated && d->chunk == 32 ? 2 : 1;  // chunks per kernel step
     // workgroups that fold tokens when the last segment (only the final state needs it) is skipped
     const long long folded = BH * std::max(1, pl.n_seg - 1);
     while (pl.rec_per_seg < kMaxRecPerSeg) {
@@ -171,7 +172,7 @@ la_status lin_attn_prefill_gated_workspace_size(const la_prefill_desc* d, size_t
   if (!bytes) return LA_ERR_NULL;
   const la_status st = validate_prefill_desc(d, true);
   if (st != LA_OK) return st;
-  *bytes = make_plan(d, -1, true).ws_bytes;
+  *bytes = make_plan(d, -1, true, true).ws_bytes;
   return LA_OK;
 }
 
@@ -246,7 +247,7 @@ la_status prefill_impl(const la_prefill_desc* d, const int32_t* cu_seqlens, int3
   st = check_gamma(gamma, d->H);
   if (st != LA_OK) return st;
   if (gated && !aligned16(log_gate)) return LA_ERR_ALIGN;
-  const bool sub = !gated && !cu_seqlens;
+  const bool sub = !cu_seqlens;
   const Plan pl = make_plan(d, cu_seqlens ? (long long)total_tokens : -1LL, gated, sub);
   if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes)) return LA_ERR_WORKSPACE;
 
@@ -273,7 +274,7 @@ la_status prefill_impl(const la_prefill_desc* d, const int32_t* cu_seqlens, int3
   // The last segment's records feed only the final state: without one, the summary pass stops
   // at the last segment's start, whose single empty record the scan turns into its prefix.
   const bool want_final = final_S || (d->normalize && final_Z);
-  if (sub && d->in_dtype == LA_BF16 && !want_final) {  // the bf16 kernels honour sum_end and n_rec
+  if (sub && d->in_dtype == LA_BF16 && !want_final) {  // the bf16 kernels (gated too) honour sum_end and n_rec
     p.n_rec = pl.rec_per_seg * (pl.n_seg - 1) + 1;
     p.sum_end = (pl.n_seg - 1) * pl.seg_chunks;
   }

@@ -327,6 +327,20 @@ struct MGeo {
   static_assert(FEND % 4 == 0 && (GC * P) % 8 == 0 && (GC * AP) % 8 == 0, "16-byte aligned regions");
 };
 
+// The summary pass's LDS image: psi(k), the gates, the chunk's end decays and the k^ and v
+// tiles, without the output pass's query, score and off-diagonal regions (59 KiB at d = 128,
+// so two summary workgroups share a CU). Offsets as in MGeo.
+template <int D>
+struct MSumGeo {
+  static constexpr int NT = 2 * D, NW = D / 32, P = D + 8;
+  static constexpr int PK = 0, AL = PK + GC * D, AEND = AL + GC * D, FEND = AEND + D;
+  static constexpr int H0 = 2 * FEND;
+  static constexpr int KH = H0, KL = KH + GC * P, V = KL + GC * P;
+  static constexpr int HEND = V + GC * P;
+  static constexpr int BYTES = HEND * 2;
+  static_assert(FEND % 4 == 0 && (GC * P) % 8 == 0, "16-byte aligned regions");
+};
+
 // Global tile of GC token rows x D bf16 (16-byte pieces) / fp32 log gates.
 template <int D>
 struct MLoad {
@@ -361,9 +375,8 @@ __device__ __forceinline__ void mload(MLoad<D>& T, const PrefillParams& p, long 
 
 // Commit: psi(q), psi(k) as fp32 (rows >= L zero), v, and the log gates (summary) or the
 // gates exp(log_gate) (output pass, Q); padded rows have gate 1.
-template <int D, bool Q>
+template <int D, bool Q, typename G = MGeo<D>>
 __device__ __forceinline__ void mcommit(const MLoad<D>& T, float* sf, __bf16* sh, int L, bool elu) {
-  using G = MGeo<D>;
   constexpr int NT = 2 * D, RP = D / 8, RPF = D / 4;
 #pragma unroll
   for (int i = 0; i < MLoad<D>::PB; ++i) {
@@ -378,7 +391,7 @@ __device__ __forceinline__ void mcommit(const MLoad<D>& T, float* sf, __bf16* sh
     }
     *(f32x4*)(sf + G::PK + row * D + col) = k0;
     *(f32x4*)(sf + G::PK + row * D + col + 4) = k1;
-    if (Q) {
+    if constexpr (Q) {
       const bf16x8 qx = __builtin_bit_cast(bf16x8, T.q[i]);
       f32x4 q0, q1;
 #pragma unroll
@@ -397,7 +410,7 @@ __device__ __forceinline__ void mcommit(const MLoad<D>& T, float* sf, __bf16* sh
     const int pc = threadIdx.x + i * NT, row = pc / RPF, col = (pc % RPF) * 4;
     const f32x4 g = __builtin_bit_cast(f32x4, T.g[i]);
     f32x4 x = row < L ? g : f32x4{0.f, 0.f, 0.f, 0.f};  // padded tokens: log gate 0, gate 1
-    if (Q) x = f32x4{__expf(x[0]), __expf(x[1]), __expf(x[2]), __expf(x[3])};
+    if constexpr (Q) x = f32x4{__expf(x[0]), __expf(x[1]), __expf(x[2]), __expf(x[3])};
     *(f32x4*)(sf + G::AL + row * D + col) = x;
   }
 }
@@ -406,9 +419,8 @@ __device__ __forceinline__ void mcommit(const MLoad<D>& T, float* sf, __bf16* sh
 // (hi + lo), and with Q also q^_j = psi(q_j) e^{G_j} (hi + lo) and the gates exp(log_gate)
 // in place of the log gates. Returns G_end (this feature's summed log gate over the chunk)
 // and adds sum_i k^_i to *ksum.
-template <int D, bool Q>
+template <int D, bool Q, typename G = MGeo<D>>
 __device__ __forceinline__ float feature_pass(float* sf, __bf16* sh, float* ksum) {
-  using G = MGeo<D>;
   const int p = threadIdx.x;
   float g[GC];
   float c = 0.f;
@@ -417,7 +429,7 @@ __device__ __forceinline__ float feature_pass(float* sf, __bf16* sh, float* ksum
     const float lg = sf[G::AL + j * D + p];
     c += lg;
     g[j] = c;
-    if (Q) {
+    if constexpr (Q) {
       sf[G::AL + j * D + p] = __expf(lg);
       const bf16_pair pr = split_bf16(sf[G::PQ + j * D + p] * __expf(c));
       sh[G::QH + j * G::P + p] = pr.hi;
@@ -438,9 +450,8 @@ __device__ __forceinline__ float feature_pass(float* sf, __bf16* sh, float* ksum
 }
 
 // State update of wave w's columns: S[p][e] = e^{G_end[p]} S[p][e] + sum_i k^_i[p] v_i[e].
-template <int D>
+template <int D, typename G = MGeo<D>>
 __device__ __forceinline__ void mstate(f32x16 (&S)[D / 32], const float* sf, const __bf16* sh, int w, int lane) {
-  using G = MGeo<D>;
 #pragma unroll
   for (int pt = 0; pt < D / 32; ++pt) {
 #pragma unroll
@@ -456,7 +467,7 @@ __device__ __forceinline__ void mstate(f32x16 (&S)[D / 32], const float* sf, con
 
 template <int D>
 __global__ __launch_bounds__(2 * D) void k_summary_gla_m(PrefillParams p) {
-  using G = MGeo<D>;
+  using G = MSumGeo<D>;
   extern __shared__ __align__(16) unsigned char smem[];
   float* sf = (float*)smem;
   __bf16* sh = (__bf16*)smem;
@@ -464,7 +475,7 @@ __global__ __launch_bounds__(2 * D) void k_summary_gla_m(PrefillParams p) {
   const bool elu = p.psi == LA_PSI_ELU1, norm = p.normalize != 0;
   const SeqSpan sq = seq_span(p, bh);
   const int T = sq.T, n_chunks = (T + GC - 1) / GC;
-  const int c0 = seg * p.seg_chunks, c1 = min(c0 + p.seg_chunks, n_chunks);
+  const int c0 = seg * p.seg_chunks, c1 = min(min(c0 + p.seg_chunks, n_chunks), p.sum_end);
   f32x16 S[D / 32];
 #pragma unroll
   for (int pt = 0; pt < D / 32; ++pt)
@@ -476,22 +487,22 @@ __global__ __launch_bounds__(2 * D) void k_summary_gla_m(PrefillParams p) {
   for (int c = c0; c < c1; ++c) {
     const int L = min(GC, T - c * GC);
     lds_barrier();
-    mcommit<D, false>(T0, sf, sh, L, elu);
+    mcommit<D, false, G>(T0, sf, sh, L, elu);
     if (c + 1 < c1) mload<D>(T0, p, sq.row0 + (long long)(c + 1) * GC * p.tok_rows, min(GC, T - (c + 1) * GC));
     lds_barrier();
     if (tid < D) {
       float ks;
-      const float ge = feature_pass<D, false>(sf, sh, &ks);
+      const float ge = feature_pass<D, false, G>(sf, sh, &ks);
       const float ae = __expf(ge);
       sf[G::AEND + tid] = ae;
       z = ae * z + ks;
       segtot += ge;
     }
     lds_barrier();
-    mstate<D>(S, sf, sh, w, lane);
+    mstate<D, G>(S, sf, sh, w, lane);
   }
   const size_t REC = (size_t)D * D + 2 * D;
-  float* out = p.ws + ((size_t)bh * p.n_seg + seg) * REC;
+  float* out = p.ws + rec_index(p, bh, seg) * REC;
 #pragma unroll
   for (int pt = 0; pt < D / 32; ++pt)
 #pragma unroll
@@ -516,7 +527,7 @@ __global__ __launch_bounds__(2 * D) void k_output_gla_m(PrefillParams p) {
   const int c0 = seg * p.seg_chunks, c1 = min(c0 + p.seg_chunks, n_chunks);
   if (c0 >= c1) return;
   const size_t REC = (size_t)D * D + 2 * D;
-  const float* pre = p.ws + ((size_t)bh * p.n_seg + seg) * REC;
+  const float* pre = p.ws + rec_index(p, bh, seg) * REC;
   f32x16 S[D / 32];  // S[p][e]: rows p in tile pt, column e = 32 w + lane % 32
 #pragma unroll
   for (int pt = 0; pt < D / 32; ++pt)
@@ -739,11 +750,12 @@ hipError_t launch_m(const PrefillParams& p, hipStream_t s, bool out) {
   using G = MGeo<D>;
   const void* kern = !out ? (const void*)k_summary_gla_m<D>
                      : p.out_bf16 ? (const void*)k_output_gla_m<D, true> : (const void*)k_output_gla_m<D, false>;
-  hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, G::BYTES);
+  const int lds = out ? G::BYTES : MSumGeo<D>::BYTES;
+  hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
   dim3 grid(p.B * p.H, p.n_seg);
   void* args[] = {(void*)&p};
-  e = hipLaunchKernel(kern, grid, dim3(G::NT), args, G::BYTES, s);
+  e = hipLaunchKernel(kern, grid, dim3(G::NT), args, lds, s);
   if (e != hipSuccess) return e;
   return hipGetLastError();
 }

@@ -162,6 +162,39 @@ def test_gated_prefill_then_decode():
         assert_close(o.cpu().reshape(B * H, d).numpy(), ref[:, T + t], "bf16", f"hand-off step {t}")
 
 
+def test_gated_subsegment_records_and_final_state():
+    """Enough sequences for 2048-token segments, so the gated summary pass folds each segment
+    as two 1024-token records: every segment when the final state is asked for, all but the
+    last otherwise. Sampled sequences against the oracle (initial state given, ragged tail)."""
+    B, H, T, d = 2, 64, 4090, 64
+    w = Workload(name="gated_subseg", B=B, H=H, T=T, d_k=d, d_v=d, n_psi=d, chunk=32, psi=PSI_ELU1, normalize=1,
+                 eps=1e-6, dtype="bf16", seed=81, qk_scale=0.5, v_scale=1.0)
+    desc = binding.prefill_desc(B, H, T, d, d, d, 32, PSI_ELU1, 1, 1e-6, binding.LA_BF16)
+    assert binding.gated_workspace_size(desc) == 4 * (d * d + 2 * d) * B * H * 2 * 2  # 2 segments x 2 records
+    announce("gated sub-segment records, with and without the final state")
+    q, k, v, lg = _inputs(w, 8.0)
+    rng = np.random.default_rng(10)
+    S0 = (rng.standard_normal((B, H, d, d)) * 0.5).astype(np.float32)
+    Z0 = (np.abs(rng.standard_normal((B, H, d))) * 10 + 1).astype(np.float32)
+    fS = torch.empty((B, H, d, d), dtype=torch.float32, device=DEV)
+    fZ = torch.empty((B, H, d), dtype=torch.float32, device=DEV)
+    dev = [t.to(DEV) for t in (q, k, v, lg)]
+    kw = dict(psi=PSI_ELU1, normalize=1, eps=w.eps, init_S=torch.from_numpy(S0).to(DEV),
+              init_Z=torch.from_numpy(Z0).to(DEV))
+    o_fin = binding.lin_attn_prefill_gated(*dev, final_S=fS, final_Z=fZ, **kw)
+    o_nof = binding.lin_attn_prefill_gated(*dev, **kw)
+    torch.cuda.synchronize()
+    for b, h in ((0, 0), (1, 63)):
+        sl = slice(h, h + 1)
+        ref, rS, rZ = oracle.prefill(q[b, sl], k[b, sl], v[b, sl], PSI_ELU1, normalize=1, eps=float(np.float32(w.eps)),
+                                     log_gate=lg[b, sl], S0=S0[b, sl].astype(np.float64),
+                                     Z0=Z0[b, sl].astype(np.float64), want_state=True)
+        assert_close(o_fin[b, sl].cpu().numpy(), ref, "bf16", f"gated o, final state asked for (b={b}, h={h})")
+        assert_close(o_nof[b, sl].cpu().numpy(), ref, "bf16", f"gated o, no final state (b={b}, h={h})")
+        assert_close(fS[b, sl].cpu().numpy(), rS, "bf16", f"gated final S (b={b}, h={h})")
+        assert_close(fZ[b, sl].cpu().numpy(), rZ, "bf16", f"gated final Z (b={b}, h={h})")
+
+
 def test_full_gated_8k_sampled():
     """The 4 x 16 x 8192 gated workload in the benchmark's launch configuration; sampled
     (batch, head) sequences against the oracle."""
