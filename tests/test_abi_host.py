@@ -221,6 +221,12 @@ def test_gated_validation_and_workspace():
         assert ws(**{**base, **kw})[0] == LA_ERR_UNSUPPORTED, kw
     assert ws(**{**base, "psi": 1, "normalize": 1, "d_k": 64, "d_v": 64, "n_psi": 64})[0] == LA_OK
     assert ws(**{**base, "in_dtype": LA_F32, "layout": 1})[0] == LA_OK
+    # the 4 x 16 x 8192 gated shape: 4 segments of 2048 tokens per sequence, summarised as two
+    # 1024-token records each in bf16 (the workspace holds them all); fp32 inputs keep one
+    st, n8 = ws(**{**base, "B": 4, "H": 16, "T": 8192})
+    assert st == LA_OK and n8 == 4 * E * 64 * 4 * 2
+    st, n8f = ws(**{**base, "B": 4, "H": 16, "T": 8192, "in_dtype": LA_F32})
+    assert st == LA_OK and n8f == 4 * E * 64 * 4
     d = _desc(**base)
     fake, odd = ctypes.c_void_p(1 << 20), ctypes.c_void_p((1 << 20) + 4)
     call = lambda g, w=fake: lib.lin_attn_prefill_gated(ctypes.byref(d), fake, fake, fake, g, None, None, fake, None,
