@@ -60,6 +60,9 @@ la_status validate_prefill_desc(const la_prefill_desc* d, bool gated = false) {
   if (d->out_dtype != LA_BF16 && d->out_dtype != LA_F32) return LA_ERR_VALUE;
   if (d->layout != LA_LAYOUT_BHTD && d->layout != LA_LAYOUT_BTHD) return LA_ERR_VALUE;
   if (!la::is_prf(d->psi) && d->n_psi != d->d_k) return LA_ERR_SHAPE;
+  // the query-row shift cancels only against a denominator; without one each output would be
+  // scaled by the query's exp(-max log-feature), a different function from plain PRF's
+  if (d->psi == LA_PSI_PRF_QSHIFT && !d->normalize) return LA_ERR_UNSUPPORTED;
   if (d->d_v % 4 != 0 || d->n_psi % 4 != 0) return LA_ERR_UNSUPPORTED;  // 16-byte state rows
   // element counts must fit comfortably in 64-bit offsets and the grid's y extent
   const double tokens = (double)d->B * d->H * d->T;
@@ -361,6 +364,7 @@ la_status decode_impl(const la_decode_desc* d, const void* q, const void* k, con
   if (d->in_dtype != LA_BF16 && d->in_dtype != LA_F32) return LA_ERR_VALUE;
   if (d->out_dtype != LA_BF16 && d->out_dtype != LA_F32) return LA_ERR_VALUE;
   if (!la::is_prf(d->psi) && d->n_psi != d->d_k) return LA_ERR_SHAPE;
+  if (d->psi == LA_PSI_PRF_QSHIFT && !d->normalize) return LA_ERR_UNSUPPORTED;  // as in prefill
   if ((long long)d->N * d->H > 2147483647LL) return LA_ERR_SHAPE;
   if (d->out_dtype != LA_F32) return LA_ERR_UNSUPPORTED;
   if (!la::decode_supported(d->d_k, d->d_v, d->n_psi, d->psi)) return LA_ERR_UNSUPPORTED;

@@ -73,7 +73,9 @@ typedef enum {
                          * - |q|^2/2; keys unshifted. The shift depends on the query
                          * row only and scales numerator and denominator alike, so the
                          * output equals LA_PSI_PRF's with eps weighted by exp(max_r l_r);
-                         * it keeps psi(q) . S finite for large-magnitude queries.   */
+                         * it keeps psi(q) . S finite for large-magnitude queries.
+                         * Requires normalize == 1 (LA_ERR_UNSUPPORTED otherwise):
+                         * without the denominator nothing cancels the shift.        */
 } la_psi;
 
 typedef enum { LA_BF16 = 0, LA_F32 = 1 } la_dtype;

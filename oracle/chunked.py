@@ -105,7 +105,7 @@ def chunked(q: np.ndarray, k: np.ndarray, v: np.ndarray, psi: int, C: int, gamma
     NC = -(-T // C)
     Tp = NC * C
     fq = feature_np(q, psi, w)
-    fk = feature_np(k, psi, w)
+    fk = feature_np(k, 2 if psi == 3 else psi, w)  # keys never take the query-row shift
     n_psi = fq.shape[1]
     # right-pad to a whole number of chunks; padded keys are zeroed after the feature map
     fq_p = np.zeros((Tp, n_psi)); fq_p[:T] = fq

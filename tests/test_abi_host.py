@@ -91,6 +91,9 @@ def _ws(desc):
     # the same features with the query-row shift; anything past it is not a feature map
     (dict(psi=3, n_psi=256), LA_OK), (dict(psi=3, n_psi=128), LA_OK), (dict(psi=3, n_psi=64), LA_ERR_UNSUPPORTED),
     (dict(psi=3, in_dtype=LA_F32, d_k=64, d_v=64, n_psi=96, chunk=32), LA_OK), (dict(psi=4), LA_ERR_VALUE),
+    # the shift cancels only against the denominator: without one it is refused
+    (dict(psi=3, n_psi=256, normalize=0), LA_ERR_UNSUPPORTED),
+    (dict(psi=3, in_dtype=LA_F32, d_k=64, d_v=64, n_psi=96, chunk=32, normalize=0), LA_ERR_UNSUPPORTED),
 ])
 def test_prefill_validation(kw, status):
     st, _ = _ws(_desc(**kw))
@@ -322,6 +325,7 @@ def test_decode_validation():
     assert call(DecodeDesc(**ok), Z=None) == LA_ERR_NULL
     assert call(DecodeDesc(**ok), S=None) == LA_ERR_NULL
     assert call(DecodeDesc(**dict(ok, psi=2, n_psi=256))) == LA_ERR_NULL  # PRF without bank
+    assert call(DecodeDesc(**dict(ok, psi=3, n_psi=256, normalize=0)), prf=fake) == LA_ERR_UNSUPPORTED
     assert call(DecodeDesc(**ok), S=ctypes.c_void_p((1 << 20) + 8)) == LA_ERR_ALIGN
     assert lib.lin_attn_decode_step(None, fake, fake, fake, None, None, fake, fake, fake, None) == LA_ERR_NULL
 

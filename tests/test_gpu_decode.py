@@ -96,14 +96,40 @@ def test_decode_prf(psi, q_mult):
     _run_steps(w, S, Z, steps, 4, prf=prf)
 
 
-def test_decode_full_size_sampled_steps():
-    """32 streams x 64 heads, state from the 4096-token prefix, 16 consecutive steps, every output."""
+def test_decode_full_size_all_steps():
+    """The decode workload as configured: 32 streams x 64 heads, the state of the seeded
+    4096-token prefix, all 256 consecutive steps. Every step's output and the final state and
+    normaliser against the oracle carried over the same 256 steps."""
     w = workloads.DECODE_32x64
-    announce("decode full size (oracle prefix state)")
+    announce("decode full size: 256 steps from the oracle's prefix state")
     prefix = inputs.make_decode_prefix(w)
     S, Z = _state_from_prefix(w, prefix)
-    steps = inputs.make_decode_steps(w, steps=16)
-    _run_steps(w, S, Z, steps, 16)
+    steps = inputs.make_decode_steps(w)
+    assert w.steps == 256 and steps["q"].shape[0] == 256
+    rel, mx = _run_steps(w, S, Z, steps, w.steps)
+    print(f"[parity] decode_32x64 worst step over 256: rel_l2={rel:.3e} max_abs={mx:.3e}", flush=True)
+
+
+def test_decode_prefix_state_from_prefill():
+    """The decode workload's starting state built on the GPU (a prefill of the 4096-token
+    prefix with zero queries, final state only), against the oracle's state after the prefix.
+    The state has no fixed scale (Z sums about a thousand features), so max-abs is taken after
+    scaling by the largest reference magnitude; rel-L2 is unscaled."""
+    w = workloads.DECODE_32x64
+    announce("decode prefix state from GPU prefill")
+    prefix = inputs.make_decode_prefix(w)
+    S, Z = _state_from_prefix(w, prefix)
+    k, v = prefix["k"].to(DEV), prefix["v"].to(DEV)
+    Sg = torch.empty((w.N, w.H, w.n_psi, w.d_v), dtype=torch.float32, device=DEV)
+    Zg = torch.empty((w.N, w.H, w.n_psi), dtype=torch.float32, device=DEV)
+    binding.lin_attn_prefill(torch.zeros_like(k), k, v, psi=w.psi, chunk=64, normalize=w.normalize, eps=w.eps,
+                             gamma=[w.gamma] * w.H, final_S=Sg, final_Z=Zg)
+    torch.cuda.synchronize()
+    sS, sZ = float(np.abs(S).max()), float(np.abs(Z).max())
+    assert_close(Sg.cpu().reshape(-1, w.n_psi, w.d_v).numpy() / sS, S / sS, "bf16",
+                 f"prefix state S (scaled by max |S| = {sS:.3g})")
+    assert_close(Zg.cpu().reshape(-1, w.n_psi).numpy() / sZ, Z / sZ, "bf16",
+                 f"prefix normaliser Z (scaled by max |Z| = {sZ:.3g})")
 
 
 def test_prefill_to_decode_handoff():

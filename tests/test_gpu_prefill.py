@@ -1,8 +1,8 @@
 """GPU parity of lin_attn_prefill against the fp64 oracle (through the C ABI).
 
 Small cases span several chunks and segments and end in a ragged chunk; they are
-compared element by element. Full-size workloads are compared on sampled
-(batch, head) sequences computed by the oracle one by one. Edge cases: T = 1,
+compared element by element. Full-size workloads are compared on every output, with the
+oracle run over groups of (batch, head) sequences. Edge cases: T = 1,
 T = C - 1, C, C + 1, initial/final state hand-off, causality, determinism, and an
 integer-valued case whose every partial sum is exact in fp32 (bit-exact check).
 """
@@ -12,31 +12,17 @@ import numpy as np
 import pytest
 import torch
 
-import oracle
 from chunked_causal_linear_k1_amd import binding, inputs, workloads
 from chunked_causal_linear_k1_amd.workloads import PSI_ELU1, PSI_IDENTITY, PSI_PRF, PSI_PRF_QSHIFT, Workload
 
-from gpu_common import announce, assert_close
+from gpu_common import announce, assert_close, compare_all_blocks, oracle_blocks
 
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
 
 
-def _oracle_o(w: Workload, inp, heads=None, S0=None, Z0=None, want_state=False):
-    """Oracle outputs for the (b, h) blocks listed in heads (default all), as [nblk, T, d_v]."""
-    q, k, v = inp["q"].cpu(), inp["k"].cpu(), inp["v"].cpu()
-    BH = w.B * w.H
-    q, k, v = q.reshape(BH, w.T, -1), k.reshape(BH, w.T, -1), v.reshape(BH, w.T, -1)
-    idx = list(range(BH)) if heads is None else list(heads)
-    qs, ks, vs = q[idx].contiguous(), k[idx].contiguous(), v[idx].contiguous()
-    g = inp["gamma"]
-    gam = None if g is None else [float(g[b % w.H]) for b in idx]
-    prf = inp.get("prf_w")
-    return oracle.prefill(qs, ks, vs, w.psi, n_psi=w.n_psi, prf_w=None if prf is None else prf.cpu(),
-                          w_head=[b % w.H for b in idx] if prf is not None else None, gamma=gam,
-                          normalize=w.normalize, eps=float(np.float32(w.eps)), S0=S0, Z0=Z0,
-                          want_state=want_state)
+_oracle_o = oracle_blocks
 
 
 def _to_dev(inp):
@@ -254,24 +240,22 @@ def test_chunk_size_invariance():
     assert_close(o64, o32, "bf16", "C=64 vs C=32")
 
 
-def _full_size(w: Workload, heads):
-    announce(f"prefill full-size {w.name} sampled heads {heads}")
+def _full_size(w: Workload):
+    """Every output of a full-size workload, in the launch configuration the benchmark times
+    (inputs drawn on the GPU, default layout, fp32 output), against the oracle."""
+    announce(f"prefill full-size {w.name}, all {w.B * w.H} (batch, head) blocks")
     inp = inputs.make_prefill_inputs(w, device=DEV)
     o = binding.prefill_workload(w, inp)
     torch.cuda.synchronize()
-    o_sel = o.reshape(w.B * w.H, w.T, w.d_v)[list(heads)].cpu().numpy()
-    del o
-    ref = _oracle_o(w, inp, heads=heads)
-    assert_close(o_sel, ref, w.dtype, f"{w.name} heads {heads}")
+    compare_all_blocks(w, o, inp, w.name)
 
 
-def test_full_prefill_8k_elu1_sampled():
-    _full_size(workloads.PREFILL_8K, heads=[0, 17, 38, 63])
+def test_full_prefill_8k_elu1():
+    _full_size(workloads.PREFILL_8K)
 
 
-def test_full_retnet_128k_sampled():
-    # the fastest-decaying head, the slowest, and two in between
-    _full_size(workloads.RETNET_128K, heads=[0, 21, 42, 63])
+def test_full_retnet_128k():
+    _full_size(workloads.RETNET_128K)
 
 
 def test_context_parallel_share_128k():
@@ -362,7 +346,6 @@ PRF_QSHIFT = [
     # name, T, n_psi, normalize, decay, query multiplier
     ("qshift256", 450, 256, 1, "none", 1.0),
     ("qshift128_decay", 333, 128, 1, "const:0.99", 1.0),
-    ("qshift256_nonorm_spread", 300, 256, 0, "retnet_spread", 1.0),
     # queries 8x larger: unshifted log-features near -300 underflow in fp32, shifted ones peak at 0
     ("qshift256_large_queries", 400, 256, 1, "none", 8.0),
     ("qshift128_large_queries_decay", 200, 128, 1, "const:0.98", 8.0),
@@ -380,12 +363,17 @@ def test_prf_qshift(case):
     inp = inputs.make_prefill_inputs(w, device="cpu")
     inp["q"] = (inp["q"].float() * q_mult).to(torch.bfloat16)  # a power of two: exact
     o = _run(w, inp).cpu().reshape(B * H, T, 128).numpy()
-    ref = _oracle_o(w, inp)
-    if normalize:
-        assert_close(o, ref, "bf16", name)
-    else:
-        scale = float(np.abs(ref).max())
-        assert_close(o / scale, ref / scale, "bf16", f"{name} (scaled by max |o| = {scale:.3g})")
+    assert_close(o, _oracle_o(w, inp), "bf16", name)
+
+
+def test_prf_qshift_without_denominator_is_refused():
+    """The shift cancels only against the denominator, so normalize = 0 is refused before launch."""
+    w = Workload(name="qshift_nonorm", B=1, H=2, T=64, d_k=128, d_v=128, n_psi=256, chunk=64, psi=PSI_PRF_QSHIFT,
+                 normalize=0, eps=1e-6, dtype="bf16", seed=19, qk_scale=128 ** -0.25, v_scale=1.0)
+    inp = inputs.make_prefill_inputs(w, device="cpu")
+    with pytest.raises(binding.LinAttnError) as e:
+        _run(w, inp)
+    assert e.value.status == binding.LA_ERR_UNSUPPORTED
 
 
 @pytest.mark.parametrize("psi", [PSI_PRF, PSI_PRF_QSHIFT])
@@ -451,8 +439,13 @@ def test_prf_initial_and_final_state():
                  "prf final Z (scaled to max 1)")
 
 
-def test_full_prf_4k_sampled():
-    _full_size(workloads.PRF_4K, heads=[0, 37, 81, 127])
+def test_full_prf_4k():
+    _full_size(workloads.PRF_4K)
+
+
+def test_full_prf_4k_qshift():
+    """The PRF workload with the query-row shift, every output."""
+    _full_size(workloads.PRF_4K.with_(name="prf256_4k_qshift", psi=PSI_PRF_QSHIFT))
 
 
 def test_max_decay_heads():

@@ -256,6 +256,21 @@ def test_exact_elu1_integer_features():
     np.testing.assert_array_equal(o[0], chunked.chunked(qa, ka, va, 1, 16, 1.0, 1, eps=0.5))
 
 
+@pytest.mark.parametrize("psi", ["prf", "prf_qshift"])
+def test_chunked_prf_matches_recurrence(psi):
+    """The chunked statement with random features, including the query-row shift (keys take
+    no shift: only the query row's largest log-feature is subtracted), against the recurrence,
+    with decay, a denominator and a ragged last chunk."""
+    T, d_k, d_v, m, C = 45, 6, 5, 12, 8
+    q, k = _rand((1, T, d_k), 31, 1.2), _rand((1, T, d_k), 32, 1.2)
+    v = _rand((1, T, d_v), 33)
+    w = _rand((m, d_k), 34)
+    o = oracle.prefill(q, k, v, PSI[psi], n_psi=m, prf_w=w[None], gamma=[0.9], normalize=1, eps=1e-3)[0]
+    oc = chunked.chunked(oracle.as_f64(q[0]), oracle.as_f64(k[0]), oracle.as_f64(v[0]), PSI[psi], C, 0.9, 1,
+                         eps=1e-3, w=oracle.as_f64(w))
+    np.testing.assert_allclose(oc, o, rtol=1e-11, atol=1e-11 * np.abs(o).max())
+
+
 @pytest.mark.parametrize("n_chunks", [1, 2, 3, 5, 8, 16, 33, 128, 1024])
 def test_scan_round_counts(n_chunks):
     """Hillis-Steele takes ceil(log2 N_C) rounds ("Log-Depth Chunked Linear-Attention
