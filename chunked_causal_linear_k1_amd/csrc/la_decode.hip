@@ -10,7 +10,8 @@
 // replaced, row by row, by alpha[p] = exp(log_gate[p]).
 //
 // The step is a pure stream over the fp32 state (n_psi*d_v*4 bytes read and written
-// per head). One workgroup per (stream, head): psi(k), psi(q) go to LDS, then every
+// per head). One workgroup per (stream, head). In the general kernel (random features,
+// whose feature map is a GEMV with the bank) psi(k), psi(q) go to LDS, then every
 // thread owns a 4-column slice of the value axis and a strided set of state rows,
 // reads and writes its rows with 16-byte accesses (a wave covers whole contiguous
 // rows), and accumulates its share of psi(q)^T S in registers; the row-group
@@ -21,7 +22,8 @@
 namespace la {
 namespace {
 
-constexpr int kDecThreads = 256;
+constexpr int kDecThreads = 256;   // general kernel
+constexpr int kElemThreads = 512;  // streaming kernel (elementwise features)
 constexpr int kMaxFeat = 256;
 constexpr int kMaxDv = 128;
 
@@ -127,6 +129,115 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeParams p) {
   }
 }
 
+// The step for identity or elu+1 features with d_k == d_v == n_psi == D (64 or 128): the
+// feature maps are elementwise, so the prologue is one global load per feature and one LDS
+// hand-off, and the stream over the state dominates. Thread t owns the 4-column group
+// cg = t % (D/4) and the rows rg + RG*i (rg = t / (D/4)); a wave covers 64 / (D/4) whole
+// consecutive rows per 16-byte access. All of a thread's state rows are loaded before the
+// prologue, so the whole state slice is in flight while the features are formed; the
+// prologue's barrier waits for LDS only. The state is read once and written once per step,
+// with nothing to reuse it before the next step, so both accesses are non-temporal (they do
+// not displace other data in the caches): with 512 threads per (stream, head) this ran at
+// 21.3k steps/s on 32 x 64 heads of d = 128 with the state rotating over four copies, against
+// 17.6k with ordinary accesses and 256 threads. Row-group partials of psi(q)^T S meet by lane
+// shuffles within a wave and through LDS across the waves, in a fixed order.
+template <int D, bool ELU, bool NORM, bool F32IN, bool GATED>
+__global__ __launch_bounds__(kElemThreads) void k_decode_elem(DecodeParams p) {
+  constexpr int CG = D / 4, RG = kElemThreads / CG, RPT = D / RG, NWV = kElemThreads / 64;
+  static_assert(2 * D <= kElemThreads && RPT * RG == D, "decode tiling");
+  __shared__ float sF[2 * D];   // psi(k) [0, D), psi(q) [D, 2D)
+  __shared__ float sA[D];       // per-row decay (gated: exp(log_gate))
+  __shared__ float sNum[NWV][D];
+  __shared__ float sDen[NWV];
+  const int b = blockIdx.x, head = b % p.H, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int cg = tid % CG, rg = tid / CG;
+  float* Sb = p.S + (size_t)b * D * D;
+
+  // the state slice first: RPT independent 16-byte loads per thread
+  f32x4 s[RPT];
+#pragma unroll
+  for (int i = 0; i < RPT; ++i)
+    s[i] = __builtin_nontemporal_load((const f32x4*)(Sb + (size_t)(rg + RG * i) * D + 4 * cg));
+  float z = 0.f;
+  if (NORM && tid < D) z = p.Z[(size_t)b * D + tid];
+  f32x4 v4;
+  if (F32IN) {
+    v4 = *(const f32x4*)((const float*)p.v + (size_t)b * D + 4 * cg);
+  } else {
+    const uint2 raw = *(const uint2*)((const uint16_t*)p.v + (size_t)b * D + 4 * cg);
+    v4 = f32x4{__uint_as_float(raw.x << 16), __uint_as_float(raw.x & 0xffff0000u), __uint_as_float(raw.y << 16),
+               __uint_as_float(raw.y & 0xffff0000u)};
+  }
+  // features: threads [0, D) take psi(k), [D, 2D) psi(q)
+  if (tid < 2 * D) {
+    const int f = tid % D;
+    const void* x = tid < D ? p.k : p.q;
+    const float xv = F32IN ? ((const float*)x)[(size_t)b * D + f] : bf16_bits_to_f32(((const uint16_t*)x)[(size_t)b * D + f]);
+    sF[tid] = ELU ? (xv > 0.f ? xv + 1.f : expf(xv)) : xv;
+  }
+  const float gam = p.has_decay ? p.gamma[head] : 1.f;
+  if (tid < D) sA[tid] = GATED ? expf(p.log_gate[(size_t)b * D + tid]) : gam;
+  lds_barrier();
+
+  // normaliser: Z <- a Z + psi(k), den = psi(q) . Z + eps (waves holding the first D threads)
+  if (NORM && tid < D) {
+    z = sA[tid] * z + sF[tid];
+    p.Z[(size_t)b * D + tid] = z;
+    float part = sF[D + tid] * z;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off);
+    if (lane == 0) sDen[w] = part;
+  }
+  // state rows: S <- a S + psi(k) v^T, then psi(q)^T S
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int row = rg + RG * i;
+    const f32x4 x = sA[row] * s[i] + sF[row] * v4;
+    __builtin_nontemporal_store(x, (f32x4*)(Sb + (size_t)row * D + 4 * cg));
+    acc += sF[D + row] * x;
+  }
+  // row groups within the wave (lanes CG apart), then across the waves
+#pragma unroll
+  for (int off = CG; off < 64; off <<= 1)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] += __shfl_xor(acc[j], off);
+  if (lane < CG) *(f32x4*)&sNum[w][4 * cg] = acc;
+  lds_barrier();
+  if (tid < D) {
+    float num = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < NWV; ++ww) num += sNum[ww][tid];
+    if (NORM) {
+      float den = p.eps;
+#pragma unroll
+      for (int ww = 0; ww < (D + 63) / 64; ++ww) den += sDen[ww];
+      num /= den;
+    }
+    p.o[(size_t)b * D + tid] = num;
+  }
+}
+
+template <int D, bool ELU, bool NORM>
+hipError_t launch_elem(const DecodeParams& p, hipStream_t s) {
+  const dim3 g(p.N * p.H), t(kElemThreads);
+  if (p.in_f32) {
+    if (p.log_gate) hipLaunchKernelGGL((k_decode_elem<D, ELU, NORM, true, true>), g, t, 0, s, p);
+    else hipLaunchKernelGGL((k_decode_elem<D, ELU, NORM, true, false>), g, t, 0, s, p);
+  } else {
+    if (p.log_gate) hipLaunchKernelGGL((k_decode_elem<D, ELU, NORM, false, true>), g, t, 0, s, p);
+    else hipLaunchKernelGGL((k_decode_elem<D, ELU, NORM, false, false>), g, t, 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_elem_d(const DecodeParams& p, hipStream_t s) {
+  const bool elu = p.psi == LA_PSI_ELU1;
+  if (elu) return p.normalize ? launch_elem<D, true, true>(p, s) : launch_elem<D, true, false>(p, s);
+  return p.normalize ? launch_elem<D, false, true>(p, s) : launch_elem<D, false, false>(p, s);
+}
+
 }  // namespace
 
 bool decode_supported(int d_k, int d_v, int n_psi, int psi) {
@@ -137,6 +248,12 @@ bool decode_supported(int d_k, int d_v, int n_psi, int psi) {
 }
 
 hipError_t launch_decode_step(const DecodeParams& p, hipStream_t s) {
+  // elementwise features at equal widths take the streaming kernel; random features (a
+  // feature GEMV per token) the general one
+  if (!is_prf(p.psi) && p.d_k == p.d_v && p.n_psi == p.d_k) {
+    if (p.d_k == 128) return launch_elem_d<128>(p, s);
+    if (p.d_k == 64) return launch_elem_d<64>(p, s);
+  }
   hipLaunchKernelGGL(k_decode, dim3(p.N * p.H), dim3(kDecThreads), 0, s, p);
   return hipGetLastError();
 }
