@@ -29,7 +29,8 @@ EXPORTED = ("lin_attn_prefill_workspace_size", "lin_attn_prefill", "lin_attn_pre
             "lin_attn_prefill_gated_workspace_size", "lin_attn_prefill_backward",
             "lin_attn_prefill_backward_workspace_size", "lin_attn_prefill_backward_varlen",
             "lin_attn_prefill_backward_varlen_workspace_size", "lin_attn_decode_step", "lin_attn_decode_step_gated",
-            "lin_attn_status_string", "lin_attn_version")
+            "lin_attn_status_string", "lin_attn_version", "lin_attn_prefill_noalloc")
+NOALLOC_SCRATCH_BYTES = 64 << 20  # LA_NOALLOC_SCRATCH_BYTES
 
 
 class PrefillDesc(ctypes.Structure):
@@ -99,6 +100,9 @@ def load() -> ctypes.CDLL:
         lib.lin_attn_decode_step_gated.argtypes = [ctypes.POINTER(DecodeDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.lin_attn_decode_step.restype = ctypes.c_int
         lib.lin_attn_decode_step.argtypes = [ctypes.POINTER(DecodeDesc), vp, vp, vp, fp, vp, vp, vp, vp, vp]
+        lib.lin_attn_prefill_noalloc.restype = ctypes.c_int
+        lib.lin_attn_prefill_noalloc.argtypes = [ctypes.POINTER(PrefillDesc), vp, vp, vp, fp, vp, vp, vp, vp, vp, vp,
+                                                 vp]
         lib.lin_attn_status_string.restype = ctypes.c_char_p
         lib.lin_attn_status_string.argtypes = [ctypes.c_int]
         lib.lin_attn_version.restype = ctypes.c_char_p
@@ -207,6 +211,39 @@ def lin_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, psi: 
         st = load().lin_attn_prefill_profiled(*args, ev)
     if st != LA_OK:
         raise LinAttnError(st, "lin_attn_prefill")
+    return o
+
+
+def lin_attn_prefill_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, psi: int, chunk: int,
+                             normalize: int = 1, eps: float = 1e-6, gamma: Optional[Sequence[float]] = None,
+                             prf_w: Optional[torch.Tensor] = None, init_S: Optional[torch.Tensor] = None,
+                             init_Z: Optional[torch.Tensor] = None, o: Optional[torch.Tensor] = None,
+                             final_S: Optional[torch.Tensor] = None, final_Z: Optional[torch.Tensor] = None,
+                             stream=None, layout: str = "bhtd") -> torch.Tensor:
+    """lin_attn_prefill through lin_attn_prefill_noalloc: no workspace; the library's per-device
+    scratch holds the summary records. o must be given by callers that allocate nothing."""
+    if layout == "bhtd":
+        B, H, T, d_k = q.shape
+        lay = LA_LAYOUT_BHTD
+    elif layout == "bthd":
+        B, T, H, d_k = q.shape
+        lay = LA_LAYOUT_BTHD
+    else:
+        raise ValueError(f"layout must be 'bhtd' or 'bthd', not {layout!r}")
+    d_v = v.shape[-1]
+    n_psi = prf_w.shape[1] if prf_w is not None else d_k
+    for t in (q, k, v):
+        if not t.is_contiguous():
+            raise ValueError(f"q, k, v must be contiguous ({layout})")
+    if o is None:
+        shape = (B, H, T, d_v) if lay == LA_LAYOUT_BHTD else (B, T, H, d_v)
+        o = torch.empty(shape, dtype=torch.float32, device=q.device)
+    desc = prefill_desc(B, H, T, d_k, d_v, n_psi, chunk, psi, normalize, eps, _dtype_code(q), _dtype_code(o), lay)
+    st = load().lin_attn_prefill_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _gamma_array(gamma, H),
+                                         _ptr(prf_w), _ptr(init_S), _ptr(init_Z), _ptr(o), _ptr(final_S),
+                                         _ptr(final_Z), _stream(stream))
+    if st != LA_OK:
+        raise LinAttnError(st, "lin_attn_prefill_noalloc")
     return o
 
 

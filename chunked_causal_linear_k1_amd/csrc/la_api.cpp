@@ -98,7 +98,12 @@ struct Plan {
 // the kernels: 64 tokens, or the gated path's 32-token chunks; at least kMinSubTokens each),
 // so that the pass takes a fraction of a segment's time; the scan then runs over the
 // sub-segment records and each segment reads the record at its start.
-Plan make_plan(const la_prefill_desc* d, long long total_tokens = -1, bool gated = false, bool sub = false) {
+//
+// ws_cap (fixed-length batches, nonzero only for lin_attn_prefill_noalloc): when the records
+// exceed it, the plan takes fewer, longer segments, one record each, at most as many per
+// sequence as fit; if not even one record per sequence fits, ws_bytes stays above the cap.
+Plan make_plan(const la_prefill_desc* d, long long total_tokens = -1, bool gated = false, bool sub = false,
+               size_t ws_cap = 0) {
   Plan pl;
   const long long BH = (long long)d->B * d->H;
   pl.n_chunks = (int)((d->T + (long long)d->chunk - 1) / d->chunk);
@@ -140,6 +145,17 @@ Plan make_plan(const la_prefill_desc* d, long long total_tokens = -1, bool gated
   // one record per segment or sub-segment: S, Z (and, gated, the segment's per-row decay)
   const size_t E = (size_t)d->n_psi * d->d_v + (gated ? 2 : 1) * (size_t)d->n_psi;
   pl.ws_bytes = (size_t)BH * pl.n_rec * E * sizeof(float);
+  if (ws_cap && total_tokens < 0 && pl.ws_bytes > ws_cap) {
+    const long long max_rec = (long long)(ws_cap / ((size_t)BH * E * sizeof(float)));
+    if (max_rec >= 1) {
+      pl.rec_per_seg = 1;
+      pl.seg_chunks = (int)((pl.n_chunks + max_rec - 1) / max_rec);
+      if (!gated && d->in_dtype == LA_BF16 && d->chunk == 32 && (pl.seg_chunks & 1)) pl.seg_chunks += 1;
+      pl.n_seg = (pl.n_chunks + pl.seg_chunks - 1) / pl.seg_chunks;
+      pl.n_rec = pl.n_seg;
+      pl.ws_bytes = (size_t)BH * pl.n_rec * E * sizeof(float);
+    }
+  }
   return pl;
 }
 
@@ -232,7 +248,7 @@ la_status prefill_impl(const la_prefill_desc* d, const int32_t* cu_seqlens, int3
                        const void* k, const void* v, const float* gamma, const void* prf_w, const float* init_S,
                        const float* init_Z, void* o, float* final_S, float* final_Z, void* workspace,
                        size_t workspace_bytes, hipStream_t stream, hipEvent_t* events,
-                       const float* log_gate = nullptr) {
+                       const float* log_gate = nullptr, size_t ws_cap = 0) {
   const bool gated = log_gate != nullptr;
   la_status st = validate_prefill_desc(d, gated);
   if (st != LA_OK) return st;
@@ -251,7 +267,7 @@ la_status prefill_impl(const la_prefill_desc* d, const int32_t* cu_seqlens, int3
   if (st != LA_OK) return st;
   if (gated && !aligned16(log_gate)) return LA_ERR_ALIGN;
   const bool sub = !cu_seqlens;
-  const Plan pl = make_plan(d, cu_seqlens ? (long long)total_tokens : -1LL, gated, sub);
+  const Plan pl = make_plan(d, cu_seqlens ? (long long)total_tokens : -1LL, gated, sub, ws_cap);
   if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes)) return LA_ERR_WORKSPACE;
 
   PrefillParams p;
@@ -321,6 +337,26 @@ la_status prefill_impl(const la_prefill_desc* d, const int32_t* cu_seqlens, int3
 }
 
 }  // namespace
+
+namespace la {
+
+// The checks lin_attn_prefill makes on the host that do not touch pointers, plus the segment
+// plan under a workspace cap: LA_ERR_WORKSPACE when not even one record per sequence fits.
+la_status prefill_capped_check(const la_prefill_desc* d, size_t ws_cap) {
+  const la_status st = validate_prefill_desc(d);
+  if (st != LA_OK) return st;
+  return make_plan(d, -1, false, true, ws_cap).ws_bytes > ws_cap ? LA_ERR_WORKSPACE : LA_OK;
+}
+
+// lin_attn_prefill with a workspace of ws_cap bytes and the plan fitted to it.
+la_status prefill_capped(const la_prefill_desc* d, const void* q, const void* k, const void* v, const float* gamma,
+                         const void* prf_w, const float* init_S, const float* init_Z, void* o, float* final_S,
+                         float* final_Z, void* workspace, size_t ws_cap, hipStream_t stream) {
+  return prefill_impl(d, nullptr, 0, q, k, v, gamma, prf_w, init_S, init_Z, o, final_S, final_Z, workspace, ws_cap,
+                      stream, nullptr, nullptr, ws_cap);
+}
+
+}  // namespace la
 
 extern "C" {
 

@@ -159,6 +159,13 @@ hipError_t launch_prefill_gated(const PrefillParams& p, hipStream_t s, bool out)
 bool prefill_backward_supported(int C, int d_k, int d_v, int n_psi, int psi);
 hipError_t launch_prefill_backward(const BackwardParams& p, hipStream_t s, bool key_sweep);
 
+// lin_attn_prefill on a caller-sized workspace whose segment plan is fitted to it (la_api.cpp):
+// the host-only checks, then the call itself.
+la_status prefill_capped_check(const la_prefill_desc* d, size_t ws_cap);
+la_status prefill_capped(const la_prefill_desc* d, const void* q, const void* k, const void* v, const float* gamma,
+                         const void* prf_w, const float* init_S, const float* init_Z, void* o, float* final_S,
+                         float* final_Z, void* workspace, size_t ws_cap, hipStream_t stream);
+
 bool decode_supported(int d_k, int d_v, int n_psi, int psi);
 hipError_t launch_decode_step(const DecodeParams& p, hipStream_t s);
 

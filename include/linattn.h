@@ -205,6 +205,30 @@ la_status lin_attn_prefill_profiled(const la_prefill_desc* d, const void* q, con
                                     size_t workspace_bytes, hipStream_t stream,
                                     hipEvent_t* events);
 
+/* Per-device scratch of lin_attn_prefill_noalloc (its summary records), in bytes. */
+#define LA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * lin_attn_prefill for callers that cannot allocate device memory: code under HIP graph
+ * capture, serving loops and harnesses that forbid hipMalloc. Same arguments, results and
+ * errors as lin_attn_prefill minus the workspace, which is replaced by a library-owned scratch
+ * array of LA_NOALLOC_SCRATCH_BYTES on each device (reserved when the library's code object
+ * is loaded on that device, held until the process ends). The call allocates nothing.
+ *   - When the usual segment plan's summary records exceed the scratch, the call uses fewer,
+ *     longer segments (the same function; results agree with lin_attn_prefill's to rounding).
+ *     When not even one record per sequence fits -- B * H * (n_psi * d_v + n_psi) * 4 bytes
+ *     above LA_NOALLOC_SCRATCH_BYTES -- it returns LA_ERR_WORKSPACE before touching the device.
+ *   - Every call on a device uses that device's one array and leaves its contents behind;
+ *     nothing in it needs to start at zero. Calls that overlap in time on one device (other
+ *     streams or threads) race on the array: the caller serialises them.
+ *   - The first call on each device looks the array's address up (hipGetSymbolAddress):
+ *     LA_ERR_HIP if that fails. Fixed-length batches only (no varlen or gated form).
+ */
+la_status lin_attn_prefill_noalloc(const la_prefill_desc* d, const void* q, const void* k, const void* v,
+                                   const float* gamma, const void* prf_w, const float* init_S,
+                                   const float* init_Z, void* o, float* final_S, float* final_Z,
+                                   hipStream_t stream);
+
 /*
  * Chunkwise causal linear attention with data-dependent forget gates ("Linear Attention
  * and Retentive Networks", Data-Dependent Gating Mechanism: S_t = G_t . S_{t-1} + k_t^T v_t
