@@ -194,7 +194,7 @@ def bench_backward(w: workloads.Workload, steps: int, warmup: int):
     ws = torch.empty(binding.backward_workspace_size(desc), dtype=torch.uint8, device="cuda")
     grads = [torch.empty((w.B, w.H, w.T, d), dtype=torch.float32, device="cuda") for d in (w.d_k, w.d_k, w.d_v)]
     kw = dict(psi=w.psi, chunk=w.chunk, normalize=w.normalize, eps=w.eps, gamma=None if g is None else list(g),
-              dq=grads[0], dk=grads[1], dv=grads[2], workspace=ws)
+              prf_w=inp["prf_w"], dq=grads[0], dk=grads[1], dv=grads[2], workspace=ws)
     for _ in range(warmup):
         binding.lin_attn_prefill_backward(inp["q"], inp["k"], inp["v"], dout, **kw)
     torch.cuda.synchronize()
@@ -564,7 +564,8 @@ def main():
                                     "algorithmic_tflops": round(tf, 1), "flop_per_token_head": flop}
         # backward: compulsory bytes per token-head (q, k, v bf16 and dout fp32 read; dq, dk, dv fp32 written)
         bwd_bytes = 3 * 128 * 2 + 128 * 4 + 3 * 128 * 4
-        for key, bw in (("backward_8k", workloads.PREFILL_8K), ("backward_128k", workloads.RETNET_128K)):
+        for key, bw in (("backward_8k", workloads.PREFILL_8K), ("backward_128k", workloads.RETNET_128K),
+                        ("backward_prf_4k", workloads.PRF_4K)):
             pb = bench_backward(bw, args.steps, args.warmup)
             ab = bwd_bytes * pb["units"] / (pb["ms_per_step"] * 1e-3) / 1e9
             line[key] = {"workload": bw.name, "token_heads_per_s": round(pb["token_heads_per_s"], 1),

@@ -86,13 +86,14 @@ def load() -> ctypes.CDLL:
                                                               ctypes.POINTER(ctypes.c_size_t)]
         lib.lin_attn_prefill_backward.restype = ctypes.c_int
         lib.lin_attn_prefill_backward.argtypes = [ctypes.POINTER(PrefillDesc), vp, vp, vp, fp, vp, vp, vp, vp, vp,
-                                                  vp, vp, vp, vp, ctypes.c_size_t, vp]
+                                                  vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         lib.lin_attn_prefill_backward_workspace_size.restype = ctypes.c_int
         lib.lin_attn_prefill_backward_workspace_size.argtypes = [ctypes.POINTER(PrefillDesc),
                                                                  ctypes.POINTER(ctypes.c_size_t)]
         lib.lin_attn_prefill_backward_varlen.restype = ctypes.c_int
         lib.lin_attn_prefill_backward_varlen.argtypes = [ctypes.POINTER(PrefillDesc), vp, ctypes.c_int32, vp, vp, vp,
-                                                         fp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+                                                         fp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                                                         vp]
         lib.lin_attn_prefill_backward_varlen_workspace_size.restype = ctypes.c_int
         lib.lin_attn_prefill_backward_varlen_workspace_size.argtypes = [ctypes.POINTER(PrefillDesc), ctypes.c_int32,
                                                                         ctypes.POINTER(ctypes.c_size_t)]
@@ -294,7 +295,8 @@ def backward_workspace_size(desc: PrefillDesc) -> int:
 
 def lin_attn_prefill_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch.Tensor, *, psi: int,
                               chunk: int, normalize: int = 1, eps: float = 1e-6,
-                              gamma: Optional[Sequence[float]] = None, init_S: Optional[torch.Tensor] = None,
+                              gamma: Optional[Sequence[float]] = None, prf_w: Optional[torch.Tensor] = None,
+                              init_S: Optional[torch.Tensor] = None,
                               init_Z: Optional[torch.Tensor] = None, dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
                               dv: Optional[torch.Tensor] = None, dinit_S: Optional[torch.Tensor] = None,
                               dinit_Z: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
@@ -302,7 +304,8 @@ def lin_attn_prefill_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     """(dq, dk, dv) of L = sum dout . o for lin_attn_prefill with the same arguments (C ABI call).
 
     dout is float32 or bfloat16, laid out like o. Gradients are float32 in the layouts of q, k,
-    v; dinit_S / dinit_Z are written when given."""
+    v; dinit_S / dinit_Z are written when given. prf_w: the random-feature bank (its n_psi sets
+    the state width)."""
     if layout == "bhtd":
         B, H, T, d_k = q.shape
         lay = LA_LAYOUT_BHTD
@@ -318,13 +321,14 @@ def lin_attn_prefill_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     dq = torch.empty(q.shape, dtype=torch.float32, device=q.device) if dq is None else dq
     dk = torch.empty(k.shape, dtype=torch.float32, device=q.device) if dk is None else dk
     dv = torch.empty(v.shape, dtype=torch.float32, device=q.device) if dv is None else dv
-    desc = prefill_desc(B, H, T, d_k, d_v, d_k, chunk, psi, normalize, eps, _dtype_code(q), _dtype_code(dout), lay)
+    n_psi = prf_w.shape[1] if prf_w is not None else d_k
+    desc = prefill_desc(B, H, T, d_k, d_v, n_psi, chunk, psi, normalize, eps, _dtype_code(q), _dtype_code(dout), lay)
     ws_bytes = backward_workspace_size(desc)
     if workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     st = load().lin_attn_prefill_backward(
-        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _gamma_array(gamma, H), _ptr(init_S), _ptr(init_Z),
-        _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dinit_S), _ptr(dinit_Z), _ptr(workspace),
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _gamma_array(gamma, H), _ptr(prf_w), _ptr(init_S),
+        _ptr(init_Z), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dinit_S), _ptr(dinit_Z), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream))
     if st != LA_OK:
         raise LinAttnError(st, "lin_attn_prefill_backward")
@@ -368,7 +372,7 @@ def lin_attn_prefill_backward_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
     st = load().lin_attn_prefill_backward_varlen(
-        ctypes.byref(desc), _ptr(cu_seqlens), total, _ptr(q), _ptr(k), _ptr(v), _gamma_array(gamma, H),
+        ctypes.byref(desc), _ptr(cu_seqlens), total, _ptr(q), _ptr(k), _ptr(v), _gamma_array(gamma, H), None,
         _ptr(init_S), _ptr(init_Z), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dinit_S), _ptr(dinit_Z),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
     if st != LA_OK:

@@ -177,7 +177,7 @@ const char* lin_attn_status_string(la_status s) {
   return "unknown status";
 }
 
-const char* lin_attn_version(void) { return "0.3.0"; }
+const char* lin_attn_version(void) { return "0.4.0"; }
 
 la_status lin_attn_prefill_workspace_size(const la_prefill_desc* d, size_t* bytes) {
   if (!bytes) return LA_ERR_NULL;
@@ -197,17 +197,45 @@ la_status lin_attn_prefill_gated_workspace_size(const la_prefill_desc* d, size_t
 
 // The backward pass: the forward segment prefixes, the adjoint segment records (same size) and,
 // with a denominator, two floats per token (1/den and dden).
-la_status validate_backward_desc(const la_prefill_desc* d) {
+// varlen: the packed form. Random features have a backward for fixed-length batches only: it
+// keeps one record per 64-token step and sequence, which for a packed batch would scale with the
+// longest sequence times the batch.
+la_status validate_backward_desc(const la_prefill_desc* d, bool varlen = false) {
   const la_status st = validate_prefill_desc(d);
   if (st != LA_OK) return st;
   if (d->in_dtype != LA_BF16) return LA_ERR_UNSUPPORTED;
+  if (la::is_prf(d->psi)) {
+    // one workgroup per 64-token step on the grid's y extent
+    if ((d->T + 63) / 64 > 65535) return LA_ERR_UNSUPPORTED;
+    return !varlen && la::prefill_backward_prf_supported(d->chunk, d->d_k, d->d_v, d->n_psi) ? LA_OK
+                                                                                             : LA_ERR_UNSUPPORTED;
+  }
   return la::prefill_backward_supported(d->chunk, d->d_k, d->d_v, d->n_psi, d->psi) ? LA_OK : LA_ERR_UNSUPPORTED;
 }
 
-// total_tokens < 0: a fixed-length batch; otherwise a packed batch of that many tokens.
+// Random features: one record per 64-token step (la_backward_prf.hip).
+constexpr int kPrfBwdStep = 64;
+Plan prf_backward_plan(const la_prefill_desc* d) {
+  Plan pl;
+  pl.n_chunks = (d->T + kPrfBwdStep - 1) / kPrfBwdStep;
+  pl.seg_chunks = 1;
+  pl.n_seg = pl.n_rec = pl.n_chunks;
+  pl.rec_per_seg = 1;
+  const size_t E = (size_t)d->n_psi * d->d_v + d->n_psi;
+  pl.ws_bytes = (size_t)d->B * d->H * pl.n_rec * E * sizeof(float);
+  return pl;
+}
+
+// total_tokens < 0: a fixed-length batch; otherwise a packed batch of that many tokens. Two
+// record regions (forward prefixes, adjoint states), 1/den and dden per token row with a
+// denominator, and for random features the transposed bank.
 size_t backward_ws_bytes(const la_prefill_desc* d, long long total_tokens = -1) {
   const long long rows = total_tokens < 0 ? (long long)d->B * d->T * d->H : total_tokens * d->H;
   const size_t tok = d->normalize ? (size_t)rows * 2 * sizeof(float) : 0;
+  if (la::is_prf(d->psi)) {
+    const size_t bank = ((size_t)d->H * d->n_psi * d->d_k * 2 + 15) & ~(size_t)15;
+    return 2 * prf_backward_plan(d).ws_bytes + tok + bank;
+  }
   return 2 * make_plan(d, total_tokens).ws_bytes + tok;
 }
 
@@ -222,7 +250,7 @@ la_status lin_attn_prefill_backward_workspace_size(const la_prefill_desc* d, siz
 la_status lin_attn_prefill_backward_varlen_workspace_size(const la_prefill_desc* d, int32_t total_tokens,
                                                           size_t* bytes) {
   if (!bytes) return LA_ERR_NULL;
-  const la_status st = validate_backward_desc(d);
+  const la_status st = validate_backward_desc(d, true);
   if (st != LA_OK) return st;
   if (total_tokens < 0) return LA_ERR_SHAPE;
   *bytes = backward_ws_bytes(d, total_tokens);
@@ -453,11 +481,14 @@ namespace {
 // Both backward entry points: fixed-length batches (cu_seqlens == nullptr) and packed
 // variable-length batches.
 la_status backward_impl(const la_prefill_desc* d, const int32_t* cu_seqlens, int32_t total_tokens, const void* q,
-                        const void* k, const void* v, const float* gamma, const float* init_S, const float* init_Z,
-                        const void* dout, float* dq, float* dk, float* dv, float* dinit_S, float* dinit_Z,
-                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  la_status st = validate_backward_desc(d);
+                        const void* k, const void* v, const float* gamma, const void* prf_w, const float* init_S,
+                        const float* init_Z, const void* dout, float* dq, float* dk, float* dv, float* dinit_S,
+                        float* dinit_Z, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  la_status st = validate_backward_desc(d, cu_seqlens != nullptr);
   if (st != LA_OK) return st;
+  const bool prf = la::is_prf(d->psi);
+  if (prf && !prf_w) return LA_ERR_NULL;
+  if (!aligned16(prf_w)) return LA_ERR_ALIGN;
   if (cu_seqlens) {
     if (d->layout != LA_LAYOUT_BTHD) return LA_ERR_VALUE;
     if (total_tokens < 0) return LA_ERR_SHAPE;
@@ -471,7 +502,7 @@ la_status backward_impl(const la_prefill_desc* d, const int32_t* cu_seqlens, int
   st = check_gamma(gamma, d->H);
   if (st != LA_OK) return st;
   const long long tt = cu_seqlens ? (long long)total_tokens : -1LL;
-  const Plan pl = make_plan(d, tt);
+  const Plan pl = prf ? prf_backward_plan(d) : make_plan(d, tt);
   const size_t need = backward_ws_bytes(d, tt);
   if (!workspace || workspace_bytes < need) return LA_ERR_WORKSPACE;
 
@@ -488,7 +519,10 @@ la_status backward_impl(const la_prefill_desc* d, const int32_t* cu_seqlens, int
   } else {
     p.tok_rows = 1; p.head_rows = d->T; p.seq_rows = (long long)d->H * d->T;
   }
-  p.d_k = d->d_k; p.d_v = d->d_v; p.n_psi = d->n_psi; p.C = d->chunk;
+  p.d_k = d->d_k; p.d_v = d->d_v; p.n_psi = d->n_psi;
+  // random features walk one 64-token step per segment (the same function for every chunk size)
+  p.C = prf ? kPrfBwdStep : d->chunk;
+  p.prf_w = prf_w;
   p.psi = d->psi; p.normalize = d->normalize; p.eps = d->eps;
   p.n_chunks = pl.n_chunks; p.seg_chunks = pl.seg_chunks; p.n_seg = pl.n_seg;
   p.n_rec = pl.n_seg; p.rec_per_seg = 1; p.sum_end = pl.n_chunks;
@@ -496,7 +530,11 @@ la_status backward_impl(const la_prefill_desc* d, const int32_t* cu_seqlens, int
   bp.dout = dout;
   bp.dq = dq; bp.dk = dk; bp.dv = dv;
   bp.rev = (float*)((char*)workspace + pl.ws_bytes);
+  const size_t tok_bytes = d->normalize ? (size_t)(cu_seqlens ? (long long)total_tokens * d->H
+                                                              : (long long)d->B * d->T * d->H) * 2 * sizeof(float)
+                                        : 0;
   bp.tok = d->normalize ? (float*)((char*)workspace + 2 * pl.ws_bytes) : nullptr;
+  bp.wt = prf ? (const uint16_t*)((char*)workspace + 2 * pl.ws_bytes + tok_bytes) : nullptr;
   bp.dout_bf16 = d->out_dtype == LA_BF16;
 
   ScanParams sp;
@@ -507,7 +545,7 @@ la_status backward_impl(const la_prefill_desc* d, const int32_t* cu_seqlens, int
   sp.cu_seqlens = cu_seqlens; sp.total = p.total;
   sp.BH = d->B * d->H; sp.H = d->H; sp.T = d->T;
   sp.n_psi = d->n_psi; sp.d_v = d->d_v;
-  sp.n_seg = pl.n_seg; sp.seg_len = pl.seg_chunks * d->chunk;
+  sp.n_seg = pl.n_seg; sp.seg_len = pl.seg_chunks * p.C;
   sp.has_decay = p.has_decay;
   memcpy(sp.log2g, p.log2g, sizeof sp.log2g);
   ScanParams rp = sp;  // the adjoint state: no initial element; its total is the initial state's gradient
@@ -517,6 +555,16 @@ la_status backward_impl(const la_prefill_desc* d, const int32_t* cu_seqlens, int
   rp.final_Z = d->normalize ? dinit_Z : nullptr;
   rp.reverse = 1;
 
+  if (prf) {
+    uint16_t* wt = const_cast<uint16_t*>(bp.wt);
+    hipError_t e = la::launch_bank_transpose(prf_w, wt, d->H, d->n_psi, stream);  // the bank, [d][p] per head
+    if (e == hipSuccess) e = la::launch_prefill_prf_bf16(p, stream, false);       // per-step forward summaries
+    if (e == hipSuccess) e = la::launch_segment_scan(sp, stream);                 // the state before each step
+    if (e == hipSuccess) e = la::launch_prefill_backward_prf(bp, stream, false);  // dq, per-step adjoint records
+    if (e == hipSuccess) e = la::launch_segment_scan(rp, stream);                 // the adjoint state after each step
+    if (e == hipSuccess) e = la::launch_prefill_backward_prf(bp, stream, true);   // dk, dv
+    return e == hipSuccess ? LA_OK : LA_ERR_HIP;
+  }
   hipError_t e = la::launch_prefill_bf16_summary(p, stream);            // forward segment summaries
   if (e == hipSuccess) e = la::launch_segment_scan(sp, stream);          // forward prefixes
   if (e == hipSuccess) e = la::launch_prefill_backward(bp, stream, false);  // query sweep: dq, adjoint summaries
@@ -530,20 +578,21 @@ la_status backward_impl(const la_prefill_desc* d, const int32_t* cu_seqlens, int
 extern "C" {
 
 la_status lin_attn_prefill_backward(const la_prefill_desc* d, const void* q, const void* k, const void* v,
-                                    const float* gamma, const float* init_S, const float* init_Z, const void* dout,
-                                    float* dq, float* dk, float* dv, float* dinit_S, float* dinit_Z,
-                                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  return backward_impl(d, nullptr, 0, q, k, v, gamma, init_S, init_Z, dout, dq, dk, dv, dinit_S, dinit_Z, workspace,
-                       workspace_bytes, stream);
+                                    const float* gamma, const void* prf_w, const float* init_S, const float* init_Z,
+                                    const void* dout, float* dq, float* dk, float* dv, float* dinit_S,
+                                    float* dinit_Z, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return backward_impl(d, nullptr, 0, q, k, v, gamma, prf_w, init_S, init_Z, dout, dq, dk, dv, dinit_S, dinit_Z,
+                       workspace, workspace_bytes, stream);
 }
 
 la_status lin_attn_prefill_backward_varlen(const la_prefill_desc* d, const int32_t* cu_seqlens, int32_t total_tokens,
                                            const void* q, const void* k, const void* v, const float* gamma,
-                                           const float* init_S, const float* init_Z, const void* dout, float* dq,
-                                           float* dk, float* dv, float* dinit_S, float* dinit_Z, void* workspace,
-                                           size_t workspace_bytes, hipStream_t stream) {
+                                           const void* prf_w, const float* init_S, const float* init_Z,
+                                           const void* dout, float* dq, float* dk, float* dv, float* dinit_S,
+                                           float* dinit_Z, void* workspace, size_t workspace_bytes,
+                                           hipStream_t stream) {
   if (!cu_seqlens) return LA_ERR_NULL;
-  return backward_impl(d, cu_seqlens, total_tokens, q, k, v, gamma, init_S, init_Z, dout, dq, dk, dv, dinit_S,
+  return backward_impl(d, cu_seqlens, total_tokens, q, k, v, gamma, prf_w, init_S, init_Z, dout, dq, dk, dv, dinit_S,
                        dinit_Z, workspace, workspace_bytes, stream);
 }
 

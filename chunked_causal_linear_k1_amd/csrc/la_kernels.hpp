@@ -83,6 +83,7 @@ struct BackwardParams {
   float* dv;             // fp32, rows like v
   float* rev;            // [BH, n_seg, E] segment summaries of the adjoint state, then their reverse prefixes
   float* tok;            // [rows, 2]: 1/den and dden per token row, rows as q's (normalize only)
+  const uint16_t* wt;    // random features: the bank transposed per head, [H][d_k][n_psi] bf16
   int dout_bf16;
 };
 
@@ -158,6 +159,13 @@ hipError_t launch_prefill_gated(const PrefillParams& p, hipStream_t s, bool out)
 
 bool prefill_backward_supported(int C, int d_k, int d_v, int n_psi, int psi);
 hipError_t launch_prefill_backward(const BackwardParams& p, hipStream_t s, bool key_sweep);
+
+// Random features (la_backward_prf.hip): one 64-token step per workgroup; the forward summary
+// pass of la_prefill_prf.hpp gives one record per step.
+bool prefill_backward_prf_supported(int C, int d_k, int d_v, int n_psi);
+hipError_t launch_prefill_backward_prf(const BackwardParams& p, hipStream_t s, bool key_sweep);
+hipError_t launch_bank_transpose(const void* w, uint16_t* wt, int H, int n_psi, hipStream_t s);
+hipError_t launch_prefill_prf_bf16(const PrefillParams& p, hipStream_t s, bool out);
 
 // lin_attn_prefill on a caller-sized workspace whose segment plan is fitted to it (la_api.cpp):
 // the host-only checks, then the call itself.

@@ -266,26 +266,34 @@ la_status lin_attn_prefill_gated(const la_prefill_desc* d, const void* q, const 
  * output is needed) and gives dq, then a state sweep over the adjoint state
  * R_t = sum_{u >= t} gamma^(u-t) psi(q_u) dnum_u^T (dnum_u = dout_u / den_u) that gives dk and dv;
  * across segments the adjoint state is the forward scan's monoid run in reverse order.
- * gamma, eps and the feature map are constants (no gradient for them).
+ * gamma, eps and the feature map's bank are constants (no gradient for them). With random
+ * features the feature map's Jacobian follows ("Linearized 2-Simplicial Attention", 3.2):
+ * dx = sum_p a_p w_p - (sum_p a_p) x with a_p = dL/dpsi_p psi_p(x), where under the query-row
+ * shift the last term of dq takes the row of the bank that attains the shift (the argmax).
  *
- *   d         as for lin_attn_prefill; supported: in_dtype LA_BF16, psi identity or elu1,
- *             d_k == d_v == n_psi == 128, chunk 32, 64 or 128 (walked in steps of 64 tokens:
- *             the gradient does not depend on the grouping), either layout. out_dtype is
- *             the type of dout (LA_F32 or LA_BF16).
+ *   d         as for lin_attn_prefill; supported: in_dtype LA_BF16, and
+ *               psi identity or elu1: d_k == d_v == n_psi == 128;
+ *               psi PRF or PRF_QSHIFT: d_k == d_v == 128, n_psi 128 or 256;
+ *             chunk 32, 64 or 128 (walked in steps of 64 tokens: the gradient does not
+ *             depend on the grouping), either layout. out_dtype is the type of dout (LA_F32
+ *             or LA_BF16).
+ *   prf_w     device [H, n_psi, d_k] bf16, the forward call's bank; required iff psi is a
+ *             random-feature map
  *   dout      device, dL/do, laid out like lin_attn_prefill's o, out_dtype
  *   dq, dk    device fp32, laid out like q and k
  *   dv        device fp32, laid out like v
  *   dinit_S   device fp32 [B, H, n_psi, d_v] or NULL; dinit_Z [B, H, n_psi] or NULL (not
  *             written when normalize == 0)
- *   workspace at least lin_attn_prefill_backward_workspace_size bytes (two segment-summary
- *             regions, plus 8 bytes per token-head when normalize == 1)
+ *   workspace at least lin_attn_prefill_backward_workspace_size bytes: two segment-summary
+ *             regions (random features: one record per 64-token step), 8 bytes per token-head
+ *             when normalize == 1, and for random features a transposed copy of the bank
  * Errors as for lin_attn_prefill. Rows past T are neither read nor written.
  */
 la_status lin_attn_prefill_backward_workspace_size(const la_prefill_desc* d, size_t* bytes);
 la_status lin_attn_prefill_backward(const la_prefill_desc* d, const void* q, const void* k, const void* v,
-                                    const float* gamma, const float* init_S, const float* init_Z, const void* dout,
-                                    float* dq, float* dk, float* dv, float* dinit_S, float* dinit_Z,
-                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+                                    const float* gamma, const void* prf_w, const float* init_S, const float* init_Z,
+                                    const void* dout, float* dq, float* dk, float* dv, float* dinit_S,
+                                    float* dinit_Z, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * lin_attn_prefill_backward over a packed batch of variable-length sequences: the backward
@@ -293,7 +301,10 @@ la_status lin_attn_prefill_backward(const la_prefill_desc* d, const void* q, con
  * init_S and init_Z. Each sequence's gradients depend only on its own tokens and initial state.
  *
  *   d, cu_seqlens, total_tokens  as for lin_attn_prefill_varlen (layout LA_LAYOUT_BTHD),
- *                subject to lin_attn_prefill_backward's support limits
+ *                subject to lin_attn_prefill_backward's support limits, identity or elu1
+ *                features only (random features: LA_ERR_UNSUPPORTED; their per-step records
+ *                would scale with the longest sequence times the batch)
+ *   prf_w        as for lin_attn_prefill_backward (NULL here)
  *   dout         device [total_tokens, H, d_v] out_dtype
  *   dq, dk       device fp32 [total_tokens, H, d_k];  dv device fp32 [total_tokens, H, d_v]
  *   dinit_S, dinit_Z  per sequence, [B, H, n_psi, d_v] / [B, H, n_psi], or NULL; an empty
@@ -305,9 +316,10 @@ la_status lin_attn_prefill_backward_varlen_workspace_size(const la_prefill_desc*
                                                           size_t* bytes);
 la_status lin_attn_prefill_backward_varlen(const la_prefill_desc* d, const int32_t* cu_seqlens, int32_t total_tokens,
                                            const void* q, const void* k, const void* v, const float* gamma,
-                                           const float* init_S, const float* init_Z, const void* dout, float* dq,
-                                           float* dk, float* dv, float* dinit_S, float* dinit_Z, void* workspace,
-                                           size_t workspace_bytes, hipStream_t stream);
+                                           const void* prf_w, const float* init_S, const float* init_Z,
+                                           const void* dout, float* dq, float* dk, float* dv, float* dinit_S,
+                                           float* dinit_Z, void* workspace, size_t workspace_bytes,
+                                           hipStream_t stream);
 
 /* Batched single-token decode description: N independent streams x H heads. */
 typedef struct {

@@ -263,21 +263,35 @@ def test_backward_validation_and_workspace():
     assert ws(**{**base, "chunk": 128, "psi": 0})[0] == LA_OK
     assert ws(**{**base, "layout": 1})[0] == LA_OK
     assert ws(**{**base, "chunk": 32})[0] == LA_OK
-    for kw in (dict(chunk=16), dict(psi=2, n_psi=256), dict(d_k=64, d_v=64, n_psi=64), dict(in_dtype=LA_F32),
-               dict(psi=3, n_psi=256)):
+    for kw in (dict(chunk=16), dict(d_k=64, d_v=64, n_psi=64), dict(in_dtype=LA_F32), dict(psi=2, n_psi=64),
+               dict(psi=2, n_psi=256, chunk=16)):
         assert ws(**{**base, **kw})[0] == LA_ERR_UNSUPPORTED, kw
+    # random features: one record per 64-token step (two regions), 1/den and dden per token-head,
+    # and the bank transposed
+    for npsi in (128, 256):
+        for psi in (2, 3):
+            st_, nb = ws(**{**base, "psi": psi, "n_psi": npsi})
+            steps = -(-base["T"] // 64)
+            recs = 2 * base["B"] * base["H"] * steps * (npsi * 128 + npsi) * 4
+            tok = 2 * 4 * base["B"] * base["H"] * base["T"] if base.get("normalize", 1) else 0
+            assert st_ == LA_OK and nb == recs + tok + base["H"] * npsi * 128 * 2, (psi, npsi, nb)
+    assert ws(**{**base, "psi": 3, "n_psi": 256, "normalize": 0})[0] == LA_ERR_UNSUPPORTED
     d = _desc(**base)
     fake, odd = ctypes.c_void_p(1 << 20), ctypes.c_void_p((1 << 20) + 4)
 
-    def call(q=fake, dout=fake, dq=fake, w=fake, gamma=None, size=n):
-        return lib.lin_attn_prefill_backward(ctypes.byref(d), q, fake, fake, gamma, None, None, dout, dq, fake, fake,
-                                             None, None, w, size, None)
+    def call(q=fake, dout=fake, dq=fake, w=fake, gamma=None, size=n, desc=d, prf=None):
+        return lib.lin_attn_prefill_backward(ctypes.byref(desc), q, fake, fake, gamma, prf, None, None, dout, dq, fake,
+                                             fake, None, None, w, size, None)
     assert call(q=None) == LA_ERR_NULL
     assert call(dout=None) == LA_ERR_NULL
     assert call(dq=odd) == LA_ERR_ALIGN
     assert call(w=None) == LA_ERR_WORKSPACE
     assert call(size=n - 16) == LA_ERR_WORKSPACE
     assert call(gamma=(ctypes.c_float * 4)(1.0, 0.5, 0.0, 1.0)) == LA_ERR_VALUE
+    dp = _desc(**{**base, "psi": 2, "n_psi": 256})
+    _, nbp = ws(**{**base, "psi": 2, "n_psi": 256})
+    assert call(desc=dp, size=nbp) == LA_ERR_NULL  # random features without the bank
+    assert call(desc=dp, size=nbp, prf=odd) == LA_ERR_ALIGN
 
 
 def test_backward_varlen_validation_and_workspace():
@@ -301,13 +315,16 @@ def test_backward_varlen_validation_and_workspace():
 
     def call(desc=d, cu=fake, tot=total, q=fake, w=fake, size=n.value):
         return lib.lin_attn_prefill_backward_varlen(ctypes.byref(desc), cu, tot, q, fake, fake, None, None, None,
-                                                    fake, fake, fake, fake, None, None, w, size, None)
+                                                    None, fake, fake, fake, fake, None, None, w, size, None)
     assert call(cu=None) == LA_ERR_NULL
     assert call(cu=odd) == LA_ERR_ALIGN
     assert call(tot=-1) == LA_ERR_SHAPE
     assert call(desc=_desc(**{**base, "layout": 0})) == LA_ERR_VALUE
     assert call(q=None) == LA_ERR_NULL
     assert call(size=n.value - 16) == LA_ERR_WORKSPACE
+    dp = _desc(**{**base, "psi": 2, "n_psi": 256})  # random features: fixed-length batches only
+    assert lib.lin_attn_prefill_backward_varlen_workspace_size(ctypes.byref(dp), total,
+                                                               ctypes.byref(n)) == LA_ERR_UNSUPPORTED
 
 
 def test_decode_validation():
@@ -345,8 +362,8 @@ def test_decay_head_limit():
         got = lib.lin_attn_prefill(ctypes.byref(d), fake, fake, fake, g, None, None, None, fake, None, None, fake, 0,
                                    None)
         assert got == want, ("prefill", H, got)
-        gotb = lib.lin_attn_prefill_backward(ctypes.byref(d), fake, fake, fake, g, None, None, fake, fake, fake, fake,
-                                             None, None, fake, 0, None)
+        gotb = lib.lin_attn_prefill_backward(ctypes.byref(d), fake, fake, fake, g, None, None, None, fake, fake, fake,
+                                             fake, None, None, fake, 0, None)
         assert gotb == want, ("backward", H, gotb)
     dd = DecodeDesc(N=1, H=257, d_k=128, d_v=128, n_psi=128, psi=0, normalize=0, eps=1e-6, in_dtype=LA_BF16,
                     out_dtype=LA_F32)

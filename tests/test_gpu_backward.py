@@ -21,7 +21,7 @@ import torch
 
 import oracle
 from chunked_causal_linear_k1_amd import binding, inputs, workloads
-from chunked_causal_linear_k1_amd.workloads import PSI_ELU1, PSI_IDENTITY, Workload
+from chunked_causal_linear_k1_amd.workloads import PSI_ELU1, PSI_IDENTITY, PSI_PRF, PSI_PRF_QSHIFT, Workload
 
 from gpu_common import BF16_MAX_ABS, BF16_REL_L2, announce, metrics
 
@@ -287,3 +287,153 @@ def test_backward_max_decay_heads():
                                   normalize=0, eps=w.eps)
     for lab, a, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref[:3]):
         _check(a.cpu().numpy(), r, f"256 heads {lab}")
+
+
+# ---- positive random features (psi(x)_p = exp(w_p . x - |x|^2/2) / sqrt(n_psi), one bf16 bank per
+# head), with and without the query-row shift: the feature Jacobians on top of the sweeps
+
+def _prf_workload(psi, n_psi, normalize, decay, B, H, T, C, seed):
+    return Workload(name="bwd_prf", B=B, H=H, T=T, d_k=128, d_v=128, n_psi=n_psi, chunk=C, psi=psi,
+                    normalize=normalize, eps=1e-6, dtype="bf16", seed=seed, qk_scale=128 ** -0.25, v_scale=1.0,
+                    decay=decay)
+
+
+def _prf_backward(w, inp, dout, S0=None, Z0=None, layout="bhtd", q_mult=1.0, label=""):
+    """GPU backward (through the C ABI) against the oracle's; returns nothing, asserts the bar."""
+    B, H, T = w.B, w.H, w.T
+    q = inp["q"] if q_mult == 1.0 else (inp["q"].float() * q_mult).to(torch.bfloat16)  # a power of two: exact
+    k, v, W = inp["k"], inp["v"], inp["prf_w"]
+    g = inp["gamma"]
+    tr = (lambda x: x.transpose(1, 2).contiguous()) if layout == "bthd" else (lambda x: x.contiguous())
+    qd, kd, vd, dod = (tr(x).to(DEV) for x in (q, k, v, dout))
+    with_state = S0 is not None
+    S0d = None if S0 is None else torch.from_numpy(np.ascontiguousarray(S0)).float().to(DEV)
+    Z0d = None if Z0 is None else torch.from_numpy(np.ascontiguousarray(Z0)).float().to(DEV)
+    dS0 = torch.zeros((B, H, w.n_psi, 128), device=DEV) if with_state else None
+    dZ0 = torch.zeros((B, H, w.n_psi), device=DEV) if with_state else None
+    dq, dk, dv = binding.lin_attn_prefill_backward(qd, kd, vd, dod, psi=w.psi, chunk=w.chunk, normalize=w.normalize,
+                                                   eps=w.eps, gamma=None if g is None else list(g), prf_w=W.to(DEV),
+                                                   init_S=S0d, init_Z=Z0d, dinit_S=dS0, dinit_Z=dZ0, layout=layout)
+    torch.cuda.synchronize()
+    untr = (lambda x: x.transpose(1, 2)) if layout == "bthd" else (lambda x: x)
+    got = [untr(x.cpu()).reshape(B * H, T, 128).numpy() for x in (dq, dk, dv)]
+    BH = B * H
+    ref = oracle.prefill_backward(q.reshape(BH, T, 128), k.reshape(BH, T, 128), v.reshape(BH, T, 128),
+                                  dout.reshape(BH, T, 128), w.psi, n_psi=w.n_psi, prf_w=W,
+                                  w_head=[b % H for b in range(BH)],
+                                  gamma=None if g is None else [float(g[b % H]) for b in range(BH)],
+                                  normalize=w.normalize, eps=w.eps,
+                                  S0=None if S0d is None else S0d.cpu().double().numpy().reshape(BH, w.n_psi, 128),
+                                  Z0=None if Z0d is None else Z0d.cpu().double().numpy().reshape(BH, w.n_psi))
+    for lab, a, r in zip(("dq", "dk", "dv"), got, ref[:3]):
+        _check(a, r, f"{label} {lab}")
+    if with_state:
+        _check(dS0.cpu().numpy().reshape(BH, w.n_psi, 128), ref[3], f"{label} dS0")
+        if w.normalize:
+            _check(dZ0.cpu().numpy().reshape(BH, w.n_psi), ref[4], f"{label} dZ0")
+
+
+def _prf_state(w, inp, T0, seed):
+    """The state after a seeded T0-token prefix with the same bank (oracle), as a hand-off gives it."""
+    gen = torch.Generator().manual_seed(seed)
+    k0 = (torch.randn((w.B * w.H, T0, 128), generator=gen) * w.qk_scale).to(torch.bfloat16)
+    v0 = torch.randn((w.B * w.H, T0, 128), generator=gen).to(torch.bfloat16)
+    g = inp["gamma"]
+    _, S, Z = oracle.prefill(None, k0, v0, PSI_PRF, n_psi=w.n_psi, prf_w=inp["prf_w"],
+                             w_head=[b % w.H for b in range(w.B * w.H)],
+                             gamma=None if g is None else [float(g[b % w.H]) for b in range(w.B * w.H)],
+                             normalize=w.normalize, want_state=True)
+    return S.reshape(w.B, w.H, w.n_psi, 128), Z.reshape(w.B, w.H, w.n_psi)
+
+
+# name, psi, n_psi, normalize, decay, B, H, T, C, init state, dout dtype, layout, query multiplier
+PRF_CASES = [
+    ("prf256_norm", PSI_PRF, 256, 1, "none", 1, 2, 300, 64, False, "f32", "bhtd", 1.0),
+    ("prf128_norm_decay", PSI_PRF, 128, 1, "const:0.99", 2, 1, 333, 64, False, "f32", "bhtd", 1.0),
+    ("prf256_nonorm_decay", PSI_PRF, 256, 0, "retnet_spread", 1, 3, 200, 128, False, "f32", "bhtd", 1.0),
+    ("prf256_state_c32", PSI_PRF, 256, 1, "const:0.995", 1, 2, 257, 32, True, "f32", "bhtd", 1.0),
+    ("prf128_bf16_dout_bthd", PSI_PRF, 128, 1, "const:0.98", 2, 2, 190, 128, True, "bf16", "bthd", 1.0),
+    ("qshift256", PSI_PRF_QSHIFT, 256, 1, "none", 1, 2, 300, 64, False, "f32", "bhtd", 1.0),
+    ("qshift128_decay_state", PSI_PRF_QSHIFT, 128, 1, "const:0.99", 1, 2, 222, 64, True, "f32", "bhtd", 1.0),
+    # queries 4x larger: the shift keeps every query feature finite (the largest is 1/sqrt(n_psi))
+    ("qshift256_large_queries", PSI_PRF_QSHIFT, 256, 1, "const:0.995", 1, 2, 200, 64, False, "f32", "bhtd", 4.0),
+]
+
+
+@pytest.mark.parametrize("case", PRF_CASES, ids=[c[0] for c in PRF_CASES])
+def test_backward_prf(case):
+    name, psi, n_psi, normalize, decay, B, H, T, C, with_state, dt, layout, q_mult = case
+    w = _prf_workload(psi, n_psi, normalize, decay, B, H, T, C, seed=300 + [c[0] for c in PRF_CASES].index(name))
+    announce(f"backward prf {name} B={B} H={H} T={T} C={C} n_psi={n_psi} layout={layout}")
+    inp = inputs.make_prefill_inputs(w)
+    dout = inputs.make_upstream_grad((B, H, T, 128), w.seed + 11,
+                                     dtype=torch.float32 if dt == "f32" else torch.bfloat16)
+    S0 = Z0 = None
+    if with_state:
+        S0, Z0 = _prf_state(w, inp, 80, w.seed + 5)
+    _prf_backward(w, inp, dout, S0=S0, Z0=Z0, layout=layout, q_mult=q_mult, label=name)
+
+
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 129])
+def test_backward_prf_edge_lengths(T):
+    """Random features at lengths around one 64-token step (one token: the degenerate case of a
+    denominator, its dq and dk are eps-sized; held like the other feature maps' edge cases)."""
+    w = _prf_workload(PSI_PRF, 256, 1, "const:0.99", 1, 2, T, 64, seed=400 + T)
+    announce(f"backward prf edge T={T}")
+    inp = inputs.make_prefill_inputs(w)
+    dout = inputs.make_upstream_grad((1, 2, T, 128), w.seed + 11)
+    if T == 1:  # o_1 = v_1 w / (w + eps): dq and dk are eps-sized differences, held to an absolute bound
+        dq, dk, dv = binding.lin_attn_prefill_backward(*(inp[x].to(DEV) for x in ("q", "k", "v")), dout.to(DEV),
+                                                       psi=PSI_PRF, chunk=64, normalize=1, eps=w.eps,
+                                                       gamma=list(inp["gamma"]), prf_w=inp["prf_w"].to(DEV))
+        torch.cuda.synchronize()
+        ref = oracle.prefill_backward(inp["q"].reshape(2, 1, 128), inp["k"].reshape(2, 1, 128),
+                                      inp["v"].reshape(2, 1, 128), dout.reshape(2, 1, 128), PSI_PRF, n_psi=256,
+                                      prf_w=inp["prf_w"], w_head=[0, 1], gamma=[float(x) for x in inp["gamma"]],
+                                      normalize=1, eps=w.eps)
+        _check(dv.cpu().reshape(2, 1, 128).numpy(), ref[2], "prf edge T=1 dv")
+        # dq and dk are the difference of two terms that cancel to an eps-sized result; the
+        # bound is the rounding level (two-term bf16 operands, about 2^-16) of either term:
+        # (dout . v / den) sum_p psi(q)_p psi(k)_p (w_p - x), x = q or k
+        W = inp["prf_w"].double().numpy()
+        for lab, a, r in (("dq", dq, ref[0]), ("dk", dk, ref[1])):
+            err = float(np.abs(a.cpu().reshape(2, 1, 128).numpy() - r).max())
+            mag = 0.0
+            for h in range(2):
+                qh, kh = (inp[x][0, h, 0].double().numpy() for x in ("q", "k"))
+                g = oracle.feature(qh, PSI_PRF, 256, W[h])
+                f = oracle.feature(kh, PSI_PRF, 256, W[h])
+                den = float(g @ f) + float(np.float32(w.eps))
+                t1 = float(dout[0, h, 0].double().numpy() @ inp["v"][0, h, 0].double().numpy()) / den
+                x = qh if lab == "dq" else kh
+                mag = max(mag, float(np.abs(t1 * ((g * f) @ W[h] - (g @ f) * x)).max()))
+            print(f"[parity] prf edge T=1 {lab} max_abs={err:.3e} (bound {3e-5 * mag:.3e}, term {mag:.3e})",
+                  flush=True)
+            assert err <= 3e-5 * mag, (lab, err, mag)
+        return
+    _prf_backward(w, inp, dout, label=f"prf edge T={T}")
+
+
+def test_full_backward_prf_4k_sampled():
+    """The 4k random-feature workload (8 x 16 heads, n_psi 256) at full size: sampled heads against
+    the oracle, and a second call bitwise equal to the first."""
+    w = workloads.PRF_4K
+    heads = [0, 77]
+    announce(f"backward full-size {w.name} sampled heads {heads}")
+    inp = inputs.make_prefill_inputs(w, device=DEV)
+    dout = inputs.make_upstream_grad((w.B, w.H, w.T, w.d_v), w.seed + 17, device=DEV)
+    kw = dict(psi=w.psi, chunk=w.chunk, normalize=w.normalize, eps=w.eps, prf_w=inp["prf_w"])
+    first = binding.lin_attn_prefill_backward(inp["q"], inp["k"], inp["v"], dout, **kw)
+    again = binding.lin_attn_prefill_backward(inp["q"], inp["k"], inp["v"], dout, **kw)
+    torch.cuda.synchronize()
+    for a, b in zip(first, again):
+        assert torch.equal(a, b), "backward is not deterministic"
+    del again
+    W = inp["prf_w"].cpu()
+    for hflat in heads:
+        b, h = divmod(hflat, w.H)
+        ref = oracle.prefill_backward(inp["q"][b, h].cpu(), inp["k"][b, h].cpu(), inp["v"][b, h].cpu(),
+                                      dout[b, h].cpu(), w.psi, n_psi=w.n_psi, prf_w=W, w_head=[h],
+                                      normalize=w.normalize, eps=w.eps)
+        for lab, a, r in zip(("dq", "dk", "dv"), first, ref[:3]):
+            _check(a[b, h].cpu().numpy(), r, f"{w.name} b={b} h={h} {lab}")
