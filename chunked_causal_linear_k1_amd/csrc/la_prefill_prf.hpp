@@ -220,24 +220,118 @@ __device__ __forceinline__ void state_update_prf(f32x16 (&S)[NP / 32], const Psi
 }
 
 // ---------------------------------------------------------------------------------------
+// Eight waves, two per SIMD. Wave w = (cb, fh), cb = w % 4, fh = w / 4: value columns
+// [32 cb, 32 cb + 32) of the state and of the outputs, and state rows (features) of half fh,
+// [fh NP/2, (fh + 1) NP/2). Each wave therefore carries a quarter of the fp32 state's columns
+// for half its rows (64 registers at n_psi = 256), the state update is not duplicated, and the
+// two halves' partial outputs meet through LDS. The feature GEMMs are split into (feature
+// tile, token tile) jobs over the waves.
+template <int C, int D, int NP>
+struct Geo8 {
+  using B = Geo<C, D, NP, true>;
+  static constexpr int NWV = 8, NT = 64 * NWV;
+  static constexpr int NJ = B::NJ, NFT = B::NFT, NFH = NFT / 2, NTILE = B::NTILE;
+  static constexpr int JPW = NFT * NJ / NWV;       // feature jobs per wave
+  static constexpr int PPR = D / 8, RSTEP = NT / PPR, NPC = C * PPR / NT;
+  static constexpr int OFF_RQ = B::OFF_RQ, OFF_RK = B::OFF_RK, OFF_A = B::OFF_A, OFF_PQ = B::OFF_PQ,
+                       OFF_PK = B::OFF_PK, OFF_V = B::OFF_V, OFF_F = B::OFF_F;
+  static constexpr int OFF_X = 0;  // half 1's partial outputs: the raw / score / psi(Q) region, dead by then
+  static constexpr int F_Z = 0;                    // Z [NP]
+  static constexpr int F_THETA = NP;               // gamma^(j+1) [C]
+  static constexpr int F_R = F_THETA + C;          // score row sums [NTILE][32]
+  static constexpr int F_NQ = F_R + NTILE * 32;    // |q_t|^2 [C]
+  static constexpr int F_NK = F_NQ + C;            // |k_t|^2 [C]
+  static constexpr int F_QZ = F_NK + C;            // psi(q_t) . Z_prev per feature tile [NFT][C]
+  static constexpr int F_ZP = F_QZ + NFT * C;      // sum_i Xi_i psi(k_i) per token tile [NJ][NP]
+  static constexpr int F_QMAX = F_ZP + NJ * NP;    // max_p w_p . q_t per feature tile [NFT][C] (query shift)
+  static constexpr int LDS_BYTES = OFF_F + 4 * (F_QMAX + NFT * C);
+  static constexpr int SUM_LDS_BYTES = Geo<C, D, NP, false>::OFF_F + 4 * F_QMAX;  // no Q tiles, no QMAX
+  static_assert(JPW * NWV == NFT * NJ && JPW >= 1 && NJ % JPW == 0,
+                "feature jobs split evenly over the waves, one feature tile per wave");
+  static_assert(NTILE <= NWV && NPC * NT == C * PPR, "tiling");
+  static_assert(4 * (NWV / 2) * NJ * 16 * 64 <= OFF_PK, "partial outputs fit in front of psi(K)");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+};
+
+// Feature job jb of a wave: feature tile jb / NJ, token tile jb % NJ (with two jobs per wave
+// both token tiles of one feature tile, so its W operands serve both).
+template <int NJ>
+__device__ __forceinline__ int job_ft(int jb) { return jb / NJ; }
+template <int NJ>
+__device__ __forceinline__ int job_jt8(int jb) { return jb % NJ; }
+
+// The raw pieces of one tile (rows prow + RSTEP i) to LDS with each row's squared norm.
+template <int D, int NPC, int RSTEP>
+__device__ __forceinline__ void commit_raw_norm8(const pf::PiecesN<NPC>& P, unsigned char* dst, int pitch_bytes,
+                                                 float* nrm, int prow, int tid) {
+  constexpr int PPR = D / 8;
+#pragma unroll
+  for (int i = 0; i < NPC; ++i) {
+    *(uint4*)(dst + i * RSTEP * pitch_bytes) = P.r[i];
+    if (nrm) {
+      const bf16x8 x = __builtin_bit_cast(bf16x8, P.r[i]);
+      float sq = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) sq += from_bf16(x[j]) * from_bf16(x[j]);
+#pragma unroll
+      for (int off = 1; off < PPR; off <<= 1) sq += __shfl_xor(sq, off);
+      if (tid % PPR == 0) nrm[prow + RSTEP * i] = sq;
+    }
+  }
+}
+
+// S[pt] += K~^T V for this wave's state rows: feature tiles f0 + pt (pt < NFH), value columns
+// at vT; k = token, software-pipelined in 16-token steps.
+template <int C, int NP, int NFH, int LO, int PV>
+__device__ __forceinline__ void state_update_half(f32x16 (&S)[NFH], const PsiKBases<NP>& kb8, const unsigned char* vT,
+                                                  int f0) {
+  constexpr int NK = C / 16;
+  bf16x8 ops[2][1 + 2 * NFH];
+  auto load_step = [&](bf16x8 (&o)[1 + 2 * NFH], int ik) {
+    const int r0 = ik * 16;
+    o[0] = cat8(lds_read_tr4((const __bf16*)(vT + r0 * PV * 2)), lds_read_tr4((const __bf16*)(vT + (r0 + 4) * PV * 2)));
+#pragma unroll
+    for (int j = 0; j < NFH; ++j) {
+      o[1 + 2 * j] = psik_tr<NP>(kb8, r0, f0 + j, 0);
+      o[2 + 2 * j] = psik_tr<NP>(kb8, r0, f0 + j, LO);
+    }
+  };
+  load_step(ops[0], 0);
+#pragma unroll
+  for (int ik = 0; ik < NK; ++ik) {
+    if (ik + 1 < NK) load_step(ops[(ik + 1) & 1], ik + 1);
+    const bf16x8(&o)[1 + 2 * NFH] = ops[ik & 1];
+#pragma unroll
+    for (int j = 0; j < NFH; ++j) {
+      S[j] = mfma32(o[1 + 2 * j], o[0], S[j]);
+      S[j] = mfma32(o[2 + 2 * j], o[0], S[j]);
+    }
+    if (ik + 1 < NK) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * (1 + 2 * NFH), 0);  // next step's reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * NFH, 0);            // this step's MFMAs
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
 // Segment summaries: per (sequence, segment), S = sum over the segment's tokens of
 // gamma^(seg_end-1-i) psi(k_i) v_i^T and Z likewise, written to the workspace.
 template <int C, int D, int NP, bool DECAY, bool NORM>
-__global__ __launch_bounds__(2 * D) void k_summary_prf(PrefillParams p) {
+__global__ __launch_bounds__(512) void k_summary_prf(PrefillParams p) {
+  using G8 = Geo8<C, D, NP>;
   using G = Geo<C, D, NP, false>;
-  using PG = pf::Geo<C, D, true>;
-  constexpr int NJ = G::NJ, NFT = G::NFT, FPW = G::FPW, NPC = PG::NPC;
+  constexpr int NJ = G8::NJ, NFH = G8::NFH, JPW = G8::JPW, NPC = G8::NPC, RSTEP = G8::RSTEP;
   constexpr int PR = G::PR, PV = G::PV, LO = G::PSIK;
   constexpr float LOG2E = 1.4426950408889634f;
   extern __shared__ __align__(16) unsigned char smem[];
   const int bh = blockIdx.x, seg = blockIdx.y, head = bh % p.H;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, n = lane & 31, hh = lane >> 5;
   const int L16 = lane & 15, g = lane >> 4;
-  const int Ew = 32 * w;
+  const int cb = w & 3, fh = w >> 2, Ew = 32 * cb;
   const float lg = DECAY ? p.log2g[head] : 0.f;
   const float log2_rsqrt = -0.5f * __log2f((float)NP);  // the 1/sqrt(n_psi) factor, as a log2
 
-  const int prow = tid / PG::PPR, pcol = (tid % PG::PPR) * 8;
+  const int prow = tid / G8::PPR, pcol = (tid % G8::PPR) * 8;
   const int trow = 8 * (g >> 1) + (L16 >> 2), tcol = 16 * (g & 1) + 4 * (L16 & 3);
   unsigned char* const rkP = smem + pin(G::OFF_RK + (prow * PR + pcol) * 2);
   const unsigned char* const rR = smem + pin(G::OFF_RK + (n * PR + 8 * hh) * 2);
@@ -247,23 +341,21 @@ __global__ __launch_bounds__(2 * D) void k_summary_prf(PrefillParams p) {
   float* const sF = (float*)(smem + pin(G::OFF_F));
   const PsiKBases<NP> kb8 = psik_bases<NP>(smem, G::OFF_PK, n, hh, trow, tcol);
 
-  // this wave's rows of W as MFMA operands (M = feature, k = input dim)
+  // W rows of this wave's feature tile as MFMA operands (M = feature, k = input dim)
   const uint16_t* Wh = (const uint16_t*)p.prf_w + (size_t)head * NP * D;
-  bf16x8 wop[FPW][D / 16];
+  const int ft0 = job_ft<NJ>(w * JPW);
+  bf16x8 wop[D / 16];
 #pragma unroll
-  for (int f = 0; f < FPW; ++f)
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk)
-      wop[f][kk] = *(const bf16x8*)(Wh + (size_t)((w * FPW + f) * 32 + n) * D + 16 * kk + 8 * hh);
+  for (int kk = 0; kk < D / 16; ++kk) wop[kk] = *(const bf16x8*)(Wh + (size_t)(ft0 * 32 + n) * D + 16 * kk + 8 * hh);
 
-  f32x16 S[NFT];
+  f32x16 S[NFH];
 #pragma unroll
-  for (int pt = 0; pt < NFT; ++pt) S[pt] = f32x16{};
-  float zacc[FPW][16];  // per-lane partial normaliser sums (this lane's tokens), decayed to the segment end
+  for (int pt = 0; pt < NFH; ++pt) S[pt] = f32x16{};
+  float zacc[JPW][16];  // per-lane normaliser sums of this wave's jobs (its tokens), decayed to the segment end
 #pragma unroll
-  for (int f = 0; f < FPW; ++f)
+  for (int u = 0; u < JPW; ++u)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) zacc[f][r] = 0.f;
+    for (int r = 0; r < 16; ++r) zacc[u][r] = 0.f;
 
   const SeqSpan sq = seq_span(p, bh);
   const int T = sq.T, n_chunks = (T + C - 1) / C;
@@ -271,71 +363,72 @@ __global__ __launch_bounds__(2 * D) void k_summary_prf(PrefillParams p) {
   const uint16_t* kg = (const uint16_t*)p.k + sq.row0 * D;
   const uint16_t* vg = (const uint16_t*)p.v + sq.row0 * D;
   const int c0 = seg * p.seg_chunks, c1 = min(min(c0 + p.seg_chunks, n_chunks), p.sum_end);
-  pf::Pieces<C, D> pk_, pv_;
+  pf::PiecesN<NPC> pk_, pv_;
   {
     const int L0 = c0 < c1 ? min(C, T - c0 * C) : 0;
-    pf::load_pieces<C, D>(pk_, kg + (size_t)c0 * C * rse, L0, rsb);
-    pf::load_pieces<C, D>(pv_, vg + (size_t)c0 * C * rse, L0, rsb);
+    pf::load_pieces_n<D, NPC, RSTEP>(pk_, kg + (size_t)c0 * C * rse, L0, prow, pcol, rsb);
+    pf::load_pieces_n<D, NPC, RSTEP>(pv_, vg + (size_t)c0 * C * rse, L0, prow, pcol, rsb);
     vm_drain();
   }
   for (int c = c0; c < c1; ++c) {
     const int L = min(C, T - c * C);
     const float a = DECAY ? exp2f((float)L * lg) : 1.f;
     lds_barrier();  // the previous chunk is done with LDS
-    commit_raw_norm<C, D>(pk_, rkP, PR * 2, sF + G::F_NK, prow, tid);
+    commit_raw_norm8<D, NPC, RSTEP>(pk_, rkP, PR * 2, sF + G8::F_NK, prow, tid);
 #pragma unroll
-    for (int i = 0; i < NPC; ++i) *(uint4*)(vP + i * 16 * PV * 2) = pv_.r[i];
+    for (int i = 0; i < NPC; ++i) *(uint4*)(vP + i * RSTEP * PV * 2) = pv_.r[i];
     {
       const bool more = c + 1 < c1;
       const int Ln = more ? min(C, T - (c + 1) * C) : 0;
-      pf::load_pieces<C, D>(pk_, kg + (size_t)(c + 1) * C * rse, Ln, rsb);
-      pf::load_pieces<C, D>(pv_, vg + (size_t)(c + 1) * C * rse, Ln, rsb);
+      pf::load_pieces_n<D, NPC, RSTEP>(pk_, kg + (size_t)(c + 1) * C * rse, Ln, prow, pcol, rsb);
+      pf::load_pieces_n<D, NPC, RSTEP>(pv_, vg + (size_t)(c + 1) * C * rse, Ln, prow, pcol, rsb);
     }
     lds_barrier();
-    // K~_t = Xi_t psi(k_t) for this wave's features; padded tokens give exactly zero
+    // K~_t = Xi_t psi(k_t) for this wave's jobs; padded tokens give exactly zero
 #pragma unroll
-    for (int f = 0; f < FPW; ++f)
+    for (int u = 0; u < JPW; ++u) {
+      const int jb = w * JPW + u, ft = job_ft<NJ>(jb), jt = job_jt8<NJ>(jb);
+      const f32x16 acc = feature_gemm<D>(wop, rR, jt, PR * 2);
+      const int t = jt * 32 + n;
+      // exponent offset: |k|^2/2, the 1/sqrt(n_psi) factor and log2 Xi_t; -inf past the end
+      const float h = t < L ? 0.5f * sF[G8::F_NK + t] * LOG2E - log2_rsqrt - (DECAY ? (float)(L - 1 - t) * lg : 0.f)
+                            : __builtin_huge_valf();
+      float v[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) zacc[f][r] *= a;
-#pragma unroll
-    for (int f = 0; f < FPW; ++f) {
-      const int ft = w * FPW + f;
-#pragma unroll
-      for (int jt = 0; jt < NJ; ++jt) {
-        const f32x16 acc = feature_gemm<D>(wop[f], rR, jt, PR * 2);
-        const int t = jt * 32 + n;
-        // exponent offset: |k|^2/2, the 1/sqrt(n_psi) factor and log2 Xi_t; -inf past the end
-        const float h = t < L ? 0.5f * sF[G::F_NK + t] * LOG2E - log2_rsqrt - (DECAY ? (float)(L - 1 - t) * lg : 0.f)
-                              : __builtin_huge_valf();
-        float v[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          v[r] = exp2f(acc[r] * LOG2E - h);
-          zacc[f][r] += v[r];
-        }
-        write_psik<NP, LO>(pk, t, ft, hh, v);
+      for (int r = 0; r < 16; ++r) {
+        v[r] = exp2f(acc[r] * LOG2E - h);
+        zacc[u][r] = zacc[u][r] * a + v[r];
       }
+      write_psik<NP, LO>(pk, t, ft, hh, v);
     }
     lds_barrier();
     if (DECAY) {
 #pragma unroll
-      for (int pt = 0; pt < NFT; ++pt) S[pt] *= a;
+      for (int pt = 0; pt < NFH; ++pt) S[pt] *= a;
     }
-    // S[pt] += K~^T V (M = feature, N = value column, k = token)
-    state_update_prf<C, D, NP, LO, PV>(S, kb8, vT);
+    state_update_half<C, NP, NFH, LO, PV>(S, kb8, vT, fh * NFH);
   }
   // segment summary -> workspace [bh][seg][E], E = NP*D + NP
   const size_t E = (size_t)NP * D + NP;
   float* out = p.ws + rec_index(p, bh, seg) * E;
 #pragma unroll
-  for (int pt = 0; pt < NFT; ++pt)
+  for (int pt = 0; pt < NFH; ++pt)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) out[(size_t)(pt * 32 + dtile_row(r, lane)) * D + Ew + n] = S[pt][r];
+    for (int r = 0; r < 16; ++r) out[(size_t)((fh * NFH + pt) * 32 + dtile_row(r, lane)) * D + Ew + n] = S[pt][r];
+  // normaliser: per feature, the sum over the token tiles' partials (one job per token tile)
 #pragma unroll
-  for (int f = 0; f < FPW; ++f) {
-    const float z = lane_total16(zacc[f], n);
+  for (int u = 0; u < JPW; ++u) {
+    const int jb = w * JPW + u, ft = job_ft<NJ>(jb), jt = job_jt8<NJ>(jb);
+    const float z = lane_total16(zacc[u], n);
     const int r = (n >> 1) & 15;
-    if ((n & 1) == 0) out[(size_t)NP * D + (w * FPW + f) * 32 + 8 * (r >> 2) + 4 * hh + (r & 3)] = NORM ? z : 0.f;
+    if ((n & 1) == 0) sF[G8::F_ZP + jt * NP + ft * 32 + 8 * (r >> 2) + 4 * hh + (r & 3)] = z;
+  }
+  lds_barrier();
+  for (int f = tid; f < NP; f += G8::NT) {
+    float z = 0.f;
+#pragma unroll
+    for (int jt = 0; jt < NJ; ++jt) z += sF[G8::F_ZP + jt * NP + f];
+    out[(size_t)NP * D + f] = NORM ? z : 0.f;
   }
 }
 
@@ -343,10 +436,10 @@ __global__ __launch_bounds__(2 * D) void k_summary_prf(PrefillParams p) {
 // Output pass: per (sequence, segment), from the segment's exclusive prefix (written by
 // the scan), walk the chunks: features, shared score tiles, outputs, state update.
 template <int C, int D, int NP, bool DECAY, bool NORM, bool OBF, bool QS>
-__global__ __launch_bounds__(2 * D) void k_output_prf(PrefillParams p) {
+__global__ __launch_bounds__(512) void k_output_prf(PrefillParams p) {
+  using G8 = Geo8<C, D, NP>;
   using G = Geo<C, D, NP, true>;
-  using PG = pf::Geo<C, D, true>;
-  constexpr int NJ = G::NJ, NFT = G::NFT, FPW = G::FPW, NPC = PG::NPC;
+  constexpr int NJ = G8::NJ, NFH = G8::NFH, NFT = G8::NFT, JPW = G8::JPW, NPC = G8::NPC, RSTEP = G8::RSTEP;
   constexpr int PR = G::PR, PQ = G::PQ, PV = G::PV, PA = G::PA;
   constexpr int LO = G::PSIK, ALO = 32 * PA * 2;
   constexpr float LOG2E = 1.4426950408889634f;
@@ -354,56 +447,42 @@ __global__ __launch_bounds__(2 * D) void k_output_prf(PrefillParams p) {
   const int bh = blockIdx.x, seg = blockIdx.y, head = bh % p.H;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, n = lane & 31, hh = lane >> 5;
   const int L16 = lane & 15, g = lane >> 4;
-  const int Ew = 32 * w;
+  const int cb = w & 3, fh = w >> 2, Ew = 32 * cb;
   const float lg = DECAY ? p.log2g[head] : 0.f;
   const float log2_rsqrt = -0.5f * __log2f((float)NP);
 
-  const int prow = tid / PG::PPR, pcol = (tid % PG::PPR) * 8;
+  const int prow = tid / G8::PPR, pcol = (tid % G8::PPR) * 8;
   const int trow = 8 * (g >> 1) + (L16 >> 2), tcol = 16 * (g & 1) + 4 * (L16 & 3);
   unsigned char* const rqP = smem + pin(G::OFF_RQ + (prow * PR + pcol) * 2);  // raw K at + RAW
   const unsigned char* const rR = smem + pin(G::OFF_RQ + (n * PR + 8 * hh) * 2);
   unsigned char* const pqW = smem + pin(G::OFF_PQ + (n * PQ + 4 * hh) * 2);  // psi(Q) writes / numT operand
   const unsigned char* const pqS = smem + pin(G::OFF_PQ + (n * PQ + 8 * hh) * 2);  // score operand
-  const unsigned char* const pqZ = smem + pin(G::OFF_PQ + (n * PQ + hh * (NP / 2)) * 2);  // psi(q) . Z
   unsigned char* const pk = smem + pin(G::OFF_PK);
   unsigned char* const vP = smem + pin(G::OFF_V + (prow * PV + pcol) * 2);
   const unsigned char* const vT = smem + pin(G::OFF_V + (trow * PV + Ew + tcol) * 2);
   unsigned char* const aW = smem + pin(G::OFF_A + (n * PA + 4 * hh) * 2);
   const unsigned char* const aR = smem + pin(G::OFF_A + (n * PA + 8 * hh) * 2);
+  float* const xch = (float*)(smem + pin(G8::OFF_X)) + lane;  // [cb][jt][r][lane] partial outputs
   float* const sF = (float*)(smem + pin(G::OFF_F));
   float* const fN = (float*)(smem + pin(G::OFF_F + 4 * n));
   const PsiKBases<NP> kb8 = psik_bases<NP>(smem, G::OFF_PK, n, hh, trow, tcol);
 
   const uint16_t* Wh = (const uint16_t*)p.prf_w + (size_t)head * NP * D;
-  bf16x8 wop[FPW][D / 16];
+  const int ft0 = job_ft<NJ>(w * JPW);
+  bf16x8 wop[D / 16];
 #pragma unroll
-  for (int f = 0; f < FPW; ++f)
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk)
-      wop[f][kk] = *(const bf16x8*)(Wh + (size_t)((w * FPW + f) * 32 + n) * D + 16 * kk + 8 * hh);
+  for (int kk = 0; kk < D / 16; ++kk) wop[kk] = *(const bf16x8*)(Wh + (size_t)(ft0 * 32 + n) * D + 16 * kk + 8 * hh);
 
-  // exclusive prefix state of this segment
+  // exclusive prefix state of this segment: this wave's rows and columns
   const size_t E = (size_t)NP * D + NP;
   const float* pre = p.ws + rec_index(p, bh, seg) * E;
-  f32x16 S[NFT];
+  f32x16 S[NFH];
 #pragma unroll
-  for (int pt = 0; pt < NFT; ++pt)
+  for (int pt = 0; pt < NFH; ++pt)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) S[pt][r] = pre[(size_t)(pt * 32 + dtile_row(r, lane)) * D + Ew + n];
-  for (int j = tid; j < NP; j += G::NT) sF[G::F_Z + j] = NORM ? pre[(size_t)NP * D + j] : 0.f;
-  for (int j = tid; j < C; j += G::NT) sF[G::F_THETA + j] = DECAY ? exp2f((float)(j + 1) * lg) : 1.f;
-
-  // score-tile factors of this lane with decay (see k_output_sh); without decay only the
-  // causal mask of the diagonal tile, applied in place
-  float fdiag[DECAY ? 16 : 1], foff[DECAY ? 16 : 1];
-  if (DECAY) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int ir = dtile_row(r, lane);
-      fdiag[r] = ir <= n ? exp2f((float)(n - ir) * lg) : 0.f;
-      foff[r] = exp2f((float)(n + 32 - ir) * lg);
-    }
-  }
+    for (int r = 0; r < 16; ++r) S[pt][r] = pre[(size_t)((fh * NFH + pt) * 32 + dtile_row(r, lane)) * D + Ew + n];
+  for (int j = tid; j < NP; j += G8::NT) sF[G8::F_Z + j] = NORM ? pre[(size_t)NP * D + j] : 0.f;
+  for (int j = tid; j < C; j += G8::NT) sF[G8::F_THETA + j] = DECAY ? exp2f((float)(j + 1) * lg) : 1.f;
 
   const SeqSpan sq = seq_span(p, bh);
   const int T = sq.T, n_chunks = (T + C - 1) / C;
@@ -415,100 +494,106 @@ __global__ __launch_bounds__(2 * D) void k_output_prf(PrefillParams p) {
   unsigned char* ob = (unsigned char*)p.o + sq.row0 * D * OES;
   const int c0 = seg * p.seg_chunks, c1 = min(c0 + p.seg_chunks, n_chunks);
   if (c0 >= c1) return;  // segment past the end of a shorter sequence: nothing to write
-  pf::Pieces<C, D> pq_, pk_, pv_;
+  pf::PiecesN<NPC> pq_, pk_, pv_;
   {
     const int L0 = min(C, T - c0 * C);
-    pf::load_pieces<C, D>(pq_, qg + (size_t)c0 * C * rse, L0, rsb);
-    pf::load_pieces<C, D>(pk_, kg + (size_t)c0 * C * rse, L0, rsb);
-    pf::load_pieces<C, D>(pv_, vg + (size_t)c0 * C * rse, L0, rsb);
+    pf::load_pieces_n<D, NPC, RSTEP>(pq_, qg + (size_t)c0 * C * rse, L0, prow, pcol, rsb);
+    pf::load_pieces_n<D, NPC, RSTEP>(pk_, kg + (size_t)c0 * C * rse, L0, prow, pcol, rsb);
+    pf::load_pieces_n<D, NPC, RSTEP>(pv_, vg + (size_t)c0 * C * rse, L0, prow, pcol, rsb);
     vm_drain();
   }
   for (int c = c0; c < c1; ++c) {
     const int t0 = c * C, L = min(C, T - t0);
     const float a = DECAY ? exp2f((float)L * lg) : 1.f;
     lds_barrier();  // the previous chunk is done with LDS (and Z is updated)
-    commit_raw_norm<C, D>(pq_, rqP, PR * 2, sF + G::F_NQ, prow, tid);
-    commit_raw_norm<C, D>(pk_, rqP + G::RAW, PR * 2, sF + G::F_NK, prow, tid);
+    commit_raw_norm8<D, NPC, RSTEP>(pq_, rqP, PR * 2, sF + G8::F_NQ, prow, tid);
+    commit_raw_norm8<D, NPC, RSTEP>(pk_, rqP + G::RAW, PR * 2, sF + G8::F_NK, prow, tid);
 #pragma unroll
-    for (int i = 0; i < NPC; ++i) *(uint4*)(vP + i * 16 * PV * 2) = pv_.r[i];
+    for (int i = 0; i < NPC; ++i) *(uint4*)(vP + i * RSTEP * PV * 2) = pv_.r[i];
     {
       const bool more = c + 1 < c1;
       const int Ln = more ? min(C, T - (c + 1) * C) : 0;
-      pf::load_pieces<C, D>(pq_, qg + (size_t)(c + 1) * C * rse, Ln, rsb);
-      pf::load_pieces<C, D>(pk_, kg + (size_t)(c + 1) * C * rse, Ln, rsb);
-      pf::load_pieces<C, D>(pv_, vg + (size_t)(c + 1) * C * rse, Ln, rsb);
+      pf::load_pieces_n<D, NPC, RSTEP>(pq_, qg + (size_t)(c + 1) * C * rse, Ln, prow, pcol, rsb);
+      pf::load_pieces_n<D, NPC, RSTEP>(pk_, kg + (size_t)(c + 1) * C * rse, Ln, prow, pcol, rsb);
+      pf::load_pieces_n<D, NPC, RSTEP>(pv_, vg + (size_t)(c + 1) * C * rse, Ln, prow, pcol, rsb);
     }
     lds_barrier();
 
-    // ---- QS: the query-row shift. l_p = w_p . q - |q|^2/2 and its maximum differ by the
-    // same |q|^2/2, so the shifted feature is exp(w_p . q - max_r w_r . q) / sqrt(m). Each
-    // wave takes the maximum over its features (the GEMM is recomputed below), the waves'
-    // maxima meet in LDS.
+    // ---- QS: the query-row shift (see the header): each job's largest logit per token, the
+    // feature tiles' maxima meet in LDS
     if (QS) {
 #pragma unroll
-      for (int jt = 0; jt < NJ; ++jt) {
+      for (int u = 0; u < JPW; ++u) {
+        const int jb = w * JPW + u, ft = job_ft<NJ>(jb), jt = job_jt8<NJ>(jb);
+        const f32x16 acc = feature_gemm<D>(wop, rR, jt, PR * 2);
         float mx = -__builtin_huge_valf();
 #pragma unroll
-        for (int f = 0; f < FPW; ++f) {
-          const f32x16 acc = feature_gemm<D>(wop[f], rR, jt, PR * 2);
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[r]);
-        }
-        mx = fmaxf(mx, __shfl_xor(mx, 32));  // the other half of the lane pair holds the other rows
-        if (hh == 0) sF[G::F_QMAX + w * C + jt * 32 + n] = mx;
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));  // the other lane half holds the tile's other rows
+        if (hh == 0) sF[G8::F_QMAX + ft * C + jt * 32 + n] = mx;
       }
       lds_barrier();
     }
 
-    // ---- features of this wave's feature tiles: psi(Q) rounded to bf16; psi(K) as hi + lo
-    // (zero past the sequence end); zt = sum_i Xi_i psi(k_i) for the feature of register
-    // (n >> 1) & 15 (see lane_total16)
-    float zt[FPW];
+    // ---- features of this wave's jobs: psi(Q) rounded to bf16 (and its dot with Z_prev per
+    // token); psi(K) as hi + lo, zero past the sequence end (and its Xi-weighted sum per feature)
 #pragma unroll
-    for (int f = 0; f < FPW; ++f) {
-      const int ft = w * FPW + f;
-      zt[f] = 0.f;
+    for (int u = 0; u < JPW; ++u) {
+      const int jb = w * JPW + u, ft = job_ft<NJ>(jb), jt = job_jt8<NJ>(jb);
+      const int t = jt * 32 + n;
+      {
+        const f32x16 acc = feature_gemm<D>(wop, rR, jt, PR * 2);
+        float qshift = 0.5f * sF[G8::F_NQ + t];  // |q|^2 / 2, or the row's largest w_p . q (QS)
+        if (QS) {
+          qshift = sF[G8::F_QMAX + t];
 #pragma unroll
-      for (int jt = 0; jt < NJ; ++jt) {
-        const int t = jt * 32 + n;
-        {
-          const f32x16 acc = feature_gemm<D>(wop[f], rR, jt, PR * 2);
-          float qshift = 0.5f * sF[G::F_NQ + t];  // |q|^2 / 2, or the row's largest w_p . q (QS)
-          if (QS) {
-            qshift = sF[G::F_QMAX + t];
-#pragma unroll
-            for (int ww = 1; ww < G::NW; ++ww) qshift = fmaxf(qshift, sF[G::F_QMAX + ww * C + t]);
-          }
-          const float h = qshift * LOG2E - log2_rsqrt;
-          float v[16];
-#pragma unroll
-          for (int r = 0; r < 16; ++r) v[r] = exp2f(acc[r] * LOG2E - h);
-#pragma unroll
-          for (int gq = 0; gq < 4; ++gq)
-            *(uint2*)(pqW + (jt * 32 * PQ + ft * 32 + 8 * gq) * 2) =
-                pack4(v[4 * gq], v[4 * gq + 1], v[4 * gq + 2], v[4 * gq + 3]);
+          for (int f = 1; f < NFT; ++f) qshift = fmaxf(qshift, sF[G8::F_QMAX + f * C + t]);
         }
-        {
-          const f32x16 acc = feature_gemm<D>(wop[f], rR + G::RAW, jt, PR * 2);
-          const bool live = t < L;
-          const float h = live ? 0.5f * sF[G::F_NK + t] * LOG2E - log2_rsqrt : __builtin_huge_valf();
-          const float xi = (DECAY && live) ? exp2f((float)(L - 1 - t) * lg) : 1.f;
-          float v[16], vz[16];
+        const float h = qshift * LOG2E - log2_rsqrt;
+        float v[16];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            v[r] = exp2f(acc[r] * LOG2E - h);
-            vz[r] = DECAY ? v[r] * xi : v[r];
+        for (int r = 0; r < 16; ++r) v[r] = exp2f(acc[r] * LOG2E - h);
+        float qz = 0.f;
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const uint2 pq4 = pack4(v[4 * gq], v[4 * gq + 1], v[4 * gq + 2], v[4 * gq + 3]);
+          *(uint2*)(pqW + (jt * 32 * PQ + ft * 32 + 8 * gq) * 2) = pq4;
+          if (NORM) {  // the same rounded features as the numerator reads
+            const bf16x4 b4 = __builtin_bit_cast(bf16x4, pq4);
+            const f32x4 z4 = *(const f32x4*)(sF + G8::F_Z + ft * 32 + 8 * gq + 4 * hh);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) qz += from_bf16(b4[e]) * z4[e];
           }
-          if (NORM) zt[f] += lane_total16(vz, n);
-          write_psik<NP, LO>(pk, t, ft, hh, v);
         }
+        if (NORM) {
+          qz += __shfl_xor(qz, 32);
+          if (hh == 0) sF[G8::F_QZ + ft * C + t] = qz;
+        }
+      }
+      {
+        const f32x16 acc = feature_gemm<D>(wop, rR + G::RAW, jt, PR * 2);
+        const bool live = t < L;
+        const float h = live ? 0.5f * sF[G8::F_NK + t] * LOG2E - log2_rsqrt : __builtin_huge_valf();
+        const float xi = (DECAY && live) ? exp2f((float)(L - 1 - t) * lg) : 1.f;
+        float v[16], vz[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          v[r] = exp2f(acc[r] * LOG2E - h);
+          vz[r] = DECAY ? v[r] * xi : v[r];
+        }
+        if (NORM) {
+          const float z = lane_total16(vz, n);
+          const int r = (n >> 1) & 15;
+          if ((n & 1) == 0) sF[G8::F_ZP + jt * NP + ft * 32 + 8 * (r >> 2) + 4 * hh + (r & 3)] = z;
+        }
+        write_psik<NP, LO>(pk, t, ft, hh, v);
       }
     }
     lds_barrier();  // features complete; the raw tiles are dead (the score tiles alias them)
 
     // ---- score tile w (M = i, N = j, k = feature), masked, decayed, split into hi + lo
-    if (w < G::NTILE) {
-      const int t = w, jt = pf::tile_jt(t), it = t - jt * (jt + 1) / 2;
+    if (w < G8::NTILE) {
+      const int tt = w, jt = pf::tile_jt(tt), it = tt - jt * (jt + 1) / 2;
       f32x16 acc = f32x16{};
 #pragma unroll
       for (int kk = 0; kk < NP / 16; ++kk) {
@@ -522,15 +607,20 @@ __global__ __launch_bounds__(2 * D) void k_output_prf(PrefillParams p) {
       float rs = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        if constexpr (DECAY) av[r] = acc[r] * ((diag ? fdiag[r] : foff[r]) * tf);
-        else av[r] = (diag && dtile_row(r, lane) > n) ? 0.f : acc[r];
+        const int ir = dtile_row(r, lane);
+        if constexpr (DECAY) {
+          const float f = diag ? (ir <= n ? exp2f((float)(n - ir) * lg) : 0.f) : exp2f((float)(n + 32 - ir) * lg) * tf;
+          av[r] = acc[r] * f;
+        } else {
+          av[r] = (diag && ir > n) ? 0.f : acc[r];
+        }
         if (NORM) rs += av[r];
       }
       if (NORM) {
         rs += __shfl_xor(rs, 32);
-        if (hh == 0) fN[G::F_R + t * 32] = rs;
+        if (hh == 0) fN[G8::F_R + tt * 32] = rs;
       }
-      unsigned char* at = aW + t * G::A_TILE;
+      unsigned char* at = aW + tt * G::A_TILE;
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         bf16x8 h8, l8;
@@ -544,13 +634,13 @@ __global__ __launch_bounds__(2 * D) void k_output_prf(PrefillParams p) {
     }
     lds_barrier();
 
-    // ---- outputs, transposed as in k_output_sh: numT[e][j] (M = value column, N = token)
-    const __amdgpu_buffer_rsrc_t ors = make_rsrc(ob + (size_t)t0 * rse * OES, rows_extent(L, rse * OES, D * OES));
+    // ---- outputs, transposed: numT[e][j] (M = value column, N = token); this wave's half of the
+    // features, theta-weighted; half 1 adds the intra-chunk term V^T A^T
     f32x16 num[NJ];
 #pragma unroll
     for (int jt = 0; jt < NJ; ++jt) num[jt] = f32x16{};
 #pragma unroll
-    for (int pt = 0; pt < NFT; ++pt) {
+    for (int pt = 0; pt < NFH; ++pt) {
       bf16x8 sh[2], sl[2];  // S_prev[pt] as hi + lo, k in the D-tile feedback order
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
@@ -559,11 +649,12 @@ __global__ __launch_bounds__(2 * D) void k_output_prf(PrefillParams p) {
         for (int j = 0; j < 8; ++j) x[j] = S[pt][8 * q + j];
         split8_trunc(x, sh[q], sl[q]);
       }
+      const int fcol = (fh * NFH + pt) * 32;
 #pragma unroll
       for (int jt = 0; jt < NJ; ++jt)
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-          const unsigned char* qa = pqW + (jt * 32 * PQ + pt * 32 + 16 * q) * 2;
+          const unsigned char* qa = pqW + (jt * 32 * PQ + fcol + 16 * q) * 2;
           const bf16x8 qo = cat8(*(const bf16x4*)qa, *(const bf16x4*)(qa + 16));
           num[jt] = mfma32(sh[q], qo, num[jt]);
           num[jt] = mfma32(sl[q], qo, num[jt]);
@@ -571,52 +662,36 @@ __global__ __launch_bounds__(2 * D) void k_output_prf(PrefillParams p) {
     }
 #pragma unroll
     for (int jt = 0; jt < NJ; ++jt) {
-      if (DECAY) num[jt] *= fN[G::F_THETA + jt * 32];
+      if (DECAY) num[jt] *= fN[G8::F_THETA + jt * 32];
+      if (fh == 1) {
 #pragma unroll
-      for (int it = 0; it <= jt; ++it) {
-        const unsigned char* at = aR + (jt * (jt + 1) / 2 + it) * G::A_TILE;
+        for (int it = 0; it <= jt; ++it) {
+          const unsigned char* at = aR + (jt * (jt + 1) / 2 + it) * G::A_TILE;
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const int r0 = it * 32 + 16 * q;
-          const bf16x8 vv = cat8(lds_read_tr4((const __bf16*)(vT + r0 * PV * 2)),
-                                 lds_read_tr4((const __bf16*)(vT + (r0 + 4) * PV * 2)));
-          num[jt] = mfma32(vv, *(const bf16x8*)(at + 32 * q), num[jt]);
-          num[jt] = mfma32(vv, *(const bf16x8*)(at + 32 * q + ALO), num[jt]);
+          for (int q = 0; q < 2; ++q) {
+            const int r0 = it * 32 + 16 * q;
+            const bf16x8 vv = cat8(lds_read_tr4((const __bf16*)(vT + r0 * PV * 2)),
+                                   lds_read_tr4((const __bf16*)(vT + (r0 + 4) * PV * 2)));
+            num[jt] = mfma32(vv, *(const bf16x8*)(at + 32 * q), num[jt]);
+            num[jt] = mfma32(vv, *(const bf16x8*)(at + 32 * q + ALO), num[jt]);
+          }
         }
       }
-      float inv = 1.f;
-      if (NORM) {
-        float qz = 0.f;
-        const unsigned char* qr = pqZ + jt * 32 * PQ * 2;
-        const f32x4* zr = (const f32x4*)(sF + G::F_Z + hh * (NP / 2));
-#pragma unroll
-        for (int e8 = 0; e8 < NP / 2; e8 += 8) {
-          const bf16x8 qv = *(const bf16x8*)(qr + e8 * 2);
-          const f32x4 z0 = zr[e8 / 4], z1 = zr[e8 / 4 + 1];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) qz += from_bf16(qv[j]) * z0[j] + from_bf16(qv[4 + j]) * z1[j];
-        }
-        qz += __shfl_xor(qz, 32);
-        float r = 0.f;
-#pragma unroll
-        for (int it = 0; it <= jt; ++it) r += fN[G::F_R + (jt * (jt + 1) / 2 + it) * 32];
-        inv = 1.f / (fN[G::F_THETA + jt * 32] * qz + r + p.eps);
-      }
-      const uint32_t row_el = (uint32_t)(jt * 32 + n) * rse + Ew + 4 * hh;
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        store_out4<OBF>(ors, row_el + 8 * q4, num[jt][4 * q4] * inv, num[jt][4 * q4 + 1] * inv,
-                        num[jt][4 * q4 + 2] * inv, num[jt][4 * q4 + 3] * inv);
     }
-
-    // ---- state update: S <- gamma^L S + K~^T V, Z <- gamma^L Z + sum_i Xi_i psi(k_i)
+    lds_barrier();  // every wave is done with psi(Q): its region takes half 1's partial outputs
+    if (fh == 1) {
+#pragma unroll
+      for (int jt = 0; jt < NJ; ++jt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xch[((cb * NJ + jt) * 16 + r) * 64] = num[jt][r];
+    }
+    // K~ = Xi psi(K) with decay: rescale the hi + lo tile in place (every wave is done with the
+    // score operands), rows past L stay zero
     if (DECAY) {
-      lds_barrier();  // every wave is done with the score tiles and psi(K)
-      // K~ = Xi psi(K): rescale the hi + lo tile in place, rows past L stay zero
       constexpr int NCH = C * NP / 8;  // 8-element chunks of the tile
 #pragma unroll
-      for (int i = 0; i < NCH / G::NT; ++i) {
-        const int ch = tid + i * G::NT, row = ch / (NP / 8), col = (ch % (NP / 8)) * 8;
+      for (int i = 0; i < NCH / G8::NT; ++i) {
+        const int ch = tid + i * G8::NT, row = ch / (NP / 8), col = (ch % (NP / 8)) * 8;
         const float xi = row < L ? exp2f((float)(L - 1 - row) * lg) : 0.f;
         const int off = swzp<NP>(row, col) * 2;
         const bf16x8 h8 = *(const bf16x8*)(pk + off), l8 = *(const bf16x8*)(pk + off + LO);
@@ -629,20 +704,46 @@ __global__ __launch_bounds__(2 * D) void k_output_prf(PrefillParams p) {
         *(bf16x8*)(pk + off + LO) = lo;
       }
     }
-    lds_barrier();  // every wave is done reading Z_prev and psi(Q)
-    if (NORM && (n & 1) == 0) {
-      const int r = (n >> 1) & 15;
+    lds_barrier();
+    if (fh == 0) {
+      const __amdgpu_buffer_rsrc_t ors = make_rsrc(ob + (size_t)t0 * rse * OES, rows_extent(L, rse * OES, D * OES));
 #pragma unroll
-      for (int f = 0; f < FPW; ++f) {
-        const int fi = (w * FPW + f) * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-        sF[G::F_Z + fi] = a * sF[G::F_Z + fi] + zt[f];
+      for (int jt = 0; jt < NJ; ++jt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) num[jt][r] += xch[((cb * NJ + jt) * 16 + r) * 64];
+        float inv = 1.f;
+        if (NORM) {
+          // psi(q_j) . Z_prev (per feature tile, from the feature phase) and the score row sums
+          float qz = 0.f;
+#pragma unroll
+          for (int f = 0; f < NFT; ++f) qz += fN[G8::F_QZ + f * C + jt * 32];
+          float rr = 0.f;
+#pragma unroll
+          for (int it = 0; it <= jt; ++it) rr += fN[G8::F_R + (jt * (jt + 1) / 2 + it) * 32];
+          inv = 1.f / (fN[G8::F_THETA + jt * 32] * qz + rr + p.eps);
+        }
+        const uint32_t row_el = (uint32_t)(jt * 32 + n) * rse + Ew + 4 * hh;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          store_out4<OBF>(ors, row_el + 8 * q4, num[jt][4 * q4] * inv, num[jt][4 * q4 + 1] * inv,
+                          num[jt][4 * q4 + 2] * inv, num[jt][4 * q4 + 3] * inv);
+      }
+    }
+
+    // ---- state update: S <- gamma^L S + K~^T V (this wave's rows), Z <- gamma^L Z + sum_i Xi_i psi(k_i)
+    if (NORM) {
+      for (int f = tid; f < NP; f += G8::NT) {
+        float z = 0.f;
+#pragma unroll
+        for (int jt = 0; jt < NJ; ++jt) z += sF[G8::F_ZP + jt * NP + f];
+        sF[G8::F_Z + f] = a * sF[G8::F_Z + f] + z;
       }
     }
     if (DECAY) {
 #pragma unroll
-      for (int pt = 0; pt < NFT; ++pt) S[pt] *= a;
+      for (int pt = 0; pt < NFH; ++pt) S[pt] *= a;
     }
-    state_update_prf<C, D, NP, LO, PV>(S, kb8, vT);
+    state_update_half<C, NP, NFH, LO, PV>(S, kb8, vT, fh * NFH);
   }
 }
 
@@ -654,7 +755,7 @@ hipError_t launch_flags(const PrefillParams& p, hipStream_t s, bool out) {
                                         : (const void*)k_output_prf<C, D, NP, DECAY, NORM, true, false>)
                                   : (qs ? (const void*)k_output_prf<C, D, NP, DECAY, NORM, false, true>
                                         : (const void*)k_output_prf<C, D, NP, DECAY, NORM, false, false>);
-  const int lds = out ? Geo<C, D, NP, true>::LDS_BYTES : Geo<C, D, NP, false>::LDS_BYTES;
+  const int lds = out ? Geo8<C, D, NP>::LDS_BYTES : Geo8<C, D, NP>::SUM_LDS_BYTES;
   hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
   // x = (batch, head), y = segment: workgroups are dealt to the 8 XCDs round-robin by linear id
@@ -663,7 +764,7 @@ hipError_t launch_flags(const PrefillParams& p, hipStream_t s, bool out) {
   // heavy first segments would pile onto a few of them.
   dim3 grid(p.B * p.H, p.n_seg);
   void* args[] = {(void*)&p};
-  e = hipLaunchKernel(kern, grid, dim3(2 * D), args, lds, s);
+  e = hipLaunchKernel(kern, grid, dim3(Geo8<C, D, NP>::NT), args, lds, s);
   if (e != hipSuccess) return e;
   return hipGetLastError();
 }
