@@ -73,48 +73,6 @@ __device__ __forceinline__ int swzp(int row, int col) {
   return row * NP + ((((col >> 3) ^ swz<128>(row)) << 3) | (col & 7));
 }
 
-// Sum of x[0..15] over the 32 token lanes of each lane half: a halving butterfly.
-// Returns the total of register r = (n >> 1) & 15 (the same in lanes n and n ^ 1).
-__device__ __forceinline__ float lane_total16(const float (&x)[16], int n) {
-  float v8[8], v4[4], v2[2];
-  const bool b16 = n & 16, b8 = n & 8, b4 = n & 4, b2 = n & 2;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const float keep = b16 ? x[k + 8] : x[k], send = b16 ? x[k] : x[k + 8];
-    v8[k] = keep + __shfl_xor(send, 16);
-  }
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const float keep = b8 ? v8[k + 4] : v8[k], send = b8 ? v8[k] : v8[k + 4];
-    v4[k] = keep + __shfl_xor(send, 8);
-  }
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const float keep = b4 ? v4[k + 2] : v4[k], send = b4 ? v4[k] : v4[k + 2];
-    v2[k] = keep + __shfl_xor(send, 4);
-  }
-  float v = (b2 ? v2[1] : v2[0]) + __shfl_xor(b2 ? v2[0] : v2[1], 2);
-  return v + __shfl_xor(v, 1);
-}
-
-// Commit the raw pieces of one tile to LDS and record each row's squared norm.
-template <int C, int D>
-__device__ __forceinline__ void commit_raw_norm(const pf::Pieces<C, D>& P, unsigned char* dst, int pitch_bytes,
-                                                float* nrm, int prow, int tid) {
-  using PG = pf::Geo<C, D, true>;
-#pragma unroll
-  for (int i = 0; i < PG::NPC; ++i) {
-    *(uint4*)(dst + i * 16 * pitch_bytes) = P.r[i];
-    const bf16x8 x = __builtin_bit_cast(bf16x8, P.r[i]);
-    float sq = 0.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) sq += from_bf16(x[j]) * from_bf16(x[j]);
-#pragma unroll
-    for (int off = 1; off < PG::PPR; off <<= 1) sq += __shfl_xor(sq, off);
-    if (tid % PG::PPR == 0) nrm[prow + 16 * i] = sq;
-  }
-}
-
 // psi^T tile (M = feature ft*32 + 0..31, N = token jt*32 + 0..31, k = input dim) from a raw
 // tile at `raw` (per-lane base: token n, input dims 8 hh + ...).
 template <int D>
@@ -152,71 +110,23 @@ __device__ __forceinline__ void write_psik(unsigned char* pk, int t, int ft, int
   }
 }
 
-// Per-lane byte bases of the hot psi(K) reads (pinned, see pin). Score operand: token
-// row n, features 16 kk + 8 hh (kk < 8; kk + 8 lies 256 bytes further, as the swizzle
-// leaves chunk-index bit 4 alone). State-update operand (transpose reads): rows trow and
-// trow + 4, features 32 pt + tcol (pt < 4; pt + 4 lies 256 bytes further).
+// Per-lane byte bases of the score operand reads of psi(K) (pinned, see pin): token row n,
+// features 16 kk + 8 hh (kk < 8; kk + 8 lies 256 bytes further, as the swizzle leaves
+// chunk-index bit 4 alone).
 template <int NP>
 struct PsiKBases {
   const unsigned char* rw[8];
-  const unsigned char* tr[4][2];
 };
 template <int NP>
-__device__ __forceinline__ PsiKBases<NP> psik_bases(unsigned char* smem, int off_pk, int n, int hh, int trow,
-                                                    int tcol) {
+__device__ __forceinline__ PsiKBases<NP> psik_bases(unsigned char* smem, int off_pk, int n, int hh) {
   PsiKBases<NP> b;
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) b.rw[kk] = smem + pin(off_pk + swzp<NP>(n, 16 * kk + 8 * hh) * 2);
-#pragma unroll
-  for (int pt = 0; pt < 4; ++pt) {
-    b.tr[pt][0] = smem + pin(off_pk + swzp<NP>(trow, 32 * pt + tcol) * 2);
-    b.tr[pt][1] = smem + pin(off_pk + swzp<NP>(trow + 4, 32 * pt + tcol) * 2);
-  }
   return b;
 }
 template <int NP>
 __device__ __forceinline__ bf16x8 psik_row(const PsiKBases<NP>& b, int row0, int kk, int extra) {
   return *(const bf16x8*)(b.rw[kk & 7] + (kk >> 3) * 256 + row0 * NP * 2 + extra);
-}
-template <int NP>
-__device__ __forceinline__ bf16x8 psik_tr(const PsiKBases<NP>& b, int row0, int pt, int extra) {
-  const int o = (pt >> 2) * 256 + row0 * NP * 2 + extra;
-  return cat8(lds_read_tr4((const __bf16*)(b.tr[pt & 3][0] + o)), lds_read_tr4((const __bf16*)(b.tr[pt & 3][1] + o)));
-}
-
-// S[pt] += K~^T V over the chunk (M = feature, N = value column, k = token), software-
-// pipelined in steps of (16 tokens, up to 4 feature tiles): the operands of the next step
-// are read from LDS while the current step's MFMAs run.
-template <int C, int D, int NP, int LO, int PV>
-__device__ __forceinline__ void state_update_prf(f32x16 (&S)[NP / 32], const PsiKBases<NP>& kb8,
-                                                 const unsigned char* vT) {
-  constexpr int NFT = NP / 32, PTS = NFT < 4 ? NFT : 4, HALVES = NFT / PTS, NSTEP = (C / 16) * HALVES;
-  bf16x8 ops[2][1 + 2 * PTS];  // [buffer][V, then psi(K) hi, lo per feature tile of the step]
-  auto load_step = [&](bf16x8 (&o)[1 + 2 * PTS], int st) {
-    const int r0 = (st / HALVES) * 16, p0 = (st % HALVES) * PTS;
-    o[0] = cat8(lds_read_tr4((const __bf16*)(vT + r0 * PV * 2)), lds_read_tr4((const __bf16*)(vT + (r0 + 4) * PV * 2)));
-#pragma unroll
-    for (int j = 0; j < PTS; ++j) {
-      o[1 + 2 * j] = psik_tr<NP>(kb8, r0, p0 + j, 0);
-      o[2 + 2 * j] = psik_tr<NP>(kb8, r0, p0 + j, LO);
-    }
-  };
-  load_step(ops[0], 0);
-#pragma unroll
-  for (int st = 0; st < NSTEP; ++st) {
-    if (st + 1 < NSTEP) load_step(ops[(st + 1) & 1], st + 1);
-    const bf16x8(&o)[1 + 2 * PTS] = ops[st & 1];
-    const int p0 = (st % HALVES) * PTS;
-#pragma unroll
-    for (int j = 0; j < PTS; ++j) {
-      S[p0 + j] = mfma32(o[1 + 2 * j], o[0], S[p0 + j]);
-      S[p0 + j] = mfma32(o[2 + 2 * j], o[0], S[p0 + j]);
-    }
-    if (st + 1 < NSTEP) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * (1 + 2 * PTS), 0);  // next step's reads
-      __builtin_amdgcn_sched_group_barrier(0x008, 2 * PTS, 0);            // this step's MFMAs
-    }
-  }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -242,8 +152,7 @@ struct Geo8 {
   static constexpr int F_NQ = F_R + NTILE * 32;    // |q_t|^2 [C]
   static constexpr int F_NK = F_NQ + C;            // |k_t|^2 [C]
   static constexpr int F_QZ = F_NK + C;            // psi(q_t) . Z_prev per feature tile [NFT][C]
-  static constexpr int F_ZP = F_QZ + NFT * C;      // sum_i Xi_i psi(k_i) per token tile [NJ][NP]
-  static constexpr int F_QMAX = F_ZP + NJ * NP;    // max_p w_p . q_t per feature tile [NFT][C] (query shift)
+  static constexpr int F_QMAX = F_QZ + NFT * C;    // max_p w_p . q_t per feature tile [NFT][C] (query shift)
   static constexpr int LDS_BYTES = OFF_F + 4 * (F_QMAX + NFT * C);
   static constexpr int SUM_LDS_BYTES = Geo<C, D, NP, false>::OFF_F + 4 * F_QMAX;  // no Q tiles, no QMAX
   static_assert(JPW * NWV == NFT * NJ && JPW >= 1 && NJ % JPW == 0,
@@ -280,11 +189,34 @@ __device__ __forceinline__ void commit_raw_norm8(const pf::PiecesN<NPC>& P, unsi
   }
 }
 
-// S[pt] += K~^T V for this wave's state rows: feature tiles f0 + pt (pt < NFH), value columns
-// at vT; k = token, software-pipelined in 16-token steps.
-template <int C, int NP, int NFH, int LO, int PV>
-__device__ __forceinline__ void state_update_half(f32x16 (&S)[NFH], const PsiKBases<NP>& kb8, const unsigned char* vT,
-                                                  int f0) {
+// Per-lane bases of the state-update operand reads (transpose reads of psi(K): M = feature,
+// k = token) for the NFH feature tiles of one wave, its j-th tile being f0 + (j + rot) % NFH:
+// rows trow and trow + 4, features 32 tile + tcol. The rotation puts a different tile first
+// in each wave of a half, so that the first tile's column sums are spread over the waves.
+template <int NFH>
+struct StBases {
+  const unsigned char* tr[NFH][2];
+};
+template <int NP, int NFH>
+__device__ __forceinline__ StBases<NFH> st_bases(unsigned char* smem, int off_pk, int trow, int tcol, int f0, int rot) {
+  StBases<NFH> b;
+#pragma unroll
+  for (int j = 0; j < NFH; ++j) {
+    const int pt = f0 + (j + rot) % NFH;
+    b.tr[j][0] = smem + pin(off_pk + swzp<NP>(trow, 32 * pt + tcol) * 2);
+    b.tr[j][1] = smem + pin(off_pk + swzp<NP>(trow + 4, 32 * pt + tcol) * 2);
+  }
+  return b;
+}
+
+// S[j] += K~^T V over the chunk for the wave's feature tiles (see StBases), value columns at
+// vT (M = feature, N = value column, k = token), software-pipelined in 16-token steps.
+// With WZ, also z += 1 K~ for the first tile: an MFMA of an all-ones operand (M) with that
+// tile as the N operand, so every row of z holds the tile's column sums sum_i K~_i (lane n:
+// feature n of the tile).
+template <int C, int NP, int NFH, int LO, int PV, bool WZ>
+__device__ __forceinline__ void state_update_half(f32x16 (&S)[NFH], f32x16& z, const StBases<NFH>& sb,
+                                                  const unsigned char* vT) {
   constexpr int NK = C / 16;
   bf16x8 ops[2][1 + 2 * NFH];
   auto load_step = [&](bf16x8 (&o)[1 + 2 * NFH], int ik) {
@@ -292,10 +224,13 @@ __device__ __forceinline__ void state_update_half(f32x16 (&S)[NFH], const PsiKBa
     o[0] = cat8(lds_read_tr4((const __bf16*)(vT + r0 * PV * 2)), lds_read_tr4((const __bf16*)(vT + (r0 + 4) * PV * 2)));
 #pragma unroll
     for (int j = 0; j < NFH; ++j) {
-      o[1 + 2 * j] = psik_tr<NP>(kb8, r0, f0 + j, 0);
-      o[2 + 2 * j] = psik_tr<NP>(kb8, r0, f0 + j, LO);
+      const int o0 = r0 * NP * 2;
+      o[1 + 2 * j] = cat8(lds_read_tr4((const __bf16*)(sb.tr[j][0] + o0)), lds_read_tr4((const __bf16*)(sb.tr[j][1] + o0)));
+      o[2 + 2 * j] =
+          cat8(lds_read_tr4((const __bf16*)(sb.tr[j][0] + o0 + LO)), lds_read_tr4((const __bf16*)(sb.tr[j][1] + o0 + LO)));
     }
   };
+  const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
   load_step(ops[0], 0);
 #pragma unroll
   for (int ik = 0; ik < NK; ++ik) {
@@ -306,9 +241,13 @@ __device__ __forceinline__ void state_update_half(f32x16 (&S)[NFH], const PsiKBa
       S[j] = mfma32(o[1 + 2 * j], o[0], S[j]);
       S[j] = mfma32(o[2 + 2 * j], o[0], S[j]);
     }
+    if (WZ) {
+      z = mfma32(ones, o[1], z);
+      z = mfma32(ones, o[2], z);
+    }
     if (ik + 1 < NK) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * (1 + 2 * NFH), 0);  // next step's reads
-      __builtin_amdgcn_sched_group_barrier(0x008, 2 * NFH, 0);            // this step's MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * (1 + 2 * NFH), 0);     // next step's reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * NFH + (WZ ? 2 : 0), 0);  // this step's MFMAs
     }
   }
 }
@@ -339,7 +278,8 @@ __global__ __launch_bounds__(512) void k_summary_prf(PrefillParams p) {
   unsigned char* const vP = smem + pin(G::OFF_V + (prow * PV + pcol) * 2);
   const unsigned char* const vT = smem + pin(G::OFF_V + (trow * PV + Ew + tcol) * 2);
   float* const sF = (float*)(smem + pin(G::OFF_F));
-  const PsiKBases<NP> kb8 = psik_bases<NP>(smem, G::OFF_PK, n, hh, trow, tcol);
+  const int rot = cb % NFH;  // this wave's first feature tile is fh NFH + rot (its column sums give Z)
+  const StBases<NFH> sb = st_bases<NP, NFH>(smem, G::OFF_PK, trow, tcol, fh * NFH, rot);
 
   // W rows of this wave's feature tile as MFMA operands (M = feature, k = input dim)
   const uint16_t* Wh = (const uint16_t*)p.prf_w + (size_t)head * NP * D;
@@ -348,14 +288,10 @@ __global__ __launch_bounds__(512) void k_summary_prf(PrefillParams p) {
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) wop[kk] = *(const bf16x8*)(Wh + (size_t)(ft0 * 32 + n) * D + 16 * kk + 8 * hh);
 
-  f32x16 S[NFH];
+  f32x16 S[NFH];  // S[j]: feature tile fh NFH + (j + rot) % NFH, value columns Ew ..
 #pragma unroll
   for (int pt = 0; pt < NFH; ++pt) S[pt] = f32x16{};
-  float zacc[JPW][16];  // per-lane normaliser sums of this wave's jobs (its tokens), decayed to the segment end
-#pragma unroll
-  for (int u = 0; u < JPW; ++u)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) zacc[u][r] = 0.f;
+  f32x16 Zs = f32x16{};  // column sums of the first tile, decayed to the segment end (every row alike)
 
   const SeqSpan sq = seq_span(p, bh);
   const int T = sq.T, n_chunks = (T + C - 1) / C;
@@ -395,41 +331,28 @@ __global__ __launch_bounds__(512) void k_summary_prf(PrefillParams p) {
                             : __builtin_huge_valf();
       float v[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        v[r] = exp2f(acc[r] * LOG2E - h);
-        zacc[u][r] = zacc[u][r] * a + v[r];
-      }
+      for (int r = 0; r < 16; ++r) v[r] = exp2_hw(acc[r] * LOG2E - h);
       write_psik<NP, LO>(pk, t, ft, hh, v);
     }
     lds_barrier();
     if (DECAY) {
 #pragma unroll
       for (int pt = 0; pt < NFH; ++pt) S[pt] *= a;
+      Zs *= a;
     }
-    state_update_half<C, NP, NFH, LO, PV>(S, kb8, vT, fh * NFH);
+    state_update_half<C, NP, NFH, LO, PV, NORM>(S, Zs, sb, vT);
   }
   // segment summary -> workspace [bh][seg][E], E = NP*D + NP
   const size_t E = (size_t)NP * D + NP;
   float* out = p.ws + rec_index(p, bh, seg) * E;
 #pragma unroll
-  for (int pt = 0; pt < NFH; ++pt)
+  for (int pt = 0; pt < NFH; ++pt) {
+    const int tile = fh * NFH + (pt + rot) % NFH;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) out[(size_t)((fh * NFH + pt) * 32 + dtile_row(r, lane)) * D + Ew + n] = S[pt][r];
-  // normaliser: per feature, the sum over the token tiles' partials (one job per token tile)
-#pragma unroll
-  for (int u = 0; u < JPW; ++u) {
-    const int jb = w * JPW + u, ft = job_ft<NJ>(jb), jt = job_jt8<NJ>(jb);
-    const float z = lane_total16(zacc[u], n);
-    const int r = (n >> 1) & 15;
-    if ((n & 1) == 0) sF[G8::F_ZP + jt * NP + ft * 32 + 8 * (r >> 2) + 4 * hh + (r & 3)] = z;
+    for (int r = 0; r < 16; ++r) out[(size_t)(tile * 32 + dtile_row(r, lane)) * D + Ew + n] = S[pt][r];
   }
-  lds_barrier();
-  for (int f = tid; f < NP; f += G8::NT) {
-    float z = 0.f;
-#pragma unroll
-    for (int jt = 0; jt < NJ; ++jt) z += sF[G8::F_ZP + jt * NP + f];
-    out[(size_t)NP * D + f] = NORM ? z : 0.f;
-  }
+  // normaliser: the column sums of the first tile, from the waves whose first tiles cover the half
+  if (cb < NFH && hh == 0) out[(size_t)NP * D + (fh * NFH + rot) * 32 + n] = NORM ? Zs[0] : 0.f;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -462,25 +385,29 @@ __global__ __launch_bounds__(512) void k_output_prf(PrefillParams p) {
   const unsigned char* const vT = smem + pin(G::OFF_V + (trow * PV + Ew + tcol) * 2);
   unsigned char* const aW = smem + pin(G::OFF_A + (n * PA + 4 * hh) * 2);
   const unsigned char* const aR = smem + pin(G::OFF_A + (n * PA + 8 * hh) * 2);
-  float* const xch = (float*)(smem + pin(G8::OFF_X)) + lane;  // [cb][jt][r][lane] partial outputs
+  float* const xch = (float*)(smem + pin(G8::OFF_X)) + 4 * lane;  // [cb][jt][r / 4][lane][r % 4] partial outputs
   float* const sF = (float*)(smem + pin(G::OFF_F));
   float* const fN = (float*)(smem + pin(G::OFF_F + 4 * n));
-  const PsiKBases<NP> kb8 = psik_bases<NP>(smem, G::OFF_PK, n, hh, trow, tcol);
+  const PsiKBases<NP> kb8 = psik_bases<NP>(smem, G::OFF_PK, n, hh);
+  const int rot = cb % NFH;  // this wave's first feature tile is fh NFH + rot (its column sums give Z)
+  const StBases<NFH> sb = st_bases<NP, NFH>(smem, G::OFF_PK, trow, tcol, fh * NFH, rot);
 
-  const uint16_t* Wh = (const uint16_t*)p.prf_w + (size_t)head * NP * D;
-  const int ft0 = job_ft<NJ>(w * JPW);
-  bf16x8 wop[D / 16];
-#pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) wop[kk] = *(const bf16x8*)(Wh + (size_t)(ft0 * 32 + n) * D + 16 * kk + 8 * hh);
+  // this lane's row of W for the wave's feature tile (M = feature, k = input dim): read again each
+  // chunk (the head's bank stays in L2), so that the operands hold registers only until the
+  // feature GEMMs are done
+  const uint16_t* const wrow =
+      (const uint16_t*)p.prf_w + (size_t)head * NP * D + (size_t)(job_ft<NJ>(w * JPW) * 32 + n) * D + 8 * hh;
 
   // exclusive prefix state of this segment: this wave's rows and columns
   const size_t E = (size_t)NP * D + NP;
   const float* pre = p.ws + rec_index(p, bh, seg) * E;
-  f32x16 S[NFH];
+  f32x16 S[NFH];  // S[j]: feature tile fh NFH + (j + rot) % NFH, value columns Ew ..
 #pragma unroll
-  for (int pt = 0; pt < NFH; ++pt)
+  for (int pt = 0; pt < NFH; ++pt) {
+    const int tile = fh * NFH + (pt + rot) % NFH;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) S[pt][r] = pre[(size_t)((fh * NFH + pt) * 32 + dtile_row(r, lane)) * D + Ew + n];
+    for (int r = 0; r < 16; ++r) S[pt][r] = pre[(size_t)(tile * 32 + dtile_row(r, lane)) * D + Ew + n];
+  }
   for (int j = tid; j < NP; j += G8::NT) sF[G8::F_Z + j] = NORM ? pre[(size_t)NP * D + j] : 0.f;
   for (int j = tid; j < C; j += G8::NT) sF[G8::F_THETA + j] = DECAY ? exp2f((float)(j + 1) * lg) : 1.f;
 
@@ -505,6 +432,9 @@ __global__ __launch_bounds__(512) void k_output_prf(PrefillParams p) {
   for (int c = c0; c < c1; ++c) {
     const int t0 = c * C, L = min(C, T - t0);
     const float a = DECAY ? exp2f((float)L * lg) : 1.f;
+    bf16x8 wop[D / 16];
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) wop[kk] = *(const bf16x8*)(wrow + 16 * kk);
     lds_barrier();  // the previous chunk is done with LDS (and Z is updated)
     commit_raw_norm8<D, NPC, RSTEP>(pq_, rqP, PR * 2, sF + G8::F_NQ, prow, tid);
     commit_raw_norm8<D, NPC, RSTEP>(pk_, rqP + G::RAW, PR * 2, sF + G8::F_NK, prow, tid);
@@ -536,7 +466,7 @@ __global__ __launch_bounds__(512) void k_output_prf(PrefillParams p) {
     }
 
     // ---- features of this wave's jobs: psi(Q) rounded to bf16 (and its dot with Z_prev per
-    // token); psi(K) as hi + lo, zero past the sequence end (and its Xi-weighted sum per feature)
+    // token); psi(K) as hi + lo, zero past the sequence end
 #pragma unroll
     for (int u = 0; u < JPW; ++u) {
       const int jb = w * JPW + u, ft = job_ft<NJ>(jb), jt = job_jt8<NJ>(jb);
@@ -552,7 +482,7 @@ __global__ __launch_bounds__(512) void k_output_prf(PrefillParams p) {
         const float h = qshift * LOG2E - log2_rsqrt;
         float v[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) v[r] = exp2f(acc[r] * LOG2E - h);
+        for (int r = 0; r < 16; ++r) v[r] = exp2_hw(acc[r] * LOG2E - h);
         float qz = 0.f;
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
@@ -572,26 +502,47 @@ __global__ __launch_bounds__(512) void k_output_prf(PrefillParams p) {
       }
       {
         const f32x16 acc = feature_gemm<D>(wop, rR + G::RAW, jt, PR * 2);
-        const bool live = t < L;
-        const float h = live ? 0.5f * sF[G8::F_NK + t] * LOG2E - log2_rsqrt : __builtin_huge_valf();
-        const float xi = (DECAY && live) ? exp2f((float)(L - 1 - t) * lg) : 1.f;
-        float v[16], vz[16];
+        const float h = t < L ? 0.5f * sF[G8::F_NK + t] * LOG2E - log2_rsqrt : __builtin_huge_valf();
+        float v[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          v[r] = exp2f(acc[r] * LOG2E - h);
-          vz[r] = DECAY ? v[r] * xi : v[r];
-        }
-        if (NORM) {
-          const float z = lane_total16(vz, n);
-          const int r = (n >> 1) & 15;
-          if ((n & 1) == 0) sF[G8::F_ZP + jt * NP + ft * 32 + 8 * (r >> 2) + 4 * hh + (r & 3)] = z;
-        }
+        for (int r = 0; r < 16; ++r) v[r] = exp2_hw(acc[r] * LOG2E - h);
         write_psik<NP, LO>(pk, t, ft, hh, v);
       }
     }
     lds_barrier();  // features complete; the raw tiles are dead (the score tiles alias them)
 
-    // ---- score tile w (M = i, N = j, k = feature), masked, decayed, split into hi + lo
+    // ---- outputs, transposed: numT[e][j] (M = value column, N = token). The inter-chunk part
+    // over this wave's half of the features: S_prev^T psi(Q)^T, S_prev as hi + lo
+    f32x16 num[NJ];
+#pragma unroll
+    for (int jt = 0; jt < NJ; ++jt) num[jt] = f32x16{};
+    auto inter = [&]() {
+#pragma unroll
+      for (int pt = 0; pt < NFH; ++pt) {
+        bf16x8 sh[2], sl[2];  // k in the D-tile feedback order
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          float x[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) x[j] = S[pt][8 * q + j];
+          split8_trunc(x, sh[q], sl[q]);
+        }
+        const int fcol = (fh * NFH + (pt + rot) % NFH) * 32;
+#pragma unroll
+        for (int jt = 0; jt < NJ; ++jt)
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const unsigned char* qa = pqW + (jt * 32 * PQ + fcol + 16 * q) * 2;
+            const bf16x8 qo = cat8(*(const bf16x4*)qa, *(const bf16x4*)(qa + 16));
+            num[jt] = mfma32(sh[q], qo, num[jt]);
+            num[jt] = mfma32(sl[q], qo, num[jt]);
+          }
+      }
+    };
+
+    // ---- score tile w (M = i, N = j, k = feature), masked, decayed, split into hi + lo. (The
+    // other waves could take their inter-chunk part meanwhile, but holding its accumulators
+    // across the score code pushes this kernel past 256 registers.)
     if (w < G8::NTILE) {
       const int tt = w, jt = pf::tile_jt(tt), it = tt - jt * (jt + 1) / 2;
       f32x16 acc = f32x16{};
@@ -634,32 +585,8 @@ __global__ __launch_bounds__(512) void k_output_prf(PrefillParams p) {
     }
     lds_barrier();
 
-    // ---- outputs, transposed: numT[e][j] (M = value column, N = token); this wave's half of the
-    // features, theta-weighted; half 1 adds the intra-chunk term V^T A^T
-    f32x16 num[NJ];
-#pragma unroll
-    for (int jt = 0; jt < NJ; ++jt) num[jt] = f32x16{};
-#pragma unroll
-    for (int pt = 0; pt < NFH; ++pt) {
-      bf16x8 sh[2], sl[2];  // S_prev[pt] as hi + lo, k in the D-tile feedback order
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        float x[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) x[j] = S[pt][8 * q + j];
-        split8_trunc(x, sh[q], sl[q]);
-      }
-      const int fcol = (fh * NFH + pt) * 32;
-#pragma unroll
-      for (int jt = 0; jt < NJ; ++jt)
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const unsigned char* qa = pqW + (jt * 32 * PQ + fcol + 16 * q) * 2;
-          const bf16x8 qo = cat8(*(const bf16x4*)qa, *(const bf16x4*)(qa + 16));
-          num[jt] = mfma32(sh[q], qo, num[jt]);
-          num[jt] = mfma32(sl[q], qo, num[jt]);
-        }
-    }
+    // ---- the inter-chunk part; theta weights; half 1 adds the intra-chunk term V^T A^T
+    inter();
 #pragma unroll
     for (int jt = 0; jt < NJ; ++jt) {
       if (DECAY) num[jt] *= fN[G8::F_THETA + jt * 32];
@@ -678,12 +605,17 @@ __global__ __launch_bounds__(512) void k_output_prf(PrefillParams p) {
         }
       }
     }
-    lds_barrier();  // every wave is done with psi(Q): its region takes half 1's partial outputs
-    if (fh == 1) {
+    // ---- the halves' partial outputs meet: half h completes token tile jt = h of its value
+    // columns, taking the other half's partial of that tile through LDS, so that every wave
+    // stores the same number of rows (and the next chunk's loads are not held behind stores)
+    static_assert(NJ == 2, "one token tile per feature half");
+    lds_barrier();  // every wave is done with psi(Q) and the score tiles: their region takes the partials
+    f32x16 mine = fh ? num[1] : num[0];
+    {
+      const f32x16 give = fh ? num[0] : num[1];
+      f32x4* const xo = (f32x4*)(xch + ((cb * NJ + (1 - fh)) * 16) * 64);
 #pragma unroll
-      for (int jt = 0; jt < NJ; ++jt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) xch[((cb * NJ + jt) * 16 + r) * 64] = num[jt][r];
+      for (int q = 0; q < 4; ++q) xo[q * 64] = f32x4{give[4 * q], give[4 * q + 1], give[4 * q + 2], give[4 * q + 3]};
     }
     // K~ = Xi psi(K) with decay: rescale the hi + lo tile in place (every wave is done with the
     // score operands), rows past L stay zero
@@ -705,45 +637,45 @@ __global__ __launch_bounds__(512) void k_output_prf(PrefillParams p) {
       }
     }
     lds_barrier();
-    if (fh == 0) {
-      const __amdgpu_buffer_rsrc_t ors = make_rsrc(ob + (size_t)t0 * rse * OES, rows_extent(L, rse * OES, D * OES));
+    {
+      const int jt = fh;
+      const f32x4* const xi4 = (const f32x4*)(xch + ((cb * NJ + jt) * 16) * 64);
 #pragma unroll
-      for (int jt = 0; jt < NJ; ++jt) {
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 o4 = xi4[q * 64];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) num[jt][r] += xch[((cb * NJ + jt) * 16 + r) * 64];
-        float inv = 1.f;
-        if (NORM) {
-          // psi(q_j) . Z_prev (per feature tile, from the feature phase) and the score row sums
-          float qz = 0.f;
-#pragma unroll
-          for (int f = 0; f < NFT; ++f) qz += fN[G8::F_QZ + f * C + jt * 32];
-          float rr = 0.f;
-#pragma unroll
-          for (int it = 0; it <= jt; ++it) rr += fN[G8::F_R + (jt * (jt + 1) / 2 + it) * 32];
-          inv = 1.f / (fN[G8::F_THETA + jt * 32] * qz + rr + p.eps);
-        }
-        const uint32_t row_el = (uint32_t)(jt * 32 + n) * rse + Ew + 4 * hh;
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-          store_out4<OBF>(ors, row_el + 8 * q4, num[jt][4 * q4] * inv, num[jt][4 * q4 + 1] * inv,
-                          num[jt][4 * q4 + 2] * inv, num[jt][4 * q4 + 3] * inv);
+        for (int e = 0; e < 4; ++e) mine[4 * q + e] += o4[e];
       }
+      float inv = 1.f;
+      if (NORM) {
+        // psi(q_j) . Z_prev (per feature tile, from the feature phase) and the score row sums
+        float qz = 0.f;
+#pragma unroll
+        for (int f = 0; f < NFT; ++f) qz += fN[G8::F_QZ + f * C + jt * 32];
+        float rr = fN[G8::F_R + (jt * (jt + 1) / 2) * 32];
+        if (jt) rr += fN[G8::F_R + 2 * 32];
+        inv = 1.f / (fN[G8::F_THETA + jt * 32] * qz + rr + p.eps);
+      }
+      const __amdgpu_buffer_rsrc_t ors = make_rsrc(ob + (size_t)t0 * rse * OES, rows_extent(L, rse * OES, D * OES));
+      const uint32_t row_el = (uint32_t)(jt * 32 + n) * rse + Ew + 4 * hh;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        store_out4<OBF>(ors, row_el + 8 * q4, mine[4 * q4] * inv, mine[4 * q4 + 1] * inv, mine[4 * q4 + 2] * inv,
+                        mine[4 * q4 + 3] * inv);
     }
 
-    // ---- state update: S <- gamma^L S + K~^T V (this wave's rows), Z <- gamma^L Z + sum_i Xi_i psi(k_i)
-    if (NORM) {
-      for (int f = tid; f < NP; f += G8::NT) {
-        float z = 0.f;
-#pragma unroll
-        for (int jt = 0; jt < NJ; ++jt) z += sF[G8::F_ZP + jt * NP + f];
-        sF[G8::F_Z + f] = a * sF[G8::F_Z + f] + z;
-      }
-    }
+    // ---- state update: S <- gamma^L S + K~^T V (this wave's rows); Z <- gamma^L Z + 1 K~, from
+    // the column sums the waves take of their first tiles (read again only in the next chunk)
     if (DECAY) {
 #pragma unroll
       for (int pt = 0; pt < NFH; ++pt) S[pt] *= a;
     }
-    state_update_half<C, NP, NFH, LO, PV>(S, kb8, vT, fh * NFH);
+    f32x16 zc = f32x16{};
+    state_update_half<C, NP, NFH, LO, PV, NORM>(S, zc, sb, vT);
+    if (NORM && cb < NFH && hh == 0) {
+      float* const zf = sF + G8::F_Z + (fh * NFH + rot) * 32 + n;
+      *zf = a * *zf + zc[0];
+    }
   }
 }
 
