@@ -249,6 +249,21 @@ __device__ __forceinline__ float gpow(float log2g, float n) { return log2g == 0.
 
 __device__ __forceinline__ float elu1(float x) { return x > 0.f ? x + 1.f : __expf(x); }
 
+// Sum over each DPP row of 16 lanes (lanes 16r .. 16r + 15), left in every lane of the row:
+// adds whose second operand is a DPP view (quad permutations, then the half-row and row
+// mirrors), so no LDS-routed lane permutes.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_mov<0x141>(v);  // row_half_mirror: lane i of 8 <- lane 7 - i
+  v += dpp_mov<0x140>(v);  // row_mirror: lane i of 16 <- lane 15 - i
+  return v;
+}
+
 // 2^x by the hardware instruction alone (about 1 ulp), without the library's rescaling of
 // arguments below -126: results under the smallest normal float flush to zero. Used for
 // feature values, where such a value is lost against the fp32 rounding of any sum it enters;

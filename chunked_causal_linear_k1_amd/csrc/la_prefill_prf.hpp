@@ -182,8 +182,8 @@ __device__ __forceinline__ void commit_raw_norm8(const pf::PiecesN<NPC>& P, unsi
       float sq = 0.f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) sq += from_bf16(x[j]) * from_bf16(x[j]);
-#pragma unroll
-      for (int off = 1; off < PPR; off <<= 1) sq += __shfl_xor(sq, off);
+      static_assert(PPR == 16, "one token row per DPP row");
+      sq = row16_sum(sq);
       if (tid % PPR == 0) nrm[prow + RSTEP * i] = sq;
     }
   }
