@@ -29,7 +29,7 @@ EXPORTED = ("lin_attn_prefill_workspace_size", "lin_attn_prefill", "lin_attn_pre
             "lin_attn_prefill_gated_workspace_size", "lin_attn_prefill_backward",
             "lin_attn_prefill_backward_workspace_size", "lin_attn_prefill_backward_varlen",
             "lin_attn_prefill_backward_varlen_workspace_size", "lin_attn_decode_step", "lin_attn_decode_step_gated",
-            "lin_attn_status_string", "lin_attn_version", "lin_attn_prefill_noalloc")
+            "lin_attn_status_string", "lin_attn_version", "lin_attn_prefill_noalloc", "lin_attn_scan_depth")
 NOALLOC_SCRATCH_BYTES = 64 << 20  # LA_NOALLOC_SCRATCH_BYTES
 
 
@@ -104,6 +104,8 @@ def load() -> ctypes.CDLL:
         lib.lin_attn_prefill_noalloc.restype = ctypes.c_int
         lib.lin_attn_prefill_noalloc.argtypes = [ctypes.POINTER(PrefillDesc), vp, vp, vp, fp, vp, vp, vp, vp, vp, vp,
                                                  vp]
+        lib.lin_attn_scan_depth.restype = ctypes.c_int
+        lib.lin_attn_scan_depth.argtypes = [ctypes.c_int32, vp, vp, vp]
         lib.lin_attn_status_string.restype = ctypes.c_char_p
         lib.lin_attn_status_string.argtypes = [ctypes.c_int]
         lib.lin_attn_version.restype = ctypes.c_char_p
@@ -118,6 +120,19 @@ def status_string(status: int) -> str:
 
 def version() -> str:
     return load().lin_attn_version().decode()
+
+
+def scan_depth(n_seg: int) -> int:
+    """lin_attn_scan_depth: the longest chain of dependent combine steps of the segment scan
+    over n_seg segments, as the kernel counts it while it runs."""
+    ws = torch.zeros(max(1, n_seg) * 20, dtype=torch.float32, device="cuda")
+    rounds = torch.zeros(1, dtype=torch.int32, device="cuda")
+    st = load().lin_attn_scan_depth(int(n_seg), ws.data_ptr(), rounds.data_ptr(),
+                                    torch.cuda.current_stream().cuda_stream)
+    if st != 0:
+        raise RuntimeError(f"lin_attn_scan_depth: {status_string(st)}")
+    torch.cuda.synchronize()
+    return int(rounds.item())
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:

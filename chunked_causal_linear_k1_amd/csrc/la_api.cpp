@@ -64,10 +64,11 @@ la_status validate_prefill_desc(const la_prefill_desc* d, bool gated = false) {
   // scaled by the query's exp(-max log-feature), a different function from plain PRF's
   if (d->psi == LA_PSI_PRF_QSHIFT && !d->normalize) return LA_ERR_UNSUPPORTED;
   if (d->d_v % 4 != 0 || d->n_psi % 4 != 0) return LA_ERR_UNSUPPORTED;  // 16-byte state rows
-  // element counts must fit comfortably in 64-bit offsets and the grid's y extent
+  // element counts must fit comfortably in 64-bit offsets; sequences go on the grid's x
+  // extent (segments and element blocks on y, each capped at 65535 by the planner)
   const double tokens = (double)d->B * d->H * d->T;
   if (tokens * std::max(d->d_k, d->d_v) > 9.0e15) return LA_ERR_SHAPE;
-  if ((long long)d->B * d->H > 65535) return LA_ERR_UNSUPPORTED;
+  if ((long long)d->B * d->H > 2147483647LL) return LA_ERR_SHAPE;
   // one chunk of one head spans (C - 1) * H + 1 rows in the interleaved layout: its byte
   // extent must fit a buffer resource's 32-bit range
   if (d->layout == LA_LAYOUT_BTHD && (double)d->chunk * d->H * std::max(d->d_k, d->d_v) * 4 >= 2147483648.0)
@@ -603,6 +604,13 @@ la_status lin_attn_prefill_gated(const la_prefill_desc* d, const void* q, const 
   if (!log_gate) return LA_ERR_NULL;
   return prefill_impl(d, nullptr, 0, q, k, v, nullptr, nullptr, init_S, init_Z, o, final_S, final_Z, workspace,
                       workspace_bytes, stream, nullptr, log_gate);
+}
+
+la_status lin_attn_scan_depth(int32_t n_seg, float* ws, int32_t* rounds, hipStream_t stream) {
+  if (!ws || !rounds) return LA_ERR_NULL;
+  if (n_seg < 1 || n_seg > 65535) return LA_ERR_SHAPE;
+  if (!aligned16(ws)) return LA_ERR_ALIGN;
+  return la::scan_depth_probe(n_seg, ws, rounds, stream) == hipSuccess ? LA_OK : LA_ERR_HIP;
 }
 
 }  // extern "C"

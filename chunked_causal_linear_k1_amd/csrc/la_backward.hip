@@ -28,12 +28,13 @@
 // each segment's adjoint summary sum_t gamma^(t - start + 1) g_t dnum_t^T; the segment scan
 // run in reverse order turns those into the adjoint state after each segment.
 //
-// Both kernels: one workgroup of four waves per (sequence, segment), d_k = d_v = n_psi =
-// 128, bf16 operands on MFMA 32x32x16 with fp32 accumulation; every operand that is not
+// Both kernels: one workgroup of eight waves per (sequence, segment), split into two
+// groups of four with different roles (see each kernel), d_k = d_v = n_psi = 128, bf16
+// operands on MFMA 32x32x16 with fp32 accumulation; every operand that is not
 // exact in bf16 (the states, scaled features, dNum, the C x C tiles, elu+1 keys) is a
 // two-term hi + lo expansion (psi(q) included, unlike the forward output pass: the adjoint
 // state sums psi(q) against signed upstream gradients without averaging the rounding out).
-// Wave w owns the 32 columns [32w, 32w + 32) of each output.
+// Wave w of a group owns the 32 columns [32w, 32w + 32) of the outputs that group produces.
 #include "la_device.hpp"
 #include "la_kernels.hpp"
 
@@ -42,7 +43,6 @@ namespace {
 
 constexpr int BC = 64;    // tokens per step
 constexpr int BD = 128;   // d_k = d_v = n_psi
-constexpr int BNT = 256;  // four waves
 constexpr int TP = BD + 8;  // pitch (elements) of the C x D bf16 tiles
 constexpr int SQ = BC + 8;  // pitch of the C x C bf16 tiles
 

@@ -71,6 +71,8 @@ struct ScanParams {
                          // the backward pass); the prefix of segment s then folds segments > s
   int has_decay;
   float log2g[LA_MAX_DECAY_HEADS];
+  int* rounds = nullptr;  // diagnostic record when set: the length of the scan's longest chain of
+                          // dependent (+) steps (device int, raised by atomic max)
 };
 
 // Backward pass of the prefill: the forward problem plus the upstream gradient, the gradient
@@ -153,6 +155,9 @@ hipError_t launch_prefill_f32_summary(const PrefillParams& p, hipStream_t s);
 hipError_t launch_prefill_f32_output(const PrefillParams& p, hipStream_t s);
 
 hipError_t launch_segment_scan(const ScanParams& p, hipStream_t s);
+// The scan over n_seg segments of a one-sequence problem with 4 x 4 states in ws (n_seg x 20
+// floats, contents arbitrary), recording its longest (+) chain in *rounds (device int).
+hipError_t scan_depth_probe(int n_seg, float* ws, int* rounds, hipStream_t s);
 
 bool prefill_gated_supported(int C, int d_k, int d_v, int n_psi, int psi);
 hipError_t launch_prefill_gated(const PrefillParams& p, hipStream_t s, bool out);

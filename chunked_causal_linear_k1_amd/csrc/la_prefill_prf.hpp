@@ -1,28 +1,30 @@
 // la_prefill_prf.hpp -- chunkwise causal linear attention with positive random features,
 // bf16 inputs, fp32 state, MFMA 32x32x16 bf16 -> fp32 on gfx950.
 //
-// Feature map ("Rethinking Attention with Performers" / the positive-random-feature
-// estimator of the softmax kernel, as restated on the linear-attention pages):
+// Feature map ("Linearized 2-Simplicial Attention", section 3.2, positive random features
+// for one tensor mode; appendix B.2 for the log-space query shift):
 //   psi(x)_f = exp(w_f . x - |x|^2 / 2) / sqrt(n_psi),   f = 0 .. n_psi - 1,
 // one bank W [n_psi, d] per head. The chunkwise method is the one of the identity / elu+1
 // kernels (la_prefill_bf16.hpp): per chunk c with L real tokens
 //   A_ji = (psi(q_j) . psi(k_i)) gamma^(j-i) [i <= j],
 //   o_j  = (gamma^(j+1) psi(q_j) S_prev + sum_i A_ji v_i) / (gamma^(j+1) psi(q_j) . Z_prev + sum_i A_ji + eps),
 //   S_next = gamma^L S_prev + sum_i gamma^(L-1-i) psi(k_i) v_i^T   (Z likewise),
-// with an n_psi x d_v state. Here the features are computed on chip from the raw tiles:
-// psi^T = W X^T is an MFMA GEMM per chunk (M = feature, N = token, k = input dim), with
-// W's operand tiles for the wave's features held in registers for the whole segment.
+// with an n_psi x d_v state. The features are computed on chip from the raw tiles:
+// psi^T = W X^T is an MFMA GEMM per chunk (M = feature, N = token, k = input dim).
 // Computing it transposed leaves each lane with one token and runs of 4 features, so
 // |x|^2, the decay Xi and the padding mask are lane scalars, and the features go to LDS
-// as 8-byte runs of a [token][feature] tile.
+// as 8-byte runs of a [token][feature] tile. The exponentials are the bare hardware 2^x:
+// features below the smallest normal float become zero.
 //
 // Precision: psi(K) is kept as hi + lo (two bf16 terms) in the scores and in the state
 // update, S as hi + lo in psi(Q) S, the score tiles as hi + lo; psi(Q) is rounded to
 // bf16 once and the same rounded values feed numerator and denominator.
 //
-// Work split: wave w owns value columns [32w, 32w + 32) of S and of the outputs (as in the
-// other kernels) and feature tiles [w FPW, (w + 1) FPW) of the feature GEMM, so each
-// feature's normaliser total is formed inside one wave (a butterfly over its token lanes).
+// Work split (eight waves, two per SIMD): wave w = (cb, fh) with cb = w % 4, fh = w / 4
+// owns value columns [32 cb, 32 cb + 32) and feature half fh of the fp32 state; the feature
+// GEMMs are (feature tile, token tile) jobs dealt over the waves; three waves compute the
+// three score tiles; the two halves' partial outputs meet through LDS, each half finishing
+// one token tile. Z comes from MFMA column sums inside the state update.
 #pragma once
 #include "la_prefill_bf16.hpp"
 

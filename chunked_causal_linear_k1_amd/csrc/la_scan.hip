@@ -53,12 +53,12 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_segment_scan(ScanParams p) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int w = wid % W, grp = wid / W, n_grp = (blockDim.x >> 6) / W;
   const int o = grp * W;  // this element group's LDS slots
-  const int bh = blockIdx.y, head = bh % p.H;
+  const int bh = blockIdx.x, head = bh % p.H;  // sequences on x (no 65535 cap), element blocks on y
   const size_t SE = (size_t)p.n_psi * p.d_v;
   const size_t E = SE + p.n_psi;  // scanned elements; a multiple of 4 (n_psi and d_v are)
   // segment record: S, Z, then (gated) the segment's per-row decay vector
   const size_t REC = E + (p.gated ? p.n_psi : 0);
-  const size_t e = (((size_t)blockIdx.x * n_grp + grp) * 64 + lane) * 4;
+  const size_t e = (((size_t)blockIdx.y * n_grp + grp) * 64 + lane) * 4;
   const bool live = e < E;
   const float lg = p.has_decay ? p.log2g[head] : 0.f;
   // scan position i is segment seg_of(i): the same segment in forward order, mirrored in reverse
@@ -90,6 +90,10 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_segment_scan(ScanParams p) {
     return f32x4{a, a, a, a};
   };
 
+  // Length of this wave's chain of dependent (+) steps, for the diagnostic record: its run's
+  // fold, the tree's levels up and down, the carry of the initial state, the run's rewrite.
+  int chain = 2 * max(0, s1 - s0) + 1;
+
   // 1. fold the run: total = X_s0 (+) ... (+) X_{s1-1}
   f32x4 run[RUN > 0 ? RUN : 1];
   f32x4 tx = {0.f, 0.f, 0.f, 0.f};
@@ -119,6 +123,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_segment_scan(ScanParams p) {
 
   // 2. Blelloch over the W wave totals (W is a power of two)
   for (int d = 1; d < W; d <<= 1) {  // up-sweep: node right <- left (+) right
+    ++chain;
     const int right = (w + 1) * 2 * d - 1;
     const bool act = right < W;
     f32x4 nx = {0.f, 0.f, 0.f, 0.f};
@@ -141,6 +146,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_segment_scan(ScanParams p) {
   }
   __syncthreads();
   for (int d = W >> 1; d >= 1; d >>= 1) {  // down-sweep
+    ++chain;
     const int right = (w + 1) * 2 * d - 1;
     f32x4 lx = {0.f, 0.f, 0.f, 0.f}, px = {0.f, 0.f, 0.f, 0.f};
     f32x4 la_ = {1.f, 1.f, 1.f, 1.f}, pa = {1.f, 1.f, 1.f, 1.f};
@@ -195,6 +201,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_segment_scan(ScanParams p) {
       }
     }
   }
+  if (p.rounds && lane == 0 && grp == 0 && blockIdx.y == 0) atomicMax(p.rounds, chain);
   // 5. the wave holding the last segment writes the final state
   if (live && s1 == p.n_seg && s0 < s1) {
     if (e < SE) {
@@ -207,12 +214,26 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_segment_scan(ScanParams p) {
 
 }  // namespace
 
+hipError_t scan_depth_probe(int n_seg, float* ws, int* rounds, hipStream_t s) {
+  ScanParams p{};
+  p.ws = ws;
+  p.init_S = p.init_Z = nullptr;
+  p.final_S = p.final_Z = nullptr;
+  p.cu_seqlens = nullptr;
+  p.BH = p.H = 1;
+  p.T = p.n_seg = n_seg;
+  p.seg_len = 1;
+  p.n_psi = p.d_v = 4;
+  p.rounds = rounds;
+  return launch_segment_scan(p, s);
+}
+
 hipError_t launch_segment_scan(const ScanParams& p, hipStream_t s) {
   const int W = scan_seg_waves(p.n_seg);
   const int G = W < kMinGroupWaves ? kMinGroupWaves / W : 1;  // element groups per workgroup
   const int per = (p.n_seg + W - 1) / W;
   const size_t E = (size_t)p.n_psi * p.d_v + p.n_psi;
-  dim3 grid((unsigned)((E + 256 * G - 1) / (256 * G)), p.BH);
+  dim3 grid(p.BH, (unsigned)((E + 256 * G - 1) / (256 * G)));
   const dim3 block(64 * W * G);
   if (per <= 4)
     hipLaunchKernelGGL(k_segment_scan<4>, grid, block, 0, s, p);

@@ -364,6 +364,19 @@ la_status lin_attn_decode_step_gated(const la_decode_desc* d, const void* q, con
                                      const float* log_gate, const void* prf_w, float* S, float* Z, void* o,
                                      hipStream_t stream);
 
+/* Diagnostic: the depth of the segment scan ("Log-Depth Chunked Linear-Attention Scan",
+ * Verification: the scan's round count is the check of its log depth). Runs the scan the
+ * prefill runs, on one sequence of n_seg segments with 4 x 4 states, and raises *rounds to
+ * the length of its longest chain of dependent (+) steps: each wave folds a run of up to
+ * ceil(n_seg / W) segments (W waves, a power of two <= 16), a Blelloch tree takes log2 W
+ * levels up and log2 W down, one step carries the initial state, and the run is rewritten
+ * with its prefixes, so rounds = 2 ceil(n_seg / W) + 2 log2 W + 1.
+ *   ws:     device fp32, n_seg * 20 floats, 16-byte aligned; overwritten (contents arbitrary).
+ *   rounds: device int32, set by the caller (e.g. to 0) before the call; raised by atomic max.
+ * Errors: LA_ERR_NULL, LA_ERR_SHAPE (n_seg outside 1 .. 65535), LA_ERR_ALIGN, LA_ERR_HIP.
+ * Asynchronous on `stream`. */
+la_status lin_attn_scan_depth(int32_t n_seg, float* ws, int32_t* rounds, hipStream_t stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* lin_attn_status_string(la_status s);
 

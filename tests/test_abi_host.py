@@ -369,3 +369,24 @@ def test_decay_head_limit():
                     out_dtype=LA_F32)
     assert lib.lin_attn_decode_step(ctypes.byref(dd), fake, fake, fake, g257, None, fake, None, fake,
                                     None) == LA_ERR_UNSUPPORTED
+
+
+def test_sequence_count_beyond_grid_y_extent():
+    """B x H is not capped at 65535: sequences go on the grid's x extent (2^31 - 1)."""
+    lib = binding.load()
+    for B, H in ((70000, 1), (4096, 64)):
+        d = _desc(B=B, H=H, T=100, chunk=64, psi=0, normalize=0)
+        nbytes = ctypes.c_size_t(0)
+        assert lib.lin_attn_prefill_workspace_size(ctypes.byref(d), ctypes.byref(nbytes)) == 0, (B, H)
+        assert nbytes.value > 0
+
+
+def test_scan_depth_validation():
+    """lin_attn_scan_depth checks its arguments before any launch."""
+    lib = binding.load()
+    fake = ctypes.c_void_p(1 << 20)
+    assert lib.lin_attn_scan_depth(8, None, fake, None) == LA_ERR_NULL
+    assert lib.lin_attn_scan_depth(8, fake, None, None) == LA_ERR_NULL
+    assert lib.lin_attn_scan_depth(0, fake, fake, None) == LA_ERR_SHAPE
+    assert lib.lin_attn_scan_depth(65536, fake, fake, None) == LA_ERR_SHAPE
+    assert lib.lin_attn_scan_depth(8, ctypes.c_void_p((1 << 20) + 8), fake, None) == LA_ERR_ALIGN

@@ -460,3 +460,38 @@ def test_max_decay_heads():
     o = _run(w, inp)
     ref = _oracle_o(w, inp)
     assert_close(o.cpu().reshape(w.H, w.T, w.d_v).numpy(), ref, "bf16", "256 decayed heads")
+
+
+def test_more_sequences_than_65535():
+    """B x H beyond 65535 (the y extent of a grid): sequences sit on the grid's x extent in
+    every pass (summaries, scan, outputs), so 70000 short sequences (T = 40: a full chunk
+    and a ragged one) are computed like any others. Every output is compared with the
+    oracle."""
+    w = Workload(name="many_sequences", B=70000, H=1, T=40, d_k=64, d_v=64, n_psi=64, chunk=32, psi=PSI_ELU1,
+                 normalize=1, eps=1e-6, dtype="bf16", seed=17, qk_scale=0.5, v_scale=1.0)
+    announce("prefill 70000 sequences of 70 tokens")
+    inp = inputs.make_prefill_inputs(w, device="cpu")
+    o = _run(w, inp)
+    ref = _oracle_o(w, inp)
+    assert_close(o.cpu().reshape(w.B * w.H, w.T, w.d_v).numpy(), ref, "bf16", w.name)
+
+
+@pytest.mark.parametrize("n_seg", [1, 2, 3, 4, 5, 8, 16, 17, 64, 65, 100, 1024, 4096, 65535])
+def test_scan_depth_record(n_seg):
+    """The segment scan's depth as the kernel counts it while it runs ("Log-Depth Chunked
+    Linear-Attention Scan", Verification: the round count is the check of the scan's depth).
+    W waves (a power of two, at most 16, about 4 segments each) fold their runs in sequence,
+    a Blelloch tree over the W totals takes log2 W levels up and log2 W down, one step
+    carries the initial state, and each run is rewritten with its prefixes: the longest
+    chain of dependent combine steps is 2 ceil(n / W) + 2 log2 W + 1. Up to 64 segments that
+    stays within 2 * 4 + 2 * 4 + 1 = 17 steps; beyond it the runs grow linearly."""
+    W = 1
+    while W < 16 and W * 4 < n_seg:
+        W *= 2
+    want = 2 * (-(-n_seg // W)) + 2 * (W.bit_length() - 1) + 1
+    announce(f"scan depth n_seg={n_seg}")
+    got = binding.scan_depth(n_seg)
+    print(f"[scan depth] n_seg={n_seg} W={W} rounds={got} (ceil(log2 n) = {(n_seg - 1).bit_length()})", flush=True)
+    assert got == want
+    if n_seg <= 64:
+        assert got <= 17
