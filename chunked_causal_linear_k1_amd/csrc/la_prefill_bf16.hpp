@@ -839,34 +839,34 @@ void k_output_sh(PrefillParams p) {
 // ---------------------------------------------------------------------------------------
 // Output kernel with two waves per SIMD (8 waves per workgroup, d = 128, chunk 64).
 //
-// The LDS image of a 128-token chunk fills the CU, so occupancy must come from within the
-// workgroup. Waves w and w + 4 share value-column block cb = w % 4: each holds the full
-// 128 x 32 state slice S[:, cb] and performs the same state update (bitwise identical
-// results), and they split the output row tiles between them (tiles {0, 3} and {1, 2} at
-// C = 128, so both do the same amount of work). The score tiles are shared as before. The
-// duplicated state update costs MFMA issue slots, which are cheap here; in exchange the
-// second wave on each SIMD hides the LDS and MFMA latencies that a lone wave exposes.
-// Register diet for 256 per wave: decay factors of the score tiles are computed per tile,
-// S is split into hi + lo one state-row tile at a time, and each thread carries half as
-// many prefetched pieces.
+// The LDS image with elu+1 keys (or a denominator) keeps the CU to one workgroup, so
+// occupancy comes from within it. Wave w = (cb, fh), cb = w % 4, fh = w / 4, owns value
+// columns [32 cb, 32 cb + 32) and state rows [64 fh, 64 fh + 64): half the state per wave
+// pair, so neither the hi + lo split of S nor the state update is done twice. Each half
+// computes the inter-chunk part over its state rows for both token tiles; half h then
+// finishes token tile h (adds the intra-chunk term V^T A^T and takes the other half's
+// partial through LDS), so every wave stores the same rows. psi(q) . Z_prev is formed per
+// token while psi(Q) is committed (DPP sums over the 16 threads of a row); Z's per-chunk
+// column sums come from MFMAs of an all-ones operand inside the state update.
 template <int C, int D, bool ELU>
 struct W8Geo {
   using B = ShGeo<C, D, ELU>;
   static constexpr int NWV = 8, NT = 64 * NWV;
-  static constexpr int NJ = B::NJ, NTILE = B::NTILE, JPR = NJ / 2;  // row tiles per wave
+  static constexpr int NJ = B::NJ, NTILE = B::NTILE;
+  static constexpr int NPH = D / 64;            // state-row tiles per wave (half of D / 32)
   static constexpr int PQ = B::PQ, PV = B::PV, PA = B::PA, A_TILE = B::A_TILE, K_BYTES = B::K_BYTES;
   static constexpr int OFF_Q = B::OFF_Q, OFF_K = B::OFF_K, OFF_A = B::OFF_A, OFF_V = B::OFF_V, OFF_F = B::OFF_F;
   static constexpr int F_Z = 0;                 // Z [D]
-  static constexpr int F_ZRED = D;              // per-wave Z partials [NWV][D]
-  static constexpr int F_THETA = D + NWV * D;   // gamma^(j+1) [C]
+  static constexpr int F_THETA = D;             // gamma^(j+1) [C]
   static constexpr int F_R = F_THETA + C;       // per-tile score row sums [NTILE][32]
-  static constexpr int LDS_BYTES = OFF_F + 4 * (F_R + NTILE * 32);
+  static constexpr int F_QZ = F_R + NTILE * 32; // psi(q_j) . Z_prev [C]
+  static constexpr int OFF_X = OFF_F + 4 * (F_QZ + C);      // partial outputs [4][NJ][16 / 4][64][4] floats
+  static constexpr int LDS_BYTES = OFF_X + 4 * 4 * NJ * 16 * 64;
   static constexpr int PPR = D / 8;             // 16-byte pieces per token row
   static constexpr int RSTEP = NT / PPR;        // rows between a thread's pieces
   static constexpr int NPC = C * PPR / NT;      // pieces per thread per tile
-  // Laid out for C = 64: at C = 128 the duplicated state update's LDS reads (each wave reads
-  // all of K~ and its V columns) cost more than the second wave per SIMD saves (measured on
-  // the 128k retention workload: 3.36 ms against 3.03 ms with four waves).
+  static_assert(OFF_X % 16 == 0, "16-byte exchange slots");
+  // Laid out for C = 64, d = 128 (two token tiles, one per feature half).
   static constexpr bool FITS = B::FITS && LDS_BYTES <= 160 * 1024 && D == 128 && C == 64;
 };
 
@@ -891,51 +891,58 @@ __global__ __launch_bounds__(512) void k_output_w8(PrefillParams p) {
   using G = W8Geo<C, D, ELU>;
   static_assert(G::FITS, "8-wave layout");
   static_assert(G::RSTEP % 16 == 0, "piece rows advance in multiples of 16 (swizzle period)");
+  static_assert(G::NJ == 2 && G::PPR == 16, "two token tiles, one DPP row per token row");
   constexpr bool SPLIT = DECAY || ELU;
-  constexpr int NJ = G::NJ, NWV = G::NWV, NPC = G::NPC, JPR = G::JPR, RSTEP = G::RSTEP;
-  constexpr int TPW = (G::NTILE + NWV - 1) / NWV;
-  constexpr int PQ = G::PQ, PV = G::PV, PA = G::PA;
+  constexpr int NJ = G::NJ, NPC = G::NPC, RSTEP = G::RSTEP, NPH = G::NPH;
+  constexpr int PQ = G::PQ, PA = G::PA;
   constexpr int KLO = G::K_BYTES;
   constexpr int ALO = 32 * PA * 2;
   extern __shared__ __align__(16) unsigned char smem[];
   const int bh = blockIdx.x, seg = blockIdx.y, head = bh % p.H;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, n = lane & 31, hh = lane >> 5;
-  const int cb = w & 3, role = w >> 2;
+  const int cb = w & 3, fh = w >> 2;
   const int L16 = lane & 15, g = lane >> 4;
   const int Ew = 32 * cb;
   const float lg = DECAY ? p.log2g[head] : 0.f;
+  // this wave's state-row tiles: j-th = NPH fh + (j + rot) % NPH; the first one's column sums
+  // give Z (waves cb < NPH of each half cover the half)
+  const int rot = cb % NPH;
+  const bool zw = __builtin_amdgcn_readfirstlane(cb) < NPH;
 
   const int prow = tid / G::PPR, pcol = (tid % G::PPR) * 8;
   const int trow = 8 * (g >> 1) + (L16 >> 2), tcol = 16 * (g & 1) + 4 * (L16 & 3);
   unsigned char* const qP = smem + pin(G::OFF_Q + (prow * PQ + pcol) * 2);
   const unsigned char* const qC = smem + pin(G::OFF_Q + (n * PQ + 4 * hh) * 2);
   const unsigned char* const qS = smem + pin(G::OFF_Q + (n * PQ + 8 * hh) * 2);
-  const unsigned char* const qZ = smem + pin(G::OFF_Q + (n * PQ + hh * (D / 2)) * 2);
   unsigned char* const kP = smem + pin(G::OFF_K + swz_off<D>(prow, pcol) * 2);
   const unsigned char* kR[D / 16];
-  const unsigned char* kT[D / 32][2];
+  const unsigned char* kT[NPH][2];
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) kR[kk] = smem + pin(G::OFF_K + swz_off<D>(n, 16 * kk + 8 * hh) * 2);
 #pragma unroll
-  for (int pt = 0; pt < D / 32; ++pt) {
-    kT[pt][0] = smem + pin(G::OFF_K + swz_off<D>(trow, 32 * pt + tcol) * 2);
-    kT[pt][1] = smem + pin(G::OFF_K + swz_off<D>(trow + 4, 32 * pt + tcol) * 2);
+  for (int j = 0; j < NPH; ++j) {
+    const int pt = NPH * fh + (j + rot) % NPH;
+    kT[j][0] = smem + pin(G::OFF_K + swz_off<D>(trow, 32 * pt + tcol) * 2);
+    kT[j][1] = smem + pin(G::OFF_K + swz_off<D>(trow + 4, 32 * pt + tcol) * 2);
   }
   unsigned char* const vP = smem + pin(G::OFF_V + swz_off<D>(prow, pcol) * 2);
   const unsigned char* const vT0 = smem + pin(G::OFF_V + swz_off<D>(trow, Ew + tcol) * 2);
   const unsigned char* const vT1 = smem + pin(G::OFF_V + swz_off<D>(trow + 4, Ew + tcol) * 2);
   unsigned char* const aW = smem + pin(G::OFF_A + (n * PA + 4 * hh) * 2);
   const unsigned char* const aR = smem + pin(G::OFF_A + (n * PA + 8 * hh) * 2);
+  float* const xch = (float*)(smem + pin(G::OFF_X)) + 4 * lane;  // [cb][jt][r / 4][lane][r % 4]
   float* const sF = (float*)(smem + pin(G::OFF_F));
   float* const fN = (float*)(smem + pin(G::OFF_F + 4 * n));
 
   const size_t E = (size_t)D * D + D;
   const float* pre = p.ws + rec_index(p, bh, seg) * E;
-  f32x16 S[D / 32];
+  f32x16 S[NPH];
 #pragma unroll
-  for (int pt = 0; pt < D / 32; ++pt)
+  for (int j = 0; j < NPH; ++j) {
+    const int pt = NPH * fh + (j + rot) % NPH;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) S[pt][r] = pre[(size_t)(pt * 32 + dtile_row(r, lane)) * D + Ew + n];
+    for (int r = 0; r < 16; ++r) S[j][r] = pre[(size_t)(pt * 32 + dtile_row(r, lane)) * D + Ew + n];
+  }
   if (tid < D) sF[G::F_Z + tid] = NORM ? pre[(size_t)D * D + tid] : 0.f;
   for (int j = tid; j < C; j += G::NT) sF[G::F_THETA + j] = DECAY ? exp2f((float)(j + 1) * lg) : 1.f;
 
@@ -963,10 +970,13 @@ __global__ __launch_bounds__(512) void k_output_w8(PrefillParams p) {
     const float a = DECAY ? exp2f((float)L * lg) : 1.f;
     lds_barrier();  // the previous chunk is done with LDS (and Z is updated)
 
-    // ---- commit (see k_output_sh)
-    float zp[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) zp[j] = 0.f;
+    // ---- commit (see k_output_sh); with a denominator, psi(q_j) . Z_prev per token row from
+    // the rounded features (the 16 threads of a row are one DPP row)
+    f32x4 zq[2];
+    if (NORM) {
+      zq[0] = *(const f32x4*)(sF + G::F_Z + pcol);
+      zq[1] = *(const f32x4*)(sF + G::F_Z + pcol + 4);
+    }
 #pragma unroll
     for (int i = 0; i < NPC; ++i) {
       uint4 raw = pq.r[i];
@@ -978,32 +988,32 @@ __global__ __launch_bounds__(512) void k_output_w8(PrefillParams p) {
         raw = __builtin_bit_cast(uint4, y);
       }
       *(uint4*)(qP + i * RSTEP * PQ * 2) = raw;
+      if (NORM) {
+        const bf16x8 y = __builtin_bit_cast(bf16x8, raw);
+        float qz = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) qz += from_bf16(y[j]) * zq[0][j] + from_bf16(y[4 + j]) * zq[1][j];
+        qz = row16_sum(qz);
+        if (tid % G::PPR == 0) sF[G::F_QZ + prow + RSTEP * i] = qz;
+      }
     }
 #pragma unroll
     for (int i = 0; i < NPC; ++i) {
       const int off = i * RSTEP * D * 2;
-      if (!ELU && !NORM) {
+      if (!ELU) {
         *(uint4*)(kP + off) = pk.r[i];
         continue;
       }
       const int row = prow + RSTEP * i;
       const float live = row < L ? 1.f : 0.f;
-      const float xi = DECAY ? live * exp2f((float)(L - 1 - row) * lg) : live;
       const bf16x8 x = __builtin_bit_cast(bf16x8, pk.r[i]);
       float f[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        f[j] = ELU ? elu1(from_bf16(x[j])) * live : from_bf16(x[j]);
-        if (NORM) zp[j] += f[j] * xi;
-      }
-      if (ELU) {
-        bf16x8 hi, lo;
-        split8_trunc(f, hi, lo);
-        *(bf16x8*)(kP + off) = hi;
-        *(bf16x8*)(kP + off + KLO) = lo;
-      } else {
-        *(uint4*)(kP + off) = pk.r[i];
-      }
+      for (int j = 0; j < 8; ++j) f[j] = elu1(from_bf16(x[j])) * live;
+      bf16x8 hi, lo;
+      split8_trunc(f, hi, lo);
+      *(bf16x8*)(kP + off) = hi;
+      *(bf16x8*)(kP + off + KLO) = lo;
     }
 #pragma unroll
     for (int i = 0; i < NPC; ++i) *(uint4*)(vP + i * RSTEP * D * 2) = pv.r[i];
@@ -1014,12 +1024,9 @@ __global__ __launch_bounds__(512) void k_output_w8(PrefillParams p) {
     load_pieces_n<D, NPC, RSTEP>(pv, vb + (size_t)(c + 1) * C * rse, Ln, prow, pcol, rsb);
     lds_barrier();
 
-    // ---- score tiles (shared): wave w computes tiles w, w + 8, ...; decay factors per tile
-#pragma unroll
-    for (int u = 0; u < TPW; ++u) {
-      const int t = w + u * NWV;
-      if (t >= G::NTILE) break;
-      const int jt = tile_jt(t), it = t - jt * (jt + 1) / 2;
+    // ---- score tiles (shared): wave t < NTILE computes tile t; decay factors per tile
+    if (w < G::NTILE) {
+      const int t = w, jt = tile_jt(t), it = t - jt * (jt + 1) / 2;
       bf16x8 ka[D / 16], qv[D / 16];
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
@@ -1059,78 +1066,62 @@ __global__ __launch_bounds__(512) void k_output_w8(PrefillParams p) {
     }
     lds_barrier();
 
-    // ---- outputs of this wave's row tiles jt(role, j) = role, NJ - 1 - role for its value
-    // columns, transposed as in k_output_sh; S split one state-row tile at a time
-    const __amdgpu_buffer_rsrc_t ors = make_rsrc(ob + (size_t)t0 * rse * OES, rows_extent(L, rse * OES, D * OES));
-    f32x16 num[JPR];
+    // ---- outputs, transposed as in k_output_sh: numT[e][j] (M = value column, N = token).
+    // The inter-chunk part over this wave's state rows for both token tiles (S split into
+    // hi + lo one tile at a time), theta-weighted; then the intra-chunk term V^T A^T for
+    // token tile fh, the tile this half finishes.
+    f32x16 num[NJ];
 #pragma unroll
-    for (int j = 0; j < JPR; ++j) num[j] = f32x16{};
+    for (int jt = 0; jt < NJ; ++jt) num[jt] = f32x16{};
 #pragma unroll
-    for (int pt = 0; pt < D / 32; ++pt) {
+    for (int j = 0; j < NPH; ++j) {
       bf16x8 sh[2], sl[2];
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         float x[8];
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) x[jj] = S[pt][8 * q + jj];
+        for (int jj = 0; jj < 8; ++jj) x[jj] = S[j][8 * q + jj];
         split8_trunc(x, sh[q], sl[q]);
       }
+      const int fcol = (NPH * fh + (j + rot) % NPH) * 32;
 #pragma unroll
-      for (int j = 0; j < JPR; ++j) {
-        const int jt = j == 0 ? role : NJ - 1 - role;
+      for (int jt = 0; jt < NJ; ++jt)
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-          const unsigned char* qa = qC + (jt * 32 * PQ + pt * 32 + 16 * q) * 2;
+          const unsigned char* qa = qC + (jt * 32 * PQ + fcol + 16 * q) * 2;
           const bf16x8 qo = cat8(*(const bf16x4*)qa, *(const bf16x4*)(qa + 16));
-          num[j] = mfma32(sh[q], qo, num[j]);
-          num[j] = mfma32(sl[q], qo, num[j]);
+          num[jt] = mfma32(sh[q], qo, num[jt]);
+          num[jt] = mfma32(sl[q], qo, num[jt]);
         }
-      }
     }
+    if (DECAY) {
 #pragma unroll
-    for (int j = 0; j < JPR; ++j) {
-      const int jt = j == 0 ? role : NJ - 1 - role;
-      if (DECAY) num[j] *= fN[G::F_THETA + jt * 32];
-      // numT += V^T A^T for it <= jt (the trip count depends on the role: a wave-uniform loop)
-      for (int it = 0; it <= jt; ++it) {
-        const unsigned char* at = aR + (jt * (jt + 1) / 2 + it) * G::A_TILE;
+      for (int jt = 0; jt < NJ; ++jt) num[jt] *= fN[G::F_THETA + jt * 32];
+    }
+    f32x16 mine = fh ? num[1] : num[0];
+    {
+      // the intra-chunk term of token tile fh: it = 0 .. fh (a wave-uniform trip count)
+      for (int it = 0; it <= fh; ++it) {
+        const unsigned char* at = aR + (fh * (fh + 1) / 2 + it) * G::A_TILE;
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
           const int r0 = it * 32 + 16 * q;
           const bf16x8 vv = cat8(lds_read_tr4((const __bf16*)(vT0 + r0 * D * 2)),
                                  lds_read_tr4((const __bf16*)(vT1 + r0 * D * 2)));
-          num[j] = mfma32(vv, *(const bf16x8*)(at + 32 * q), num[j]);
-          num[j] = mfma32(vv, *(const bf16x8*)(at + 32 * q + ALO), num[j]);
+          mine = mfma32(vv, *(const bf16x8*)(at + 32 * q), mine);
+          mine = mfma32(vv, *(const bf16x8*)(at + 32 * q + ALO), mine);
         }
       }
-      float inv = 1.f;
-      if (NORM) {
-        float qz = 0.f;
-        const unsigned char* qr = qZ + jt * 32 * PQ * 2;
-        const f32x4* zr = (const f32x4*)(sF + G::F_Z + hh * (D / 2));
+      const f32x16 give = fh ? num[0] : num[1];
+      f32x4* const xo = (f32x4*)(xch + (cb * NJ + (1 - fh)) * 16 * 64);
 #pragma unroll
-        for (int e8 = 0; e8 < D / 2; e8 += 8) {
-          const bf16x8 qv = *(const bf16x8*)(qr + e8 * 2);
-          const f32x4 z0 = zr[e8 / 4], z1 = zr[e8 / 4 + 1];
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) qz += from_bf16(qv[jj]) * z0[jj] + from_bf16(qv[4 + jj]) * z1[jj];
-        }
-        qz += __shfl_xor(qz, 32);
-        float r = 0.f;
-        for (int it = 0; it <= jt; ++it) r += fN[G::F_R + (jt * (jt + 1) / 2 + it) * 32];
-        inv = 1.f / (fN[G::F_THETA + jt * 32] * qz + r + p.eps);
-      }
-      const uint32_t row_el = (uint32_t)(jt * 32 + n) * rse + Ew + 4 * hh;
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        store_out4<OBF>(ors, row_el + 8 * q4, num[j][4 * q4] * inv, num[j][4 * q4 + 1] * inv,
-                        num[j][4 * q4 + 2] * inv, num[j][4 * q4 + 3] * inv);
+      for (int q = 0; q < 4; ++q) xo[q * 64] = f32x4{give[4 * q], give[4 * q + 1], give[4 * q + 2], give[4 * q + 3]};
     }
+    lds_barrier();  // partials published; every wave is done with the score tiles and with K
 
-    // ---- state update (every wave: its value columns, all state rows)
-    if (NORM) reduce_zp<D>(zp, sF + G::F_ZRED);
+    // K~ = Xi psi(K) with decay: rescale the hi + lo tile in place (identity keys: K lo
+    // aliases the score tiles, dead now)
     if (DECAY) {
-      lds_barrier();  // every wave is done with the score tiles (K lo aliases them) and K
 #pragma unroll
       for (int i = 0; i < NPC; ++i) {
         const int row = prow + RSTEP * i, off = i * RSTEP * D * 2;
@@ -1151,30 +1142,50 @@ __global__ __launch_bounds__(512) void k_output_w8(PrefillParams p) {
         *(bf16x8*)(kP + off + KLO) = lo;
       }
     }
-    lds_barrier();
-    if (NORM && tid < D) {
-      float z = 0.f;
+    {
+      const int jt = fh;
+      const f32x4* const xi4 = (const f32x4*)(xch + (cb * NJ + jt) * 16 * 64);
 #pragma unroll
-      for (int ww = 0; ww < NWV; ++ww) z += sF[G::F_ZRED + ww * D + tid];
-      sF[G::F_Z + tid] = a * sF[G::F_Z + tid] + z;
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 o4 = xi4[q * 64];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mine[4 * q + e] += o4[e];
+      }
+      float inv = 1.f;
+      if (NORM) {
+        float r = fN[G::F_R + (jt * (jt + 1) / 2) * 32];
+        if (jt) r += fN[G::F_R + 2 * 32];
+        inv = 1.f / (fN[G::F_THETA + jt * 32] * fN[G::F_QZ + jt * 32] + r + p.eps);
+      }
+      const __amdgpu_buffer_rsrc_t ors = make_rsrc(ob + (size_t)t0 * rse * OES, rows_extent(L, rse * OES, D * OES));
+      const uint32_t row_el = (uint32_t)(jt * 32 + n) * rse + Ew + 4 * hh;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        store_out4<OBF>(ors, row_el + 8 * q4, mine[4 * q4] * inv, mine[4 * q4 + 1] * inv, mine[4 * q4 + 2] * inv,
+                        mine[4 * q4 + 3] * inv);
     }
+    if (DECAY) lds_barrier();  // K~ complete
+
+    // ---- state update: S <- gamma^L S + K~^T V over this wave's state rows, and Z's column
+    // sums 1 K~ of its first tile (waves cb < NPH), read again only in the next chunk
     if (DECAY) {
 #pragma unroll
-      for (int pt = 0; pt < D / 32; ++pt) S[pt] *= a;
+      for (int j = 0; j < NPH; ++j) S[j] *= a;
     }
     {
-      constexpr int NK = C / 16, NM = (SPLIT ? 2 : 1) * (D / 32);
+      constexpr int NK = C / 16, KP = SPLIT ? 2 : 1, NM = KP * NPH;
+      const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+      f32x16 zc = f32x16{};
       bf16x8 ops[2][1 + NM];
       auto load_ops = [&](bf16x8 (&o)[1 + NM], int ik) {
         const int r0 = ik * 16, ko = r0 * D * 2;
         o[0] = cat8(lds_read_tr4((const __bf16*)(vT0 + r0 * D * 2)), lds_read_tr4((const __bf16*)(vT1 + r0 * D * 2)));
 #pragma unroll
-        for (int pt = 0; pt < D / 32; ++pt) {
-          o[1 + (SPLIT ? 2 : 1) * pt] =
-              cat8(lds_read_tr4((const __bf16*)(kT[pt][0] + ko)), lds_read_tr4((const __bf16*)(kT[pt][1] + ko)));
+        for (int j = 0; j < NPH; ++j) {
+          o[1 + KP * j] = cat8(lds_read_tr4((const __bf16*)(kT[j][0] + ko)), lds_read_tr4((const __bf16*)(kT[j][1] + ko)));
           if (SPLIT)
-            o[2 + 2 * pt] = cat8(lds_read_tr4((const __bf16*)(kT[pt][0] + ko + KLO)),
-                                 lds_read_tr4((const __bf16*)(kT[pt][1] + ko + KLO)));
+            o[2 + 2 * j] = cat8(lds_read_tr4((const __bf16*)(kT[j][0] + ko + KLO)),
+                                lds_read_tr4((const __bf16*)(kT[j][1] + ko + KLO)));
         }
       };
       load_ops(ops[0], 0);
@@ -1183,14 +1194,22 @@ __global__ __launch_bounds__(512) void k_output_w8(PrefillParams p) {
         if (ik + 1 < NK) load_ops(ops[(ik + 1) & 1], ik + 1);
         const bf16x8(&o)[1 + NM] = ops[ik & 1];
 #pragma unroll
-        for (int pt = 0; pt < D / 32; ++pt) {
-          S[pt] = mfma32(o[1 + (SPLIT ? 2 : 1) * pt], o[0], S[pt]);
-          if (SPLIT) S[pt] = mfma32(o[2 + 2 * pt], o[0], S[pt]);
+        for (int j = 0; j < NPH; ++j) {
+          S[j] = mfma32(o[1 + KP * j], o[0], S[j]);
+          if (SPLIT) S[j] = mfma32(o[2 + 2 * j], o[0], S[j]);
+        }
+        if (NORM && zw) {
+          zc = mfma32(ones, o[1], zc);
+          if (SPLIT) zc = mfma32(ones, o[2], zc);
         }
         if (ik + 1 < NK) {
           __builtin_amdgcn_sched_group_barrier(0x100, 2 * (1 + NM), 0);
           __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
         }
+      }
+      if (NORM && zw && hh == 0) {
+        float* const zf = sF + G::F_Z + (NPH * fh + rot) * 32 + n;
+        *zf = a * *zf + zc[0];
       }
     }
   }
