@@ -41,12 +41,11 @@ __host__ __device__ inline F32Layout f32_layout(int C, int d_k, int d_v, int n_p
 
 // psi of the chunk rows [0, valid) of x (fp32, row length d_k, rows rs elements apart) into
 // out[C][n_psi]; rows >= valid -> 0.
+__device__ void load_rows_f32(const float* __restrict__ x, size_t rs, float* out, int C, int valid, int d);
+
 __device__ void features_f32(const float* __restrict__ x, size_t rs, float* raw, float* out, int C, int valid,
                              int d_k, int n_psi, int psi, const float* __restrict__ w) {
-  for (int idx = threadIdx.x; idx < C * d_k; idx += kThreads) {
-    const int r = idx / d_k;
-    raw[idx] = r < valid ? x[(size_t)r * rs + (idx - r * d_k)] : 0.f;
-  }
+  load_rows_f32(x, rs, raw, C, valid, d_k);
   __syncthreads();
   for (int idx = threadIdx.x; idx < C * n_psi; idx += kThreads) {
     const int r = idx / n_psi, f = idx % n_psi;
@@ -86,23 +85,94 @@ __device__ void features_f32(const float* __restrict__ x, size_t rs, float* raw,
   }
 }
 
+// Rows [0, valid) of x (row length d, a multiple of 4; rows rs elements apart) into out[C][d],
+// rows past `valid` zero: 16-byte loads, several in flight per thread.
 __device__ void load_rows_f32(const float* __restrict__ x, size_t rs, float* out, int C, int valid, int d) {
-  for (int idx = threadIdx.x; idx < C * d; idx += kThreads) {
-    const int r = idx / d;
-    out[idx] = r < valid ? x[(size_t)r * rs + (idx - r * d)] : 0.f;
+  const int n4 = C * d / 4, d4 = d / 4;
+#pragma unroll 4
+  for (int q = threadIdx.x; q < n4; q += kThreads) {
+    const int r = q / d4, c = (q - r * d4) * 4;
+    ((f32x4*)out)[q] = r < valid ? *(const f32x4*)(x + (size_t)r * rs + c) : f32x4{0.f, 0.f, 0.f, 0.f};
   }
 }
 
-// S <- a S + sum_i xi_i fK_i v_i^T ; Z likewise. Needs FK, V, XI in LDS.
+// n floats (a multiple of 4) from global to LDS or back, 16 bytes at a time
+__device__ __forceinline__ void copy4(float* dst, const float* __restrict__ src, int n) {
+#pragma unroll 4
+  for (int q = threadIdx.x; q < n / 4; q += kThreads) ((f32x4*)dst)[q] = ((const f32x4*)src)[q];
+}
+
+// 4 x 4 output blocks of fp32 products over LDS operands, one block per thread per pass;
+// every operand read is 16 bytes (the tile sizes, offsets and leading dimensions are
+// multiples of 4 floats), so each pair of reads feeds 16 or 64 FMAs.
+using F4 = f32x4;
+__device__ __forceinline__ F4 ld4s(const float* p) { return *(const F4*)p; }
+
+// acc[r][c] += sum_k X[(m0 + r) ldx + k] Y[(n0 + c) ldy + k]            (X Y^T)
+__device__ __forceinline__ void mm_abt(float (&acc)[4][4], const float* X, int ldx, const float* Y, int ldy, int m0,
+                                       int n0, int K) {
+  for (int k = 0; k < K; k += 4) {
+    F4 x[4], y[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) x[r] = ld4s(X + (m0 + r) * ldx + k);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) y[c] = ld4s(Y + (n0 + c) * ldy + k);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) acc[r][c] += x[r][kk] * y[c][kk];
+  }
+}
+
+// acc[r][c] += sum_k X[(m0 + r) ldx + k] Y[k ldy + n0 + c]               (X Y)
+__device__ __forceinline__ void mm_ab(float (&acc)[4][4], const float* X, int ldx, const float* Y, int ldy, int m0,
+                                      int n0, int K) {
+  for (int k = 0; k < K; k += 4) {
+    F4 x[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) x[r] = ld4s(X + (m0 + r) * ldx + k);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const F4 y = ld4s(Y + (k + kk) * ldy + n0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[r][c] += x[r][kk] * y[c];
+    }
+  }
+}
+
+// acc[r][c] += sum_k w[k] X[k ldx + m0 + r] Y[k ldy + n0 + c]            (X^T diag(w) Y)
+__device__ __forceinline__ void mm_atb(float (&acc)[4][4], const float* X, int ldx, const float* Y, int ldy,
+                                       const float* w, int m0, int n0, int K) {
+  for (int k = 0; k < K; ++k) {
+    const F4 x = ld4s(X + k * ldx + m0) * w[k];
+    const F4 y = ld4s(Y + k * ldy + n0);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[r][c] += x[r] * y[c];
+  }
+}
+
+// S <- a S + sum_i xi_i fK_i v_i^T ; Z likewise. Needs FK, V in LDS; writes XI.
 __device__ void state_update_f32(float* sm, const F32Layout& Ly, int C, int L, int d_v, int n_psi, float lg) {
   for (int i = threadIdx.x; i < C; i += kThreads) sm[Ly.XI + i] = i < L ? gpow(lg, (float)(L - 1 - i)) : 0.f;
   __syncthreads();
   const float a = gpow(lg, (float)L);
-  for (int idx = threadIdx.x; idx < n_psi * d_v; idx += kThreads) {
-    const int pp = idx / d_v, e = idx % d_v;
-    float acc = 0.f;
-    for (int i = 0; i < L; ++i) acc += sm[Ly.XI + i] * sm[Ly.FK + i * n_psi + pp] * sm[Ly.V + i * d_v + e];
-    sm[Ly.S + idx] = a * sm[Ly.S + idx] + acc;
+  const int nb = d_v / 4, blocks = (n_psi / 4) * nb;
+  const int K = (L + 3) & ~3;  // rows past L are zero in FK and XI
+  for (int b = threadIdx.x; b < blocks; b += kThreads) {
+    const int m0 = (b / nb) * 4, n0 = (b % nb) * 4;
+    float acc[4][4] = {};
+    mm_atb(acc, sm + Ly.FK, n_psi, sm + Ly.V, d_v, sm + Ly.XI, m0, n0, K);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      F4* sp = (F4*)(sm + Ly.S + (m0 + r) * d_v + n0);
+      *sp = *sp * a + F4{acc[r][0], acc[r][1], acc[r][2], acc[r][3]};
+    }
   }
   for (int pp = threadIdx.x; pp < n_psi; pp += kThreads) {
     float acc = 0.f;
@@ -135,8 +205,7 @@ __global__ __launch_bounds__(kThreads) void k_summary_f32(PrefillParams p) {
   }
   __syncthreads();
   const size_t E = (size_t)p.n_psi * p.d_v + p.n_psi;
-  float* out = p.ws + ((size_t)bh * p.n_seg + seg) * E;
-  for (int idx = threadIdx.x; idx < (int)E; idx += kThreads) out[idx] = sm[Ly.S + idx];
+  copy4(p.ws + ((size_t)bh * p.n_seg + seg) * E, sm + Ly.S, (int)E);
 }
 
 __global__ __launch_bounds__(kThreads) void k_output_f32(PrefillParams p) {
@@ -149,7 +218,7 @@ __global__ __launch_bounds__(kThreads) void k_output_f32(PrefillParams p) {
   const int kpsi = p.psi == LA_PSI_PRF_QSHIFT ? LA_PSI_PRF : p.psi;  // keys take no query shift
   const size_t E = (size_t)n_psi * d_v + n_psi;
   const float* pre = p.ws + ((size_t)bh * p.n_seg + seg) * E;
-  for (int idx = threadIdx.x; idx < (int)E; idx += kThreads) sm[Ly.S + idx] = pre[idx];  // S then Z
+  copy4(sm + Ly.S, pre, (int)E);  // S then Z
   for (int j = threadIdx.x; j < C; j += kThreads) sm[Ly.THETA + j] = gpow(lg, (float)(j + 1));
   const SeqSpan sq = seq_span(p, bh);
   const int T = sq.T, n_chunks = (T + C - 1) / C;
@@ -165,38 +234,62 @@ __global__ __launch_bounds__(kThreads) void k_output_f32(PrefillParams p) {
     load_rows_f32(vb + (size_t)t0 * rv, rv, sm + Ly.V, C, L, d_v);
     features_f32(qb + (size_t)t0 * rk, rk, sm + Ly.RAW, sm + Ly.FQ, C, L, p.d_k, n_psi, p.psi, w);
     features_f32(kb + (size_t)t0 * rk, rk, sm + Ly.RAW, sm + Ly.FK, C, L, p.d_k, n_psi, kpsi, w);
-    // scores
-    for (int idx = threadIdx.x; idx < C * C; idx += kThreads) {
-      const int j = idx / C, i = idx % C;
-      float a = 0.f;
-      if (i <= j && j < L) {
-        for (int f = 0; f < n_psi; ++f) a += sm[Ly.FQ + j * n_psi + f] * sm[Ly.FK + i * n_psi + f];
-        a *= gpow(lg, (float)(j - i));
+    // scores A[j][i] = psi(q_j).psi(k_i) gamma^(j-i), i <= j < L, in 4 x 4 blocks on or below
+    // the diagonal (blocks above it are zero)
+    {
+      const int nb = C / 4;
+      for (int b = threadIdx.x; b < nb * nb; b += kThreads) {
+        const int m0 = (b / nb) * 4, n0 = (b % nb) * 4;
+        float acc[4][4] = {};
+        if (n0 <= m0 && m0 < L) mm_abt(acc, sm + Ly.FQ, n_psi, sm + Ly.FK, n_psi, m0, n0, n_psi);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float o4[4];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const int j = m0 + r, i = n0 + c;
+            o4[c] = (i <= j && j < L) ? acc[r][c] * gpow(lg, (float)(j - i)) : 0.f;
+          }
+          *(F4*)(sm + Ly.A + (m0 + r) * C + n0) = F4{o4[0], o4[1], o4[2], o4[3]};
+        }
       }
-      sm[Ly.A + idx] = a;
     }
     __syncthreads();
     if (p.normalize) {
       for (int j = threadIdx.x; j < C; j += kThreads) {
-        float qz = 0.f, r = 0.f;
-        for (int f = 0; f < n_psi; ++f) qz += sm[Ly.FQ + j * n_psi + f] * sm[Ly.Z + f];
-        for (int i = 0; i <= j; ++i) r += sm[Ly.A + j * C + i];
-        sm[Ly.DEN + j] = sm[Ly.THETA + j] * qz + r + p.eps;
+        F4 qz = {0.f, 0.f, 0.f, 0.f}, r = {0.f, 0.f, 0.f, 0.f};
+        for (int f = 0; f < n_psi; f += 4) qz += ld4s(sm + Ly.FQ + j * n_psi + f) * ld4s(sm + Ly.Z + f);
+        for (int i = 0; i <= j; i += 4) r += ld4s(sm + Ly.A + j * C + i);  // zero above the diagonal
+        sm[Ly.DEN + j] = sm[Ly.THETA + j] * ((qz[0] + qz[1]) + (qz[2] + qz[3])) + ((r[0] + r[1]) + (r[2] + r[3])) + p.eps;
       }
       __syncthreads();
     }
-    for (int idx = threadIdx.x; idx < C * d_v; idx += kThreads) {
-      const int j = idx / d_v, e = idx % d_v;
-      if (j >= L) continue;
-      float inter = 0.f, intra = 0.f;
-      for (int f = 0; f < n_psi; ++f) inter += sm[Ly.FQ + j * n_psi + f] * sm[Ly.S + f * d_v + e];
-      for (int i = 0; i <= j; ++i) intra += sm[Ly.A + j * C + i] * sm[Ly.V + i * d_v + e];
-      float num = sm[Ly.THETA + j] * inter + intra;
-      if (p.normalize) num = num / sm[Ly.DEN + j];
-      ob[(size_t)(t0 + j) * rv + e] = num;
+    // outputs: theta_j psi(q_j) S_prev + sum_{i <= j} A_ji v_i, over the denominator
+    {
+      const int nb = d_v / 4;
+      for (int b = threadIdx.x; b < (C / 4) * nb; b += kThreads) {
+        const int m0 = (b / nb) * 4, n0 = (b % nb) * 4;
+        if (m0 >= L) continue;
+        float inter[4][4] = {}, intra[4][4] = {};
+        mm_ab(inter, sm + Ly.FQ, n_psi, sm + Ly.S, d_v, m0, n0, n_psi);
+        mm_ab(intra, sm + Ly.A, C, sm + Ly.V, d_v, m0, n0, m0 + 4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int j = m0 + r;
+          if (j >= L) break;
+          const float th = sm[Ly.THETA + j];
+          F4 o4;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const float num = th * inter[r][c] + intra[r][c];
+            o4[c] = p.normalize ? num / sm[Ly.DEN + j] : num;
+          }
+          *(F4*)(ob + (size_t)(t0 + j) * rv + n0) = o4;
+        }
+      }
     }
     __syncthreads();
-    state_update_f32(sm, Ly, C, L, d_v, n_psi, lg);
+    if (c + 1 < c1) state_update_f32(sm, Ly, C, L, d_v, n_psi, lg);  // the segment's last state is not needed
   }
 }
 
@@ -210,6 +303,7 @@ bool prefill_f32_supported(int C, int d_k, int d_v, int n_psi, int psi) {
   if (psi < LA_PSI_IDENTITY || psi > LA_PSI_PRF_QSHIFT) return false;
   if (!is_prf(psi) && n_psi != d_k) return false;
   if (d_k > 128 || d_v > 128 || n_psi > 256) return false;
+  if (d_k % 4 != 0) return false;  // 16-byte row loads
   if (C != 16 && C != 32 && C != 64) return false;
   return f32_lds_bytes(C, d_k, d_v, n_psi) <= 160 * 1024;
 }

@@ -116,7 +116,7 @@ typedef struct {
  *                     chunk in {32, 64, 128};
  *                     psi PRF, PRF_QSHIFT: d_k == d_v == 128, n_psi in {128, 256},
  *                     chunk in {32, 64, 128}.
- *   in_dtype LA_F32 : d_k, d_v <= 128, n_psi <= 256 (LDS permitting),
+ *   in_dtype LA_F32 : d_k, d_v <= 128, d_k a multiple of 4, n_psi <= 256 (LDS permitting),
  *                     chunk in {16, 32, 64}, any psi.
  *   always: d_v and n_psi multiples of 4 (16-byte state rows in the workspace).
  *   out_dtype LA_BF16 with in_dtype LA_BF16 only.
