@@ -122,17 +122,19 @@ def version() -> str:
     return load().lin_attn_version().decode()
 
 
-def scan_depth(n_seg: int) -> int:
-    """lin_attn_scan_depth: the longest chain of dependent combine steps of the segment scan
-    over n_seg segments, as the kernel counts it while it runs."""
-    ws = torch.zeros(max(1, n_seg) * 20, dtype=torch.float32, device="cuda")
+def scan_depth(n_seg: int, records: Optional[torch.Tensor] = None):
+    """lin_attn_scan_depth: the segment scan over n_seg records of 20 floats (4 x 4 state, then
+    4 normaliser entries; zeros unless given). Returns (rounds, prefixes): the dependent
+    combine levels the kernel executed, and the exclusive prefixes it wrote [n_seg, 20]."""
+    ws = (torch.zeros(max(1, n_seg) * 20, dtype=torch.float32, device="cuda") if records is None
+          else records.to(device="cuda", dtype=torch.float32).contiguous().reshape(-1).clone())
     rounds = torch.zeros(1, dtype=torch.int32, device="cuda")
     st = load().lin_attn_scan_depth(int(n_seg), ws.data_ptr(), rounds.data_ptr(),
                                     torch.cuda.current_stream().cuda_stream)
     if st != 0:
         raise RuntimeError(f"lin_attn_scan_depth: {status_string(st)}")
     torch.cuda.synchronize()
-    return int(rounds.item())
+    return int(rounds.item()), ws.reshape(-1, 20)[:n_seg]
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:

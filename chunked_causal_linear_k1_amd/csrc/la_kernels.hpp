@@ -156,7 +156,7 @@ hipError_t launch_prefill_f32_output(const PrefillParams& p, hipStream_t s);
 
 hipError_t launch_segment_scan(const ScanParams& p, hipStream_t s);
 // The scan over n_seg segments of a one-sequence problem with 4 x 4 states in ws (n_seg x 20
-// floats, contents arbitrary), recording its longest (+) chain in *rounds (device int).
+// floats, replaced by their exclusive prefixes), recording its (+) depth in *rounds (device int).
 hipError_t scan_depth_probe(int n_seg, float* ws, int* rounds, hipStream_t s);
 
 bool prefill_gated_supported(int C, int d_k, int d_v, int n_psi, int psi);

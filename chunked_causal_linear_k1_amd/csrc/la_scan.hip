@@ -14,15 +14,17 @@
 // the fold of all of them. This is the adjoint state of the backward pass, which gathers
 // every later read of a state and decays the same way on its way back.
 //
-// The state elements (n_psi*d_v + n_psi per sequence) are independent. A workgroup
-// takes 256 consecutive elements (4 per lane, 16-byte accesses) and spreads the segment
-// axis over W waves: each wave folds its run of segments (holding the run in registers
-// when it is at most RUN long, so every element is read once and written once), the W
-// wave totals are scanned with a Blelloch up-sweep/down-sweep in LDS (log2 W levels
-// each; the down-sweep combines parent-prefix (+) left-sum in that order because the
-// monoid does not commute), and each wave then writes its run's exclusive prefixes.
-// With few segments (W below 4) a workgroup holds several such groups of W waves, each on
-// its own 256 elements, so that short scans still run four waves per workgroup.
+// The state elements (n_psi*d_v + n_psi per sequence) are independent. Up to 128 segments,
+// a workgroup takes 256 consecutive elements (4 per lane, 16-byte accesses) and spreads the
+// segment axis over W waves: each wave folds its run of at most 8 segments in registers (so
+// every element is read once and written once), the W wave totals are scanned with a
+// Blelloch up-sweep/down-sweep in LDS (log2 W levels each; the down-sweep combines
+// parent-prefix (+) left-sum in that order because the monoid does not commute), and each
+// wave then writes its run's exclusive prefixes. With few segments (W below 4) a workgroup
+// holds several such groups of W waves, each on its own 256 elements, so that short scans
+// still run four waves per workgroup. Beyond 128 segments the lanes hold segments instead
+// (k_segment_scan_lanes): a Hillis-Steele scan across each wavefront's 64 lanes, a Blelloch
+// scan across its waves, and a carried prefix across blocks of up to 1024 segments.
 // The order of all floating-point operations is fixed: results are deterministic.
 #include "la_device.hpp"
 #include "la_kernels.hpp"
@@ -43,8 +45,7 @@ __host__ __device__ inline int scan_seg_waves(int n_seg) {
 __device__ __forceinline__ f32x4 ld4(const float* p) { return *(const f32x4*)p; }
 __device__ __forceinline__ void st4(float* p, const f32x4& v) { *(f32x4*)p = v; }
 
-// RUN > 0: runs of up to RUN segments are kept in registers between the fold and the
-// rewrite; RUN == 0: the rewrite reads the run again (any run length).
+// Runs of up to RUN segments are kept in registers between the fold and the rewrite.
 template <int RUN>
 __global__ __launch_bounds__(64 * kMaxWaves) void k_segment_scan(ScanParams p) {
   __shared__ f32x4 sx[kMaxWaves][64];
@@ -95,25 +96,17 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_segment_scan(ScanParams p) {
   int chain = 2 * max(0, s1 - s0) + 1;
 
   // 1. fold the run: total = X_s0 (+) ... (+) X_{s1-1}
-  f32x4 run[RUN > 0 ? RUN : 1];
+  f32x4 run[RUN];
   f32x4 tx = {0.f, 0.f, 0.f, 0.f};
   f32x4 ta = {1.f, 1.f, 1.f, 1.f};
-  if (RUN > 0) {
 #pragma unroll
-    for (int i = 0; i < (RUN > 0 ? RUN : 1); ++i)
-      run[i] = (live && s0 + i < s1) ? ld4(base + (size_t)seg_of(s0 + i) * REC) : f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < RUN; ++i)
+    run[i] = (live && s0 + i < s1) ? ld4(base + (size_t)seg_of(s0 + i) * REC) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < (RUN > 0 ? RUN : 1); ++i) {
-      if (s0 + i < s1) {
-        const f32x4 as = seg_decay(seg_of(s0 + i));
-        tx = as * tx + run[i];
-        ta *= as;
-      }
-    }
-  } else {
-    for (int s = s0; s < s1; ++s) {
-      const f32x4 as = seg_decay(seg_of(s));
-      if (live) tx = as * tx + ld4(base + (size_t)seg_of(s) * REC);
+  for (int i = 0; i < RUN; ++i) {
+    if (s0 + i < s1) {
+      const f32x4 as = seg_decay(seg_of(s0 + i));
+      tx = as * tx + run[i];
       ta *= as;
     }
   }
@@ -182,28 +175,163 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_segment_scan(ScanParams p) {
     cx = ca * init + cx;
   }
   // 4. rewrite the run with exclusive prefixes
-  if (RUN > 0) {
 #pragma unroll
-    for (int i = 0; i < (RUN > 0 ? RUN : 1); ++i) {
-      if (s0 + i < s1) {
-        const f32x4 as = seg_decay(seg_of(s0 + i));
-        if (live) st4(base + (size_t)seg_of(s0 + i) * REC, cx);
-        cx = as * cx + run[i];
-      }
-    }
-  } else {
-    for (int s = s0; s < s1; ++s) {
-      const f32x4 as = seg_decay(seg_of(s));
-      if (live) {
-        const f32x4 xs = ld4(base + (size_t)seg_of(s) * REC);
-        st4(base + (size_t)seg_of(s) * REC, cx);
-        cx = as * cx + xs;
-      }
+  for (int i = 0; i < RUN; ++i) {
+    if (s0 + i < s1) {
+      const f32x4 as = seg_decay(seg_of(s0 + i));
+      if (live) st4(base + (size_t)seg_of(s0 + i) * REC, cx);
+      cx = as * cx + run[i];
     }
   }
   if (p.rounds && lane == 0 && grp == 0 && blockIdx.y == 0) atomicMax(p.rounds, chain);
   // 5. the wave holding the last segment writes the final state
   if (live && s1 == p.n_seg && s0 < s1) {
+    if (e < SE) {
+      if (p.final_S) st4(p.final_S + (size_t)bh * SE + e, cx);
+    } else if (p.final_Z) {
+      st4(p.final_Z + (size_t)bh * p.n_psi + (e - SE), cx);
+    }
+  }
+}
+
+// Many segments: lanes hold consecutive segments. A workgroup takes one 16-byte element
+// group (4 state elements) of one sequence; wave w holds segments [blk + 64 w, blk + 64 w + 64)
+// of a block of 64 NW. Inside a wavefront, an inclusive Hillis-Steele scan across the lanes
+// (log2 64 = 6 rounds of lane shifts); across the wavefronts, a Blelloch up-sweep/down-sweep
+// over the NW wave totals in LDS (log2 NW levels each); across blocks, the prefix of the
+// blocks before, carried in registers (one combine per block). Every lane of a wave reads
+// its segment's 16 bytes of one record; the element groups of neighbouring workgroups share
+// those lines in L2.
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void k_segment_scan_lanes(ScanParams p) {
+  __shared__ f32x4 tx[NW], ta[NW];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int bh = blockIdx.x, head = bh % p.H;
+  const size_t SE = (size_t)p.n_psi * p.d_v;
+  const size_t E = SE + p.n_psi;
+  const size_t REC = E + (p.gated ? p.n_psi : 0);
+  const size_t e = (size_t)blockIdx.y * 4;  // E is a multiple of 4: every group is whole
+  const float lg = p.has_decay ? p.log2g[head] : 0.f;
+  auto seg_of = [&](int i) -> int { return p.reverse ? p.n_seg - 1 - i : i; };
+  float* base = p.ws + (size_t)bh * p.n_seg * REC + e;
+  const bool zpart = e >= SE;
+  const size_t row = zpart ? e - SE : e / p.d_v;
+  const float* gvec = p.ws + (size_t)bh * p.n_seg * REC + E + row;
+  int T = p.T;
+  if (p.cu_seqlens) {
+    int start;
+    T = packed_len(p.cu_seqlens, bh / p.H, p.total, p.T, &start);
+  }
+  auto seg_decay = [&](int s) -> f32x4 {
+    if (p.gated) {
+      if (zpart) return ld4(gvec + (size_t)s * REC);
+      const float a = gvec[(size_t)s * REC];
+      return f32x4{a, a, a, a};
+    }
+    const int len = max(0, min(p.seg_len, T - s * p.seg_len));
+    const float a = gpow(lg, (float)len);
+    return f32x4{a, a, a, a};
+  };
+  auto shfl_up4 = [&](const f32x4& v, int d) {
+    return f32x4{__shfl_up(v[0], d), __shfl_up(v[1], d), __shfl_up(v[2], d), __shfl_up(v[3], d)};
+  };
+
+  // the prefix of everything before the current block: init (+) X_0 (+) ...
+  f32x4 cx = {0.f, 0.f, 0.f, 0.f}, ca = {1.f, 1.f, 1.f, 1.f};
+  if (e < SE) {
+    if (p.init_S) cx = ld4(p.init_S + (size_t)bh * SE + e);
+  } else if (p.init_Z) {
+    cx = ld4(p.init_Z + (size_t)bh * p.n_psi + (e - SE));
+  }
+  int chain = 0;  // dependent (+) levels, for the diagnostic record
+  for (int blk = 0; blk < p.n_seg; blk += 64 * NW) {
+    const int s = blk + 64 * w + lane;
+    const bool in = s < p.n_seg;
+    f32x4 x = in ? ld4(base + (size_t)seg_of(s) * REC) : f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 a = in ? seg_decay(seg_of(s)) : f32x4{1.f, 1.f, 1.f, 1.f};
+    // 1. inclusive scan across the wavefront's lanes: lane l <- (lane l - d) (+) lane l
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const f32x4 xp = shfl_up4(x, d), ap = shfl_up4(a, d);
+      if (lane >= d) {
+        x = a * xp + x;
+        a = ap * a;
+      }
+    }
+    chain += 6;
+    // the lane's exclusive prefix within its wave
+    f32x4 lx = shfl_up4(x, 1), la = shfl_up4(a, 1);
+    if (lane == 0) {
+      lx = f32x4{0.f, 0.f, 0.f, 0.f};
+      la = f32x4{1.f, 1.f, 1.f, 1.f};
+    }
+    if (lane == 63) {
+      tx[w] = x;
+      ta[w] = a;
+    }
+    __syncthreads();
+    // 2. Blelloch over the NW wave totals (node w held by lane 0 of wave w)
+    for (int d = 1; d < NW; d <<= 1) {
+      ++chain;
+      const int right = (w + 1) * 2 * d - 1;
+      const bool act = lane == 0 && right < NW;
+      f32x4 nx = {0.f, 0.f, 0.f, 0.f}, na = {1.f, 1.f, 1.f, 1.f};
+      if (act) {
+        const int left = right - d;
+        nx = ta[right] * tx[left] + tx[right];
+        na = ta[left] * ta[right];
+      }
+      __syncthreads();
+      if (act) {
+        tx[right] = nx;
+        ta[right] = na;
+      }
+      __syncthreads();
+    }
+    const f32x4 bx = tx[NW - 1], ba = ta[NW - 1];  // the block's total
+    __syncthreads();
+    if (w == NW - 1 && lane == 0) {
+      tx[NW - 1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      ta[NW - 1] = f32x4{1.f, 1.f, 1.f, 1.f};
+    }
+    __syncthreads();
+    for (int d = NW >> 1; d >= 1; d >>= 1) {
+      ++chain;
+      const int right = (w + 1) * 2 * d - 1;
+      const bool act = lane == 0 && right < NW;
+      f32x4 lx2 = {0.f, 0.f, 0.f, 0.f}, px = {0.f, 0.f, 0.f, 0.f};
+      f32x4 la2 = {1.f, 1.f, 1.f, 1.f}, pa = {1.f, 1.f, 1.f, 1.f};
+      if (act) {
+        const int left = right - d;
+        lx2 = tx[left];
+        la2 = ta[left];
+        px = tx[right];
+        pa = ta[right];
+      }
+      __syncthreads();
+      if (act) {
+        const int left = right - d;
+        tx[left] = px;
+        tx[right] = la2 * px + lx2;
+        ta[left] = pa;
+        ta[right] = pa * la2;
+      }
+      __syncthreads();
+    }
+    // 3. the segment's exclusive prefix: carry (+) wave prefix (+) lane prefix
+    const f32x4 wx = tx[w], wa = ta[w];
+    const f32x4 px = wa * cx + wx, pa = ca * wa;
+    if (in) st4(base + (size_t)seg_of(s) * REC, la * px + lx);
+    chain += 2;
+    (void)pa;
+    // 4. carry the block's total
+    cx = ba * cx + bx;
+    ca = ca * ba;
+    __syncthreads();  // the wave totals are rewritten by the next block
+  }
+  if (p.rounds && threadIdx.x == 0 && blockIdx.y == 0) atomicMax(p.rounds, chain);
+  // 5. the final state: the prefix of all segments
+  if (threadIdx.x == 0) {
     if (e < SE) {
       if (p.final_S) st4(p.final_S + (size_t)bh * SE + e, cx);
     } else if (p.final_Z) {
@@ -235,12 +363,20 @@ hipError_t launch_segment_scan(const ScanParams& p, hipStream_t s) {
   const size_t E = (size_t)p.n_psi * p.d_v + p.n_psi;
   dim3 grid(p.BH, (unsigned)((E + 256 * G - 1) / (256 * G)));
   const dim3 block(64 * W * G);
+  if (per > 8) {  // many segments: lanes over segments (log-depth within each block of 64 NW)
+    const dim3 lgrid(p.BH, (unsigned)(E / 4));
+    if (p.n_seg <= 256)
+      hipLaunchKernelGGL(k_segment_scan_lanes<4>, lgrid, dim3(256), 0, s, p);
+    else if (p.n_seg <= 512)
+      hipLaunchKernelGGL(k_segment_scan_lanes<8>, lgrid, dim3(512), 0, s, p);
+    else
+      hipLaunchKernelGGL(k_segment_scan_lanes<16>, lgrid, dim3(1024), 0, s, p);
+    return hipGetLastError();
+  }
   if (per <= 4)
     hipLaunchKernelGGL(k_segment_scan<4>, grid, block, 0, s, p);
-  else if (per <= 8)
-    hipLaunchKernelGGL(k_segment_scan<8>, grid, block, 0, s, p);
   else
-    hipLaunchKernelGGL(k_segment_scan<0>, grid, block, 0, s, p);
+    hipLaunchKernelGGL(k_segment_scan<8>, grid, block, 0, s, p);
   return hipGetLastError();
 }
 

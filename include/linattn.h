@@ -364,14 +364,19 @@ la_status lin_attn_decode_step_gated(const la_decode_desc* d, const void* q, con
                                      const float* log_gate, const void* prf_w, float* S, float* Z, void* o,
                                      hipStream_t stream);
 
-/* Diagnostic: the depth of the segment scan ("Log-Depth Chunked Linear-Attention Scan",
+/* Diagnostic: the segment scan and its depth ("Log-Depth Chunked Linear-Attention Scan",
  * Verification: the scan's round count is the check of its log depth). Runs the scan the
- * prefill runs, on one sequence of n_seg segments with 4 x 4 states, and raises *rounds to
- * the length of its longest chain of dependent (+) steps: each wave folds a run of up to
- * ceil(n_seg / W) segments (W waves, a power of two <= 16), a Blelloch tree takes log2 W
- * levels up and log2 W down, one step carries the initial state, and the run is rewritten
- * with its prefixes, so rounds = 2 ceil(n_seg / W) + 2 log2 W + 1.
- *   ws:     device fp32, n_seg * 20 floats, 16-byte aligned; overwritten (contents arbitrary).
+ * prefill runs on one sequence of n_seg segments with 4 x 4 states and no decay, replacing
+ * each record with its exclusive prefix, and raises *rounds to the number of dependent (+)
+ * levels the kernel executed:
+ *   n_seg <= 128: W waves (a power of two <= 16) fold runs of up to ceil(n_seg / W) segments
+ *     in sequence, a Blelloch tree takes log2 W levels up and log2 W down, one step carries
+ *     the initial state and each run is rewritten: 2 ceil(n_seg / W) + 2 log2 W + 1;
+ *   n_seg > 128: lanes hold segments; per block of 64 NW segments (NW = 4, 8 or 16 waves)
+ *     6 lane-shift rounds, log2 NW levels up and down, and 2 combines with the carried
+ *     prefix: ceil(n_seg / (64 NW)) (8 + 2 log2 NW).
+ *   ws:     device fp32, n_seg records of 20 floats (S row-major 4 x 4, then Z), 16-byte
+ *           aligned; on return record s holds the sum of records 0 .. s-1.
  *   rounds: device int32, set by the caller (e.g. to 0) before the call; raised by atomic max.
  * Errors: LA_ERR_NULL, LA_ERR_SHAPE (n_seg outside 1 .. 65535), LA_ERR_ALIGN, LA_ERR_HIP.
  * Asynchronous on `stream`. */

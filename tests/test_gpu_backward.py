@@ -357,6 +357,8 @@ PRF_CASES = [
     ("qshift128_decay_state", PSI_PRF_QSHIFT, 128, 1, "const:0.99", 1, 2, 222, 64, True, "f32", "bhtd", 1.0),
     # queries 4x larger: the shift keeps every query feature finite (the largest is 1/sqrt(n_psi))
     ("qshift256_large_queries", PSI_PRF_QSHIFT, 256, 1, "const:0.995", 1, 2, 200, 64, False, "f32", "bhtd", 4.0),
+    # 141 steps of 64 tokens: the per-step records take the many-segment scan, forward and reversed
+    ("prf128_many_steps_state", PSI_PRF, 128, 1, "const:0.999", 1, 1, 9000, 64, True, "f32", "bhtd", 1.0),
 ]
 
 

@@ -476,22 +476,68 @@ def test_more_sequences_than_65535():
     assert_close(o.cpu().reshape(w.B * w.H, w.T, w.d_v).numpy(), ref, "bf16", w.name)
 
 
-@pytest.mark.parametrize("n_seg", [1, 2, 3, 4, 5, 8, 16, 17, 64, 65, 100, 1024, 4096, 65535])
+@pytest.mark.parametrize("n_seg", [1, 2, 3, 4, 5, 8, 16, 17, 64, 65, 100, 128, 129, 256, 257, 600, 1024, 1025, 4096,
+                                   65535])
 def test_scan_depth_record(n_seg):
     """The segment scan's depth as the kernel counts it while it runs ("Log-Depth Chunked
-    Linear-Attention Scan", Verification: the round count is the check of the scan's depth).
-    W waves (a power of two, at most 16, about 4 segments each) fold their runs in sequence,
-    a Blelloch tree over the W totals takes log2 W levels up and log2 W down, one step
-    carries the initial state, and each run is rewritten with its prefixes: the longest
-    chain of dependent combine steps is 2 ceil(n / W) + 2 log2 W + 1. Up to 64 segments that
-    stays within 2 * 4 + 2 * 4 + 1 = 17 steps; beyond it the runs grow linearly."""
-    W = 1
-    while W < 16 and W * 4 < n_seg:
-        W *= 2
-    want = 2 * (-(-n_seg // W)) + 2 * (W.bit_length() - 1) + 1
+    Linear-Attention Scan", Verification: the round count is the check of the scan's depth),
+    and its result. Up to 128 segments, W waves (a power of two, at most 16, about 4
+    segments each) fold their runs in sequence, a Blelloch tree over the W totals takes
+    log2 W levels up and log2 W down, one step carries the initial state and each run is
+    rewritten: 2 ceil(n / W) + 2 log2 W + 1 levels, at most 17 up to 64 segments. Beyond 128
+    the lanes hold segments: per block of 64 NW segments, 6 rounds of lane shifts
+    (Hillis-Steele across a wavefront), log2 NW levels up and down across the waves
+    (Blelloch) and 2 combines with the carried prefix: ceil(n / (64 NW)) (8 + 2 log2 NW), 16
+    levels for 1024 segments. Integer-valued records make every prefix exact in fp32, so the
+    exclusive prefixes must equal the host's cumulative sums bit for bit."""
+    if n_seg <= 128:
+        W = 1
+        while W < 16 and W * 4 < n_seg:
+            W *= 2
+        want = 2 * (-(-n_seg // W)) + 2 * (W.bit_length() - 1) + 1
+    else:
+        NW = 4 if n_seg <= 256 else 8 if n_seg <= 512 else 16
+        want = (-(-n_seg // (64 * NW))) * (8 + 2 * (NW.bit_length() - 1))
     announce(f"scan depth n_seg={n_seg}")
-    got = binding.scan_depth(n_seg)
-    print(f"[scan depth] n_seg={n_seg} W={W} rounds={got} (ceil(log2 n) = {(n_seg - 1).bit_length()})", flush=True)
+    gen = torch.Generator().manual_seed(n_seg)
+    rec = torch.randint(-8, 9, (n_seg, 20), generator=gen).to(torch.float32)
+    got, pre = binding.scan_depth(n_seg, rec)
+    print(f"[scan depth] n_seg={n_seg} rounds={got} (ceil(log2 n) = {(n_seg - 1).bit_length()})", flush=True)
     assert got == want
     if n_seg <= 64:
         assert got <= 17
+    ref = torch.cumsum(rec.double(), 0) - rec.double()
+    assert torch.equal(pre.cpu().double(), ref)
+
+
+@pytest.mark.parametrize("psi,decay", [(PSI_IDENTITY, "retnet_spread"), (PSI_ELU1, "const:0.9995")])
+def test_long_sequence_many_segments(psi, decay):
+    """A sequence long enough for more than 128 segments (300,000 tokens: 247 segments of
+    1216 tokens), so the segment scan runs its many-segment form (lanes over segments), with
+    an initial state handed in and the final state taken out. Every output and the final
+    state are compared with the oracle."""
+    normalize = 1 if psi == PSI_ELU1 else 0
+    w = Workload(name="long_many_segments", B=1, H=1, T=300000, d_k=64, d_v=64, n_psi=64, chunk=64, psi=psi,
+                 normalize=normalize, eps=1e-6, dtype="bf16", seed=29, qk_scale=(64 ** -0.5) if psi == PSI_IDENTITY else 0.5,
+                 v_scale=1.0, decay=decay)
+    announce(f"prefill long sequence psi={psi} T={w.T}")
+    inp = inputs.make_prefill_inputs(w, device="cpu")
+    gen = torch.Generator().manual_seed(31)
+    S0 = (torch.randn((1, 1, 64, 64), generator=gen) * 0.1).float()
+    Z0 = (torch.rand((1, 1, 64), generator=gen) + 0.5).float()
+    fS = torch.empty((1, 1, 64, 64), device=DEV)
+    fZ = torch.empty((1, 1, 64), device=DEV)
+    dinp = _to_dev(inp)
+    o = binding.lin_attn_prefill(dinp["q"], dinp["k"], dinp["v"], psi=psi, chunk=64, normalize=normalize, eps=w.eps,
+                                 gamma=None if inp["gamma"] is None else list(inp["gamma"]), init_S=S0.to(DEV),
+                                 init_Z=Z0.to(DEV) if normalize else None, final_S=fS,
+                                 final_Z=fZ if normalize else None)
+    torch.cuda.synchronize()
+    ref, rS, rZ = oracle_blocks(w, inp, S0=S0.double().numpy().reshape(1, 64, 64),
+                                Z0=Z0.double().numpy().reshape(1, 64) if normalize else None, want_state=True)
+    assert_close(o.cpu().reshape(1, w.T, 64).numpy(), ref, "bf16", "long sequence outputs")
+    sref = rS.reshape(1, 64, 64)
+    rel = float(np.linalg.norm(fS.cpu().double().numpy().reshape(1, 64, 64) - sref) / np.linalg.norm(sref))
+    print(f"[parity] long sequence final S rel_l2={rel:.3e}", flush=True)
+    assert rel <= 2e-3
+
