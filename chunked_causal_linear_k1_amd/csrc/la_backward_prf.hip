@@ -751,13 +751,16 @@ __global__ __launch_bounds__(PNT) void k_bwd_prf_key(BackwardParams bp) {
 // their operand reads are 16-byte rows of this copy.
 __global__ __launch_bounds__(256) void k_bank_transpose(const uint16_t* __restrict__ w, uint16_t* __restrict__ wt,
                                                         int np) {
-  const int h = blockIdx.x;
+  // one 32 x 32 tile per workgroup, through LDS, so that both the reads and the writes are rows
+  __shared__ uint16_t t[32][34];
+  constexpr int NTD = PD / 32;
+  const int h = blockIdx.x, p0 = (blockIdx.y / NTD) * 32, d0 = (blockIdx.y % NTD) * 32;
   const uint16_t* src = w + (size_t)h * np * PD;
   uint16_t* dst = wt + (size_t)h * np * PD;
-  for (int i = threadIdx.x; i < np * PD; i += 256) {
-    const int pp = i / PD, d = i % PD;
-    dst[(size_t)d * np + pp] = src[i];
-  }
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  for (int r = ty; r < 32; r += 8) t[r][tx] = src[(size_t)(p0 + r) * PD + d0 + tx];
+  __syncthreads();
+  for (int r = ty; r < 32; r += 8) dst[(size_t)(d0 + r) * np + p0 + tx] = t[tx][r];
 }
 
 template <int NP, bool DECAY, bool NORM, bool DBF, bool QS>
@@ -797,7 +800,9 @@ bool prefill_backward_prf_supported(int C, int d_k, int d_v, int n_psi) {
 }
 
 hipError_t launch_bank_transpose(const void* w, uint16_t* wt, int H, int n_psi, hipStream_t s) {
-  hipLaunchKernelGGL(k_bank_transpose, dim3(H), dim3(256), 0, s, (const uint16_t*)w, wt, n_psi);
+  if (n_psi % 32 != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_bank_transpose, dim3(H, (n_psi / 32) * (PD / 32)), dim3(256), 0, s, (const uint16_t*)w, wt,
+                     n_psi);
   return hipGetLastError();
 }
 
