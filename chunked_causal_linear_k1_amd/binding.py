@@ -446,14 +446,15 @@ def lin_attn_prefill_gated(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, lo
 def lin_attn_decode_step_gated(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_gate: torch.Tensor,
                                S: torch.Tensor, Z: Optional[torch.Tensor], *, psi: int, normalize: int = 1,
                                eps: float = 1e-6, prf_w: Optional[torch.Tensor] = None,
-                               o: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+                               o: Optional[torch.Tensor] = None, stream=None,
+                               out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
     """One gated decode step: q, k, v [N, H, d], log_gate fp32 [N, H, n_psi]; S, Z in place."""
     N, H, d_k = q.shape
     d_v = v.shape[-1]
     n_psi = S.shape[-2]
-    desc = DecodeDesc(N, H, d_k, d_v, n_psi, psi, normalize, eps, _dtype_code(q), LA_F32)
     if o is None:
-        o = torch.empty((N, H, d_v), dtype=torch.float32, device=q.device)
+        o = torch.empty((N, H, d_v), dtype=out_dtype, device=q.device)
+    desc = DecodeDesc(N, H, d_k, d_v, n_psi, psi, normalize, eps, _dtype_code(q), _dtype_code(o))
     st = load().lin_attn_decode_step_gated(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_gate),
                                            _ptr(prf_w), _ptr(S), _ptr(Z), _ptr(o), _stream(stream))
     if st != LA_OK:
@@ -464,14 +465,16 @@ def lin_attn_decode_step_gated(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor
 def lin_attn_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, S: torch.Tensor,
                          Z: Optional[torch.Tensor], *, psi: int, normalize: int = 1, eps: float = 1e-6,
                          gamma: Optional[Sequence[float]] = None, prf_w: Optional[torch.Tensor] = None,
-                         o: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """One decode step for q, k, v [N, H, d]; S [N, H, n_psi, d_v], Z [N, H, n_psi] updated in place."""
+                         o: Optional[torch.Tensor] = None, stream=None,
+                         out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
+    """One decode step for q, k, v [N, H, d]; S [N, H, n_psi, d_v], Z [N, H, n_psi] updated in place.
+    o is out_dtype (float32, or bfloat16 = the fp32 result rounded to nearest even) unless given."""
     N, H, d_k = q.shape
     d_v = v.shape[-1]
     n_psi = S.shape[-2]
-    desc = DecodeDesc(N, H, d_k, d_v, n_psi, psi, normalize, eps, _dtype_code(q), LA_F32)
     if o is None:
-        o = torch.empty((N, H, d_v), dtype=torch.float32, device=q.device)
+        o = torch.empty((N, H, d_v), dtype=out_dtype, device=q.device)
+    desc = DecodeDesc(N, H, d_k, d_v, n_psi, psi, normalize, eps, _dtype_code(q), _dtype_code(o))
     g = _gamma_array(gamma, H)
     st = load().lin_attn_decode_step(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), g, _ptr(prf_w), _ptr(S),
                                      _ptr(Z), _ptr(o), _stream(stream))

@@ -431,7 +431,7 @@ la_status decode_impl(const la_decode_desc* d, const void* q, const void* k, con
   if (!la::is_prf(d->psi) && d->n_psi != d->d_k) return LA_ERR_SHAPE;
   if (d->psi == LA_PSI_PRF_QSHIFT && !d->normalize) return LA_ERR_UNSUPPORTED;  // as in prefill
   if ((long long)d->N * d->H > 2147483647LL) return LA_ERR_SHAPE;
-  if (d->out_dtype != LA_F32) return LA_ERR_UNSUPPORTED;
+  if (d->out_dtype == LA_BF16 && d->in_dtype != LA_BF16) return LA_ERR_UNSUPPORTED;  // as in prefill
   if (!la::decode_supported(d->d_k, d->d_v, d->n_psi, d->psi)) return LA_ERR_UNSUPPORTED;
   if (!q || !k || !v || !S || !o) return LA_ERR_NULL;
   if (d->normalize && !Z) return LA_ERR_NULL;
@@ -444,7 +444,8 @@ la_status decode_impl(const la_decode_desc* d, const void* q, const void* k, con
 
   la::DecodeParams p;
   memset(&p, 0, sizeof p);
-  p.q = q; p.k = k; p.v = v; p.prf_w = prf_w; p.S = S; p.Z = Z; p.o = (float*)o;
+  p.q = q; p.k = k; p.v = v; p.prf_w = prf_w; p.S = S; p.Z = Z; p.o = o;
+  p.out_bf16 = d->out_dtype == LA_BF16;
   p.N = d->N; p.H = d->H; p.d_k = d->d_k; p.d_v = d->d_v; p.n_psi = d->n_psi;
   p.psi = d->psi; p.normalize = d->normalize; p.eps = d->eps;
   p.in_f32 = d->in_dtype == LA_F32;

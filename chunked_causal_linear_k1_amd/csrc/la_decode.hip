@@ -22,6 +22,15 @@
 namespace la {
 namespace {
 
+// One output element: fp32, or the fp32 result rounded to bf16 (nearest even).
+__device__ __forceinline__ void store_o(const DecodeParams& p, size_t idx, float x) {
+  if (p.out_bf16)
+    ((__bf16*)p.o)[idx] = to_bf16(x);
+  else
+    ((float*)p.o)[idx] = x;
+}
+
+
 constexpr int kDecThreads = 256;   // general kernel
 constexpr int kElemThreads = 512;  // streaming kernel (elementwise features)
 constexpr int kMaxFeat = 256;
@@ -125,7 +134,7 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeParams p) {
   for (int e = tid; e < d_v; e += kDecThreads) {
     float num = 0.f;
     for (int r = 0; r < RG; ++r) num += snum[r][e];
-    p.o[(size_t)b * d_v + e] = p.normalize ? num / sden : num;
+    store_o(p, (size_t)b * d_v + e, p.normalize ? num / sden : num);
   }
 }
 
@@ -214,7 +223,7 @@ __global__ __launch_bounds__(kElemThreads) void k_decode_elem(DecodeParams p) {
       for (int ww = 0; ww < (D + 63) / 64; ++ww) den += sDen[ww];
       num /= den;
     }
-    p.o[(size_t)b * D + tid] = num;
+    store_o(p, (size_t)b * D + tid, num);
   }
 }
 

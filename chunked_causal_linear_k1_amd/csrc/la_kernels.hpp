@@ -96,7 +96,8 @@ struct DecodeParams {
   const void* prf_w;
   float* S;
   float* Z;
-  float* o;
+  void* o;               // [N, H, d_v]: fp32, or bf16 (the fp32 result rounded to nearest even) with out_bf16
+  int out_bf16;
   int N, H;
   int d_k, d_v, n_psi;
   int psi;

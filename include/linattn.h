@@ -329,7 +329,8 @@ typedef struct {
   int32_t normalize;
   float eps;
   int32_t in_dtype;  /* la_dtype of q, k, v, prf_w */
-  int32_t out_dtype; /* la_dtype of o (LA_F32 only in this build) */
+  int32_t out_dtype; /* la_dtype of o: LA_F32, or LA_BF16 with bf16 inputs (the fp32
+                        result rounded to nearest even)                          */
 } la_decode_desc;
 
 /* Supported: in_dtype LA_BF16 or LA_F32; d_k == d_v in {64, 128}; psi identity

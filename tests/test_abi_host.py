@@ -345,6 +345,10 @@ def test_decode_validation():
     assert call(DecodeDesc(**dict(ok, psi=3, n_psi=256, normalize=0)), prf=fake) == LA_ERR_UNSUPPORTED
     assert call(DecodeDesc(**ok), S=ctypes.c_void_p((1 << 20) + 8)) == LA_ERR_ALIGN
     assert lib.lin_attn_decode_step(None, fake, fake, fake, None, None, fake, fake, fake, None) == LA_ERR_NULL
+    # bf16 output: with bf16 inputs only (as in prefill), an unknown dtype is a value error
+    assert call(DecodeDesc(**dict(ok, out_dtype=LA_BF16, in_dtype=LA_F32))) == LA_ERR_UNSUPPORTED
+    assert call(DecodeDesc(**dict(ok, out_dtype=7))) == LA_ERR_VALUE
+    assert call(DecodeDesc(**dict(ok, out_dtype=LA_BF16)), S=ctypes.c_void_p((1 << 20) + 8)) == LA_ERR_ALIGN
 
 
 def test_decay_head_limit():

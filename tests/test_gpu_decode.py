@@ -154,3 +154,35 @@ def test_prefill_to_decode_handoff():
     ref = oracle.prefill(inp["q"].reshape(6, P + n, d), inp["k"].reshape(6, P + n, d), inp["v"].reshape(6, P + n, d),
                          PSI_ELU1, gamma=[gam[b % 3] for b in range(6)], normalize=1, eps=float(np.float32(1e-6)))
     assert_close(got, ref[:, P:], "bf16", "decode after prefill")
+
+
+@pytest.mark.parametrize("psi,n_psi,gated", [(PSI_ELU1, 128, False), (PSI_IDENTITY, 64, False), (PSI_PRF, 256, False),
+                                             (PSI_ELU1, 128, True)])
+def test_decode_bf16_output_is_rounded_fp32(psi, n_psi, gated):
+    """bf16 outputs of the decode step are the fp32 outputs rounded to nearest even, bit for bit:
+    two copies of one state take the same step, one writing fp32 and one bf16, and end in
+    bitwise equal states."""
+    d = 128 if psi == PSI_PRF else n_psi
+    N, H = 4, 6
+    announce(f"decode bf16 output psi={psi} n_psi={n_psi} gated={gated}")
+    gen = torch.Generator().manual_seed(91 + psi)
+    q, k, v = ((torch.randn((N, H, d), generator=gen) * 0.5).to(torch.bfloat16).to(DEV) for _ in range(3))
+    S = (torch.randn((N, H, n_psi, d), generator=gen) * 0.1).abs().to(DEV)
+    Z = (torch.rand((N, H, n_psi), generator=gen) + 1.0).to(DEV)
+    prf = (torch.randn((H, n_psi, d), generator=gen)).to(torch.bfloat16).to(DEV) if psi == PSI_PRF else None
+    lg = (torch.rand((N, H, n_psi), generator=gen) * -0.1).to(DEV) if gated else None
+    outs, states = [], []
+    for dt in (torch.float32, torch.bfloat16):
+        S1, Z1 = S.clone(), Z.clone()
+        if gated:
+            o = binding.lin_attn_decode_step_gated(q, k, v, lg, S1, Z1, psi=psi, normalize=1, prf_w=prf, out_dtype=dt)
+        else:
+            o = binding.lin_attn_decode_step(q, k, v, S1, Z1, psi=psi, normalize=1, gamma=[0.99] * H, prf_w=prf,
+                                             out_dtype=dt)
+        torch.cuda.synchronize()
+        outs.append(o)
+        states.append((S1, Z1))
+    assert outs[1].dtype == torch.bfloat16
+    assert torch.equal(outs[0].to(torch.bfloat16), outs[1])
+    assert torch.equal(states[0][0], states[1][0]) and torch.equal(states[0][1], states[1][1])
+
