@@ -297,16 +297,18 @@ def bench_decode(w: workloads.DecodeWorkload, steps: int, warmup: int, replicas:
 
 
 def copy_probe(mib: int):
-    """One plain device-to-device copy of mib MiB: the reference kernel for scaling the HBM byte
-    counters (FETCH_SIZE, WRITE_SIZE) of a counter run to bytes."""
-    n = mib * (1 << 20) // 4
-    a = torch.ones(n, dtype=torch.float32, device="cuda")
-    b = torch.empty_like(a)
-    torch.cuda.synchronize()
-    torch.neg(a, out=b)  # one elementwise kernel, the only negation in the run: reads mib MiB, writes mib MiB
-    torch.cuda.synchronize()
-    del a, b
-    torch.cuda.empty_cache()
+    """Plain device-to-device copies of mib MiB and then mib/4 MiB: the reference kernels for
+    scaling the HBM byte counters (FETCH_SIZE, WRITE_SIZE) of a counter run to bytes (two sizes,
+    so that the scale is shown not to depend on the size)."""
+    for size in (mib, mib // 4):
+        n = size * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        torch.neg(a, out=b)  # one elementwise kernel, the only negations in the run: reads size MiB, writes size MiB
+        torch.cuda.synchronize()
+        del a, b
+        torch.cuda.empty_cache()
 
 
 def host_threads() -> int:
@@ -439,7 +441,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="headline workload only (no 8k elu+1, PRF, layout, bf16-output, gated, backward and packed-batch lines)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
-                    help="first run one plain copy of MIB MiB (counter calibration)")
+                    help="first run plain copies of MIB and MIB/4 MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported by this build "

@@ -3,7 +3,8 @@
 Reads the counter_collection CSV of a FETCH_SIZE run and of a WRITE_SIZE run (both in KiB
 per dispatch), scales each counter by what it reads for a plain copy kernel of known
 size in the same run (the --copy-probe of bench.py: the negation of an fp32 vector into
-another, reading and writing MIB MiB each), and writes bytes per launch for the prefill
+another, reading and writing MIB MiB each, then MIB/4 MiB; the two sizes must agree on the
+scale within 1%), and writes bytes per launch for the prefill
 and decode kernels to profiles/traffic.json, stamped with a hash of the kernel sources
 so that bench.py can tell when the figures no longer describe the current kernels.
 
@@ -58,7 +59,7 @@ def read_counter(run_dir: str, counter: str) -> dict:
                 if r["Counter_Name"] != counter:
                     continue
                 per[r["Kernel_Name"]][r["Dispatch_Id"]] += float(r["Counter_Value"])
-    return {k: list(v.values()) for k, v in per.items()}
+    return {k: [v[d] for d in sorted(v, key=int)] for k, v in per.items()}  # in dispatch order
 
 
 def pick(per: dict, sub: str):
@@ -69,14 +70,23 @@ def pick(per: dict, sub: str):
 def main(fetch_dir: str, write_dir: str, copy_mib: int, path: str = "") -> dict:
     fetch = read_counter(fetch_dir, "FETCH_SIZE")
     write = read_counter(write_dir, "WRITE_SIZE")
-    copy_kib = copy_mib * 1024.0
-    f_copy, w_copy = pick(fetch, COPY_KERNEL), pick(write, COPY_KERNEL)
-    if not f_copy or not w_copy:
-        raise RuntimeError("copy probe kernel not found in the counter runs")
-    fs, ws = copy_kib / f_copy, copy_kib / w_copy
+    # the probe runs the copy twice, copy_mib MiB and then a quarter of it: both sizes must give
+    # the same scale for the counters to be read as bytes
+    fl = [x for name, xs in fetch.items() if COPY_KERNEL in name for x in xs]
+    wl = [x for name, xs in write.items() if COPY_KERNEL in name for x in xs]
+    if len(fl) < 2 or len(wl) < 2:
+        raise RuntimeError("the two copy probe dispatches were not found in the counter runs")
+    sizes_kib = (copy_mib * 1024.0, copy_mib * 256.0)
+    fsc = [sizes_kib[i] / fl[i] for i in range(2)]
+    wsc = [sizes_kib[i] / wl[i] for i in range(2)]
+    for a, b in (fsc, wsc):
+        if abs(a - b) > 0.01 * a:
+            raise RuntimeError(f"copy probe scales disagree between sizes: {a:.4f} vs {b:.4f}")
+    fs, ws = fsc[0], wsc[0]
     out = {"source_hash": source_hash(),
-           "calibration": {"copy_MiB": copy_mib, "fetch_KiB_read": f_copy, "write_KiB_read": w_copy,
-                           "fetch_scale": fs, "write_scale": ws}}
+           "calibration": {"copy_MiB": [copy_mib, copy_mib // 4], "fetch_KiB_read": fl[:2], "write_KiB_read": wl[:2],
+                           "fetch_scale": fs, "write_scale": ws, "fetch_scale_small": fsc[1],
+                           "write_scale_small": wsc[1]}}
     for sub, key in KERNELS.items():
         f, w = pick(fetch, sub), pick(write, sub)
         if f is None or w is None:
