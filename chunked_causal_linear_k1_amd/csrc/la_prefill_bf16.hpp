@@ -40,7 +40,9 @@
 // when it multiplies psi(Q), the score tile A, and K~_i = gamma^(L-1-i) psi(k_i)
 // in the state update, so the carried state is accurate to about 2^-16. In the
 // score tile psi(q) and psi(k) of elu+1 are rounded to bf16 once; numerator and
-// denominator use the same rounded scores.
+// denominator use the same rounded scores. With elu+1 features, a denominator and no decay,
+// the output pass also rounds S (in psi(Q) S) and psi(k) (in the state update) to bf16 once
+// (see k_output_w8); the summary pass keeps them hi + lo.
 #pragma once
 #include "la_device.hpp"
 #include "la_kernels.hpp"
@@ -893,6 +895,12 @@ __global__ __launch_bounds__(512) void k_output_w8(PrefillParams p) {
   static_assert(G::RSTEP % 16 == 0, "piece rows advance in multiples of 16 (swizzle period)");
   static_assert(G::NJ == 2 && G::PPR == 16, "two token tiles, one DPP row per token row");
   constexpr bool SPLIT = DECAY || ELU;
+  // elu+1 features with a denominator and no decay: the state and psi(k) enter the outputs
+  // rounded to bf16 once (the features are positive and the outputs are ratios of sums over all
+  // of them, so single roundings average out: see the precision readings); the score tiles stay
+  // hi + lo. Elsewhere, and in the summary pass that gives the final state, every inexact
+  // operand is hi + lo.
+  constexpr bool PLAIN = ELU && NORM && !DECAY;
   constexpr int NJ = G::NJ, NPC = G::NPC, RSTEP = G::RSTEP, NPH = G::NPH;
   constexpr int PQ = G::PQ, PA = G::PA;
   constexpr int KLO = G::K_BYTES;
@@ -1010,6 +1018,13 @@ __global__ __launch_bounds__(512) void k_output_w8(PrefillParams p) {
       float f[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) f[j] = elu1(from_bf16(x[j])) * live;
+      if (PLAIN) {
+        bf16x8 y;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) y[j] = to_bf16(f[j]);
+        *(bf16x8*)(kP + off) = y;
+        continue;
+      }
       bf16x8 hi, lo;
       split8_trunc(f, hi, lo);
       *(bf16x8*)(kP + off) = hi;
@@ -1081,7 +1096,12 @@ __global__ __launch_bounds__(512) void k_output_w8(PrefillParams p) {
         float x[8];
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) x[jj] = S[j][8 * q + jj];
-        split8_trunc(x, sh[q], sl[q]);
+        if (PLAIN) {
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) sh[q][jj] = to_bf16(x[jj]);
+        } else {
+          split8_trunc(x, sh[q], sl[q]);
+        }
       }
       const int fcol = (NPH * fh + (j + rot) % NPH) * 32;
 #pragma unroll
@@ -1091,7 +1111,7 @@ __global__ __launch_bounds__(512) void k_output_w8(PrefillParams p) {
           const unsigned char* qa = qC + (jt * 32 * PQ + fcol + 16 * q) * 2;
           const bf16x8 qo = cat8(*(const bf16x4*)qa, *(const bf16x4*)(qa + 16));
           num[jt] = mfma32(sh[q], qo, num[jt]);
-          num[jt] = mfma32(sl[q], qo, num[jt]);
+          if (!PLAIN) num[jt] = mfma32(sl[q], qo, num[jt]);
         }
     }
     if (DECAY) {
@@ -1173,7 +1193,7 @@ __global__ __launch_bounds__(512) void k_output_w8(PrefillParams p) {
       for (int j = 0; j < NPH; ++j) S[j] *= a;
     }
     {
-      constexpr int NK = C / 16, KP = SPLIT ? 2 : 1, NM = KP * NPH;
+      constexpr int NK = C / 16, KP = (SPLIT && !PLAIN) ? 2 : 1, NM = KP * NPH;
       const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
       f32x16 zc = f32x16{};
       bf16x8 ops[2][1 + NM];
@@ -1183,7 +1203,7 @@ __global__ __launch_bounds__(512) void k_output_w8(PrefillParams p) {
 #pragma unroll
         for (int j = 0; j < NPH; ++j) {
           o[1 + KP * j] = cat8(lds_read_tr4((const __bf16*)(kT[j][0] + ko)), lds_read_tr4((const __bf16*)(kT[j][1] + ko)));
-          if (SPLIT)
+          if (KP == 2)
             o[2 + 2 * j] = cat8(lds_read_tr4((const __bf16*)(kT[j][0] + ko + KLO)),
                                 lds_read_tr4((const __bf16*)(kT[j][1] + ko + KLO)));
         }
@@ -1196,11 +1216,11 @@ __global__ __launch_bounds__(512) void k_output_w8(PrefillParams p) {
 #pragma unroll
         for (int j = 0; j < NPH; ++j) {
           S[j] = mfma32(o[1 + KP * j], o[0], S[j]);
-          if (SPLIT) S[j] = mfma32(o[2 + 2 * j], o[0], S[j]);
+          if (KP == 2) S[j] = mfma32(o[2 + 2 * j], o[0], S[j]);
         }
         if (NORM && zw) {
           zc = mfma32(ones, o[1], zc);
-          if (SPLIT) zc = mfma32(ones, o[2], zc);
+          if (KP == 2) zc = mfma32(ones, o[2], zc);
         }
         if (ik + 1 < NK) {
           __builtin_amdgcn_sched_group_barrier(0x100, 2 * (1 + NM), 0);
