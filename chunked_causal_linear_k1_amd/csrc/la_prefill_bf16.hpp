@@ -1085,9 +1085,13 @@ __global__ __launch_bounds__(512) void k_output_w8(PrefillParams p) {
     // The inter-chunk part over this wave's state rows for both token tiles (S split into
     // hi + lo one tile at a time), theta-weighted; then the intra-chunk term V^T A^T for
     // token tile fh, the tile this half finishes.
+    // num[0] accumulates token tile fh (the one this half finishes), num[1] the other half's
+    // tile (handed over through LDS): the accumulators are named by role, so no per-register
+    // select between the tiles is needed afterwards
     f32x16 num[NJ];
 #pragma unroll
-    for (int jt = 0; jt < NJ; ++jt) num[jt] = f32x16{};
+    for (int u = 0; u < NJ; ++u) num[u] = f32x16{};
+    const int jtu[2] = {fh, 1 - fh};
 #pragma unroll
     for (int j = 0; j < NPH; ++j) {
       bf16x8 sh[2], sl[2];
@@ -1105,20 +1109,20 @@ __global__ __launch_bounds__(512) void k_output_w8(PrefillParams p) {
       }
       const int fcol = (NPH * fh + (j + rot) % NPH) * 32;
 #pragma unroll
-      for (int jt = 0; jt < NJ; ++jt)
+      for (int u = 0; u < NJ; ++u)
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-          const unsigned char* qa = qC + (jt * 32 * PQ + fcol + 16 * q) * 2;
+          const unsigned char* qa = qC + (jtu[u] * 32 * PQ + fcol + 16 * q) * 2;
           const bf16x8 qo = cat8(*(const bf16x4*)qa, *(const bf16x4*)(qa + 16));
-          num[jt] = mfma32(sh[q], qo, num[jt]);
-          if (!PLAIN) num[jt] = mfma32(sl[q], qo, num[jt]);
+          num[u] = mfma32(sh[q], qo, num[u]);
+          if (!PLAIN) num[u] = mfma32(sl[q], qo, num[u]);
         }
     }
     if (DECAY) {
 #pragma unroll
-      for (int jt = 0; jt < NJ; ++jt) num[jt] *= fN[G::F_THETA + jt * 32];
+      for (int u = 0; u < NJ; ++u) num[u] *= fN[G::F_THETA + jtu[u] * 32];
     }
-    f32x16 mine = fh ? num[1] : num[0];
+    f32x16 mine = num[0];
     {
       // the intra-chunk term of token tile fh: it = 0 .. fh (a wave-uniform trip count)
       for (int it = 0; it <= fh; ++it) {
@@ -1132,7 +1136,7 @@ __global__ __launch_bounds__(512) void k_output_w8(PrefillParams p) {
           mine = mfma32(vv, *(const bf16x8*)(at + 32 * q + ALO), mine);
         }
       }
-      const f32x16 give = fh ? num[0] : num[1];
+      const f32x16 give = num[1];
       f32x4* const xo = (f32x4*)(xch + (cb * NJ + (1 - fh)) * 16 * 64);
 #pragma unroll
       for (int q = 0; q < 4; ++q) xo[q * 64] = f32x4{give[4 * q], give[4 * q + 1], give[4 * q + 2], give[4 * q + 3]};
