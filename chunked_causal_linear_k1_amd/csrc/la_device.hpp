@@ -266,8 +266,9 @@ __device__ __forceinline__ float row16_sum(float v) {
 
 // 2^x by the hardware instruction alone (about 1 ulp), without the library's rescaling of
 // arguments below -126: results under the smallest normal float flush to zero. Used for
-// feature values, where such a value is lost against the fp32 rounding of any sum it enters;
-// the library form spends four more VALU instructions per value on that range.
+// feature values and for decay factors gamma^n (n >= 0), where such a value is lost against the
+// fp32 rounding of any sum it enters; the library form spends four more VALU instructions per
+// value on that range.
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
 }  // namespace la

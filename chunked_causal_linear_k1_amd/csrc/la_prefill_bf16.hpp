@@ -132,7 +132,7 @@ __device__ __forceinline__ void commit_k(const Pieces<C, D>& P, __bf16* sK, __bf
   for (int i = 0; i < Geo<C, D, true>::NPC; ++i) {
     const int row = piece_row<C, D>(i), c8 = piece_cols<C, D>(i);
     const float live = row < L ? 1.f : 0.f;
-    const float xi = DECAY ? live * exp2f((float)(L - 1 - row) * lg) : live;
+    const float xi = row < L ? (DECAY ? exp2_hw((float)(L - 1 - row) * lg) : 1.f) : 0.f;
     const float xs = FOLD ? xi : live;
     const bf16x8 x = __builtin_bit_cast(bf16x8, P.r[i]);
     bf16x8 hi, lo;
@@ -269,7 +269,7 @@ __global__ __launch_bounds__(2 * D) void k_summary(PrefillParams p) {
   load_pieces<C, D>(pv, vb + (size_t)c0 * C * rse, L0, rsb);
   for (int c = c0; c < c1; ++c) {
     const int L = min(C, T - c * C);
-    const float a = DECAY ? exp2f((float)L * lg) : 1.f;
+    const float a = DECAY ? exp2_hw((float)L * lg) : 1.f;
     lds_barrier();  // the previous chunk is done with LDS
     float zp[8];
 #pragma unroll
@@ -277,7 +277,7 @@ __global__ __launch_bounds__(2 * D) void k_summary(PrefillParams p) {
     commit_k<C, D, ELU, DECAY, !VDEC, SPLIT>(pk, sK, sKlo, G::PK, L, lg, zp);
     commit_v<C, D>(pv, sV, G::PK);
     if (VDEC) {
-      for (int j = tid; j < C; j += 2 * D) sF[G::F_XI + j] = j < L ? exp2f((float)(L - 1 - j) * lg) : 0.f;
+      for (int j = tid; j < C; j += 2 * D) sF[G::F_XI + j] = j < L ? exp2_hw((float)(L - 1 - j) * lg) : 0.f;
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) zrun[j] = a * zrun[j] + zp[j];
@@ -449,7 +449,7 @@ void k_output_sh(PrefillParams p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) S[pt][r] = pre[(size_t)(pt * 32 + dtile_row(r, lane)) * D + Ew + n];
   if (tid < D) sF[G::F_Z + tid] = NORM ? pre[(size_t)D * D + tid] : 0.f;
-  for (int j = tid; j < C; j += 2 * D) sF[G::F_THETA + j] = DECAY ? exp2f((float)(j + 1) * lg) : 1.f;
+  for (int j = tid; j < C; j += 2 * D) sF[G::F_THETA + j] = DECAY ? exp2_hw((float)(j + 1) * lg) : 1.f;
 
   // this lane's score-tile factors (column j%32 = n and register rows fixed):
   // diagonal tile gamma^(n - i_r) masked to i_r <= n; off-diagonal base gamma^(n + 32 - i_r)
@@ -457,8 +457,8 @@ void k_output_sh(PrefillParams p) {
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int ir = dtile_row(r, lane);
-    fdiag[r] = ir <= n ? (DECAY ? exp2f((float)(n - ir) * lg) : 1.f) : 0.f;
-    foff[r] = DECAY ? exp2f((float)(n + 32 - ir) * lg) : 1.f;
+    fdiag[r] = ir <= n ? (DECAY ? exp2_hw((float)(n - ir) * lg) : 1.f) : 0.f;
+    foff[r] = DECAY ? exp2_hw((float)(n + 32 - ir) * lg) : 1.f;
   }
 
   const SeqSpan sq = seq_span(p, bh);
@@ -482,7 +482,7 @@ void k_output_sh(PrefillParams p) {
   }
   for (int c = c0; c < c1; ++c) {
     const int t0 = c * C, L = min(C, T - t0);
-    const float a = DECAY ? exp2f((float)L * lg) : 1.f;
+    const float a = DECAY ? exp2_hw((float)L * lg) : 1.f;
     lds_barrier();  // the previous chunk is done with LDS (and Z is updated)
 
     // ---- commit this chunk's tiles: psi(Q) rounded to bf16; K swizzled (psi(k) as hi + lo
@@ -511,7 +511,7 @@ void k_output_sh(PrefillParams p) {
       }
       const int row = prow + 16 * i;
       const float live = row < L ? 1.f : 0.f;
-      const float xi = DECAY ? live * exp2f((float)(L - 1 - row) * lg) : live;
+      const float xi = row < L ? (DECAY ? exp2_hw((float)(L - 1 - row) * lg) : 1.f) : 0.f;
       const bf16x8 x = __builtin_bit_cast(bf16x8, pk.r[i]);
       float f[8];
 #pragma unroll
@@ -531,7 +531,7 @@ void k_output_sh(PrefillParams p) {
 #pragma unroll
     for (int i = 0; i < NPC; ++i) *(uint4*)(vP + i * 16 * D * 2) = pv.r[i];
     if (VDEC) {  // Xi of this chunk (the previous chunk's state update is done: barrier above)
-      for (int j = tid; j < C; j += 2 * D) sF[G::F_XI + j] = j < L ? exp2f((float)(L - 1 - j) * lg) : 0.f;
+      for (int j = tid; j < C; j += 2 * D) sF[G::F_XI + j] = j < L ? exp2_hw((float)(L - 1 - j) * lg) : 0.f;
     }
     const bool more = c + 1 < c1;
     const int Ln = more ? min(C, T - (c + 1) * C) : 0;
@@ -565,7 +565,7 @@ void k_output_sh(PrefillParams p) {
     auto score_epilogue = [&](int t, const f32x16& acc) {
       const int jt = tile_jt(t), it = t - jt * (jt + 1) / 2;
       const bool diag = it == jt;
-      const float tf = (DECAY && !diag) ? exp2f((float)(32 * (jt - it - 1)) * lg) : 1.f;
+      const float tf = (DECAY && !diag) ? exp2_hw((float)(32 * (jt - it - 1)) * lg) : 1.f;
       float av[16];
       float rs = 0.f;
 #pragma unroll
@@ -746,7 +746,7 @@ void k_output_sh(PrefillParams p) {
 #pragma unroll
       for (int i = 0; i < NPC; ++i) {
         const int row = prow + 16 * i, off = i * 16 * D * 2;
-        const float xi = row < L ? exp2f((float)(L - 1 - row) * lg) : 0.f;
+        const float xi = row < L ? exp2_hw((float)(L - 1 - row) * lg) : 0.f;
         const bf16x8 h8 = *(const bf16x8*)(kP + off);
         float x[8];
         if (ELU) {
@@ -952,7 +952,7 @@ __global__ __launch_bounds__(512) void k_output_w8(PrefillParams p) {
     for (int r = 0; r < 16; ++r) S[j][r] = pre[(size_t)(pt * 32 + dtile_row(r, lane)) * D + Ew + n];
   }
   if (tid < D) sF[G::F_Z + tid] = NORM ? pre[(size_t)D * D + tid] : 0.f;
-  for (int j = tid; j < C; j += G::NT) sF[G::F_THETA + j] = DECAY ? exp2f((float)(j + 1) * lg) : 1.f;
+  for (int j = tid; j < C; j += G::NT) sF[G::F_THETA + j] = DECAY ? exp2_hw((float)(j + 1) * lg) : 1.f;
 
   const SeqSpan sq = seq_span(p, bh);
   const int T = sq.T, n_chunks = (T + C - 1) / C;
@@ -975,7 +975,7 @@ __global__ __launch_bounds__(512) void k_output_w8(PrefillParams p) {
   }
   for (int c = c0; c < c1; ++c) {
     const int t0 = c * C, L = min(C, T - t0);
-    const float a = DECAY ? exp2f((float)L * lg) : 1.f;
+    const float a = DECAY ? exp2_hw((float)L * lg) : 1.f;
     lds_barrier();  // the previous chunk is done with LDS (and Z is updated)
 
     // ---- commit (see k_output_sh); with a denominator, psi(q_j) . Z_prev per token row from
@@ -1058,7 +1058,7 @@ __global__ __launch_bounds__(512) void k_output_w8(PrefillParams p) {
       for (int r = 0; r < 16; ++r) {
         const int ir = dtile_row(r, lane);
         float f;
-        if constexpr (DECAY) f = (diag && ir > n) ? 0.f : exp2f((float)(32 * (jt - it) + n - ir) * lg);
+        if constexpr (DECAY) f = (diag && ir > n) ? 0.f : exp2_hw((float)(32 * (jt - it) + n - ir) * lg);
         else f = (diag && ir > n) ? 0.f : 1.f;
         av[r] = acc[r] * f;
         if (NORM) rs += av[r];
@@ -1149,7 +1149,7 @@ __global__ __launch_bounds__(512) void k_output_w8(PrefillParams p) {
 #pragma unroll
       for (int i = 0; i < NPC; ++i) {
         const int row = prow + RSTEP * i, off = i * RSTEP * D * 2;
-        const float xi = row < L ? exp2f((float)(L - 1 - row) * lg) : 0.f;
+        const float xi = row < L ? exp2_hw((float)(L - 1 - row) * lg) : 0.f;
         const bf16x8 h8 = *(const bf16x8*)(kP + off);
         float x[8];
         if (ELU) {

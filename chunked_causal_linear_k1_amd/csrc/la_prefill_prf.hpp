@@ -310,7 +310,7 @@ __global__ __launch_bounds__(512) void k_summary_prf(PrefillParams p) {
   }
   for (int c = c0; c < c1; ++c) {
     const int L = min(C, T - c * C);
-    const float a = DECAY ? exp2f((float)L * lg) : 1.f;
+    const float a = DECAY ? exp2_hw((float)L * lg) : 1.f;
     lds_barrier();  // the previous chunk is done with LDS
     commit_raw_norm8<D, NPC, RSTEP>(pk_, rkP, PR * 2, sF + G8::F_NK, prow, tid);
 #pragma unroll
@@ -411,7 +411,7 @@ __global__ __launch_bounds__(512) void k_output_prf(PrefillParams p) {
     for (int r = 0; r < 16; ++r) S[pt][r] = pre[(size_t)(tile * 32 + dtile_row(r, lane)) * D + Ew + n];
   }
   for (int j = tid; j < NP; j += G8::NT) sF[G8::F_Z + j] = NORM ? pre[(size_t)NP * D + j] : 0.f;
-  for (int j = tid; j < C; j += G8::NT) sF[G8::F_THETA + j] = DECAY ? exp2f((float)(j + 1) * lg) : 1.f;
+  for (int j = tid; j < C; j += G8::NT) sF[G8::F_THETA + j] = DECAY ? exp2_hw((float)(j + 1) * lg) : 1.f;
 
   const SeqSpan sq = seq_span(p, bh);
   const int T = sq.T, n_chunks = (T + C - 1) / C;
@@ -433,7 +433,7 @@ __global__ __launch_bounds__(512) void k_output_prf(PrefillParams p) {
   }
   for (int c = c0; c < c1; ++c) {
     const int t0 = c * C, L = min(C, T - t0);
-    const float a = DECAY ? exp2f((float)L * lg) : 1.f;
+    const float a = DECAY ? exp2_hw((float)L * lg) : 1.f;
     bf16x8 wop[D / 16];
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) wop[kk] = *(const bf16x8*)(wrow + 16 * kk);
@@ -555,14 +555,14 @@ __global__ __launch_bounds__(512) void k_output_prf(PrefillParams p) {
         acc = mfma32(psik_row<NP>(kb8, it * 32, kk, LO), qv, acc);
       }
       const bool diag = it == jt;
-      const float tf = (DECAY && !diag) ? exp2f((float)(32 * (jt - it - 1)) * lg) : 1.f;
+      const float tf = (DECAY && !diag) ? exp2_hw((float)(32 * (jt - it - 1)) * lg) : 1.f;
       float av[16];
       float rs = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int ir = dtile_row(r, lane);
         if constexpr (DECAY) {
-          const float f = diag ? (ir <= n ? exp2f((float)(n - ir) * lg) : 0.f) : exp2f((float)(n + 32 - ir) * lg) * tf;
+          const float f = diag ? (ir <= n ? exp2_hw((float)(n - ir) * lg) : 0.f) : exp2_hw((float)(n + 32 - ir) * lg) * tf;
           av[r] = acc[r] * f;
         } else {
           av[r] = (diag && ir > n) ? 0.f : acc[r];
@@ -626,7 +626,7 @@ __global__ __launch_bounds__(512) void k_output_prf(PrefillParams p) {
 #pragma unroll
       for (int i = 0; i < NCH / G8::NT; ++i) {
         const int ch = tid + i * G8::NT, row = ch / (NP / 8), col = (ch % (NP / 8)) * 8;
-        const float xi = row < L ? exp2f((float)(L - 1 - row) * lg) : 0.f;
+        const float xi = row < L ? exp2_hw((float)(L - 1 - row) * lg) : 0.f;
         const int off = swzp<NP>(row, col) * 2;
         const bf16x8 h8 = *(const bf16x8*)(pk + off), l8 = *(const bf16x8*)(pk + off + LO);
         float x[8];

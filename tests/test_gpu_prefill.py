@@ -439,6 +439,41 @@ def test_prf_initial_and_final_state():
                  "prf final Z (scaled to max 1)")
 
 
+STRONG_DECAY = [
+    # name, psi, normalize, d, n_psi, decay: gamma far below 1, where gamma^n for the padded rows of
+    # a ragged last chunk (n < 0) would overflow fp32
+    ("identity_g0.1", PSI_IDENTITY, 0, 128, 128, "const:0.1"),
+    ("elu1_norm_g0.05", PSI_ELU1, 1, 128, 128, "const:0.05"),
+    ("elu1_norm_g0.1_d64", PSI_ELU1, 1, 64, 64, "const:0.1"),
+    ("prf256_norm_g0.1", PSI_PRF, 1, 128, 256, "const:0.1"),
+]
+
+
+@pytest.mark.parametrize("case", STRONG_DECAY, ids=[c[0] for c in STRONG_DECAY])
+def test_strong_decay_ragged_final_state(case):
+    """Strong decay, a ragged last chunk and the final state asked for: the padded rows' decay
+    factors are never formed, so outputs and the final state stay finite and match the oracle."""
+    name, psi, norm, d, NP, decay = case
+    B, H, T = 1, 2, 2 * 2048 + 1  # one real token in the last 64-token step: 63 padded rows
+    qks = {PSI_IDENTITY: d ** -0.5, PSI_ELU1: 0.5, PSI_PRF: d ** -0.25}[psi]
+    w = Workload(name=f"strong_{name}", B=B, H=H, T=T, d_k=d, d_v=d, n_psi=NP, chunk=64, psi=psi, normalize=norm,
+                 eps=1e-6, dtype="bf16", seed=41, qk_scale=qks, v_scale=1.0, decay=decay)
+    announce(f"prefill strong decay {name}")
+    inp = inputs.make_prefill_inputs(w, device="cpu")
+    fS = torch.empty((B, H, NP, d), dtype=torch.float32, device=DEV)
+    fZ = torch.empty((B, H, NP), dtype=torch.float32, device=DEV)
+    o = _run(w, inp, final_S=fS, final_Z=fZ)
+    ref, rS, rZ = _oracle_o(w, inp, want_state=True)
+    assert torch.isfinite(o).all() and torch.isfinite(fS).all(), name
+    assert_close(o.cpu().reshape(B * H, T, d).numpy(), ref, "bf16", f"{name} o")
+    assert_close(fS.cpu().reshape(B * H, NP, d).numpy() / np.abs(rS).max(), rS / np.abs(rS).max(), "bf16",
+                 f"{name} final S (scaled to max 1)")
+    if norm:
+        assert torch.isfinite(fZ).all(), name
+        assert_close(fZ.cpu().reshape(B * H, NP).numpy() / np.abs(rZ).max(), rZ / np.abs(rZ).max(), "bf16",
+                     f"{name} final Z (scaled to max 1)")
+
+
 def test_full_prf_4k():
     _full_size(workloads.PRF_4K)
 
