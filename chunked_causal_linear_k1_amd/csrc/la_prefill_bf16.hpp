@@ -1122,21 +1122,29 @@ __global__ __launch_bounds__(512) void k_output_w8(PrefillParams p) {
 #pragma unroll
       for (int u = 0; u < NJ; ++u) num[u] *= fN[G::F_THETA + jtu[u] * 32];
     }
-    f32x16 mine = num[0];
+    f32x16 mine = num[0], give = num[1];
     {
-      // the intra-chunk term of token tile fh: it = 0 .. fh (a wave-uniform trip count)
-      for (int it = 0; it <= fh; ++it) {
-        const unsigned char* at = aR + (fh * (fh + 1) / 2 + it) * G::A_TILE;
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const int r0 = it * 32 + 16 * q;
-          const bf16x8 vv = cat8(lds_read_tr4((const __bf16*)(vT0 + r0 * D * 2)),
-                                 lds_read_tr4((const __bf16*)(vT1 + r0 * D * 2)));
-          mine = mfma32(vv, *(const bf16x8*)(at + 32 * q), mine);
-          mine = mfma32(vv, *(const bf16x8*)(at + 32 * q + ALO), mine);
-        }
+      // the intra-chunk terms, in equal shares: each half adds the diagonal score tile of its
+      // own token tile, and one 16-key half (k-half fh) of the off-diagonal tile (queries of
+      // token tile 1, keys of token tile 0), half 0 into the partial it hands over
+      auto av_step = [&](f32x16& acc, int t, int it, int q) {
+        const unsigned char* at = aR + t * G::A_TILE;
+        const int r0 = it * 32 + 16 * q;
+        const bf16x8 vv = cat8(lds_read_tr4((const __bf16*)(vT0 + r0 * D * 2)),
+                               lds_read_tr4((const __bf16*)(vT1 + r0 * D * 2)));
+        acc = mfma32(vv, *(const bf16x8*)(at + 32 * q), acc);
+        acc = mfma32(vv, *(const bf16x8*)(at + 32 * q + ALO), acc);
+      };
+      static_assert(NJ == 2, "tiles (0, 0) = 0, (1, 0) = 1, (1, 1) = 2");
+      if (__builtin_amdgcn_readfirstlane(fh)) {
+        av_step(mine, 2, 1, 0);
+        av_step(mine, 2, 1, 1);
+        av_step(mine, 1, 0, 1);
+      } else {
+        av_step(mine, 0, 0, 0);
+        av_step(mine, 0, 0, 1);
+        av_step(give, 1, 0, 0);
       }
-      const f32x16 give = num[1];
       f32x4* const xo = (f32x4*)(xch + (cb * NJ + (1 - fh)) * 16 * 64);
 #pragma unroll
       for (int q = 0; q < 4; ++q) xo[q * 64] = f32x4{give[4 * q], give[4 * q + 1], give[4 * q + 2], give[4 * q + 3]};
