@@ -587,30 +587,37 @@ __global__ __launch_bounds__(512) void k_output_prf(PrefillParams p) {
     }
     lds_barrier();
 
-    // ---- the inter-chunk part; theta weights; half 1 adds the intra-chunk term V^T A^T
+    // ---- the inter-chunk part; theta weights; the intra-chunk term V^T A^T in equal shares:
+    // each half adds the diagonal score tile of token tile fh and one 16-key half (k-half fh)
+    // of the off-diagonal tile (queries of token tile 1, keys of token tile 0)
+    static_assert(NJ == 2, "one token tile per feature half; tiles (0, 0) = 0, (1, 0) = 1, (1, 1) = 2");
     inter();
+    if (DECAY) {
 #pragma unroll
-    for (int jt = 0; jt < NJ; ++jt) {
-      if (DECAY) num[jt] *= fN[G8::F_THETA + jt * 32];
-      if (fh == 1) {
-#pragma unroll
-        for (int it = 0; it <= jt; ++it) {
-          const unsigned char* at = aR + (jt * (jt + 1) / 2 + it) * G::A_TILE;
-#pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            const int r0 = it * 32 + 16 * q;
-            const bf16x8 vv = cat8(lds_read_tr4((const __bf16*)(vT + r0 * PV * 2)),
-                                   lds_read_tr4((const __bf16*)(vT + (r0 + 4) * PV * 2)));
-            num[jt] = mfma32(vv, *(const bf16x8*)(at + 32 * q), num[jt]);
-            num[jt] = mfma32(vv, *(const bf16x8*)(at + 32 * q + ALO), num[jt]);
-          }
-        }
+      for (int jt = 0; jt < NJ; ++jt) num[jt] *= fN[G8::F_THETA + jt * 32];
+    }
+    {
+      auto av_step = [&](f32x16& acc, int t, int it, int q) {
+        const unsigned char* at = aR + t * G::A_TILE;
+        const int r0 = it * 32 + 16 * q;
+        const bf16x8 vv = cat8(lds_read_tr4((const __bf16*)(vT + r0 * PV * 2)),
+                               lds_read_tr4((const __bf16*)(vT + (r0 + 4) * PV * 2)));
+        acc = mfma32(vv, *(const bf16x8*)(at + 32 * q), acc);
+        acc = mfma32(vv, *(const bf16x8*)(at + 32 * q + ALO), acc);
+      };
+      if (__builtin_amdgcn_readfirstlane(fh)) {
+        av_step(num[1], 2, 1, 0);
+        av_step(num[1], 2, 1, 1);
+        av_step(num[1], 1, 0, 1);
+      } else {
+        av_step(num[0], 0, 0, 0);
+        av_step(num[0], 0, 0, 1);
+        av_step(num[1], 1, 0, 0);
       }
     }
     // ---- the halves' partial outputs meet: half h completes token tile jt = h of its value
     // columns, taking the other half's partial of that tile through LDS, so that every wave
     // stores the same number of rows (and the next chunk's loads are not held behind stores)
-    static_assert(NJ == 2, "one token tile per feature half");
     lds_barrier();  // every wave is done with psi(Q) and the score tiles: their region takes the partials
     f32x16 mine = fh ? num[1] : num[0];
     {
