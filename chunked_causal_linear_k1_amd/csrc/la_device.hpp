@@ -81,6 +81,25 @@ __device__ __forceinline__ void split8_trunc(const float* x, bf16x8& hi, bf16x8&
   lo = __builtin_bit_cast(bf16x8, l);
 }
 
+// The same hi + lo split with hi rounded to nearest even (lo = RNE(x - hi), x - hi exact
+// in fp32): for operands whose hi part also serves alone, where truncation would bias it
+// toward zero by about a quarter of a bf16 ulp on average.
+__device__ __forceinline__ void split8_rne(const float* x, bf16x8& hi, bf16x8& lo) {
+  u32x4v h, l;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const bf16x2 hp = __builtin_convertvector((f32x2){x[2 * k], x[2 * k + 1]}, bf16x2);
+    const unsigned hb = __builtin_bit_cast(unsigned, hp);
+    const float ra = x[2 * k] - __uint_as_float(hb << 16);
+    const float rb = x[2 * k + 1] - __uint_as_float(hb & 0xffff0000u);
+    h[k] = hb;
+    const bf16x2 lp = __builtin_convertvector((f32x2){ra, rb}, bf16x2);
+    l[k] = __builtin_bit_cast(unsigned, lp);
+  }
+  hi = __builtin_bit_cast(bf16x8, h);
+  lo = __builtin_bit_cast(bf16x8, l);
+}
+
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }

@@ -361,6 +361,12 @@ struct ShGeo {
   static constexpr int OCC = 2 * LDS_BYTES <= 160 * 1024 ? 2 : 1;
 };
 
+// The shared-score kernel's LDS image for (ELU, NORM, DECAY): elu+1 keys keep a K lo tile
+// except under the single-rounding policy (elu+1 with a denominator and no decay, see
+// k_output_w8), which takes the identity layout (score tiles where K lo would be).
+template <int C, int D, bool DECAY, bool NORM, bool ELU>
+using ShGeoF = ShGeo<C, D, ELU && (DECAY || !NORM)>;
+
 // tile t <-> (it, jt) with it <= jt, t = jt (jt + 1) / 2 + it; branch-free (up to 16 row tiles)
 __device__ __forceinline__ int tile_jt(int t) {
   int jt = 0;
@@ -391,13 +397,17 @@ __device__ __forceinline__ void state_mfma_p(f32x16 (&S)[D / 32], const __bf16* 
 // is a multiple of 16 and x < 32, a swizzled read of any row block is one of a few
 // per-lane bases plus the row block's constant offset.
 template <int C, int D, bool DECAY, bool NORM, bool ELU, bool OBF>
-__global__ __launch_bounds__(2 * D) __attribute__((amdgpu_waves_per_eu(ShGeo<C, D, ELU>::OCC, ShGeo<C, D, ELU>::OCC)))
+__global__ __launch_bounds__(2 * D)
+__attribute__((amdgpu_waves_per_eu(ShGeoF<C, D, DECAY, NORM, ELU>::OCC, ShGeoF<C, D, DECAY, NORM, ELU>::OCC)))
 void k_output_sh(PrefillParams p) {
-  using G = ShGeo<C, D, ELU>;
+  using G = ShGeoF<C, D, DECAY, NORM, ELU>;
   using PG = Geo<C, D, true>;  // piece geometry of the global -> LDS copies
   static_assert(G::FITS, "LDS budget");
   static_assert(PG::NT / PG::PPR == 16, "piece i of a thread covers row 16 i + tid / PPR");
-  constexpr bool SPLIT = DECAY || ELU;
+  // elu+1 with a denominator and no decay: S (in psi(Q) S) and psi(K) (scores, state update,
+  // Z) are rounded to bf16 once, as in k_output_w8; the score tiles stay hi + lo
+  constexpr bool PLAIN = ELU && NORM && !DECAY;
+  constexpr bool SPLIT = (DECAY || ELU) && !PLAIN;
   // Identity keys are exact in bf16, so the decay of the state update goes on the values:
   // S += K^T (Xi V), with Xi V split into hi + lo in registers from the transpose reads of V.
   // K stays as committed: no K~ pass, no barrier around it. (elu+1 keys are already two-term,
@@ -515,13 +525,24 @@ void k_output_sh(PrefillParams p) {
       const bf16x8 x = __builtin_bit_cast(bf16x8, pk.r[i]);
       float f[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        f[j] = ELU ? elu1(from_bf16(x[j])) * live : from_bf16(x[j]);
-        if (NORM) zp[j] += f[j] * xi;
+      for (int j = 0; j < 8; ++j) f[j] = ELU ? elu1(from_bf16(x[j])) * live : from_bf16(x[j]);
+      if (PLAIN) {  // Z from the same rounded features as the state
+        bf16x8 y;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          y[j] = to_bf16(f[j]);
+          zp[j] += from_bf16(y[j]);
+        }
+        *(bf16x8*)(kP + off) = y;
+        continue;
+      }
+      if (NORM) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) zp[j] += f[j] * xi;
       }
       if (ELU) {
         bf16x8 hi, lo;
-        split8_trunc(f, hi, lo);
+        split8_rne(f, hi, lo);  // hi alone is the score operand
         *(bf16x8*)(kP + off) = hi;
         *(bf16x8*)(kP + off + KLO) = lo;
       } else {
@@ -672,23 +693,28 @@ void k_output_sh(PrefillParams p) {
       constexpr int pt = decltype(ipt)::value;
       if constexpr (pt + 1 < NPT) load_s(pt + 1, (pt + 1) & 1);
       else load_av(0, 0);
-      bf16x8 sh[2], sl[2];  // this state-row tile of S_prev as hi + lo, straight from its accumulator
+      bf16x8 sh[2], sl[2];  // this state-row tile of S_prev as hi + lo (or rounded once), from its accumulator
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         float x[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) x[j] = S[pt][8 * q + j];
-        split8_trunc(x, sh[q], sl[q]);
+        if (PLAIN) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) sh[q][j] = to_bf16(x[j]);
+        } else {
+          split8_trunc(x, sh[q], sl[q]);
+        }
       }
 #pragma unroll
       for (int jt = 0; jt < NJ; ++jt)
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
           num[jt] = mfma32(sh[q], qo[pt & 1][jt][q], num[jt]);
-          num[jt] = mfma32(sl[q], qo[pt & 1][jt][q], num[jt]);
+          if (!PLAIN) num[jt] = mfma32(sl[q], qo[pt & 1][jt][q], num[jt]);
         }
       __builtin_amdgcn_sched_group_barrier(0x100, pt + 1 < NPT ? RD_S : rd_av(0), 0);  // next step's reads
-      __builtin_amdgcn_sched_group_barrier(0x008, 4 * NJ, 0);                            // this step's MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x008, (PLAIN ? 2 : 4) * NJ, 0);              // this step's MFMAs
     });
     if (DECAY) {
 #pragma unroll
@@ -1026,7 +1052,7 @@ __global__ __launch_bounds__(512) void k_output_w8(PrefillParams p) {
         continue;
       }
       bf16x8 hi, lo;
-      split8_trunc(f, hi, lo);
+      split8_rne(f, hi, lo);  // hi alone is the score operand
       *(bf16x8*)(kP + off) = hi;
       *(bf16x8*)(kP + off + KLO) = lo;
     }
@@ -1251,7 +1277,9 @@ __global__ __launch_bounds__(512) void k_output_w8(PrefillParams p) {
 // denominator at d = 128, else the shared-score kernel (two workgroups per CU where their LDS
 // fits). Measured at C = 64, d = 128 on the output pass: identity features with a denominator
 // 0.222 ms (eight waves) against 0.234 ms (shared scores, two workgroups) on 8k x 64 heads;
-// retention without one 2.22 ms (shared scores) against 2.94 ms (eight waves) on 128k x 64.
+// retention without one 2.22 ms (shared scores) against 2.94 ms (eight waves) on 128k x 64;
+// elu+1 with a denominator, both single-rounding, 0.153 ms (eight waves, 2048-token segments)
+// against 0.192 ms (shared scores; 0.154 ms with 1024-token segments, two workgroups per CU).
 template <int C, int D, bool DECAY, bool NORM, bool ELU, bool OBF>
 const void* output_kernel(int& lds, int& threads) {
   if constexpr (W8Geo<C, D, ELU>::FITS && (ELU || NORM)) {
@@ -1259,8 +1287,9 @@ const void* output_kernel(int& lds, int& threads) {
     threads = W8Geo<C, D, ELU>::NT;
     return (const void*)k_output_w8<C, D, DECAY, NORM, ELU, OBF>;
   } else {
-    static_assert(ShGeo<C, D, ELU>::FITS, "LDS budget of the shared-score output kernel");
-    lds = ShGeo<C, D, ELU>::LDS_BYTES;
+    using G = ShGeoF<C, D, DECAY, NORM, ELU>;
+    static_assert(G::FITS, "LDS budget of the shared-score output kernel");
+    lds = G::LDS_BYTES;
     return (const void*)k_output_sh<C, D, DECAY, NORM, ELU, OBF>;
   }
 }

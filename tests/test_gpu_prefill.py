@@ -54,6 +54,8 @@ SMALL = [
     # chunks of 32 tokens (walked in 64-token steps; segments hold an even number of chunks)
     ("identity_decay_c32", 1, 3, 777, 128, 32, PSI_IDENTITY, 0, "retnet_spread", "bf16"),
     ("elu1_norm_c32_d64", 2, 2, 501, 64, 32, PSI_ELU1, 1, "const:0.99", "bf16"),
+    # elu+1 with a denominator and no decay at d = 64 (shared-score kernel, single roundings)
+    ("elu1_norm_nodecay_d64_c64", 1, 2, 700, 64, 64, PSI_ELU1, 1, "none", "bf16"),
     ("f32_elu1_c32", 1, 2, 300, 64, 32, PSI_ELU1, 1, "none", "f32"),
     ("f32_identity_decay_c16", 1, 2, 200, 32, 16, PSI_IDENTITY, 0, "const:0.9", "f32"),
 ]
@@ -87,6 +89,24 @@ def test_identity_with_denominator(d, C, decay):
     o = _run(w, inp)
     ref = _oracle_o(w, inp)
     assert_close(o.cpu().reshape(3, T, d).numpy(), ref, "bf16", w.name)
+
+
+@pytest.mark.parametrize("d,C,decay", [(128, 64, "none"), (128, 64, "const:0.99"), (128, 128, "retnet_spread"),
+                                       (64, 64, "none"), (64, 32, "const:0.99")])
+def test_elu1_without_denominator(d, C, decay):
+    """elu+1 features without the denominator: the unnormalised sums have no fixed scale
+    (|o| reaches about 1e3 here), so rel-L2 is taken as is and max-abs on outputs scaled by
+    the largest reference magnitude."""
+    T = 700
+    w = Workload(name=f"elu1_nonorm_d{d}_c{C}_{decay}", B=1, H=2, T=T, d_k=d, d_v=d, n_psi=d, chunk=C,
+                 psi=PSI_ELU1, normalize=0, eps=1e-6, dtype="bf16", seed=d + C + 7, qk_scale=0.5, v_scale=1.0,
+                 decay=decay)
+    announce(f"prefill {w.name}")
+    inp = inputs.make_prefill_inputs(w, device="cpu")
+    o = _run(w, inp).cpu().reshape(2, T, d).numpy()
+    ref = _oracle_o(w, inp)
+    scale = float(np.abs(ref).max())
+    assert_close(o / scale, ref / scale, "bf16", f"{w.name} (scaled by max |o| = {scale:.3g})")
 
 
 def test_tiny_f32_workload_full():
