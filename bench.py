@@ -296,6 +296,43 @@ def bench_decode(w: workloads.DecodeWorkload, steps: int, warmup: int, replicas:
     return res
 
 
+def stream_ceiling(w: workloads.Workload, reps: int = 10):
+    """Plain streaming kernels with the byte patterns of the two prefill passes at the
+    workload's size (probe/stream_probe.hip): three bf16 reads and one fp32 write per element
+    (the output pass), and two bf16 reads (the summary pass). Their rates are the practical
+    ceiling the memory-bound passes are compared with on the same box."""
+    import ctypes
+    from chunked_causal_linear_k1_amd import build as hip_build
+    lib = ctypes.CDLL(hip_build.PROBE_LIB)
+    lib.ccl_stream_mix.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_size_t, ctypes.c_void_p]
+    lib.ccl_stream_read2.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_size_t, ctypes.c_void_p]
+    lib.ccl_stream_read2_parts.restype = ctypes.c_size_t
+    n = w.B * w.H * w.T * w.d_v
+    q, k, v = (torch.ones(n, dtype=torch.bfloat16, device="cuda") for _ in range(3))
+    o = torch.empty(n, dtype=torch.float32, device="cuda")
+    part = torch.empty(lib.ccl_stream_read2_parts(), dtype=torch.float32, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    calls = {"mix": lambda: lib.ccl_stream_mix(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), n, st),
+             "read2": lambda: lib.ccl_stream_read2(k.data_ptr(), v.data_ptr(), part.data_ptr(), n, st)}
+    out = {}
+    for name, fn in calls.items():
+        for _ in range(2):
+            assert fn() == 0, name
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        nbytes = n * (10 if name == "mix" else 4)
+        out[name] = {"ms": round(ms, 4), "bytes": nbytes, "GBs": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+    assert float(o[0]) == 2.0 and float(part.double().sum()) == float(n), "stream probe results"
+    del q, k, v, o, part
+    torch.cuda.empty_cache()
+    return out
+
+
 def copy_probe(mib: int):
     """Plain device-to-device copies of mib MiB and then mib/4 MiB: the reference kernels for
     scaling the HBM byte counters (FETCH_SIZE, WRITE_SIZE) of a counter run to bytes (two sizes,
@@ -499,6 +536,14 @@ def main():
                                     f"kernel-source hash {pmc_traffic.source_hash()}; null when taken on other sources"},
     }
     targets = {"prefill_128k": _rate_vs_target(pre["token_heads_per_s"], 3.125e9)}
+    sc = stream_ceiling(w)
+    sum_bytes = 4 * w.d_v * pre["units"]  # k and v read once (the records are 1.3% more)
+    sum_gbs = sum_bytes / (pre["phase_ms"]["summary"] * 1e-3) / 1e9
+    line["stream_ceiling"] = {
+        "note": "plain streaming kernels with each pass's byte pattern at this size, timed in this run",
+        "output_pattern": sc["mix"], "summary_pattern": sc["read2"],
+        "output_pass_of_stream": round(achieved / sc["mix"]["GBs"], 4),
+        "summary_pass_of_stream": round(sum_gbs / sc["read2"]["GBs"], 4)}
 
     tw = workloads.TINY_F32
     pt = bench_tiny(tw, 200, 20)

@@ -52,10 +52,31 @@ def _compile(src: str) -> str:
     return obj
 
 
+PROBE_SRC = os.path.join(HERE, "probe", "stream_probe.hip")
+PROBE_LIB = os.path.join(HERE, "libstreamprobe.so")
+
+
+def build_probe(verbose: bool = True) -> str:
+    """The streaming reference kernels bench.py times beside the prefill passes (a library of
+    their own: measurement only, not part of liblinattn)."""
+    tmp = PROBE_LIB + ".tmp"
+    flags = [f for f in COMMON if f not in ("-mllvm", "-amdgpu-mfma-vgpr-form=true")]
+    cmd = [HIPCC] + flags + ["-shared", "-x", "hip", PROBE_SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {PROBE_SRC}:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, PROBE_LIB)
+    if verbose:
+        print(f"built {PROBE_LIB}")
+    return PROBE_LIB
+
+
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
+    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES) + 1, os.cpu_count() or 4)) as ex:
+        probe = ex.submit(build_probe, verbose)
         objs = list(ex.map(_compile, SOURCES))
+        probe.result()
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
