@@ -19,7 +19,7 @@ BUILD_DIR = os.path.join(HERE, "_build")
 SOURCES = ["la_api.cpp", "la_decode.hip", "la_scan.hip", "la_prefill_bf16.hip", "la_prefill_f32.hip", "la_gla.hip",
            "la_backward.hip",
            "la_prefill_bf16_c64_d64.hip", "la_prefill_bf16_c64_d128.hip", "la_prefill_prf.hip", "la_noalloc.hip",
-           "la_backward_prf.hip"]
+           "la_backward_prf.hip", "la_backward_gen.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

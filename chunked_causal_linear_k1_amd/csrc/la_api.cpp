@@ -204,18 +204,24 @@ la_status lin_attn_prefill_gated_workspace_size(const la_prefill_desc* d, size_t
 la_status validate_backward_desc(const la_prefill_desc* d, bool varlen = false) {
   const la_status st = validate_prefill_desc(d);
   if (st != LA_OK) return st;
-  if (d->in_dtype != LA_BF16) return LA_ERR_UNSUPPORTED;
+  if (d->in_dtype == LA_F32)  // the fp32 vector-ALU sweeps, segment records as for bf16 inputs
+    return la::prefill_backward_gen_supported(d->chunk, d->d_k, d->d_v, d->n_psi, d->psi, true) ? LA_OK
+                                                                                               : LA_ERR_UNSUPPORTED;
   if (la::is_prf(d->psi)) {
     // one workgroup per 64-token step on the grid's y extent
     if ((d->T + 63) / 64 > 65535) return LA_ERR_UNSUPPORTED;
     return !varlen && la::prefill_backward_prf_supported(d->chunk, d->d_k, d->d_v, d->n_psi) ? LA_OK
                                                                                              : LA_ERR_UNSUPPORTED;
   }
-  return la::prefill_backward_supported(d->chunk, d->d_k, d->d_v, d->n_psi, d->psi) ? LA_OK : LA_ERR_UNSUPPORTED;
+  if (la::prefill_backward_supported(d->chunk, d->d_k, d->d_v, d->n_psi, d->psi)) return LA_OK;
+  return la::prefill_backward_gen_supported(d->chunk, d->d_k, d->d_v, d->n_psi, d->psi, false) ? LA_OK
+                                                                                              : LA_ERR_UNSUPPORTED;
 }
 
-// Random features: one record per 64-token step (la_backward_prf.hip).
+// Random features with bf16 inputs: one record per 64-token step (la_backward_prf.hip). With fp32
+// inputs they take the vector-ALU sweeps over segment records like every other feature map.
 constexpr int kPrfBwdStep = 64;
+bool prf_steps(const la_prefill_desc* d) { return la::is_prf(d->psi) && d->in_dtype == LA_BF16; }
 Plan prf_backward_plan(const la_prefill_desc* d) {
   Plan pl;
   pl.n_chunks = (d->T + kPrfBwdStep - 1) / kPrfBwdStep;
@@ -233,7 +239,7 @@ Plan prf_backward_plan(const la_prefill_desc* d) {
 size_t backward_ws_bytes(const la_prefill_desc* d, long long total_tokens = -1) {
   const long long rows = total_tokens < 0 ? (long long)d->B * d->T * d->H : total_tokens * d->H;
   const size_t tok = d->normalize ? (size_t)rows * 2 * sizeof(float) : 0;
-  if (la::is_prf(d->psi)) {
+  if (prf_steps(d)) {
     const size_t bank = ((size_t)d->H * d->n_psi * d->d_k * 2 + 15) & ~(size_t)15;
     return 2 * prf_backward_plan(d).ws_bytes + tok + bank;
   }
@@ -488,8 +494,8 @@ la_status backward_impl(const la_prefill_desc* d, const int32_t* cu_seqlens, int
                         float* dinit_Z, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   la_status st = validate_backward_desc(d, cu_seqlens != nullptr);
   if (st != LA_OK) return st;
-  const bool prf = la::is_prf(d->psi);
-  if (prf && !prf_w) return LA_ERR_NULL;
+  const bool prf = prf_steps(d);
+  if (la::is_prf(d->psi) && !prf_w) return LA_ERR_NULL;
   if (!aligned16(prf_w)) return LA_ERR_ALIGN;
   if (cu_seqlens) {
     if (d->layout != LA_LAYOUT_BTHD) return LA_ERR_VALUE;
@@ -565,6 +571,16 @@ la_status backward_impl(const la_prefill_desc* d, const int32_t* cu_seqlens, int
     if (e == hipSuccess) e = la::launch_prefill_backward_prf(bp, stream, false);  // dq, per-step adjoint records
     if (e == hipSuccess) e = la::launch_segment_scan(rp, stream);                 // the adjoint state after each step
     if (e == hipSuccess) e = la::launch_prefill_backward_prf(bp, stream, true);   // dk, dv
+    return e == hipSuccess ? LA_OK : LA_ERR_HIP;
+  }
+  if (d->in_dtype == LA_F32 || !la::prefill_backward_supported(d->chunk, d->d_k, d->d_v, d->n_psi, d->psi)) {
+    // fp32 inputs, or bf16 at d = 64: the vector-ALU sweeps over the same records
+    p.in_f32 = d->in_dtype == LA_F32;
+    hipError_t e = p.in_f32 ? la::launch_prefill_f32_summary(p, stream) : la::launch_prefill_bf16_summary(p, stream);
+    if (e == hipSuccess) e = la::launch_segment_scan(sp, stream);
+    if (e == hipSuccess) e = la::launch_prefill_backward_gen(bp, stream, false);  // query sweep
+    if (e == hipSuccess) e = la::launch_segment_scan(rp, stream);
+    if (e == hipSuccess) e = la::launch_prefill_backward_gen(bp, stream, true);   // state sweep
     return e == hipSuccess ? LA_OK : LA_ERR_HIP;
   }
   hipError_t e = la::launch_prefill_bf16_summary(p, stream);            // forward segment summaries

@@ -166,6 +166,12 @@ hipError_t launch_prefill_gated(const PrefillParams& p, hipStream_t s, bool out)
 bool prefill_backward_supported(int C, int d_k, int d_v, int n_psi, int psi);
 hipError_t launch_prefill_backward(const BackwardParams& p, hipStream_t s, bool key_sweep);
 
+// The fp32 vector-ALU backward (la_backward_gen.hip) for the shapes the matrix-core kernels do
+// not take: fp32 inputs (f.in_f32 set; dout fp32), bf16 inputs at d = 64. Same two sweeps over
+// the same segment records.
+bool prefill_backward_gen_supported(int C, int d_k, int d_v, int n_psi, int psi, bool in_f32);
+hipError_t launch_prefill_backward_gen(const BackwardParams& p, hipStream_t s, bool state_sweep);
+
 // Random features (la_backward_prf.hip): one 64-token step per workgroup; the forward summary
 // pass of la_prefill_prf.hpp gives one record per step.
 bool prefill_backward_prf_supported(int C, int d_k, int d_v, int n_psi);

@@ -271,12 +271,20 @@ la_status lin_attn_prefill_gated(const la_prefill_desc* d, const void* q, const 
  * dx = sum_p a_p w_p - (sum_p a_p) x with a_p = dL/dpsi_p psi_p(x), where under the query-row
  * shift the last term of dq takes the row of the bank that attains the shift (the argmax).
  *
- *   d         as for lin_attn_prefill; supported: in_dtype LA_BF16, and
- *               psi identity or elu1: d_k == d_v == n_psi == 128;
- *               psi PRF or PRF_QSHIFT: d_k == d_v == 128, n_psi 128 or 256;
- *             chunk 32, 64 or 128 (walked in steps of 64 tokens: the gradient does not
- *             depend on the grouping), either layout. out_dtype is the type of dout (LA_F32
- *             or LA_BF16).
+ *   d         as for lin_attn_prefill; supported:
+ *               in_dtype LA_BF16 on the matrix cores, chunk 32, 64 or 128 (walked in steps of
+ *               64 tokens: the gradient does not depend on the grouping):
+ *                 psi identity or elu1: d_k == d_v == n_psi == 128;
+ *                 psi PRF or PRF_QSHIFT: d_k == d_v == 128, n_psi 128 or 256;
+ *               in fp32 on the vector ALUs (steps of 16 tokens, the same segment records):
+ *                 in_dtype LA_BF16, psi identity or elu1, d_k == d_v == n_psi == 64, chunk 32,
+ *                 64 or 128;
+ *                 in_dtype LA_F32 (out_dtype LA_F32), every psi, wherever lin_attn_prefill
+ *                 takes the shape (chunk 16, 32 or 64) and the state plus one step's rows fit
+ *                 in 160 KiB of LDS with n_psi * d_v <= 16384 (d = 128 with n_psi 128; d = 64
+ *                 with n_psi up to 256);
+ *             either layout. out_dtype is the type of dout (LA_F32, or LA_BF16 with bf16
+ *             inputs).
  *   prf_w     device [H, n_psi, d_k] bf16, the forward call's bank; required iff psi is a
  *             random-feature map
  *   dout      device, dL/do, laid out like lin_attn_prefill's o, out_dtype

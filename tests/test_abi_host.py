@@ -263,8 +263,21 @@ def test_backward_validation_and_workspace():
     assert ws(**{**base, "chunk": 128, "psi": 0})[0] == LA_OK
     assert ws(**{**base, "layout": 1})[0] == LA_OK
     assert ws(**{**base, "chunk": 32})[0] == LA_OK
-    for kw in (dict(chunk=16), dict(d_k=64, d_v=64, n_psi=64), dict(in_dtype=LA_F32), dict(psi=2, n_psi=64),
-               dict(psi=2, n_psi=256, chunk=16)):
+    # fp32 inputs and bf16 at d = 64 take the vector-ALU sweeps: where the fp32 (or bf16) forward runs
+    # and one step's tiles plus the state fit in LDS (random features up to n_psi = 128 at d = 128)
+    for kw in (dict(d_k=64, d_v=64, n_psi=64), dict(d_k=64, d_v=64, n_psi=64, chunk=128),
+               dict(in_dtype=LA_F32, chunk=32), dict(in_dtype=LA_F32, d_k=64, d_v=64, n_psi=64),
+               dict(in_dtype=LA_F32, chunk=16, psi=0), dict(in_dtype=LA_F32, chunk=32, psi=2, n_psi=128),
+               dict(in_dtype=LA_F32, chunk=32, psi=3, n_psi=128), dict(in_dtype=LA_F32, psi=2, n_psi=256, d_k=64,
+                                                                     d_v=64, chunk=16)):
+        st_, nb = ws(**{**base, **kw})
+        assert st_ == LA_OK, kw
+        f_ = ctypes.c_size_t(0)
+        assert lib.lin_attn_prefill_workspace_size(ctypes.byref(_desc(**{**base, **kw})), ctypes.byref(f_)) == LA_OK
+        assert nb == 2 * f_.value + 2 * 4 * base["B"] * base["H"] * base["T"], kw
+    for kw in (dict(chunk=16), dict(in_dtype=LA_F32), dict(psi=2, n_psi=64), dict(psi=2, n_psi=256, chunk=16),
+               dict(in_dtype=LA_F32, chunk=32, psi=2, n_psi=256), dict(in_dtype=LA_F32, chunk=128),
+               dict(d_k=96, d_v=96, n_psi=96)):
         assert ws(**{**base, **kw})[0] == LA_ERR_UNSUPPORTED, kw
     # random features: one record per 64-token step (two regions), 1/den and dden per token-head,
     # and the bank transposed
