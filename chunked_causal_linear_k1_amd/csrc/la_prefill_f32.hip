@@ -19,7 +19,8 @@ namespace {
 constexpr int kThreads = 256;
 
 struct F32Layout {
-  int S, Z, FQ, FK, RAW, V, A, DEN, THETA, XI, total;  // float offsets
+  int S, Z, FQ, FK, RQ, RK, V, A, DEN, THETA, XI, total;  // float offsets
+  int PF;  // feature row pitch: n_psi + 4, so that rows 4 apart fall in different LDS banks
 };
 
 __host__ __device__ inline F32Layout f32_layout(int C, int d_k, int d_v, int n_psi) {
@@ -27,9 +28,11 @@ __host__ __device__ inline F32Layout f32_layout(int C, int d_k, int d_v, int n_p
   int off = 0;
   L.S = off; off += n_psi * d_v;
   L.Z = off; off += n_psi;
-  L.FQ = off; off += C * n_psi;
-  L.FK = off; off += C * n_psi;
-  L.RAW = off; off += C * d_k;   // raw rows (PRF needs them beside the features)
+  L.PF = n_psi + 4;
+  L.FQ = off; off += C * L.PF;
+  L.FK = off; off += C * L.PF;
+  L.RQ = off; off += C * d_k;    // raw q and k rows, loaded together with v (PRF needs them
+  L.RK = off; off += C * d_k;    // beside the features)
   L.V = off; off += C * d_v;
   L.A = off; off += C * C;
   L.DEN = off; off += C;
@@ -39,14 +42,10 @@ __host__ __device__ inline F32Layout f32_layout(int C, int d_k, int d_v, int n_p
   return L;
 }
 
-// psi of the chunk rows [0, valid) of x (fp32, row length d_k, rows rs elements apart) into
-// out[C][n_psi]; rows >= valid -> 0.
-__device__ void load_rows_f32(const float* __restrict__ x, size_t rs, float* out, int C, int valid, int d);
-
-__device__ void features_f32(const float* __restrict__ x, size_t rs, float* raw, float* out, int C, int valid,
-                             int d_k, int n_psi, int psi, const float* __restrict__ w) {
-  load_rows_f32(x, rs, raw, C, valid, d_k);
-  __syncthreads();
+// psi of the raw chunk rows [0, valid) (LDS, row length d_k, loaded and made visible by the
+// caller) into out[C][pf] (row pitch pf >= n_psi); rows >= valid -> 0.
+__device__ void features_f32(const float* raw, float* out, int pf, int C, int valid, int d_k, int n_psi, int psi,
+                             const float* __restrict__ w) {
   for (int idx = threadIdx.x; idx < C * n_psi; idx += kThreads) {
     const int r = idx / n_psi, f = idx % n_psi;
     float val = 0.f;
@@ -66,21 +65,23 @@ __device__ void features_f32(const float* __restrict__ x, size_t rs, float* raw,
         val = dot - 0.5f * sq;  // log-feature; exponentiated below
       }
     }
-    out[idx] = val;
+    out[(idx / n_psi) * pf + idx % n_psi] = val;
   }
   __syncthreads();
   if (is_prf(psi)) {
     // PRF_QSHIFT: subtract each row's largest log-feature (rows past `valid` stay zero)
     if (psi == LA_PSI_PRF_QSHIFT) {
       for (int r = threadIdx.x; r < valid; r += kThreads) {
-        float mx = out[r * n_psi];
-        for (int f = 1; f < n_psi; ++f) mx = fmaxf(mx, out[r * n_psi + f]);
-        for (int f = 0; f < n_psi; ++f) out[r * n_psi + f] -= mx;
+        float mx = out[r * pf];
+        for (int f = 1; f < n_psi; ++f) mx = fmaxf(mx, out[r * pf + f]);
+        for (int f = 0; f < n_psi; ++f) out[r * pf + f] -= mx;
       }
       __syncthreads();
     }
-    for (int idx = threadIdx.x; idx < C * n_psi; idx += kThreads)
-      if (idx / n_psi < valid) out[idx] = expf(out[idx]) * rsqrtf((float)n_psi);
+    for (int idx = threadIdx.x; idx < C * n_psi; idx += kThreads) {
+      const int r = idx / n_psi, o = r * pf + idx % n_psi;
+      if (r < valid) out[o] = expf(out[o]) * rsqrtf((float)n_psi);
+    }
     __syncthreads();
   }
 }
@@ -167,7 +168,7 @@ __device__ void state_update_f32(float* sm, const F32Layout& Ly, int C, int L, i
   for (int b = threadIdx.x; b < blocks; b += kThreads) {
     const int m0 = (b / nb) * 4, n0 = (b % nb) * 4;
     float acc[4][4] = {};
-    mm_atb(acc, sm + Ly.FK, n_psi, sm + Ly.V, d_v, sm + Ly.XI, m0, n0, K);
+    mm_atb(acc, sm + Ly.FK, Ly.PF, sm + Ly.V, d_v, sm + Ly.XI, m0, n0, K);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       F4* sp = (F4*)(sm + Ly.S + (m0 + r) * d_v + n0);
@@ -176,7 +177,7 @@ __device__ void state_update_f32(float* sm, const F32Layout& Ly, int C, int L, i
   }
   for (int pp = threadIdx.x; pp < n_psi; pp += kThreads) {
     float acc = 0.f;
-    for (int i = 0; i < L; ++i) acc += sm[Ly.XI + i] * sm[Ly.FK + i * n_psi + pp];
+    for (int i = 0; i < L; ++i) acc += sm[Ly.XI + i] * sm[Ly.FK + i * Ly.PF + pp];
     sm[Ly.Z + pp] = a * sm[Ly.Z + pp] + acc;
   }
   __syncthreads();
@@ -200,7 +201,9 @@ __global__ __launch_bounds__(kThreads) void k_summary_f32(PrefillParams p) {
     const int t0 = c * p.C, L = min(p.C, T - t0);
     __syncthreads();
     load_rows_f32(vb + (size_t)t0 * rv, rv, sm + Ly.V, p.C, L, p.d_v);
-    features_f32(kb + (size_t)t0 * rk, rk, sm + Ly.RAW, sm + Ly.FK, p.C, L, p.d_k, p.n_psi, kpsi, w);
+    load_rows_f32(kb + (size_t)t0 * rk, rk, sm + Ly.RK, p.C, L, p.d_k);
+    __syncthreads();
+    features_f32(sm + Ly.RK, sm + Ly.FK, Ly.PF, p.C, L, p.d_k, p.n_psi, kpsi, w);
     state_update_f32(sm, Ly, p.C, L, p.d_v, p.n_psi, lg);
   }
   __syncthreads();
@@ -231,9 +234,13 @@ __global__ __launch_bounds__(kThreads) void k_output_f32(PrefillParams p) {
   for (int c = c0; c < c1; ++c) {
     const int t0 = c * C, L = min(C, T - t0);
     __syncthreads();
+    // v, q and k rows in one round of loads, then both feature maps
     load_rows_f32(vb + (size_t)t0 * rv, rv, sm + Ly.V, C, L, d_v);
-    features_f32(qb + (size_t)t0 * rk, rk, sm + Ly.RAW, sm + Ly.FQ, C, L, p.d_k, n_psi, p.psi, w);
-    features_f32(kb + (size_t)t0 * rk, rk, sm + Ly.RAW, sm + Ly.FK, C, L, p.d_k, n_psi, kpsi, w);
+    load_rows_f32(qb + (size_t)t0 * rk, rk, sm + Ly.RQ, C, L, p.d_k);
+    load_rows_f32(kb + (size_t)t0 * rk, rk, sm + Ly.RK, C, L, p.d_k);
+    __syncthreads();
+    features_f32(sm + Ly.RQ, sm + Ly.FQ, Ly.PF, C, L, p.d_k, n_psi, p.psi, w);
+    features_f32(sm + Ly.RK, sm + Ly.FK, Ly.PF, C, L, p.d_k, n_psi, kpsi, w);
     // scores A[j][i] = psi(q_j).psi(k_i) gamma^(j-i), i <= j < L, in 4 x 4 blocks on or below
     // the diagonal (blocks above it are zero)
     {
@@ -241,7 +248,7 @@ __global__ __launch_bounds__(kThreads) void k_output_f32(PrefillParams p) {
       for (int b = threadIdx.x; b < nb * nb; b += kThreads) {
         const int m0 = (b / nb) * 4, n0 = (b % nb) * 4;
         float acc[4][4] = {};
-        if (n0 <= m0 && m0 < L) mm_abt(acc, sm + Ly.FQ, n_psi, sm + Ly.FK, n_psi, m0, n0, n_psi);
+        if (n0 <= m0 && m0 < L) mm_abt(acc, sm + Ly.FQ, Ly.PF, sm + Ly.FK, Ly.PF, m0, n0, n_psi);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           float o4[4];
@@ -258,7 +265,7 @@ __global__ __launch_bounds__(kThreads) void k_output_f32(PrefillParams p) {
     if (p.normalize) {
       for (int j = threadIdx.x; j < C; j += kThreads) {
         F4 qz = {0.f, 0.f, 0.f, 0.f}, r = {0.f, 0.f, 0.f, 0.f};
-        for (int f = 0; f < n_psi; f += 4) qz += ld4s(sm + Ly.FQ + j * n_psi + f) * ld4s(sm + Ly.Z + f);
+        for (int f = 0; f < n_psi; f += 4) qz += ld4s(sm + Ly.FQ + j * Ly.PF + f) * ld4s(sm + Ly.Z + f);
         for (int i = 0; i <= j; i += 4) r += ld4s(sm + Ly.A + j * C + i);  // zero above the diagonal
         sm[Ly.DEN + j] = sm[Ly.THETA + j] * ((qz[0] + qz[1]) + (qz[2] + qz[3])) + ((r[0] + r[1]) + (r[2] + r[3])) + p.eps;
       }
@@ -271,7 +278,7 @@ __global__ __launch_bounds__(kThreads) void k_output_f32(PrefillParams p) {
         const int m0 = (b / nb) * 4, n0 = (b % nb) * 4;
         if (m0 >= L) continue;
         float inter[4][4] = {}, intra[4][4] = {};
-        mm_ab(inter, sm + Ly.FQ, n_psi, sm + Ly.S, d_v, m0, n0, n_psi);
+        mm_ab(inter, sm + Ly.FQ, Ly.PF, sm + Ly.S, d_v, m0, n0, n_psi);
         mm_ab(intra, sm + Ly.A, C, sm + Ly.V, d_v, m0, n0, m0 + 4);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
