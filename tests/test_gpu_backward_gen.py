@@ -98,6 +98,12 @@ GEN_CASES = [
     ("f32_elu1_bthd_state_d64", "f32", PSI_ELU1, 64, 64, 1, "const:0.99", 2, 3, 210, 64, True, "f32", "bthd"),
     ("f32_retention_many_segments", "f32", PSI_IDENTITY, 64, 64, 0, "const:0.999", 1, 1, 9000, 64, True, "f32",
      "bhtd"),
+    # the largest records the query sweep holds in registers (n_psi * d_v = 16384, four blocks per thread)
+    ("f32_prf256_d64_decay_state_c16", "f32", PSI_PRF, 256, 64, 1, "const:0.995", 1, 2, 140, 16, True, "f32", "bhtd"),
+    ("f32_qshift128_d128_c32", "f32", PSI_PRF_QSHIFT, 128, 128, 1, "none", 1, 1, 120, 32, False, "f32", "bhtd"),
+    # widths that are multiples of 4 but not of 16 or 64
+    ("f32_elu1_d48", "f32", PSI_ELU1, 48, 48, 1, "const:0.99", 1, 3, 111, 32, True, "f32", "bhtd"),
+    ("f32_retention_d20_bthd", "f32", PSI_IDENTITY, 20, 20, 0, "retnet_spread", 2, 2, 77, 16, False, "f32", "bthd"),
     ("bf16_elu1_norm_d64_bf16_dout", "bf16", PSI_ELU1, 64, 64, 1, "none", 2, 2, 300, 64, False, "bf16", "bhtd"),
     ("bf16_retention_d64_c32_state_bthd", "bf16", PSI_IDENTITY, 64, 64, 0, "retnet_spread", 1, 3, 260, 32, True,
      "f32", "bthd"),
