@@ -332,6 +332,7 @@ la_status prefill_impl(const la_prefill_desc* d, const int32_t* cu_seqlens, int3
     p.n_rec = pl.rec_per_seg * (pl.n_seg - 1) + 1;
     p.sum_end = (pl.n_seg - 1) * pl.seg_chunks;
   }
+  p.sum_rounded = !want_final && !gated;  // the records reach only outputs
   // the summary pass: one workgroup per record
   PrefillParams ps = p;
   ps.seg_chunks = pl.seg_chunks / pl.rec_per_seg;

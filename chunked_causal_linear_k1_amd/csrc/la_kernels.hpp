@@ -51,6 +51,9 @@ struct PrefillParams {
   int n_rec;             // summary records per sequence in ws (the record stride)
   int rec_per_seg;       // records per segment
   int sum_end;           // the summary pass folds chunks below this index only
+  int sum_rounded;       // 1: no final state is asked for, so the bf16 summary pass may round
+                         // elu+1 key features (denominator, no decay) to bf16 once, as the
+                         // output pass does; 0: every inexact operand stays hi + lo
   int has_decay;
   float log2g[LA_MAX_DECAY_HEADS];  // log2(gamma_h), 0 when gamma_h == 1
 };

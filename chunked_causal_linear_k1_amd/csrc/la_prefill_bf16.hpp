@@ -233,12 +233,16 @@ struct SumGeo {
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
 
-template <int C, int D, bool DECAY, bool NORM, bool ELU>
+template <int C, int D, bool DECAY, bool NORM, bool ELU, bool ONE = false>
 __global__ __launch_bounds__(2 * D) void k_summary(PrefillParams p) {
   // Identity keys are exact in bf16: the decay goes on the values, S += K^T (Xi V), with Xi V
-  // split hi + lo in registers. elu+1 keys keep K~ = Xi psi(K) as hi + lo.
+  // split hi + lo in registers. elu+1 keys keep K~ = Xi psi(K) as hi + lo, except with ONE
+  // (elu+1, a denominator, no decay, no final state asked for): psi(K) rounded to bf16 once
+  // (nearest even), the policy of the output pass, since these records reach only outputs,
+  // which average the rounding over the features; Z still sums the unrounded features.
+  static_assert(!ONE || (ELU && NORM && !DECAY), "single rounding: elu+1 keys with a denominator, no decay");
   constexpr bool VDEC = DECAY && !ELU;
-  constexpr bool SPLIT = (DECAY || ELU) && !VDEC;  // K~ inexact in bf16: keep a lo part
+  constexpr bool SPLIT = (DECAY || ELU) && !VDEC && !ONE;  // K~ inexact in bf16: keep a lo part
   using G = SumGeo<C, D, VDEC>;
   extern __shared__ __align__(16) unsigned char smem[];
   const int bh = blockIdx.x, seg = blockIdx.y, head = bh % p.H;
@@ -1297,6 +1301,8 @@ const void* output_kernel(int& lds, int& threads) {
 template <int C, int D, bool DECAY, bool NORM, bool ELU>
 hipError_t launch_flags(const PrefillParams& p, hipStream_t s, bool out) {
   const void* kern = (const void*)k_summary<C, D, DECAY, NORM, ELU>;
+  if constexpr (ELU && NORM && !DECAY)
+    if (p.sum_rounded) kern = (const void*)k_summary<C, D, DECAY, NORM, ELU, true>;
   int lds = SumGeo<C, D, DECAY && !ELU>::LDS_BYTES;
   int threads = 2 * D;
   if (out)
