@@ -353,6 +353,8 @@ la_status prefill_impl(const la_prefill_desc* d, const int32_t* cu_seqlens, int3
   sp.n_seg = ps.n_seg; sp.seg_len = ps.seg_chunks * d->chunk;
   sp.has_decay = p.has_decay;
   memcpy(sp.log2g, p.log2g, sizeof sp.log2g);
+  sp.write_every = pl.rec_per_seg;       // the output pass reads the record at each segment start
+  if (!want_final) sp.n_read = p.n_rec - 1;  // the last record feeds only the final state
 
   auto mark = [&](int i) -> hipError_t {
     return (events && events[i]) ? hipEventRecord(events[i], stream) : hipSuccess;

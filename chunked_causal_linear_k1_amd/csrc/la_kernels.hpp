@@ -74,6 +74,11 @@ struct ScanParams {
                          // the backward pass); the prefix of segment s then folds segments > s
   int has_decay;
   float log2g[LA_MAX_DECAY_HEADS];
+  // Work the prefill's output pass does not need (0: none skipped): records at or past n_read
+  // are not read (taken as empty; only a final state would need them), and only every
+  // write_every-th prefix is written (the output pass reads the record at each segment start).
+  int n_read;
+  int write_every;
   int* rounds = nullptr;  // diagnostic record when set: the length of the scan's longest chain of
                           // dependent (+) steps (device int, raised by atomic max)
 };

@@ -101,7 +101,9 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_segment_scan(ScanParams p) {
   f32x4 ta = {1.f, 1.f, 1.f, 1.f};
 #pragma unroll
   for (int i = 0; i < RUN; ++i)
-    run[i] = (live && s0 + i < s1) ? ld4(base + (size_t)seg_of(s0 + i) * REC) : f32x4{0.f, 0.f, 0.f, 0.f};
+    run[i] = (live && s0 + i < s1 && (p.n_read <= 0 || seg_of(s0 + i) < p.n_read))
+                 ? ld4(base + (size_t)seg_of(s0 + i) * REC)
+                 : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < RUN; ++i) {
     if (s0 + i < s1) {
@@ -179,7 +181,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_segment_scan(ScanParams p) {
   for (int i = 0; i < RUN; ++i) {
     if (s0 + i < s1) {
       const f32x4 as = seg_decay(seg_of(s0 + i));
-      if (live) st4(base + (size_t)seg_of(s0 + i) * REC, cx);
+      if (live && (p.write_every <= 1 || seg_of(s0 + i) % p.write_every == 0))
+        st4(base + (size_t)seg_of(s0 + i) * REC, cx);
       cx = as * cx + run[i];
     }
   }
