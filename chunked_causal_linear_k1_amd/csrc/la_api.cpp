@@ -333,6 +333,9 @@ la_status prefill_impl(const la_prefill_desc* d, const int32_t* cu_seqlens, int3
     p.sum_end = (pl.n_seg - 1) * pl.seg_chunks;
   }
   p.sum_rounded = !want_final && !gated;  // the records reach only outputs
+  // few records before each segment, no initial or final state: the output pass folds them
+  p.fold_records = d->in_dtype == LA_BF16 && !gated && !want_final && !init_S && !(d->normalize && init_Z) &&
+                   la::prefill_bf16_output_folds(p);
   // the summary pass: one workgroup per record
   PrefillParams ps = p;
   ps.seg_chunks = pl.seg_chunks / pl.rec_per_seg;
@@ -365,7 +368,7 @@ la_status prefill_impl(const la_prefill_desc* d, const int32_t* cu_seqlens, int3
     e = gated ? la::launch_prefill_gated(ps, stream, false)
               : bf ? la::launch_prefill_bf16_summary(ps, stream) : la::launch_prefill_f32_summary(ps, stream);
   if (e == hipSuccess) e = mark(1);
-  if (e == hipSuccess) e = la::launch_segment_scan(sp, stream);
+  if (e == hipSuccess && !p.fold_records) e = la::launch_segment_scan(sp, stream);
   if (e == hipSuccess) e = mark(2);
   if (e == hipSuccess)
     e = gated ? la::launch_prefill_gated(p, stream, true)

@@ -51,6 +51,8 @@ struct PrefillParams {
   int n_rec;             // summary records per sequence in ws (the record stride)
   int rec_per_seg;       // records per segment
   int sum_end;           // the summary pass folds chunks below this index only
+  int fold_records;      // 1: no scan ran; the output pass folds the summary records before its
+                         // segment itself (few records, no initial or final state)
   int sum_rounded;       // 1: no final state is asked for, so the bf16 summary pass may round
                          // elu+1 key features (denominator, no decay) to bf16 once, as the
                          // output pass does; 0: every inexact operand stays hi + lo
@@ -156,6 +158,9 @@ __device__ __forceinline__ SeqSpan seq_span(const PrefillParams& p, int bh) {
 
 // Launchers: return hipSuccess or the launch error. Shapes are validated by the caller.
 bool prefill_bf16_supported(int C, int d_k, int d_v, int n_psi, int psi);
+// Whether the bf16 output kernel for these parameters can fold the summary records before its
+// segment itself (then the scan between the passes is not launched).
+bool prefill_bf16_output_folds(const PrefillParams& p);
 hipError_t launch_prefill_bf16_summary(const PrefillParams& p, hipStream_t s);
 hipError_t launch_prefill_bf16_output(const PrefillParams& p, hipStream_t s);
 

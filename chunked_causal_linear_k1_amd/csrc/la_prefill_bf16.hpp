@@ -973,15 +973,57 @@ __global__ __launch_bounds__(512) void k_output_w8(PrefillParams p) {
   float* const fN = (float*)(smem + pin(G::OFF_F + 4 * n));
 
   const size_t E = (size_t)D * D + D;
-  const float* pre = p.ws + rec_index(p, bh, seg) * E;
   f32x16 S[NPH];
+  if (p.fold_records) {
+    // no scan ran: the state before this segment is the fold of the summary records before it,
+    // X_0 (+) X_1 (+) ... in order (each record's decay gamma^len applied to what came before;
+    // every one of them is a whole sub-segment), two records' loads in flight at a time
+    const float* rec = p.ws + (size_t)bh * p.n_rec * E;
+    const int nr = seg * p.rec_per_seg;
+    const float a = DECAY ? exp2_hw((float)((p.seg_chunks / p.rec_per_seg) * C) * lg) : 1.f;
+    float z = 0.f;
 #pragma unroll
-  for (int j = 0; j < NPH; ++j) {
-    const int pt = NPH * fh + (j + rot) % NPH;
+    for (int j = 0; j < NPH; ++j) S[j] = f32x16{};
+    for (int r0 = 0; r0 < nr; r0 += 2) {
+      const bool two = r0 + 1 < nr;
+      const float* x0 = rec + (size_t)r0 * E;
+      const float* x1 = rec + (size_t)(two ? r0 + 1 : r0) * E;
+      f32x16 y0[NPH], y1[NPH];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) S[j][r] = pre[(size_t)(pt * 32 + dtile_row(r, lane)) * D + Ew + n];
+      for (int j = 0; j < NPH; ++j) {
+        const int pt = NPH * fh + (j + rot) % NPH;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const size_t o = (size_t)(pt * 32 + dtile_row(r, lane)) * D + Ew + n;
+          y0[j][r] = x0[o];
+          y1[j][r] = x1[o];
+        }
+      }
+      const float z0 = (NORM && tid < D) ? x0[(size_t)D * D + tid] : 0.f;
+      const float z1 = (NORM && tid < D) ? x1[(size_t)D * D + tid] : 0.f;
+#pragma unroll
+      for (int j = 0; j < NPH; ++j) {
+        if (DECAY) S[j] *= a;
+        S[j] += y0[j];
+        if (two) {
+          if (DECAY) S[j] *= a;
+          S[j] += y1[j];
+        }
+      }
+      z = a * z + z0;
+      if (two) z = a * z + z1;
+    }
+    if (tid < D) sF[G::F_Z + tid] = NORM ? z : 0.f;
+  } else {
+    const float* pre = p.ws + rec_index(p, bh, seg) * E;
+#pragma unroll
+    for (int j = 0; j < NPH; ++j) {
+      const int pt = NPH * fh + (j + rot) % NPH;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) S[j][r] = pre[(size_t)(pt * 32 + dtile_row(r, lane)) * D + Ew + n];
+    }
+    if (tid < D) sF[G::F_Z + tid] = NORM ? pre[(size_t)D * D + tid] : 0.f;
   }
-  if (tid < D) sF[G::F_Z + tid] = NORM ? pre[(size_t)D * D + tid] : 0.f;
   for (int j = tid; j < C; j += G::NT) sF[G::F_THETA + j] = DECAY ? exp2_hw((float)(j + 1) * lg) : 1.f;
 
   const SeqSpan sq = seq_span(p, bh);
