@@ -48,12 +48,13 @@ static PrefillParams in_64_token_steps(const PrefillParams& p) {
   return q;
 }
 
-// The eight-wave output kernel (d = 128 with elu+1 features or a denominator) folds up to
-// kMaxFold records itself: a few loads per lane and record, against a scan launch.
+// The eight-wave output kernels (d = 128 with elu+1 features or a denominator, and random
+// features) fold up to kMaxFold records themselves: a few loads per lane and record, against a
+// scan launch.
 constexpr int kMaxFold = 8;
 bool prefill_bf16_output_folds(const PrefillParams& p) {
-  if (is_prf(p.psi) || p.cu_seqlens || p.d_k != 128 || p.d_v != 128) return false;
-  if (p.psi != LA_PSI_ELU1 && !p.normalize) return false;  // the shared-score kernel reads scanned prefixes
+  if (p.cu_seqlens || p.d_k != 128 || p.d_v != 128) return false;
+  if (!is_prf(p.psi) && p.psi != LA_PSI_ELU1 && !p.normalize) return false;  // the shared-score kernel reads scanned prefixes
   if (p.rec_per_seg < 1 || p.seg_chunks % p.rec_per_seg != 0) return false;
   return (long long)(p.n_seg - 1) * p.rec_per_seg <= kMaxFold;
 }

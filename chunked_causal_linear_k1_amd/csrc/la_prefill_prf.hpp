@@ -402,15 +402,45 @@ __global__ __launch_bounds__(512) void k_output_prf(PrefillParams p) {
 
   // exclusive prefix state of this segment: this wave's rows and columns
   const size_t E = (size_t)NP * D + NP;
-  const float* pre = p.ws + rec_index(p, bh, seg) * E;
   f32x16 S[NFH];  // S[j]: feature tile fh NFH + (j + rot) % NFH, value columns Ew ..
+  if (p.fold_records) {
+    // no scan ran: fold the summary records before this segment in order (each record's decay
+    // gamma^len applied to what came before; all of them are whole sub-segments), one record's
+    // loads in flight at a time
+    const float* rec = p.ws + (size_t)bh * p.n_rec * E;
+    const int nr = seg * p.rec_per_seg;
+    const float a = DECAY ? exp2_hw((float)((p.seg_chunks / p.rec_per_seg) * C) * lg) : 1.f;
 #pragma unroll
-  for (int pt = 0; pt < NFH; ++pt) {
-    const int tile = fh * NFH + (pt + rot) % NFH;
+    for (int pt = 0; pt < NFH; ++pt) S[pt] = f32x16{};
+    float z = 0.f;
+    for (int r0 = 0; r0 < nr; ++r0) {
+      const float* x = rec + (size_t)r0 * E;
+      f32x16 y[NFH];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) S[pt][r] = pre[(size_t)(tile * 32 + dtile_row(r, lane)) * D + Ew + n];
+      for (int pt = 0; pt < NFH; ++pt) {
+        const int tile = fh * NFH + (pt + rot) % NFH;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) y[pt][r] = x[(size_t)(tile * 32 + dtile_row(r, lane)) * D + Ew + n];
+      }
+      const float zr = (NORM && tid < NP) ? x[(size_t)NP * D + tid] : 0.f;
+#pragma unroll
+      for (int pt = 0; pt < NFH; ++pt) {
+        if (DECAY) S[pt] *= a;
+        S[pt] += y[pt];
+      }
+      z = a * z + zr;
+    }
+    if (tid < NP) sF[G8::F_Z + tid] = NORM ? z : 0.f;
+  } else {
+    const float* pre = p.ws + rec_index(p, bh, seg) * E;
+#pragma unroll
+    for (int pt = 0; pt < NFH; ++pt) {
+      const int tile = fh * NFH + (pt + rot) % NFH;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) S[pt][r] = pre[(size_t)(tile * 32 + dtile_row(r, lane)) * D + Ew + n];
+    }
+    for (int j = tid; j < NP; j += G8::NT) sF[G8::F_Z + j] = NORM ? pre[(size_t)NP * D + j] : 0.f;
   }
-  for (int j = tid; j < NP; j += G8::NT) sF[G8::F_Z + j] = NORM ? pre[(size_t)NP * D + j] : 0.f;
   for (int j = tid; j < C; j += G8::NT) sF[G8::F_THETA + j] = DECAY ? exp2_hw((float)(j + 1) * lg) : 1.f;
 
   const SeqSpan sq = seq_span(p, bh);

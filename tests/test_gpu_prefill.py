@@ -184,25 +184,29 @@ def test_subsegment_records_and_final_state():
     assert_close(fZ.cpu().reshape(B * H, d).numpy()[heads], rZ, "bf16", "final Z")
 
 
-@pytest.mark.parametrize("decay,C", [("none", 64), ("const:0.999", 64), ("retnet_spread", 128), ("const:0.99", 32)])
-def test_output_pass_folds_records(decay, C):
-    """Few sequences of d = 128 with elu+1 features and a denominator: 2048-token segments of two
-    1024-token records, at most six records before a segment, so with no initial or final state
-    the eight-wave output pass folds the records itself (no scan), with the decay of each record
-    between them. Every output against the oracle, and against the same call with a final state
-    asked for (which takes the scan and the two-term summary records)."""
+@pytest.mark.parametrize("psi,decay,C", [(PSI_ELU1, "none", 64), (PSI_ELU1, "const:0.999", 64),
+                                         (PSI_ELU1, "retnet_spread", 128), (PSI_ELU1, "const:0.99", 32),
+                                         (PSI_PRF, "const:0.995", 64), (PSI_PRF_QSHIFT, "none", 128)])
+def test_output_pass_folds_records(psi, decay, C):
+    """Few sequences at d = 128 (elu+1 features with a denominator, or random features with
+    n_psi 256): segments of two records each, at most six records before a segment, so with no
+    initial or final state the eight-wave output pass folds the records itself (no scan), with
+    the decay of each record between them. Every output against the oracle, and against the same
+    call with a final state asked for (which takes the scan and, for elu+1, two-term summary
+    records)."""
     B, H, T, d = 1, 2, 8000, 128
-    w = Workload(name="fold", B=B, H=H, T=T, d_k=d, d_v=d, n_psi=d, chunk=C, psi=PSI_ELU1, normalize=1, eps=1e-6,
-                 dtype="bf16", seed=21, qk_scale=0.5, v_scale=0.5, decay=decay)
-    announce(f"prefill output pass folding records decay={decay} C={C}")
+    prf = psi in (PSI_PRF, PSI_PRF_QSHIFT)
+    w = Workload(name="fold", B=B, H=H, T=T, d_k=d, d_v=d, n_psi=256 if prf else d, chunk=C, psi=psi, normalize=1,
+                 eps=1e-6, dtype="bf16", seed=21, qk_scale=d ** -0.25 if prf else 0.5, v_scale=0.5, decay=decay)
+    announce(f"prefill output pass folding records psi={psi} decay={decay} C={C}")
     inp = inputs.make_prefill_inputs(w, device="cpu")
     o_fold = _run(w, inp).cpu().reshape(B * H, T, d).numpy()
-    fS = torch.empty((B, H, d, d), dtype=torch.float32, device=DEV)
-    fZ = torch.empty((B, H, d), dtype=torch.float32, device=DEV)
+    fS = torch.empty((B, H, w.n_psi, d), dtype=torch.float32, device=DEV)
+    fZ = torch.empty((B, H, w.n_psi), dtype=torch.float32, device=DEV)
     o_scan = _run(w, inp, final_S=fS, final_Z=fZ).cpu().reshape(B * H, T, d).numpy()
     ref = _oracle_o(w, inp)
-    assert_close(o_fold, ref, "bf16", f"o folded records ({decay}, C={C})")
-    assert_close(o_scan, ref, "bf16", f"o scanned records ({decay}, C={C})")
+    assert_close(o_fold, ref, "bf16", f"o folded records (psi {psi}, {decay}, C={C})")
+    assert_close(o_scan, ref, "bf16", f"o scanned records (psi {psi}, {decay}, C={C})")
     assert_close(o_fold, o_scan, "bf16", "o folded against scanned")
 
 
