@@ -28,7 +28,7 @@ ROOT = os.path.dirname(HERE)
 # kernel-name substring -> key in traffic.json
 KERNELS = {
     "k_output_sh<64, 128, true, false, false, false>": "k_output_retnet_128k",
-    "k_summary<64, 128, true, false, false>": "k_summary_retnet_128k",  # 128k summaries fold 64-token steps
+    "k_summary<64, 128, true, false, false, false>": "k_summary_retnet_128k",  # 128k summaries fold 64-token steps
     "k_segment_scan": "k_segment_scan",
     "k_decode": "k_decode_32x64",
 }
