@@ -194,7 +194,7 @@ def bench_backward(w: workloads.Workload, steps: int, warmup: int):
     dout = inputs.make_upstream_grad((w.B, w.H, w.T, w.d_v), w.seed + 11, device="cuda")
     g = inp["gamma"]
     desc = binding.prefill_desc(w.B, w.H, w.T, w.d_k, w.d_v, w.n_psi, w.chunk, w.psi, w.normalize, w.eps,
-                                binding.LA_BF16, binding.LA_F32)
+                                binding.LA_F32 if w.dtype == "f32" else binding.LA_BF16, binding.LA_F32)
     ws = torch.empty(binding.backward_workspace_size(desc), dtype=torch.uint8, device="cuda")
     grads = [torch.empty((w.B, w.H, w.T, d), dtype=torch.float32, device="cuda") for d in (w.d_k, w.d_k, w.d_v)]
     kw = dict(psi=w.psi, chunk=w.chunk, normalize=w.normalize, eps=w.eps, gamma=None if g is None else list(g),
@@ -613,10 +613,11 @@ def main():
                                                             "frac": round(gb / HBM_PEAK_GBS, 4),
                                                             "bytes_per_token_head": gbytes},
                                     "algorithmic_tflops": round(tf, 1), "flop_per_token_head": flop}
-        # backward: compulsory bytes per token-head (q, k, v bf16 and dout fp32 read; dq, dk, dv fp32 written)
-        bwd_bytes = 3 * 128 * 2 + 128 * 4 + 3 * 128 * 4
+        # backward: compulsory bytes per token-head (q, k, v and dout fp32 read; dq, dk, dv fp32 written)
         for key, bw in (("backward_8k", workloads.PREFILL_8K), ("backward_128k", workloads.RETNET_128K),
-                        ("backward_prf_4k", workloads.PRF_4K)):
+                        ("backward_prf_4k", workloads.PRF_4K), ("backward_tiny_f32", workloads.TINY_F32)):
+            ib = 4 if bw.dtype == "f32" else 2
+            bwd_bytes = 3 * bw.d_k * ib + bw.d_v * 4 + 3 * bw.d_k * 4
             pb = bench_backward(bw, args.steps, args.warmup)
             ab = bwd_bytes * pb["units"] / (pb["ms_per_step"] * 1e-3) / 1e9
             line[key] = {"workload": bw.name, "token_heads_per_s": round(pb["token_heads_per_s"], 1),
@@ -624,6 +625,9 @@ def main():
                          "whole_call_roofline": {"bound": "hbm", "achieved": round(ab, 1), "peak": HBM_PEAK_GBS,
                                                  "unit": "GB/s", "frac": round(ab / HBM_PEAK_GBS, 4),
                                                  "bytes_per_token_head": bwd_bytes}}
+            if bw.dtype == "f32":  # the fp32 vector-ALU sweeps at the tiny fp32 shape: latency, not bandwidth
+                line[key]["us_per_call"] = round(pb["ms_per_step"] * 1e3, 2)
+                line[key]["note"] = "fp32 inputs (vector-ALU sweeps); bound by its chain of launches, like the forward"
         vw = workloads.VARLEN_32
         pv = bench_varlen(vw, args.steps, args.warmup)
         av = BYTES_PER_TOKEN_HEAD * pv["units"] / (pv["ms_per_step"] * 1e-3) / 1e9
