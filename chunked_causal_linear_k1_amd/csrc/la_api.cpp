@@ -83,6 +83,7 @@ la_status validate_prefill_desc(const la_prefill_desc* d, bool gated = false) {
 }
 
 struct Plan {
+  int chunk;  // the chunk the kernels walk (the caller's, or kF32LatencyChunk, see make_plan)
   int n_chunks, seg_chunks, n_seg;
   int rec_per_seg, n_rec;  // summary records per segment and per sequence (at most)
   size_t ws_bytes;
@@ -103,11 +104,22 @@ struct Plan {
 // ws_cap (fixed-length batches, nonzero only for lin_attn_prefill_noalloc): when the records
 // exceed it, the plan takes fewer, longer segments, one record each, at most as many per
 // sequence as fit; if not even one record per sequence fits, ws_bytes stays above the cap.
+//
+// latency_chunk (the forward prefill of fixed-length batches): fp32 inputs whose chunks cannot
+// fill the GPU walk chunks of kF32LatencyChunk tokens instead of the caller's, for more and
+// shorter workgroups. The result does not depend on the grouping of tokens into chunks (the
+// same function; only the rounding differs).
+constexpr int kF32LatencyChunk = 16;
 Plan make_plan(const la_prefill_desc* d, long long total_tokens = -1, bool gated = false, bool sub = false,
-               size_t ws_cap = 0) {
+               size_t ws_cap = 0, bool latency_chunk = false) {
   Plan pl;
   const long long BH = (long long)d->B * d->H;
-  pl.n_chunks = (int)((d->T + (long long)d->chunk - 1) / d->chunk);
+  int C = d->chunk;
+  if (latency_chunk && total_tokens < 0 && !gated && d->in_dtype == LA_F32 && C > kF32LatencyChunk &&
+      BH * ((d->T + C - 1) / C) < kTargetWorkgroups)
+    C = kF32LatencyChunk;
+  pl.chunk = C;
+  pl.n_chunks = (int)((d->T + (long long)C - 1) / C);
   if (total_tokens < 0) {
     long long want = (kTargetWorkgroups + BH - 1) / BH;  // segments per sequence
     want = std::min<long long>(want, std::max(1LL, (long long)d->T / kMinSegTokens));
@@ -117,7 +129,7 @@ Plan make_plan(const la_prefill_desc* d, long long total_tokens = -1, bool gated
   } else {
     const long long work = total_tokens * d->H;  // token-heads in the batch
     const long long seg_tokens = std::max<long long>(kMinSegTokens, (work + kTargetWorkgroups - 1) / kTargetWorkgroups);
-    pl.seg_chunks = (int)std::min<long long>(pl.n_chunks, (seg_tokens + d->chunk - 1) / d->chunk);
+    pl.seg_chunks = (int)std::min<long long>(pl.n_chunks, (seg_tokens + C - 1) / C);
   }
   pl.n_seg = (pl.n_chunks + pl.seg_chunks - 1) / pl.seg_chunks;
   if (pl.n_seg > 65535) {  // the grid's y extent
@@ -125,19 +137,19 @@ Plan make_plan(const la_prefill_desc* d, long long total_tokens = -1, bool gated
     pl.n_seg = (pl.n_chunks + pl.seg_chunks - 1) / pl.seg_chunks;
   }
   // the bf16 kernels walk 64-token steps: with 32-token chunks a segment holds an even number
-  if (!gated && d->in_dtype == LA_BF16 && d->chunk == 32 && (pl.seg_chunks & 1)) {
+  if (!gated && d->in_dtype == LA_BF16 && C == 32 && (pl.seg_chunks & 1)) {
     pl.seg_chunks += 1;
     pl.n_seg = (pl.n_chunks + pl.seg_chunks - 1) / pl.seg_chunks;
   }
   pl.rec_per_seg = 1;
   if (sub && total_tokens < 0 && d->in_dtype == LA_BF16) {
-    const int step = !gated && d->chunk == 32 ? 2 : 1;  // chunks per kernel step
+    const int step = !gated && C == 32 ? 2 : 1;  // chunks per kernel step
     // workgroups that fold tokens when the last segment (only the final state needs it) is skipped
     const long long folded = BH * std::max(1, pl.n_seg - 1);
     while (pl.rec_per_seg < kMaxRecPerSeg) {
       const int k2 = 2 * pl.rec_per_seg;
       if (pl.seg_chunks % (k2 * step) != 0) break;
-      if ((long long)(pl.seg_chunks / k2) * d->chunk < kMinSubTokens) break;
+      if ((long long)(pl.seg_chunks / k2) * C < kMinSubTokens) break;
       if (folded * k2 > kTargetWorkgroups || (long long)pl.n_seg * k2 > 65535) break;
       pl.rec_per_seg = k2;
     }
@@ -151,7 +163,7 @@ Plan make_plan(const la_prefill_desc* d, long long total_tokens = -1, bool gated
     if (max_rec >= 1) {
       pl.rec_per_seg = 1;
       pl.seg_chunks = (int)((pl.n_chunks + max_rec - 1) / max_rec);
-      if (!gated && d->in_dtype == LA_BF16 && d->chunk == 32 && (pl.seg_chunks & 1)) pl.seg_chunks += 1;
+      if (!gated && d->in_dtype == LA_BF16 && C == 32 && (pl.seg_chunks & 1)) pl.seg_chunks += 1;
       pl.n_seg = (pl.n_chunks + pl.seg_chunks - 1) / pl.seg_chunks;
       pl.n_rec = pl.n_seg;
       pl.ws_bytes = (size_t)BH * pl.n_rec * E * sizeof(float);
@@ -184,7 +196,7 @@ la_status lin_attn_prefill_workspace_size(const la_prefill_desc* d, size_t* byte
   if (!bytes) return LA_ERR_NULL;
   const la_status st = validate_prefill_desc(d);
   if (st != LA_OK) return st;
-  *bytes = make_plan(d, -1, false, true).ws_bytes;
+  *bytes = make_plan(d, -1, false, true, 0, true).ws_bytes;
   return LA_OK;
 }
 
@@ -302,7 +314,7 @@ la_status prefill_impl(const la_prefill_desc* d, const int32_t* cu_seqlens, int3
   if (st != LA_OK) return st;
   if (gated && !aligned16(log_gate)) return LA_ERR_ALIGN;
   const bool sub = !cu_seqlens;
-  const Plan pl = make_plan(d, cu_seqlens ? (long long)total_tokens : -1LL, gated, sub, ws_cap);
+  const Plan pl = make_plan(d, cu_seqlens ? (long long)total_tokens : -1LL, gated, sub, ws_cap, true);
   if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes)) return LA_ERR_WORKSPACE;
 
   PrefillParams p;
@@ -319,7 +331,7 @@ la_status prefill_impl(const la_prefill_desc* d, const int32_t* cu_seqlens, int3
   } else {
     p.tok_rows = 1; p.head_rows = d->T; p.seq_rows = (long long)d->H * d->T;
   }
-  p.d_k = d->d_k; p.d_v = d->d_v; p.n_psi = d->n_psi; p.C = d->chunk;
+  p.d_k = d->d_k; p.d_v = d->d_v; p.n_psi = d->n_psi; p.C = pl.chunk;
   p.psi = d->psi; p.normalize = d->normalize; p.eps = d->eps;
   p.out_bf16 = d->out_dtype == LA_BF16;
   p.n_chunks = pl.n_chunks; p.seg_chunks = pl.seg_chunks; p.n_seg = pl.n_seg;
@@ -353,7 +365,7 @@ la_status prefill_impl(const la_prefill_desc* d, const int32_t* cu_seqlens, int3
   sp.gated = gated;
   sp.BH = d->B * d->H; sp.H = d->H; sp.T = d->T;
   sp.n_psi = d->n_psi; sp.d_v = d->d_v;
-  sp.n_seg = ps.n_seg; sp.seg_len = ps.seg_chunks * d->chunk;
+  sp.n_seg = ps.n_seg; sp.seg_len = ps.seg_chunks * pl.chunk;
   sp.has_decay = p.has_decay;
   memcpy(sp.log2g, p.log2g, sizeof sp.log2g);
   sp.write_every = pl.rec_per_seg;       // the output pass reads the record at each segment start
@@ -386,7 +398,7 @@ namespace la {
 la_status prefill_capped_check(const la_prefill_desc* d, size_t ws_cap) {
   const la_status st = validate_prefill_desc(d);
   if (st != LA_OK) return st;
-  return make_plan(d, -1, false, true, ws_cap).ws_bytes > ws_cap ? LA_ERR_WORKSPACE : LA_OK;
+  return make_plan(d, -1, false, true, ws_cap, true).ws_bytes > ws_cap ? LA_ERR_WORKSPACE : LA_OK;
 }
 
 // lin_attn_prefill with a workspace of ws_cap bytes and the plan fitted to it.

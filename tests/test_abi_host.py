@@ -274,7 +274,14 @@ def test_backward_validation_and_workspace():
         assert st_ == LA_OK, kw
         f_ = ctypes.c_size_t(0)
         assert lib.lin_attn_prefill_workspace_size(ctypes.byref(_desc(**{**base, **kw})), ctypes.byref(f_)) == LA_OK
-        assert nb == 2 * f_.value + 2 * 4 * base["B"] * base["H"] * base["T"], kw
+        tok = 2 * 4 * base["B"] * base["H"] * base["T"]
+        if kw.get("in_dtype") == LA_F32:
+            # two record regions of at least one record per sequence (the fp32 forward may plan its
+            # own chunking for latency, so its workspace is not the backward's half)
+            d_v, n_psi = kw.get("d_v", 128), kw.get("n_psi", 128)
+            assert nb >= 2 * base["B"] * base["H"] * (n_psi * d_v + n_psi) * 4 + tok, kw
+        else:
+            assert nb == 2 * f_.value + tok, kw
     for kw in (dict(chunk=16), dict(in_dtype=LA_F32), dict(psi=2, n_psi=64), dict(psi=2, n_psi=256, chunk=16),
                dict(in_dtype=LA_F32, chunk=32, psi=2, n_psi=256), dict(in_dtype=LA_F32, chunk=128),
                dict(d_k=96, d_v=96, n_psi=96)):
