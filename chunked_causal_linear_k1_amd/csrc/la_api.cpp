@@ -105,7 +105,7 @@ struct Plan {
 // exceed it, the plan takes fewer, longer segments, one record each, at most as many per
 // sequence as fit; if not even one record per sequence fits, ws_bytes stays above the cap.
 //
-// latency_chunk (the forward prefill of fixed-length batches): fp32 inputs whose chunks cannot
+// latency_chunk (the prefill and its backward, fixed-length batches): fp32 inputs whose chunks cannot
 // fill the GPU walk chunks of kF32LatencyChunk tokens instead of the caller's, for more and
 // shorter workgroups. The result does not depend on the grouping of tokens into chunks (the
 // same function; only the rounding differs).
@@ -255,7 +255,7 @@ size_t backward_ws_bytes(const la_prefill_desc* d, long long total_tokens = -1) 
     const size_t bank = ((size_t)d->H * d->n_psi * d->d_k * 2 + 15) & ~(size_t)15;
     return 2 * prf_backward_plan(d).ws_bytes + tok + bank;
   }
-  return 2 * make_plan(d, total_tokens).ws_bytes + tok;
+  return 2 * make_plan(d, total_tokens, false, false, 0, true).ws_bytes + tok;
 }
 
 la_status lin_attn_prefill_backward_workspace_size(const la_prefill_desc* d, size_t* bytes) {
@@ -528,7 +528,7 @@ la_status backward_impl(const la_prefill_desc* d, const int32_t* cu_seqlens, int
   st = check_gamma(gamma, d->H);
   if (st != LA_OK) return st;
   const long long tt = cu_seqlens ? (long long)total_tokens : -1LL;
-  const Plan pl = prf ? prf_backward_plan(d) : make_plan(d, tt);
+  const Plan pl = prf ? prf_backward_plan(d) : make_plan(d, tt, false, false, 0, true);
   const size_t need = backward_ws_bytes(d, tt);
   if (!workspace || workspace_bytes < need) return LA_ERR_WORKSPACE;
 
@@ -547,7 +547,7 @@ la_status backward_impl(const la_prefill_desc* d, const int32_t* cu_seqlens, int
   }
   p.d_k = d->d_k; p.d_v = d->d_v; p.n_psi = d->n_psi;
   // random features walk one 64-token step per segment (the same function for every chunk size)
-  p.C = prf ? kPrfBwdStep : d->chunk;
+  p.C = prf ? kPrfBwdStep : pl.chunk;
   p.prf_w = prf_w;
   p.psi = d->psi; p.normalize = d->normalize; p.eps = d->eps;
   p.n_chunks = pl.n_chunks; p.seg_chunks = pl.seg_chunks; p.n_seg = pl.n_seg;
