@@ -8,6 +8,8 @@ integer-valued case whose every partial sum is exact in fp32 (bit-exact check).
 """
 from __future__ import annotations
 
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -208,6 +210,19 @@ def test_output_pass_folds_records(psi, decay, C):
     assert_close(o_fold, ref, "bf16", f"o folded records (psi {psi}, {decay}, C={C})")
     assert_close(o_scan, ref, "bf16", f"o scanned records (psi {psi}, {decay}, C={C})")
     assert_close(o_fold, o_scan, "bf16", "o folded against scanned")
+
+
+def test_f32_latency_chunking():
+    """An fp32 call too small to fill the GPU with its own chunks walks 16-token chunks: chunk 64
+    and chunk 16 then take the same plan and give bitwise equal outputs, both at the fp32 bar."""
+    w = Workload(name="f32_lat", B=1, H=2, T=700, d_k=64, d_v=64, n_psi=64, chunk=64, psi=PSI_ELU1, normalize=1,
+                 eps=1e-6, dtype="f32", seed=31, qk_scale=0.5, v_scale=1.0, decay="const:0.99")
+    announce("prefill fp32 latency chunking")
+    inp = inputs.make_prefill_inputs(w, device="cpu")
+    o64 = _run(w, inp).cpu().numpy()
+    o16 = _run(dataclasses.replace(w, chunk=16), inp).cpu().numpy()
+    assert np.array_equal(o64, o16), "chunk 64 and chunk 16 took different plans"
+    assert_close(o64.reshape(2, w.T, 64), _oracle_o(w, inp), "f32", "o, fp32 latency chunking")
 
 
 def test_initial_and_final_state_c64():
